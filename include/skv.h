@@ -1,0 +1,134 @@
+/*
+ * skv.h -- C ABI of libskv: lossless KV-cache coding on MI355X (gfx950).
+ *
+ * The library codes a target KV cache against a predictor cache that the
+ * decoder can reproduce on its own, so only the residual is stored, and the
+ * decoder returns the original bytes exactly ("Speculative KV coding:
+ * losslessly compressing KV cache by up to ~4x", section "Core idea").
+ * The residual is entropy-coded with rANS against static per-channel
+ * discretized-Laplace tables fitted once on calibration data (same page,
+ * "What to use as the predictor"; "DCKV compresses the prompt KV cache of
+ * hybrid language models with learned transform coding", section "How it
+ * differs": GPU rANS, Laplace integrated over quantization cells).  The
+ * checkerboard mode codes DCKV-style transform coefficients whose Laplace is
+ * shifted by a token-conditioned mean, even tokens first and odd tokens
+ * from their decoded neighbours (DCKV page, "How it differs").
+ *
+ * Conventions for every call:
+ *   - returns SKV_OK (0) or a negative skv_status; nothing is thrown;
+ *   - "host" pointers are CPU memory, "device" pointers are HIP device
+ *     memory of the current device; the caller owns every buffer it passes;
+ *   - device work runs on the caller's hipStream_t (0 = legacy default);
+ *   - on error, output buffers hold unspecified bytes, but nothing outside
+ *     the given buffers is written.
+ * Byte layouts of the table blob and of the container are fixed,
+ * little-endian, and described next to the calls that produce them.
+ */
+#ifndef SKV_H
+#define SKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SKV_ABI_VERSION 1u
+
+typedef enum {
+    SKV_OK = 0,
+    SKV_ERR_ARG = -1,      /* null / invalid argument, unknown blob pointer       */
+    SKV_ERR_SHAPE = -2,    /* tokens or channels not multiples of the tile sizes,
+                              dtype/mode combination not supported, ABI mismatch  */
+    SKV_ERR_CAPACITY = -3, /* an output or work buffer is too small               */
+    SKV_ERR_CORRUPT = -4,  /* container malformed or a stream fails its checks   */
+    SKV_ERR_TABLES = -5,   /* table blob malformed, or not the one a container
+                              was coded with (hash mismatch), or shape mismatch  */
+    SKV_ERR_DEVICE = -6,   /* a HIP runtime call failed                           */
+    SKV_ERR_NOMEM = -7     /* host or device allocation failed                   */
+} skv_status;
+
+typedef enum { SKV_BF16 = 1, SKV_E4M3 = 2, SKV_INT16 = 3 } skv_dtype;
+typedef enum { SKV_RESIDUAL = 0, SKV_CHECKERBOARD = 1 } skv_mode;
+
+/* Cache shape.  Residual mode: arrays are [layers][kv][tokens][channels]
+ * of bf16 bit patterns (2 B) or e4m3 codes (1 B), channel fastest; tokens a
+ * multiple of 128, channels a multiple of 32.  Checkerboard mode: dtype
+ * SKV_INT16, layers = kv = 1, arrays are [tokens][channels] int16 with
+ * tokens a multiple of 256.  abi_version must be SKV_ABI_VERSION. */
+typedef struct {
+    uint32_t abi_version;
+    uint32_t dtype;      /* skv_dtype */
+    uint32_t mode;       /* skv_mode  */
+    uint32_t layers, kv, tokens, channels;
+} skv_shape;
+
+/* Fit the frequency tables once from calibration data (host only, fp64).
+ *   calib_target, calib_aux (host):
+ *     residual mode: target / predictor elements, [layers][kv][calib_tokens][channels];
+ *     checkerboard:  int16 coefficients / int16 side input G (each token's
+ *                    mean in 1/16 cells), [calib_tokens][channels], calib_tokens even.
+ *   s->tokens is ignored.
+ * Each table is a Laplace integrated over unit cells (location 0, or f/16
+ * for shifted table f in checkerboard mode; scale = mean |residual| over
+ * calibration values with |residual| <= 127, floored at 0.05), with a direct
+ * range of 1..255 symbols (all with cell mass >= 2^-12) and an escape symbol
+ * whose probability is the smoothed calibration escape rate, quantized to
+ * 12-bit frequencies >= 1 summing to 4096.
+ * On success *tables_blob points to a library-owned, immutable blob of
+ * *blob_bytes bytes (layout: 64 B header "SKVT" | u16 version | u8 dtype |
+ * u8 mode | u32 n_tables | u32 layers | u32 kv | u32 channels | u32
+ * calib_tokens | u32 0 | u64 total bytes | 24 B zero; then n_tables records
+ * of u16 n, u16 freq[256]).  Release it with skv_free. */
+int skv_fit_tables(const skv_shape* s, const void* calib_target, const void* calib_aux,
+                   uint32_t calib_tokens, void** tables_blob, size_t* blob_bytes);
+
+/* Copy a blob produced elsewhere (same layout as above) into a library-owned
+ * blob after validating it: every table has 1 <= n <= 255, freq[0..n] >= 1
+ * summing to 4096 and zeros beyond.  Release with skv_free. */
+int skv_load_tables(const void* blob, size_t blob_bytes, void** tables_blob);
+
+/* Encode (device).  d_target and d_aux (predictor, or G in checkerboard mode)
+ * are device arrays of the shape's layout.  The container written to d_out:
+ *   64 B header: "SKV1" | u16 1 | u8 dtype | u8 mode | u8 12 | u8 32 | u16 128 |
+ *                u32 layers | u32 kv | u32 tokens | u32 channels | u32 0 |
+ *                u64 n_streams | u64 FNV-1a-64 of the blob | u64 payload bytes | u64 0
+ *   index: (n_streams+1) u64 payload offsets, bit 63 = stream stored raw,
+ *          last entry = payload bytes
+ *   payload: streams (32 lanes x 128 steps) in id order; coded streams are
+ *          32 u32 final rANS states, the u16 words, a zero u16 if their
+ *          count is odd; raw streams are the 4096 target elements.
+ * Two-phase sizing: with d_out == NULL, *out_bytes receives the bound (every
+ * stream raw); with d_work == NULL, *work_bytes receives the workspace need.
+ * Otherwise out_capacity must hold the container (else SKV_ERR_CAPACITY and
+ * *out_bytes = the size needed) and *work_bytes the need.  Blocks the host
+ * until the container size is known (one stream synchronization). */
+int skv_encode(const void* tables_blob, const skv_shape* s, const void* d_target, const void* d_aux,
+               void* d_out, size_t out_capacity, size_t* out_bytes,
+               void* d_work, size_t* work_bytes, hipStream_t stream);
+
+/* Decode (device).  d_in holds in_bytes of container; d_aux is the
+ * predictor (or G) in the shape's layout; d_out receives the reconstruction
+ * (out_capacity bytes available).  The shape comes from the header, which is
+ * validated against the blob (hash, dtype, mode, layers, kv, channels).
+ * With d_work == NULL, *work_bytes receives the workspace need.  Every
+ * stream checks that its rANS states end at 2^16 and that it consumed its
+ * words exactly; any failure returns SKV_ERR_CORRUPT.  Checkerboard
+ * containers decode in two launches on the same stream: even tokens, then
+ * odd tokens.  Blocks the host to read the header and the integrity word. */
+int skv_decode(const void* tables_blob, const void* d_in, size_t in_bytes, const void* d_aux,
+               void* d_out, size_t out_capacity, void* d_work, size_t* work_bytes, hipStream_t stream);
+
+/* Release a library-owned blob and its device copies.  NULL is a no-op. */
+void skv_free(void* tables_blob);
+
+/* Library ABI version (SKV_ABI_VERSION) and a static message per status. */
+uint32_t skv_version(void);
+const char* skv_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SKV_H */

@@ -1,0 +1,266 @@
+// skv_fit.cpp -- host-side table fit, blob validation and hashing.
+//
+// Statistics are measured once on calibration data and then frozen
+// ("Speculative KV coding ..." page, section "What to use as the
+// predictor").  The model is a Laplace per channel (or per component and
+// shift) integrated over unit quantization cells (DCKV page, "How it
+// differs").  Everything here is fp64 and runs once; the coding kernels
+// only ever see the resulting integer frequencies.
+//
+// The order of floating-point operations is part of the format: the scale
+// is an exact sum divided once, the cell mass uses one of three closed forms
+// chosen by the cell's position, the direct masses are summed in symbol order
+// and rescaled as 4096 * (P * ((1 - p_esc) / sum)).
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <numeric>
+#include <vector>
+
+#include "skv_internal.h"
+
+namespace skv {
+
+bool shape_supported(const skv_shape& s, bool need_tokens) {
+    if (s.abi_version != SKV_ABI_VERSION) return false;
+    if (s.channels == 0 || s.channels % kLanes != 0) return false;
+    if (s.mode == SKV_RESIDUAL) {
+        if (s.dtype != SKV_BF16 && s.dtype != SKV_E4M3) return false;
+        if (s.layers == 0 || s.kv == 0) return false;
+        return !need_tokens || (s.tokens > 0 && s.tokens % kSteps == 0);
+    }
+    if (s.mode == SKV_CHECKERBOARD) {
+        if (s.dtype != SKV_INT16 || s.layers != 1 || s.kv != 1) return false;
+        return !need_tokens || (s.tokens > 0 && s.tokens % (2 * kSteps) == 0);
+    }
+    return false;
+}
+
+uint64_t table_count(const skv_shape& s) {
+    return s.mode == SKV_RESIDUAL ? uint64_t(s.layers) * s.kv * s.channels : uint64_t(s.channels) * 16;
+}
+
+uint64_t stream_count(const skv_shape& s) {
+    uint64_t groups = s.channels / kLanes;
+    if (s.mode == SKV_RESIDUAL) return uint64_t(s.layers) * s.kv * (s.tokens / kSteps) * groups;
+    return 2 * uint64_t(s.tokens / (2 * kSteps)) * groups;
+}
+
+uint64_t element_count(const skv_shape& s) {
+    return uint64_t(s.layers) * s.kv * s.tokens * s.channels;
+}
+
+uint64_t fnv1a64(const uint8_t* p, size_t n) {
+    uint64_t h = 0xcbf29ce484222325ull;   // FNV-1a 64-bit offset basis
+    const uint64_t prime = 0x100000001b3ull;
+    for (size_t i = 0; i < n; ++i) h = (h ^ p[i]) * prime;
+    return h;
+}
+
+namespace {
+
+// Mass of [v - 1/2, v + 1/2] under a Laplace of location m and scale b.
+double laplace_cell(double v, double m, double b) {
+    const double lo = v - 0.5 - m;
+    const double hi = v + 0.5 - m;
+    if (lo >= 0.0) return 0.5 * (std::exp(-lo / b) - std::exp(-hi / b));
+    if (hi <= 0.0) return 0.5 * (std::exp(hi / b) - std::exp(lo / b));
+    return 1.0 - 0.5 * std::exp(-hi / b) - 0.5 * std::exp(lo / b);
+}
+
+// Signed value of zigzag code z (0, -1, 1, -2, ...).
+inline int32_t unzig(uint32_t z) { return (z & 1u) ? -int32_t((z + 1) >> 1) : int32_t(z >> 1); }
+
+// ordered-integer residual of two N-bit float patterns, as signed N-bit.
+inline int32_t ordered_residual(uint32_t t, uint32_t p, int nbits) {
+    const uint32_t span = 1u << nbits, half = span >> 1, mask = span - 1;
+    auto ordv = [&](uint32_t u) { return (u & half) ? (~u & mask) : (u | half); };
+    uint32_t d = (ordv(t) - ordv(p)) & mask;
+    return d >= half ? int32_t(d) - int32_t(span) : int32_t(d);
+}
+
+inline uint32_t zig_of(int32_t r, int nbits) {
+    const uint32_t mask = (1u << nbits) - 1u;
+    return (uint32_t(r) << 1 ^ uint32_t(r >> 31)) & mask;
+}
+
+// checkerboard mean in sixteenths (int32): G, plus 8 x (left + right) on odd rows
+inline int32_t cb_mean(const int16_t* coef, const int16_t* G, uint32_t T, uint32_t C, uint32_t t, uint32_t c) {
+    int32_t m = G[size_t(t) * C + c];
+    if (t % 2 == 1) {
+        const int32_t l = coef[size_t(t - 1) * C + c];
+        const int32_t r = (t + 1 < T) ? coef[size_t(t + 1) * C + c] : l;
+        m += 8 * (l + r);
+    }
+    return m;
+}
+
+struct Record {
+    uint32_t n;
+    uint32_t f[256];
+};
+
+// Largest-remainder rounding of q (sums to 4096) to frequencies >= 1.
+void round_freqs(const std::vector<double>& q, uint32_t* f) {
+    const size_t m = q.size();
+    std::vector<double> rem(m);
+    int64_t total = 0;
+    for (size_t i = 0; i < m; ++i) {
+        const double fl = std::floor(q[i]);
+        f[i] = fl < 1.0 ? 1u : uint32_t(fl);
+        rem[i] = q[i] - double(f[i]);
+        total += f[i];
+    }
+    int64_t left = int64_t(kM) - total;
+    if (left > 0) {
+        std::vector<uint32_t> order(m);
+        std::iota(order.begin(), order.end(), 0u);
+        std::stable_sort(order.begin(), order.end(), [&](uint32_t a, uint32_t b) { return rem[a] > rem[b]; });
+        for (int64_t i = 0; i < left; ++i) f[order[size_t(i)]] += 1;
+    }
+    for (; left < 0; ++left) {
+        size_t best = m;
+        for (size_t i = 0; i < m; ++i)
+            if (f[i] > 1 && (best == m || f[i] > f[best])) best = i;
+        f[best] -= 1;
+    }
+}
+
+// Table from cell masses over z = 0..254, escape probability pe.
+Record make_record(const double* mass, double pe) {
+    Record r{};
+    uint32_t n = 1;
+    for (uint32_t z = 0; z < 255; ++z)
+        if (mass[z] >= 1.0 / double(kM)) n = z + 1;
+    double sum = 0.0;
+    for (uint32_t z = 0; z < n; ++z) sum += mass[z];
+    const double scale = (1.0 - pe) / sum;
+    std::vector<double> q(n + 1);
+    for (uint32_t z = 0; z < n; ++z) q[z] = double(kM) * (mass[z] * scale);
+    q[n] = double(kM) * pe;
+    r.n = n;
+    round_freqs(q, r.f);
+    return r;
+}
+
+void put_record(uint8_t* dst, const Record& r) {
+    std::memset(dst, 0, kTableRecord);
+    wr16(dst, r.n);
+    for (uint32_t s = 0; s <= r.n; ++s) wr16(dst + 2 + 2 * s, r.f[s]);
+}
+
+void masses_for(double m, double b, double* out) {
+    for (uint32_t z = 0; z < 255; ++z) out[z] = laplace_cell(double(unzig(z)), m, b);
+}
+
+}  // namespace
+
+int fit_tables_host(const skv_shape& s, const void* calib_t, const void* calib_a, uint32_t calib_tokens,
+                    uint8_t* blob, size_t blob_bytes) {
+    const uint64_t nt = table_count(s);
+    if (blob_bytes != kHeaderBytes + nt * kTableRecord) return SKV_ERR_ARG;
+    std::memset(blob, 0, kHeaderBytes);
+    std::memcpy(blob, "SKVT", 4);
+    wr16(blob + 4, 1);
+    blob[6] = uint8_t(s.dtype);
+    blob[7] = uint8_t(s.mode);
+    wr32(blob + 8, uint32_t(nt));
+    wr32(blob + 12, s.layers);
+    wr32(blob + 16, s.kv);
+    wr32(blob + 20, s.channels);
+    wr32(blob + 24, calib_tokens);
+    wr64(blob + 32, blob_bytes);
+    uint8_t* rec = blob + kHeaderBytes;
+    const uint32_t C = s.channels, N = calib_tokens;
+    double mass[255];
+
+    if (s.mode == SKV_RESIDUAL) {
+        const int nbits = s.dtype == SKV_E4M3 ? 8 : 16;
+        const uint64_t slabs = uint64_t(s.layers) * s.kv;
+        auto elem = [&](const void* a, size_t i) -> uint32_t {
+            return nbits == 8 ? static_cast<const uint8_t*>(a)[i] : static_cast<const uint16_t*>(a)[i];
+        };
+        std::vector<int32_t> r(N);
+        for (uint64_t sl = 0; sl < slabs; ++sl) {
+            for (uint32_t c = 0; c < C; ++c) {
+                double acc = 0.0;
+                uint64_t used = 0;
+                for (uint32_t t = 0; t < N; ++t) {
+                    const size_t i = (size_t(sl) * N + t) * C + c;
+                    r[t] = ordered_residual(elem(calib_t, i), elem(calib_a, i), nbits);
+                    const int32_t a = std::abs(r[t]);
+                    if (a <= 127) {
+                        acc += double(a);
+                        ++used;
+                    }
+                }
+                double b = used ? acc / double(used) : 0.0;
+                b = std::max(b, 0.05);
+                masses_for(0.0, b, mass);
+                Record R = make_record(mass, 0.0);   // direct range only depends on the masses
+                uint64_t esc = 0;
+                for (uint32_t t = 0; t < N; ++t) esc += zig_of(r[t], nbits) >= R.n;
+                const double pe = (double(esc) + 1.0) / (double(N) + 2.0);
+                put_record(rec + (sl * C + c) * kTableRecord, make_record(mass, pe));
+            }
+        }
+        return SKV_OK;
+    }
+
+    const int16_t* coef = static_cast<const int16_t*>(calib_t);
+    const int16_t* G = static_cast<const int16_t*>(calib_a);
+    std::vector<int32_t> mu(N);
+    for (uint32_t c = 0; c < C; ++c) {
+        double acc = 0.0;
+        uint64_t used = 0;
+        for (uint32_t t = 0; t < N; ++t) {
+            mu[t] = cb_mean(coef, G, N, C, t, c);
+            const double e = std::fabs(double(coef[size_t(t) * C + c]) - double(mu[t]) / 16.0);
+            if (e <= 127.0) {
+                acc += e;
+                ++used;
+            }
+        }
+        double b = used ? acc / double(used) : 0.0;
+        b = std::max(b, 0.05);
+        double shifted[16][255];
+        uint32_t ndir[16];
+        for (int f = 0; f < 16; ++f) {
+            masses_for(double(f) / 16.0, b, shifted[f]);
+            ndir[f] = make_record(shifted[f], 0.0).n;
+        }
+        uint64_t esc = 0;
+        for (uint32_t t = 0; t < N; ++t) {
+            const int32_t k = mu[t] >> 4;   // arithmetic shift: floor
+            const int32_t f = mu[t] & 15;
+            const int32_t d = int32_t(int16_t(uint16_t(uint32_t(coef[size_t(t) * C + c] - k))));
+            esc += zig_of(d, 16) >= ndir[f];
+        }
+        const double pe = (double(esc) + 1.0) / (double(N) + 2.0);
+        for (int f = 0; f < 16; ++f) put_record(rec + (size_t(c) * 16 + f) * kTableRecord, make_record(shifted[f], pe));
+    }
+    return SKV_OK;
+}
+
+int validate_blob(const uint8_t* b, size_t bytes) {
+    if (bytes < kHeaderBytes || std::memcmp(b, "SKVT", 4) != 0 || rd16(b + 4) != 1) return SKV_ERR_TABLES;
+    skv_shape s{SKV_ABI_VERSION, b[6], b[7], rd32(b + 12), rd32(b + 16), 0, rd32(b + 20)};
+    if (!shape_supported(s, false)) return SKV_ERR_TABLES;
+    const uint64_t nt = table_count(s);
+    if (rd32(b + 8) != nt || rd64(b + 32) != bytes || bytes != kHeaderBytes + nt * kTableRecord) return SKV_ERR_TABLES;
+    for (uint64_t j = 0; j < nt; ++j) {
+        const uint8_t* r = b + kHeaderBytes + j * kTableRecord;
+        const uint32_t n = rd16(r);
+        if (n < 1 || n > uint32_t(kMaxDirect)) return SKV_ERR_TABLES;
+        uint32_t sum = 0;
+        for (uint32_t q = 0; q < 256; ++q) {
+            const uint32_t f = rd16(r + 2 + 2 * q);
+            if (q <= n ? f == 0 : f != 0) return SKV_ERR_TABLES;
+            sum += f;
+        }
+        if (sum != kM) return SKV_ERR_TABLES;
+    }
+    return SKV_OK;
+}
+
+}  // namespace skv

@@ -1,0 +1,91 @@
+// skv_internal.h -- private declarations shared by the libskv sources.
+//
+// Format constants: rANS with 12-bit probabilities (M = 4096), 32-bit state
+// normalized to [2^16, 2^32), 16-bit words; a stream is 32 interleaved lanes
+// x 128 steps; direct alphabets hold at most 255 symbols plus an escape.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+#include <hip/hip_runtime.h>
+
+#include "../../include/skv.h"
+
+namespace skv {
+
+constexpr uint32_t kProbBits = 12;
+constexpr uint32_t kM = 1u << kProbBits;
+constexpr uint32_t kStateLow = 1u << 16;
+constexpr int kLanes = 32;
+constexpr int kSteps = 128;
+constexpr int kSyms = kLanes * kSteps;
+constexpr int kMaxDirect = 255;
+constexpr size_t kHeaderBytes = 64;
+constexpr size_t kTableRecord = 514;  // u16 n + u16 freq[256]
+constexpr size_t kStateBytes = 4 * kLanes;
+constexpr uint64_t kRawBit = 1ull << 63;
+
+inline uint32_t elem_bytes(uint32_t dtype) { return dtype == SKV_E4M3 ? 1u : 2u; }
+
+// Shape checks shared by fit / encode / decode.
+bool shape_supported(const skv_shape& s, bool need_tokens);
+uint64_t table_count(const skv_shape& s);
+uint64_t stream_count(const skv_shape& s);
+uint64_t element_count(const skv_shape& s);
+
+// Host table fit (fp64).  Writes a complete blob (header + records).
+int fit_tables_host(const skv_shape& s, const void* calib_t, const void* calib_a, uint32_t calib_tokens,
+                    uint8_t* blob, size_t blob_bytes);
+int validate_blob(const uint8_t* blob, size_t bytes);
+uint64_t fnv1a64(const uint8_t* p, size_t n);
+
+inline void wr16(uint8_t* p, uint32_t v) { p[0] = uint8_t(v); p[1] = uint8_t(v >> 8); }
+inline void wr32(uint8_t* p, uint32_t v) { for (int i = 0; i < 4; ++i) p[i] = uint8_t(v >> (8 * i)); }
+inline void wr64(uint8_t* p, uint64_t v) { for (int i = 0; i < 8; ++i) p[i] = uint8_t(v >> (8 * i)); }
+inline uint32_t rd16(const uint8_t* p) { return uint32_t(p[0]) | (uint32_t(p[1]) << 8); }
+inline uint32_t rd32(const uint8_t* p) { return rd16(p) | (rd16(p + 2) << 16); }
+inline uint64_t rd64(const uint8_t* p) { return uint64_t(rd32(p)) | (uint64_t(rd32(p + 4)) << 32); }
+
+// ------------------------------------------------------------------ device
+// Expanded tables resident in HBM (built once per blob and device).
+struct DevTables {
+    uint32_t n_tables = 0;
+    uint32_t* n = nullptr;         // [n_tables] direct-symbol count (ESC index)
+    uint2* enc = nullptr;          // [n_tables][256] {divisor magic, freq | cum<<13 | shift<<25}
+    uint32_t* fc = nullptr;        // [n_tables][256] freq | cum<<16
+    uint8_t* slot = nullptr;       // [n_tables][4096] slot -> symbol
+};
+
+struct EncodeLaunch {
+    const void* target;
+    const void* aux;
+    uint8_t* scratch;       // [n_streams][raw_bytes]: states at the front, words packed at the back
+    uint32_t* meta;         // [n_streams] bytes | raw<<31
+    uint32_t* block_sum;    // [n_blocks]
+    uint64_t* block_off;    // [n_blocks]
+    uint64_t* total;        // payload bytes
+    uint8_t* out;           // container
+    uint64_t out_capacity;
+    uint64_t blob_hash;
+    skv_shape shape;
+    uint64_t n_streams;
+};
+
+struct DecodeLaunch {
+    const uint8_t* in;
+    uint64_t payload_bytes;
+    const void* aux;
+    void* out;
+    uint32_t* status;
+    skv_shape shape;
+    uint64_t n_streams;
+};
+
+hipError_t build_dev_tables(const uint8_t* blob, DevTables* t, hipStream_t stream);
+void free_dev_tables(DevTables* t);
+hipError_t launch_encode(const EncodeLaunch& a, const DevTables& t, hipStream_t stream);
+hipError_t launch_decode(const DecodeLaunch& a, const DevTables& t, hipStream_t stream);
+hipError_t launch_clear_u32(uint32_t* p, uint32_t n, hipStream_t stream);
+uint64_t encode_work_bytes(uint64_t n_streams, uint32_t raw_bytes);
+
+}  // namespace skv

@@ -1,0 +1,518 @@
+// skv_kernels.hip -- gfx950 kernels of the coding path.
+//
+//   expand_tables   blob records -> per-table encode entries (frequency,
+//                   start, divisor magic), decode slot->symbol maps and
+//                   (frequency, start) words, resident in HBM
+//   encode_streams  symbolize + 32-lane interleaved rANS encode, one
+//                   stream per half wavefront; words placed by ballot
+//   stream_block_sums / stream_block_scan / place_streams
+//                   stream sizes -> exclusive scan -> u64 index and the
+//                   compacted container
+//   decode_streams  rANS decode + reconstruction, one stream per half
+//                   wavefront; checkerboard mode runs it twice
+//
+// The residual of the target against the predictor is what is coded
+// ("Speculative KV coding ..." page, section "Core idea"); the coder is rANS
+// against per-channel Laplace tables (DCKV page, section "How it differs"),
+// and checkerboard mode shifts the table by a mean from the side input and,
+// on odd tokens, from the two decoded even neighbours (same section).
+// Everything on the device is integer arithmetic.
+#include "skv_internal.h"
+
+namespace skv {
+namespace {
+
+constexpr uint32_t kStreamsPerBlock = 8;    // 256 threads = 4 wavefronts x 2 streams
+constexpr uint32_t kScanBlock = 1024;
+
+struct Geo {
+    uint32_t C, T, ncg, ntb;
+};
+
+__device__ __forceinline__ Geo geometry(const skv_shape& s) {
+    Geo g;
+    g.C = s.channels;
+    g.T = s.tokens;
+    g.ncg = s.channels / kLanes;
+    g.ntb = (s.mode == SKV_RESIDUAL ? s.tokens : s.tokens / 2) / kSteps;
+    return g;
+}
+
+// --------------------------------------------------------------- symbol maps
+// Order-preserving integer of a 16-bit / 8-bit sign-magnitude pattern.
+__device__ __forceinline__ uint32_t ord16(uint32_t u) {
+    const uint32_t neg = 0u - (u >> 15);                 // all ones when the sign is set
+    return (u ^ (0x8000u | (neg & 0x7FFFu))) & 0xFFFFu;
+}
+__device__ __forceinline__ uint32_t unord16(uint32_t o) {
+    const uint32_t pos = 0u - (o >> 15);                 // all ones when o came from a non-negative value
+    return (o ^ (0xFFFFu ^ (pos & 0x7FFFu))) & 0xFFFFu;
+}
+__device__ __forceinline__ uint32_t ord8(uint32_t u) {
+    const uint32_t neg = 0u - (u >> 7);
+    return (u ^ (0x80u | (neg & 0x7Fu))) & 0xFFu;
+}
+__device__ __forceinline__ uint32_t unord8(uint32_t o) {
+    const uint32_t pos = 0u - (o >> 7);
+    return (o ^ (0xFFu ^ (pos & 0x7Fu))) & 0xFFu;
+}
+// zigzag of an N-bit two's-complement value held in the low N bits
+__device__ __forceinline__ uint32_t zig16(uint32_t r) { return ((r << 1) ^ (0u - ((r >> 15) & 1u))) & 0xFFFFu; }
+__device__ __forceinline__ uint32_t zig8(uint32_t r) { return ((r << 1) ^ (0u - ((r >> 7) & 1u))) & 0xFFu; }
+__device__ __forceinline__ uint32_t unzig(uint32_t z) { return (z >> 1) ^ (0u - (z & 1u)); }   // mod 2^32
+
+// --------------------------------------------------------------- tables
+__global__ __launch_bounds__(256) void expand_tables(const uint8_t* rec, uint32_t* tn, uint2* enc, uint32_t* fc,
+                                                     uint8_t* slot) {
+    __shared__ uint32_t cum[257];
+    const uint32_t j = blockIdx.x, tid = threadIdx.x;
+    const uint8_t* r = rec + size_t(j) * kTableRecord;
+    const uint32_t n = uint32_t(r[0]) | (uint32_t(r[1]) << 8);
+    const uint32_t f = tid <= n ? (uint32_t(r[2 + 2 * tid]) | (uint32_t(r[3 + 2 * tid]) << 8)) : 0u;
+    cum[tid + 1] = f;
+    if (tid == 0) cum[0] = 0;
+    __syncthreads();
+    for (uint32_t d = 1; d < 256; d <<= 1) {
+        const uint32_t v = (tid + 1 >= d) ? cum[tid + 1 - d] : 0u;
+        __syncthreads();
+        cum[tid + 1] += v;
+        __syncthreads();
+    }
+    const uint32_t c = cum[tid];
+    if (tid == 0) tn[j] = n;
+    uint2 e = make_uint2(0u, 0u);
+    if (tid <= n) {
+        uint32_t sh = 0;
+        while ((1u << sh) < f) ++sh;                                    // ceil(log2 f)
+        const uint64_t m = ((1ull << (32 + sh)) + f - 1) / f;           // ceil(2^(32+sh) / f), in (2^32, 2^33]
+        e.x = uint32_t(m - (1ull << 32));
+        e.y = f | (c << 13) | (sh << 25);
+    }
+    enc[size_t(j) * 256 + tid] = e;
+    fc[size_t(j) * 256 + tid] = f | (c << 16);
+    uint8_t* st = slot + size_t(j) * kM;
+    for (uint32_t q = c; q < c + f; ++q) st[q] = uint8_t(tid);
+}
+
+// --------------------------------------------------------------- encode
+// One rANS put shared by every lane of a wavefront.  Lanes whose state is too
+// large for their symbol first emit their low 16 bits; inside a stream the
+// words are ranked from lane 31 down to lane 0 (reverse of the decoder's
+// refill order) and written backwards from the end of the stream's scratch.
+__device__ __forceinline__ void emit_words(uint32_t& x, uint32_t& cnt, bool emit, uint32_t lane, uint32_t half,
+                                           uint16_t* wend, uint32_t maxw) {
+    const uint64_t b = __ballot(emit);
+    const uint32_t mine = uint32_t(b >> half);
+    if (emit) {
+        const uint32_t above = __popc(uint32_t((uint64_t)mine >> (lane + 1)));
+        const uint32_t pos = cnt + above;
+        if (pos < maxw) *(wend - pos) = uint16_t(x & 0xFFFFu);
+        x >>= 16;
+    }
+    cnt += __popc(mine);
+}
+
+template <uint32_t DT, uint32_t MODE>
+__global__ __launch_bounds__(256) void encode_streams(EncodeLaunch a, DevTables t) {
+    const uint32_t tid = threadIdx.x;
+    const uint64_t sid = uint64_t(blockIdx.x) * kStreamsPerBlock + (tid >> 5);
+    if (sid >= a.n_streams) return;
+    const uint32_t lane = tid & 31u, half = tid & 32u;
+    const Geo g = geometry(a.shape);
+    const uint32_t cg = uint32_t(sid % g.ncg);
+    const uint32_t tb = uint32_t((sid / g.ncg) % g.ntb);
+    const uint32_t slab = uint32_t(sid / (uint64_t(g.ncg) * g.ntb));
+    const uint32_t ch = cg * kLanes + lane;
+    constexpr uint32_t EB = DT == SKV_E4M3 ? 1u : 2u;
+    constexpr uint32_t NCHUNK = DT == SKV_E4M3 ? 1u : 2u;
+    constexpr uint32_t RAW = kSyms * EB;
+    constexpr uint32_t MAXW = (RAW - kStateBytes) / 2;
+    uint8_t* area = a.scratch + sid * RAW;
+    uint16_t* wend = reinterpret_cast<uint16_t*>(area) + RAW / 2 - 1;
+    const uint32_t res_table = slab * g.C + ch;
+
+    uint32_t x = kStateLow, cnt = 0;
+    for (int k = kSteps - 1; k >= 0; --k) {
+        uint32_t z, table;
+        if (MODE == SKV_RESIDUAL) {
+            const size_t idx = (size_t(slab) * g.T + size_t(tb) * kSteps + k) * g.C + ch;
+            if (DT == SKV_E4M3) {
+                const uint32_t tv = static_cast<const uint8_t*>(a.target)[idx];
+                const uint32_t pv = static_cast<const uint8_t*>(a.aux)[idx];
+                z = zig8((ord8(tv) - ord8(pv)) & 0xFFu);
+            } else {
+                const uint32_t tv = static_cast<const uint16_t*>(a.target)[idx];
+                const uint32_t pv = static_cast<const uint16_t*>(a.aux)[idx];
+                z = zig16((ord16(tv) - ord16(pv)) & 0xFFFFu);
+            }
+            table = res_table;
+        } else {
+            const uint32_t tok = 2u * (tb * kSteps + uint32_t(k)) + slab;
+            const int16_t* coef = static_cast<const int16_t*>(a.target);
+            const int16_t* G = static_cast<const int16_t*>(a.aux);
+            int32_t mu = G[size_t(tok) * g.C + ch];
+            if (slab == 1) {
+                const int32_t l = coef[size_t(tok - 1) * g.C + ch];
+                const int32_t r = (tok + 1 < g.T) ? int32_t(coef[size_t(tok + 1) * g.C + ch]) : l;
+                mu += 8 * (l + r);
+            }
+            const int32_t kk = mu >> 4;
+            table = ch * 16u + uint32_t(mu & 15);
+            z = zig16(uint32_t(int32_t(coef[size_t(tok) * g.C + ch]) - kk) & 0xFFFFu);
+        }
+        const uint32_t n = t.n[table];
+        const bool esc = z >= n;
+        const uint32_t s = esc ? n : z;
+        if (__any(esc)) {
+            for (int q = int(NCHUNK) - 1; q >= 0; --q) {
+                emit_words(x, cnt, esc && x >= (16u << 20), lane, half, wend, MAXW);
+                if (esc) {
+                    const uint32_t chunk = (z >> (8 * q)) & 0xFFu;
+                    x = ((x >> 4) << 12) + (x & 15u) + 16u * chunk;
+                }
+            }
+        }
+        const uint2 e = t.enc[size_t(table) * 256 + s];
+        const uint32_t f = e.y & 0x1FFFu, c = (e.y >> 13) & 0xFFFu, sh = e.y >> 25;
+        emit_words(x, cnt, x >= (f << 20), lane, half, wend, MAXW);
+        const uint32_t qt = uint32_t((uint64_t(x) + __umulhi(x, e.x)) >> sh);   // floor(x / f)
+        x = x + qt * (kM - f) + c;
+    }
+    reinterpret_cast<uint32_t*>(area)[lane] = x;
+    if (lane == 0) {
+        const uint32_t bytes = kStateBytes + 2 * cnt + 2 * (cnt & 1u);
+        a.meta[sid] = bytes >= RAW ? 0x80000000u : cnt;
+    }
+}
+
+// --------------------------------------------------------------- index + compaction
+// meta word of a stream: bit 31 = stored raw, else the number of rANS words.
+__device__ __forceinline__ uint32_t meta_bytes(uint32_t m, uint32_t raw) {
+    return (m >> 31) ? raw : kStateBytes + 2 * m + 2 * (m & 1u);
+}
+
+__global__ __launch_bounds__(kScanBlock) void stream_block_sums(const uint32_t* meta, uint64_t n, uint32_t raw,
+                                                               uint32_t* bsum) {
+    __shared__ uint32_t part[kScanBlock / 64];
+    const uint64_t i = uint64_t(blockIdx.x) * kScanBlock + threadIdx.x;
+    uint32_t v = i < n ? meta_bytes(meta[i], raw) : 0u;
+    for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d, 64);
+    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = v;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint32_t s = 0;
+        for (uint32_t w = 0; w < kScanBlock / 64; ++w) s += part[w];
+        bsum[blockIdx.x] = s;
+    }
+}
+
+// Exclusive scan of the block sums by one workgroup, chunk by chunk.
+__global__ __launch_bounds__(kScanBlock) void stream_block_scan(const uint32_t* bsum, uint32_t nb, uint64_t* boff,
+                                                               uint64_t* total) {
+    __shared__ uint64_t wsum[kScanBlock / 64];
+    __shared__ uint64_t carry;
+    if (threadIdx.x == 0) carry = 0;
+    __syncthreads();
+    const uint32_t lane = threadIdx.x & 63u, w = threadIdx.x >> 6;
+    for (uint32_t base = 0; base < nb; base += kScanBlock) {
+        const uint32_t i = base + threadIdx.x;
+        const uint64_t v = i < nb ? uint64_t(bsum[i]) : 0ull;
+        uint64_t incl = v;
+        for (uint32_t d = 1; d < 64; d <<= 1) {
+            const uint64_t o = __shfl_up(incl, d, 64);
+            if (lane >= d) incl += o;
+        }
+        if (lane == 63) wsum[w] = incl;
+        __syncthreads();
+        uint64_t before = carry;
+        for (uint32_t q = 0; q < w; ++q) before += wsum[q];
+        if (i < nb) boff[i] = before + incl - v;
+        __syncthreads();
+        if (threadIdx.x == kScanBlock - 1) carry = before + incl;
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) *total = carry;
+}
+
+template <uint32_t DT, uint32_t MODE>
+__global__ __launch_bounds__(kScanBlock) void place_streams(EncodeLaunch a, const uint64_t* boff) {
+    __shared__ uint64_t offs[kScanBlock];
+    __shared__ uint32_t wsum[kScanBlock / 64];
+    constexpr uint32_t EB = DT == SKV_E4M3 ? 1u : 2u;
+    constexpr uint32_t RAW = kSyms * EB;
+    const uint64_t n = a.n_streams;
+    const uint64_t head = kHeaderBytes + 8 * (n + 1);
+    const uint64_t total = *a.total;
+    if (head + total > a.out_capacity) return;        // caller reports SKV_ERR_CAPACITY
+    const uint32_t lane = threadIdx.x & 63u, w = threadIdx.x >> 6;
+    const uint64_t first = uint64_t(blockIdx.x) * kScanBlock;
+    const uint64_t i = first + threadIdx.x;
+    const uint32_t m = i < n ? a.meta[i] : 0u;
+    const uint32_t v = i < n ? meta_bytes(m, RAW) : 0u;
+    uint32_t incl = v;
+    for (uint32_t d = 1; d < 64; d <<= 1) {
+        const uint32_t o = __shfl_up(incl, d, 64);
+        if (lane >= d) incl += o;
+    }
+    if (lane == 63) wsum[w] = incl;
+    __syncthreads();
+    uint64_t off = boff[blockIdx.x];
+    for (uint32_t q = 0; q < w; ++q) off += wsum[q];
+    off += incl - v;
+    offs[threadIdx.x] = off;
+    uint64_t* index = reinterpret_cast<uint64_t*>(a.out + kHeaderBytes);
+    if (i < n) index[i] = off | (uint64_t(m >> 31) << 63);
+    if (i == n - 1) index[n] = total;
+    if (i == 0) {
+        uint8_t* h = a.out;
+        const uint32_t words[16] = {
+            0x31564B53u,                                                    // "SKV1"
+            1u | (a.shape.dtype << 16) | (a.shape.mode << 24),
+            kProbBits | (uint32_t(kLanes) << 8) | (uint32_t(kSteps) << 16),
+            a.shape.layers, a.shape.kv, a.shape.tokens, a.shape.channels, 0u,
+            uint32_t(n), uint32_t(n >> 32),
+            uint32_t(a.blob_hash), uint32_t(a.blob_hash >> 32),
+            uint32_t(total), uint32_t(total >> 32), 0u, 0u};
+        for (int q = 0; q < 16; ++q) reinterpret_cast<uint32_t*>(h)[q] = words[q];
+    }
+    __syncthreads();
+    // copy: each wavefront moves 64 streams, one at a time
+    const Geo g = geometry(a.shape);
+    uint8_t* pay = a.out + head;
+    for (uint32_t j = 0; j < 64; ++j) {
+        const uint32_t li = w * 64 + j;
+        const uint64_t sid = first + li;
+        if (sid >= n) break;
+        const uint32_t ms = a.meta[sid];
+        uint8_t* dst = pay + offs[li];
+        const uint8_t* src = a.scratch + sid * RAW;
+        if (ms >> 31) {
+            const uint32_t cg = uint32_t(sid % g.ncg);
+            const uint32_t tb = uint32_t((sid / g.ncg) % g.ntb);
+            const uint32_t slab = uint32_t(sid / (uint64_t(g.ncg) * g.ntb));
+            for (uint32_t e = lane; e < uint32_t(kSyms); e += 64) {
+                const uint32_t k = e >> 5, ln = e & 31u;
+                const uint32_t tok = MODE == SKV_RESIDUAL ? tb * kSteps + k : 2u * (tb * kSteps + k) + slab;
+                const size_t idx = MODE == SKV_RESIDUAL ? (size_t(slab) * g.T + tok) * g.C + cg * kLanes + ln
+                                                        : size_t(tok) * g.C + cg * kLanes + ln;
+                if (EB == 1) dst[e] = static_cast<const uint8_t*>(a.target)[idx];
+                else reinterpret_cast<uint16_t*>(dst)[e] = static_cast<const uint16_t*>(a.target)[idx];
+            }
+        } else {
+            // states from the front of the scratch area, words from its back
+            if (lane < 32) reinterpret_cast<uint32_t*>(dst)[lane] = reinterpret_cast<const uint32_t*>(src)[lane];
+            const uint32_t cnt = ms;
+            const uint16_t* ws = reinterpret_cast<const uint16_t*>(src) + RAW / 2 - cnt;
+            uint16_t* wd = reinterpret_cast<uint16_t*>(dst + kStateBytes);
+            const uint32_t slots = cnt + (cnt & 1u);
+            for (uint32_t q = lane; q < slots; q += 64) wd[q] = q < cnt ? ws[q] : uint16_t(0);
+        }
+    }
+}
+
+// --------------------------------------------------------------- decode
+__device__ __forceinline__ void refill(uint32_t& x, uint32_t& p, bool need, uint32_t lane, uint32_t half,
+                                       const uint16_t* W, uint32_t navail, bool& bad) {
+    const uint64_t b = __ballot(need);
+    const uint32_t mine = uint32_t(b >> half);
+    if (need) {
+        const uint32_t pos = p + __popc(mine & ((1u << lane) - 1u));
+        uint32_t w = 0;
+        if (pos < navail) w = W[pos];
+        else bad = true;
+        x = (x << 16) | w;
+    }
+    p += __popc(mine);
+}
+
+template <uint32_t DT, uint32_t MODE>
+__global__ __launch_bounds__(256) void decode_streams(DecodeLaunch a, DevTables t, uint64_t first, uint64_t count) {
+    const uint32_t tid = threadIdx.x;
+    const uint64_t local = uint64_t(blockIdx.x) * kStreamsPerBlock + (tid >> 5);
+    if (local >= count) return;
+    const uint64_t sid = first + local;
+    const uint32_t lane = tid & 31u, half = tid & 32u;
+    const Geo g = geometry(a.shape);
+    const uint32_t cg = uint32_t(sid % g.ncg);
+    const uint32_t tb = uint32_t((sid / g.ncg) % g.ntb);
+    const uint32_t slab = uint32_t(sid / (uint64_t(g.ncg) * g.ntb));
+    const uint32_t ch = cg * kLanes + lane;
+    constexpr uint32_t EB = DT == SKV_E4M3 ? 1u : 2u;
+    constexpr uint32_t NCHUNK = DT == SKV_E4M3 ? 1u : 2u;
+    constexpr uint32_t RAW = kSyms * EB;
+    const uint64_t* index = reinterpret_cast<const uint64_t*>(a.in + kHeaderBytes);
+    const uint8_t* pay = a.in + kHeaderBytes + 8 * (a.n_streams + 1);
+    const uint64_t e0 = index[sid], e1 = index[sid + 1];
+    const uint64_t off = e0 & ~kRawBit, end = e1 & ~kRawBit;
+    bool bad = false;
+    if (end < off || end > a.payload_bytes) {
+        if (lane == 0) atomicOr(a.status, 1u);
+        return;
+    }
+    const uint64_t size = end - off;
+    auto out_index = [&](uint32_t k) -> size_t {
+        if (MODE == SKV_RESIDUAL) return (size_t(slab) * g.T + size_t(tb) * kSteps + k) * g.C + ch;
+        return size_t(2u * (tb * kSteps + k) + slab) * g.C + ch;
+    };
+    if (e0 & kRawBit) {
+        if (size != RAW) {
+            if (lane == 0) atomicOr(a.status, 1u);
+            return;
+        }
+        for (uint32_t k = 0; k < uint32_t(kSteps); ++k) {
+            if (EB == 1) static_cast<uint8_t*>(a.out)[out_index(k)] = pay[off + k * kLanes + lane];
+            else static_cast<uint16_t*>(a.out)[out_index(k)] =
+                reinterpret_cast<const uint16_t*>(pay + off)[k * kLanes + lane];
+        }
+        return;
+    }
+    if (size < kStateBytes || (size - kStateBytes) % 4 != 0) {
+        if (lane == 0) atomicOr(a.status, 1u);
+        return;
+    }
+    uint32_t x = reinterpret_cast<const uint32_t*>(pay + off)[lane];
+    if (x < kStateLow) bad = true;
+    const uint16_t* W = reinterpret_cast<const uint16_t*>(pay + off + kStateBytes);
+    const uint32_t navail = uint32_t((size - kStateBytes) / 2);
+    uint32_t p = 0;
+    const uint32_t res_table = slab * g.C + ch;
+    for (uint32_t k = 0; k < uint32_t(kSteps); ++k) {
+        const size_t oi = out_index(k);
+        uint32_t table;
+        int32_t kk = 0;
+        if (MODE == SKV_RESIDUAL) {
+            table = res_table;
+        } else {
+            const uint32_t tok = 2u * (tb * kSteps + k) + slab;
+            const int16_t* dec = static_cast<const int16_t*>(a.out);
+            int32_t mu = static_cast<const int16_t*>(a.aux)[oi];
+            if (slab == 1) {
+                const int32_t l = dec[size_t(tok - 1) * g.C + ch];
+                const int32_t r = (tok + 1 < g.T) ? int32_t(dec[size_t(tok + 1) * g.C + ch]) : l;
+                mu += 8 * (l + r);
+            }
+            kk = mu >> 4;
+            table = ch * 16u + uint32_t(mu & 15);
+        }
+        const uint32_t n = t.n[table];
+        const uint32_t slot = x & (kM - 1u);
+        const uint32_t s = t.slot[size_t(table) * kM + slot];
+        const uint32_t fcv = t.fc[size_t(table) * 256 + s];
+        x = (fcv & 0xFFFFu) * (x >> kProbBits) + slot - (fcv >> 16);
+        refill(x, p, x < kStateLow, lane, half, W, navail, bad);
+        const bool esc = s == n;
+        uint32_t z = s;
+        if (__any(esc)) {
+            uint32_t val = 0;
+            for (uint32_t q = 0; q < NCHUNK; ++q) {
+                if (esc) {
+                    const uint32_t sl = x & (kM - 1u);
+                    val |= (sl >> 4) << (8 * q);
+                    x = ((x >> kProbBits) << 4) + (sl & 15u);
+                }
+                refill(x, p, esc && x < kStateLow, lane, half, W, navail, bad);
+            }
+            if (esc) {
+                if (val < n) bad = true;
+                z = val;
+            }
+        }
+        if (MODE == SKV_RESIDUAL) {
+            if (DT == SKV_E4M3) {
+                const uint32_t pv = static_cast<const uint8_t*>(a.aux)[oi];
+                static_cast<uint8_t*>(a.out)[oi] = uint8_t(unord8((ord8(pv) + unzig(z)) & 0xFFu));
+            } else {
+                const uint32_t pv = static_cast<const uint16_t*>(a.aux)[oi];
+                static_cast<uint16_t*>(a.out)[oi] = uint16_t(unord16((ord16(pv) + unzig(z)) & 0xFFFFu));
+            }
+        } else {
+            static_cast<int16_t*>(a.out)[oi] = int16_t(uint16_t(uint32_t(kk) + unzig(z)));
+        }
+    }
+    if (x != kStateLow) bad = true;
+    if (!(p == navail || (p + 1 == navail && W[p] == 0))) bad = true;
+    if (bad) atomicOr(a.status, 1u);
+}
+
+__global__ void clear_u32(uint32_t* p, uint32_t n) {
+    const uint32_t i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) p[i] = 0u;
+}
+
+template <uint32_t DT, uint32_t MODE>
+hipError_t encode_all(const EncodeLaunch& a, const DevTables& t, hipStream_t st) {
+    const uint64_t n = a.n_streams;
+    const uint32_t nb = uint32_t((n + kScanBlock - 1) / kScanBlock);
+    const uint32_t eg = uint32_t((n + kStreamsPerBlock - 1) / kStreamsPerBlock);
+    hipLaunchKernelGGL((encode_streams<DT, MODE>), dim3(eg), dim3(256), 0, st, a, t);
+    hipLaunchKernelGGL(stream_block_sums, dim3(nb), dim3(kScanBlock), 0, st, a.meta, n, kSyms * (DT == SKV_E4M3 ? 1u : 2u),
+                       a.block_sum);
+    hipLaunchKernelGGL(stream_block_scan, dim3(1), dim3(kScanBlock), 0, st, a.block_sum, nb, a.block_off, a.total);
+    hipLaunchKernelGGL((place_streams<DT, MODE>), dim3(nb), dim3(kScanBlock), 0, st, a, a.block_off);
+    return hipGetLastError();
+}
+
+template <uint32_t DT, uint32_t MODE>
+hipError_t decode_all(const DecodeLaunch& a, const DevTables& t, hipStream_t st) {
+    const uint64_t passes = MODE == SKV_RESIDUAL ? 1 : 2;
+    const uint64_t per = a.n_streams / passes;
+    const uint32_t grid = uint32_t((per + kStreamsPerBlock - 1) / kStreamsPerBlock);
+    for (uint64_t ps = 0; ps < passes; ++ps)
+        hipLaunchKernelGGL((decode_streams<DT, MODE>), dim3(grid), dim3(256), 0, st, a, t, ps * per, per);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+uint64_t encode_work_bytes(uint64_t n_streams, uint32_t raw_bytes) {
+    auto al = [](uint64_t v) { return (v + 255) & ~uint64_t(255); };
+    const uint64_t nb = (n_streams + kScanBlock - 1) / kScanBlock;
+    return al(n_streams * raw_bytes) + al(4 * n_streams) + al(4 * nb) + al(8 * nb) + 256;
+}
+
+hipError_t build_dev_tables(const uint8_t* blob, DevTables* t, hipStream_t st) {
+    const uint32_t nt = rd32(blob + 8);
+    uint8_t* rec = nullptr;
+    hipError_t e = hipMalloc(&rec, size_t(nt) * kTableRecord);
+    if (e == hipSuccess) e = hipMalloc(&t->n, size_t(nt) * 4);
+    if (e == hipSuccess) e = hipMalloc(&t->enc, size_t(nt) * 256 * sizeof(uint2));
+    if (e == hipSuccess) e = hipMalloc(&t->fc, size_t(nt) * 256 * 4);
+    if (e == hipSuccess) e = hipMalloc(&t->slot, size_t(nt) * kM);
+    if (e == hipSuccess) e = hipMemcpyAsync(rec, blob + kHeaderBytes, size_t(nt) * kTableRecord, hipMemcpyHostToDevice, st);
+    if (e == hipSuccess) {
+        hipLaunchKernelGGL(expand_tables, dim3(nt), dim3(256), 0, st, rec, t->n, t->enc, t->fc, t->slot);
+        e = hipGetLastError();
+    }
+    if (e == hipSuccess) e = hipStreamSynchronize(st);
+    if (rec) (void)hipFree(rec);
+    t->n_tables = nt;
+    if (e != hipSuccess) free_dev_tables(t);
+    return e;
+}
+
+void free_dev_tables(DevTables* t) {
+    if (t->n) (void)hipFree(t->n);
+    if (t->enc) (void)hipFree(t->enc);
+    if (t->fc) (void)hipFree(t->fc);
+    if (t->slot) (void)hipFree(t->slot);
+    *t = DevTables{};
+}
+
+hipError_t launch_encode(const EncodeLaunch& a, const DevTables& t, hipStream_t st) {
+    if (a.shape.mode == SKV_CHECKERBOARD) return encode_all<SKV_INT16, SKV_CHECKERBOARD>(a, t, st);
+    if (a.shape.dtype == SKV_E4M3) return encode_all<SKV_E4M3, SKV_RESIDUAL>(a, t, st);
+    return encode_all<SKV_BF16, SKV_RESIDUAL>(a, t, st);
+}
+
+hipError_t launch_decode(const DecodeLaunch& a, const DevTables& t, hipStream_t st) {
+    if (a.shape.mode == SKV_CHECKERBOARD) return decode_all<SKV_INT16, SKV_CHECKERBOARD>(a, t, st);
+    if (a.shape.dtype == SKV_E4M3) return decode_all<SKV_E4M3, SKV_RESIDUAL>(a, t, st);
+    return decode_all<SKV_BF16, SKV_RESIDUAL>(a, t, st);
+}
+
+hipError_t launch_clear_u32(uint32_t* p, uint32_t n, hipStream_t st) {
+    hipLaunchKernelGGL(clear_u32, dim3((n + 255) / 256), dim3(256), 0, st, p, n);
+    return hipGetLastError();
+}
+
+}  // namespace skv

@@ -1,0 +1,214 @@
+"""ctypes binding of libskv (argument marshalling only).
+
+Torch tensors provide device memory, and the current torch stream provides
+the HIP stream. Every step of the coding runs in the library's HIP
+kernels. There is no CPU fallback: a missing library or GPU raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libskv.so")
+
+ABI_VERSION = 1
+BF16, E4M3, INT16 = 1, 2, 3
+RESIDUAL, CHECKERBOARD = 0, 1
+OK, ERR_ARG, ERR_SHAPE, ERR_CAPACITY, ERR_CORRUPT, ERR_TABLES, ERR_DEVICE, ERR_NOMEM = 0, -1, -2, -3, -4, -5, -6, -7
+
+
+class SkvError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {lib().skv_strerror(status).decode()} ({status})")
+
+
+class Shape(ctypes.Structure):
+    _fields_ = [("abi_version", ctypes.c_uint32), ("dtype", ctypes.c_uint32), ("mode", ctypes.c_uint32),
+                ("layers", ctypes.c_uint32), ("kv", ctypes.c_uint32), ("tokens", ctypes.c_uint32),
+                ("channels", ctypes.c_uint32)]
+
+
+_lib = None
+
+
+def lib():
+    """Load libskv.so (built in-tree by lossless_kv_cache_amd.build)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: run `python -m lossless_kv_cache_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, sz, u32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_uint32
+        psz = ctypes.POINTER(sz)
+        sp = ctypes.POINTER(Shape)
+        L.skv_version.restype = u32
+        L.skv_version.argtypes = []
+        L.skv_strerror.restype = ctypes.c_char_p
+        L.skv_strerror.argtypes = [ctypes.c_int]
+        L.skv_fit_tables.restype = ctypes.c_int
+        L.skv_fit_tables.argtypes = [sp, vp, vp, u32, ctypes.POINTER(vp), psz]
+        L.skv_load_tables.restype = ctypes.c_int
+        L.skv_load_tables.argtypes = [vp, sz, ctypes.POINTER(vp)]
+        L.skv_encode.restype = ctypes.c_int
+        L.skv_encode.argtypes = [vp, sp, vp, vp, vp, sz, psz, vp, psz, vp]
+        L.skv_decode.restype = ctypes.c_int
+        L.skv_decode.argtypes = [vp, vp, sz, vp, vp, sz, vp, psz, vp]
+        L.skv_free.restype = None
+        L.skv_free.argtypes = [vp]
+        if L.skv_version() != ABI_VERSION:
+            raise RuntimeError("libskv ABI version mismatch")
+        _lib = L
+    return _lib
+
+
+def _check(rc: int, what: str):
+    if rc != OK:
+        raise SkvError(rc, what)
+
+
+def make_shape(dtype: int, mode: int, layers: int, kv: int, tokens: int, channels: int) -> Shape:
+    return Shape(ABI_VERSION, dtype, mode, layers, kv, tokens, channels)
+
+
+class Tables:
+    """A library-owned table blob (host), uploaded to each device on first use."""
+
+    def __init__(self, ptr: int, nbytes: int):
+        self._ptr = ctypes.c_void_p(ptr)
+        self.nbytes = nbytes
+        b = self.bytes()[:64]
+        self.dtype, self.mode = b[6], b[7]
+        self.layers = int.from_bytes(b[12:16], "little")
+        self.kv = int.from_bytes(b[16:20], "little")
+        self.channels = int.from_bytes(b[20:24], "little")
+
+    @property
+    def ptr(self):
+        return self._ptr
+
+    def bytes(self) -> bytes:
+        return ctypes.string_at(self._ptr, self.nbytes)
+
+    def shape(self, tokens: int) -> Shape:
+        return make_shape(self.dtype, self.mode, self.layers, self.kv, tokens, self.channels)
+
+    def close(self):
+        if self._ptr and self._ptr.value and _lib is not None:
+            _lib.skv_free(self._ptr)
+        self._ptr = ctypes.c_void_p(None)
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def _host_ptr(a) -> tuple[int, object]:
+    if isinstance(a, torch.Tensor):
+        if a.is_cuda:
+            raise ValueError("calibration arrays are host arrays")
+        a = a.contiguous()
+        return a.data_ptr(), a
+    a = np.ascontiguousarray(a)
+    return a.ctypes.data, a
+
+
+def fit_tables(dtype: int, mode: int, layers: int, kv: int, channels: int, calib_target, calib_aux,
+               calib_tokens: int) -> Tables:
+    """Fit the tables once from host calibration arrays (see skv_fit_tables)."""
+    s = make_shape(dtype, mode, layers, kv, 0, channels)
+    pt, keep_t = _host_ptr(calib_target)
+    pa, keep_a = _host_ptr(calib_aux)
+    out, nb = ctypes.c_void_p(), ctypes.c_size_t()
+    _check(lib().skv_fit_tables(ctypes.byref(s), pt, pa, calib_tokens, ctypes.byref(out), ctypes.byref(nb)),
+           "skv_fit_tables")
+    return Tables(out.value, nb.value)
+
+
+def load_tables(blob: bytes) -> Tables:
+    buf = ctypes.create_string_buffer(bytes(blob), len(blob))
+    out = ctypes.c_void_p()
+    _check(lib().skv_load_tables(buf, len(blob), ctypes.byref(out)), "skv_load_tables")
+    return Tables(out.value, len(blob))
+
+
+def _dev(t: torch.Tensor, name: str) -> int:
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def tokens_of(tables: Tables, target: torch.Tensor) -> int:
+    if tables.mode == CHECKERBOARD:
+        if target.dim() != 2:
+            raise ValueError("checkerboard arrays are [tokens][channels]")
+        return target.shape[0]
+    if target.dim() != 4:
+        raise ValueError("residual arrays are [layers][kv][tokens][channels]")
+    return target.shape[2]
+
+
+class Encoder:
+    """Encodes repeatedly with one set of tables, reusing its buffers."""
+
+    def __init__(self, tables: Tables, tokens: int, device=None):
+        self.tables = tables
+        self.shape = tables.shape(tokens)
+        dev = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
+        ob, wb = ctypes.c_size_t(), ctypes.c_size_t()
+        _check(lib().skv_encode(tables.ptr, ctypes.byref(self.shape), None, None, None, 0, ctypes.byref(ob), None,
+                                ctypes.byref(wb), None), "skv_encode(size query)")
+        self.out = torch.empty(ob.value, dtype=torch.uint8, device=dev)
+        self.work = torch.empty(wb.value, dtype=torch.uint8, device=dev)
+
+    def __call__(self, target: torch.Tensor, aux: torch.Tensor) -> torch.Tensor:
+        """Returns a view of the container (valid until the next call)."""
+        ob = ctypes.c_size_t()
+        wb = ctypes.c_size_t(self.work.numel())
+        rc = lib().skv_encode(self.tables.ptr, ctypes.byref(self.shape), _dev(target, "target"), _dev(aux, "aux"),
+                              self.out.data_ptr(), self.out.numel(), ctypes.byref(ob), self.work.data_ptr(),
+                              ctypes.byref(wb), _stream())
+        _check(rc, "skv_encode")
+        return self.out[: ob.value]
+
+
+def encode(tables: Tables, target: torch.Tensor, aux: torch.Tensor) -> torch.Tensor:
+    """Encode a device cache; returns a fresh uint8 device tensor (the container)."""
+    enc = Encoder(tables, tokens_of(tables, target), target.device)
+    return enc(target, aux).clone()
+
+
+_decode_work = {}
+
+
+def decode_into(tables: Tables, container: torch.Tensor, aux: torch.Tensor, out: torch.Tensor) -> torch.Tensor:
+    key = container.device
+    work = _decode_work.get(key)
+    if work is None:
+        wb = ctypes.c_size_t()
+        _check(lib().skv_decode(tables.ptr, None, 0, None, None, 0, None, ctypes.byref(wb), None), "skv_decode(size)")
+        work = _decode_work[key] = torch.empty(wb.value, dtype=torch.uint8, device=key)
+    wb = ctypes.c_size_t(work.numel())
+    rc = lib().skv_decode(tables.ptr, _dev(container, "container"), container.numel(), _dev(aux, "aux"),
+                          _dev(out, "out"), out.numel() * out.element_size(), work.data_ptr(), ctypes.byref(wb),
+                          _stream())
+    _check(rc, "skv_decode")
+    return out
+
+
+def decode(tables: Tables, container: torch.Tensor, aux: torch.Tensor) -> torch.Tensor:
+    """Decode a container against the predictor (or G); returns a tensor shaped like aux."""
+    out = torch.empty_like(aux)
+    return decode_into(tables, container, aux, out)

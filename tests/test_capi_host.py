@@ -1,0 +1,119 @@
+"""libskv on the CPU: the library loads and exports every call declared in
+include/skv.h; the host table fit matches the oracle's fit byte for byte;
+blob validation and size queries behave as documented.  No device calls."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from workloads import gen
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def skv():
+    from lossless_kv_cache_amd import skv as m
+    if not os.path.exists(m.LIB_PATH):
+        from lossless_kv_cache_amd import build
+        build.build()
+    m.lib()
+    return m
+
+
+def test_exports_every_declared_symbol(skv):
+    text = open(os.path.join(ROOT, "include", "skv.h")).read()
+    names = set(re.findall(r"^\s*(?:int|void|uint32_t|const char\*)\s+(skv_\w+)\s*\(", text, re.M))
+    assert {"skv_fit_tables", "skv_load_tables", "skv_encode", "skv_decode", "skv_free",
+            "skv_version", "skv_strerror"} <= names
+    L = ctypes.CDLL(skv.LIB_PATH)
+    for n in sorted(names):
+        assert hasattr(L, n), n
+    assert skv.lib().skv_version() == 1
+
+
+def _residual_calib(cfg):
+    ct, cp = gen.residual_array(cfg, gen.CALIB, tokens=256)
+    return ct.numpy(), cp.numpy()
+
+
+@pytest.mark.parametrize("cid,layers", [(0, 1), (1, 2), (2, 2), (3, 1)])
+def test_fit_matches_oracle_residual(skv, orc, cid, layers):
+    cfg = gen.CONFIGS[cid].with_tokens(256, layers=layers)
+    ct, cp = _residual_calib(cfg)
+    dt = skv.E4M3 if cfg.dtype == "e4m3" else skv.BF16
+    tabs = skv.fit_tables(dt, skv.RESIDUAL, cfg.layers, cfg.kv, cfg.channels, ct, cp, 256)
+    shape = orc.make_shape(dt, orc.RESIDUAL, cfg.layers, cfg.kv, 128, cfg.channels)
+    want = orc.fit_tables(shape, ct, cp, 256)
+    got = tabs.bytes()
+    assert len(got) == len(want)
+    assert got == want
+
+
+def test_fit_matches_oracle_checkerboard(skv, orc):
+    cfg = gen.CONFIGS[4].with_tokens(256, channels=256)
+    cc, cg = gen.dckv_draw(cfg, gen.CALIB, tokens=256)
+    tabs = skv.fit_tables(skv.INT16, skv.CHECKERBOARD, 1, 1, 256, cc.numpy(), cg.numpy(), 256)
+    shape = orc.make_shape(orc.INT16, orc.CHECKERBOARD, 1, 1, 256, 256)
+    assert tabs.bytes() == orc.fit_tables(shape, cc.numpy(), cg.numpy(), 256)
+
+
+def test_fit_matches_oracle_adversarial(skv, orc):
+    """Calibration with constant channels, sign crossings and all-escape
+    channels exercises the floor on b, tiny direct ranges and R < 0."""
+    rng = np.random.default_rng(9)
+    T, C = 64, 64
+    t = rng.integers(0, 65536, size=(1, 2, T, C), dtype=np.uint16)
+    p = t.copy()
+    p[0, 0, :, :8] = t[0, 0, :, :8]                      # exact: b -> floor
+    p[0, 0, :, 8:16] ^= 0x8000                            # sign flips: huge residuals
+    p[0, 1] = (t[0, 1].astype(np.int32) + rng.integers(-3, 4, size=(T, C))).astype(np.uint16)
+    tabs = skv.fit_tables(skv.BF16, skv.RESIDUAL, 1, 2, C, t, p, T)
+    shape = orc.make_shape(orc.BF16, orc.RESIDUAL, 1, 2, 128, C)
+    assert tabs.bytes() == orc.fit_tables(shape, t, p, T)
+
+
+def test_load_tables_validates(skv, orc):
+    cfg = gen.CONFIGS[0].with_tokens(256)
+    ct, cp = _residual_calib(cfg)
+    good = orc.fit_tables(orc.make_shape(orc.BF16, orc.RESIDUAL, 1, 2, 128, 1024), ct, cp, 256)
+    t = skv.load_tables(good)
+    assert t.bytes() == good
+    bad = bytearray(good)
+    bad[64 + 2] ^= 1                                      # freq[0] changes: sum != 4096
+    with pytest.raises(skv.SkvError, match="-5"):
+        skv.load_tables(bytes(bad))
+    bad = bytearray(good)
+    bad[64] = 0                                           # n = 0
+    with pytest.raises(skv.SkvError):
+        skv.load_tables(bytes(bad))
+    with pytest.raises(skv.SkvError):
+        skv.load_tables(good[:-2])
+
+
+def test_size_queries_and_shape_errors(skv):
+    cfg = gen.CONFIGS[0].with_tokens(256)
+    ct, cp = _residual_calib(cfg)
+    tabs = skv.fit_tables(skv.BF16, skv.RESIDUAL, 1, 2, 1024, ct, cp, 256)
+    L = skv.lib()
+    ob, wb = ctypes.c_size_t(), ctypes.c_size_t()
+    s = tabs.shape(1024)
+    assert L.skv_encode(tabs.ptr, ctypes.byref(s), None, None, None, 0, ctypes.byref(ob), None, ctypes.byref(wb), None) == 0
+    n = 2 * 8 * 32
+    assert ob.value == 64 + 8 * (n + 1) + n * 8192
+    assert wb.value >= n * 8192
+    for bad in (tabs.shape(1000), skv.make_shape(skv.BF16, skv.RESIDUAL, 1, 2, 1024, 1000),
+                skv.make_shape(skv.INT16, skv.RESIDUAL, 1, 2, 1024, 1024)):
+        assert L.skv_encode(tabs.ptr, ctypes.byref(bad), None, None, None, 0, ctypes.byref(ob), None,
+                            ctypes.byref(wb), None) == skv.ERR_SHAPE
+    other = skv.make_shape(skv.BF16, skv.RESIDUAL, 2, 2, 1024, 1024)           # blob is for 1 layer
+    assert L.skv_encode(tabs.ptr, ctypes.byref(other), None, None, None, 0, ctypes.byref(ob), None,
+                        ctypes.byref(wb), None) == skv.ERR_TABLES
+    dummy = ctypes.c_void_p(12345)
+    assert L.skv_encode(dummy, ctypes.byref(s), None, None, None, 0, ctypes.byref(ob), None,
+                        ctypes.byref(wb), None) == skv.ERR_ARG                  # not a library blob
+    s.abi_version = 2
+    assert L.skv_encode(tabs.ptr, ctypes.byref(s), None, None, None, 0, ctypes.byref(ob), None,
+                        ctypes.byref(wb), None) == skv.ERR_SHAPE

@@ -1,0 +1,279 @@
+"""GPU parity: containers and reconstructions from libskv's HIP kernels are
+bit-identical to the CPU oracle's.
+
+The coding path is integer end to end, so there is no tolerance: container
+bytes must equal the oracle's byte for byte and the decode must return the
+target exactly (lossless reconstruction, Speculative KV coding summary,
+'Core idea'; checkerboard decoding in two passes, DCKV page, 'How it
+differs').  Small cases compare whole containers; full-size workloads
+compare sampled streams (the oracle encodes them one by one from the
+gathered tiles) plus the exact GPU round trip.
+"""
+import struct
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from workloads import gen
+
+pytestmark = pytest.mark.gpu
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def skv():
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible")
+    from lossless_kv_cache_amd import skv as m
+    m.lib()
+    return m
+
+
+def _dt(cfg, skv):
+    return {"bf16": skv.BF16, "e4m3": skv.E4M3, "int16": skv.INT16}[cfg.dtype]
+
+
+def _parse(c: bytes):
+    n = struct.unpack_from("<Q", c, 32)[0]
+    idx = np.frombuffer(c[64:64 + 8 * (n + 1)], dtype=np.uint64)
+    return n, idx, 64 + 8 * (n + 1)
+
+
+def residual_case(skv, orc, cfg, device="cuda"):
+    t, p = gen.residual_array(cfg, device=device)
+    ct, cp = gen.residual_array(cfg, gen.CALIB, tokens=256, device=device)
+    ct, cp = ct.cpu().numpy(), cp.cpu().numpy()
+    dt = _dt(cfg, skv)
+    tabs = skv.fit_tables(dt, skv.RESIDUAL, cfg.layers, cfg.kv, cfg.channels, ct, cp, 256)
+    oshape = orc.make_shape(dt, orc.RESIDUAL, cfg.layers, cfg.kv, cfg.tokens, cfg.channels)
+    return t, p, tabs, oshape
+
+
+def full_compare(skv, orc, t, p, tabs, oshape, what):
+    say(f"[parity] {what}: encode on GPU")
+    cont = skv.encode(tabs, t, p)
+    torch.cuda.synchronize()
+    tn, pn = t.cpu().numpy(), p.cpu().numpy()
+    say(f"[parity] {what}: encode with oracle")
+    want = orc.encode(tabs.bytes(), oshape, tn, pn, threads=8)
+    got = cont.cpu().numpy().tobytes()
+    assert len(got) == len(want), (len(got), len(want))
+    if got != want:
+        n, idx, head = _parse(want)
+        gi = np.frombuffer(got[64:head], dtype=np.uint64)
+        bad = np.nonzero(gi != idx)[0]
+        raise AssertionError(f"container differs; first index mismatch {bad[:5]}")
+    say(f"[parity] {what}: decode on GPU")
+    back = skv.decode(tabs, cont, p)
+    assert torch.equal(back, t)
+    # the GPU decodes the oracle's container as well
+    back2 = skv.decode(tabs, torch.from_numpy(np.frombuffer(want, dtype=np.uint8).copy()).cuda(), p)
+    assert torch.equal(back2, t)
+    return want
+
+
+def test_cfg0_full_container(skv, orc):
+    cfg = gen.CONFIGS[0]
+    t, p, tabs, oshape = residual_case(skv, orc, cfg)
+    c = full_compare(skv, orc, t, p, tabs, oshape, "cfg0 bf16 1x2x1024x1024")
+    say(f"[parity] cfg0 ratio {t.numel() * 2 / len(c):.3f}")
+
+
+def test_ragged_grid_bf16(skv, orc):
+    """1188 streams: several scan blocks with a partial last one, and a
+    partial last workgroup of the encoder and decoder grids."""
+    cfg = gen.Config(90, "ragged-bf16", "bf16", 6, 2, 1152, 352)
+    t, p, tabs, oshape = residual_case(skv, orc, cfg)
+    assert orc.n_streams(oshape) == 1188
+    full_compare(skv, orc, t, p, tabs, oshape, "ragged bf16 6x2x1152x352")
+
+
+def test_e4m3_small(skv, orc):
+    cfg = gen.CONFIGS[2].with_tokens(640, layers=3, channels=160)
+    t, p, tabs, oshape = residual_case(skv, orc, cfg)
+    full_compare(skv, orc, t, p, tabs, oshape, "e4m3 3x2x640x160")
+
+
+def test_checkerboard_small(skv, orc):
+    cfg = gen.CONFIGS[4].with_tokens(1280, channels=192)
+    coef, G = gen.dckv_draw(cfg, device="cuda")
+    cc, cg = gen.dckv_draw(cfg, gen.CALIB, tokens=256, device="cuda")
+    tabs = skv.fit_tables(skv.INT16, skv.CHECKERBOARD, 1, 1, 192, cc.cpu().numpy(), cg.cpu().numpy(), 256)
+    oshape = orc.make_shape(orc.INT16, orc.CHECKERBOARD, 1, 1, 1280, 192)
+    full_compare(skv, orc, coef, G, tabs, oshape, "checkerboard 1280x192")
+
+
+@pytest.mark.parametrize("kind", ["equal", "random", "maxz", "escapes"])
+def test_edge_inputs(skv, orc, kind):
+    """Degenerate inputs: target == predictor; incompressible (raw
+    fallback); residual -2^15 everywhere (largest escape); every value
+    escaping but still coded."""
+    cfg = gen.Config(91, "edge-bf16", "bf16", 1, 2, 256, 96)
+    t, p, tabs, oshape = residual_case(skv, orc, cfg)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(17)
+    if kind == "equal":
+        t = p.clone()
+    elif kind == "random":
+        t = torch.randint(-32768, 32768, p.shape, generator=g, device="cuda", dtype=torch.int32).to(torch.int16)
+    elif kind == "maxz":
+        t = (p.to(torch.int32) ^ 0x8000).to(torch.int16)          # sign flip: r = -2^15 or near
+    elif kind == "escapes":
+        t = (p.to(torch.int32) + 300).to(torch.int16)             # |r| = 300 > every direct range
+    full_compare(skv, orc, t, p, tabs, oshape, f"edge {kind}")
+
+
+def test_corruption_and_wrong_tables(skv, orc):
+    cfg = gen.Config(92, "corrupt-bf16", "bf16", 1, 2, 256, 64)
+    t, p, tabs, oshape = residual_case(skv, orc, cfg)
+    cont = skv.encode(tabs, t, p)
+    good = cont.cpu().numpy()
+    n, idx, head = _parse(good.tobytes())
+    rng = np.random.default_rng(4)
+    for trial in range(6):
+        bad = good.copy()
+        s = int(rng.integers(0, n))
+        a = int(idx[s] & np.uint64((1 << 63) - 1))
+        b = int(idx[s + 1] & np.uint64((1 << 63) - 1))
+        if idx[s] >> np.uint64(63):
+            continue
+        pos = head + int(rng.integers(a + 128, b))
+        bad[pos] ^= np.uint8(1 << int(rng.integers(0, 8)))
+        say(f"[parity] corrupt trial {trial}: stream {s} byte {pos}")
+        with pytest.raises(skv.SkvError) as e:
+            skv.decode(tabs, torch.from_numpy(bad).cuda(), p)
+        assert e.value.status == skv.ERR_CORRUPT
+    # index pointing past the payload
+    bad = good.copy()
+    bad[64 + 8 * 3:64 + 8 * 4] = np.frombuffer(struct.pack("<Q", 1 << 40), np.uint8)
+    with pytest.raises(skv.SkvError) as e:
+        skv.decode(tabs, torch.from_numpy(bad).cuda(), p)
+    assert e.value.status == skv.ERR_CORRUPT
+    # truncated container
+    with pytest.raises(skv.SkvError) as e:
+        skv.decode(tabs, cont[:-8].contiguous(), p)
+    assert e.value.status == skv.ERR_CORRUPT
+    # another blob
+    ct2, cp2 = gen.residual_array(cfg.with_tokens(256), gen.EVAL, tokens=256)
+    other = skv.fit_tables(skv.BF16, skv.RESIDUAL, 1, 2, 64, ct2.numpy(), cp2.numpy(), 256)
+    with pytest.raises(skv.SkvError) as e:
+        skv.decode(other, cont, p)
+    assert e.value.status == skv.ERR_TABLES
+    # output too small
+    with pytest.raises(skv.SkvError) as e:
+        skv.decode_into(tabs, cont, p, torch.empty(10, dtype=torch.int16, device="cuda"))
+    assert e.value.status == skv.ERR_CAPACITY
+    assert torch.equal(skv.decode(tabs, cont, p), t)
+
+
+# ------------------------------------------------------------------ full-size workloads
+def _sample_ids(n, k, seed):
+    rng = np.random.default_rng(seed)
+    ids = set(rng.choice(n, size=min(k, n), replace=False).tolist())
+    ids.update({0, n - 1})
+    return sorted(ids)
+
+
+def _check_sampled_streams(orc, blob, oshape, cont_host, tile_fn, lane_fn, n, ids, what):
+    head = 64 + 8 * (n + 1)
+    idx = np.frombuffer(cont_host[64:head], dtype=np.uint64)
+    mask = np.uint64((1 << 63) - 1)
+    offs = idx & mask
+    assert offs[0] == 0 and np.all(offs[1:] >= offs[:-1])
+    assert int(offs[-1]) == len(cont_host) - head
+    for s in ids:
+        tt, ta, nl, nr = tile_fn(s)
+        data, raw = orc.encode_tile(blob, oshape, tt, ta, lane_fn(s), nl, nr)
+        a, b = int(offs[s]), int(offs[s + 1])
+        assert bool(int(idx[s]) >> 63) == raw, (what, s)
+        assert cont_host[head + a:head + b] == data, (what, s)
+
+
+@pytest.mark.parametrize("cid", [1, 2, 3])
+def test_full_size_residual(skv, orc, cid):
+    cfg = gen.CONFIGS[cid]
+    say(f"[parity] cfg{cid} {cfg.name}: generating {cfg.values} values on GPU")
+    t, p, tabs, oshape = residual_case(skv, orc, cfg)
+    say(f"[parity] cfg{cid}: encode")
+    cont = skv.encode(tabs, t, p)
+    torch.cuda.synchronize()
+    n = orc.n_streams(oshape)
+    ratio = cfg.raw_bytes / cont.numel()
+    say(f"[parity] cfg{cid}: {n} streams, container {cont.numel()} B, ratio {ratio:.3f}")
+    head = 64 + 8 * (n + 1)
+    ids = _sample_ids(n, 48, cid)
+    # copy back only the header+index and the sampled streams' bytes
+    host_head = cont[:head].cpu().numpy().tobytes()
+    idx = np.frombuffer(host_head[64:], dtype=np.uint64) & np.uint64((1 << 63) - 1)
+    assert int(idx[-1]) == cont.numel() - head
+    ncg, ntb = cfg.channels // 32, cfg.tokens // 128
+    blob = tabs.bytes()
+
+    def tile(s):
+        cg, rest = s % ncg, s // ncg
+        tb, slab = rest % ntb, rest // ntb
+        l, k = divmod(slab, cfg.kv)
+        sl = (l, k, slice(tb * 128, tb * 128 + 128), slice(cg * 32, cg * 32 + 32))
+        return t[sl].cpu().numpy(), p[sl].cpu().numpy(), None, None
+
+    def lanes(s):
+        cg, slab = s % ncg, s // (ncg * ntb)
+        return np.arange(32, dtype=np.uint32) + slab * cfg.channels + cg * 32
+
+    head_raw = np.frombuffer(host_head[64:], dtype=np.uint64)
+    for s in ids:
+        tt, ta, _, _ = tile(s)
+        data, raw = orc.encode_tile(blob, oshape, tt, ta, lanes(s))
+        a, b = int(idx[s]), int(idx[s + 1])
+        assert bool(int(head_raw[s]) >> 63) == raw, s
+        got = cont[head + a:head + b].cpu().numpy().tobytes()
+        assert got == data, (cid, s)
+    say(f"[parity] cfg{cid}: {len(ids)} sampled streams identical; decoding")
+    del cont
+    back = skv.decode(tabs, skv.encode(tabs, t, p), p)
+    assert torch.equal(back, t)
+    say(f"[parity] cfg{cid}: round trip exact")
+
+
+def test_full_size_checkerboard(skv, orc):
+    cfg = gen.CONFIGS[4]
+    say("[parity] cfg4: generating")
+    coef, G = gen.dckv_draw(cfg, device="cuda")
+    cc, cg = gen.dckv_draw(cfg, gen.CALIB, tokens=256, device="cuda")
+    tabs = skv.fit_tables(skv.INT16, skv.CHECKERBOARD, 1, 1, cfg.channels, cc.cpu().numpy(), cg.cpu().numpy(), 256)
+    oshape = orc.make_shape(orc.INT16, orc.CHECKERBOARD, 1, 1, cfg.tokens, cfg.channels)
+    cont = skv.encode(tabs, coef, G)
+    torch.cuda.synchronize()
+    n = orc.n_streams(oshape)
+    head = 64 + 8 * (n + 1)
+    say(f"[parity] cfg4: {n} streams, ratio {cfg.raw_bytes / cont.numel():.3f}")
+    idx_raw = np.frombuffer(cont[:head].cpu().numpy().tobytes()[64:], dtype=np.uint64)
+    idx = idx_raw & np.uint64((1 << 63) - 1)
+    ncg, ntb = cfg.channels // 32, cfg.tokens // 2 // 128
+    T = cfg.tokens
+    blob = tabs.bytes()
+    for s in _sample_ids(n, 48, 4):
+        cgi, rest = s % ncg, s // ncg
+        tb, ps = rest % ntb, rest // ntb
+        toks = torch.arange(128, device="cuda") * 2 + 2 * 128 * tb + ps
+        cols = slice(cgi * 32, cgi * 32 + 32)
+        tt = coef[toks, cols].cpu().numpy()
+        ta = G[toks, cols].cpu().numpy()
+        nl = nr = None
+        if ps == 1:
+            nl = coef[toks - 1, cols].cpu().numpy()
+            right = torch.where(toks + 1 < T, toks + 1, toks - 1)
+            nr = coef[right, cols].cpu().numpy()
+        data, raw = orc.encode_tile(blob, oshape, tt, ta, np.arange(32, dtype=np.uint32) + cgi * 32, nl, nr)
+        a, b = int(idx[s]), int(idx[s + 1])
+        assert bool(int(idx_raw[s]) >> 63) == raw
+        assert cont[head + a:head + b].cpu().numpy().tobytes() == data, s
+    back = skv.decode(tabs, cont, G)
+    assert torch.equal(back, coef)
+    say("[parity] cfg4: sampled streams identical, round trip exact")
