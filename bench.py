@@ -1,0 +1,247 @@
+#!/usr/bin/env python3
+"""Throughput of lossless KV-cache coding on one MI355X.
+
+A step is one pass of the whole coding path over the cache: encode
+(symbolize, table lookup, 32-lane rANS, index + compaction) and decode (rANS
+decode, reconstruction) of the Qwen3-8B-shaped e4m3 cache, 36 layers x K,V
+x 32768 tokens x 1024 channels, with inputs resident in HBM.  The tables are
+fitted once before timing (their fit is not part of a step).
+
+Prints one JSON line: uncompressed GB/s of the round trip, encode and decode
+rates, the ratio, per-kernel times from HIP events recorded on the launch
+stream, the roofline position of the dominant kernel and the CPU oracle
+timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "KV rANS encode/decode GB/s (uncompressed) + ratio, % HBM roofline, 1 GPU"
+HBM_PEAK_GBPS = 8000.0
+KERNEL_SRC = os.path.join(ROOT, "lossless_kv_cache_amd", "csrc", "skv_kernels.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_sha() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", type=int, default=2, help="workload id (2 = Qwen3-8B-shaped e4m3)")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target length of the CPU-oracle sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="also time a plain device copy of the cache (HBM ceiling; counter scale reference)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the coding path has no multi-GPU part "
+              "(streams are independent; sharding is described in DESIGN.md). Run with --gpus 1.",
+              flush=True)
+        return 2
+
+    import numpy as np
+    import torch
+
+    from lossless_kv_cache_amd import skv
+    from workloads import gen
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", flush=True)
+        return 1
+    torch.cuda.set_device(0)
+    cfg = gen.CONFIGS[args.config]
+    if cfg.dtype == "int16":
+        raise SystemExit("the checkerboard workload is a parity case; bench times the residual workloads")
+    dt = skv.E4M3 if cfg.dtype == "e4m3" else skv.BF16
+
+    log(f"generating {cfg.name}: {cfg.values} values on the GPU")
+    t0 = time.perf_counter()
+    tgt, prd = gen.residual_array(cfg, device="cuda")
+    ct, cp = gen.residual_array(cfg, gen.CALIB, tokens=gen.CALIB_TOKENS, device="cuda")
+    torch.cuda.synchronize()
+    log(f"generated in {time.perf_counter() - t0:.1f} s; fitting tables")
+    t0 = time.perf_counter()
+    tabs = skv.fit_tables(dt, skv.RESIDUAL, cfg.layers, cfg.kv, cfg.channels, ct.cpu().numpy(), cp.cpu().numpy(),
+                          gen.CALIB_TOKENS)
+    fit_s = time.perf_counter() - t0
+    del ct, cp
+    log(f"fit {tabs.nbytes} B of tables in {fit_s:.2f} s")
+
+    enc = skv.Encoder(tabs, cfg.tokens)
+    out = torch.empty_like(tgt)
+    raw_bytes = cfg.raw_bytes
+
+    def step():
+        a = time.perf_counter()
+        cont = enc(tgt, prd)
+        b = time.perf_counter()
+        ke = skv.kernel_times()
+        skv.decode_into(tabs, cont, prd, out)
+        c = time.perf_counter()
+        kd = skv.kernel_times()
+        return cont.numel(), b - a, c - b, ke + kd
+
+    skv.kernel_timing(True)
+    for i in range(args.warmup):
+        step()
+        log(f"warmup {i + 1}/{args.warmup} done")
+    torch.cuda.synchronize()
+    enc_s, dec_s, ktot, kcnt = [], [], {}, {}
+    cont_bytes = 0
+    t_start = time.perf_counter()
+    for i in range(args.steps):
+        cont_bytes, e, d, ks = step()
+        enc_s.append(e)
+        dec_s.append(d)
+        for name, ms in ks:
+            ktot[name] = ktot.get(name, 0.0) + ms
+            kcnt[name] = kcnt.get(name, 0) + 1
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    skv.kernel_timing(False)
+    log(f"timed {args.steps} steps in {wall:.3f} s")
+
+    ok = bool(torch.equal(out, tgt))
+    if not ok:
+        log("RECONSTRUCTION MISMATCH")
+    n_streams = cfg.layers * cfg.kv * (cfg.tokens // 128) * (cfg.channels // 32)
+    head = 64 + 8 * (n_streams + 1)
+    payload = cont_bytes - head
+    ratio = raw_bytes / cont_bytes
+    ms_per_step = wall / args.steps * 1e3
+    enc_ms = 1e3 * sum(enc_s) / len(enc_s)
+    dec_ms = 1e3 * sum(dec_s) / len(dec_s)
+    kavg = {k: ktot[k] / kcnt[k] for k in ktot}
+
+    # algorithmic bytes per launch (what the method itself must move)
+    alg = {
+        "encode_streams": 2 * raw_bytes + payload,               # target + predictor read, coded streams out
+        "place_streams": cont_bytes,                             # the container written
+        "decode_streams": raw_bytes + cont_bytes + raw_bytes,    # predictor + container read, reconstruction out
+        "stream_block_sums": 0, "stream_block_scan": 0,
+    }
+    dom = max(ktot, key=lambda k: ktot[k] / args.steps)
+    dur_s = kavg[dom] / 1e3
+    achieved = alg.get(dom, 0) / dur_s / 1e9
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as f:
+            tr = json.load(f)
+        ent = tr.get(dom)
+        if ent and ent.get("kernel_sha") == kernel_sha() and ent.get("workload") == cfg.name:
+            traffic = ent["bytes_per_launch"]
+    roofline = {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
+                "algorithmic_bytes": alg.get(dom, 0), "avg_ms": round(kavg[dom], 4)}
+
+    copy = None
+    if args.copy_probe:
+        src = tgt.view(-1).view(torch.uint8)
+        dst = torch.empty_like(src)
+        for _ in range(2):
+            dst.copy_(src)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(5):
+            dst.copy_(src)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / 5
+        copy = {"bytes_copied": src.numel(), "ms": round(ms, 4),
+                "GBps_read_plus_write": round(2 * src.numel() / (ms / 1e3) / 1e9, 1)}
+        del dst
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(cfg, tabs, tgt, prd, args.cpu_seconds)
+
+    res = {
+        "metric": METRIC,
+        "value": round(raw_bytes / (ms_per_step / 1e3) / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "u32",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "shape": f"[{cfg.layers}][{cfg.kv}][{cfg.tokens}][{cfg.channels}]",
+                   "element": cfg.dtype, "values": cfg.values, "raw_bytes": raw_bytes, "streams": n_streams,
+                   "step": "encode + decode of the whole cache", "container_bytes": cont_bytes},
+        "ratio": round(ratio, 4),
+        "encode_GBps": round(raw_bytes / (enc_ms / 1e3) / 1e9, 2),
+        "decode_GBps": round(raw_bytes / (dec_ms / 1e3) / 1e9, 2),
+        "encode_ms": round(enc_ms, 3),
+        "decode_ms": round(dec_ms, 3),
+        "kernels_ms": {k: round(v, 4) for k, v in kavg.items()},
+        "table_fit_s": round(fit_s, 3),
+        "verified_roundtrip": ok,
+        "roofline": roofline,
+        "copy_ceiling": copy,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res), flush=True)
+    return 0 if ok else 1
+
+
+def cpu_baseline(cfg, tabs, tgt, prd, seconds):
+    """The oracle (plain C, OpenMP over streams) on the host: encode + decode
+    of whole layers of the same workload until about `seconds` of work."""
+    import numpy as np
+    import oracle
+
+    threads = max(1, min(16, len(os.sched_getaffinity(0))))
+    blob = tabs.bytes()
+    per_layer_tables = cfg.kv * cfg.channels
+    rec = 514
+    done_bytes, spent, layers = 0, 0.0, 0
+    for layer in range(cfg.layers):
+        hdr = bytearray(blob[:64])
+        hdr[8:12] = per_layer_tables.to_bytes(4, "little")
+        hdr[12:16] = (1).to_bytes(4, "little")
+        total = 64 + per_layer_tables * rec
+        hdr[32:40] = total.to_bytes(8, "little")
+        sub = bytes(hdr) + blob[64 + layer * per_layer_tables * rec:64 + (layer + 1) * per_layer_tables * rec]
+        t = tgt[layer:layer + 1].cpu().numpy()
+        p = prd[layer:layer + 1].cpu().numpy()
+        dt = oracle.E4M3 if cfg.dtype == "e4m3" else oracle.BF16
+        shape = oracle.make_shape(dt, oracle.RESIDUAL, 1, cfg.kv, cfg.tokens, cfg.channels)
+        a = time.perf_counter()
+        c = oracle.encode(sub, shape, t, p, threads=threads)
+        back = oracle.decode(sub, c, p, t, threads=threads)
+        spent += time.perf_counter() - a
+        if not np.array_equal(back, t):
+            raise RuntimeError("oracle round trip failed")
+        done_bytes += t.nbytes
+        layers += 1
+        log(f"cpu oracle: layer {layer} done, {spent:.1f} s so far")
+        if spent >= seconds:
+            break
+    return {"value": round(done_bytes / spent / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"encode + decode of {layers} of {cfg.layers} layers (K and V, {done_bytes} B of "
+                      f"{cfg.dtype} codes) of the same workload and tables, {threads} OpenMP threads",
+            "seconds": round(spent, 2)}
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -124,6 +124,17 @@ int skv_decode(const void* tables_blob, const void* d_in, size_t in_bytes, const
 /* Release a library-owned blob and its device copies.  NULL is a no-op. */
 void skv_free(void* tables_blob);
 
+/* Diagnostics.  skv_kernel_timing(1) creates HIP events on the current
+ * device; from then on every skv_encode / skv_decode records an event pair
+ * around each kernel it launches on the caller's stream.
+ * skv_kernel_times fills names[i] (static strings) and ms[i] (elapsed
+ * milliseconds) for the kernels of the last call, in launch order, and
+ * returns their count (at most `capacity`; either array may be NULL).
+ * skv_kernel_timing(0) releases the events.  Process-wide state: callers
+ * encoding concurrently should not enable it. */
+int skv_kernel_timing(int enable);
+int skv_kernel_times(const char** names, float* ms, int capacity);
+
 /* Library ABI version (SKV_ABI_VERSION) and a static message per status. */
 uint32_t skv_version(void);
 const char* skv_strerror(int status);

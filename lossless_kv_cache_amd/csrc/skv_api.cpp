@@ -185,10 +185,12 @@ int skv_encode(const void* tables_blob, const skv_shape* s, const void* d_target
     a.blob_hash = b->hash;
     a.shape = *s;
     a.n_streams = n;
+    skv::timing_reset();
     if (skv::launch_encode(a, *t, stream) != hipSuccess) return SKV_ERR_DEVICE;
     uint64_t payload = 0;
     if (hipMemcpyAsync(&payload, a.total, 8, hipMemcpyDeviceToHost, stream) != hipSuccess) return SKV_ERR_DEVICE;
     if (hipStreamSynchronize(stream) != hipSuccess) return SKV_ERR_DEVICE;
+    skv::timing_collect();
     const uint64_t total = skv::kHeaderBytes + 8 * (n + 1) + payload;
     *out_bytes = total;
     return total > out_capacity ? SKV_ERR_CAPACITY : SKV_OK;
@@ -237,11 +239,20 @@ int skv_decode(const void* tables_blob, const void* d_in, size_t in_bytes, const
     a.shape = s;
     a.n_streams = n;
     if (skv::launch_clear_u32(a.status, 1, stream) != hipSuccess) return SKV_ERR_DEVICE;
+    skv::timing_reset();
     if (skv::launch_decode(a, *t, stream) != hipSuccess) return SKV_ERR_DEVICE;
     uint32_t status = 0;
     if (hipMemcpyAsync(&status, a.status, 4, hipMemcpyDeviceToHost, stream) != hipSuccess) return SKV_ERR_DEVICE;
     if (hipStreamSynchronize(stream) != hipSuccess) return SKV_ERR_DEVICE;
+    skv::timing_collect();
     return status ? SKV_ERR_CORRUPT : SKV_OK;
+}
+
+int skv_kernel_timing(int enable) { return skv::timing_enable(enable != 0); }
+
+int skv_kernel_times(const char** names, float* ms, int capacity) {
+    if (capacity < 0) return SKV_ERR_ARG;
+    return skv::timing_read(names, ms, capacity);
 }
 
 }  // extern "C"

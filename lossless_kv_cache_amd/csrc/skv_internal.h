@@ -24,6 +24,7 @@ constexpr size_t kHeaderBytes = 64;
 constexpr size_t kTableRecord = 514;  // u16 n + u16 freq[256]
 constexpr size_t kStateBytes = 4 * kLanes;
 constexpr uint64_t kRawBit = 1ull << 63;
+constexpr int kMaxTimedKernels = 16;
 
 inline uint32_t elem_bytes(uint32_t dtype) { return dtype == SKV_E4M3 ? 1u : 2u; }
 
@@ -87,5 +88,11 @@ hipError_t launch_encode(const EncodeLaunch& a, const DevTables& t, hipStream_t 
 hipError_t launch_decode(const DecodeLaunch& a, const DevTables& t, hipStream_t stream);
 hipError_t launch_clear_u32(uint32_t* p, uint32_t n, hipStream_t stream);
 uint64_t encode_work_bytes(uint64_t n_streams, uint32_t raw_bytes);
+
+// per-kernel timing diagnostics (process-wide, not for concurrent callers)
+int timing_enable(bool on);
+void timing_reset();
+void timing_collect();
+int timing_read(const char** names, float* ms, int cap);
 
 }  // namespace skv

@@ -439,16 +439,49 @@ __global__ void clear_u32(uint32_t* p, uint32_t n) {
     if (i < n) p[i] = 0u;
 }
 
+// Optional per-kernel timing: a HIP event pair around each launch on the
+// caller's stream, read back after the call's final synchronization.
+struct KernelTiming {
+    bool on = false;
+    int count = 0;
+    hipEvent_t ev[2 * kMaxTimedKernels] = {};
+    const char* name[kMaxTimedKernels] = {};
+    float ms[kMaxTimedKernels] = {};
+    int done = 0;
+};
+KernelTiming g_timing;
+
+template <class F>
+void timed(const char* name, hipStream_t st, F&& launch) {
+    KernelTiming& T = g_timing;
+    if (T.on && T.count < kMaxTimedKernels) {
+        (void)hipEventRecord(T.ev[2 * T.count], st);
+        launch();
+        (void)hipEventRecord(T.ev[2 * T.count + 1], st);
+        T.name[T.count++] = name;
+    } else {
+        launch();
+    }
+}
+
 template <uint32_t DT, uint32_t MODE>
 hipError_t encode_all(const EncodeLaunch& a, const DevTables& t, hipStream_t st) {
     const uint64_t n = a.n_streams;
     const uint32_t nb = uint32_t((n + kScanBlock - 1) / kScanBlock);
     const uint32_t eg = uint32_t((n + kStreamsPerBlock - 1) / kStreamsPerBlock);
-    hipLaunchKernelGGL((encode_streams<DT, MODE>), dim3(eg), dim3(256), 0, st, a, t);
-    hipLaunchKernelGGL(stream_block_sums, dim3(nb), dim3(kScanBlock), 0, st, a.meta, n, kSyms * (DT == SKV_E4M3 ? 1u : 2u),
-                       a.block_sum);
-    hipLaunchKernelGGL(stream_block_scan, dim3(1), dim3(kScanBlock), 0, st, a.block_sum, nb, a.block_off, a.total);
-    hipLaunchKernelGGL((place_streams<DT, MODE>), dim3(nb), dim3(kScanBlock), 0, st, a, a.block_off);
+    timed("encode_streams", st, [&] {
+        hipLaunchKernelGGL((encode_streams<DT, MODE>), dim3(eg), dim3(256), 0, st, a, t);
+    });
+    timed("stream_block_sums", st, [&] {
+        hipLaunchKernelGGL(stream_block_sums, dim3(nb), dim3(kScanBlock), 0, st, a.meta, n,
+                           kSyms * (DT == SKV_E4M3 ? 1u : 2u), a.block_sum);
+    });
+    timed("stream_block_scan", st, [&] {
+        hipLaunchKernelGGL(stream_block_scan, dim3(1), dim3(kScanBlock), 0, st, a.block_sum, nb, a.block_off, a.total);
+    });
+    timed("place_streams", st, [&] {
+        hipLaunchKernelGGL((place_streams<DT, MODE>), dim3(nb), dim3(kScanBlock), 0, st, a, a.block_off);
+    });
     return hipGetLastError();
 }
 
@@ -458,7 +491,9 @@ hipError_t decode_all(const DecodeLaunch& a, const DevTables& t, hipStream_t st)
     const uint64_t per = a.n_streams / passes;
     const uint32_t grid = uint32_t((per + kStreamsPerBlock - 1) / kStreamsPerBlock);
     for (uint64_t ps = 0; ps < passes; ++ps)
-        hipLaunchKernelGGL((decode_streams<DT, MODE>), dim3(grid), dim3(256), 0, st, a, t, ps * per, per);
+        timed("decode_streams", st, [&] {
+            hipLaunchKernelGGL((decode_streams<DT, MODE>), dim3(grid), dim3(256), 0, st, a, t, ps * per, per);
+        });
     return hipGetLastError();
 }
 
@@ -508,6 +543,45 @@ hipError_t launch_decode(const DecodeLaunch& a, const DevTables& t, hipStream_t 
     if (a.shape.mode == SKV_CHECKERBOARD) return decode_all<SKV_INT16, SKV_CHECKERBOARD>(a, t, st);
     if (a.shape.dtype == SKV_E4M3) return decode_all<SKV_E4M3, SKV_RESIDUAL>(a, t, st);
     return decode_all<SKV_BF16, SKV_RESIDUAL>(a, t, st);
+}
+
+int timing_enable(bool on) {
+    KernelTiming& T = g_timing;
+    if (on == T.on) return SKV_OK;
+    for (int i = 0; i < 2 * kMaxTimedKernels; ++i) {
+        if (on) {
+            if (hipEventCreate(&T.ev[i]) != hipSuccess) return SKV_ERR_DEVICE;
+        } else if (T.ev[i]) {
+            (void)hipEventDestroy(T.ev[i]);
+            T.ev[i] = nullptr;
+        }
+    }
+    T.on = on;
+    T.count = T.done = 0;
+    return SKV_OK;
+}
+
+void timing_reset() { g_timing.count = 0; }
+
+void timing_collect() {
+    KernelTiming& T = g_timing;
+    if (!T.on) return;
+    for (int i = 0; i < T.count; ++i) {
+        float ms = 0.f;
+        if (hipEventElapsedTime(&ms, T.ev[2 * i], T.ev[2 * i + 1]) != hipSuccess) ms = -1.f;
+        T.ms[i] = ms;
+    }
+    T.done = T.count;
+}
+
+int timing_read(const char** names, float* ms, int cap) {
+    const KernelTiming& T = g_timing;
+    int n = 0;
+    for (; n < T.done && n < cap; ++n) {
+        if (names) names[n] = T.name[n];
+        if (ms) ms[n] = T.ms[n];
+    }
+    return n;
 }
 
 hipError_t launch_clear_u32(uint32_t* p, uint32_t n, hipStream_t st) {

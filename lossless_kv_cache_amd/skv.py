@@ -60,6 +60,10 @@ def lib():
         L.skv_decode.argtypes = [vp, vp, sz, vp, vp, sz, vp, psz, vp]
         L.skv_free.restype = None
         L.skv_free.argtypes = [vp]
+        L.skv_kernel_timing.restype = ctypes.c_int
+        L.skv_kernel_timing.argtypes = [ctypes.c_int]
+        L.skv_kernel_times.restype = ctypes.c_int
+        L.skv_kernel_times.argtypes = [ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(ctypes.c_float), ctypes.c_int]
         if L.skv_version() != ABI_VERSION:
             raise RuntimeError("libskv ABI version mismatch")
         _lib = L
@@ -206,6 +210,20 @@ def decode_into(tables: Tables, container: torch.Tensor, aux: torch.Tensor, out:
                           _stream())
     _check(rc, "skv_decode")
     return out
+
+
+def kernel_timing(enable: bool) -> None:
+    """Enable per-kernel HIP-event timing of the following encode/decode calls."""
+    _check(lib().skv_kernel_timing(1 if enable else 0), "skv_kernel_timing")
+
+
+def kernel_times() -> list[tuple[str, float]]:
+    """(kernel name, milliseconds) of the last encode/decode call."""
+    cap = 16
+    names = (ctypes.c_char_p * cap)()
+    ms = (ctypes.c_float * cap)()
+    n = lib().skv_kernel_times(names, ms, cap)
+    return [(names[i].decode(), float(ms[i])) for i in range(n)]
 
 
 def decode(tables: Tables, container: torch.Tensor, aux: torch.Tensor) -> torch.Tensor:
