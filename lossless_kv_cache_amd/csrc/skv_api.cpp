@@ -171,7 +171,7 @@ int skv_encode(const void* tables_blob, const skv_shape* s, const void* d_target
     a.target = d_target;
     a.aux = d_aux;
     a.scratch = w;
-    w += align256(n * raw);
+    w += align256(2 * n * raw);
     a.meta = reinterpret_cast<uint32_t*>(w);
     w += align256(4 * n);
     const uint64_t nb = (n + 1023) / 1024;

@@ -23,6 +23,7 @@ constexpr int kMaxDirect = 255;
 constexpr size_t kHeaderBytes = 64;
 constexpr size_t kTableRecord = 514;  // u16 n + u16 freq[256]
 constexpr size_t kStateBytes = 4 * kLanes;
+constexpr uint32_t kStreamHead = 4 * kLanes + 4;   // final states + word count
 constexpr uint64_t kRawBit = 1ull << 63;
 constexpr int kMaxTimedKernels = 16;
 
@@ -60,7 +61,7 @@ struct DevTables {
 struct EncodeLaunch {
     const void* target;
     const void* aux;
-    uint8_t* scratch;       // [n_streams][raw_bytes]: states at the front, words packed at the back
+    uint8_t* scratch;       // [n_streams][2 * raw_bytes]: states, escapes (back of 1st half), words (back of 2nd)
     uint32_t* meta;         // [n_streams] bytes | raw<<31
     uint32_t* block_sum;    // [n_blocks]
     uint64_t* block_off;    // [n_blocks]

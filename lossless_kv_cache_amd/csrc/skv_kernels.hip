@@ -124,14 +124,15 @@ __global__ __launch_bounds__(256) void encode_streams(EncodeLaunch a, DevTables 
     const uint32_t slab = uint32_t(sid / (uint64_t(g.ncg) * g.ntb));
     const uint32_t ch = cg * kLanes + lane;
     constexpr uint32_t EB = DT == SKV_E4M3 ? 1u : 2u;
-    constexpr uint32_t NCHUNK = DT == SKV_E4M3 ? 1u : 2u;
     constexpr uint32_t RAW = kSyms * EB;
-    constexpr uint32_t MAXW = (RAW - kStateBytes) / 2;
-    uint8_t* area = a.scratch + sid * RAW;
-    uint16_t* wend = reinterpret_cast<uint16_t*>(area) + RAW / 2 - 1;
+    constexpr uint32_t MAXW = (RAW - kStreamHead) / 2;     // more words or escapes mean a raw stream
+    constexpr uint32_t MAXE = (RAW - kStreamHead) / EB;
+    uint8_t* area = a.scratch + sid * (2 * RAW);
+    uint16_t* wend = reinterpret_cast<uint16_t*>(area + 2 * RAW) - 1;   // words, backwards
+    uint8_t* eend = area + RAW - EB;                                     // escaped values, backwards
     const uint32_t res_table = slab * g.C + ch;
 
-    uint32_t x = kStateLow, cnt = 0;
+    uint32_t x = kStateLow, cnt = 0, ecnt = 0;
     for (int k = kSteps - 1; k >= 0; --k) {
         uint32_t z, table;
         if (MODE == SKV_RESIDUAL) {
@@ -163,14 +164,18 @@ __global__ __launch_bounds__(256) void encode_streams(EncodeLaunch a, DevTables 
         const uint32_t n = t.n[table];
         const bool esc = z >= n;
         const uint32_t s = esc ? n : z;
-        if (__any(esc)) {
-            for (int q = int(NCHUNK) - 1; q >= 0; --q) {
-                emit_words(x, cnt, esc && x >= (16u << 20), lane, half, wend, MAXW);
-                if (esc) {
-                    const uint32_t chunk = (z >> (8 * q)) & 0xFFu;
-                    x = ((x >> 4) << 12) + (x & 15u) + 16u * chunk;
+        {
+            // escaped values keep decode order: ranked like the words, written backwards
+            const uint64_t b = __ballot(esc);
+            const uint32_t mine = uint32_t(b >> half);
+            if (esc) {
+                const uint32_t pos = ecnt + __popc(uint32_t((uint64_t)mine >> (lane + 1)));
+                if (pos < MAXE) {
+                    if (EB == 1) *(eend - pos) = uint8_t(z);
+                    else *reinterpret_cast<uint16_t*>(eend - 2 * pos) = uint16_t(z);
                 }
             }
+            ecnt += __popc(mine);
         }
         const uint2 e = t.enc[size_t(table) * 256 + s];
         const uint32_t f = e.y & 0x1FFFu, c = (e.y >> 13) & 0xFFFu, sh = e.y >> 25;
@@ -180,15 +185,17 @@ __global__ __launch_bounds__(256) void encode_streams(EncodeLaunch a, DevTables 
     }
     reinterpret_cast<uint32_t*>(area)[lane] = x;
     if (lane == 0) {
-        const uint32_t bytes = kStateBytes + 2 * cnt + 2 * (cnt & 1u);
-        a.meta[sid] = bytes >= RAW ? 0x80000000u : cnt;
+        const uint32_t bytes = (kStreamHead + 2 * cnt + EB * ecnt + 3) & ~3u;
+        a.meta[sid] = bytes >= RAW ? 0x80000000u : (cnt | (ecnt << 14));
     }
 }
 
 // --------------------------------------------------------------- index + compaction
-// meta word of a stream: bit 31 = stored raw, else the number of rANS words.
+// meta word of a stream: bit 31 = stored raw; else rANS word count in bits
+// 0..13 and escaped-value count in bits 14..27.
 __device__ __forceinline__ uint32_t meta_bytes(uint32_t m, uint32_t raw) {
-    return (m >> 31) ? raw : kStateBytes + 2 * m + 2 * (m & 1u);
+    const uint32_t eb = raw / kSyms;
+    return (m >> 31) ? raw : (kStreamHead + 2 * (m & 0x3FFFu) + eb * ((m >> 14) & 0x3FFFu) + 3) & ~3u;
 }
 
 __global__ __launch_bounds__(kScanBlock) void stream_block_sums(const uint32_t* meta, uint64_t n, uint32_t raw,
@@ -285,7 +292,7 @@ __global__ __launch_bounds__(kScanBlock) void place_streams(EncodeLaunch a, cons
         if (sid >= n) break;
         const uint32_t ms = a.meta[sid];
         uint8_t* dst = pay + offs[li];
-        const uint8_t* src = a.scratch + sid * RAW;
+        const uint8_t* src = a.scratch + sid * (2 * RAW);
         if (ms >> 31) {
             const uint32_t cg = uint32_t(sid % g.ncg);
             const uint32_t tb = uint32_t((sid / g.ncg) % g.ntb);
@@ -299,13 +306,19 @@ __global__ __launch_bounds__(kScanBlock) void place_streams(EncodeLaunch a, cons
                 else reinterpret_cast<uint16_t*>(dst)[e] = static_cast<const uint16_t*>(a.target)[idx];
             }
         } else {
-            // states from the front of the scratch area, words from its back
+            // states from the front of the scratch area, escapes before its middle, words at its back
+            const uint32_t cnt = ms & 0x3FFFu, ecnt = (ms >> 14) & 0x3FFFu;
             if (lane < 32) reinterpret_cast<uint32_t*>(dst)[lane] = reinterpret_cast<const uint32_t*>(src)[lane];
-            const uint32_t cnt = ms;
-            const uint16_t* ws = reinterpret_cast<const uint16_t*>(src) + RAW / 2 - cnt;
-            uint16_t* wd = reinterpret_cast<uint16_t*>(dst + kStateBytes);
-            const uint32_t slots = cnt + (cnt & 1u);
-            for (uint32_t q = lane; q < slots; q += 64) wd[q] = q < cnt ? ws[q] : uint16_t(0);
+            if (lane == 32) reinterpret_cast<uint32_t*>(dst)[32] = cnt;
+            const uint16_t* ws = reinterpret_cast<const uint16_t*>(src + 2 * RAW) - cnt;
+            uint16_t* wd = reinterpret_cast<uint16_t*>(dst + kStreamHead);
+            for (uint32_t q = lane; q < cnt; q += 64) wd[q] = ws[q];
+            const uint8_t* es = src + RAW - EB * ecnt;
+            uint8_t* ed = dst + kStreamHead + 2 * cnt;
+            const uint32_t eb = EB * ecnt;
+            const uint32_t total = (kStreamHead + 2 * cnt + eb + 3) & ~3u;
+            const uint32_t tail = total - (kStreamHead + 2 * cnt);
+            for (uint32_t q = lane; q < tail; q += 64) ed[q] = q < eb ? es[q] : uint8_t(0);
         }
     }
 }
@@ -338,7 +351,6 @@ __global__ __launch_bounds__(256) void decode_streams(DecodeLaunch a, DevTables 
     const uint32_t slab = uint32_t(sid / (uint64_t(g.ncg) * g.ntb));
     const uint32_t ch = cg * kLanes + lane;
     constexpr uint32_t EB = DT == SKV_E4M3 ? 1u : 2u;
-    constexpr uint32_t NCHUNK = DT == SKV_E4M3 ? 1u : 2u;
     constexpr uint32_t RAW = kSyms * EB;
     const uint64_t* index = reinterpret_cast<const uint64_t*>(a.in + kHeaderBytes);
     const uint8_t* pay = a.in + kHeaderBytes + 8 * (a.n_streams + 1);
@@ -366,15 +378,22 @@ __global__ __launch_bounds__(256) void decode_streams(DecodeLaunch a, DevTables 
         }
         return;
     }
-    if (size < kStateBytes || (size - kStateBytes) % 4 != 0) {
+    const uint8_t* sp = pay + off;
+    if (size < kStreamHead || size % 4 != 0) {
         if (lane == 0) atomicOr(a.status, 1u);
         return;
     }
-    uint32_t x = reinterpret_cast<const uint32_t*>(pay + off)[lane];
+    const uint32_t nw = reinterpret_cast<const uint32_t*>(sp)[32];
+    if (nw > (size - kStreamHead) / 2) {
+        if (lane == 0) atomicOr(a.status, 1u);
+        return;
+    }
+    uint32_t x = reinterpret_cast<const uint32_t*>(sp)[lane];
     if (x < kStateLow) bad = true;
-    const uint16_t* W = reinterpret_cast<const uint16_t*>(pay + off + kStateBytes);
-    const uint32_t navail = uint32_t((size - kStateBytes) / 2);
-    uint32_t p = 0;
+    const uint16_t* W = reinterpret_cast<const uint16_t*>(sp + kStreamHead);
+    const uint8_t* E = sp + kStreamHead + 2 * nw;
+    const uint32_t ecap = uint32_t((size - kStreamHead - 2 * nw) / EB);
+    uint32_t p = 0, ep = 0;
     const uint32_t res_table = slab * g.C + ch;
     for (uint32_t k = 0; k < uint32_t(kSteps); ++k) {
         const size_t oi = out_index(k);
@@ -399,23 +418,21 @@ __global__ __launch_bounds__(256) void decode_streams(DecodeLaunch a, DevTables 
         const uint32_t s = t.slot[size_t(table) * kM + slot];
         const uint32_t fcv = t.fc[size_t(table) * 256 + s];
         x = (fcv & 0xFFFFu) * (x >> kProbBits) + slot - (fcv >> 16);
-        refill(x, p, x < kStateLow, lane, half, W, navail, bad);
+        refill(x, p, x < kStateLow, lane, half, W, nw, bad);
         const bool esc = s == n;
         uint32_t z = s;
-        if (__any(esc)) {
-            uint32_t val = 0;
-            for (uint32_t q = 0; q < NCHUNK; ++q) {
-                if (esc) {
-                    const uint32_t sl = x & (kM - 1u);
-                    val |= (sl >> 4) << (8 * q);
-                    x = ((x >> kProbBits) << 4) + (sl & 15u);
-                }
-                refill(x, p, esc && x < kStateLow, lane, half, W, navail, bad);
-            }
+        {
+            const uint64_t b = __ballot(esc);
+            const uint32_t mine = uint32_t(b >> half);
             if (esc) {
-                if (val < n) bad = true;
-                z = val;
+                const uint32_t pos = ep + __popc(mine & ((1u << lane) - 1u));
+                uint32_t v = 0;
+                if (pos < ecap) v = EB == 1 ? uint32_t(E[pos]) : uint32_t(reinterpret_cast<const uint16_t*>(E)[pos]);
+                else bad = true;
+                if (v < n) bad = true;
+                z = v;
             }
+            ep += __popc(mine);
         }
         if (MODE == SKV_RESIDUAL) {
             if (DT == SKV_E4M3) {
@@ -429,8 +446,10 @@ __global__ __launch_bounds__(256) void decode_streams(DecodeLaunch a, DevTables 
             static_cast<int16_t*>(a.out)[oi] = int16_t(uint16_t(uint32_t(kk) + unzig(z)));
         }
     }
-    if (x != kStateLow) bad = true;
-    if (!(p == navail || (p + 1 == navail && W[p] == 0))) bad = true;
+    if (x != kStateLow || p != nw) bad = true;
+    const uint32_t used = kStreamHead + 2 * nw + EB * ep;
+    if (((used + 3) & ~3u) != size) bad = true;
+    else if (lane < size - used && sp[used + lane] != 0) bad = true;   // zero pad
     if (bad) atomicOr(a.status, 1u);
 }
 
@@ -502,7 +521,7 @@ hipError_t decode_all(const DecodeLaunch& a, const DevTables& t, hipStream_t st)
 uint64_t encode_work_bytes(uint64_t n_streams, uint32_t raw_bytes) {
     auto al = [](uint64_t v) { return (v + 255) & ~uint64_t(255); };
     const uint64_t nb = (n_streams + kScanBlock - 1) / kScanBlock;
-    return al(n_streams * raw_bytes) + al(4 * n_streams) + al(4 * nb) + al(8 * nb) + 256;
+    return al(2 * n_streams * raw_bytes) + al(4 * n_streams) + al(4 * nb) + al(8 * nb) + 256;
 }
 
 hipError_t build_dev_tables(const uint8_t* blob, DevTables* t, hipStream_t st) {

@@ -181,25 +181,26 @@ def _tables_arrays(tables):
     return n, fr
 
 
-def stream_encode(z, tab_of, tables, steps: int, nchunk: int) -> bytes:
-    """Encode one stream of `steps` x 32 symbol values with explicit tables."""
+def stream_encode(z, tab_of, tables, steps: int, ebytes: int) -> bytes:
+    """Encode one stream of `steps` x 32 symbol values with explicit tables;
+    escaped values take `ebytes` bytes each."""
     z = np.ascontiguousarray(z, dtype=np.uint32).reshape(-1)
     tab_of = np.ascontiguousarray(tab_of, dtype=np.uint32).reshape(-1)
     assert z.size == steps * 32 and tab_of.size == steps * 32
     n, fr = _tables_arrays(tables)
-    cap = 128 + 2 * steps * 32 * (1 + nchunk) + 4
+    cap = 128 + 4 + 4 * steps * 32 + 4
     out = np.zeros(cap, dtype=np.uint8)
-    nb = lib().skvo_stream_encode_ext(steps, nchunk, len(tables), _ptr(n), _ptr(fr), _ptr(tab_of), _ptr(z), _ptr(out), cap)
+    nb = lib().skvo_stream_encode_ext(steps, ebytes, len(tables), _ptr(n), _ptr(fr), _ptr(tab_of), _ptr(z), _ptr(out), cap)
     return out[:nb].tobytes()
 
 
-def stream_decode(data: bytes, tab_of, tables, steps: int, nchunk: int):
+def stream_decode(data: bytes, tab_of, tables, steps: int, ebytes: int):
     """Returns (rc, z) for one stream."""
     tab_of = np.ascontiguousarray(tab_of, dtype=np.uint32).reshape(-1)
     n, fr = _tables_arrays(tables)
     buf = np.frombuffer(data, dtype=np.uint8).copy() if len(data) else np.zeros(1, np.uint8)
     z = np.zeros(steps * 32, dtype=np.uint32)
-    rc = lib().skvo_stream_decode_ext(steps, nchunk, len(tables), _ptr(n), _ptr(fr), _ptr(tab_of), _ptr(buf), len(data), _ptr(z))
+    rc = lib().skvo_stream_decode_ext(steps, ebytes, len(tables), _ptr(n), _ptr(fr), _ptr(tab_of), _ptr(buf), len(data), _ptr(z))
     return rc, z
 
 

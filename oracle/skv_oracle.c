@@ -31,8 +31,8 @@
  * The pages fix none of the bit-level details; every such choice below is a
  * reading of the pages (rANS with 12-bit probabilities, 32 interleaved
  * lanes x 128 steps per stream, ordered-integer residual with zigzag, escape
- * symbol with uniform 8-bit chunks, raw fallback, container and table-blob
- * layout).  The rANS steps follow the published definition of range
+ * symbol whose raw value is stored in the stream's escape region, raw
+ * fallback, container and table-blob layout).  The rANS steps follow the published definition of range
  * asymmetric numeral systems (J. Duda, "Asymmetric numeral systems",
  * arXiv:1311.2540) with word-wise renormalization and lane interleaving as
  * in F. Giesen, "Interleaved entropy coders" (arXiv:1402.3392).
@@ -233,34 +233,32 @@ uint32_t skvo_rans_pop(uint32_t* x, const uint32_t* freq, const uint32_t* cum, u
 /* One stream: 32 interleaved lanes x `steps` steps.                   */
 /*   z[k*32 + i]   symbol value of lane i at step k                     */
 /*   tab[k*32 + i] table used by lane i at step k                       */
-/*   nchunk        raw 8-bit chunks that follow an ESC (2 for 16-bit,  */
-/*                 1 for 8-bit elements)                                */
-/* Decode order per step: every lane pops its main symbol, then the     */
-/* lanes needing a word refill in lane order; then, chunk by chunk, the */
-/* escaped lanes pop a chunk (uniform frequency 16) and refill in lane  */
-/* order.  The encoder runs that order backwards and finally reverses   */
-/* its word list.                                                       */
-/* Layout: 32 final states (u32, lane order), the words (u16), one zero */
-/* u16 if the word count is odd.  Returns the byte count.              */
+/*   ebytes        bytes of an escaped value (2 for 16-bit elements,    */
+/*                 1 for 8-bit ones)                                    */
+/* A value z < n is coded directly as symbol z; a larger one codes the  */
+/* ESC symbol (index n) and its raw value goes to the stream's escape   */
+/* region.  Decode order per step: every lane pops its symbol, then the */
+/* lanes whose state fell below 2^16 take the next word, in lane order. */
+/* The encoder pushes the symbols in exactly the reverse order and      */
+/* finally reverses its word list.                                      */
+/* Layout: 32 final states (u32, lane order) | u32 word count | words   */
+/* (u16) | escaped values (u8 or u16) in decode order, i.e. by step,    */
+/* then lane | zero bytes up to a multiple of 4.  Returns the size.     */
 /* ------------------------------------------------------------------ */
-size_t skvo_stream_encode(int steps, int nchunk, const uint32_t* z, const skvo_table* const* tab,
+static size_t pad4(size_t n) { return (n + 3) & ~(size_t)3; }
+
+size_t skvo_stream_encode(int steps, int ebytes, const uint32_t* z, const skvo_table* const* tab,
                           uint8_t* out, size_t cap) {
     uint32_t x[SKVO_LANES];
-    size_t maxw = (size_t)steps * SKVO_LANES * (size_t)(1 + nchunk);
-    uint16_t* w = (uint16_t*)malloc(maxw * sizeof(uint16_t) + 2);
-    size_t nw = 0;
+    size_t nsym = (size_t)steps * SKVO_LANES;
+    uint16_t* w = (uint16_t*)malloc(nsym * sizeof(uint16_t) + 2);
+    uint32_t* esc = (uint32_t*)malloc(nsym * sizeof(uint32_t) + 4);
+    size_t nw = 0, ne = 0;
+    /* escaped values, in decode order */
+    for (size_t j = 0; j < nsym; ++j)
+        if (z[j] >= tab[j]->n) esc[ne++] = z[j];
     for (int i = 0; i < SKVO_LANES; ++i) x[i] = SKVO_L;
     for (int k = steps - 1; k >= 0; --k) {
-        for (int q = nchunk - 1; q >= 0; --q) {
-            for (int i = SKVO_LANES - 1; i >= 0; --i) {
-                const skvo_table* t = tab[k * SKVO_LANES + i];
-                uint32_t zz = z[k * SKVO_LANES + i];
-                if (zz >= t->n) {
-                    uint32_t chunk = (zz >> (8 * q)) & 0xFFu;
-                    if (skvo_rans_put(&x[i], 16, 16 * chunk, &w[nw])) ++nw;
-                }
-            }
-        }
         for (int i = SKVO_LANES - 1; i >= 0; --i) {
             const skvo_table* t = tab[k * SKVO_LANES + i];
             uint32_t zz = z[k * SKVO_LANES + i];
@@ -268,60 +266,61 @@ size_t skvo_stream_encode(int steps, int nchunk, const uint32_t* z, const skvo_t
             if (skvo_rans_put(&x[i], t->freq[s], t->cum[s], &w[nw])) ++nw;
         }
     }
-    size_t bytes = 4 * SKVO_LANES + 2 * nw + ((nw & 1) ? 2 : 0);
+    size_t head = 4 * SKVO_LANES + 4;
+    size_t bytes = pad4(head + 2 * nw + (size_t)ebytes * ne);
     if (bytes <= cap) {
+        memset(out, 0, bytes);
         for (int i = 0; i < SKVO_LANES; ++i) put32(out + 4 * i, x[i]);
-        uint8_t* o = out + 4 * SKVO_LANES;
+        put32(out + 4 * SKVO_LANES, (uint32_t)nw);
+        uint8_t* o = out + head;
         for (size_t j = 0; j < nw; ++j) put16(o + 2 * j, w[nw - 1 - j]);
-        if (nw & 1) put16(o + 2 * nw, 0);
+        o += 2 * nw;
+        for (size_t j = 0; j < ne; ++j) {
+            if (ebytes == 1) o[j] = (uint8_t)esc[j];
+            else put16(o + 2 * j, esc[j]);
+        }
     }
     free(w);
+    free(esc);
     return bytes;
 }
 
 /* Returns E_OK and fills z[k*32+i], or E_CORRUPT when the stream does not
- * decode to a canonical encoding that consumes exactly its words. */
-int skvo_stream_decode(int steps, int nchunk, const uint8_t* in, size_t nbytes,
+ * decode to a canonical encoding that uses exactly its words and escapes. */
+int skvo_stream_decode(int steps, int ebytes, const uint8_t* in, size_t nbytes,
                        const skvo_table* const* tab, uint32_t* z) {
-    if (nbytes < 4 * SKVO_LANES || ((nbytes - 4 * SKVO_LANES) % 4) != 0) return E_CORRUPT;
+    size_t head = 4 * SKVO_LANES + 4;
+    if (nbytes < head || (nbytes % 4) != 0) return E_CORRUPT;
     uint32_t x[SKVO_LANES];
     for (int i = 0; i < SKVO_LANES; ++i) {
         x[i] = get32(in + 4 * i);
         if (x[i] < SKVO_L) return E_CORRUPT;
     }
-    const uint8_t* W = in + 4 * SKVO_LANES;
-    size_t navail = (nbytes - 4 * SKVO_LANES) / 2, p = 0;
+    size_t nw = get32(in + 4 * SKVO_LANES);
+    if (nw > (nbytes - head) / 2) return E_CORRUPT;
+    const uint8_t* W = in + head;
+    const uint8_t* E = W + 2 * nw;
+    size_t ecap = (nbytes - head - 2 * nw) / (size_t)ebytes;
+    size_t p = 0, e = 0;
     for (int k = 0; k < steps; ++k) {
-        uint32_t sym[SKVO_LANES], val[SKVO_LANES];
+        uint32_t sym[SKVO_LANES];
         for (int i = 0; i < SKVO_LANES; ++i) {
             const skvo_table* t = tab[k * SKVO_LANES + i];
             sym[i] = skvo_rans_pop(&x[i], t->freq, t->cum, t->n + 1);
-            val[i] = 0;
         }
         for (int i = 0; i < SKVO_LANES; ++i)
             if (x[i] < SKVO_L) {
-                if (p >= navail) return E_CORRUPT;
+                if (p >= nw) return E_CORRUPT;
                 x[i] = (x[i] << 16) | get16(W + 2 * p++);
             }
-        for (int q = 0; q < nchunk; ++q) {
-            for (int i = 0; i < SKVO_LANES; ++i) {
-                if (sym[i] != tab[k * SKVO_LANES + i]->n) continue;
-                uint32_t slot = x[i] & (SKVO_M - 1u);
-                uint32_t chunk = slot / 16;      /* uniform: frequency 16, start 16*chunk */
-                x[i] = 16 * (x[i] >> 12) + slot - 16 * chunk;
-                val[i] |= chunk << (8 * q);
-            }
-            for (int i = 0; i < SKVO_LANES; ++i)
-                if (sym[i] == tab[k * SKVO_LANES + i]->n && x[i] < SKVO_L) {
-                    if (p >= navail) return E_CORRUPT;
-                    x[i] = (x[i] << 16) | get16(W + 2 * p++);
-                }
-        }
         for (int i = 0; i < SKVO_LANES; ++i) {
             uint32_t n = tab[k * SKVO_LANES + i]->n;
             if (sym[i] == n) {
-                if (val[i] < n) return E_CORRUPT;   /* a canonical encoder codes it directly */
-                z[k * SKVO_LANES + i] = val[i];
+                if (e >= ecap) return E_CORRUPT;
+                uint32_t v = (ebytes == 1) ? E[e] : get16(E + 2 * e);
+                ++e;
+                if (v < n) return E_CORRUPT;   /* a canonical encoder codes it directly */
+                z[k * SKVO_LANES + i] = v;
             } else {
                 z[k * SKVO_LANES + i] = sym[i];
             }
@@ -329,9 +328,12 @@ int skvo_stream_decode(int steps, int nchunk, const uint8_t* in, size_t nbytes,
     }
     for (int i = 0; i < SKVO_LANES; ++i)
         if (x[i] != SKVO_L) return E_CORRUPT;
-    if (p == navail) return E_OK;
-    if (p + 1 == navail && get16(W + 2 * p) == 0) return E_OK;   /* pad word */
-    return E_CORRUPT;
+    if (p != nw) return E_CORRUPT;
+    size_t used = head + 2 * nw + (size_t)ebytes * e;
+    if (pad4(used) != nbytes) return E_CORRUPT;
+    for (size_t j = used; j < nbytes; ++j)
+        if (in[j] != 0) return E_CORRUPT;
+    return E_OK;
 }
 
 /* ------------------------------------------------------------------ */
@@ -502,8 +504,9 @@ static size_t encode_one(const skvo_shape* s, const skvo_table* tabs, const void
     int eb = elem_bytes(s->dtype);
     size_t rawb = (size_t)SKVO_SYMS * eb;
     gather_stream(s, tabs, tgt, aux, id, z, tp, 1);
-    uint8_t* tmp = (uint8_t*)malloc(4 * SKVO_LANES + 2 * (size_t)SKVO_SYMS * 3 + 4);
-    size_t nb = skvo_stream_encode(SKVO_STEPS, eb, z, tp, tmp, 4 * SKVO_LANES + 2 * (size_t)SKVO_SYMS * 3 + 4);
+    const size_t tcap = 4 * SKVO_LANES + 4 + 4 * (size_t)SKVO_SYMS + 4;
+    uint8_t* tmp = (uint8_t*)malloc(tcap);
+    size_t nb = skvo_stream_encode(SKVO_STEPS, eb, z, tp, tmp, tcap);
     if (nb >= rawb) {
         /* Raw fallback: the stream's target elements in (step, lane) order. */
         stream_pos sp = stream_at(s, id);
@@ -861,8 +864,9 @@ int64_t skvo_encode_tile(const uint8_t* blob, size_t blob_bytes, const skvo_shap
         }
     }
     size_t rawb = (size_t)SKVO_SYMS * eb;
-    uint8_t* tmp = (uint8_t*)malloc(4 * SKVO_LANES + 6 * (size_t)SKVO_SYMS + 4);
-    size_t nb = skvo_stream_encode(SKVO_STEPS, eb, z, tp, tmp, 4 * SKVO_LANES + 6 * (size_t)SKVO_SYMS + 4);
+    const size_t tcap = 4 * SKVO_LANES + 4 + 4 * (size_t)SKVO_SYMS + 4;
+    uint8_t* tmp = (uint8_t*)malloc(tcap);
+    size_t nb = skvo_stream_encode(SKVO_STEPS, eb, z, tp, tmp, tcap);
     if (nb >= rawb) {
         memcpy(out, tile_t, rawb);   /* (step, lane) order = tile order */
         *raw = 1;
@@ -900,23 +904,23 @@ static skvo_table* make_tables(int ntab, const uint32_t* tabs_n, const uint32_t*
     return t;
 }
 
-int64_t skvo_stream_encode_ext(int steps, int nchunk, int ntab, const uint32_t* tabs_n, const uint32_t* tabs_freq,
+int64_t skvo_stream_encode_ext(int steps, int ebytes, int ntab, const uint32_t* tabs_n, const uint32_t* tabs_freq,
                                const uint32_t* tab_of, const uint32_t* z, uint8_t* out, uint64_t cap) {
     skvo_table* t = make_tables(ntab, tabs_n, tabs_freq);
     const skvo_table** tp = (const skvo_table**)malloc((size_t)steps * SKVO_LANES * sizeof(*tp));
     for (int j = 0; j < steps * SKVO_LANES; ++j) tp[j] = &t[tab_of[j]];
-    size_t nb = skvo_stream_encode(steps, nchunk, z, tp, out, cap);
+    size_t nb = skvo_stream_encode(steps, ebytes, z, tp, out, cap);
     free(tp);
     free(t);
     return (int64_t)nb;
 }
 
-int skvo_stream_decode_ext(int steps, int nchunk, int ntab, const uint32_t* tabs_n, const uint32_t* tabs_freq,
+int skvo_stream_decode_ext(int steps, int ebytes, int ntab, const uint32_t* tabs_n, const uint32_t* tabs_freq,
                            const uint32_t* tab_of, const uint8_t* in, uint64_t nbytes, uint32_t* z) {
     skvo_table* t = make_tables(ntab, tabs_n, tabs_freq);
     const skvo_table** tp = (const skvo_table**)malloc((size_t)steps * SKVO_LANES * sizeof(*tp));
     for (int j = 0; j < steps * SKVO_LANES; ++j) tp[j] = &t[tab_of[j]];
-    int rc = skvo_stream_decode(steps, nchunk, in, nbytes, tp, z);
+    int rc = skvo_stream_decode(steps, ebytes, in, nbytes, tp, z);
     free(tp);
     free(t);
     return rc;

@@ -143,7 +143,10 @@ def test_corruption_and_wrong_tables(skv, orc):
         b = int(idx[s + 1] & np.uint64((1 << 63) - 1))
         if idx[s] >> np.uint64(63):
             continue
-        pos = head + int(rng.integers(a + 128, b))
+        # the coded part (states, word count, words); escaped raw values and raw
+        # streams carry no redundancy, so a flip there is not detectable
+        nw = int.from_bytes(good[head + a + 128:head + a + 132].tobytes(), "little")
+        pos = head + int(rng.integers(a, a + 132 + 2 * nw))
         bad[pos] ^= np.uint8(1 << int(rng.integers(0, 8)))
         say(f"[parity] corrupt trial {trial}: stream {s} byte {pos}")
         with pytest.raises(skv.SkvError) as e:

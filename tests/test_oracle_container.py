@@ -212,7 +212,8 @@ def test_corruption_is_detected(orc, cfg0):
         s = int(rng.integers(0, n))
         a = int(idx[s] & np.uint64((1 << 63) - 1))
         b = int(idx[s + 1] & np.uint64((1 << 63) - 1))
-        pos = head + int(rng.integers(a + 128, b))          # a payload word
+        nw = int.from_bytes(c[head + a + 128:head + a + 132], "little")
+        pos = head + int(rng.integers(a, a + 132 + 2 * nw))  # states, word count or a word
         flip = bytearray(c)
         flip[pos] ^= 1 << int(rng.integers(0, 8))
         assert orc.decode_rc(blob, bytes(flip), p, out) == orc.E_CORRUPT
@@ -250,11 +251,15 @@ def test_coded_size_within_half_percent_of_cross_entropy(orc, cfg0):
             bits = np.log2(4096.0 / f.astype(np.float64))
             zz = z[kv, :, ch]
             ideal += bits[np.minimum(zz, n_j)].sum() + 16.0 * (zz >= n_j).sum()
-    coded = pad_slack = 0.0
+    coded = 0.0
+    nesc_total = 0
     for s in range(n):
         data, raw = stream_bytes(idx, pay, s)
         assert not raw
         st = np.frombuffer(data[:128], np.uint32).astype(np.float64)
-        coded += 16.0 * ((len(data) - 128) // 2) + np.log2(st / 65536.0).sum()
-        pad_slack += 16.0                       # a pad word is counted as a word
-    assert ideal * 0.995 <= coded <= ideal * 1.005 + pad_slack
+        nw = int.from_bytes(data[128:132], "little")
+        nesc = (len(data) - 132 - 2 * nw) // 2          # u16 escapes; the pad is at most one u16
+        coded += 16.0 * nw + np.log2(st / 65536.0).sum() + 16.0 * nesc
+        nesc_total += nesc
+    slack = 16.0 * n                                    # a pad u16 counted as an escape
+    assert ideal * 0.995 <= coded <= ideal * 1.005 + slack

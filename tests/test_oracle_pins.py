@@ -52,48 +52,63 @@ def test_e3_lane_order(orc):
     z = np.array([[32 - i for i in range(32)]] * steps, dtype=np.uint32)
     tab = (33, [4064] + [1] * 32 + [0])
     data = orc.stream_encode(z, np.zeros(steps * 32, np.uint32), [tab], steps, 2)
-    words = np.frombuffer(data[128:], dtype=np.uint16)
-    assert list(words[: len(e["words"])]) == e["words"]
-    assert len(data) == 128 + 2 * len(e["words"])
+    assert int.from_bytes(data[128:132], "little") == len(e["words"])
+    words = np.frombuffer(data[132:], dtype=np.uint16)
+    assert list(words) == e["words"]
+    assert len(data) == e["bytes"]
     states = np.frombuffer(data[:128], dtype=np.uint32)
     assert list(states) == [e["state_lane0"] - i for i in range(32)]
     rc, zz = orc.stream_decode(data, np.zeros(steps * 32, np.uint32), [tab], steps, 2)
     assert rc == 0 and np.array_equal(zz, z.reshape(-1))
 
 
-def test_e4_escape_chunks(orc):
-    e = _load("rans_pins.json")["E4"]
-    z = np.zeros(32, dtype=np.uint32)
-    z[0] = e["z_lane0"]
+@pytest.mark.parametrize("name", ["E4", "E5"])
+def test_escape_region(orc, name):
+    e = _load("rans_pins.json")[name]
+    steps = e["steps"]
+    z = np.zeros((steps, 32), dtype=np.uint32)
+    for key, v in e["z"].items():
+        k, i = (0, int(key)) if "," not in key else map(int, key.split(","))
+        z[k, i] = v
     tab = (1, e["table"])
-    data = orc.stream_encode(z, np.zeros(32, np.uint32), [tab], e["steps"], e["nchunk"])
+    data = orc.stream_encode(z, np.zeros(steps * 32, np.uint32), [tab], steps, e["ebytes"])
     assert len(data) == e["bytes"]
     st = np.frombuffer(data[:128], dtype=np.uint32)
-    assert st[0] == e["state_lane0"] and all(st[1:] == e["state_other"])
-    w = np.frombuffer(data[128:], dtype=np.uint16)
-    assert list(w) == e["words"] + [0]          # odd word count -> one zero pad word
-    rc, zz = orc.stream_decode(data, np.zeros(32, np.uint32), [tab], 1, 2)
-    assert rc == 0 and np.array_equal(zz, z)
+    for i in range(32):
+        assert st[i] == e["states"].get(str(i), e["states"]["other"]), i
+    nw = int.from_bytes(data[128:132], "little")
+    assert nw == len(e["words"])
+    esc = np.frombuffer(data[132 + 2 * nw:132 + 2 * nw + 2 * len(e["escapes"])], dtype=np.uint16)
+    assert list(esc) == e["escapes"]
+    assert not any(data[132 + 2 * nw + 2 * len(e["escapes"]):])     # zero pad
+    rc, zz = orc.stream_decode(data, np.zeros(steps * 32, np.uint32), [tab], steps, e["ebytes"])
+    assert rc == 0 and np.array_equal(zz, z.reshape(-1))
+    # any change in the pad or a truncated escape region is rejected
+    if len(data) > 132 + 2 * nw + 2 * len(e["escapes"]):
+        bad = bytearray(data)
+        bad[-1] ^= 1
+        rc, _ = orc.stream_decode(bytes(bad), np.zeros(steps * 32, np.uint32), [tab], steps, e["ebytes"])
+        assert rc == orc.E_CORRUPT
 
 
 def test_uniform_table_is_bit_insertion(orc):
-    """All 256 values at frequency 16 (255 direct + ESC + one 8-bit chunk):
-    each put shifts the state left by exactly 8 bits, each word removes 16, so
-    sum_i (floor(log2 x_i) - 16) = 8 * puts - 16 * words, and every symbol
-    costs exactly 8 bits."""
+    """255 direct values at frequency 16 plus ESC at 16: each put shifts the
+    state left by exactly 8 bits and each word removes 16, so
+    sum_i (floor(log2 x_i) - 16) = 8 * symbols - 16 * words; escaped values
+    (255) are stored raw, one byte each."""
     rng = np.random.default_rng(1)
     steps = 16
     z = rng.integers(0, 256, size=steps * 32).astype(np.uint32)
     tab = (255, [16] * 256)
     data = orc.stream_encode(z, np.zeros(steps * 32, np.uint32), [tab], steps, 1)
     nesc = int((z == 255).sum())
-    puts = steps * 32 + nesc
     st = np.frombuffer(data[:128], dtype=np.uint32).astype(np.int64)
-    nbytes_words = len(data) - 128
+    nw = int.from_bytes(data[128:132], "little")
     bitlen = sum(int(x).bit_length() - 17 for x in st)
-    # candidate word counts: with or without the pad word
-    cands = [nbytes_words // 2, nbytes_words // 2 - 1]
-    assert any(bitlen == 8 * puts - 16 * w for w in cands)
+    assert bitlen == 8 * steps * 32 - 16 * nw
+    assert len(data) == (132 + 2 * nw + nesc + 3) // 4 * 4
+    esc = data[132 + 2 * nw:132 + 2 * nw + nesc]
+    assert list(esc) == [255] * nesc
     rc, zz = orc.stream_decode(data, np.zeros(steps * 32, np.uint32), [tab], steps, 1)
     assert rc == 0 and np.array_equal(zz, z)
     # closed form of one put: x' = ((x >> 4) << 12) | (s << 4) | (x & 15)
