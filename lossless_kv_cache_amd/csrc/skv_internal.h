@@ -52,8 +52,9 @@ inline uint64_t rd64(const uint8_t* p) { return uint64_t(rd32(p)) | (uint64_t(rd
 // Expanded tables resident in HBM (built once per blob and device).
 struct DevTables {
     uint32_t n_tables = 0;
+    uint32_t max_n = 0;            // largest direct-symbol count over all tables
     uint32_t* n = nullptr;         // [n_tables] direct-symbol count (ESC index)
-    uint2* enc = nullptr;          // [n_tables][256] {divisor magic, freq | cum<<13 | shift<<25}
+    uint4* enc = nullptr;          // [n_tables][256] {freq<<20, divisor magic, 4096-freq, cum<<16 | shift}
     uint32_t* fc = nullptr;        // [n_tables][256] freq | cum<<16
     uint8_t* slot = nullptr;       // [n_tables][4096] slot -> symbol
 };

@@ -17,6 +17,10 @@
 // and checkerboard mode shifts the table by a mean from the side input and,
 // on odd tokens, from the two decoded even neighbours (same section).
 // Everything on the device is integer arithmetic.
+#include <algorithm>
+#include <cstdio>
+#include <cstdlib>
+
 #include "skv_internal.h"
 
 namespace skv {
@@ -62,7 +66,7 @@ __device__ __forceinline__ uint32_t zig8(uint32_t r) { return ((r << 1) ^ (0u - 
 __device__ __forceinline__ uint32_t unzig(uint32_t z) { return (z >> 1) ^ (0u - (z & 1u)); }   // mod 2^32
 
 // --------------------------------------------------------------- tables
-__global__ __launch_bounds__(256) void expand_tables(const uint8_t* rec, uint32_t* tn, uint2* enc, uint32_t* fc,
+__global__ __launch_bounds__(256) void expand_tables(const uint8_t* rec, uint32_t* tn, uint4* enc, uint32_t* fc,
                                                      uint8_t* slot) {
     __shared__ uint32_t cum[257];
     const uint32_t j = blockIdx.x, tid = threadIdx.x;
@@ -80,13 +84,19 @@ __global__ __launch_bounds__(256) void expand_tables(const uint8_t* rec, uint32_
     }
     const uint32_t c = cum[tid];
     if (tid == 0) tn[j] = n;
-    uint2 e = make_uint2(0u, 0u);
+    // encode entry: renormalization bound, divisor magic, 4096 - f, start | shift.
+    // floor(x / f) = (x + mulhi(x, magic)) >> shift for every 32-bit x, with
+    // shift = ceil(log2 f) and magic = ceil(2^(32+shift) / f) - 2^32
+    // (Granlund & Montgomery, division by invariant integers).
+    uint4 e = make_uint4(0u, 0u, 0u, 0u);
     if (tid <= n) {
         uint32_t sh = 0;
-        while ((1u << sh) < f) ++sh;                                    // ceil(log2 f)
-        const uint64_t m = ((1ull << (32 + sh)) + f - 1) / f;           // ceil(2^(32+sh) / f), in (2^32, 2^33]
-        e.x = uint32_t(m - (1ull << 32));
-        e.y = f | (c << 13) | (sh << 25);
+        while ((1u << sh) < f) ++sh;
+        const uint64_t m = ((1ull << (32 + sh)) + f - 1) / f;
+        e.x = f << 20;
+        e.y = uint32_t(m - (1ull << 32));
+        e.z = kM - f;
+        e.w = (c << 16) | sh;
     }
     enc[size_t(j) * 256 + tid] = e;
     fc[size_t(j) * 256 + tid] = f | (c << 16);
@@ -177,11 +187,10 @@ __global__ __launch_bounds__(256) void encode_streams(EncodeLaunch a, DevTables 
             }
             ecnt += __popc(mine);
         }
-        const uint2 e = t.enc[size_t(table) * 256 + s];
-        const uint32_t f = e.y & 0x1FFFu, c = (e.y >> 13) & 0xFFFu, sh = e.y >> 25;
-        emit_words(x, cnt, x >= (f << 20), lane, half, wend, MAXW);
-        const uint32_t qt = uint32_t((uint64_t(x) + __umulhi(x, e.x)) >> sh);   // floor(x / f)
-        x = x + qt * (kM - f) + c;
+        const uint4 e = t.enc[size_t(table) * 256 + s];
+        emit_words(x, cnt, x >= e.x, lane, half, wend, MAXW);
+        const uint32_t qt = uint32_t((uint64_t(x) + __umulhi(x, e.y)) >> (e.w & 31u));   // floor(x / f)
+        x = x + qt * e.z + (e.w >> 16);
     }
     reinterpret_cast<uint32_t*>(area)[lane] = x;
     if (lane == 0) {
@@ -453,6 +462,381 @@ __global__ __launch_bounds__(256) void decode_streams(DecodeLaunch a, DevTables 
     if (bad) atomicOr(a.status, 1u);
 }
 
+// =============================================================== LDS kernels
+// Residual mode.  A workgroup owns one channel group (32 channels = one stream
+// width) of one slab over a range of token blocks, so the 32 lane tables sit
+// in LDS for the workgroup's lifetime.  Each thread runs lane `lane` of S
+// streams at once (independent rANS chains interleaved for latency hiding).
+// Blocks are numbered so that the channel groups sharing 128-byte rows of the
+// cache land on the same XCD back to back (dispatch is round-robin over the
+// 8 XCDs), which lets that XCD's L2 serve the other quarters or halves of each
+// line.
+struct LdsGeo {
+    uint32_t groups;   // line groups = slabs x token-block chunks x (channel groups / G)
+    uint32_t G;        // channel groups per line group
+    uint32_t ntbc;     // token-block chunks per slab
+    uint32_t tbc;      // token blocks per chunk
+};
+
+struct LdsPos {
+    uint32_t slab, cg, tb_begin, tb_end;
+    bool valid;
+};
+
+__device__ __forceinline__ LdsPos lds_position(const Geo& geo, const LdsGeo& lg) {
+    const uint32_t b = blockIdx.x;
+    const uint32_t g = (b / (8u * lg.G)) * 8u + (b % 8u);
+    LdsPos r;
+    r.valid = g < lg.groups;
+    const uint32_t c = (b / 8u) % lg.G;
+    const uint32_t ncgg = geo.ncg / lg.G;
+    r.cg = (g % ncgg) * lg.G + c;
+    const uint32_t rest = g / ncgg;
+    const uint32_t tbc = rest % lg.ntbc;
+    r.slab = rest / lg.ntbc;
+    r.tb_begin = tbc * lg.tbc;
+    r.tb_end = min(r.tb_begin + lg.tbc, geo.ntb);
+    return r;
+}
+
+// Streams of one round: the token blocks tb0, tb0+1, ... of this half-wave.
+// FULL rounds have all S streams present, so the loop body needs no
+// activity predicates; partial rounds (short token ranges) use ACT = true.
+
+// Decoder LDS layout: static LUTs (e4m3 only) and, dynamically, (freq, start)
+// words [fs + 1][32] then slot->symbol maps [32][4096 >> HALF].  With HALF, a map entry covers a
+// pair of slots and holds the symbol of the even one; the odd slot belongs to
+// the next symbol exactly when that symbol starts there.
+template <uint32_t DT, int S, int D, bool ACT, bool HALF>
+__device__ __forceinline__ void decode_round(const DecodeLaunch& a, const LdsPos& ps, const Geo& geo, uint32_t tb0,
+                                             const uint8_t* lut, const uint32_t* lfc, const uint8_t* lslot,
+                                             uint32_t n, bool& bad) {
+    constexpr uint32_t EB = DT == SKV_E4M3 ? 1u : 2u;
+    constexpr uint32_t RAW = kSyms * EB;
+    const uint32_t lane = threadIdx.x & 31u, half = threadIdx.x & 32u;
+    const uint32_t ltmask = (1u << lane) - 1u;
+    const uint64_t* index = reinterpret_cast<const uint64_t*>(a.in + kHeaderBytes);
+    const uint8_t* pay = a.in + kHeaderBytes + 8 * (a.n_streams + 1);
+    const uint32_t rowb = geo.C * EB;                      // bytes per cache row
+    // slab bases are uniform over the workgroup; lanes add 32-bit offsets
+    const size_t slab_b = size_t(ps.slab) * geo.T * rowb + size_t(ps.cg) * kLanes * EB;
+    const uint8_t* aux = static_cast<const uint8_t*>(a.aux) + slab_b;
+    uint8_t* out = static_cast<uint8_t*>(a.out) + slab_b;
+    const uint8_t* my_slot = lslot + lane * (kM >> (HALF ? 1 : 0));
+
+    // Per stream: state, word / escape cursors and bounds.  A stream that is
+    // absent, raw or malformed runs as an idle chain: its escape symbol can never
+    // match (256), its cursors never trip the checks and its reads stay inside the
+    // payload.  Only partial rounds need to mask stores.
+    uint32_t x[S], p[S], ep[S], nwc[S], nwl[S], ecc[S], ecl[S], ns[S], off[S], sz[S];
+    const uint16_t* W[S];
+    const uint8_t* E[S];
+    bool act[S], rawc[S];
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+        const uint32_t tb = tb0 + s;
+        const bool present = !ACT || tb < ps.tb_end;
+        off[s] = (present ? tb : tb0) * kSteps * rowb + lane * EB;
+        x[s] = kStateLow;
+        p[s] = ep[s] = 0;
+        nwc[s] = ecc[s] = 0xFFFFFFFFu;       // check bounds (idle: never reached)
+        nwl[s] = ecl[s] = 0;                 // clamp bounds for reads
+        ns[s] = 256;
+        sz[s] = 0;
+        W[s] = reinterpret_cast<const uint16_t*>(pay);
+        E[s] = pay;
+        act[s] = rawc[s] = false;
+        if (!present) continue;
+        const uint64_t sid = (uint64_t(ps.slab) * geo.ntb + tb) * geo.ncg + ps.cg;
+        const uint64_t e0 = index[sid], e1 = index[sid + 1];
+        const uint64_t o = e0 & ~kRawBit, end = e1 & ~kRawBit;
+        const uint64_t size = end - o;
+        const uint8_t* sp = pay + o;
+        if (end < o || end > a.payload_bytes) {
+            bad = true;
+            continue;
+        }
+        if (e0 & kRawBit) {
+            if (size != RAW) bad = true;
+            else rawc[s] = true;             // copied after the coded streams of the round
+            E[s] = sp;
+            continue;
+        }
+        uint32_t nw = 0;
+        bool ok = size >= kStreamHead && size % 4 == 0;
+        if (ok) {
+            nw = reinterpret_cast<const uint32_t*>(sp)[32];
+            ok = nw <= (size - kStreamHead) / 2;
+        }
+        if (!ok) {
+            bad = true;
+            continue;
+        }
+        act[s] = true;
+        x[s] = reinterpret_cast<const uint32_t*>(sp)[lane];
+        if (x[s] < kStateLow) bad = true;
+        sz[s] = uint32_t(size);
+        const uint32_t ecap = uint32_t((size - kStreamHead - 2 * nw) / EB);
+        nwc[s] = nw;
+        ecc[s] = ecap;
+        nwl[s] = nw ? nw - 1 : 0;
+        ecl[s] = ecap ? ecap - 1 : 0;
+        ns[s] = n;
+        W[s] = nw ? reinterpret_cast<const uint16_t*>(sp + kStreamHead) : reinterpret_cast<const uint16_t*>(sp);
+        E[s] = ecap ? sp + kStreamHead + 2 * nw : sp;
+    }
+
+    uint32_t pbuf[S][D];
+#pragma unroll
+    for (int s = 0; s < S; ++s)
+#pragma unroll
+        for (int d = 0; d < D; ++d)
+            pbuf[s][d] = EB == 1 ? uint32_t(aux[off[s] + d * rowb])
+                                 : uint32_t(*reinterpret_cast<const uint16_t*>(aux + off[s] + d * rowb));
+    for (uint32_t kk = 0; kk < uint32_t(kSteps); kk += D) {
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+            const uint32_t k = kk + d;
+            const uint32_t kn = min(k + uint32_t(D), uint32_t(kSteps) - 1u);
+#pragma unroll
+            for (int s = 0; s < S; ++s) {
+                const uint32_t pv = pbuf[s][d];
+                const uint32_t slot = x[s] & (kM - 1u);
+                uint32_t sym, fcv;
+                if (HALF) {
+                    const uint32_t s0 = my_slot[slot >> 1];
+                    const uint32_t f0 = lfc[s0 * kLanes + lane];
+                    const uint32_t f1 = lfc[(s0 + 1) * kLanes + lane];
+                    const bool adv = slot >= (f1 >> 16);   // start past the last symbol is a sentinel
+                    sym = adv ? s0 + 1 : s0;
+                    fcv = adv ? f1 : f0;
+                } else {
+                    sym = my_slot[slot];
+                    fcv = lfc[sym * kLanes + lane];
+                }
+                uint32_t xs = (fcv & 0xFFFFu) * (x[s] >> kProbBits) + slot - (fcv >> 16);
+                // Refill in lane order from the stream's words.  Reads are clamped
+                // into the stream; running past its words shows in the final count.
+                const uint32_t mw = uint32_t(__ballot(xs < kStateLow) >> half);
+                const bool need = (mw >> lane) & 1u;
+                const uint32_t w = W[s][min(p[s] + __popc(mw & ltmask), nwl[s])];
+                p[s] += __popc(mw);
+                // escaped values, in lane order, from the escape region
+                const uint32_t me = uint32_t(__ballot(sym == ns[s]) >> half);
+                const bool esc = (me >> lane) & 1u;
+                const uint32_t ei = min(ep[s] + __popc(me & ltmask), ecl[s]);
+                const uint32_t v = EB == 1 ? uint32_t(E[s][ei]) : uint32_t(reinterpret_cast<const uint16_t*>(E[s])[ei]);
+                ep[s] += __popc(me);
+                // the next predictor row is requested after this step's payload reads:
+                // waits for those reads then leave it in flight
+                pbuf[s][d] = EB == 1 ? uint32_t(aux[off[s] + kn * rowb])
+                                     : uint32_t(*reinterpret_cast<const uint16_t*>(aux + off[s] + kn * rowb));
+                x[s] = need ? ((xs << 16) | w) : xs;
+                if (esc && v < n) bad = true;      // a canonical encoder codes such a value directly
+                const uint32_t z = esc ? v : sym;
+                uint32_t t;
+                if (DT == SKV_E4M3) t = lut[512 + uint32_t(lut[pv]) + uint32_t(lut[256 + z])];
+                else t = unord16((ord16(pv) + unzig(z)) & 0xFFFFu);
+                if (!ACT || act[s] || rawc[s]) {
+                    if (EB == 1) out[off[s] + k * rowb] = uint8_t(t);
+                    else *reinterpret_cast<uint16_t*>(out + off[s] + k * rowb) = uint16_t(t);
+                }
+            }
+        }
+    }
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+        if (rawc[s]) {
+            // raw stream: its elements in (step, lane) order replace what the idle chain wrote
+            const uint8_t* sp = E[s];
+            for (uint32_t k = 0; k < uint32_t(kSteps); ++k) {
+                if (EB == 1) out[off[s] + k * rowb] = sp[k * kLanes + lane];
+                else *reinterpret_cast<uint16_t*>(out + off[s] + k * rowb) =
+                    reinterpret_cast<const uint16_t*>(sp)[k * kLanes + lane];
+            }
+        }
+        if (!act[s]) continue;
+        if (x[s] != kStateLow || p[s] != nwc[s] || ep[s] > ecc[s]) bad = true;
+        const uint8_t* sp = pay + (index[(uint64_t(ps.slab) * geo.ntb + tb0 + s) * geo.ncg + ps.cg] & ~kRawBit);
+        const uint32_t used = kStreamHead + 2 * nwc[s] + EB * ep[s];
+        if (((used + 3) & ~3u) != sz[s]) bad = true;
+        else if (lane < sz[s] - used && sp[used + lane] != 0) bad = true;   // zero pad
+    }
+}
+
+template <uint32_t DT, int S, int D, bool HALF>
+__global__ __launch_bounds__(1024, HALF ? 8 : 4) void decode_lds(DecodeLaunch a, DevTables t, uint32_t fs, LdsGeo lg) {
+    extern __shared__ __align__(16) uint8_t lds[];
+    __shared__ uint8_t lut[DT == SKV_E4M3 ? 1024 : 4];                    // e4m3: ord | unzig | unord x2
+    const Geo geo = geometry(a.shape);
+    const LdsPos ps = lds_position(geo, lg);
+    if (!ps.valid) return;
+    const uint32_t tab0 = ps.slab * geo.C + ps.cg * kLanes;
+    constexpr uint32_t MAPN = kM >> (HALF ? 1 : 0);                         // map entries per table
+    uint32_t* lfc = reinterpret_cast<uint32_t*>(lds);                      // [fs + 1 symbols][32 lanes]
+    uint8_t* lslot = lds + kLanes * (fs + 1) * 4;                          // [32 lanes][MAPN]
+    for (uint32_t i = threadIdx.x; i < kLanes * (fs + 1); i += blockDim.x) {
+        const uint32_t sym = i / kLanes, j = i % kLanes;
+        lfc[i] = sym < fs ? t.fc[size_t(tab0 + j) * 256 + sym] : 0xFFFF0000u;   // sentinel start past 4095
+    }
+    if (DT == SKV_E4M3)
+        for (uint32_t i = threadIdx.x; i < 256; i += blockDim.x) {
+            lut[i] = uint8_t(ord8(i));
+            lut[256 + i] = uint8_t(unzig(i));
+            lut[512 + i] = uint8_t(unord8(i));
+            lut[768 + i] = uint8_t(unord8(i));
+        }
+    __syncthreads();
+    // slot -> symbol maps: each thread fills one dword (4 entries) of every map,
+    // finding the first symbol by binary search over the symbol starts
+    constexpr uint32_t STRIDE = HALF ? 2u : 1u;
+    for (uint32_t d = threadIdx.x; d < kLanes * (MAPN / 4); d += blockDim.x) {
+        const uint32_t j = d / (MAPN / 4), slot0 = (d % (MAPN / 4)) * 4 * STRIDE;
+        const uint32_t nn = t.n[tab0 + j];
+        uint32_t lo = 0, hi = nn;
+        while (lo < hi) {
+            const uint32_t mid = (lo + hi + 1) >> 1;
+            if ((lfc[mid * kLanes + j] >> 16) <= slot0) lo = mid;
+            else hi = mid - 1;
+        }
+        uint32_t word = 0, sym = lo;
+        for (uint32_t q = 0; q < 4; ++q) {
+            while (sym < nn && (lfc[(sym + 1) * kLanes + j] >> 16) <= slot0 + q * STRIDE) ++sym;
+            word |= sym << (8 * q);
+        }
+        reinterpret_cast<uint32_t*>(lslot)[d] = word;
+    }
+    __syncthreads();
+
+    const uint32_t lane = threadIdx.x & 31u;
+    const uint32_t hw = threadIdx.x >> 5, nhw = blockDim.x >> 5;
+    const uint32_t n = t.n[tab0 + lane];
+    bool bad = false;
+    for (uint32_t tb0 = ps.tb_begin + hw * S; tb0 < ps.tb_end; tb0 += nhw * S) {
+        if (tb0 + S <= ps.tb_end) decode_round<DT, S, D, false, HALF>(a, ps, geo, tb0, lut, lfc, lslot, n, bad);
+        else decode_round<DT, S, D, true, HALF>(a, ps, geo, tb0, lut, lfc, lslot, n, bad);
+    }
+    if (bad) atomicOr(a.status, 1u);
+}
+
+template <uint32_t DT, int S, int D, bool ACT>
+__device__ __forceinline__ void encode_round(const EncodeLaunch& a, const LdsPos& ps, const Geo& geo, uint32_t tb0,
+                                             const uint4* lenc, const uint8_t* zlut, uint32_t n) {
+    constexpr uint32_t EB = DT == SKV_E4M3 ? 1u : 2u;
+    constexpr uint32_t RAW = kSyms * EB;
+    constexpr uint32_t MAXW = (RAW - kStreamHead) / 2;
+    constexpr uint32_t MAXE = (RAW - kStreamHead) / EB;
+    const uint32_t lane = threadIdx.x & 31u, half = threadIdx.x & 32u;
+    const uint32_t rowb = geo.C * EB;
+    const size_t slab_b = size_t(ps.slab) * geo.T * rowb + size_t(ps.cg) * kLanes * EB;
+    const uint8_t* tgt = static_cast<const uint8_t*>(a.target) + slab_b;
+    const uint8_t* aux = static_cast<const uint8_t*>(a.aux) + slab_b;
+
+    uint32_t x[S], cnt[S], ecnt[S], off[S];
+    uint8_t* area[S];
+    bool act[S];
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+        const uint32_t tb = tb0 + s;
+        act[s] = !ACT || tb < ps.tb_end;
+        const uint32_t tbs = act[s] ? tb : tb0;
+        off[s] = tbs * kSteps * rowb + lane * EB;
+        const uint64_t sid = (uint64_t(ps.slab) * geo.ntb + tbs) * geo.ncg + ps.cg;
+        area[s] = a.scratch + sid * (2 * RAW);
+        x[s] = kStateLow;
+        cnt[s] = ecnt[s] = 0;
+    }
+    // target / predictor values D steps ahead (steps run backwards)
+    uint32_t tbuf[S][D], pbuf[S][D];
+#pragma unroll
+    for (int s = 0; s < S; ++s)
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+            const uint32_t o = off[s] + (kSteps - 1 - d) * rowb;
+            tbuf[s][d] = EB == 1 ? uint32_t(tgt[o]) : uint32_t(*reinterpret_cast<const uint16_t*>(tgt + o));
+            pbuf[s][d] = EB == 1 ? uint32_t(aux[o]) : uint32_t(*reinterpret_cast<const uint16_t*>(aux + o));
+        }
+    for (int kk = kSteps - 1; kk >= 0; kk -= D) {
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+            const int k = kk - d;
+            const uint32_t kn = uint32_t(max(k - D, 0));
+#pragma unroll
+            for (int s = 0; s < S; ++s) {
+                const uint32_t tv = tbuf[s][d], pv = pbuf[s][d];
+                const uint32_t o = off[s] + kn * rowb;
+                tbuf[s][d] = EB == 1 ? uint32_t(tgt[o]) : uint32_t(*reinterpret_cast<const uint16_t*>(tgt + o));
+                pbuf[s][d] = EB == 1 ? uint32_t(aux[o]) : uint32_t(*reinterpret_cast<const uint16_t*>(aux + o));
+                const uint32_t z = DT == SKV_E4M3 ? uint32_t(zlut[256 + ((uint32_t(zlut[tv]) - uint32_t(zlut[pv])) & 0xFFu)])
+                                                  : zig16((ord16(tv) - ord16(pv)) & 0xFFFFu);
+                const uint32_t sym = min(z, n);
+                const uint4 e = lenc[sym * kLanes + lane];
+                // escaped values: ranked from lane 31 down, written backwards
+                const bool esc = (!ACT || act[s]) && z >= n;
+                const uint32_t me = uint32_t(__ballot(esc) >> half);
+                const uint32_t epos = ecnt[s] + __popc((me >> lane) >> 1);
+                // lanes with nothing to write target an unused byte of the stream head
+                const bool ew = esc && epos < MAXE;
+                uint8_t* ea = ew ? area[s] + RAW - EB * (epos + 1) : area[s] + kStateBytes;
+                if (EB == 1) *ea = uint8_t(z);
+                else *reinterpret_cast<uint16_t*>(ea) = uint16_t(z);
+                ecnt[s] += __popc(me);
+                // words leave before the state absorbs the symbol
+                uint32_t xs = x[s];
+                const bool emit = (!ACT || act[s]) && xs >= e.x;
+                const uint32_t mw = uint32_t(__ballot(emit) >> half);
+                const uint32_t pos = cnt[s] + __popc((mw >> lane) >> 1);
+                const bool ww = emit && pos < MAXW;
+                uint16_t* wa = ww ? reinterpret_cast<uint16_t*>(area[s] + 2 * RAW) - (pos + 1)
+                                  : reinterpret_cast<uint16_t*>(area[s] + kStateBytes + 2);
+                *wa = uint16_t(xs & 0xFFFFu);
+                xs = emit ? xs >> 16 : xs;
+                cnt[s] += __popc(mw);
+                const uint32_t qt = uint32_t((uint64_t(xs) + __umulhi(xs, e.y)) >> (e.w & 31u));
+                x[s] = xs + qt * e.z + (e.w >> 16);
+            }
+        }
+    }
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+        if (!act[s]) continue;
+        const uint64_t sid = (uint64_t(ps.slab) * geo.ntb + tb0 + s) * geo.ncg + ps.cg;
+        reinterpret_cast<uint32_t*>(area[s])[lane] = x[s];
+        if (lane == 0) {
+            const uint32_t bytes = (kStreamHead + 2 * cnt[s] + EB * ecnt[s] + 3) & ~3u;
+            a.meta[sid] = bytes >= RAW ? 0x80000000u : (cnt[s] | (ecnt[s] << 14));
+        }
+    }
+}
+
+template <uint32_t DT, int S, int D>
+__global__ __launch_bounds__(1024) void encode_lds(EncodeLaunch a, DevTables t, uint32_t fs, LdsGeo lg) {
+    extern __shared__ __align__(16) uint8_t lds[];
+    __shared__ uint8_t zlut[DT == SKV_E4M3 ? 512 : 4];                   // e4m3: ord | zigzag of a byte
+    const Geo geo = geometry(a.shape);
+    const LdsPos ps = lds_position(geo, lg);
+    if (!ps.valid) return;
+    const uint32_t tab0 = ps.slab * geo.C + ps.cg * kLanes;
+    uint4* lenc = reinterpret_cast<uint4*>(lds);                            // [fs symbols][32 lanes]
+    for (uint32_t i = threadIdx.x; i < kLanes * fs; i += blockDim.x) {
+        const uint32_t sym = i / kLanes, j = i % kLanes;
+        lenc[i] = t.enc[size_t(tab0 + j) * 256 + sym];
+    }
+    if (DT == SKV_E4M3)
+        for (uint32_t i = threadIdx.x; i < 256; i += blockDim.x) {
+            zlut[i] = uint8_t(ord8(i));
+            zlut[256 + i] = uint8_t(zig8(i));
+        }
+    __syncthreads();
+    const uint32_t lane = threadIdx.x & 31u;
+    const uint32_t hw = threadIdx.x >> 5, nhw = blockDim.x >> 5;
+    const uint32_t n = t.n[tab0 + lane];
+    for (uint32_t tb0 = ps.tb_begin + hw * S; tb0 < ps.tb_end; tb0 += nhw * S) {
+        if (tb0 + S <= ps.tb_end) encode_round<DT, S, D, false>(a, ps, geo, tb0, lenc, zlut, n);
+        else encode_round<DT, S, D, true>(a, ps, geo, tb0, lenc, zlut, n);
+    }
+}
+
 __global__ void clear_u32(uint32_t* p, uint32_t n) {
     const uint32_t i = blockIdx.x * blockDim.x + threadIdx.x;
     if (i < n) p[i] = 0u;
@@ -469,6 +853,7 @@ struct KernelTiming {
     int done = 0;
 };
 KernelTiming g_timing;
+bool g_force_v1 = false;     // use the one-stream-per-half-wave kernels (diagnostics)
 
 template <class F>
 void timed(const char* name, hipStream_t st, F&& launch) {
@@ -483,14 +868,74 @@ void timed(const char* name, hipStream_t st, F&& launch) {
     }
 }
 
+constexpr uint32_t kLdsThreads = 1024;
+
+// Kernel variant selection for tuning runs: SKV_VARIANT="<enc>,<dec>" (0 = default).
+struct Variant {
+    int enc = 0, dec = 0;
+};
+const Variant& variant() {
+    static const Variant v = [] {
+        Variant r;
+        if (const char* e = std::getenv("SKV_VARIANT")) std::sscanf(e, "%d,%d", &r.enc, &r.dec);
+        return r;
+    }();
+    return v;
+}
+constexpr size_t kLdsLimit = 160 * 1024;
+
+// Work decomposition of the LDS kernels for a residual-mode shape.
+LdsGeo lds_geometry(const skv_shape& s) {
+    const uint32_t ncg = s.channels / kLanes, ntb = s.tokens / kSteps;
+    const uint32_t line = s.dtype == SKV_E4M3 ? 4u : 2u;    // channel groups per 128-byte row segment
+    LdsGeo g;
+    g.G = (ncg % line == 0) ? line : (ncg % 2 == 0 ? 2u : 1u);
+    g.tbc = std::min<uint32_t>(ntb, 256u);
+    g.ntbc = (ntb + g.tbc - 1) / g.tbc;
+    g.groups = s.layers * s.kv * g.ntbc * (ncg / g.G);
+    return g;
+}
+
+inline uint32_t lds_grid(const LdsGeo& g) { return ((g.groups + 7) / 8) * 8 * g.G; }
+inline uint32_t fc_stride(const DevTables& t) { return (t.max_n + 1 + 3) & ~3u; }
+
+size_t decode_lds_bytes(const DevTables& t, uint32_t dtype, bool half) {
+    return size_t(kLanes) * (kM >> (half ? 1 : 0)) + size_t(kLanes) * (fc_stride(t) + 1) * 4;
+}
+size_t encode_lds_bytes(const DevTables& t, uint32_t dtype) { return size_t(kLanes) * fc_stride(t) * 16; }
+
+template <class K>
+hipError_t allow_lds(K kernel, size_t bytes) {
+    return hipFuncSetAttribute(reinterpret_cast<const void*>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
+                               int(bytes));
+}
+
 template <uint32_t DT, uint32_t MODE>
 hipError_t encode_all(const EncodeLaunch& a, const DevTables& t, hipStream_t st) {
     const uint64_t n = a.n_streams;
     const uint32_t nb = uint32_t((n + kScanBlock - 1) / kScanBlock);
     const uint32_t eg = uint32_t((n + kStreamsPerBlock - 1) / kStreamsPerBlock);
-    timed("encode_streams", st, [&] {
-        hipLaunchKernelGGL((encode_streams<DT, MODE>), dim3(eg), dim3(256), 0, st, a, t);
-    });
+    const size_t lb = encode_lds_bytes(t, DT);
+    if (MODE == SKV_RESIDUAL && lb <= kLdsLimit && !g_force_v1 && variant().enc >= 0) {
+        const LdsGeo lg = lds_geometry(a.shape);
+        auto k = encode_lds<DT, 1, 4>;
+        switch (variant().enc) {
+            case 1: k = encode_lds<DT, 2, 4>; break;
+            case 2: k = encode_lds<DT, 2, 2>; break;
+            case 3: k = encode_lds<DT, 2, 8>; break;
+            case 4: k = encode_lds<DT, 4, 2>; break;
+            default: break;
+        }
+        hipError_t e = allow_lds(k, lb);
+        if (e != hipSuccess) return e;
+        timed("encode_streams", st, [&] {
+            hipLaunchKernelGGL(k, dim3(lds_grid(lg)), dim3(kLdsThreads), lb, st, a, t, fc_stride(t), lg);
+        });
+    } else {
+        timed("encode_streams", st, [&] {
+            hipLaunchKernelGGL((encode_streams<DT, MODE>), dim3(eg), dim3(256), 0, st, a, t);
+        });
+    }
     timed("stream_block_sums", st, [&] {
         hipLaunchKernelGGL(stream_block_sums, dim3(nb), dim3(kScanBlock), 0, st, a.meta, n,
                            kSyms * (DT == SKV_E4M3 ? 1u : 2u), a.block_sum);
@@ -506,6 +951,26 @@ hipError_t encode_all(const EncodeLaunch& a, const DevTables& t, hipStream_t st)
 
 template <uint32_t DT, uint32_t MODE>
 hipError_t decode_all(const DecodeLaunch& a, const DevTables& t, hipStream_t st) {
+    const int v = variant().dec;
+    const bool half = v != 1 && v != 3;
+    const size_t lb = decode_lds_bytes(t, DT, half);
+    if (MODE == SKV_RESIDUAL && lb <= kLdsLimit && !g_force_v1 && v >= 0) {
+        const LdsGeo lg = lds_geometry(a.shape);
+        auto k = decode_lds<DT, 1, 4, true>;
+        switch (v) {
+            case 1: k = decode_lds<DT, 1, 4, false>; break;
+            case 2: k = decode_lds<DT, 1, 8, true>; break;
+            case 3: k = decode_lds<DT, 2, 2, false>; break;
+            case 4: k = decode_lds<DT, 2, 2, true>; break;
+            default: break;
+        }
+        hipError_t e = allow_lds(k, lb);
+        if (e != hipSuccess) return e;
+        timed("decode_streams", st, [&] {
+            hipLaunchKernelGGL(k, dim3(lds_grid(lg)), dim3(kLdsThreads), lb, st, a, t, fc_stride(t), lg);
+        });
+        return hipGetLastError();
+    }
     const uint64_t passes = MODE == SKV_RESIDUAL ? 1 : 2;
     const uint64_t per = a.n_streams / passes;
     const uint32_t grid = uint32_t((per + kStreamsPerBlock - 1) / kStreamsPerBlock);
@@ -529,7 +994,7 @@ hipError_t build_dev_tables(const uint8_t* blob, DevTables* t, hipStream_t st) {
     uint8_t* rec = nullptr;
     hipError_t e = hipMalloc(&rec, size_t(nt) * kTableRecord);
     if (e == hipSuccess) e = hipMalloc(&t->n, size_t(nt) * 4);
-    if (e == hipSuccess) e = hipMalloc(&t->enc, size_t(nt) * 256 * sizeof(uint2));
+    if (e == hipSuccess) e = hipMalloc(&t->enc, size_t(nt) * 256 * sizeof(uint4));
     if (e == hipSuccess) e = hipMalloc(&t->fc, size_t(nt) * 256 * 4);
     if (e == hipSuccess) e = hipMalloc(&t->slot, size_t(nt) * kM);
     if (e == hipSuccess) e = hipMemcpyAsync(rec, blob + kHeaderBytes, size_t(nt) * kTableRecord, hipMemcpyHostToDevice, st);
@@ -540,6 +1005,8 @@ hipError_t build_dev_tables(const uint8_t* blob, DevTables* t, hipStream_t st) {
     if (e == hipSuccess) e = hipStreamSynchronize(st);
     if (rec) (void)hipFree(rec);
     t->n_tables = nt;
+    t->max_n = 0;
+    for (uint32_t j = 0; j < nt; ++j) t->max_n = std::max(t->max_n, rd16(blob + kHeaderBytes + size_t(j) * kTableRecord));
     if (e != hipSuccess) free_dev_tables(t);
     return e;
 }
