@@ -133,7 +133,8 @@ def main() -> int:
     # algorithmic bytes per launch (what the method itself must move)
     alg = {
         "encode_streams": 2 * raw_bytes + payload,               # target + predictor read, coded streams out
-        "place_streams": cont_bytes,                             # the container written
+        "place_streams": 8 * (n_streams + 1) + 64,              # index + header written
+        "copy_streams": payload,                                 # the stream payload written
         "decode_streams": raw_bytes + cont_bytes + raw_bytes,    # predictor + container read, reconstruction out
         "stream_block_sums": 0, "stream_block_scan": 0,
     }
@@ -150,6 +151,10 @@ def main() -> int:
     roofline = {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
                 "algorithmic_bytes": alg.get(dom, 0), "avg_ms": round(kavg[dom], 4)}
+    per_kernel = {k: {"avg_ms": round(kavg[k], 4), "algorithmic_bytes": alg.get(k, 0),
+                      "achieved_GBps": round(alg.get(k, 0) / (kavg[k] / 1e3) / 1e9, 1),
+                      "frac": round(alg.get(k, 0) / (kavg[k] / 1e3) / 1e9 / HBM_PEAK_GBPS, 4)}
+                  for k in kavg if alg.get(k, 0)}
 
     copy = None
     if args.copy_probe:
@@ -197,6 +202,7 @@ def main() -> int:
         "table_fit_s": round(fit_s, 3),
         "verified_roundtrip": ok,
         "roofline": roofline,
+        "kernels_roofline": per_kernel,
         "copy_ceiling": copy,
         "cpu_baseline": cpu,
     }

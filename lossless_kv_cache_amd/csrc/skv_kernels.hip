@@ -5,9 +5,9 @@
 //                   (frequency, start) words, resident in HBM
 //   encode_streams  symbolize + 32-lane interleaved rANS encode, one
 //                   stream per half wavefront; words placed by ballot
-//   stream_block_sums / stream_block_scan / place_streams
-//                   stream sizes -> exclusive scan -> u64 index and the
-//                   compacted container
+//   stream_block_sums / stream_block_scan / place_streams / copy_streams
+//                   stream sizes -> exclusive scan -> u64 index, header, and
+//                   the compacted container
 //   decode_streams  rANS decode + reconstruction, one stream per half
 //                   wavefront; checkerboard mode runs it twice
 //
@@ -110,13 +110,13 @@ __global__ __launch_bounds__(256) void expand_tables(const uint8_t* rec, uint32_
 // words are ranked from lane 31 down to lane 0 (reverse of the decoder's
 // refill order) and written backwards from the end of the stream's scratch.
 __device__ __forceinline__ void emit_words(uint32_t& x, uint32_t& cnt, bool emit, uint32_t lane, uint32_t half,
-                                           uint16_t* wend, uint32_t maxw) {
+                                           uint16_t* words, uint32_t maxw) {
     const uint64_t b = __ballot(emit);
     const uint32_t mine = uint32_t(b >> half);
     if (emit) {
         const uint32_t above = __popc(uint32_t((uint64_t)mine >> (lane + 1)));
         const uint32_t pos = cnt + above;
-        if (pos < maxw) *(wend - pos) = uint16_t(x & 0xFFFFu);
+        if (pos < maxw) words[pos] = uint16_t(x & 0xFFFFu);
         x >>= 16;
     }
     cnt += __popc(mine);
@@ -138,8 +138,8 @@ __global__ __launch_bounds__(256) void encode_streams(EncodeLaunch a, DevTables 
     constexpr uint32_t MAXW = (RAW - kStreamHead) / 2;     // more words or escapes mean a raw stream
     constexpr uint32_t MAXE = (RAW - kStreamHead) / EB;
     uint8_t* area = a.scratch + sid * (2 * RAW);
-    uint16_t* wend = reinterpret_cast<uint16_t*>(area + 2 * RAW) - 1;   // words, backwards
-    uint8_t* eend = area + RAW - EB;                                     // escaped values, backwards
+    uint16_t* wfwd = reinterpret_cast<uint16_t*>(area + RAW);           // words, emission order
+    uint8_t* efwd = area + kStreamHead;                                  // escaped values, emission order
     const uint32_t res_table = slab * g.C + ch;
 
     uint32_t x = kStateLow, cnt = 0, ecnt = 0;
@@ -181,14 +181,14 @@ __global__ __launch_bounds__(256) void encode_streams(EncodeLaunch a, DevTables 
             if (esc) {
                 const uint32_t pos = ecnt + __popc(uint32_t((uint64_t)mine >> (lane + 1)));
                 if (pos < MAXE) {
-                    if (EB == 1) *(eend - pos) = uint8_t(z);
-                    else *reinterpret_cast<uint16_t*>(eend - 2 * pos) = uint16_t(z);
+                    if (EB == 1) efwd[pos] = uint8_t(z);
+                    else reinterpret_cast<uint16_t*>(efwd)[pos] = uint16_t(z);
                 }
             }
             ecnt += __popc(mine);
         }
         const uint4 e = t.enc[size_t(table) * 256 + s];
-        emit_words(x, cnt, x >= e.x, lane, half, wend, MAXW);
+        emit_words(x, cnt, x >= e.x, lane, half, wfwd, MAXW);
         const uint32_t qt = uint32_t((uint64_t(x) + __umulhi(x, e.y)) >> (e.w & 31u));   // floor(x / f)
         x = x + qt * e.z + (e.w >> 16);
     }
@@ -252,7 +252,6 @@ __global__ __launch_bounds__(kScanBlock) void stream_block_scan(const uint32_t* 
 
 template <uint32_t DT, uint32_t MODE>
 __global__ __launch_bounds__(kScanBlock) void place_streams(EncodeLaunch a, const uint64_t* boff) {
-    __shared__ uint64_t offs[kScanBlock];
     __shared__ uint32_t wsum[kScanBlock / 64];
     constexpr uint32_t EB = DT == SKV_E4M3 ? 1u : 2u;
     constexpr uint32_t RAW = kSyms * EB;
@@ -275,7 +274,6 @@ __global__ __launch_bounds__(kScanBlock) void place_streams(EncodeLaunch a, cons
     uint64_t off = boff[blockIdx.x];
     for (uint32_t q = 0; q < w; ++q) off += wsum[q];
     off += incl - v;
-    offs[threadIdx.x] = off;
     uint64_t* index = reinterpret_cast<uint64_t*>(a.out + kHeaderBytes);
     if (i < n) index[i] = off | (uint64_t(m >> 31) << 63);
     if (i == n - 1) index[n] = total;
@@ -291,45 +289,57 @@ __global__ __launch_bounds__(kScanBlock) void place_streams(EncodeLaunch a, cons
             uint32_t(total), uint32_t(total >> 32), 0u, 0u};
         for (int q = 0; q < 16; ++q) reinterpret_cast<uint32_t*>(h)[q] = words[q];
     }
-    __syncthreads();
-    // copy: each wavefront moves 64 streams, one at a time
-    const Geo g = geometry(a.shape);
-    uint8_t* pay = a.out + head;
-    for (uint32_t j = 0; j < 64; ++j) {
-        const uint32_t li = w * 64 + j;
-        const uint64_t sid = first + li;
-        if (sid >= n) break;
-        const uint32_t ms = a.meta[sid];
-        uint8_t* dst = pay + offs[li];
-        const uint8_t* src = a.scratch + sid * (2 * RAW);
-        if (ms >> 31) {
-            const uint32_t cg = uint32_t(sid % g.ncg);
-            const uint32_t tb = uint32_t((sid / g.ncg) % g.ntb);
-            const uint32_t slab = uint32_t(sid / (uint64_t(g.ncg) * g.ntb));
-            for (uint32_t e = lane; e < uint32_t(kSyms); e += 64) {
-                const uint32_t k = e >> 5, ln = e & 31u;
-                const uint32_t tok = MODE == SKV_RESIDUAL ? tb * kSteps + k : 2u * (tb * kSteps + k) + slab;
-                const size_t idx = MODE == SKV_RESIDUAL ? (size_t(slab) * g.T + tok) * g.C + cg * kLanes + ln
-                                                        : size_t(tok) * g.C + cg * kLanes + ln;
-                if (EB == 1) dst[e] = static_cast<const uint8_t*>(a.target)[idx];
-                else reinterpret_cast<uint16_t*>(dst)[e] = static_cast<const uint16_t*>(a.target)[idx];
-            }
-        } else {
-            // states from the front of the scratch area, escapes before its middle, words at its back
-            const uint32_t cnt = ms & 0x3FFFu, ecnt = (ms >> 14) & 0x3FFFu;
-            if (lane < 32) reinterpret_cast<uint32_t*>(dst)[lane] = reinterpret_cast<const uint32_t*>(src)[lane];
-            if (lane == 32) reinterpret_cast<uint32_t*>(dst)[32] = cnt;
-            const uint16_t* ws = reinterpret_cast<const uint16_t*>(src + 2 * RAW) - cnt;
-            uint16_t* wd = reinterpret_cast<uint16_t*>(dst + kStreamHead);
-            for (uint32_t q = lane; q < cnt; q += 64) wd[q] = ws[q];
-            const uint8_t* es = src + RAW - EB * ecnt;
-            uint8_t* ed = dst + kStreamHead + 2 * cnt;
-            const uint32_t eb = EB * ecnt;
-            const uint32_t total = (kStreamHead + 2 * cnt + eb + 3) & ~3u;
-            const uint32_t tail = total - (kStreamHead + 2 * cnt);
-            for (uint32_t q = lane; q < tail; q += 64) ed[q] = q < eb ? es[q] : uint8_t(0);
+}
+
+// One wavefront per stream: copy its bytes from the scratch area to its place
+// in the container (states, words and escaped values reversed from emission
+// into decode order, zero pad; raw streams gather the target tile).
+template <uint32_t DT, uint32_t MODE>
+__global__ __launch_bounds__(256) void copy_streams(EncodeLaunch a) {
+    constexpr uint32_t EB = DT == SKV_E4M3 ? 1u : 2u;
+    constexpr uint32_t RAW = kSyms * EB;
+    const uint64_t n = a.n_streams;
+    const uint64_t sid = uint64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
+    if (sid >= n) return;
+    const uint64_t head = kHeaderBytes + 8 * (n + 1);
+    if (head + *a.total > a.out_capacity) return;        // caller reports SKV_ERR_CAPACITY
+    const uint32_t lane = threadIdx.x & 63u;
+    const uint64_t* index = reinterpret_cast<const uint64_t*>(a.out + kHeaderBytes);
+    uint8_t* dst = a.out + head + (index[sid] & ~kRawBit);
+    const uint32_t ms = a.meta[sid];
+    const uint8_t* src = a.scratch + sid * (2 * RAW);
+    if (ms >> 31) {
+        const Geo g = geometry(a.shape);
+        const uint32_t cg = uint32_t(sid % g.ncg);
+        const uint32_t tb = uint32_t((sid / g.ncg) % g.ntb);
+        const uint32_t slab = uint32_t(sid / (uint64_t(g.ncg) * g.ntb));
+        for (uint32_t e = lane; e < uint32_t(kSyms); e += 64) {
+            const uint32_t k = e >> 5, ln = e & 31u;
+            const uint32_t tok = MODE == SKV_RESIDUAL ? tb * kSteps + k : 2u * (tb * kSteps + k) + slab;
+            const size_t idx = MODE == SKV_RESIDUAL ? (size_t(slab) * g.T + tok) * g.C + cg * kLanes + ln
+                                                    : size_t(tok) * g.C + cg * kLanes + ln;
+            if (EB == 1) dst[e] = static_cast<const uint8_t*>(a.target)[idx];
+            else reinterpret_cast<uint16_t*>(dst)[e] = static_cast<const uint16_t*>(a.target)[idx];
         }
+        return;
     }
+    const uint32_t cnt = ms & 0x3FFFu, ecnt = (ms >> 14) & 0x3FFFu;
+    if (lane < 32) reinterpret_cast<uint32_t*>(dst)[lane] = reinterpret_cast<const uint32_t*>(src)[lane];
+    if (lane == 32) reinterpret_cast<uint32_t*>(dst)[32] = cnt;
+    const uint16_t* ws = reinterpret_cast<const uint16_t*>(src + RAW);
+    uint16_t* wd = reinterpret_cast<uint16_t*>(dst + kStreamHead);
+    for (uint32_t q = lane; q < cnt; q += 64) wd[q] = ws[cnt - 1 - q];
+    uint8_t* ed = dst + kStreamHead + 2 * cnt;
+    if (EB == 1) {
+        const uint8_t* es = src + kStreamHead;
+        for (uint32_t q = lane; q < ecnt; q += 64) ed[q] = es[ecnt - 1 - q];
+    } else {
+        const uint16_t* es = reinterpret_cast<const uint16_t*>(src + kStreamHead);
+        for (uint32_t q = lane; q < ecnt; q += 64) reinterpret_cast<uint16_t*>(ed)[q] = es[ecnt - 1 - q];
+    }
+    const uint32_t eb = EB * ecnt;
+    const uint32_t total = (kStreamHead + 2 * cnt + eb + 3) & ~3u;
+    for (uint32_t q = eb + lane; q < total - (kStreamHead + 2 * cnt); q += 64) ed[q] = 0;
 }
 
 // --------------------------------------------------------------- decode
@@ -719,6 +729,11 @@ __global__ __launch_bounds__(1024, HALF ? 8 : 4) void decode_lds(DecodeLaunch a,
     if (bad) atomicOr(a.status, 1u);
 }
 
+// Encoder scratch per stream (2 x raw bytes): final states [0, 128), a sink
+// for lanes with nothing to store [128, 132), escaped values from 132 and
+// words from `raw`, both in emission order (the compaction reverses them into
+// decode order).  Inside a half-wave, hardware lane L runs format lane 31 - L,
+// so "emitted earlier in this step" means "lower hardware lane".
 template <uint32_t DT, int S, int D, bool ACT>
 __device__ __forceinline__ void encode_round(const EncodeLaunch& a, const LdsPos& ps, const Geo& geo, uint32_t tb0,
                                              const uint4* lenc, const uint8_t* zlut, uint32_t n) {
@@ -726,14 +741,19 @@ __device__ __forceinline__ void encode_round(const EncodeLaunch& a, const LdsPos
     constexpr uint32_t RAW = kSyms * EB;
     constexpr uint32_t MAXW = (RAW - kStreamHead) / 2;
     constexpr uint32_t MAXE = (RAW - kStreamHead) / EB;
-    const uint32_t lane = threadIdx.x & 31u, half = threadIdx.x & 32u;
+    const uint32_t hl = threadIdx.x & 31u, half = threadIdx.x & 32u;
+    const uint32_t lane = 31u - hl;                        // format lane
+    const uint32_t ltmask = (1u << hl) - 1u;
     const uint32_t rowb = geo.C * EB;
     const size_t slab_b = size_t(ps.slab) * geo.T * rowb + size_t(ps.cg) * kLanes * EB;
     const uint8_t* tgt = static_cast<const uint8_t*>(a.target) + slab_b;
     const uint8_t* aux = static_cast<const uint8_t*>(a.aux) + slab_b;
+    // the workgroup's streams are ncg apart in stream order: 32-bit offsets from a common base
+    const uint64_t sid0 = (uint64_t(ps.slab) * geo.ntb + ps.tb_begin) * geo.ncg + ps.cg;
+    uint8_t* wgs = a.scratch + sid0 * (2 * RAW);
+    const uint32_t sstride = geo.ncg * (2 * RAW);
 
-    uint32_t x[S], cnt[S], ecnt[S], off[S];
-    uint8_t* area[S];
+    uint32_t x[S], cnt[S], ecnt[S], off[S], ao[S];
     bool act[S];
 #pragma unroll
     for (int s = 0; s < S; ++s) {
@@ -741,8 +761,7 @@ __device__ __forceinline__ void encode_round(const EncodeLaunch& a, const LdsPos
         act[s] = !ACT || tb < ps.tb_end;
         const uint32_t tbs = act[s] ? tb : tb0;
         off[s] = tbs * kSteps * rowb + lane * EB;
-        const uint64_t sid = (uint64_t(ps.slab) * geo.ntb + tbs) * geo.ncg + ps.cg;
-        area[s] = a.scratch + sid * (2 * RAW);
+        ao[s] = (tbs - ps.tb_begin) * sstride;
         x[s] = kStateLow;
         cnt[s] = ecnt[s] = 0;
     }
@@ -771,25 +790,21 @@ __device__ __forceinline__ void encode_round(const EncodeLaunch& a, const LdsPos
                                                   : zig16((ord16(tv) - ord16(pv)) & 0xFFFFu);
                 const uint32_t sym = min(z, n);
                 const uint4 e = lenc[sym * kLanes + lane];
-                // escaped values: ranked from lane 31 down, written backwards
+                // escaped values, in emission order
                 const bool esc = (!ACT || act[s]) && z >= n;
                 const uint32_t me = uint32_t(__ballot(esc) >> half);
-                const uint32_t epos = ecnt[s] + __popc((me >> lane) >> 1);
-                // lanes with nothing to write target an unused byte of the stream head
-                const bool ew = esc && epos < MAXE;
-                uint8_t* ea = ew ? area[s] + RAW - EB * (epos + 1) : area[s] + kStateBytes;
-                if (EB == 1) *ea = uint8_t(z);
-                else *reinterpret_cast<uint16_t*>(ea) = uint16_t(z);
+                const uint32_t epos = ecnt[s] + __popc(me & ltmask);
+                const uint32_t eo = esc && epos < MAXE ? ao[s] + kStreamHead + EB * epos : ao[s] + kStateBytes;
+                if (EB == 1) wgs[eo] = uint8_t(z);
+                else *reinterpret_cast<uint16_t*>(wgs + eo) = uint16_t(z);
                 ecnt[s] += __popc(me);
                 // words leave before the state absorbs the symbol
                 uint32_t xs = x[s];
                 const bool emit = (!ACT || act[s]) && xs >= e.x;
                 const uint32_t mw = uint32_t(__ballot(emit) >> half);
-                const uint32_t pos = cnt[s] + __popc((mw >> lane) >> 1);
-                const bool ww = emit && pos < MAXW;
-                uint16_t* wa = ww ? reinterpret_cast<uint16_t*>(area[s] + 2 * RAW) - (pos + 1)
-                                  : reinterpret_cast<uint16_t*>(area[s] + kStateBytes + 2);
-                *wa = uint16_t(xs & 0xFFFFu);
+                const uint32_t pos = cnt[s] + __popc(mw & ltmask);
+                const uint32_t wo = emit && pos < MAXW ? ao[s] + RAW + 2 * pos : ao[s] + kStateBytes + 2;
+                *reinterpret_cast<uint16_t*>(wgs + wo) = uint16_t(xs & 0xFFFFu);
                 xs = emit ? xs >> 16 : xs;
                 cnt[s] += __popc(mw);
                 const uint32_t qt = uint32_t((uint64_t(xs) + __umulhi(xs, e.y)) >> (e.w & 31u));
@@ -800,9 +815,9 @@ __device__ __forceinline__ void encode_round(const EncodeLaunch& a, const LdsPos
 #pragma unroll
     for (int s = 0; s < S; ++s) {
         if (!act[s]) continue;
-        const uint64_t sid = (uint64_t(ps.slab) * geo.ntb + tb0 + s) * geo.ncg + ps.cg;
-        reinterpret_cast<uint32_t*>(area[s])[lane] = x[s];
-        if (lane == 0) {
+        reinterpret_cast<uint32_t*>(wgs + ao[s])[lane] = x[s];
+        if (hl == 0) {
+            const uint64_t sid = sid0 + uint64_t(tb0 + s - ps.tb_begin) * geo.ncg;
             const uint32_t bytes = (kStreamHead + 2 * cnt[s] + EB * ecnt[s] + 3) & ~3u;
             a.meta[sid] = bytes >= RAW ? 0x80000000u : (cnt[s] | (ecnt[s] << 14));
         }
@@ -828,7 +843,7 @@ __global__ __launch_bounds__(1024) void encode_lds(EncodeLaunch a, DevTables t, 
             zlut[256 + i] = uint8_t(zig8(i));
         }
     __syncthreads();
-    const uint32_t lane = threadIdx.x & 31u;
+    const uint32_t lane = 31u - (threadIdx.x & 31u);      // format lane (reversed within the half-wave)
     const uint32_t hw = threadIdx.x >> 5, nhw = blockDim.x >> 5;
     const uint32_t n = t.n[tab0 + lane];
     for (uint32_t tb0 = ps.tb_begin + hw * S; tb0 < ps.tb_end; tb0 += nhw * S) {
@@ -945,6 +960,9 @@ hipError_t encode_all(const EncodeLaunch& a, const DevTables& t, hipStream_t st)
     });
     timed("place_streams", st, [&] {
         hipLaunchKernelGGL((place_streams<DT, MODE>), dim3(nb), dim3(kScanBlock), 0, st, a, a.block_off);
+    });
+    timed("copy_streams", st, [&] {
+        hipLaunchKernelGGL((copy_streams<DT, MODE>), dim3(uint32_t((n + 3) / 4)), dim3(256), 0, st, a);
     });
     return hipGetLastError();
 }
