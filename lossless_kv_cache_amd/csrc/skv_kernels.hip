@@ -729,21 +729,29 @@ __global__ __launch_bounds__(1024, HALF ? 8 : 4) void decode_lds(DecodeLaunch a,
     if (bad) atomicOr(a.status, 1u);
 }
 
-// Encoder scratch per stream (2 x raw bytes): final states [0, 128), a sink
-// for lanes with nothing to store [128, 132), escaped values from 132 and
-// words from `raw`, both in emission order (the compaction reverses them into
-// decode order).  Inside a half-wave, hardware lane L runs format lane 31 - L,
-// so "emitted earlier in this step" means "lower hardware lane".
+// Encoder scratch per stream (2 x raw bytes): final states [0, 128), escaped
+// values from 132 and words from `raw`, both in emission order (the compaction
+// reverses them into decode order).  Inside a half-wave, hardware lane L runs
+// format lane 31 - L, so "emitted earlier in this step" means "lower hardware
+// lane".  The two half-waves of a wavefront run two streams in lockstep; their
+// word and escape counts are wave-uniform scalars and a lane finds its slot
+// with mbcnt over the whole 64-lane ballot.  Counts stop advancing the write
+// position once a stream is certain to be stored raw, so a stream never writes
+// outside its own scratch area (any slot at or past the limit implies raw).
 template <uint32_t DT, int S, int D, bool ACT>
 __device__ __forceinline__ void encode_round(const EncodeLaunch& a, const LdsPos& ps, const Geo& geo, uint32_t tb0,
                                              const uint4* lenc, const uint8_t* zlut, uint32_t n) {
+    static_assert(D >= 2, "the one-step lookahead reads the next ring slot");
     constexpr uint32_t EB = DT == SKV_E4M3 ? 1u : 2u;
     constexpr uint32_t RAW = kSyms * EB;
     constexpr uint32_t MAXW = (RAW - kStreamHead) / 2;
     constexpr uint32_t MAXE = (RAW - kStreamHead) / EB;
-    const uint32_t hl = threadIdx.x & 31u, half = threadIdx.x & 32u;
+    static_assert(kStreamHead + EB * (MAXE + 32) <= 2 * RAW && RAW + 2 * (MAXW + 32) <= 2 * RAW,
+                  "clamped slots stay inside the stream's scratch area");
+    const uint32_t hl = threadIdx.x & 31u;
+    const bool upper = (threadIdx.x & 32u) != 0;
+    const uint32_t fsh = upper ? 16u : 0u;                 // which 16-bit field of a packed pair is this half's
     const uint32_t lane = 31u - hl;                        // format lane
-    const uint32_t ltmask = (1u << hl) - 1u;
     const uint32_t rowb = geo.C * EB;
     const size_t slab_b = size_t(ps.slab) * geo.T * rowb + size_t(ps.cg) * kLanes * EB;
     const uint8_t* tgt = static_cast<const uint8_t*>(a.target) + slab_b;
@@ -753,7 +761,10 @@ __device__ __forceinline__ void encode_round(const EncodeLaunch& a, const LdsPos
     uint8_t* wgs = a.scratch + sid0 * (2 * RAW);
     const uint32_t sstride = geo.ncg * (2 * RAW);
 
-    uint32_t x[S], cnt[S], ecnt[S], off[S], ao[S];
+    // upper-half slots carry a bias of 32 (mbcnt_lo counts the whole lower half for them)
+    const uint32_t bias_b = upper ? 32u : 0u;
+    uint32_t x[S], off[S], ao[S], wbase[S], ebase[S];
+    uint32_t wlo[S], whi[S], elo[S], ehi[S];               // wave-uniform counts per half
     bool act[S];
 #pragma unroll
     for (int s = 0; s < S; ++s) {
@@ -762,8 +773,10 @@ __device__ __forceinline__ void encode_round(const EncodeLaunch& a, const LdsPos
         const uint32_t tbs = act[s] ? tb : tb0;
         off[s] = tbs * kSteps * rowb + lane * EB;
         ao[s] = (tbs - ps.tb_begin) * sstride;
+        wbase[s] = ao[s] + RAW - 2 * bias_b;
+        ebase[s] = ao[s] + kStreamHead - EB * bias_b;
         x[s] = kStateLow;
-        cnt[s] = ecnt[s] = 0;
+        wlo[s] = whi[s] = elo[s] = ehi[s] = 0;
     }
     // target / predictor values D steps ahead (steps run backwards)
     uint32_t tbuf[S][D], pbuf[S][D];
@@ -775,6 +788,20 @@ __device__ __forceinline__ void encode_round(const EncodeLaunch& a, const LdsPos
             tbuf[s][d] = EB == 1 ? uint32_t(tgt[o]) : uint32_t(*reinterpret_cast<const uint16_t*>(tgt + o));
             pbuf[s][d] = EB == 1 ? uint32_t(aux[o]) : uint32_t(*reinterpret_cast<const uint16_t*>(aux + o));
         }
+    // e4m3: zlut[0, 256) is the order-preserving map of a byte, zlut[256, 768)
+    // the zigzag of (a - b) mod 256 at index 512 + a - b
+    auto symbol_of = [&](uint32_t tv, uint32_t pv) -> uint32_t {
+        return DT == SKV_E4M3 ? uint32_t(zlut[512u + uint32_t(zlut[tv]) - uint32_t(zlut[pv])])
+                              : zig16((ord16(tv) - ord16(pv)) & 0xFFFFu);
+    };
+    // symbol value and table entry run one step ahead of the state chain
+    uint32_t zc[S];
+    uint4 ec[S];
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+        zc[s] = symbol_of(tbuf[s][0], pbuf[s][0]);
+        ec[s] = lenc[min(zc[s], n) * kLanes + lane];
+    }
     for (int kk = kSteps - 1; kk >= 0; kk -= D) {
 #pragma unroll
         for (int d = 0; d < D; ++d) {
@@ -782,33 +809,45 @@ __device__ __forceinline__ void encode_round(const EncodeLaunch& a, const LdsPos
             const uint32_t kn = uint32_t(max(k - D, 0));
 #pragma unroll
             for (int s = 0; s < S; ++s) {
-                const uint32_t tv = tbuf[s][d], pv = pbuf[s][d];
+                const uint32_t z = zc[s];
+                const uint4 e = ec[s];
+                // next step's symbol and entry (step k - 1, held in ring slot d + 1)
+                const uint32_t zn = symbol_of(tbuf[s][(d + 1) % D], pbuf[s][(d + 1) % D]);
+                const uint4 en = lenc[min(zn, n) * kLanes + lane];
                 const uint32_t o = off[s] + kn * rowb;
                 tbuf[s][d] = EB == 1 ? uint32_t(tgt[o]) : uint32_t(*reinterpret_cast<const uint16_t*>(tgt + o));
                 pbuf[s][d] = EB == 1 ? uint32_t(aux[o]) : uint32_t(*reinterpret_cast<const uint16_t*>(aux + o));
-                const uint32_t z = DT == SKV_E4M3 ? uint32_t(zlut[256 + ((uint32_t(zlut[tv]) - uint32_t(zlut[pv])) & 0xFFu)])
-                                                  : zig16((ord16(tv) - ord16(pv)) & 0xFFFFu);
-                const uint32_t sym = min(z, n);
-                const uint4 e = lenc[sym * kLanes + lane];
-                // escaped values, in emission order
+                // escaped values, in emission order (rare: the whole block is skipped by the wavefront)
                 const bool esc = (!ACT || act[s]) && z >= n;
-                const uint32_t me = uint32_t(__ballot(esc) >> half);
-                const uint32_t epos = ecnt[s] + __popc(me & ltmask);
-                const uint32_t eo = esc && epos < MAXE ? ao[s] + kStreamHead + EB * epos : ao[s] + kStateBytes;
-                if (EB == 1) wgs[eo] = uint8_t(z);
-                else *reinterpret_cast<uint16_t*>(wgs + eo) = uint16_t(z);
-                ecnt[s] += __popc(me);
+                const uint64_t me = __ballot(esc);
+                if (me) {
+                    const uint32_t mlo = uint32_t(me), mhi = uint32_t(me >> 32), plo = __popc(mlo);
+                    const uint32_t pk = min(elo[s], MAXE) | ((min(ehi[s], MAXE) + 32u - plo) << 16);
+                    const uint32_t slot = __builtin_amdgcn_mbcnt_hi(
+                        mhi, __builtin_amdgcn_mbcnt_lo(mlo, __builtin_amdgcn_ubfe(pk, fsh, 16)));
+                    if (esc) {
+                        if (EB == 1) wgs[ebase[s] + slot] = uint8_t(z);
+                        else *reinterpret_cast<uint16_t*>(wgs + (ebase[s] + 2 * slot)) = uint16_t(z);
+                    }
+                    elo[s] += plo;
+                    ehi[s] += __popc(mhi);
+                }
                 // words leave before the state absorbs the symbol
                 uint32_t xs = x[s];
                 const bool emit = (!ACT || act[s]) && xs >= e.x;
-                const uint32_t mw = uint32_t(__ballot(emit) >> half);
-                const uint32_t pos = cnt[s] + __popc(mw & ltmask);
-                const uint32_t wo = emit && pos < MAXW ? ao[s] + RAW + 2 * pos : ao[s] + kStateBytes + 2;
-                *reinterpret_cast<uint16_t*>(wgs + wo) = uint16_t(xs & 0xFFFFu);
+                const uint64_t mw = __ballot(emit);
+                const uint32_t mlo = uint32_t(mw), mhi = uint32_t(mw >> 32), plo = __popc(mlo);
+                const uint32_t pk = min(wlo[s], MAXW) | ((min(whi[s], MAXW) + 32u - plo) << 16);
+                const uint32_t slot =
+                    __builtin_amdgcn_mbcnt_hi(mhi, __builtin_amdgcn_mbcnt_lo(mlo, __builtin_amdgcn_ubfe(pk, fsh, 16)));
+                if (emit) *reinterpret_cast<uint16_t*>(wgs + (wbase[s] + 2 * slot)) = uint16_t(xs & 0xFFFFu);
+                wlo[s] += plo;
+                whi[s] += __popc(mhi);
                 xs = emit ? xs >> 16 : xs;
-                cnt[s] += __popc(mw);
                 const uint32_t qt = uint32_t((uint64_t(xs) + __umulhi(xs, e.y)) >> (e.w & 31u));
-                x[s] = xs + qt * e.z + (e.w >> 16);
+                x[s] = xs + __umul24(qt, e.z) + (e.w >> 16);    // quotient < 2^20, 4096 - f < 2^12
+                zc[s] = zn;
+                ec[s] = en;
             }
         }
     }
@@ -817,9 +856,10 @@ __device__ __forceinline__ void encode_round(const EncodeLaunch& a, const LdsPos
         if (!act[s]) continue;
         reinterpret_cast<uint32_t*>(wgs + ao[s])[lane] = x[s];
         if (hl == 0) {
+            const uint32_t cnt = upper ? whi[s] : wlo[s], ecnt = upper ? ehi[s] : elo[s];
             const uint64_t sid = sid0 + uint64_t(tb0 + s - ps.tb_begin) * geo.ncg;
-            const uint32_t bytes = (kStreamHead + 2 * cnt[s] + EB * ecnt[s] + 3) & ~3u;
-            a.meta[sid] = bytes >= RAW ? 0x80000000u : (cnt[s] | (ecnt[s] << 14));
+            const uint32_t bytes = (kStreamHead + 2 * cnt + EB * ecnt + 3) & ~3u;
+            a.meta[sid] = bytes >= RAW ? 0x80000000u : (cnt | (ecnt << 14));
         }
     }
 }
@@ -827,7 +867,7 @@ __device__ __forceinline__ void encode_round(const EncodeLaunch& a, const LdsPos
 template <uint32_t DT, int S, int D>
 __global__ __launch_bounds__(1024) void encode_lds(EncodeLaunch a, DevTables t, uint32_t fs, LdsGeo lg) {
     extern __shared__ __align__(16) uint8_t lds[];
-    __shared__ uint8_t zlut[DT == SKV_E4M3 ? 512 : 4];                   // e4m3: ord | zigzag of a byte
+    __shared__ uint8_t zlut[DT == SKV_E4M3 ? 768 : 4];                   // e4m3: ord | zigzag of a difference
     const Geo geo = geometry(a.shape);
     const LdsPos ps = lds_position(geo, lg);
     if (!ps.valid) return;
@@ -838,9 +878,9 @@ __global__ __launch_bounds__(1024) void encode_lds(EncodeLaunch a, DevTables t, 
         lenc[i] = t.enc[size_t(tab0 + j) * 256 + sym];
     }
     if (DT == SKV_E4M3)
-        for (uint32_t i = threadIdx.x; i < 256; i += blockDim.x) {
-            zlut[i] = uint8_t(ord8(i));
-            zlut[256 + i] = uint8_t(zig8(i));
+        for (uint32_t i = threadIdx.x; i < 512; i += blockDim.x) {
+            if (i < 256) zlut[i] = uint8_t(ord8(i));
+            zlut[256 + i] = uint8_t(zig8((i - 256u) & 0xFFu));
         }
     __syncthreads();
     const uint32_t lane = 31u - (threadIdx.x & 31u);      // format lane (reversed within the half-wave)
