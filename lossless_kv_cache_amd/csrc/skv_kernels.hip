@@ -746,6 +746,7 @@ __device__ __forceinline__ void encode_round(const EncodeLaunch& a, const LdsPos
     constexpr uint32_t RAW = kSyms * EB;
     constexpr uint32_t MAXW = (RAW - kStreamHead) / 2;
     constexpr uint32_t MAXE = (RAW - kStreamHead) / EB;
+    constexpr uint32_t kDrop = 0x80000000u;                // buffer offset past the range: the store is dropped
     static_assert(kStreamHead + EB * (MAXE + 32) <= 2 * RAW && RAW + 2 * (MAXW + 32) <= 2 * RAW,
                   "clamped slots stay inside the stream's scratch area");
     const uint32_t hl = threadIdx.x & 31u;
@@ -756,10 +757,13 @@ __device__ __forceinline__ void encode_round(const EncodeLaunch& a, const LdsPos
     const size_t slab_b = size_t(ps.slab) * geo.T * rowb + size_t(ps.cg) * kLanes * EB;
     const uint8_t* tgt = static_cast<const uint8_t*>(a.target) + slab_b;
     const uint8_t* aux = static_cast<const uint8_t*>(a.aux) + slab_b;
-    // the workgroup's streams are ncg apart in stream order: 32-bit offsets from a common base
+    // the workgroup's streams are ncg apart in stream order: 32-bit offsets from a common base,
+    // stores go through a buffer resource spanning the workgroup's scratch (span < 2^31, host-checked)
     const uint64_t sid0 = (uint64_t(ps.slab) * geo.ntb + ps.tb_begin) * geo.ncg + ps.cg;
     uint8_t* wgs = a.scratch + sid0 * (2 * RAW);
     const uint32_t sstride = geo.ncg * (2 * RAW);
+    const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
+        wgs, (short)0, int((ps.tb_end - ps.tb_begin - 1) * sstride + 2 * RAW), 0x00020000);
 
     // upper-half slots carry a bias of 32 (mbcnt_lo counts the whole lower half for them)
     const uint32_t bias_b = upper ? 32u : 0u;
@@ -779,14 +783,15 @@ __device__ __forceinline__ void encode_round(const EncodeLaunch& a, const LdsPos
         wlo[s] = whi[s] = elo[s] = ehi[s] = 0;
     }
     // target / predictor values D steps ahead (steps run backwards)
-    uint32_t tbuf[S][D], pbuf[S][D];
+    using V = std::conditional_t<EB == 1, uint8_t, uint16_t>;
+    V tbuf[S][D], pbuf[S][D];
 #pragma unroll
     for (int s = 0; s < S; ++s)
 #pragma unroll
         for (int d = 0; d < D; ++d) {
             const uint32_t o = off[s] + (kSteps - 1 - d) * rowb;
-            tbuf[s][d] = EB == 1 ? uint32_t(tgt[o]) : uint32_t(*reinterpret_cast<const uint16_t*>(tgt + o));
-            pbuf[s][d] = EB == 1 ? uint32_t(aux[o]) : uint32_t(*reinterpret_cast<const uint16_t*>(aux + o));
+            tbuf[s][d] = *reinterpret_cast<const V*>(tgt + o);
+            pbuf[s][d] = *reinterpret_cast<const V*>(aux + o);
         }
     // e4m3: zlut[0, 256) is the order-preserving map of a byte, zlut[256, 768)
     // the zigzag of (a - b) mod 256 at index 512 + a - b
@@ -803,6 +808,7 @@ __device__ __forceinline__ void encode_round(const EncodeLaunch& a, const LdsPos
         ec[s] = lenc[min(zc[s], n) * kLanes + lane];
     }
     for (int kk = kSteps - 1; kk >= 0; kk -= D) {
+        uint32_t zs[S][D];                                 // this iteration's symbols, for the escape pass
 #pragma unroll
         for (int d = 0; d < D; ++d) {
             const int k = kk - d;
@@ -811,27 +817,13 @@ __device__ __forceinline__ void encode_round(const EncodeLaunch& a, const LdsPos
             for (int s = 0; s < S; ++s) {
                 const uint32_t z = zc[s];
                 const uint4 e = ec[s];
+                zs[s][d] = z;
                 // next step's symbol and entry (step k - 1, held in ring slot d + 1)
                 const uint32_t zn = symbol_of(tbuf[s][(d + 1) % D], pbuf[s][(d + 1) % D]);
                 const uint4 en = lenc[min(zn, n) * kLanes + lane];
                 const uint32_t o = off[s] + kn * rowb;
-                tbuf[s][d] = EB == 1 ? uint32_t(tgt[o]) : uint32_t(*reinterpret_cast<const uint16_t*>(tgt + o));
-                pbuf[s][d] = EB == 1 ? uint32_t(aux[o]) : uint32_t(*reinterpret_cast<const uint16_t*>(aux + o));
-                // escaped values, in emission order (rare: the whole block is skipped by the wavefront)
-                const bool esc = (!ACT || act[s]) && z >= n;
-                const uint64_t me = __ballot(esc);
-                if (me) {
-                    const uint32_t mlo = uint32_t(me), mhi = uint32_t(me >> 32), plo = __popc(mlo);
-                    const uint32_t pk = min(elo[s], MAXE) | ((min(ehi[s], MAXE) + 32u - plo) << 16);
-                    const uint32_t slot = __builtin_amdgcn_mbcnt_hi(
-                        mhi, __builtin_amdgcn_mbcnt_lo(mlo, __builtin_amdgcn_ubfe(pk, fsh, 16)));
-                    if (esc) {
-                        if (EB == 1) wgs[ebase[s] + slot] = uint8_t(z);
-                        else *reinterpret_cast<uint16_t*>(wgs + (ebase[s] + 2 * slot)) = uint16_t(z);
-                    }
-                    elo[s] += plo;
-                    ehi[s] += __popc(mhi);
-                }
+                tbuf[s][d] = *reinterpret_cast<const V*>(tgt + o);
+                pbuf[s][d] = *reinterpret_cast<const V*>(aux + o);
                 // words leave before the state absorbs the symbol
                 uint32_t xs = x[s];
                 const bool emit = (!ACT || act[s]) && xs >= e.x;
@@ -840,14 +832,38 @@ __device__ __forceinline__ void encode_round(const EncodeLaunch& a, const LdsPos
                 const uint32_t pk = min(wlo[s], MAXW) | ((min(whi[s], MAXW) + 32u - plo) << 16);
                 const uint32_t slot =
                     __builtin_amdgcn_mbcnt_hi(mhi, __builtin_amdgcn_mbcnt_lo(mlo, __builtin_amdgcn_ubfe(pk, fsh, 16)));
-                if (emit) *reinterpret_cast<uint16_t*>(wgs + (wbase[s] + 2 * slot)) = uint16_t(xs & 0xFFFFu);
+                __builtin_amdgcn_raw_buffer_store_b16(uint16_t(xs & 0xFFFFu), wrs,
+                                                      emit ? wbase[s] + 2 * slot : kDrop, 0, 0);
                 wlo[s] += plo;
                 whi[s] += __popc(mhi);
                 xs = emit ? xs >> 16 : xs;
                 const uint32_t qt = uint32_t((uint64_t(xs) + __umulhi(xs, e.y)) >> (e.w & 31u));
-                x[s] = xs + __umul24(qt, e.z) + (e.w >> 16);    // quotient < 2^20, 4096 - f < 2^12
+                x[s] = (xs + (e.w >> 16)) + __umul24(qt, e.z);    // quotient < 2^20, 4096 - f < 2^12
                 zc[s] = zn;
                 ec[s] = en;
+            }
+        }
+        // escaped values of this iteration, in emission order (rare: skipped by the whole wavefront)
+#pragma unroll
+        for (int s = 0; s < S; ++s) {
+            uint32_t zm = zs[s][0];
+#pragma unroll
+            for (int d = 1; d < D; ++d) zm = max(zm, zs[s][d]);
+            if (__ballot((!ACT || act[s]) && zm >= n) == 0) continue;
+#pragma unroll
+            for (int d = 0; d < D; ++d) {
+                const uint32_t z = zs[s][d];
+                const bool esc = (!ACT || act[s]) && z >= n;
+                const uint64_t me = __ballot(esc);
+                const uint32_t mlo = uint32_t(me), mhi = uint32_t(me >> 32), plo = __popc(mlo);
+                const uint32_t pk = min(elo[s], MAXE) | ((min(ehi[s], MAXE) + 32u - plo) << 16);
+                const uint32_t slot =
+                    __builtin_amdgcn_mbcnt_hi(mhi, __builtin_amdgcn_mbcnt_lo(mlo, __builtin_amdgcn_ubfe(pk, fsh, 16)));
+                const uint32_t eo = esc ? ebase[s] + EB * slot : kDrop;
+                if (EB == 1) __builtin_amdgcn_raw_buffer_store_b8(uint8_t(z), wrs, eo, 0, 0);
+                else __builtin_amdgcn_raw_buffer_store_b16(uint16_t(z), wrs, eo, 0, 0);
+                elo[s] += plo;
+                ehi[s] += __popc(mhi);
             }
         }
     }
@@ -946,6 +962,9 @@ LdsGeo lds_geometry(const skv_shape& s) {
     LdsGeo g;
     g.G = (ncg % line == 0) ? line : (ncg % 2 == 0 ? 2u : 1u);
     g.tbc = std::min<uint32_t>(ntb, 256u);
+    // a workgroup's encoder scratch (tbc streams, ncg apart) is addressed with offsets below 2^31
+    const uint64_t sstride = uint64_t(ncg) * 2 * kSyms * (s.dtype == SKV_E4M3 ? 1u : 2u);
+    while (g.tbc > 1 && uint64_t(g.tbc) * sstride >= (1ull << 31)) g.tbc /= 2;
     g.ntbc = (ntb + g.tbc - 1) / g.tbc;
     g.groups = s.layers * s.kv * g.ntbc * (ncg / g.G);
     return g;
@@ -976,9 +995,9 @@ hipError_t encode_all(const EncodeLaunch& a, const DevTables& t, hipStream_t st)
         auto k = encode_lds<DT, 1, 4>;
         switch (variant().enc) {
             case 1: k = encode_lds<DT, 2, 4>; break;
-            case 2: k = encode_lds<DT, 2, 2>; break;
+            case 2: k = encode_lds<DT, 1, 8>; break;
             case 3: k = encode_lds<DT, 2, 8>; break;
-            case 4: k = encode_lds<DT, 4, 2>; break;
+            case 4: k = encode_lds<DT, 1, 16>; break;
             default: break;
         }
         hipError_t e = allow_lds(k, lb);
