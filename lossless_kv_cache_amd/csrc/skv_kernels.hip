@@ -84,19 +84,40 @@ __global__ __launch_bounds__(256) void expand_tables(const uint8_t* rec, uint32_
     }
     const uint32_t c = cum[tid];
     if (tid == 0) tn[j] = n;
-    // encode entry: renormalization bound, divisor magic, 4096 - f, start | shift.
-    // floor(x / f) = (x + mulhi(x, magic)) >> shift for every 32-bit x, with
-    // shift = ceil(log2 f) and magic = ceil(2^(32+shift) / f) - 2^32
-    // (Granlund & Montgomery, division by invariant integers).
+    // encode entry: renormalization bound f * 2^20, divisor magic m,
+    // (4096 - f) | inc << 24 and l | start << 16, where
+    // floor(x / f) = mulhi(x + inc, m) >> l for every x < 2^32 - 1.  With
+    // 2^l < f < 2^(l+1), m rounds 2^(32+l) / f up when that error is at most
+    // 2^l and down otherwise (then inc = 1); one of the two always holds
+    // (Robison, "N-bit unsigned division via N-bit multiply-add").  Powers of
+    // two shift, and f = 1 uses m = 2^32 - 1 with inc = 1.
     uint4 e = make_uint4(0u, 0u, 0u, 0u);
-    if (tid <= n) {
-        uint32_t sh = 0;
-        while ((1u << sh) < f) ++sh;
-        const uint64_t m = ((1ull << (32 + sh)) + f - 1) / f;
+    if (tid <= n && f > 0) {
+        uint32_t m, inc = 0, l = 0;
+        if ((f & (f - 1)) == 0) {
+            while ((1u << (l + 1)) <= f) ++l;                   // f = 2^l
+            if (l == 0) {
+                m = 0xFFFFFFFFu;
+                inc = 1;
+            } else {
+                m = 0x80000000u;
+                l -= 1;
+            }
+        } else {
+            while ((2u << l) <= f) ++l;
+            const uint64_t P = 1ull << (32 + l);
+            const uint64_t mu = (P + f - 1) / f;
+            if (mu * f - P <= (1ull << l)) {
+                m = uint32_t(mu);
+            } else {
+                m = uint32_t(mu - 1);
+                inc = 1;
+            }
+        }
         e.x = f << 20;
-        e.y = uint32_t(m - (1ull << 32));
-        e.z = kM - f;
-        e.w = (c << 16) | sh;
+        e.y = m;
+        e.z = (kM - f) | (inc << 24);
+        e.w = l | (c << 16);
     }
     enc[size_t(j) * 256 + tid] = e;
     fc[size_t(j) * 256 + tid] = f | (c << 16);
@@ -189,8 +210,8 @@ __global__ __launch_bounds__(256) void encode_streams(EncodeLaunch a, DevTables 
         }
         const uint4 e = t.enc[size_t(table) * 256 + s];
         emit_words(x, cnt, x >= e.x, lane, half, wfwd, MAXW);
-        const uint32_t qt = uint32_t((uint64_t(x) + __umulhi(x, e.y)) >> (e.w & 31u));   // floor(x / f)
-        x = x + qt * e.z + (e.w >> 16);
+        const uint32_t qt = __umulhi(x + (e.z >> 24), e.y) >> (e.w & 31u);    // floor(x / f)
+        x = x + (e.w >> 16) + __umul24(qt, e.z);
     }
     reinterpret_cast<uint32_t*>(area)[lane] = x;
     if (lane == 0) {
@@ -837,8 +858,8 @@ __device__ __forceinline__ void encode_round(const EncodeLaunch& a, const LdsPos
                 wlo[s] += plo;
                 whi[s] += __popc(mhi);
                 xs = emit ? xs >> 16 : xs;
-                const uint32_t qt = uint32_t((uint64_t(xs) + __umulhi(xs, e.y)) >> (e.w & 31u));
-                x[s] = (xs + (e.w >> 16)) + __umul24(qt, e.z);    // quotient < 2^20, 4096 - f < 2^12
+                const uint32_t qt = __umulhi(xs + (e.z >> 24), e.y) >> (e.w & 31u);   // floor(xs / f)
+                x[s] = (xs + (e.w >> 16)) + __umul24(qt, e.z);    // quotient < 2^20, low 24 bits: 4096 - f
                 zc[s] = zn;
                 ec[s] = en;
             }
@@ -905,6 +926,194 @@ __global__ __launch_bounds__(1024) void encode_lds(EncodeLaunch a, DevTables t, 
     for (uint32_t tb0 = ps.tb_begin + hw * S; tb0 < ps.tb_end; tb0 += nhw * S) {
         if (tb0 + S <= ps.tb_end) encode_round<DT, S, D, false>(a, ps, geo, tb0, lenc, zlut, n);
         else encode_round<DT, S, D, true>(a, ps, geo, tb0, lenc, zlut, n);
+    }
+}
+
+// --------------------------------------------------------------- tiled e4m3 encode
+// The e4m3 encoder moves data in wide pieces and gathers bytes from LDS.  Each
+// wavefront runs two streams (one per half) in 8-step tiles: a lane loads 8
+// bytes of target and of predictor (8 channels of one token), maps both to
+// the order-preserving code and subtracts them bytewise in registers, and
+// stores the 8 difference bytes in the wavefront's LDS tile; after that every
+// lane reads its own channel for the tile's 8 steps and zigzags it through a
+// 256-byte table.  Emitted words go to a 128-word LDS ring per stream and
+// leave in 128-byte chunks as soon as a chunk is full.  The scratch layout is
+// the one the compaction reads: states [0, 128), escaped values from 132 and
+// words from `raw`, both in emission order.
+constexpr uint32_t kTileSteps = 8;
+constexpr uint32_t kRingWords = 128;                      // two 64-word chunks per stream
+constexpr uint32_t kTileLds = 2 * kTileSteps * kLanes;    // difference bytes of both halves
+constexpr uint32_t kRingLds = 2 * kRingWords * 2;
+constexpr uint32_t kTileWaveLds = kTileLds + kRingLds;
+
+// bytewise order-preserving map: x ^ 0x80 for a clear sign bit, x ^ 0xFF for a set one
+__device__ __forceinline__ uint32_t ord8x4(uint32_t v) {
+    const uint32_t s = v & 0x80808080u;
+    return v ^ 0x80808080u ^ (s - (s >> 7));
+}
+// bytewise (a - b) mod 256
+__device__ __forceinline__ uint32_t sub8x4(uint32_t a, uint32_t b) {
+    return ((a | 0x80808080u) - (b & 0x7F7F7F7Fu)) ^ (~(a ^ b) & 0x80808080u);
+}
+
+template <uint32_t DT>
+__global__ __launch_bounds__(1024) void encode_tiles(EncodeLaunch a, DevTables t, uint32_t fs, LdsGeo lg) {
+    static_assert(DT == SKV_E4M3, "byte elements");
+    constexpr uint32_t RAW = kSyms;
+    constexpr uint32_t MAXE = RAW - kStreamHead;
+    constexpr uint32_t kDrop = 0x80000000u;               // buffer offset past the range: the access is dropped
+    constexpr uint32_t kChunks = RAW / 128;                // 64-word chunks that fit the words region
+    extern __shared__ __align__(16) uint8_t lds[];
+    __shared__ uint8_t zig[256];
+    const Geo geo = geometry(a.shape);
+    const LdsPos ps = lds_position(geo, lg);
+    if (!ps.valid) return;
+    const uint32_t tab0 = ps.slab * geo.C + ps.cg * kLanes;
+    uint4* lenc = reinterpret_cast<uint4*>(lds);                            // [fs symbols][32 lanes]
+    for (uint32_t i = threadIdx.x; i < kLanes * fs; i += blockDim.x) {
+        const uint32_t sym = i / kLanes, j = i % kLanes;
+        lenc[i] = t.enc[size_t(tab0 + j) * 256 + sym];
+    }
+    for (uint32_t i = threadIdx.x; i < 256; i += blockDim.x) zig[i] = uint8_t(zig8(i));
+    __syncthreads();
+
+    const uint32_t wave = threadIdx.x >> 6, nwave = blockDim.x >> 6;
+    const uint32_t hl = threadIdx.x & 31u;
+    const bool upper = (threadIdx.x & 32u) != 0;
+    const uint32_t fsh = upper ? 16u : 0u;
+    const uint32_t lane = 31u - hl;                        // format lane (reversed within the half)
+    const uint32_t n = t.n[tab0 + lane];
+    uint8_t* tile = lds + size_t(kLanes) * fs * 16 + wave * kTileWaveLds;
+    uint8_t* ring = tile + kTileLds;
+    // tile: [half][step][32 channels]; this lane loads 8 channels of one step and reads its channel back
+    const uint32_t ld_row = hl >> 2, ld_q = hl & 3u;
+    uint2* tile_st = reinterpret_cast<uint2*>(tile + (upper ? kTileSteps * kLanes : 0u) + ld_row * kLanes + ld_q * 8);
+    const uint8_t* tile_rd = tile + (upper ? kTileSteps * kLanes : 0u) + lane;
+    uint16_t* ring_h = reinterpret_cast<uint16_t*>(ring + (upper ? kRingWords * 2 : 0u));
+
+    const uint32_t rowb = geo.C;
+    const size_t slab_b = size_t(ps.slab) * geo.T * rowb + size_t(ps.cg) * kLanes;
+    const uint8_t* tgt = static_cast<const uint8_t*>(a.target) + slab_b + ld_q * 8;
+    const uint8_t* aux = static_cast<const uint8_t*>(a.aux) + slab_b + ld_q * 8;
+    const uint64_t sid0 = (uint64_t(ps.slab) * geo.ntb + ps.tb_begin) * geo.ncg + ps.cg;
+    uint8_t* wgs = a.scratch + sid0 * (2 * RAW);
+    const uint32_t sstride = geo.ncg * (2 * RAW);
+    const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
+        wgs, (short)0, int((ps.tb_end - ps.tb_begin - 1) * sstride + 2 * RAW), 0x00020000);
+
+    // z of one tile: difference bytes into LDS, then each lane's channel through the zigzag table
+    auto stage = [&](uint2 tv, uint2 pv, uint32_t* z) {
+        *tile_st = make_uint2(sub8x4(ord8x4(tv.x), ord8x4(pv.x)), sub8x4(ord8x4(tv.y), ord8x4(pv.y)));
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (uint32_t r = 0; r < kTileSteps; ++r) z[r] = zig[tile_rd[r * kLanes]];
+        __builtin_amdgcn_wave_barrier();
+    };
+
+    for (uint32_t r0 = ps.tb_begin + 2 * wave; r0 < ps.tb_end; r0 += 2 * nwave) {
+        const uint32_t tb = r0 + (upper ? 1u : 0u);
+        const bool act = tb < ps.tb_end;
+        const uint32_t tbs = act ? tb : r0;
+        const uint32_t ao = (tbs - ps.tb_begin) * sstride;
+        const uint32_t ebase = ao + kStreamHead - (upper ? 32u : 0u);   // upper-half slots carry a bias of 32
+        const uint32_t wreg = ao + RAW;
+        const uint8_t* tsrc = tgt + size_t(tbs * kSteps + ld_row) * rowb;
+        const uint8_t* psrc = aux + size_t(tbs * kSteps + ld_row) * rowb;
+        const size_t tstride = size_t(kTileSteps) * rowb;
+        constexpr int kTiles = kSteps / kTileSteps;
+
+        uint32_t zc[kTileSteps], zn[kTileSteps];
+        uint2 tv = *reinterpret_cast<const uint2*>(tsrc + (kTiles - 1) * tstride);
+        uint2 pv = *reinterpret_cast<const uint2*>(psrc + (kTiles - 1) * tstride);
+        stage(tv, pv, zc);
+        tv = *reinterpret_cast<const uint2*>(tsrc + (kTiles - 2) * tstride);
+        pv = *reinterpret_cast<const uint2*>(psrc + (kTiles - 2) * tstride);
+
+        uint32_t x = kStateLow;
+        uint32_t wp = 0;                                   // word counts: lower half | upper half << 16
+        uint32_t elo = 0, ehi = 0;                         // escape counts per half
+        uint4 ec = lenc[min(zc[kTileSteps - 1], n) * kLanes + lane];
+        for (int j = kTiles - 1; j >= 0; --j) {
+            if (j > 0) {
+                stage(tv, pv, zn);
+                if (j > 1) {
+                    tv = *reinterpret_cast<const uint2*>(tsrc + size_t(j - 2) * tstride);
+                    pv = *reinterpret_cast<const uint2*>(psrc + size_t(j - 2) * tstride);
+                }
+            }
+#pragma unroll
+            for (int r = kTileSteps - 1; r >= 0; --r) {
+                const uint4 e = ec;
+                const uint32_t znext = r > 0 ? zc[r - 1] : zn[kTileSteps - 1];
+                ec = lenc[min(znext, n) * kLanes + lane];
+                // words leave before the state absorbs the symbol (an idle half runs a copy of its
+                // partner's stream into its own ring and stores nothing)
+                uint32_t xs = x;
+                const bool emit = xs >= e.x;
+                const uint64_t mw = __ballot(emit);
+                const uint32_t mlo = uint32_t(mw), mhi = uint32_t(mw >> 32);
+                const uint32_t pp = __popc(mlo) | (__popc(mhi) << 16);
+                // ring slot: this half's count mod 128 plus the emitting lanes below (mbcnt_lo counts the
+                // entire lower half for an upper lane, which the packed base subtracts again)
+                const uint32_t pk = (wp - (pp << 16)) & 0x007F007Fu;
+                const uint32_t slot =
+                    __builtin_amdgcn_mbcnt_hi(mhi, __builtin_amdgcn_mbcnt_lo(mlo, __builtin_amdgcn_ubfe(pk, fsh, 16)));
+                if (emit) ring_h[slot & (kRingWords - 1)] = uint16_t(xs & 0xFFFFu);
+                xs = emit ? xs >> 16 : xs;
+                const uint32_t qt = __umulhi(xs + (e.z >> 24), e.y) >> (e.w & 31u);   // floor(xs / f)
+                x = (xs + (e.w >> 16)) + __umul24(qt, e.z);
+                // a completed 64-word chunk leaves the ring (at most one per step and stream)
+                const uint32_t cross = ((wp & 0x003F003Fu) + pp) & 0x00400040u;
+                if (cross) {
+                    __builtin_amdgcn_wave_barrier();
+                    const uint32_t ck = __builtin_amdgcn_ubfe(wp >> 6, fsh, 10);
+                    const uint32_t w = reinterpret_cast<const uint32_t*>(ring_h)[(ck & 1u) * 32 + hl];
+                    const bool mine = act && __builtin_amdgcn_ubfe(cross, fsh + 6, 1);
+                    __builtin_amdgcn_raw_buffer_store_b32(
+                        w, wrs, mine && ck < kChunks ? wreg + ck * 128 + 4 * hl : kDrop, 0, 0);
+                    __builtin_amdgcn_wave_barrier();
+                }
+                wp += pp;
+            }
+            // escaped values of this tile, in emission order (rare: skipped by the whole wavefront)
+            uint32_t zm = zc[0];
+#pragma unroll
+            for (uint32_t r = 1; r < kTileSteps; ++r) zm = max(zm, zc[r]);
+            if (__ballot(zm >= n) != 0) {
+#pragma unroll
+                for (int r = kTileSteps - 1; r >= 0; --r) {
+                    const bool esc = zc[r] >= n;
+                    const uint64_t me = __ballot(esc);
+                    if (me == 0) continue;
+                    const uint32_t mlo = uint32_t(me), mhi = uint32_t(me >> 32), plo = __popc(mlo);
+                    const uint32_t pk = min(elo, MAXE) | ((min(ehi, MAXE) + 32u - plo) << 16);
+                    const uint32_t slot = __builtin_amdgcn_mbcnt_hi(
+                        mhi, __builtin_amdgcn_mbcnt_lo(mlo, __builtin_amdgcn_ubfe(pk, fsh, 16)));
+                    __builtin_amdgcn_raw_buffer_store_b8(uint8_t(zc[r]), wrs, act && esc ? ebase + slot : kDrop, 0,
+                                                         0);
+                    elo += plo;
+                    ehi += __popc(mhi);
+                }
+            }
+#pragma unroll
+            for (uint32_t r = 0; r < kTileSteps; ++r) zc[r] = zn[r];
+        }
+        // the partial last chunk, the final states and the stream's counts
+        __builtin_amdgcn_wave_barrier();
+        const uint32_t cnt = __builtin_amdgcn_ubfe(wp, fsh, 16), ecnt = upper ? ehi : elo;
+        const uint32_t ck = cnt >> 6;
+        const uint32_t w = reinterpret_cast<const uint32_t*>(ring_h)[(ck & 1u) * 32 + hl];
+        __builtin_amdgcn_raw_buffer_store_b32(
+            w, wrs, act && ck < kChunks && 2 * hl < (cnt & 63u) ? wreg + ck * 128 + 4 * hl : kDrop, 0, 0);
+        __builtin_amdgcn_wave_barrier();
+        if (act) {
+            reinterpret_cast<uint32_t*>(wgs + ao)[lane] = x;
+            if (hl == 0) {
+                const uint64_t sid = sid0 + uint64_t(tb - ps.tb_begin) * geo.ncg;
+                const uint32_t bytes = (kStreamHead + 2 * cnt + ecnt + 3) & ~3u;
+                a.meta[sid] = bytes >= RAW ? 0x80000000u : (cnt | (ecnt << 14));
+            }
+        }
     }
 }
 
@@ -990,7 +1199,17 @@ hipError_t encode_all(const EncodeLaunch& a, const DevTables& t, hipStream_t st)
     const uint32_t nb = uint32_t((n + kScanBlock - 1) / kScanBlock);
     const uint32_t eg = uint32_t((n + kStreamsPerBlock - 1) / kStreamsPerBlock);
     const size_t lb = encode_lds_bytes(t, DT);
-    if (MODE == SKV_RESIDUAL && lb <= kLdsLimit && !g_force_v1 && variant().enc >= 0) {
+    const size_t lt = size_t(kLanes) * fc_stride(t) * 16 + (kLdsThreads / 64) * kTileWaveLds;
+    const bool aligned = (reinterpret_cast<uintptr_t>(a.target) | reinterpret_cast<uintptr_t>(a.aux)) % 8 == 0;
+    if (DT == SKV_E4M3 && MODE == SKV_RESIDUAL && lt <= kLdsLimit && aligned && !g_force_v1 && variant().enc == 0) {
+        const LdsGeo lg = lds_geometry(a.shape);
+        auto k = encode_tiles<SKV_E4M3>;
+        hipError_t e = allow_lds(k, lt);
+        if (e != hipSuccess) return e;
+        timed("encode_streams", st, [&] {
+            hipLaunchKernelGGL(k, dim3(lds_grid(lg)), dim3(kLdsThreads), lt, st, a, t, fc_stride(t), lg);
+        });
+    } else if (MODE == SKV_RESIDUAL && lb <= kLdsLimit && !g_force_v1 && variant().enc >= 0) {
         const LdsGeo lg = lds_geometry(a.shape);
         auto k = encode_lds<DT, 1, 4>;
         switch (variant().enc) {

@@ -129,6 +129,30 @@ def test_edge_inputs(skv, orc, kind):
     full_compare(skv, orc, t, p, tabs, oshape, f"edge {kind}")
 
 
+@pytest.mark.parametrize("kind", ["equal", "random", "maxz", "escapes", "mixed"])
+def test_edge_inputs_e4m3(skv, orc, kind):
+    """The same degenerate inputs for byte elements, on a grid with an odd
+    number of token blocks (a wavefront runs one stream and idles the other
+    half); "mixed" alternates compressible and raw token blocks."""
+    cfg = gen.Config(92, "edge-e4m3", "e4m3", 2, 2, 640, 96)
+    t, p, tabs, oshape = residual_case(skv, orc, cfg)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(19)
+    if kind == "equal":
+        t = p.clone()
+    elif kind == "random":
+        t = torch.randint(0, 256, p.shape, generator=g, device="cuda", dtype=torch.int32).to(torch.uint8)
+    elif kind == "maxz":
+        t = (p.to(torch.int32) ^ 0x80).to(torch.uint8)            # sign flip: residual near -128
+    elif kind == "escapes":
+        t = ((p.to(torch.int32) + 40) & 0xFF).to(torch.uint8)     # |r| about 40: past every direct range
+    elif kind == "mixed":
+        r = torch.randint(0, 256, p.shape, generator=g, device="cuda", dtype=torch.int32).to(torch.uint8)
+        blk = (torch.arange(p.shape[2], device="cuda") // 128) % 2 == 1
+        t = torch.where(blk[None, None, :, None], r, t)
+    full_compare(skv, orc, t, p, tabs, oshape, f"edge e4m3 {kind}")
+
+
 def test_corruption_and_wrong_tables(skv, orc):
     cfg = gen.Config(92, "corrupt-bf16", "bf16", 1, 2, 256, 64)
     t, p, tabs, oshape = residual_case(skv, orc, cfg)
