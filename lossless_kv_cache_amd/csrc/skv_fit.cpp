@@ -126,12 +126,14 @@ void round_freqs(const std::vector<double>& q, uint32_t* f) {
     }
 }
 
-// Table from cell masses over z = 0..254, escape probability pe.
-Record make_record(const double* mass, double pe) {
+// Table from cell masses over z = 0..254, escape probability pe; the direct
+// range covers every cell of mass >= 2^-12 and at least the first nmin symbols.
+Record make_record(const double* mass, double pe, uint32_t nmin = 1) {
     Record r{};
     uint32_t n = 1;
     for (uint32_t z = 0; z < 255; ++z)
         if (mass[z] >= 1.0 / double(kM)) n = z + 1;
+    n = std::max(n, std::min(nmin, 255u));
     double sum = 0.0;
     for (uint32_t z = 0; z < n; ++z) sum += mass[z];
     const double scale = (1.0 - pe) / sum;
@@ -151,6 +153,18 @@ void put_record(uint8_t* dst, const Record& r) {
 
 void masses_for(double m, double b, double* out) {
     for (uint32_t z = 0; z < 255; ++z) out[z] = laplace_cell(double(unzig(z)), m, b);
+}
+
+// Smallest direct range (z in [1, 255]) that leaves at most total / 1024 of a
+// slab's calibration symbols to escape.  The Laplace fit sets the direct range
+// of each table from its masses; where the data's tail is heavier than the
+// Laplace's, this floor keeps escapes near 1/1024 of the symbols.
+uint32_t slab_tail_floor(const std::vector<uint64_t>& above_count_by_z, uint64_t total) {
+    // above_count_by_z[z] = number of calibration symbols >= z (z = 0..255)
+    const uint64_t budget = total / 1024;
+    uint32_t z = 1;
+    while (z < 255 && above_count_by_z[z] > budget) ++z;
+    return z;
 }
 
 }  // namespace
@@ -181,7 +195,14 @@ int fit_tables_host(const skv_shape& s, const void* calib_t, const void* calib_a
             return nbits == 8 ? static_cast<const uint8_t*>(a)[i] : static_cast<const uint16_t*>(a)[i];
         };
         std::vector<int32_t> r(N);
+        std::vector<uint64_t> above(257);
         for (uint64_t sl = 0; sl < slabs; ++sl) {
+            // the slab's pooled symbol counts, turned into counts of symbols >= z
+            std::fill(above.begin(), above.end(), 0ull);
+            for (size_t i = size_t(sl) * N * C, e = i + size_t(N) * C; i < e; ++i)
+                above[std::min<uint32_t>(zig_of(ordered_residual(elem(calib_t, i), elem(calib_a, i), nbits), nbits), 255u)] += 1;
+            for (int z = 254; z >= 0; --z) above[size_t(z)] += above[size_t(z) + 1];
+            const uint32_t floor_n = slab_tail_floor(above, uint64_t(N) * C);
             for (uint32_t c = 0; c < C; ++c) {
                 double acc = 0.0;
                 uint64_t used = 0;
@@ -197,11 +218,11 @@ int fit_tables_host(const skv_shape& s, const void* calib_t, const void* calib_a
                 double b = used ? acc / double(used) : 0.0;
                 b = std::max(b, 0.05);
                 masses_for(0.0, b, mass);
-                Record R = make_record(mass, 0.0);   // direct range only depends on the masses
+                Record R = make_record(mass, 0.0, floor_n);   // direct range does not depend on pe
                 uint64_t esc = 0;
                 for (uint32_t t = 0; t < N; ++t) esc += zig_of(r[t], nbits) >= R.n;
                 const double pe = (double(esc) + 1.0) / (double(N) + 2.0);
-                put_record(rec + (sl * C + c) * kTableRecord, make_record(mass, pe));
+                put_record(rec + (sl * C + c) * kTableRecord, make_record(mass, pe, floor_n));
             }
         }
         return SKV_OK;

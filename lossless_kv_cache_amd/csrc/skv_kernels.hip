@@ -1117,6 +1117,366 @@ __global__ __launch_bounds__(1024) void encode_tiles(EncodeLaunch a, DevTables t
     }
 }
 
+// --------------------------------------------------------------- tiled e4m3 decode
+// One workgroup owns the 32 tables of a channel group: the complete
+// slot -> symbol maps (4096 bytes per table) and per symbol the 16-bit
+// values 4096 - frequency and start, so a pop is one map byte, two 16-bit
+// reads and x' = x - (x >> 12) * (4096 - f) - start.  Each half wavefront runs
+// two streams as independent chains (4 streams per wavefront), which hides
+// the latency of the dependent LDS reads of a step.  Words come from a
+// 128-word ring per stream in LDS, refilled with one 32-word chunk per 4-step
+// tile; a chunk is requested one tile before it is written and predictor rows
+// two tiles before they are used, so global loads are rarely waited for.  A
+// tile whose steps needed a word the ring did not hold yet is decoded again
+// from its saved state with words read from global memory.  A step only
+// flags escapes; a tile with any escaped symbol ranks and reads them at its
+// end.  Symbols of 4 steps then go through a 4 x 32 byte tile in LDS so that
+// every lane reconstructs 4 channels of one token with bytewise arithmetic on
+// 4-byte predictor loads and stores.
+constexpr uint32_t kDecChains = 2;                           // streams per half wavefront
+constexpr uint32_t kDecTile = 4;                             // steps per tile
+constexpr uint32_t kDecRing = 128;                           // words per stream ring
+constexpr uint32_t kDecChunk = 32;                           // words per ring chunk
+constexpr uint32_t kDecStreams = (1024 / 32) * kDecChains;   // streams in flight per workgroup
+constexpr uint32_t kDecEscWin = 128;                         // bytes of escape region per stream held in a register
+
+// LDS: maps [32][4096] | 4096 - f [fs][32] u16 | start [fs][32] u16 | rings [64][128 words] | tiles [64][4][32]
+__host__ __device__ constexpr uint32_t dec_e4m3_rings(uint32_t fs) {
+    return (kLanes * kM + 2 * fs * kLanes * 2 + 255) & ~255u;
+}
+__host__ __device__ constexpr uint32_t dec_e4m3_lds(uint32_t fs) {
+    return dec_e4m3_rings(fs) + kDecStreams * (2 * kDecRing + kDecTile * kLanes);
+}
+
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+typedef __attribute__((address_space(3))) uint16_t lds_u16;
+typedef __attribute__((address_space(3))) uint32_t lds_u32;
+
+// bytewise helpers on 4 packed e4m3 codes / symbols
+__device__ __forceinline__ uint32_t sflip8x4(uint32_t v) {   // v ^ 0x7F in the bytes whose sign bit is set
+    const uint32_t s = v & 0x80808080u;
+    return v ^ (s - (s >> 7));
+}
+__device__ __forceinline__ uint32_t unzig8x4(uint32_t z) {
+    const uint32_t l = z & 0x01010101u;
+    return ((z >> 1) & 0x7F7F7F7Fu) ^ ((l << 8) - l);
+}
+__device__ __forceinline__ uint32_t add8x4(uint32_t a, uint32_t b) {
+    return ((a & 0x7F7F7F7Fu) + (b & 0x7F7F7F7Fu)) ^ ((a ^ b) & 0x80808080u);
+}
+// target codes from predictor codes and symbols: the order-preserving code
+// of a byte is flip(u) ^ 0x80, so ord(t) = ord(p) + r mod 256 becomes
+// flip(t) = flip(p) + r mod 256 (flip is its own inverse)
+__device__ __forceinline__ uint32_t recon8x4(uint32_t p, uint32_t z) {
+    return sflip8x4(add8x4(sflip8x4(p), unzig8x4(z)));
+}
+
+// Rank of each flagged lane among the flagged lanes of its half, plus the
+// half's count from a packed wave-uniform counter (lower half in bits 0..15,
+// upper half in bits 16..31 with a bias of 256); advances the counter.
+__device__ __forceinline__ uint32_t half_rank(uint64_t m, uint32_t& C, uint32_t fsh) {
+    const uint32_t lo = uint32_t(m), hi = uint32_t(m >> 32);
+    const uint32_t clo = __popc(lo);
+    const uint32_t pk = C - (clo << 16);           // the upper half's mbcnt_lo counts the whole lower half
+    C = pk + clo + (uint32_t(__popcll(m)) << 16);
+    return __builtin_amdgcn_mbcnt_hi(hi, __builtin_amdgcn_mbcnt_lo(lo, __builtin_amdgcn_ubfe(pk, fsh, 16)));
+}
+
+// Decoder state of one chain: the lane's rANS state and the packed counts
+// of words and escaped values consumed by the two streams of the chain.
+struct DecState {
+    uint32_t x, P, E;
+};
+
+struct DecLane {
+    uint32_t mapb, gb, fsh, n;
+    __amdgpu_buffer_rsrc_t rs;
+};
+
+struct DecChain {
+    uint32_t ringb, tileb, wofs, eofs;
+};
+
+// The steps of one tile for both chains.  GLOBAL = false takes words from the
+// rings, GLOBAL = true from the streams in memory (a tile decoded again).  The
+// step is branch-free so that the two chains' instructions interleave.
+template <bool GLOBAL, uint32_t FS>
+__device__ __forceinline__ void dec_tile_steps(DecState (&st)[kDecChains], const DecLane& L,
+                                               const DecChain (&ch)[kDecChains], uint32_t (&sy)[kDecChains][kDecTile],
+                                               uint64_t& anyesc) {
+#pragma unroll
+    for (uint32_t r = 0; r < kDecTile; ++r) {
+#pragma unroll
+        for (uint32_t c = 0; c < kDecChains; ++c) {
+            const uint32_t x = st[c].x;
+            const uint32_t sym = *reinterpret_cast<const lds_u8*>((x & (kM - 1u)) | L.mapb);
+            const uint32_t ga = (sym << 6) + L.gb;
+            const uint32_t g = *reinterpret_cast<const lds_u16*>(ga);                 // 4096 - f
+            const uint32_t cu = *reinterpret_cast<const lds_u16*>(ga + FS * kLanes * 2);   // start
+            const uint32_t xn = x - (__umul24(x >> kProbBits, g) + cu);
+            // refill in lane order
+            const bool need = xn < kStateLow;
+            const uint32_t idx = half_rank(__ballot(need), st[c].P, L.fsh);
+            uint32_t w;
+            if (GLOBAL) w = __builtin_amdgcn_raw_buffer_load_b16(L.rs, ch[c].wofs + 2 * idx, 0, 0);
+            // volatile: the read stays unconditional, with no branch around it
+            else w = *reinterpret_cast<const volatile lds_u16*>(((idx << 1) & (2 * kDecRing - 2)) | ch[c].ringb);
+            st[c].x = need ? ((xn << 16) | w) : xn;
+            anyesc |= __ballot(sym == L.n);
+            sy[c][r] = sym;
+        }
+    }
+}
+
+template <uint32_t FS>
+__global__ __launch_bounds__(1024, 1) void decode_e4m3(DecodeLaunch a, DevTables t, LdsGeo lg) {
+    constexpr uint32_t OFF_G = kLanes * kM;
+    constexpr uint32_t OFF_C = OFF_G + FS * kLanes * 2;
+    constexpr uint32_t OFF_R = dec_e4m3_rings(FS);
+    constexpr uint32_t OFF_T = OFF_R + kDecStreams * 2 * kDecRing;
+    constexpr uint32_t kTiles = kSteps / kDecTile;
+    extern __shared__ __align__(16) uint8_t lds[];
+    const uint32_t lb = uint32_t(uintptr_t(lds));                  // LDS offset of the dynamic block
+    const Geo geo = geometry(a.shape);
+    const LdsPos ps = lds_position(geo, lg);
+    if (!ps.valid) return;
+    const uint32_t tid = threadIdx.x;
+    const uint32_t tab0 = ps.slab * geo.C + ps.cg * kLanes;
+    uint16_t* lg16 = reinterpret_cast<uint16_t*>(lds + OFF_G);    // [FS symbols][32 lanes]
+    uint16_t* lc16 = reinterpret_cast<uint16_t*>(lds + OFF_C);
+    for (uint32_t i = tid; i < FS * kLanes; i += blockDim.x) {
+        const uint32_t fc = t.fc[size_t(tab0 + i % kLanes) * 256 + i / kLanes];
+        lg16[i] = uint16_t(kM - (fc & 0xFFFFu));
+        lc16[i] = uint16_t(fc >> 16);                             // rows past n: start 4096
+    }
+    __syncthreads();
+    {
+        // maps: thread (j, part) fills slots [128 part, 128 part + 128) of table j
+        const uint32_t j = tid >> 5, part = tid & 31u;
+        const uint32_t nn = t.n[tab0 + j];
+        uint32_t s = 0, slot = part * 128u;
+        uint32_t* dst = reinterpret_cast<uint32_t*>(lds + j * kM + slot);
+        for (uint32_t w = 0; w < 32; ++w) {
+            uint32_t word = 0;
+            for (uint32_t q = 0; q < 4; ++q, ++slot) {
+                while (s < nn && lc16[(s + 1) * kLanes + j] <= slot) ++s;
+                word |= s << (8 * q);
+            }
+            dst[w] = word;
+        }
+    }
+    __syncthreads();
+
+    const uint32_t wave = tid >> 6, nwave = blockDim.x >> 6;
+    const uint32_t hl = tid & 31u;
+    const bool upper = (tid & 32u) != 0;
+    const uint32_t r4 = hl >> 3, q4 = (hl & 7u) * 4;               // tile-domain row and byte column
+
+    const uint32_t rowb = geo.C;
+    const uint64_t* index = reinterpret_cast<const uint64_t*>(a.in + kHeaderBytes);
+    const uint8_t* pay = a.in + kHeaderBytes + 8 * (a.n_streams + 1);
+    const uint64_t sfirst = (uint64_t(ps.slab) * geo.ntb + ps.tb_begin) * geo.ncg + ps.cg;
+    const uint64_t slast = (uint64_t(ps.slab) * geo.ntb + ps.tb_end - 1) * geo.ncg + ps.cg;
+    const uint64_t wlo = index[sfirst] & ~kRawBit, whi = index[slast + 1] & ~kRawBit;
+    if (whi < wlo || whi > a.payload_bytes || whi - wlo >= (1ull << 31)) {
+        if (tid == 0) atomicOr(a.status, 1u);
+        return;
+    }
+    DecLane L;
+    L.mapb = lb + hl * kM;
+    L.gb = lb + OFF_G + hl * 2;
+    L.fsh = upper ? 16u : 0u;
+    L.n = t.n[tab0 + hl];
+    // every payload read of the workgroup goes through one range-checked resource
+    L.rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(pay + wlo), (short)0, int(whi - wlo), 0x00020000);
+    // predictor and output rows of the slab's channel group, 32-bit offsets from one base each
+    const size_t slab_b = size_t(ps.slab) * geo.T * rowb + size_t(ps.cg) * kLanes;
+    const __amdgpu_buffer_rsrc_t prs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<void*>(static_cast<const void*>(static_cast<const uint8_t*>(a.aux) + slab_b)), (short)0,
+        int(uint32_t(geo.T - 1) * rowb + kLanes), 0x00020000);
+    const __amdgpu_buffer_rsrc_t ors = __builtin_amdgcn_make_buffer_rsrc(
+        static_cast<void*>(static_cast<uint8_t*>(a.out) + slab_b), (short)0, int(uint32_t(geo.T - 1) * rowb + kLanes),
+        0x00020000);
+    bool bad = false;
+
+    for (uint32_t tb0 = ps.tb_begin + 2 * kDecChains * wave; tb0 < ps.tb_end; tb0 += 2 * kDecChains * nwave) {
+        DecChain ch[kDecChains];
+        DecState st[kDecChains];
+        uint32_t tb[kDecChains], nw[kDecChains], size[kDecChains], rel[kDecChains];
+        uint32_t woff[kDecChains], cw[kDecChains], pva[kDecChains], pvb[kDecChains], rowo[kDecChains];
+        uint32_t ew[kDecChains], ea[kDecChains];
+        uint32_t hi_lo[kDecChains], hi_hi[kDecChains], ld_lo[kDecChains], ld_hi[kDecChains];
+        uint32_t lim_lo[kDecChains], lim_hi[kDecChains];
+        bool coded[kDecChains], raw[kDecChains];
+#pragma unroll
+        for (uint32_t c = 0; c < kDecChains; ++c) {
+            const uint32_t hs = (tid >> 5) * kDecChains + c;          // stream slot in the workgroup
+            ch[c].ringb = lb + OFF_R + hs * 2 * kDecRing;             // 256-byte aligned
+            ch[c].tileb = lb + OFF_T + hs * kDecTile * kLanes + hl;
+            tb[c] = tb0 + 2 * c + (upper ? 1u : 0u);
+            // byte offset of this lane's first tile-domain row; an absent stream reads rows of tb0
+            rowo[c] = ((tb[c] < ps.tb_end ? tb[c] : tb0) * kSteps + r4) * rowb + q4;
+            // ---- stream header (every lane of the half reads the same entries)
+            uint32_t x = kStateLow;
+            nw[c] = size[c] = rel[c] = 0;
+            coded[c] = raw[c] = false;
+            if (tb[c] < ps.tb_end) {
+                const uint64_t sid = (uint64_t(ps.slab) * geo.ntb + tb[c]) * geo.ncg + ps.cg;
+                const uint64_t e0 = index[sid], e1 = index[sid + 1];
+                const uint64_t o = e0 & ~kRawBit, end = e1 & ~kRawBit;
+                if (end < o || o < wlo || end > whi) {
+                    bad = true;
+                } else if (e0 & kRawBit) {
+                    if (end - o != kSyms) bad = true;
+                    else raw[c] = true;
+                    rel[c] = uint32_t(o - wlo);
+                } else {
+                    size[c] = uint32_t(end - o);
+                    rel[c] = uint32_t(o - wlo);
+                    if (size[c] < kStreamHead || size[c] % 4 != 0) {
+                        bad = true;
+                    } else {
+                        nw[c] = __builtin_amdgcn_raw_buffer_load_b32(L.rs, rel[c] + 128, 0, 0);
+                        if (nw[c] > (size[c] - kStreamHead) / 2) {
+                            bad = true;
+                        } else {
+                            coded[c] = true;
+                            x = __builtin_amdgcn_raw_buffer_load_b32(L.rs, rel[c] + 4 * hl, 0, 0);
+                            if (x < kStateLow) bad = true;
+                        }
+                    }
+                }
+            }
+            const uint64_t cm = __ballot(coded[c]);
+            // word and escape offsets in the window, with the upper half's bias of 256 taken out
+            woff[c] = coded[c] ? rel[c] + kStreamHead : 0u;
+            ch[c].wofs = woff[c] - (upper ? 512u : 0u);
+            ch[c].eofs = woff[c] + 2 * nw[c] - (upper ? 256u : 0u);
+            // window: the 4-byte aligned dwords from the start of the escape region (which sits 0 or
+            // 2 bytes past a dword boundary); a stream's dwords never cross its 4-byte padded end
+            ea[c] = (woff[c] + 2 * nw[c]) & 3u;
+            ew[c] = __builtin_amdgcn_raw_buffer_load_b32(L.rs, ((woff[c] + 2 * nw[c]) & ~3u) + 4 * hl, 0, 0);
+            // ring: chunk k (words [32k, 32k + 32)) sits in slot k % 4; chunks 0 and 1 now,
+            // chunk 2 requested for the first tile end
+            lds_u16* ring16 = reinterpret_cast<lds_u16*>(ch[c].ringb);
+            ring16[hl] = __builtin_amdgcn_raw_buffer_load_b16(L.rs, woff[c] + 2 * hl, 0, 0);
+            ring16[kDecChunk + hl] = __builtin_amdgcn_raw_buffer_load_b16(L.rs, woff[c] + 2 * kDecChunk + 2 * hl, 0, 0);
+            hi_lo[c] = hi_hi[c] = ld_lo[c] = ld_hi[c] = 2;            // chunks present / chunk in flight
+            cw[c] = __builtin_amdgcn_raw_buffer_load_b16(L.rs, woff[c] + 4 * kDecChunk + 2 * hl, 0, 0);
+            // a half without a coded stream never asks for a tile to be decoded again
+            lim_lo[c] = (cm & 1u) ? 2 * kDecChunk : 0xFFFFFFFFu;
+            lim_hi[c] = (cm >> 32) ? 2 * kDecChunk + 256u : 0xFFFFFFFFu;
+            st[c] = DecState{x, 256u << 16, 256u << 16};
+        }
+#pragma unroll
+        for (uint32_t c = 0; c < kDecChains; ++c) {
+            pva[c] = __builtin_amdgcn_raw_buffer_load_b32(prs, rowo[c], 0, 0);
+            pvb[c] = __builtin_amdgcn_raw_buffer_load_b32(prs, rowo[c] + kDecTile * rowb, 0, 0);
+        }
+        __builtin_amdgcn_wave_barrier();
+
+        // one tile: its steps, escaped values, reconstruction, ring upkeep; pv holds the
+        // tile's predictor row and is reloaded with the row two tiles ahead
+        auto tile_at = [&](uint32_t T, uint32_t (&pv)[kDecChains]) {
+            uint32_t sy[kDecChains][kDecTile];
+            uint64_t anyesc = 0;
+            const DecState s0 = st[0], s1 = st[1];
+            dec_tile_steps<false, FS>(st, L, ch, sy, anyesc);
+            bool over = false;
+#pragma unroll
+            for (uint32_t c = 0; c < kDecChains; ++c)
+                over |= (st[c].P & 0xFFFFu) > lim_lo[c] || (st[c].P >> 16) > lim_hi[c];
+            if (__builtin_expect(over, 0)) {
+                st[0] = s0;
+                st[1] = s1;
+                anyesc = 0;
+                dec_tile_steps<true, FS>(st, L, ch, sy, anyesc);
+            }
+            if (anyesc != 0) {
+                // escaped values in decode order (step, then lane); the first 128 of a stream
+                // come from the window register, later ones from the escape region in memory
+#pragma unroll
+                for (uint32_t r = 0; r < kDecTile; ++r)
+#pragma unroll
+                    for (uint32_t c = 0; c < kDecChains; ++c) {
+                        const bool esc = sy[c][r] == L.n;
+                        const uint64_t m = __ballot(esc);
+                        if (m == 0) continue;
+                        const uint32_t eidx = half_rank(m, st[c].E, L.fsh);
+                        // byte of the window holding this lane's escaped value
+                        const uint32_t pos = eidx - (upper ? 256u : 0u) + ea[c];
+                        const uint32_t wv = __builtin_amdgcn_ds_bpermute(
+                            int(((pos >> 2) + (upper ? 32u : 0u)) << 2), int(ew[c]));
+                        uint32_t v = (wv >> ((pos & 3u) * 8)) & 0xFFu;
+                        if (__ballot(esc && pos >= kDecEscWin) != 0) {
+                            const uint32_t g = __builtin_amdgcn_raw_buffer_load_b8(L.rs, ch[c].eofs + eidx, 0, 0);
+                            v = pos >= kDecEscWin ? g : v;
+                        }
+                        // a canonical encoder codes a value below n directly
+                        if (esc && coded[c] && v < L.n) bad = true;
+                        sy[c][r] = esc ? v : sy[c][r];
+                    }
+            }
+#pragma unroll
+            for (uint32_t c = 0; c < kDecChains; ++c)
+#pragma unroll
+                for (uint32_t r = 0; r < kDecTile; ++r)
+                    *reinterpret_cast<lds_u8*>(ch[c].tileb + r * kLanes) = uint8_t(sy[c][r]);
+            __builtin_amdgcn_wave_barrier();
+#pragma unroll
+            for (uint32_t c = 0; c < kDecChains; ++c) {
+                const uint32_t zt = *reinterpret_cast<const lds_u32*>(ch[c].tileb - hl + r4 * kLanes + q4);
+                if (coded[c])
+                    __builtin_amdgcn_raw_buffer_store_b32(recon8x4(pv[c], zt), ors, rowo[c] + T * kDecTile * rowb, 0, 0);
+                // the chunk requested one tile ago goes into its slot; request the next one
+                reinterpret_cast<lds_u16*>(ch[c].ringb)[(upper ? ld_hi[c] : ld_lo[c]) % 4 * kDecChunk + hl] = cw[c];
+                hi_lo[c] = max(hi_lo[c], ld_lo[c] + 1);
+                hi_hi[c] = max(hi_hi[c], ld_hi[c] + 1);
+                ld_lo[c] = min(hi_lo[c], (st[c].P & 0xFFFFu) / kDecChunk + 3);
+                ld_hi[c] = min(hi_hi[c], ((st[c].P >> 16) - 256u) / kDecChunk + 3);
+                if (lim_lo[c] != 0xFFFFFFFFu) lim_lo[c] = kDecChunk * hi_lo[c];
+                if (lim_hi[c] != 0xFFFFFFFFu) lim_hi[c] = kDecChunk * hi_hi[c] + 256u;
+                cw[c] = __builtin_amdgcn_raw_buffer_load_b16(
+                    L.rs, woff[c] + 2 * kDecChunk * (upper ? ld_hi[c] : ld_lo[c]) + 2 * hl, 0, 0);
+            }
+#pragma unroll
+            for (uint32_t c = 0; c < kDecChains; ++c)
+                if (T + 2 < kTiles)
+                    pv[c] = __builtin_amdgcn_raw_buffer_load_b32(prs, rowo[c] + (T + 2) * kDecTile * rowb, 0, 0);
+            __builtin_amdgcn_wave_barrier();
+        };
+        for (uint32_t T = 0; T < kTiles; T += 2) {
+            tile_at(T, pva);
+            tile_at(T + 1, pvb);
+        }
+#pragma unroll
+        for (uint32_t c = 0; c < kDecChains; ++c) {
+            // ---- stream checks: states back at L, every word and escape consumed, zero pad
+            if (coded[c]) {
+                const uint32_t pc = upper ? (st[c].P >> 16) - 256u : st[c].P & 0xFFFFu;
+                const uint32_t ec = upper ? (st[c].E >> 16) - 256u : st[c].E & 0xFFFFu;
+                const uint32_t used = kStreamHead + 2 * nw[c] + ec;
+                if (st[c].x != kStateLow || pc != nw[c] || used > size[c]) bad = true;
+                else if (((used + 3) & ~3u) != size[c]) bad = true;
+                else if (hl < size[c] - used &&
+                         __builtin_amdgcn_raw_buffer_load_b8(L.rs, rel[c] + used + hl, 0, 0) != 0)
+                    bad = true;
+            }
+            if (raw[c]) {
+                // raw stream: its 4096 codes in (step, lane) order, copied row by row
+                for (uint32_t T = 0; T < kTiles; ++T) {
+                    const uint32_t k = T * kDecTile + r4;
+                    __builtin_amdgcn_raw_buffer_store_b32(
+                        __builtin_amdgcn_raw_buffer_load_b32(L.rs, rel[c] + k * kLanes + q4, 0, 0), ors,
+                        rowo[c] + T * kDecTile * rowb, 0, 0);
+                }
+            }
+        }
+        __builtin_amdgcn_wave_barrier();
+    }
+    if (bad) atomicOr(a.status, 1u);
+}
+
 __global__ void clear_u32(uint32_t* p, uint32_t n) {
     const uint32_t i = blockIdx.x * blockDim.x + threadIdx.x;
     if (i < n) p[i] = 0u;
@@ -1248,6 +1608,19 @@ hipError_t encode_all(const EncodeLaunch& a, const DevTables& t, hipStream_t st)
 template <uint32_t DT, uint32_t MODE>
 hipError_t decode_all(const DecodeLaunch& a, const DevTables& t, hipStream_t st) {
     const int v = variant().dec;
+    if (DT == SKV_E4M3 && MODE == SKV_RESIDUAL && !g_force_v1 && v == 0 && t.max_n + 1 <= 64 &&
+        dec_e4m3_lds(64) <= kLdsLimit) {
+        const LdsGeo lg = lds_geometry(a.shape);
+        const bool small = t.max_n + 1 <= 32;
+        auto k = small ? decode_e4m3<32> : decode_e4m3<64>;
+        const size_t lb = small ? dec_e4m3_lds(32) : dec_e4m3_lds(64);
+        hipError_t e = allow_lds(k, lb);
+        if (e != hipSuccess) return e;
+        timed("decode_streams", st, [&] {
+            hipLaunchKernelGGL(k, dim3(lds_grid(lg)), dim3(kLdsThreads), lb, st, a, t, lg);
+        });
+        return hipGetLastError();
+    }
     const bool half = v != 1 && v != 3;
     const size_t lb = decode_lds_bytes(t, DT, half);
     if (MODE == SKV_RESIDUAL && lb <= kLdsLimit && !g_force_v1 && v >= 0) {

@@ -724,6 +724,25 @@ static uint32_t direct_count(const double* p) {
     return n;
 }
 
+/* Calibration tail of one (layer, K|V) slab: the smallest z in [1, 255] such
+ * that at most floor(count / 1024) of the slab's calibration symbols are z or
+ * larger.  Every table of the slab codes at least the symbols below it
+ * directly, so that escapes stay near 1/1024 of the symbols even where the
+ * Laplace tail is lighter than the data's. */
+static uint32_t tail_count(const uint32_t* z, uint64_t count) {
+    uint64_t hist[256] = {0};
+    for (uint64_t i = 0; i < count; ++i) hist[z[i] > 255 ? 255 : z[i]] += 1;
+    uint64_t allow = count / 1024, above = 0;
+    uint32_t q = 255;
+    /* walk down from 255: q stays the smallest z whose tail count is within the allowance */
+    for (uint32_t v = 255; v >= 1; --v) {
+        above += hist[v];
+        if (above > allow) break;
+        q = v;
+    }
+    return q;
+}
+
 /* Build one table from cell masses p[0..254], direct count n and escape
  * probability pe: direct masses are rescaled to 1 - pe, ESC gets pe. */
 static void build_table(const double* p, uint32_t n, double pe, uint8_t* dst) {
@@ -775,7 +794,15 @@ int skvo_fit_tables(const skvo_shape* s, const void* calib_t, const void* calib_
     if (s->mode == MODE_RESIDUAL) {
         int nbits = elem_bits(s->dtype);
         uint64_t slabs = (uint64_t)s->layers * s->kv;
-        for (uint64_t sl = 0; sl < slabs; ++sl)
+        uint64_t per_slab = (uint64_t)calib_tokens * C;
+        uint32_t* zs = (uint32_t*)malloc(per_slab * sizeof(uint32_t));
+        if (!zs) return E_ARG;
+        for (uint64_t sl = 0; sl < slabs; ++sl) {
+            for (uint64_t i = 0; i < per_slab; ++i) {
+                size_t idx = (size_t)sl * per_slab + i;
+                zs[i] = skvo_zigzag(skvo_residual(load_elem(calib_t, s->dtype, idx), load_elem(calib_a, s->dtype, idx), nbits));
+            }
+            uint32_t zq = tail_count(zs, per_slab);
             for (size_t ch = 0; ch < C; ++ch) {
                 double sum = 0.0;
                 uint64_t cnt = 0;
@@ -788,6 +815,7 @@ int skvo_fit_tables(const skvo_shape* s, const void* calib_t, const void* calib_
                 if (b < 0.05) b = 0.05;
                 for (uint32_t z = 0; z < 255; ++z) p[z] = skvo_cell_mass((double)skvo_unzigzag(z), 0.0, b);
                 uint32_t n = direct_count(p);
+                if (n < zq) n = zq;   /* zq <= 255 */
                 uint64_t esc = 0;
                 for (uint32_t t = 0; t < calib_tokens; ++t) {
                     size_t idx = ((size_t)sl * calib_tokens + t) * C + ch;
@@ -797,6 +825,8 @@ int skvo_fit_tables(const skvo_shape* s, const void* calib_t, const void* calib_
                 double pe = ((double)esc + 1.0) / ((double)calib_tokens + 2.0);
                 build_table(p, n, pe, blob + SKVO_HDR + (sl * C + ch) * SKVO_TAB_BYTES);
             }
+        }
+        free(zs);
         return E_OK;
     }
     const int16_t* coef = (const int16_t*)calib_t;

@@ -31,16 +31,49 @@ def test_cell_mass_matches_scipy(orc, m, b):
             assert got == pytest.approx(want, rel=1e-9, abs=1e-15)
 
 
-def _check_table(n, f, masses, pe):
+def _zigzag_residuals(t, p, nbits):
+    """Zigzag of the ordered-integer residual, vectorized (the definition:
+    order-preserving integer of each bit pattern, difference mod 2^N read as
+    signed, zigzag)."""
+    span, half = 1 << nbits, 1 << (nbits - 1)
+    t = np.asarray(t).astype(np.int64) & (span - 1)
+    p = np.asarray(p).astype(np.int64) & (span - 1)
+    ordv = lambda u: np.where(u & half, (span - 1) ^ u, u ^ half)
+    r = (ordv(t) - ordv(p)) % span
+    r = np.where(r >= half, r - span, r)
+    return np.where(r >= 0, 2 * r, -2 * r - 1)
+
+
+def _tail_floor(z):
+    """Smallest z0 in [1, 255] with at most len(z) // 1024 symbols >= z0."""
+    allow = len(z) // 1024
+    for z0 in range(1, 256):
+        if np.count_nonzero(z >= z0) <= allow:
+            return z0
+    return 255
+
+
+def _check_table(n, f, masses, pe, floor_n=1):
     f = np.asarray(f, dtype=np.int64)
     assert f.sum() == 4096 and (f >= 1).all() and 1 <= n <= 255 and len(f) == n + 1
-    # direct range: z = 0 always, then up to the last z <= 254 with mass >= 2^-12
+    # direct range: z = 0 always, then up to the last z <= 254 with mass >= 2^-12,
+    # and at least the slab's calibration tail floor
     big = [z for z in range(255) if masses[z] >= 2.0 ** -12]
-    assert n == max([0] + big) + 1
+    assert n == max(max([0] + big) + 1, floor_n)
     q = np.empty(n + 1)
     q[:n] = 4096.0 * masses[:n] * (1.0 - pe) / masses[:n].sum()
     q[n] = 4096.0 * pe
-    assert np.all(np.abs(f - np.maximum(q, 1.0)) <= 1.0 + 1e-9)
+    # the quantization rule applied to the scipy masses: floor with minimum 1,
+    # then +1 on the largest remainders or -1 on the largest frequencies; a
+    # last-bit difference between the two mass evaluations can move one unit
+    g = np.maximum(np.floor(q), 1.0).astype(np.int64)
+    left = 4096 - int(g.sum())
+    if left > 0:
+        for i in sorted(range(n + 1), key=lambda i: (-(q[i] - g[i]), i))[:left]:
+            g[i] += 1
+    for _ in range(-left):
+        g[int(np.argmax(np.where(g > 1, g, -1)))] -= 1
+    assert np.all(np.abs(f - g) <= 1)
 
 
 def test_residual_fit_matches_laplace(orc):
@@ -50,6 +83,7 @@ def test_residual_fit_matches_laplace(orc):
     shape = orc.make_shape(orc.BF16, orc.RESIDUAL, 1, 2, 128, 1024)
     blob = orc.fit_tables(shape, ct, cp, 256)
     assert len(blob) == 64 + 2048 * 514
+    floors = [_tail_floor(_zigzag_residuals(ct[0, kv], cp[0, kv], 16).ravel()) for kv in range(2)]
     rng = np.random.default_rng(3)
     for j in rng.choice(2048, 24, replace=False):
         kv, ch = divmod(int(j), 1024)
@@ -60,7 +94,7 @@ def test_residual_fit_matches_laplace(orc):
         n, f = orc.blob_table(blob, int(j))
         z = np.array([orc.zigzag(int(x)) for x in r])
         pe = ((z >= n).sum() + 1.0) / (256 + 2.0)
-        _check_table(n, f, masses, pe)
+        _check_table(n, f, masses, pe, floors[kv])
 
 
 def test_e4m3_fit_matches_laplace(orc):
@@ -69,6 +103,7 @@ def test_e4m3_fit_matches_laplace(orc):
     ct, cp = ct.numpy(), cp.numpy()
     shape = orc.make_shape(orc.E4M3, orc.RESIDUAL, 1, 2, 128, 1024)
     blob = orc.fit_tables(shape, ct, cp, 256)
+    floors = [_tail_floor(_zigzag_residuals(ct[0, kv], cp[0, kv], 8).ravel()) for kv in range(2)]
     for j in (0, 1, 517, 1500, 2047):
         kv, ch = divmod(j, 1024)
         r = np.array([orc.residual(int(a), int(b), 8) for a, b in zip(ct[0, kv, :, ch], cp[0, kv, :, ch])])
@@ -78,7 +113,32 @@ def test_e4m3_fit_matches_laplace(orc):
         n, f = orc.blob_table(blob, j)
         z = np.array([orc.zigzag(int(x)) for x in r])
         pe = ((z >= n).sum() + 1.0) / 258.0
-        _check_table(n, f, masses, pe)
+        _check_table(n, f, masses, pe, floors[kv])
+
+
+@pytest.mark.parametrize("tail, floor_n", [(256, None), (257, 101)])
+def test_tail_floor_boundary(orc, tail, floor_n):
+    """262,144 calibration symbols of one slab allow 256 escapes: 256
+    symbols at z = 100 leave the Laplace direct range alone, 257 push every
+    table of the slab to n = 101."""
+    C, T = 1024, 256
+    p = np.full((1, 1, T, C), 0x3F80, dtype=np.uint16)           # bf16 1.0
+    t = p.copy()
+    rng = np.random.default_rng(11)
+    # small residuals everywhere (ordered step +-1 or 0) so that the Laplace scale is small
+    t[0, 0] = (p[0, 0].astype(np.int64) + rng.integers(-1, 2, size=(T, C))).astype(np.uint16)
+    flat = t.reshape(-1)
+    pos = rng.choice(T * C, size=tail, replace=False)
+    flat[pos] = 0x3F80 + 50                                         # residual +50 -> z = 100
+    z = _zigzag_residuals(t, p, 16).ravel()
+    assert np.count_nonzero(z >= 100) == tail and z.max() == 100
+    shape = orc.make_shape(orc.BF16, orc.RESIDUAL, 1, 1, 128, C)
+    blob = orc.fit_tables(shape, t.view(np.int16), p.view(np.int16), T)
+    ns = [orc.blob_table(blob, j)[0] for j in range(0, C, 37)]
+    if floor_n is None:
+        assert max(ns) < 101
+    else:
+        assert ns == [floor_n] * len(ns)
 
 
 def test_checkerboard_fit_matches_laplace(orc):
