@@ -1121,7 +1121,10 @@ __global__ __launch_bounds__(1024) void encode_tiles(EncodeLaunch a, DevTables t
 // One workgroup owns the 32 tables of a channel group: the complete
 // slot -> symbol maps (4096 bytes per table) and per symbol the 16-bit
 // values 4096 - frequency and start, so a pop is one map byte, two 16-bit
-// reads and x' = x - (x >> 12) * (4096 - f) - start.  Each half wavefront runs
+// reads and x' = x - (x >> 12) * (4096 - f) - start.  A map byte is the
+// symbol's signed residual plus 128 (the escape symbol gets the byte its
+// zigzag value would have), and the (4096 - f, start) rows are indexed by
+// that byte, so the reconstruction needs no zigzag decode.  Each half wavefront runs
 // two streams as independent chains (4 streams per wavefront), which hides
 // the latency of the dependent LDS reads of a step.  Words come from a
 // 128-word ring per stream in LDS, refilled with one 32-word chunk per 4-step
@@ -1164,12 +1167,15 @@ __device__ __forceinline__ uint32_t unzig8x4(uint32_t z) {
 __device__ __forceinline__ uint32_t add8x4(uint32_t a, uint32_t b) {
     return ((a & 0x7F7F7F7Fu) + (b & 0x7F7F7F7Fu)) ^ ((a ^ b) & 0x80808080u);
 }
-// target codes from predictor codes and symbols: the order-preserving code
-// of a byte is flip(u) ^ 0x80, so ord(t) = ord(p) + r mod 256 becomes
-// flip(t) = flip(p) + r mod 256 (flip is its own inverse)
-__device__ __forceinline__ uint32_t recon8x4(uint32_t p, uint32_t z) {
-    return sflip8x4(add8x4(sflip8x4(p), unzig8x4(z)));
+// target codes from predictor codes and residual bytes b = r + 128: the
+// order-preserving code of a byte is flip(u) ^ 0x80, so ord(t) = ord(p) + r
+// mod 256 becomes flip(t) = flip(p) + (b ^ 0x80) mod 256 (flip is its own
+// inverse), and a bytewise sum with b ^ 0x80 is the sum with b, ^ 0x80
+__device__ __forceinline__ uint32_t recon8x4(uint32_t p, uint32_t b) {
+    return sflip8x4(add8x4(sflip8x4(p), b) ^ 0x80808080u);
 }
+// residual byte r + 128 of a zigzag symbol value z < 256
+__device__ __forceinline__ uint32_t rbyte(uint32_t z) { return (unzig(z) + 128u) & 0xFFu; }
 
 // Rank of each flagged lane among the flagged lanes of its half, plus the
 // half's count from a packed wave-uniform counter (lower half in bits 0..15,
@@ -1189,7 +1195,7 @@ struct DecState {
 };
 
 struct DecLane {
-    uint32_t mapb, gb, fsh, n;
+    uint32_t mapb, gb, fsh, n, esc;
     __amdgpu_buffer_rsrc_t rs;
 };
 
@@ -1198,32 +1204,50 @@ struct DecChain {
 };
 
 // The steps of one tile for both chains.  GLOBAL = false takes words from the
-// rings, GLOBAL = true from the streams in memory (a tile decoded again).  The
-// step is branch-free so that the two chains' instructions interleave.
+// rings, GLOBAL = true from the streams in memory (a tile decoded again).  A
+// step is written stage by stage over the two chains (map bytes, then table
+// rows, then ring words) so that their LDS reads are in flight together, and
+// it is branch-free: the refill select is a v_cndmask on the ballot mask,
+// which keeps the ring read unconditional.
 template <bool GLOBAL, uint32_t FS>
 __device__ __forceinline__ void dec_tile_steps(DecState (&st)[kDecChains], const DecLane& L,
                                                const DecChain (&ch)[kDecChains], uint32_t (&sy)[kDecChains][kDecTile],
                                                uint64_t& anyesc) {
 #pragma unroll
     for (uint32_t r = 0; r < kDecTile; ++r) {
+        uint32_t sym[kDecChains], g[kDecChains], cu[kDecChains], xn[kDecChains], idx[kDecChains], w[kDecChains];
+        uint64_t mw[kDecChains];
+#pragma unroll
+        for (uint32_t c = 0; c < kDecChains; ++c)
+            sym[c] = *reinterpret_cast<const lds_u8*>((st[c].x & (kM - 1u)) | L.mapb);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (uint32_t c = 0; c < kDecChains; ++c) {
-            const uint32_t x = st[c].x;
-            const uint32_t sym = *reinterpret_cast<const lds_u8*>((x & (kM - 1u)) | L.mapb);
-            const uint32_t ga = (sym << 6) + L.gb;
-            const uint32_t g = *reinterpret_cast<const lds_u16*>(ga);                 // 4096 - f
-            const uint32_t cu = *reinterpret_cast<const lds_u16*>(ga + FS * kLanes * 2);   // start
-            const uint32_t xn = x - (__umul24(x >> kProbBits, g) + cu);
+            const uint32_t ga = (sym[c] << 6) + L.gb;
+            g[c] = *reinterpret_cast<const lds_u16*>(ga);                         // 4096 - f
+            cu[c] = *reinterpret_cast<const lds_u16*>(ga + FS * kLanes * 2);       // start
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (uint32_t c = 0; c < kDecChains; ++c) {
+            xn[c] = st[c].x - (__umul24(st[c].x >> kProbBits, g[c]) + cu[c]);
             // refill in lane order
-            const bool need = xn < kStateLow;
-            const uint32_t idx = half_rank(__ballot(need), st[c].P, L.fsh);
-            uint32_t w;
-            if (GLOBAL) w = __builtin_amdgcn_raw_buffer_load_b16(L.rs, ch[c].wofs + 2 * idx, 0, 0);
-            // volatile: the read stays unconditional, with no branch around it
-            else w = *reinterpret_cast<const volatile lds_u16*>(((idx << 1) & (2 * kDecRing - 2)) | ch[c].ringb);
-            st[c].x = need ? ((xn << 16) | w) : xn;
-            anyesc |= __ballot(sym == L.n);
-            sy[c][r] = sym;
+            mw[c] = __ballot(xn[c] < kStateLow);
+            idx[c] = half_rank(mw[c], st[c].P, L.fsh);
+            if (GLOBAL) w[c] = __builtin_amdgcn_raw_buffer_load_b16(L.rs, ch[c].wofs + 2 * idx[c], 0, 0);
+            else w[c] = *reinterpret_cast<const lds_u16*>(((idx[c] << 1) & (2 * kDecRing - 2)) | ch[c].ringb);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (uint32_t c = 0; c < kDecChains; ++c) {
+            anyesc |= __ballot(sym[c] == L.esc);
+            sy[c][r] = sym[c];
+        }
+#pragma unroll
+        for (uint32_t c = 0; c < kDecChains; ++c) {
+            uint32_t x;
+            asm("v_cndmask_b32_e64 %0, %1, %2, %3" : "=v"(x) : "v"(xn[c]), "v"((xn[c] << 16) | w[c]), "s"(mw[c]));
+            st[c].x = x;
         }
     }
 }
@@ -1242,25 +1266,31 @@ __global__ __launch_bounds__(1024, 1) void decode_e4m3(DecodeLaunch a, DevTables
     if (!ps.valid) return;
     const uint32_t tid = threadIdx.x;
     const uint32_t tab0 = ps.slab * geo.C + ps.cg * kLanes;
-    uint16_t* lg16 = reinterpret_cast<uint16_t*>(lds + OFF_G);    // [FS symbols][32 lanes]
+    // rows by residual byte: row = r + FS/2 for the symbol of residual r (|r| < FS/2 when n < FS)
+    constexpr uint32_t RB = 128u - FS / 2;                        // residual byte of row 0
+    uint16_t* lg16 = reinterpret_cast<uint16_t*>(lds + OFF_G);    // [FS rows][32 lanes]
     uint16_t* lc16 = reinterpret_cast<uint16_t*>(lds + OFF_C);
     for (uint32_t i = tid; i < FS * kLanes; i += blockDim.x) {
-        const uint32_t fc = t.fc[size_t(tab0 + i % kLanes) * 256 + i / kLanes];
+        const uint32_t row = i / kLanes;
+        const uint32_t z = zig8((row + RB - 128u) & 0xFFu);         // symbol of the row's residual
+        const uint32_t fc = t.fc[size_t(tab0 + i % kLanes) * 256 + z];
         lg16[i] = uint16_t(kM - (fc & 0xFFFFu));
-        lc16[i] = uint16_t(fc >> 16);                             // rows past n: start 4096
+        lc16[i] = uint16_t(fc >> 16);                             // symbols past n: start 4096
     }
     __syncthreads();
     {
-        // maps: thread (j, part) fills slots [128 part, 128 part + 128) of table j
+        // maps: thread (j, part) fills slots [128 part, 128 part + 128) of table j with the
+        // residual byte of the slot's symbol
         const uint32_t j = tid >> 5, part = tid & 31u;
         const uint32_t nn = t.n[tab0 + j];
+        auto start_of = [&](uint32_t z) { return uint32_t(lc16[(rbyte(z) - RB) * kLanes + j]); };
         uint32_t s = 0, slot = part * 128u;
         uint32_t* dst = reinterpret_cast<uint32_t*>(lds + j * kM + slot);
         for (uint32_t w = 0; w < 32; ++w) {
             uint32_t word = 0;
             for (uint32_t q = 0; q < 4; ++q, ++slot) {
-                while (s < nn && lc16[(s + 1) * kLanes + j] <= slot) ++s;
-                word |= s << (8 * q);
+                while (s < nn && start_of(s + 1) <= slot) ++s;
+                word |= rbyte(s) << (8 * q);
             }
             dst[w] = word;
         }
@@ -1284,9 +1314,10 @@ __global__ __launch_bounds__(1024, 1) void decode_e4m3(DecodeLaunch a, DevTables
     }
     DecLane L;
     L.mapb = lb + hl * kM;
-    L.gb = lb + OFF_G + hl * 2;
+    L.gb = lb + OFF_G + hl * 2 - RB * kLanes * 2;                  // row of residual byte b at b * 64 + gb
     L.fsh = upper ? 16u : 0u;
     L.n = t.n[tab0 + hl];
+    L.esc = rbyte(L.n);                                             // map byte of the escape symbol
     // every payload read of the workgroup goes through one range-checked resource
     L.rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(pay + wlo), (short)0, int(whi - wlo), 0x00020000);
     // predictor and output rows of the slab's channel group, 32-bit offsets from one base each
@@ -1399,7 +1430,7 @@ __global__ __launch_bounds__(1024, 1) void decode_e4m3(DecodeLaunch a, DevTables
                 for (uint32_t r = 0; r < kDecTile; ++r)
 #pragma unroll
                     for (uint32_t c = 0; c < kDecChains; ++c) {
-                        const bool esc = sy[c][r] == L.n;
+                        const bool esc = sy[c][r] == L.esc;
                         const uint64_t m = __ballot(esc);
                         if (m == 0) continue;
                         const uint32_t eidx = half_rank(m, st[c].E, L.fsh);
@@ -1414,7 +1445,7 @@ __global__ __launch_bounds__(1024, 1) void decode_e4m3(DecodeLaunch a, DevTables
                         }
                         // a canonical encoder codes a value below n directly
                         if (esc && coded[c] && v < L.n) bad = true;
-                        sy[c][r] = esc ? v : sy[c][r];
+                        sy[c][r] = esc ? rbyte(v) : sy[c][r];
                     }
             }
 #pragma unroll
