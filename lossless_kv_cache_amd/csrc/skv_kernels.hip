@@ -313,8 +313,11 @@ __global__ __launch_bounds__(kScanBlock) void place_streams(EncodeLaunch a, cons
 }
 
 // One wavefront per stream: copy its bytes from the scratch area to its place
-// in the container (states, words and escaped values reversed from emission
-// into decode order, zero pad; raw streams gather the target tile).
+// in the container (states, word count, words and escaped values reversed from
+// emission into decode order, zero pad; raw streams gather the target tile).
+// Words move a dword at a time: with an even word count, container dword j is
+// scratch dword cnt/2 - 1 - j with its halves swapped; with an odd count it
+// takes the low half of one scratch dword and the high half of the one below.
 template <uint32_t DT, uint32_t MODE>
 __global__ __launch_bounds__(256) void copy_streams(EncodeLaunch a) {
     constexpr uint32_t EB = DT == SKV_E4M3 ? 1u : 2u;
@@ -330,26 +333,41 @@ __global__ __launch_bounds__(256) void copy_streams(EncodeLaunch a) {
     const uint32_t ms = a.meta[sid];
     const uint8_t* src = a.scratch + sid * (2 * RAW);
     if (ms >> 31) {
+        // raw stream: 128 rows of 32 channels from the target, 16 bytes per lane per pass
         const Geo g = geometry(a.shape);
         const uint32_t cg = uint32_t(sid % g.ncg);
         const uint32_t tb = uint32_t((sid / g.ncg) % g.ntb);
         const uint32_t slab = uint32_t(sid / (uint64_t(g.ncg) * g.ntb));
-        for (uint32_t e = lane; e < uint32_t(kSyms); e += 64) {
-            const uint32_t k = e >> 5, ln = e & 31u;
+        constexpr uint32_t PER_ROW = kLanes * EB / 16;          // 16-byte pieces per row segment
+        for (uint32_t e = lane; e < kSteps * PER_ROW; e += 64) {
+            const uint32_t k = e / PER_ROW, piece = e % PER_ROW;
             const uint32_t tok = MODE == SKV_RESIDUAL ? tb * kSteps + k : 2u * (tb * kSteps + k) + slab;
-            const size_t idx = MODE == SKV_RESIDUAL ? (size_t(slab) * g.T + tok) * g.C + cg * kLanes + ln
-                                                    : size_t(tok) * g.C + cg * kLanes + ln;
-            if (EB == 1) dst[e] = static_cast<const uint8_t*>(a.target)[idx];
-            else reinterpret_cast<uint16_t*>(dst)[e] = static_cast<const uint16_t*>(a.target)[idx];
+            const size_t idx = MODE == SKV_RESIDUAL ? (size_t(slab) * g.T + tok) * g.C + cg * kLanes
+                                                    : size_t(tok) * g.C + cg * kLanes;
+            const uint4 v = *reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(a.target) + idx * EB + piece * 16);
+            *reinterpret_cast<uint4*>(dst + e * 16) = v;
         }
         return;
     }
     const uint32_t cnt = ms & 0x3FFFu, ecnt = (ms >> 14) & 0x3FFFu;
     if (lane < 32) reinterpret_cast<uint32_t*>(dst)[lane] = reinterpret_cast<const uint32_t*>(src)[lane];
     if (lane == 32) reinterpret_cast<uint32_t*>(dst)[32] = cnt;
-    const uint16_t* ws = reinterpret_cast<const uint16_t*>(src + RAW);
-    uint16_t* wd = reinterpret_cast<uint16_t*>(dst + kStreamHead);
-    for (uint32_t q = lane; q < cnt; q += 64) wd[q] = ws[cnt - 1 - q];
+    const uint32_t* ws = reinterpret_cast<const uint32_t*>(src + RAW);
+    uint32_t* wd = reinterpret_cast<uint32_t*>(dst + kStreamHead);
+    if ((cnt & 1u) == 0) {
+        for (uint32_t j = lane; j < cnt / 2; j += 64) {
+            const uint32_t v = ws[cnt / 2 - 1 - j];
+            wd[j] = __builtin_amdgcn_alignbit(v, v, 16);
+        }
+    } else {
+        for (uint32_t j = lane; j < cnt / 2; j += 64) {
+            const uint32_t e = cnt - 1 - 2 * j;                // scratch word at container word 2j (even index)
+            wd[j] = (ws[e / 2] & 0xFFFFu) | (ws[e / 2 - 1] & 0xFFFF0000u);
+        }
+        // the last word (scratch word 0) alone: the escaped values follow it directly
+        if (lane == 0) reinterpret_cast<uint16_t*>(wd)[cnt - 1] = uint16_t(ws[0]);
+    }
+    // escaped values (few): element by element, reversed
     uint8_t* ed = dst + kStreamHead + 2 * cnt;
     if (EB == 1) {
         const uint8_t* es = src + kStreamHead;
@@ -358,9 +376,10 @@ __global__ __launch_bounds__(256) void copy_streams(EncodeLaunch a) {
         const uint16_t* es = reinterpret_cast<const uint16_t*>(src + kStreamHead);
         for (uint32_t q = lane; q < ecnt; q += 64) reinterpret_cast<uint16_t*>(ed)[q] = es[ecnt - 1 - q];
     }
-    const uint32_t eb = EB * ecnt;
-    const uint32_t total = (kStreamHead + 2 * cnt + eb + 3) & ~3u;
-    for (uint32_t q = eb + lane; q < total - (kStreamHead + 2 * cnt); q += 64) ed[q] = 0;
+    // zero pad after the escaped values
+    const uint32_t used = kStreamHead + 2 * cnt + EB * ecnt;
+    const uint32_t total = (used + 3) & ~3u;
+    for (uint32_t q = used + lane; q < total; q += 64) dst[q] = 0;
 }
 
 // --------------------------------------------------------------- decode
