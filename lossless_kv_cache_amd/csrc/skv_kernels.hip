@@ -960,7 +960,7 @@ __global__ __launch_bounds__(1024) void encode_lds(EncodeLaunch a, DevTables t, 
 // the one the compaction reads: states [0, 128), escaped values from 132 and
 // words from `raw`, both in emission order.
 constexpr uint32_t kTileSteps = 8;
-constexpr uint32_t kRingWords = 128;                      // two 64-word chunks per stream
+constexpr uint32_t kRingWords = 512;                      // eight 64-word chunks per stream
 constexpr uint32_t kTileLds = 2 * kTileSteps * kLanes;    // difference bytes of both halves
 constexpr uint32_t kRingLds = 2 * kRingWords * 2;
 constexpr uint32_t kTileWaveLds = kTileLds + kRingLds;
@@ -1028,6 +1028,7 @@ __global__ __launch_bounds__(1024) void encode_tiles(EncodeLaunch a, DevTables t
         for (uint32_t r = 0; r < kTileSteps; ++r) z[r] = zig[tile_rd[r * kLanes]];
         __builtin_amdgcn_wave_barrier();
     };
+    const uint32_t* ring32 = reinterpret_cast<const uint32_t*>(ring_h);
 
     for (uint32_t r0 = ps.tb_begin + 2 * wave; r0 < ps.tb_end; r0 += 2 * nwave) {
         const uint32_t tb = r0 + (upper ? 1u : 0u);
@@ -1050,6 +1051,7 @@ __global__ __launch_bounds__(1024) void encode_tiles(EncodeLaunch a, DevTables t
 
         uint32_t x = kStateLow;
         uint32_t wp = 0;                                   // word counts: lower half | upper half << 16
+        uint32_t fl = 0;                                   // chunks stored: lower half | upper half << 16
         uint32_t elo = 0, ehi = 0;                         // escape counts per half
         uint4 ec = lenc[min(zc[kTileSteps - 1], n) * kLanes + lane];
         for (int j = kTiles - 1; j >= 0; --j) {
@@ -1072,27 +1074,32 @@ __global__ __launch_bounds__(1024) void encode_tiles(EncodeLaunch a, DevTables t
                 const uint64_t mw = __ballot(emit);
                 const uint32_t mlo = uint32_t(mw), mhi = uint32_t(mw >> 32);
                 const uint32_t pp = __popc(mlo) | (__popc(mhi) << 16);
-                // ring slot: this half's count mod 128 plus the emitting lanes below (mbcnt_lo counts the
+                // ring slot: this half's count mod 512 plus the emitting lanes below (mbcnt_lo counts the
                 // entire lower half for an upper lane, which the packed base subtracts again)
-                const uint32_t pk = (wp - (pp << 16)) & 0x007F007Fu;
+                const uint32_t pk = (wp - (pp << 16)) & 0x01FF01FFu;
                 const uint32_t slot =
                     __builtin_amdgcn_mbcnt_hi(mhi, __builtin_amdgcn_mbcnt_lo(mlo, __builtin_amdgcn_ubfe(pk, fsh, 16)));
                 if (emit) ring_h[slot & (kRingWords - 1)] = uint16_t(xs & 0xFFFFu);
                 xs = emit ? xs >> 16 : xs;
                 const uint32_t qt = __umulhi(xs + (e.z >> 24), e.y) >> (e.w & 31u);   // floor(xs / f)
-                x = (xs + (e.w >> 16)) + __umul24(qt, e.z);
-                // a completed 64-word chunk leaves the ring (at most one per step and stream)
-                const uint32_t cross = ((wp & 0x003F003Fu) + pp) & 0x00400040u;
-                if (cross) {
-                    __builtin_amdgcn_wave_barrier();
-                    const uint32_t ck = __builtin_amdgcn_ubfe(wp >> 6, fsh, 10);
-                    const uint32_t w = reinterpret_cast<const uint32_t*>(ring_h)[(ck & 1u) * 32 + hl];
-                    const bool mine = act && __builtin_amdgcn_ubfe(cross, fsh + 6, 1);
-                    __builtin_amdgcn_raw_buffer_store_b32(
-                        w, wrs, mine && ck < kChunks ? wreg + ck * 128 + 4 * hl : kDrop, 0, 0);
-                    __builtin_amdgcn_wave_barrier();
-                }
+                // x = xs + qt (4096 - f) + start, the start taken from the high half of e.w
+                const uint32_t xq = __umul24(qt, e.z) + xs;
+                asm("v_add_u32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:WORD_1"
+                    : "=v"(x) : "v"(xq), "v"(e.w));
                 wp += pp;
+            }
+            // completed 64-word chunks leave the ring (a tile adds at most 256 words per stream, so
+            // the 512-word ring never overruns the chunks still waiting)
+            const uint32_t done = (wp >> 6) & 0x03FF03FFu;
+            while (fl != done) {
+                __builtin_amdgcn_wave_barrier();
+                const uint32_t ck = __builtin_amdgcn_ubfe(fl, fsh, 16);
+                const bool mine = act && ck < __builtin_amdgcn_ubfe(done, fsh, 16);
+                const uint32_t w = ring32[(ck & (kRingWords / 64 - 1)) * 32 + hl];
+                __builtin_amdgcn_raw_buffer_store_b32(w, wrs, mine && ck < kChunks ? wreg + ck * 128 + 4 * hl : kDrop,
+                                                      0, 0);
+                fl += ((fl & 0xFFFFu) != (done & 0xFFFFu) ? 1u : 0u) + ((fl >> 16) != (done >> 16) ? 0x10000u : 0u);
+                __builtin_amdgcn_wave_barrier();
             }
             // escaped values of this tile, in emission order (rare: skipped by the whole wavefront)
             uint32_t zm = zc[0];
@@ -1121,7 +1128,7 @@ __global__ __launch_bounds__(1024) void encode_tiles(EncodeLaunch a, DevTables t
         __builtin_amdgcn_wave_barrier();
         const uint32_t cnt = __builtin_amdgcn_ubfe(wp, fsh, 16), ecnt = upper ? ehi : elo;
         const uint32_t ck = cnt >> 6;
-        const uint32_t w = reinterpret_cast<const uint32_t*>(ring_h)[(ck & 1u) * 32 + hl];
+        const uint32_t w = ring32[(ck & (kRingWords / 64 - 1)) * 32 + hl];
         __builtin_amdgcn_raw_buffer_store_b32(
             w, wrs, act && ck < kChunks && 2 * hl < (cnt & 63u) ? wreg + ck * 128 + 4 * hl : kDrop, 0, 0);
         __builtin_amdgcn_wave_barrier();
@@ -1159,6 +1166,10 @@ constexpr uint32_t kDecChains = 2;                           // streams per half
 constexpr uint32_t kDecTile = 4;                             // steps per tile
 constexpr uint32_t kDecRing = 128;                           // words per stream ring
 constexpr uint32_t kDecChunk = 32;                           // words per ring chunk
+constexpr uint32_t kDecSlots = kDecRing / kDecChunk;           // chunks a ring holds
+constexpr uint32_t kDecSlotBits = kDecSlots == 4 ? 2 : 1;
+constexpr uint32_t kDecFirst = kDecSlots > 2 ? 2 : 1;          // chunk requested at the start of a stream
+static_assert(kDecSlots == 2 || kDecSlots == 4, "ring of 2 or 4 chunks");
 constexpr uint32_t kDecStreams = (1024 / 32) * kDecChains;   // streams in flight per workgroup
 constexpr uint32_t kDecEscWin = 128;                         // bytes of escape region per stream held in a register
 
@@ -1179,10 +1190,6 @@ __device__ __forceinline__ uint32_t sflip8x4(uint32_t v) {   // v ^ 0x7F in the 
     const uint32_t s = v & 0x80808080u;
     return v ^ (s - (s >> 7));
 }
-__device__ __forceinline__ uint32_t unzig8x4(uint32_t z) {
-    const uint32_t l = z & 0x01010101u;
-    return ((z >> 1) & 0x7F7F7F7Fu) ^ ((l << 8) - l);
-}
 __device__ __forceinline__ uint32_t add8x4(uint32_t a, uint32_t b) {
     return ((a & 0x7F7F7F7Fu) + (b & 0x7F7F7F7Fu)) ^ ((a ^ b) & 0x80808080u);
 }
@@ -1196,15 +1203,22 @@ __device__ __forceinline__ uint32_t recon8x4(uint32_t p, uint32_t b) {
 // residual byte r + 128 of a zigzag symbol value z < 256
 __device__ __forceinline__ uint32_t rbyte(uint32_t z) { return (unzig(z) + 128u) & 0xFFu; }
 
-// Rank of each flagged lane among the flagged lanes of its half, plus the
-// half's count from a packed wave-uniform counter (lower half in bits 0..15,
-// upper half in bits 16..31 with a bias of 256); advances the counter.
-__device__ __forceinline__ uint32_t half_rank(uint64_t m, uint32_t& C, uint32_t fsh) {
+// Rank of each flagged lane among the flagged lanes of its half plus the
+// half's running count (lower half in bits 0..15 of C, upper half in bits
+// 16..31); advances C.  `lowm` is all ones in the lower half and zero in the
+// upper half, so an upper lane's mbcnt_lo sees none of the lower half's
+// flags and no scalar work sits between the ballot and the rank.
+__device__ __forceinline__ uint32_t half_rank(uint64_t m, uint32_t& C, uint32_t fsh, uint32_t lowm) {
     const uint32_t lo = uint32_t(m), hi = uint32_t(m >> 32);
-    const uint32_t clo = __popc(lo);
-    const uint32_t pk = C - (clo << 16);           // the upper half's mbcnt_lo counts the whole lower half
-    C = pk + clo + (uint32_t(__popcll(m)) << 16);
-    return __builtin_amdgcn_mbcnt_hi(hi, __builtin_amdgcn_mbcnt_lo(lo, __builtin_amdgcn_ubfe(pk, fsh, 16)));
+    const uint32_t base = __builtin_amdgcn_ubfe(C, fsh, 16);
+    C += uint32_t(__popc(lo)) | (uint32_t(__popc(hi)) << 16);
+    return __builtin_amdgcn_mbcnt_hi(hi, __builtin_amdgcn_mbcnt_lo(lo & lowm, base));
+}
+
+// 0x80 in every byte of v that is zero, 0 elsewhere (exact per byte: no carry
+// crosses a byte boundary)
+__device__ __forceinline__ uint32_t zero_bytes(uint32_t v) {
+    return ~(((v & 0x7F7F7F7Fu) + 0x7F7F7F7Fu) | v) & 0x80808080u;
 }
 
 // Decoder state of one chain: the lane's rANS state and the packed counts
@@ -1214,12 +1228,12 @@ struct DecState {
 };
 
 struct DecLane {
-    uint32_t mapb, gb, fsh, n, esc;
+    uint32_t mapb, gb, fsh, lowm;
     __amdgpu_buffer_rsrc_t rs;
 };
 
 struct DecChain {
-    uint32_t ringb, tileb, wofs, eofs;
+    uint32_t ringb, tileb, woff;
 };
 
 // The steps of one tile for both chains.  GLOBAL = false takes words from the
@@ -1230,8 +1244,7 @@ struct DecChain {
 // which keeps the ring read unconditional.
 template <bool GLOBAL, uint32_t FS>
 __device__ __forceinline__ void dec_tile_steps(DecState (&st)[kDecChains], const DecLane& L,
-                                               const DecChain (&ch)[kDecChains], uint32_t (&sy)[kDecChains][kDecTile],
-                                               uint64_t& anyesc) {
+                                               const DecChain (&ch)[kDecChains], uint32_t (&sy)[kDecChains][kDecTile]) {
 #pragma unroll
     for (uint32_t r = 0; r < kDecTile; ++r) {
         uint32_t sym[kDecChains], g[kDecChains], cu[kDecChains], xn[kDecChains], idx[kDecChains], w[kDecChains];
@@ -1252,21 +1265,17 @@ __device__ __forceinline__ void dec_tile_steps(DecState (&st)[kDecChains], const
             xn[c] = st[c].x - (__umul24(st[c].x >> kProbBits, g[c]) + cu[c]);
             // refill in lane order
             mw[c] = __ballot(xn[c] < kStateLow);
-            idx[c] = half_rank(mw[c], st[c].P, L.fsh);
-            if (GLOBAL) w[c] = __builtin_amdgcn_raw_buffer_load_b16(L.rs, ch[c].wofs + 2 * idx[c], 0, 0);
+            idx[c] = half_rank(mw[c], st[c].P, L.fsh, L.lowm);
+            if (GLOBAL) w[c] = __builtin_amdgcn_raw_buffer_load_b16(L.rs, ch[c].woff + 2 * idx[c], 0, 0);
             else w[c] = *reinterpret_cast<const lds_u16*>(((idx[c] << 1) & (2 * kDecRing - 2)) | ch[c].ringb);
         }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (uint32_t c = 0; c < kDecChains; ++c) {
-            anyesc |= __ballot(sym[c] == L.esc);
-            sy[c][r] = sym[c];
-        }
-#pragma unroll
-        for (uint32_t c = 0; c < kDecChains; ++c) {
             uint32_t x;
             asm("v_cndmask_b32_e64 %0, %1, %2, %3" : "=v"(x) : "v"(xn[c]), "v"((xn[c] << 16) | w[c]), "s"(mw[c]));
             st[c].x = x;
+            sy[c][r] = sym[c];
         }
     }
 }
@@ -1298,20 +1307,18 @@ __global__ __launch_bounds__(1024, 1) void decode_e4m3(DecodeLaunch a, DevTables
     }
     __syncthreads();
     {
-        // maps: thread (j, part) fills slots [128 part, 128 part + 128) of table j with the
-        // residual byte of the slot's symbol
-        const uint32_t j = tid >> 5, part = tid & 31u;
-        const uint32_t nn = t.n[tab0 + j];
-        auto start_of = [&](uint32_t z) { return uint32_t(lc16[(rbyte(z) - RB) * kLanes + j]); };
-        uint32_t s = 0, slot = part * 128u;
-        uint32_t* dst = reinterpret_cast<uint32_t*>(lds + j * kM + slot);
-        for (uint32_t w = 0; w < 32; ++w) {
-            uint32_t word = 0;
-            for (uint32_t q = 0; q < 4; ++q, ++slot) {
-                while (s < nn && start_of(s + 1) <= slot) ++s;
-                word |= rbyte(s) << (8 * q);
-            }
-            dst[w] = word;
+        // maps: the 32 slot -> symbol tables of the group are contiguous in memory; each byte
+        // becomes the residual byte of its symbol, unzig(z) + 128 = unzig(z) ^ 0x80, 4 at a time
+        const uint4* src = reinterpret_cast<const uint4*>(t.slot + size_t(tab0) * kM);
+        uint4* dst = reinterpret_cast<uint4*>(lds);
+        auto rb4 = [](uint32_t z) {
+            const uint32_t l = z & 0x01010101u;
+            return ((z >> 1) & 0x7F7F7F7Fu) ^ ((l << 8) - l) ^ 0x80808080u;
+        };
+#pragma unroll
+        for (uint32_t k = 0; k < kLanes * kM / 16 / 1024; ++k) {
+            const uint4 v = src[k * 1024 + tid];
+            dst[k * 1024 + tid] = make_uint4(rb4(v.x), rb4(v.y), rb4(v.z), rb4(v.w));
         }
     }
     __syncthreads();
@@ -1335,10 +1342,17 @@ __global__ __launch_bounds__(1024, 1) void decode_e4m3(DecodeLaunch a, DevTables
     L.mapb = lb + hl * kM;
     L.gb = lb + OFF_G + hl * 2 - RB * kLanes * 2;                  // row of residual byte b at b * 64 + gb
     L.fsh = upper ? 16u : 0u;
-    L.n = t.n[tab0 + hl];
-    L.esc = rbyte(L.n);                                             // map byte of the escape symbol
+    L.lowm = upper ? 0u : 0xFFFFFFFFu;
     // every payload read of the workgroup goes through one range-checked resource
     L.rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(pay + wlo), (short)0, int(whi - wlo), 0x00020000);
+    // tile-domain bytes: the escape symbol's map byte and n of the lane's 4 channels
+    uint32_t escp = 0, np = 0;
+#pragma unroll
+    for (uint32_t k = 0; k < 4; ++k) {
+        const uint32_t nk = t.n[tab0 + q4 + k];
+        escp |= rbyte(nk) << (8 * k);
+        np |= min(nk, 255u) << (8 * k);
+    }
     // predictor and output rows of the slab's channel group, 32-bit offsets from one base each
     const size_t slab_b = size_t(ps.slab) * geo.T * rowb + size_t(ps.cg) * kLanes;
     const __amdgpu_buffer_rsrc_t prs = __builtin_amdgcn_make_buffer_rsrc(
@@ -1353,10 +1367,12 @@ __global__ __launch_bounds__(1024, 1) void decode_e4m3(DecodeLaunch a, DevTables
         DecChain ch[kDecChains];
         DecState st[kDecChains];
         uint32_t tb[kDecChains], nw[kDecChains], size[kDecChains], rel[kDecChains];
-        uint32_t woff[kDecChains], cw[kDecChains], pva[kDecChains], pvb[kDecChains], rowo[kDecChains];
+        uint32_t cw[kDecChains], pva[kDecChains], pvb[kDecChains], rowo[kDecChains];
         uint32_t ew[kDecChains], ea[kDecChains];
-        uint32_t hi_lo[kDecChains], hi_hi[kDecChains], ld_lo[kDecChains], ld_hi[kDecChains];
-        uint32_t lim_lo[kDecChains], lim_hi[kDecChains];
+        // ring upkeep, both halves packed (lower in bits 0..15): ldk = chunk held in cw,
+        // wrk = last chunk written to the ring, live = 0x8000 in the field of a half with
+        // a coded stream
+        uint32_t ldk[kDecChains], wrk[kDecChains], live[kDecChains];
         bool coded[kDecChains], raw[kDecChains];
 #pragma unroll
         for (uint32_t c = 0; c < kDecChains; ++c) {
@@ -1398,25 +1414,23 @@ __global__ __launch_bounds__(1024, 1) void decode_e4m3(DecodeLaunch a, DevTables
                 }
             }
             const uint64_t cm = __ballot(coded[c]);
-            // word and escape offsets in the window, with the upper half's bias of 256 taken out
-            woff[c] = coded[c] ? rel[c] + kStreamHead : 0u;
-            ch[c].wofs = woff[c] - (upper ? 512u : 0u);
-            ch[c].eofs = woff[c] + 2 * nw[c] - (upper ? 256u : 0u);
-            // window: the 4-byte aligned dwords from the start of the escape region (which sits 0 or
-            // 2 bytes past a dword boundary); a stream's dwords never cross its 4-byte padded end
-            ea[c] = (woff[c] + 2 * nw[c]) & 3u;
-            ew[c] = __builtin_amdgcn_raw_buffer_load_b32(L.rs, ((woff[c] + 2 * nw[c]) & ~3u) + 4 * hl, 0, 0);
-            // ring: chunk k (words [32k, 32k + 32)) sits in slot k % 4; chunks 0 and 1 now,
-            // chunk 2 requested for the first tile end
+            live[c] = (uint32_t(cm) ? 0x8000u : 0u) | ((cm >> 32) ? 0x80000000u : 0u);
+            // word offset in the window (an absent stream reads from the window start)
+            const uint32_t woff = coded[c] ? rel[c] + kStreamHead : 0u;
+            ch[c].woff = woff;
+            // escape window: the 4-byte aligned dwords from the start of the escape region (which
+            // sits 0 or 2 bytes past a dword boundary); a stream's dwords never cross its padded end
+            ea[c] = (woff + 2 * nw[c]) & 3u;
+            ew[c] = __builtin_amdgcn_raw_buffer_load_b32(L.rs, ((woff + 2 * nw[c]) & ~3u) + 4 * hl, 0, 0);
+            // ring: chunk k (words [32k, 32k + 32)) sits in slot k % slots; chunks 0 and 1 now,
+            // the next one (chunk 1 again for a 2-chunk ring) requested for the first tile end
             lds_u16* ring16 = reinterpret_cast<lds_u16*>(ch[c].ringb);
-            ring16[hl] = __builtin_amdgcn_raw_buffer_load_b16(L.rs, woff[c] + 2 * hl, 0, 0);
-            ring16[kDecChunk + hl] = __builtin_amdgcn_raw_buffer_load_b16(L.rs, woff[c] + 2 * kDecChunk + 2 * hl, 0, 0);
-            hi_lo[c] = hi_hi[c] = ld_lo[c] = ld_hi[c] = 2;            // chunks present / chunk in flight
-            cw[c] = __builtin_amdgcn_raw_buffer_load_b16(L.rs, woff[c] + 4 * kDecChunk + 2 * hl, 0, 0);
-            // a half without a coded stream never asks for a tile to be decoded again
-            lim_lo[c] = (cm & 1u) ? 2 * kDecChunk : 0xFFFFFFFFu;
-            lim_hi[c] = (cm >> 32) ? 2 * kDecChunk + 256u : 0xFFFFFFFFu;
-            st[c] = DecState{x, 256u << 16, 256u << 16};
+            ring16[hl] = __builtin_amdgcn_raw_buffer_load_b16(L.rs, woff + 2 * hl, 0, 0);
+            ring16[kDecChunk + hl] = __builtin_amdgcn_raw_buffer_load_b16(L.rs, woff + 2 * kDecChunk + 2 * hl, 0, 0);
+            cw[c] = __builtin_amdgcn_raw_buffer_load_b16(L.rs, woff + 2 * kDecChunk * kDecFirst + 2 * hl, 0, 0);
+            ldk[c] = kDecFirst * 0x00010001u;
+            wrk[c] = 0x00010001u;
+            st[c] = DecState{x, 0u, 0u};
         }
 #pragma unroll
         for (uint32_t c = 0; c < kDecChains; ++c) {
@@ -1425,47 +1439,24 @@ __global__ __launch_bounds__(1024, 1) void decode_e4m3(DecodeLaunch a, DevTables
         }
         __builtin_amdgcn_wave_barrier();
 
-        // one tile: its steps, escaped values, reconstruction, ring upkeep; pv holds the
+        // one tile: its steps, reconstruction, escaped values, ring upkeep; pv holds the
         // tile's predictor row and is reloaded with the row two tiles ahead
         auto tile_at = [&](uint32_t T, uint32_t (&pv)[kDecChains]) {
             uint32_t sy[kDecChains][kDecTile];
-            uint64_t anyesc = 0;
-            const DecState s0 = st[0], s1 = st[1];
-            dec_tile_steps<false, FS>(st, L, ch, sy, anyesc);
-            bool over = false;
+            DecState s0[kDecChains];
+#pragma unroll
+            for (uint32_t c = 0; c < kDecChains; ++c) s0[c] = st[c];
+            dec_tile_steps<false, FS>(st, L, ch, sy);
+            // a half of a coded stream that read past the last chunk written (word count above
+            // 32 (wrk + 1) in its field) decodes the tile again from memory
+            uint32_t over = 0;
 #pragma unroll
             for (uint32_t c = 0; c < kDecChains; ++c)
-                over |= (st[c].P & 0xFFFFu) > lim_lo[c] || (st[c].P >> 16) > lim_hi[c];
-            if (__builtin_expect(over, 0)) {
-                st[0] = s0;
-                st[1] = s1;
-                anyesc = 0;
-                dec_tile_steps<true, FS>(st, L, ch, sy, anyesc);
-            }
-            if (anyesc != 0) {
-                // escaped values in decode order (step, then lane); the first 128 of a stream
-                // come from the window register, later ones from the escape region in memory
+                over |= ~((wrk[c] << 5) + 0x80208020u - st[c].P) & live[c];
+            if (__builtin_expect(over != 0, 0)) {
 #pragma unroll
-                for (uint32_t r = 0; r < kDecTile; ++r)
-#pragma unroll
-                    for (uint32_t c = 0; c < kDecChains; ++c) {
-                        const bool esc = sy[c][r] == L.esc;
-                        const uint64_t m = __ballot(esc);
-                        if (m == 0) continue;
-                        const uint32_t eidx = half_rank(m, st[c].E, L.fsh);
-                        // byte of the window holding this lane's escaped value
-                        const uint32_t pos = eidx - (upper ? 256u : 0u) + ea[c];
-                        const uint32_t wv = __builtin_amdgcn_ds_bpermute(
-                            int(((pos >> 2) + (upper ? 32u : 0u)) << 2), int(ew[c]));
-                        uint32_t v = (wv >> ((pos & 3u) * 8)) & 0xFFu;
-                        if (__ballot(esc && pos >= kDecEscWin) != 0) {
-                            const uint32_t g = __builtin_amdgcn_raw_buffer_load_b8(L.rs, ch[c].eofs + eidx, 0, 0);
-                            v = pos >= kDecEscWin ? g : v;
-                        }
-                        // a canonical encoder codes a value below n directly
-                        if (esc && coded[c] && v < L.n) bad = true;
-                        sy[c][r] = esc ? rbyte(v) : sy[c][r];
-                    }
+                for (uint32_t c = 0; c < kDecChains; ++c) st[c] = s0[c];
+                dec_tile_steps<true, FS>(st, L, ch, sy);
             }
 #pragma unroll
             for (uint32_t c = 0; c < kDecChains; ++c)
@@ -1473,21 +1464,71 @@ __global__ __launch_bounds__(1024, 1) void decode_e4m3(DecodeLaunch a, DevTables
                 for (uint32_t r = 0; r < kDecTile; ++r)
                     *reinterpret_cast<lds_u8*>(ch[c].tileb + r * kLanes) = uint8_t(sy[c][r]);
             __builtin_amdgcn_wave_barrier();
+            // lane hl now holds the 4 symbols of step r4, lanes q4..q4+3 of its half, so the lanes
+            // of a half and the bytes of a lane run in decode order
+            uint32_t zt[kDecChains], ef[kDecChains];
 #pragma unroll
             for (uint32_t c = 0; c < kDecChains; ++c) {
-                const uint32_t zt = *reinterpret_cast<const lds_u32*>(ch[c].tileb - hl + r4 * kLanes + q4);
+                zt[c] = *reinterpret_cast<const lds_u32*>(ch[c].tileb - hl + r4 * kLanes + q4);
+                ef[c] = zero_bytes(zt[c] ^ escp);
+            }
+            uint32_t efa = 0;
+#pragma unroll
+            for (uint32_t c = 0; c < kDecChains; ++c) efa |= ef[c];
+            if (__builtin_expect(__ballot(efa != 0) != 0, 0)) {
+#pragma unroll
+                for (uint32_t c = 0; c < kDecChains; ++c) {
+                    if (__ballot(ef[c] != 0) == 0) continue;
+                    // escaped values of the half before this lane's (prefix sum of counts <= 4)
+                    const uint32_t cnt = __popc(ef[c]);
+                    const uint32_t base = __builtin_amdgcn_ubfe(st[c].E, L.fsh, 16);
+                    uint32_t pre = 0;
+                    for (uint32_t j = 0; j < 4; ++j) {
+                        const uint64_t m = __ballot(cnt > j);
+                        if (m == 0) break;
+                        uint32_t E = 0;
+                        pre += half_rank(m, E, L.fsh, L.lowm);
+                        st[c].E += E;
+                    }
+                    // the lane's escaped bytes in order; the first 128 bytes of a stream's escape
+                    // region come from the window register, later ones from memory
+                    uint32_t f = ef[c], v = zt[c];
+                    uint32_t eidx = base + pre;
+                    while (__ballot(f != 0) != 0) {
+                        const uint32_t sh = (__builtin_ctz(f | 0x80000000u) >> 3) * 8;   // byte of the value
+                        const uint32_t pos = eidx + ea[c];
+                        const uint32_t wv = __builtin_amdgcn_ds_bpermute(
+                            int(((pos >> 2) + (upper ? 32u : 0u)) << 2), int(ew[c]));
+                        uint32_t e = (wv >> ((pos & 3u) * 8)) & 0xFFu;
+                        if (__ballot(f != 0 && pos >= kDecEscWin) != 0) {
+                            const uint32_t g = __builtin_amdgcn_raw_buffer_load_b8(
+                                L.rs, ch[c].woff + 2 * nw[c] + eidx, 0, 0);
+                            e = pos >= kDecEscWin ? g : e;
+                        }
+                        if (f != 0) {
+                            // a canonical encoder codes a value below n directly
+                            if (coded[c] && e < ((np >> sh) & 0xFFu)) bad = true;
+                            v = (v & ~(0xFFu << sh)) | (rbyte(e) << sh);
+                            f &= f - 1u;
+                            ++eidx;
+                        }
+                    }
+                    zt[c] = v;
+                }
+            }
+#pragma unroll
+            for (uint32_t c = 0; c < kDecChains; ++c) {
                 if (coded[c])
-                    __builtin_amdgcn_raw_buffer_store_b32(recon8x4(pv[c], zt), ors, rowo[c] + T * kDecTile * rowb, 0, 0);
-                // the chunk requested one tile ago goes into its slot; request the next one
-                reinterpret_cast<lds_u16*>(ch[c].ringb)[(upper ? ld_hi[c] : ld_lo[c]) % 4 * kDecChunk + hl] = cw[c];
-                hi_lo[c] = max(hi_lo[c], ld_lo[c] + 1);
-                hi_hi[c] = max(hi_hi[c], ld_hi[c] + 1);
-                ld_lo[c] = min(hi_lo[c], (st[c].P & 0xFFFFu) / kDecChunk + 3);
-                ld_hi[c] = min(hi_hi[c], ((st[c].P >> 16) - 256u) / kDecChunk + 3);
-                if (lim_lo[c] != 0xFFFFFFFFu) lim_lo[c] = kDecChunk * hi_lo[c];
-                if (lim_hi[c] != 0xFFFFFFFFu) lim_hi[c] = kDecChunk * hi_hi[c] + 256u;
+                    __builtin_amdgcn_raw_buffer_store_b32(recon8x4(pv[c], zt[c]), ors, rowo[c] + T * kDecTile * rowb, 0, 0);
+                // the chunk in cw goes into its slot; the next one is requested while the ring
+                // has a free slot (chunk ldk + 1 fits when ldk <= words consumed / 32 + slots - 2)
+                reinterpret_cast<lds_u16*>(ch[c].ringb)[__builtin_amdgcn_ubfe(ldk[c], L.fsh, kDecSlotBits) * kDecChunk + hl] =
+                    cw[c];
+                wrk[c] = ldk[c];
+                const uint32_t room = ((st[c].P >> 5) & 0x07FF07FFu) + (0x8000u + kDecSlots - 2) * 0x00010001u - ldk[c];
+                ldk[c] += (room >> 15) & 0x00010001u;
                 cw[c] = __builtin_amdgcn_raw_buffer_load_b16(
-                    L.rs, woff[c] + 2 * kDecChunk * (upper ? ld_hi[c] : ld_lo[c]) + 2 * hl, 0, 0);
+                    L.rs, ch[c].woff + 2 * kDecChunk * __builtin_amdgcn_ubfe(ldk[c], L.fsh, 16) + 2 * hl, 0, 0);
             }
 #pragma unroll
             for (uint32_t c = 0; c < kDecChains; ++c)
@@ -1503,8 +1544,8 @@ __global__ __launch_bounds__(1024, 1) void decode_e4m3(DecodeLaunch a, DevTables
         for (uint32_t c = 0; c < kDecChains; ++c) {
             // ---- stream checks: states back at L, every word and escape consumed, zero pad
             if (coded[c]) {
-                const uint32_t pc = upper ? (st[c].P >> 16) - 256u : st[c].P & 0xFFFFu;
-                const uint32_t ec = upper ? (st[c].E >> 16) - 256u : st[c].E & 0xFFFFu;
+                const uint32_t pc = __builtin_amdgcn_ubfe(st[c].P, L.fsh, 16);
+                const uint32_t ec = __builtin_amdgcn_ubfe(st[c].E, L.fsh, 16);
                 const uint32_t used = kStreamHead + 2 * nw[c] + ec;
                 if (st[c].x != kStateLow || pc != nw[c] || used > size[c]) bad = true;
                 else if (((used + 3) & ~3u) != size[c]) bad = true;
