@@ -965,10 +965,14 @@ constexpr uint32_t kTileLds = 2 * kTileSteps * kLanes;    // difference bytes of
 constexpr uint32_t kRingLds = 2 * kRingWords * 2;
 constexpr uint32_t kTileWaveLds = kTileLds + kRingLds;
 
-// bytewise order-preserving map: x ^ 0x80 for a clear sign bit, x ^ 0xFF for a set one
-__device__ __forceinline__ uint32_t ord8x4(uint32_t v) {
-    const uint32_t s = v & 0x80808080u;
-    return v ^ 0x80808080u ^ (s - (s >> 7));
+// Bytewise sign flip of 4 packed e4m3 codes: v ^ 0x7F in the bytes whose sign
+// bit is set.  The order-preserving code of a byte is flip(u) ^ 0x80, so the
+// difference of two order codes mod 256 is the difference of their flips.
+// v_perm_b32 spreads a sign into a whole byte only from bytes 1 and 3 of each
+// source dword; with v << 8 as the second dword, the signs of v's bytes 0, 1,
+// 2, 3 sit at permute bytes 5, 1, 7, 3 (selectors 10, 8, 11, 9).
+__device__ __forceinline__ uint32_t sflip8x4(uint32_t v) {
+    return v ^ (__builtin_amdgcn_perm(v << 8, v, 0x090B080Au) & 0x7F7F7F7Fu);
 }
 // bytewise (a - b) mod 256
 __device__ __forceinline__ uint32_t sub8x4(uint32_t a, uint32_t b) {
@@ -1022,7 +1026,7 @@ __global__ __launch_bounds__(1024) void encode_tiles(EncodeLaunch a, DevTables t
 
     // z of one tile: difference bytes into LDS, then each lane's channel through the zigzag table
     auto stage = [&](uint2 tv, uint2 pv, uint32_t* z) {
-        *tile_st = make_uint2(sub8x4(ord8x4(tv.x), ord8x4(pv.x)), sub8x4(ord8x4(tv.y), ord8x4(pv.y)));
+        *tile_st = make_uint2(sub8x4(sflip8x4(tv.x), sflip8x4(pv.x)), sub8x4(sflip8x4(tv.y), sflip8x4(pv.y)));
         __builtin_amdgcn_wave_barrier();
 #pragma unroll
         for (uint32_t r = 0; r < kTileSteps; ++r) z[r] = zig[tile_rd[r * kLanes]];
@@ -1186,10 +1190,6 @@ typedef __attribute__((address_space(3))) uint16_t lds_u16;
 typedef __attribute__((address_space(3))) uint32_t lds_u32;
 
 // bytewise helpers on 4 packed e4m3 codes / symbols
-__device__ __forceinline__ uint32_t sflip8x4(uint32_t v) {   // v ^ 0x7F in the bytes whose sign bit is set
-    const uint32_t s = v & 0x80808080u;
-    return v ^ (s - (s >> 7));
-}
 __device__ __forceinline__ uint32_t add8x4(uint32_t a, uint32_t b) {
     return ((a & 0x7F7F7F7Fu) + (b & 0x7F7F7F7Fu)) ^ ((a ^ b) & 0x80808080u);
 }
@@ -1363,7 +1363,23 @@ __global__ __launch_bounds__(1024, 1) void decode_e4m3(DecodeLaunch a, DevTables
         0x00020000);
     bool bad = false;
 
-    for (uint32_t tb0 = ps.tb_begin + 2 * kDecChains * wave; tb0 < ps.tb_end; tb0 += 2 * kDecChains * nwave) {
+    // index entries of a round's streams, requested one round ahead (an absent stream reads the
+    // entries of the workgroup's last stream)
+    constexpr uint32_t kRound = 2 * kDecChains;
+    uint64_t ix0[kDecChains], ix1[kDecChains];
+    auto fetch_index = [&](uint32_t tb0) {
+#pragma unroll
+        for (uint32_t c = 0; c < kDecChains; ++c) {
+            const uint32_t tbc = min(tb0 + 2 * c + (upper ? 1u : 0u), ps.tb_end - 1);
+            const uint64_t sid = (uint64_t(ps.slab) * geo.ntb + tbc) * geo.ncg + ps.cg;
+            ix0[c] = index[sid];
+            ix1[c] = index[sid + 1];
+        }
+    };
+    fetch_index(ps.tb_begin + kRound * wave);
+    uint32_t padv = 0;                              // pad bytes of the previous round, checked late
+
+    for (uint32_t tb0 = ps.tb_begin + kRound * wave; tb0 < ps.tb_end; tb0 += kRound * nwave) {
         DecChain ch[kDecChains];
         DecState st[kDecChains];
         uint32_t tb[kDecChains], nw[kDecChains], size[kDecChains], rel[kDecChains];
@@ -1374,48 +1390,62 @@ __global__ __launch_bounds__(1024, 1) void decode_e4m3(DecodeLaunch a, DevTables
         // a coded stream
         uint32_t ldk[kDecChains], wrk[kDecChains], live[kDecChains];
         bool coded[kDecChains], raw[kDecChains];
+        uint64_t e0[kDecChains], e1[kDecChains];
+        uint32_t x0[kDecChains], c0[kDecChains], c1[kDecChains];
+        // every header and ring load of the round is issued before any of them is checked
+#pragma unroll
+        for (uint32_t c = 0; c < kDecChains; ++c) {
+            e0[c] = ix0[c];
+            e1[c] = ix1[c];
+            const uint64_t o = e0[c] & ~kRawBit;
+            rel[c] = o >= wlo && o - wlo < (1ull << 31) ? uint32_t(o - wlo) : 0u;
+            nw[c] = __builtin_amdgcn_raw_buffer_load_b32(L.rs, rel[c] + 128, 0, 0);
+            x0[c] = __builtin_amdgcn_raw_buffer_load_b32(L.rs, rel[c] + 4 * hl, 0, 0);
+            const uint32_t woff = rel[c] + kStreamHead;
+            c0[c] = __builtin_amdgcn_raw_buffer_load_b16(L.rs, woff + 2 * hl, 0, 0);
+            c1[c] = __builtin_amdgcn_raw_buffer_load_b16(L.rs, woff + 2 * kDecChunk + 2 * hl, 0, 0);
+            cw[c] = __builtin_amdgcn_raw_buffer_load_b16(L.rs, woff + 2 * kDecChunk * kDecFirst + 2 * hl, 0, 0);
+        }
+#pragma unroll
+        for (uint32_t c = 0; c < kDecChains; ++c) {
+            tb[c] = tb0 + 2 * c + (upper ? 1u : 0u);
+            // byte offset of this lane's first tile-domain row; an absent stream reads rows of tb0
+            rowo[c] = ((tb[c] < ps.tb_end ? tb[c] : tb0) * kSteps + r4) * rowb + q4;
+            pva[c] = __builtin_amdgcn_raw_buffer_load_b32(prs, rowo[c], 0, 0);
+            pvb[c] = __builtin_amdgcn_raw_buffer_load_b32(prs, rowo[c] + kDecTile * rowb, 0, 0);
+        }
+        if (tb0 + kRound * nwave < ps.tb_end) fetch_index(tb0 + kRound * nwave);
 #pragma unroll
         for (uint32_t c = 0; c < kDecChains; ++c) {
             const uint32_t hs = (tid >> 5) * kDecChains + c;          // stream slot in the workgroup
             ch[c].ringb = lb + OFF_R + hs * 2 * kDecRing;             // 256-byte aligned
             ch[c].tileb = lb + OFF_T + hs * kDecTile * kLanes + hl;
-            tb[c] = tb0 + 2 * c + (upper ? 1u : 0u);
-            // byte offset of this lane's first tile-domain row; an absent stream reads rows of tb0
-            rowo[c] = ((tb[c] < ps.tb_end ? tb[c] : tb0) * kSteps + r4) * rowb + q4;
-            // ---- stream header (every lane of the half reads the same entries)
+            // ---- stream header checks (every lane of the half holds the same entries)
             uint32_t x = kStateLow;
-            nw[c] = size[c] = rel[c] = 0;
+            size[c] = 0;
             coded[c] = raw[c] = false;
             if (tb[c] < ps.tb_end) {
-                const uint64_t sid = (uint64_t(ps.slab) * geo.ntb + tb[c]) * geo.ncg + ps.cg;
-                const uint64_t e0 = index[sid], e1 = index[sid + 1];
-                const uint64_t o = e0 & ~kRawBit, end = e1 & ~kRawBit;
+                const uint64_t o = e0[c] & ~kRawBit, end = e1[c] & ~kRawBit;
                 if (end < o || o < wlo || end > whi) {
                     bad = true;
-                } else if (e0 & kRawBit) {
+                } else if (e0[c] & kRawBit) {
                     if (end - o != kSyms) bad = true;
                     else raw[c] = true;
-                    rel[c] = uint32_t(o - wlo);
                 } else {
                     size[c] = uint32_t(end - o);
-                    rel[c] = uint32_t(o - wlo);
-                    if (size[c] < kStreamHead || size[c] % 4 != 0) {
+                    if (size[c] < kStreamHead || size[c] % 4 != 0 || nw[c] > (size[c] - kStreamHead) / 2) {
                         bad = true;
                     } else {
-                        nw[c] = __builtin_amdgcn_raw_buffer_load_b32(L.rs, rel[c] + 128, 0, 0);
-                        if (nw[c] > (size[c] - kStreamHead) / 2) {
-                            bad = true;
-                        } else {
-                            coded[c] = true;
-                            x = __builtin_amdgcn_raw_buffer_load_b32(L.rs, rel[c] + 4 * hl, 0, 0);
-                            if (x < kStateLow) bad = true;
-                        }
+                        coded[c] = true;
+                        x = x0[c];
+                        if (x < kStateLow) bad = true;
                     }
                 }
             }
+            if (!coded[c]) nw[c] = 0;
             const uint64_t cm = __ballot(coded[c]);
             live[c] = (uint32_t(cm) ? 0x8000u : 0u) | ((cm >> 32) ? 0x80000000u : 0u);
-            // word offset in the window (an absent stream reads from the window start)
+            // word offset in the window (a stream that is not coded reads from the window start)
             const uint32_t woff = coded[c] ? rel[c] + kStreamHead : 0u;
             ch[c].woff = woff;
             // escape window: the 4-byte aligned dwords from the start of the escape region (which
@@ -1425,18 +1455,13 @@ __global__ __launch_bounds__(1024, 1) void decode_e4m3(DecodeLaunch a, DevTables
             // ring: chunk k (words [32k, 32k + 32)) sits in slot k % slots; chunks 0 and 1 now,
             // the next one (chunk 1 again for a 2-chunk ring) requested for the first tile end
             lds_u16* ring16 = reinterpret_cast<lds_u16*>(ch[c].ringb);
-            ring16[hl] = __builtin_amdgcn_raw_buffer_load_b16(L.rs, woff + 2 * hl, 0, 0);
-            ring16[kDecChunk + hl] = __builtin_amdgcn_raw_buffer_load_b16(L.rs, woff + 2 * kDecChunk + 2 * hl, 0, 0);
-            cw[c] = __builtin_amdgcn_raw_buffer_load_b16(L.rs, woff + 2 * kDecChunk * kDecFirst + 2 * hl, 0, 0);
+            ring16[hl] = c0[c];
+            ring16[kDecChunk + hl] = c1[c];
             ldk[c] = kDecFirst * 0x00010001u;
             wrk[c] = 0x00010001u;
             st[c] = DecState{x, 0u, 0u};
         }
-#pragma unroll
-        for (uint32_t c = 0; c < kDecChains; ++c) {
-            pva[c] = __builtin_amdgcn_raw_buffer_load_b32(prs, rowo[c], 0, 0);
-            pvb[c] = __builtin_amdgcn_raw_buffer_load_b32(prs, rowo[c] + kDecTile * rowb, 0, 0);
-        }
+        if (padv != 0) bad = true;
         __builtin_amdgcn_wave_barrier();
 
         // one tile: its steps, reconstruction, escaped values, ring upkeep; pv holds the
@@ -1549,9 +1574,9 @@ __global__ __launch_bounds__(1024, 1) void decode_e4m3(DecodeLaunch a, DevTables
                 const uint32_t used = kStreamHead + 2 * nw[c] + ec;
                 if (st[c].x != kStateLow || pc != nw[c] || used > size[c]) bad = true;
                 else if (((used + 3) & ~3u) != size[c]) bad = true;
-                else if (hl < size[c] - used &&
-                         __builtin_amdgcn_raw_buffer_load_b8(L.rs, rel[c] + used + hl, 0, 0) != 0)
-                    bad = true;
+                // the pad bytes are read now and checked at the next round's start
+                padv |= __builtin_amdgcn_raw_buffer_load_b8(L.rs, hl < size[c] - used ? rel[c] + used + hl : 0x80000000u,
+                                                            0, 0);
             }
             if (raw[c]) {
                 // raw stream: its 4096 codes in (step, lane) order, copied row by row
@@ -1565,7 +1590,7 @@ __global__ __launch_bounds__(1024, 1) void decode_e4m3(DecodeLaunch a, DevTables
         }
         __builtin_amdgcn_wave_barrier();
     }
-    if (bad) atomicOr(a.status, 1u);
+    if (bad || padv != 0) atomicOr(a.status, 1u);
 }
 
 __global__ void clear_u32(uint32_t* p, uint32_t n) {
