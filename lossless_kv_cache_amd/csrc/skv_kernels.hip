@@ -323,7 +323,7 @@ __global__ __launch_bounds__(256) void copy_streams(EncodeLaunch a) {
     constexpr uint32_t EB = DT == SKV_E4M3 ? 1u : 2u;
     constexpr uint32_t RAW = kSyms * EB;
     const uint64_t n = a.n_streams;
-    const uint64_t sid = uint64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
+    const uint64_t sid = uint64_t(blockIdx.x) * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     if (sid >= n) return;
     const uint64_t head = kHeaderBytes + 8 * (n + 1);
     if (head + *a.total > a.out_capacity) return;        // caller reports SKV_ERR_CAPACITY
@@ -350,36 +350,67 @@ __global__ __launch_bounds__(256) void copy_streams(EncodeLaunch a) {
         return;
     }
     const uint32_t cnt = ms & 0x3FFFu, ecnt = (ms >> 14) & 0x3FFFu;
-    if (lane < 32) reinterpret_cast<uint32_t*>(dst)[lane] = reinterpret_cast<const uint32_t*>(src)[lane];
-    if (lane == 32) reinterpret_cast<uint32_t*>(dst)[32] = cnt;
-    const uint32_t* ws = reinterpret_cast<const uint32_t*>(src + RAW);
-    uint32_t* wd = reinterpret_cast<uint32_t*>(dst + kStreamHead);
-    if ((cnt & 1u) == 0) {
-        for (uint32_t j = lane; j < cnt / 2; j += 64) {
-            const uint32_t v = ws[cnt / 2 - 1 - j];
-            wd[j] = __builtin_amdgcn_alignbit(v, v, 16);
-        }
-    } else {
-        for (uint32_t j = lane; j < cnt / 2; j += 64) {
-            const uint32_t e = cnt - 1 - 2 * j;                // scratch word at container word 2j (even index)
-            wd[j] = (ws[e / 2] & 0xFFFFu) | (ws[e / 2 - 1] & 0xFFFF0000u);
-        }
-        // the last word (scratch word 0) alone: the escaped values follow it directly
-        if (lane == 0) reinterpret_cast<uint16_t*>(wd)[cnt - 1] = uint16_t(ws[0]);
-    }
-    // escaped values (few): element by element, reversed
-    uint8_t* ed = dst + kStreamHead + 2 * cnt;
-    if (EB == 1) {
-        const uint8_t* es = src + kStreamHead;
-        for (uint32_t q = lane; q < ecnt; q += 64) ed[q] = es[ecnt - 1 - q];
-    } else {
-        const uint16_t* es = reinterpret_cast<const uint16_t*>(src + kStreamHead);
-        for (uint32_t q = lane; q < ecnt; q += 64) reinterpret_cast<uint16_t*>(ed)[q] = es[ecnt - 1 - q];
-    }
-    // zero pad after the escaped values
     const uint32_t used = kStreamHead + 2 * cnt + EB * ecnt;
     const uint32_t total = (used + 3) & ~3u;
-    for (uint32_t q = used + lane; q < total; q += 64) dst[q] = 0;
+    // range-checked views of the stream's scratch and its container bytes: an access at
+    // kOut is dropped (loads return 0), so no load or store below needs a branch
+    constexpr uint32_t kOut = 0x80000000u;
+    const __amdgpu_buffer_rsrc_t srs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(src), (short)0, int(2 * RAW), 0x00020000);
+    const __amdgpu_buffer_rsrc_t drs = __builtin_amdgcn_make_buffer_rsrc(dst, (short)0, int(total), 0x00020000);
+    const uint32_t nd = cnt / 2;                              // container dwords holding two words
+    const bool odd = (cnt & 1u) != 0;
+    // one batch of container word dwords [j0, j0 + 256): even count, scratch dword nd - 1 - j
+    // with its halves swapped; odd count, the low half of scratch dword (cnt - 1) / 2 - j and
+    // the high half of the one below.  All loads are issued before the stores.
+    constexpr uint32_t B = 4;
+    auto words = [&](uint32_t j0, uint32_t (&wa)[B], uint32_t (&wb)[B]) {
+#pragma unroll
+        for (uint32_t k = 0; k < B; ++k) {
+            const uint32_t j = j0 + lane + 64 * k;
+            const uint32_t e = odd ? (cnt - 1) / 2 - j : nd - 1 - j;
+            wa[k] = __builtin_amdgcn_raw_buffer_load_b32(srs, j < nd ? RAW + 4 * e : kOut, 0, 0);
+            wb[k] = __builtin_amdgcn_raw_buffer_load_b32(srs, j < nd && odd ? RAW + 4 * e - 4 : kOut, 0, 0);
+        }
+    };
+    auto put_words = [&](uint32_t j0, const uint32_t (&wa)[B], const uint32_t (&wb)[B]) {
+#pragma unroll
+        for (uint32_t k = 0; k < B; ++k) {
+            const uint32_t j = j0 + lane + 64 * k;
+            const uint32_t v = odd ? (wa[k] & 0xFFFFu) | (wb[k] & 0xFFFF0000u) : __builtin_amdgcn_alignbit(wa[k], wa[k], 16);
+            __builtin_amdgcn_raw_buffer_store_b32(v, drs, j < nd ? kStreamHead + 4 * j : kOut, 0, 0);
+        }
+    };
+    // escaped values [q0, q0 + 64), reversed
+    auto esc_at = [&](uint32_t q0) {
+        const uint32_t q = q0 + lane;
+        const uint32_t o = q < ecnt ? kStreamHead + EB * (ecnt - 1 - q) : kOut;
+        return EB == 1 ? uint32_t(__builtin_amdgcn_raw_buffer_load_b8(srs, o, 0, 0))
+                       : uint32_t(__builtin_amdgcn_raw_buffer_load_b16(srs, o, 0, 0));
+    };
+    auto put_esc = [&](uint32_t q0, uint32_t v) {
+        const uint32_t q = q0 + lane;
+        const uint32_t o = q < ecnt ? kStreamHead + 2 * cnt + EB * q : kOut;
+        if (EB == 1) __builtin_amdgcn_raw_buffer_store_b8(uint8_t(v), drs, o, 0, 0);
+        else __builtin_amdgcn_raw_buffer_store_b16(uint16_t(v), drs, o, 0, 0);
+    };
+    const uint32_t hv = __builtin_amdgcn_raw_buffer_load_b32(srs, lane < 32 ? 4 * lane : kOut, 0, 0);
+    const uint32_t w0 = __builtin_amdgcn_raw_buffer_load_b32(srs, RAW, 0, 0);     // scratch word 0 (low half)
+    uint32_t wa[B], wb[B];
+    words(0, wa, wb);
+    const uint32_t ev = esc_at(0);
+    // states and count, words, the lone last word of an odd count, escaped values, zero pad
+    __builtin_amdgcn_raw_buffer_store_b32(lane == 32 ? cnt : hv, drs, lane <= 32 ? 4 * lane : kOut, 0, 0);
+    put_words(0, wa, wb);
+    __builtin_amdgcn_raw_buffer_store_b16(uint16_t(w0), drs, odd && lane == 0 ? kStreamHead + 2 * (cnt - 1) : kOut, 0, 0);
+    put_esc(0, ev);
+    __builtin_amdgcn_raw_buffer_store_b8(uint8_t(0), drs, used + lane < total ? used + lane : kOut, 0, 0);
+    // long streams: further batches
+    for (uint32_t j0 = 64 * B; j0 < nd; j0 += 64 * B) {
+        words(j0, wa, wb);
+        put_words(j0, wa, wb);
+    }
+    for (uint32_t q0 = 64; q0 < ecnt; q0 += 64) put_esc(q0, esc_at(q0));
 }
 
 // --------------------------------------------------------------- decode
