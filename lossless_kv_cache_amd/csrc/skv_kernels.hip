@@ -1534,23 +1534,27 @@ __global__ __launch_bounds__(1024, 1) void decode_e4m3(DecodeLaunch a, DevTables
             if (__builtin_expect(__ballot(efa != 0) != 0, 0)) {
 #pragma unroll
                 for (uint32_t c = 0; c < kDecChains; ++c) {
-                    if (__ballot(ef[c] != 0) == 0) continue;
-                    // escaped values of the half before this lane's (prefix sum of counts <= 4)
-                    const uint32_t cnt = __popc(ef[c]);
-                    const uint32_t base = __builtin_amdgcn_ubfe(st[c].E, L.fsh, 16);
-                    uint32_t pre = 0;
-                    for (uint32_t j = 0; j < 4; ++j) {
-                        const uint64_t m = __ballot(cnt > j);
-                        if (m == 0) break;
-                        uint32_t E = 0;
-                        pre += half_rank(m, E, L.fsh, L.lowm);
-                        st[c].E += E;
+                    const uint64_t m1 = __ballot(ef[c] != 0);
+                    if (m1 == 0) continue;
+                    // index of the lane's first escaped value in the stream's escape region: the
+                    // half's count so far plus the values of lower lanes (usually one per lane)
+                    uint32_t E1 = 0;
+                    uint32_t eidx = __builtin_amdgcn_ubfe(st[c].E, L.fsh, 16) + half_rank(m1, E1, L.fsh, L.lowm);
+                    st[c].E += E1;
+                    uint32_t f = ef[c], v = zt[c];
+                    if (__ballot((f & (f - 1u)) != 0) != 0) {
+                        const uint32_t cnt = __popc(f);
+                        for (uint32_t j = 1; j < 4; ++j) {
+                            const uint64_t m = __ballot(cnt > j);
+                            if (m == 0) break;
+                            uint32_t E = 0;
+                            eidx += half_rank(m, E, L.fsh, L.lowm);
+                            st[c].E += E;
+                        }
                     }
                     // the lane's escaped bytes in order; the first 128 bytes of a stream's escape
                     // region come from the window register, later ones from memory
-                    uint32_t f = ef[c], v = zt[c];
-                    uint32_t eidx = base + pre;
-                    while (__ballot(f != 0) != 0) {
+                    do {
                         const uint32_t sh = (__builtin_ctz(f | 0x80000000u) >> 3) * 8;   // byte of the value
                         const uint32_t pos = eidx + ea[c];
                         const uint32_t wv = __builtin_amdgcn_ds_bpermute(
@@ -1568,14 +1572,14 @@ __global__ __launch_bounds__(1024, 1) void decode_e4m3(DecodeLaunch a, DevTables
                             f &= f - 1u;
                             ++eidx;
                         }
-                    }
+                    } while (__ballot(f != 0) != 0);
                     zt[c] = v;
                 }
             }
 #pragma unroll
             for (uint32_t c = 0; c < kDecChains; ++c) {
                 if (coded[c])
-                    __builtin_amdgcn_raw_buffer_store_b32(recon8x4(pv[c], zt[c]), ors, rowo[c] + T * kDecTile * rowb, 0, 0);
+                    __builtin_amdgcn_raw_buffer_store_b32(recon8x4(pv[c], zt[c]), ors, rowo[c], T * kDecTile * rowb, 0);
                 // the chunk in cw goes into its slot; the next one is requested while the ring
                 // has a free slot (chunk ldk + 1 fits when ldk <= words consumed / 32 + slots - 2)
                 reinterpret_cast<lds_u16*>(ch[c].ringb)[__builtin_amdgcn_ubfe(ldk[c], L.fsh, kDecSlotBits) * kDecChunk + hl] =
@@ -1589,7 +1593,7 @@ __global__ __launch_bounds__(1024, 1) void decode_e4m3(DecodeLaunch a, DevTables
 #pragma unroll
             for (uint32_t c = 0; c < kDecChains; ++c)
                 if (T + 2 < kTiles)
-                    pv[c] = __builtin_amdgcn_raw_buffer_load_b32(prs, rowo[c] + (T + 2) * kDecTile * rowb, 0, 0);
+                    pv[c] = __builtin_amdgcn_raw_buffer_load_b32(prs, rowo[c], (T + 2) * kDecTile * rowb, 0);
             __builtin_amdgcn_wave_barrier();
         };
         for (uint32_t T = 0; T < kTiles; T += 2) {
