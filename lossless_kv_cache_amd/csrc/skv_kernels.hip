@@ -1272,17 +1272,22 @@ struct DecChain {
 // step is written stage by stage over the two chains (map bytes, then table
 // rows, then ring words) so that their LDS reads are in flight together, and
 // it is branch-free: the refill select is a v_cndmask on the ballot mask,
-// which keeps the ring read unconditional.
-template <bool GLOBAL, uint32_t FS>
+// which keeps the ring read unconditional.  `pre` runs before the first
+// step's map reads and `post` right after them, so work on the previous tile
+// fills the wait for those reads.
+template <bool GLOBAL, uint32_t FS, class Pre, class Post>
 __device__ __forceinline__ void dec_tile_steps(DecState (&st)[kDecChains], const DecLane& L,
-                                               const DecChain (&ch)[kDecChains], uint32_t (&sy)[kDecChains][kDecTile]) {
+                                               const DecChain (&ch)[kDecChains], uint32_t (&sy)[kDecChains][kDecTile],
+                                               Pre&& pre, Post&& post) {
 #pragma unroll
     for (uint32_t r = 0; r < kDecTile; ++r) {
         uint32_t sym[kDecChains], g[kDecChains], cu[kDecChains], xn[kDecChains], idx[kDecChains], w[kDecChains];
         uint64_t mw[kDecChains];
+        if (r == 0) pre();
 #pragma unroll
         for (uint32_t c = 0; c < kDecChains; ++c)
             sym[c] = *reinterpret_cast<const lds_u8*>((st[c].x & (kM - 1u)) | L.mapb);
+        if (r == 0) post();
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (uint32_t c = 0; c < kDecChains; ++c) {
@@ -1495,39 +1500,20 @@ __global__ __launch_bounds__(1024, 1) void decode_e4m3(DecodeLaunch a, DevTables
         if (padv != 0) bad = true;
         __builtin_amdgcn_wave_barrier();
 
-        // one tile: its steps, reconstruction, escaped values, ring upkeep; pv holds the
-        // tile's predictor row and is reloaded with the row two tiles ahead
-        auto tile_at = [&](uint32_t T, uint32_t (&pv)[kDecChains]) {
-            uint32_t sy[kDecChains][kDecTile];
-            DecState s0[kDecChains];
-#pragma unroll
-            for (uint32_t c = 0; c < kDecChains; ++c) s0[c] = st[c];
-            dec_tile_steps<false, FS>(st, L, ch, sy);
-            // a half of a coded stream that read past the last chunk written (word count above
-            // 32 (wrk + 1) in its field) decodes the tile again from memory
-            uint32_t over = 0;
+        // A tile's symbols go to the tile buffer at the end of its steps; the next tile's first
+        // step reads them back transposed (lane hl: step r4, lanes q4..q4+3 of its half, so the
+        // lanes of a half and the bytes of a lane run in decode order), resolves escaped values,
+        // reconstructs and stores the rows and reloads pv with the row two tiles ahead.
+        uint32_t zt[kDecChains];
+        auto fetch_tile = [&]() {
 #pragma unroll
             for (uint32_t c = 0; c < kDecChains; ++c)
-                over |= ~((wrk[c] << 5) + 0x80208020u - st[c].P) & live[c];
-            if (__builtin_expect(over != 0, 0)) {
-#pragma unroll
-                for (uint32_t c = 0; c < kDecChains; ++c) st[c] = s0[c];
-                dec_tile_steps<true, FS>(st, L, ch, sy);
-            }
-#pragma unroll
-            for (uint32_t c = 0; c < kDecChains; ++c)
-#pragma unroll
-                for (uint32_t r = 0; r < kDecTile; ++r)
-                    *reinterpret_cast<lds_u8*>(ch[c].tileb + r * kLanes) = uint8_t(sy[c][r]);
-            __builtin_amdgcn_wave_barrier();
-            // lane hl now holds the 4 symbols of step r4, lanes q4..q4+3 of its half, so the lanes
-            // of a half and the bytes of a lane run in decode order
-            uint32_t zt[kDecChains], ef[kDecChains];
-#pragma unroll
-            for (uint32_t c = 0; c < kDecChains; ++c) {
                 zt[c] = *reinterpret_cast<const lds_u32*>(ch[c].tileb - hl + r4 * kLanes + q4);
-                ef[c] = zero_bytes(zt[c] ^ escp);
-            }
+        };
+        auto finish = [&](uint32_t T, uint32_t (&pv)[kDecChains]) {
+            uint32_t ef[kDecChains];
+#pragma unroll
+            for (uint32_t c = 0; c < kDecChains; ++c) ef[c] = zero_bytes(zt[c] ^ escp);
             uint32_t efa = 0;
 #pragma unroll
             for (uint32_t c = 0; c < kDecChains; ++c) efa |= ef[c];
@@ -1580,6 +1566,37 @@ __global__ __launch_bounds__(1024, 1) void decode_e4m3(DecodeLaunch a, DevTables
             for (uint32_t c = 0; c < kDecChains; ++c) {
                 if (coded[c])
                     __builtin_amdgcn_raw_buffer_store_b32(recon8x4(pv[c], zt[c]), ors, rowo[c], T * kDecTile * rowb, 0);
+                if (T + 2 < kTiles)
+                    pv[c] = __builtin_amdgcn_raw_buffer_load_b32(prs, rowo[c], (T + 2) * kDecTile * rowb, 0);
+            }
+        };
+        // one tile: its steps (with the previous tile's finish inside the first one), its symbols
+        // to the tile buffer, ring upkeep; pvp holds the previous tile's predictor row
+        auto tile_at = [&](uint32_t T, uint32_t (&pvp)[kDecChains]) {
+            uint32_t sy[kDecChains][kDecTile];
+            DecState s0[kDecChains];
+#pragma unroll
+            for (uint32_t c = 0; c < kDecChains; ++c) s0[c] = st[c];
+            dec_tile_steps<false, FS>(
+                st, L, ch, sy, [&] { if (T > 0) fetch_tile(); }, [&] { if (T > 0) finish(T - 1, pvp); });
+            // a half of a coded stream that read past the last chunk written (word count above
+            // 32 (wrk + 1) in its field) decodes the tile again from memory
+            uint32_t over = 0;
+#pragma unroll
+            for (uint32_t c = 0; c < kDecChains; ++c)
+                over |= ~((wrk[c] << 5) + 0x80208020u - st[c].P) & live[c];
+            if (__builtin_expect(over != 0, 0)) {
+#pragma unroll
+                for (uint32_t c = 0; c < kDecChains; ++c) st[c] = s0[c];
+                dec_tile_steps<true, FS>(st, L, ch, sy, [] {}, [] {});
+            }
+#pragma unroll
+            for (uint32_t c = 0; c < kDecChains; ++c)
+#pragma unroll
+                for (uint32_t r = 0; r < kDecTile; ++r)
+                    *reinterpret_cast<lds_u8*>(ch[c].tileb + r * kLanes) = uint8_t(sy[c][r]);
+#pragma unroll
+            for (uint32_t c = 0; c < kDecChains; ++c) {
                 // the chunk in cw goes into its slot; the next one is requested while the ring
                 // has a free slot (chunk ldk + 1 fits when ldk <= words consumed / 32 + slots - 2)
                 reinterpret_cast<lds_u16*>(ch[c].ringb)[__builtin_amdgcn_ubfe(ldk[c], L.fsh, kDecSlotBits) * kDecChunk + hl] =
@@ -1590,16 +1607,14 @@ __global__ __launch_bounds__(1024, 1) void decode_e4m3(DecodeLaunch a, DevTables
                 cw[c] = __builtin_amdgcn_raw_buffer_load_b16(
                     L.rs, ch[c].woff + 2 * kDecChunk * __builtin_amdgcn_ubfe(ldk[c], L.fsh, 16) + 2 * hl, 0, 0);
             }
-#pragma unroll
-            for (uint32_t c = 0; c < kDecChains; ++c)
-                if (T + 2 < kTiles)
-                    pv[c] = __builtin_amdgcn_raw_buffer_load_b32(prs, rowo[c], (T + 2) * kDecTile * rowb, 0);
             __builtin_amdgcn_wave_barrier();
         };
         for (uint32_t T = 0; T < kTiles; T += 2) {
-            tile_at(T, pva);
-            tile_at(T + 1, pvb);
+            tile_at(T, pvb);
+            tile_at(T + 1, pva);
         }
+        fetch_tile();
+        finish(kTiles - 1, pvb);
 #pragma unroll
         for (uint32_t c = 0; c < kDecChains; ++c) {
             // ---- stream checks: states back at L, every word and escape consumed, zero pad
