@@ -553,10 +553,11 @@ __global__ __launch_bounds__(256) void decode_streams(DecodeLaunch a, DevTables 
 // 8 XCDs), which lets that XCD's L2 serve the other quarters or halves of each
 // line.
 struct LdsGeo {
-    uint32_t groups;   // line groups = slabs x token-block chunks x (channel groups / G)
-    uint32_t G;        // channel groups per line group
+    uint32_t groups;   // line groups = slabs x token-block chunks x (channel groups / (G cgw))
+    uint32_t G;        // workgroups per line group
     uint32_t ntbc;     // token-block chunks per slab
     uint32_t tbc;      // token blocks per chunk
+    uint32_t cgw;      // channel groups per workgroup
 };
 
 struct LdsPos {
@@ -570,8 +571,8 @@ __device__ __forceinline__ LdsPos lds_position(const Geo& geo, const LdsGeo& lg)
     LdsPos r;
     r.valid = g < lg.groups;
     const uint32_t c = (b / 8u) % lg.G;
-    const uint32_t ncgg = geo.ncg / lg.G;
-    r.cg = (g % ncgg) * lg.G + c;
+    const uint32_t ncgg = geo.ncg / (lg.G * lg.cgw);
+    r.cg = ((g % ncgg) * lg.G + c) * lg.cgw;
     const uint32_t rest = g / ncgg;
     const uint32_t tbc = rest % lg.ntbc;
     r.slab = rest / lg.ntbc;
@@ -1178,6 +1179,175 @@ __global__ __launch_bounds__(1024) void encode_tiles(EncodeLaunch a, DevTables t
     }
 }
 
+// The same coder with a workgroup on two adjacent channel groups: the two
+// half-waves of a wavefront code the two groups' streams of one token block,
+// so every row load covers 64 contiguous bytes of target and predictor.  The
+// tables of both groups sit in LDS ([symbols][64 lanes]); a stream's words
+// go through a 128-word ring that stores each completed 64-word chunk at
+// once, which keeps a workgroup's LDS small enough for two per CU.
+constexpr uint32_t kPairRing = 128;
+constexpr uint32_t kPairWaveLds = 2 * kTileSteps * kLanes + 2 * kPairRing * 2;
+__host__ __device__ constexpr uint32_t encode_pairs_lds(uint32_t fs) { return 2 * kLanes * fs * 16 + 16 * kPairWaveLds; }
+
+template <uint32_t DT>
+__global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8))) void encode_pairs(EncodeLaunch a, DevTables t, uint32_t fs, LdsGeo lg) {
+    static_assert(DT == SKV_E4M3, "byte elements");
+    constexpr uint32_t RAW = kSyms;
+    constexpr uint32_t MAXE = RAW - kStreamHead;
+    constexpr uint32_t kDrop = 0x80000000u;               // buffer offset past the range: the access is dropped
+    constexpr uint32_t kChunks = RAW / 128;                // 64-word chunks that fit the words region
+    extern __shared__ __align__(16) uint8_t lds[];
+    __shared__ uint8_t zig[256];
+    const Geo geo = geometry(a.shape);
+    const LdsPos ps = lds_position(geo, lg);
+    if (!ps.valid) return;
+    const uint32_t tab0 = ps.slab * geo.C + ps.cg * kLanes;                 // first table of the pair
+    uint4* lenc = reinterpret_cast<uint4*>(lds);                            // [fs symbols][64 lanes]
+    for (uint32_t i = threadIdx.x; i < 2 * kLanes * fs; i += blockDim.x) {
+        const uint32_t sym = i / (2 * kLanes), j = i % (2 * kLanes);
+        lenc[i] = t.enc[size_t(tab0 + j) * 256 + sym];
+    }
+    for (uint32_t i = threadIdx.x; i < 256; i += blockDim.x) zig[i] = uint8_t(zig8(i));
+    __syncthreads();
+
+    const uint32_t wave = threadIdx.x >> 6, nwave = blockDim.x >> 6;
+    const uint32_t hl = threadIdx.x & 31u;
+    const bool upper = (threadIdx.x & 32u) != 0;
+    const uint32_t fsh = upper ? 16u : 0u;
+    const uint32_t lane = 31u - hl;                        // format lane (reversed within the half)
+    const uint32_t tl = (upper ? kLanes : 0u) + lane;      // table column of the lane's channel
+    const uint32_t n = t.n[tab0 + tl];
+    uint8_t* tile = lds + size_t(2 * kLanes) * fs * 16 + wave * kPairWaveLds;
+    uint8_t* ring = tile + 2 * kTileSteps * kLanes;
+    // tile: [half][step][32 channels]; this lane loads 8 channels of one step and reads its channel back
+    const uint32_t ld_row = hl >> 2, ld_q = hl & 3u;
+    uint2* tile_st = reinterpret_cast<uint2*>(tile + (upper ? kTileSteps * kLanes : 0u) + ld_row * kLanes + ld_q * 8);
+    const uint8_t* tile_rd = tile + (upper ? kTileSteps * kLanes : 0u) + lane;
+    uint16_t* ring_h = reinterpret_cast<uint16_t*>(ring + (upper ? kPairRing * 2 : 0u));
+
+    const uint32_t rowb = geo.C;
+    const size_t slab_b = size_t(ps.slab) * geo.T * rowb + size_t(ps.cg) * kLanes + (upper ? kLanes : 0u) + ld_q * 8;
+    const uint8_t* tgt = static_cast<const uint8_t*>(a.target) + slab_b;
+    const uint8_t* aux = static_cast<const uint8_t*>(a.aux) + slab_b;
+    const uint64_t sid0 = (uint64_t(ps.slab) * geo.ntb + ps.tb_begin) * geo.ncg + ps.cg;
+    uint8_t* wgs = a.scratch + sid0 * (2 * RAW);
+    const uint32_t sstride = geo.ncg * (2 * RAW);
+    const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
+        wgs, (short)0, int((ps.tb_end - ps.tb_begin - 1) * sstride + 4 * RAW), 0x00020000);
+
+    // z of one tile: difference bytes into LDS, then each lane's channel through the zigzag table
+    auto stage = [&](uint2 tv, uint2 pv, uint32_t* z) {
+        *tile_st = make_uint2(sub8x4(sflip8x4(tv.x), sflip8x4(pv.x)), sub8x4(sflip8x4(tv.y), sflip8x4(pv.y)));
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (uint32_t r = 0; r < kTileSteps; ++r) z[r] = zig[tile_rd[r * kLanes]];
+        __builtin_amdgcn_wave_barrier();
+    };
+    const uint32_t* ring32 = reinterpret_cast<const uint32_t*>(ring_h);
+
+    for (uint32_t tb = ps.tb_begin + wave; tb < ps.tb_end; tb += nwave) {
+        const uint32_t ao = (tb - ps.tb_begin) * sstride + (upper ? 2 * RAW : 0u);
+        const uint32_t ebase = ao + kStreamHead - (upper ? 32u : 0u);   // upper-half slots carry a bias of 32
+        const uint32_t wreg = ao + RAW;
+        const uint8_t* tsrc = tgt + size_t(tb * kSteps + ld_row) * rowb;
+        const uint8_t* psrc = aux + size_t(tb * kSteps + ld_row) * rowb;
+        const size_t tstride = size_t(kTileSteps) * rowb;
+        constexpr int kTiles = kSteps / kTileSteps;
+
+        uint32_t zc[kTileSteps], zn[kTileSteps];
+        uint2 tv = *reinterpret_cast<const uint2*>(tsrc + (kTiles - 1) * tstride);
+        uint2 pv = *reinterpret_cast<const uint2*>(psrc + (kTiles - 1) * tstride);
+        stage(tv, pv, zc);
+        tv = *reinterpret_cast<const uint2*>(tsrc + (kTiles - 2) * tstride);
+        pv = *reinterpret_cast<const uint2*>(psrc + (kTiles - 2) * tstride);
+
+        uint32_t x = kStateLow;
+        uint32_t wp = 0;                                   // word counts: lower half | upper half << 16
+        uint32_t elo = 0, ehi = 0;                         // escape counts per half
+        uint4 ec = lenc[min(zc[kTileSteps - 1], n) * (2 * kLanes) + tl];
+        for (int j = kTiles - 1; j >= 0; --j) {
+            if (j > 0) {
+                stage(tv, pv, zn);
+                if (j > 1) {
+                    tv = *reinterpret_cast<const uint2*>(tsrc + size_t(j - 2) * tstride);
+                    pv = *reinterpret_cast<const uint2*>(psrc + size_t(j - 2) * tstride);
+                }
+            }
+#pragma unroll
+            for (int r = kTileSteps - 1; r >= 0; --r) {
+                const uint4 e = ec;
+                const uint32_t znext = r > 0 ? zc[r - 1] : zn[kTileSteps - 1];
+                ec = lenc[min(znext, n) * (2 * kLanes) + tl];
+                // words leave before the state absorbs the symbol
+                uint32_t xs = x;
+                const bool emit = xs >= e.x;
+                const uint64_t mw = __ballot(emit);
+                const uint32_t mlo = uint32_t(mw), mhi = uint32_t(mw >> 32);
+                const uint32_t pp = __popc(mlo) | (__popc(mhi) << 16);
+                // ring slot: this half's count mod 128 plus the emitting lanes below (mbcnt_lo counts the
+                // entire lower half for an upper lane, which the packed base subtracts again)
+                const uint32_t pk = (wp - (pp << 16)) & 0x007F007Fu;
+                const uint32_t slot =
+                    __builtin_amdgcn_mbcnt_hi(mhi, __builtin_amdgcn_mbcnt_lo(mlo, __builtin_amdgcn_ubfe(pk, fsh, 16)));
+                if (emit) ring_h[slot & (kPairRing - 1)] = uint16_t(xs & 0xFFFFu);
+                xs = emit ? xs >> 16 : xs;
+                const uint32_t qt = __umulhi(xs + (e.z >> 24), e.y) >> (e.w & 31u);   // floor(xs / f)
+                // x = xs + qt (4096 - f) + start, the start taken from the high half of e.w
+                const uint32_t xq = __umul24(qt, e.z) + xs;
+                asm("v_add_u32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:WORD_1"
+                    : "=v"(x) : "v"(xq), "v"(e.w));
+                // a completed 64-word chunk leaves the ring (at most one per step and stream)
+                const uint32_t cross = ((wp & 0x003F003Fu) + pp) & 0x00400040u;
+                if (cross) {
+                    __builtin_amdgcn_wave_barrier();
+                    const uint32_t ck = __builtin_amdgcn_ubfe(wp >> 6, fsh, 10);
+                    const uint32_t w = ring32[(ck & 1u) * 32 + hl];
+                    const bool mine = __builtin_amdgcn_ubfe(cross, fsh + 6, 1) != 0;
+                    __builtin_amdgcn_raw_buffer_store_b32(
+                        w, wrs, mine && ck < kChunks ? wreg + ck * 128 + 4 * hl : kDrop, 0, 0);
+                    __builtin_amdgcn_wave_barrier();
+                }
+                wp += pp;
+            }
+            // escaped values of this tile, in emission order (rare: skipped by the whole wavefront)
+            uint32_t zm = zc[0];
+#pragma unroll
+            for (uint32_t r = 1; r < kTileSteps; ++r) zm = max(zm, zc[r]);
+            if (__ballot(zm >= n) != 0) {
+#pragma unroll
+                for (int r = kTileSteps - 1; r >= 0; --r) {
+                    const bool esc = zc[r] >= n;
+                    const uint64_t me = __ballot(esc);
+                    if (me == 0) continue;
+                    const uint32_t mlo = uint32_t(me), mhi = uint32_t(me >> 32), plo = __popc(mlo);
+                    const uint32_t pk = min(elo, MAXE) | ((min(ehi, MAXE) + 32u - plo) << 16);
+                    const uint32_t slot = __builtin_amdgcn_mbcnt_hi(
+                        mhi, __builtin_amdgcn_mbcnt_lo(mlo, __builtin_amdgcn_ubfe(pk, fsh, 16)));
+                    __builtin_amdgcn_raw_buffer_store_b8(uint8_t(zc[r]), wrs, esc ? ebase + slot : kDrop, 0, 0);
+                    elo += plo;
+                    ehi += __popc(mhi);
+                }
+            }
+#pragma unroll
+            for (uint32_t r = 0; r < kTileSteps; ++r) zc[r] = zn[r];
+        }
+        // the partial last chunk, the final states and the stream's counts
+        __builtin_amdgcn_wave_barrier();
+        const uint32_t cnt = __builtin_amdgcn_ubfe(wp, fsh, 16), ecnt = upper ? ehi : elo;
+        const uint32_t ck = cnt >> 6;
+        const uint32_t w = ring32[(ck & 1u) * 32 + hl];
+        __builtin_amdgcn_raw_buffer_store_b32(w, wrs, ck < kChunks && 2 * hl < (cnt & 63u) ? wreg + ck * 128 + 4 * hl : kDrop,
+                                              0, 0);
+        __builtin_amdgcn_wave_barrier();
+        reinterpret_cast<uint32_t*>(wgs + ao)[lane] = x;
+        if (hl == 0) {
+            const uint64_t sid = sid0 + uint64_t(tb - ps.tb_begin) * geo.ncg + (upper ? 1u : 0u);
+            const uint32_t bytes = (kStreamHead + 2 * cnt + ecnt + 3) & ~3u;
+            a.meta[sid] = bytes >= RAW ? 0x80000000u : (cnt | (ecnt << 14));
+        }
+    }
+}
+
 // --------------------------------------------------------------- tiled e4m3 decode
 // One workgroup owns the 32 tables of a channel group: the complete
 // slot -> symbol maps (4096 bytes per table) and per symbol the 16-bit
@@ -1691,17 +1861,19 @@ const Variant& variant() {
 constexpr size_t kLdsLimit = 160 * 1024;
 
 // Work decomposition of the LDS kernels for a residual-mode shape.
-LdsGeo lds_geometry(const skv_shape& s) {
+LdsGeo lds_geometry(const skv_shape& s, uint32_t cgw = 1) {
     const uint32_t ncg = s.channels / kLanes, ntb = s.tokens / kSteps;
     const uint32_t line = s.dtype == SKV_E4M3 ? 4u : 2u;    // channel groups per 128-byte row segment
     LdsGeo g;
+    g.cgw = cgw;
     g.G = (ncg % line == 0) ? line : (ncg % 2 == 0 ? 2u : 1u);
+    g.G = std::max(1u, g.G / cgw);
     g.tbc = std::min<uint32_t>(ntb, 256u);
     // a workgroup's encoder scratch (tbc streams, ncg apart) is addressed with offsets below 2^31
     const uint64_t sstride = uint64_t(ncg) * 2 * kSyms * (s.dtype == SKV_E4M3 ? 1u : 2u);
     while (g.tbc > 1 && uint64_t(g.tbc) * sstride >= (1ull << 31)) g.tbc /= 2;
     g.ntbc = (ntb + g.tbc - 1) / g.tbc;
-    g.groups = s.layers * s.kv * g.ntbc * (ncg / g.G);
+    g.groups = s.layers * s.kv * g.ntbc * (ncg / (g.G * cgw));
     return g;
 }
 
@@ -1727,7 +1899,18 @@ hipError_t encode_all(const EncodeLaunch& a, const DevTables& t, hipStream_t st)
     const size_t lb = encode_lds_bytes(t, DT);
     const size_t lt = size_t(kLanes) * fc_stride(t) * 16 + (kLdsThreads / 64) * kTileWaveLds;
     const bool aligned = (reinterpret_cast<uintptr_t>(a.target) | reinterpret_cast<uintptr_t>(a.aux)) % 8 == 0;
-    if (DT == SKV_E4M3 && MODE == SKV_RESIDUAL && lt <= kLdsLimit && aligned && !g_force_v1 && variant().enc == 0) {
+    const uint32_t ncg = a.shape.channels / kLanes;
+    if (DT == SKV_E4M3 && MODE == SKV_RESIDUAL && ncg % 4 == 0 && 2 * encode_pairs_lds(fc_stride(t)) + 512 <= kLdsLimit &&
+        aligned && !g_force_v1 && variant().enc == 0) {
+        const LdsGeo lg = lds_geometry(a.shape, 2);
+        const size_t lp = encode_pairs_lds(fc_stride(t));
+        auto k = encode_pairs<SKV_E4M3>;
+        hipError_t e = allow_lds(k, lp);
+        if (e != hipSuccess) return e;
+        timed("encode_streams", st, [&] {
+            hipLaunchKernelGGL(k, dim3(lds_grid(lg)), dim3(kLdsThreads), lp, st, a, t, fc_stride(t), lg);
+        });
+    } else if (DT == SKV_E4M3 && MODE == SKV_RESIDUAL && lt <= kLdsLimit && aligned && !g_force_v1 && variant().enc == 0) {
         const LdsGeo lg = lds_geometry(a.shape);
         auto k = encode_tiles<SKV_E4M3>;
         hipError_t e = allow_lds(k, lt);

@@ -94,10 +94,14 @@ def test_ragged_grid_bf16(skv, orc):
     full_compare(skv, orc, t, p, tabs, oshape, "ragged bf16 6x2x1152x352")
 
 
-def test_e4m3_small(skv, orc):
-    cfg = gen.CONFIGS[2].with_tokens(640, layers=3, channels=160)
+@pytest.mark.parametrize("channels", [160, 256])
+def test_e4m3_small(skv, orc, channels):
+    """160 channels (5 channel groups) take the one-group encoder, 256 (a
+    multiple of 4 groups) the two-group one; 640 tokens leave a partial
+    round of token blocks."""
+    cfg = gen.CONFIGS[2].with_tokens(640, layers=3, channels=channels)
     t, p, tabs, oshape = residual_case(skv, orc, cfg)
-    full_compare(skv, orc, t, p, tabs, oshape, "e4m3 3x2x640x160")
+    full_compare(skv, orc, t, p, tabs, oshape, f"e4m3 3x2x640x{channels}")
 
 
 def test_checkerboard_small(skv, orc):
@@ -129,12 +133,14 @@ def test_edge_inputs(skv, orc, kind):
     full_compare(skv, orc, t, p, tabs, oshape, f"edge {kind}")
 
 
+@pytest.mark.parametrize("channels", [96, 128])
 @pytest.mark.parametrize("kind", ["equal", "random", "maxz", "escapes", "mixed"])
-def test_edge_inputs_e4m3(skv, orc, kind):
+def test_edge_inputs_e4m3(skv, orc, kind, channels):
     """The same degenerate inputs for byte elements, on a grid with an odd
-    number of token blocks (a wavefront runs one stream and idles the other
-    half); "mixed" alternates compressible and raw token blocks."""
-    cfg = gen.Config(92, "edge-e4m3", "e4m3", 2, 2, 640, 96)
+    number of token blocks (in the one-group encoder a wavefront runs one
+    stream and idles the other half; 128 channels take the two-group
+    encoder); "mixed" alternates compressible and raw token blocks."""
+    cfg = gen.Config(92, "edge-e4m3", "e4m3", 2, 2, 640, channels)
     t, p, tabs, oshape = residual_case(skv, orc, cfg)
     g = torch.Generator(device="cuda")
     g.manual_seed(19)
@@ -150,7 +156,7 @@ def test_edge_inputs_e4m3(skv, orc, kind):
         r = torch.randint(0, 256, p.shape, generator=g, device="cuda", dtype=torch.int32).to(torch.uint8)
         blk = (torch.arange(p.shape[2], device="cuda") // 128) % 2 == 1
         t = torch.where(blk[None, None, :, None], r, t)
-    full_compare(skv, orc, t, p, tabs, oshape, f"edge e4m3 {kind}")
+    full_compare(skv, orc, t, p, tabs, oshape, f"edge e4m3 {kind} {channels}")
 
 
 def test_corruption_and_wrong_tables(skv, orc):
