@@ -1356,8 +1356,9 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8))) void 
 // symbol's signed residual plus 128 (the escape symbol gets the byte its
 // zigzag value would have), and the (4096 - f, start) rows are indexed by
 // that byte, so the reconstruction needs no zigzag decode.  Each half wavefront runs
-// two streams as independent chains (4 streams per wavefront), which hides
-// the latency of the dependent LDS reads of a step.  Words come from a
+// one stream (kDecChains streams per half wavefront are supported; two chains
+// hide more LDS latency but measured slower, the kernel being bound by its
+// predictor and output traffic rather than by the chain).  Words come from a
 // 128-word ring per stream in LDS, refilled with one 32-word chunk per 4-step
 // tile; a chunk is requested one tile before it is written and predictor rows
 // two tiles before they are used, so global loads are rarely waited for.  A
@@ -1367,18 +1368,18 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8))) void 
 // end.  Symbols of 4 steps then go through a 4 x 32 byte tile in LDS so that
 // every lane reconstructs 4 channels of one token with bytewise arithmetic on
 // 4-byte predictor loads and stores.
-constexpr uint32_t kDecChains = 2;                           // streams per half wavefront
+constexpr uint32_t kDecChains = 1;                           // streams per half wavefront
 constexpr uint32_t kDecTile = 4;                             // steps per tile
 constexpr uint32_t kDecRing = 128;                           // words per stream ring
 constexpr uint32_t kDecChunk = 32;                           // words per ring chunk
-constexpr uint32_t kDecSlots = kDecRing / kDecChunk;           // chunks a ring holds
-constexpr uint32_t kDecSlotBits = kDecSlots == 4 ? 2 : 1;
-constexpr uint32_t kDecFirst = kDecSlots > 2 ? 2 : 1;          // chunk requested at the start of a stream
-static_assert(kDecSlots == 2 || kDecSlots == 4, "ring of 2 or 4 chunks");
+constexpr uint32_t kDecSlots = kDecRing / kDecChunk;         // chunks a ring holds
+constexpr uint32_t kDecSlotBits = 2;
+constexpr uint32_t kDecFirst = 2;                            // chunk requested at the start of a stream
+static_assert(kDecSlots == 4, "the ring upkeep assumes 4 chunks");
 constexpr uint32_t kDecStreams = (1024 / 32) * kDecChains;   // streams in flight per workgroup
 constexpr uint32_t kDecEscWin = 128;                         // bytes of escape region per stream held in a register
 
-// LDS: maps [32][4096] | 4096 - f [fs][32] u16 | start [fs][32] u16 | rings [64][128 words] | tiles [64][4][32]
+// LDS: maps [32][4096] | 4096 - f [fs][32] u16 | start [fs][32] u16 | rings [streams][RING words] | tiles [streams][4][32]
 __host__ __device__ constexpr uint32_t dec_e4m3_rings(uint32_t fs) {
     return (kLanes * kM + 2 * fs * kLanes * 2 + 255) & ~255u;
 }
@@ -1461,6 +1462,8 @@ __device__ __forceinline__ void dec_tile_steps(DecState (&st)[kDecChains], const
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (uint32_t c = 0; c < kDecChains; ++c) {
+            // the byte load already zero-extends; an empty asm hides the extension from the compiler
+            asm("" : "+v"(sym[c]));
             const uint32_t ga = (sym[c] << 6) + L.gb;
             g[c] = *reinterpret_cast<const lds_u16*>(ga);                         // 4096 - f
             cu[c] = *reinterpret_cast<const lds_u16*>(ga + FS * kLanes * 2);       // start
