@@ -1759,8 +1759,12 @@ __global__ __launch_bounds__(1024, 1) void decode_e4m3(DecodeLaunch a, DevTables
             for (uint32_t c = 0; c < kDecChains; ++c)
                 over |= ~((wrk[c] << 5) + 0x80208020u - st[c].P) & live[c];
             if (__builtin_expect(over != 0, 0)) {
+                // the escape count keeps what the previous tile's finish added meanwhile
 #pragma unroll
-                for (uint32_t c = 0; c < kDecChains; ++c) st[c] = s0[c];
+                for (uint32_t c = 0; c < kDecChains; ++c) {
+                    st[c].x = s0[c].x;
+                    st[c].P = s0[c].P;
+                }
                 dec_tile_steps<true, FS>(st, L, ch, sy, [] {}, [] {});
             }
 #pragma unroll
@@ -1808,6 +1812,432 @@ __global__ __launch_bounds__(1024, 1) void decode_e4m3(DecodeLaunch a, DevTables
                     __builtin_amdgcn_raw_buffer_store_b32(
                         __builtin_amdgcn_raw_buffer_load_b32(L.rs, rel[c] + k * kLanes + q4, 0, 0), ors,
                         rowo[c] + T * kDecTile * rowb, 0, 0);
+                }
+            }
+        }
+        __builtin_amdgcn_wave_barrier();
+    }
+    if (bad || padv != 0) atomicOr(a.status, 1u);
+}
+
+// --------------------------------------------------------------- tiled bf16 decode
+// The e4m3 decoder's structure (word rings, tile transposition, escapes
+// resolved once per tile) for 16-bit elements, whose tables use up to 255
+// direct symbols.  The 32 slot -> symbol maps would not fit next to 257-row
+// tables, so each map keeps the symbol of every even slot (2048 bytes per
+// table); the odd slot belongs to that symbol or to the next one, which then
+// starts there, so a step reads the rows of both and keeps the second when the
+// slot is at or past its start.  Rows are indexed by symbol (the escape
+// symbol is n), the 4 symbols of a tile row go through 16-bit arithmetic
+// (zigzag decode, order-preserving map, residual add mod 2^16) two per dword,
+// and predictor and output rows move 8 bytes per lane.
+constexpr uint32_t kBf16Rows = 257;                          // 256 symbols and a sentinel
+// a bf16 stream uses about 40 words per tile, so its ring takes 64-word chunks (two words per lane)
+constexpr uint32_t kBfChunk = 64;                            // words per ring chunk
+constexpr uint32_t kBfRing = 256;                            // words per stream ring (4 chunks)
+constexpr uint32_t kBfSlots = kBfRing / kBfChunk;
+constexpr uint32_t kBfFirst = 2;                             // chunk requested at the start of a stream
+__host__ __device__ constexpr uint32_t dec_bf16_rings() { return (kLanes * (kM / 2) + kBf16Rows * kLanes * 4 + 511) & ~511u; }
+__host__ __device__ constexpr uint32_t dec_bf16_lds() {
+    return dec_bf16_rings() + kDecStreams * (2 * kBfRing + kDecTile * kLanes);
+}
+
+__device__ __forceinline__ uint2 ld8(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t soff) {
+    typedef uint32_t v2u __attribute__((ext_vector_type(2)));
+    const v2u v = __builtin_amdgcn_raw_buffer_load_b64(r, off, soff, 0);
+    return make_uint2(v[0], v[1]);
+}
+__device__ __forceinline__ void st8(uint2 v, __amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t soff) {
+    typedef uint32_t v2u __attribute__((ext_vector_type(2)));
+    const v2u w = {v.x, v.y};
+    __builtin_amdgcn_raw_buffer_store_b64(w, r, off, soff, 0);
+}
+// v ^ 0x7FFF in each 16-bit half whose sign bit is set (the order-preserving
+// code of a bf16 pattern is this flip ^ 0x8000); v_perm selectors 8 and 9
+// spread the signs of bytes 1 and 3 over their halves
+__device__ __forceinline__ uint32_t sflip16x2(uint32_t v) {
+    return v ^ (__builtin_amdgcn_perm(v, v, 0x09090808u) & 0x7FFF7FFFu);
+}
+// targets of two predictor values and two zigzag symbols: ord(t) = ord(p) + r
+// mod 2^16 is flip(t) = flip(p) + r mod 2^16
+__device__ __forceinline__ uint32_t recon16x2(uint32_t p, uint32_t z) {
+    typedef unsigned short us2 __attribute__((ext_vector_type(2)));
+    const uint32_t r = ((z >> 1) & 0x7FFF7FFFu) ^ __umul24(z & 0x00010001u, 0xFFFFu);
+    const us2 s = __builtin_bit_cast(us2, sflip16x2(p)) + __builtin_bit_cast(us2, r);
+    return sflip16x2(__builtin_bit_cast(uint32_t, s));
+}
+
+// The steps of one tile (see dec_tile_steps); the map lookup reads the rows of
+// the even slot's symbol and of the next symbol.
+template <bool GLOBAL, class Pre, class Post>
+__device__ __forceinline__ void dec_tile_steps_bf16(DecState (&st)[kDecChains], const DecLane& L,
+                                                    const DecChain (&ch)[kDecChains],
+                                                    uint32_t (&sy)[kDecChains][kDecTile], Pre&& pre, Post&& post) {
+#pragma unroll
+    for (uint32_t r = 0; r < kDecTile; ++r) {
+        uint32_t s0[kDecChains], e0[kDecChains], e1[kDecChains], xn[kDecChains], idx[kDecChains], w[kDecChains];
+        uint64_t mw[kDecChains];
+        if (r == 0) pre();
+#pragma unroll
+        for (uint32_t c = 0; c < kDecChains; ++c)
+            s0[c] = *reinterpret_cast<const lds_u8*>(__builtin_amdgcn_ubfe(st[c].x, 1, 11) | L.mapb);
+        if (r == 0) post();
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (uint32_t c = 0; c < kDecChains; ++c) {
+            asm("" : "+v"(s0[c]));
+            const uint32_t ra = (s0[c] << 7) + L.gb;
+            e0[c] = *reinterpret_cast<const lds_u32*>(ra);
+            e1[c] = *reinterpret_cast<const lds_u32*>(ra + kLanes * 4);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (uint32_t c = 0; c < kDecChains; ++c) {
+            const bool adv = (st[c].x & (kM - 1u)) >= (e1[c] >> 16);
+            const uint32_t e = adv ? e1[c] : e0[c];
+            sy[c][r] = s0[c] + (adv ? 1u : 0u);
+            // x - (x >> 12) (4096 - f) - start, both from the row word
+            uint32_t m, y;
+            asm("v_mul_u32_u24_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:WORD_0"
+                : "=v"(m) : "v"(st[c].x >> kProbBits), "v"(e));
+            asm("v_sub_u32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:WORD_1"
+                : "=v"(y) : "v"(st[c].x - m), "v"(e));
+            xn[c] = y;
+            mw[c] = __ballot(xn[c] < kStateLow);
+            idx[c] = half_rank(mw[c], st[c].P, L.fsh, L.lowm);
+            if (GLOBAL) w[c] = __builtin_amdgcn_raw_buffer_load_b16(L.rs, ch[c].woff + 2 * idx[c], 0, 0);
+            else w[c] = *reinterpret_cast<const lds_u16*>(((idx[c] << 1) & (2 * kBfRing - 2)) | ch[c].ringb);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (uint32_t c = 0; c < kDecChains; ++c) {
+            uint32_t x;
+            asm("v_cndmask_b32_e64 %0, %1, %2, %3" : "=v"(x) : "v"(xn[c]), "v"((xn[c] << 16) | w[c]), "s"(mw[c]));
+            st[c].x = x;
+        }
+    }
+}
+
+__global__ __launch_bounds__(1024, 1) void decode_bf16(DecodeLaunch a, DevTables t, LdsGeo lg) {
+    constexpr uint32_t OFF_G = kLanes * (kM / 2);
+    constexpr uint32_t OFF_R = dec_bf16_rings();
+    constexpr uint32_t OFF_T = OFF_R + kDecStreams * 2 * kBfRing;
+    constexpr uint32_t kTiles = kSteps / kDecTile;
+    extern __shared__ __align__(16) uint8_t lds[];
+    const uint32_t lb = uint32_t(uintptr_t(lds));                  // LDS offset of the dynamic block
+    const Geo geo = geometry(a.shape);
+    const LdsPos ps = lds_position(geo, lg);
+    if (!ps.valid) return;
+    const uint32_t tid = threadIdx.x;
+    const uint32_t tab0 = ps.slab * geo.C + ps.cg * kLanes;
+    // rows by symbol: (4096 - f) | start << 16; symbols past n and the sentinel row 256 start at 4096
+    uint32_t* lrow = reinterpret_cast<uint32_t*>(lds + OFF_G);           // [257 rows][32 lanes]
+    for (uint32_t i = tid; i < kBf16Rows * kLanes; i += blockDim.x) {
+        const uint32_t row = i / kLanes;
+        const uint32_t fc = row < 256 ? t.fc[size_t(tab0 + i % kLanes) * 256 + row] : (kM << 16);
+        lrow[i] = (kM - (fc & 0xFFFFu)) | (fc & 0xFFFF0000u);
+    }
+    {
+        // half maps: the symbol of every even slot (the odd slot belongs to the same symbol or
+        // to the next one, which then starts there), from the group's contiguous slot maps
+        const uint4* src = reinterpret_cast<const uint4*>(t.slot + size_t(tab0) * kM);
+        uint2* dst = reinterpret_cast<uint2*>(lds);
+#pragma unroll
+        for (uint32_t q = 0; q < kLanes * kM / 16 / 1024; ++q) {
+            const uint4 v = src[q * 1024 + tid];
+            dst[q * 1024 + tid] = make_uint2(__builtin_amdgcn_perm(v.y, v.x, 0x06040200u),
+                                             __builtin_amdgcn_perm(v.w, v.z, 0x06040200u));
+        }
+    }
+    __syncthreads();
+
+    const uint32_t wave = tid >> 6, nwave = blockDim.x >> 6;
+    const uint32_t hl = tid & 31u;
+    const bool upper = (tid & 32u) != 0;
+    const uint32_t r4 = hl >> 3, q4 = (hl & 7u) * 4;               // tile-domain row and byte column
+
+    const uint32_t rowb = geo.C * 2;
+    const uint64_t* index = reinterpret_cast<const uint64_t*>(a.in + kHeaderBytes);
+    const uint8_t* pay = a.in + kHeaderBytes + 8 * (a.n_streams + 1);
+    const uint64_t sfirst = (uint64_t(ps.slab) * geo.ntb + ps.tb_begin) * geo.ncg + ps.cg;
+    const uint64_t slast = (uint64_t(ps.slab) * geo.ntb + ps.tb_end - 1) * geo.ncg + ps.cg;
+    const uint64_t wlo = index[sfirst] & ~kRawBit, whi = index[slast + 1] & ~kRawBit;
+    if (whi < wlo || whi > a.payload_bytes || whi - wlo >= (1ull << 31)) {
+        if (tid == 0) atomicOr(a.status, 1u);
+        return;
+    }
+    DecLane L;
+    L.mapb = lb + hl * (kM / 2);
+    L.gb = lb + OFF_G + hl * 4;                                     // row of symbol z at z * 128 + gb
+    L.fsh = upper ? 16u : 0u;
+    L.lowm = upper ? 0u : 0xFFFFFFFFu;
+    // every payload read of the workgroup goes through one range-checked resource
+    L.rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(pay + wlo), (short)0, int(whi - wlo), 0x00020000);
+    // tile-domain bytes: n (the escape symbol) of the lane's 4 channels
+    uint32_t np = 0;
+#pragma unroll
+    for (uint32_t k = 0; k < 4; ++k) np |= min(t.n[tab0 + q4 + k], 255u) << (8 * k);
+    // predictor and output rows of the slab's channel group, 32-bit offsets from one base each
+    const size_t slab_b = size_t(ps.slab) * geo.T * rowb + size_t(ps.cg) * kLanes * 2;
+    const __amdgpu_buffer_rsrc_t prs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<void*>(static_cast<const void*>(static_cast<const uint8_t*>(a.aux) + slab_b)), (short)0,
+        int(uint32_t(geo.T - 1) * rowb + 2 * kLanes), 0x00020000);
+    const __amdgpu_buffer_rsrc_t ors = __builtin_amdgcn_make_buffer_rsrc(
+        static_cast<void*>(static_cast<uint8_t*>(a.out) + slab_b), (short)0,
+        int(uint32_t(geo.T - 1) * rowb + 2 * kLanes), 0x00020000);
+    bool bad = false;
+
+    // index entries of a round's streams, requested one round ahead (an absent stream reads the
+    // entries of the workgroup's last stream)
+    constexpr uint32_t kRound = 2 * kDecChains;
+    uint64_t ix0[kDecChains], ix1[kDecChains];
+    auto fetch_index = [&](uint32_t tb0) {
+#pragma unroll
+        for (uint32_t c = 0; c < kDecChains; ++c) {
+            const uint32_t tbc = min(tb0 + 2 * c + (upper ? 1u : 0u), ps.tb_end - 1);
+            const uint64_t sid = (uint64_t(ps.slab) * geo.ntb + tbc) * geo.ncg + ps.cg;
+            ix0[c] = index[sid];
+            ix1[c] = index[sid + 1];
+        }
+    };
+    fetch_index(ps.tb_begin + kRound * wave);
+    uint32_t padv = 0;                              // pad bytes of the previous round, checked late
+
+    for (uint32_t tb0 = ps.tb_begin + kRound * wave; tb0 < ps.tb_end; tb0 += kRound * nwave) {
+        DecChain ch[kDecChains];
+        DecState st[kDecChains];
+        uint32_t tb[kDecChains], nw[kDecChains], size[kDecChains], rel[kDecChains];
+        uint32_t cw[kDecChains], rowo[kDecChains];
+        uint2 pva[kDecChains], pvb[kDecChains];
+        uint32_t ew[kDecChains], ea[kDecChains];
+        // ring upkeep, both halves packed (lower in bits 0..15): ldk = chunk held in cw,
+        // wrk = last chunk written to the ring, live = 0x8000 in the field of a half with
+        // a coded stream
+        uint32_t ldk[kDecChains], wrk[kDecChains], live[kDecChains];
+        bool coded[kDecChains], raw[kDecChains];
+        uint64_t e0[kDecChains], e1[kDecChains];
+        uint32_t x0[kDecChains], c0[kDecChains], c1[kDecChains];
+        // every header and ring load of the round is issued before any of them is checked
+#pragma unroll
+        for (uint32_t c = 0; c < kDecChains; ++c) {
+            e0[c] = ix0[c];
+            e1[c] = ix1[c];
+            const uint64_t o = e0[c] & ~kRawBit;
+            rel[c] = o >= wlo && o - wlo < (1ull << 31) ? uint32_t(o - wlo) : 0u;
+            nw[c] = __builtin_amdgcn_raw_buffer_load_b32(L.rs, rel[c] + 128, 0, 0);
+            x0[c] = __builtin_amdgcn_raw_buffer_load_b32(L.rs, rel[c] + 4 * hl, 0, 0);
+            const uint32_t woff = rel[c] + kStreamHead;
+            c0[c] = __builtin_amdgcn_raw_buffer_load_b32(L.rs, woff + 4 * hl, 0, 0);
+            c1[c] = __builtin_amdgcn_raw_buffer_load_b32(L.rs, woff + 2 * kBfChunk + 4 * hl, 0, 0);
+            cw[c] = __builtin_amdgcn_raw_buffer_load_b32(L.rs, woff + 2 * kBfChunk * kBfFirst + 4 * hl, 0, 0);
+        }
+#pragma unroll
+        for (uint32_t c = 0; c < kDecChains; ++c) {
+            tb[c] = tb0 + 2 * c + (upper ? 1u : 0u);
+            // byte offset of this lane's first tile-domain row; an absent stream reads rows of tb0
+            rowo[c] = ((tb[c] < ps.tb_end ? tb[c] : tb0) * kSteps + r4) * rowb + 2 * q4;
+            pva[c] = ld8(prs, rowo[c], 0);
+            pvb[c] = ld8(prs, rowo[c], kDecTile * rowb);
+        }
+        if (tb0 + kRound * nwave < ps.tb_end) fetch_index(tb0 + kRound * nwave);
+#pragma unroll
+        for (uint32_t c = 0; c < kDecChains; ++c) {
+            const uint32_t hs = (tid >> 5) * kDecChains + c;          // stream slot in the workgroup
+            ch[c].ringb = lb + OFF_R + hs * 2 * kBfRing;              // 512-byte aligned
+            ch[c].tileb = lb + OFF_T + hs * kDecTile * kLanes + hl;
+            // ---- stream header checks (every lane of the half holds the same entries)
+            uint32_t x = kStateLow;
+            size[c] = 0;
+            coded[c] = raw[c] = false;
+            if (tb[c] < ps.tb_end) {
+                const uint64_t o = e0[c] & ~kRawBit, end = e1[c] & ~kRawBit;
+                if (end < o || o < wlo || end > whi) {
+                    bad = true;
+                } else if (e0[c] & kRawBit) {
+                    if (end - o != 2 * kSyms) bad = true;
+                    else raw[c] = true;
+                } else {
+                    size[c] = uint32_t(end - o);
+                    if (size[c] < kStreamHead || size[c] % 4 != 0 || nw[c] > (size[c] - kStreamHead) / 2) {
+                        bad = true;
+                    } else {
+                        coded[c] = true;
+                        x = x0[c];
+                        if (x < kStateLow) bad = true;
+                    }
+                }
+            }
+            if (!coded[c]) nw[c] = 0;
+            const uint64_t cm = __ballot(coded[c]);
+            live[c] = (uint32_t(cm) ? 0x8000u : 0u) | ((cm >> 32) ? 0x80000000u : 0u);
+            // word offset in the window (a stream that is not coded reads from the window start)
+            const uint32_t woff = coded[c] ? rel[c] + kStreamHead : 0u;
+            ch[c].woff = woff;
+            // escape window: the 4-byte aligned dwords from the start of the escape region (which
+            // sits 0 or 2 bytes past a dword boundary), 64 values; a stream's dwords never cross its
+            // padded end
+            ea[c] = (woff + 2 * nw[c]) & 3u;
+            ew[c] = __builtin_amdgcn_raw_buffer_load_b32(L.rs, ((woff + 2 * nw[c]) & ~3u) + 4 * hl, 0, 0);
+            // ring: chunk k (words [64k, 64k + 64), two per lane) sits in slot k % 4; chunks 0
+            // and 1 now, chunk 2 requested for the first tile end
+            lds_u32* ring32 = reinterpret_cast<lds_u32*>(ch[c].ringb);
+            ring32[hl] = c0[c];
+            ring32[kBfChunk / 2 + hl] = c1[c];
+            ldk[c] = kBfFirst * 0x00010001u;
+            wrk[c] = 0x00010001u;
+            st[c] = DecState{x, 0u, 0u};
+        }
+        if (padv != 0) bad = true;
+        __builtin_amdgcn_wave_barrier();
+
+        // A tile's symbols go to the tile buffer at the end of its steps; the next tile's first
+        // step reads them back transposed (lane hl: step r4, lanes q4..q4+3 of its half, so the
+        // lanes of a half and the bytes of a lane run in decode order), resolves escaped values,
+        // reconstructs and stores the rows and reloads pv with the row two tiles ahead.
+        uint32_t zt[kDecChains];
+        auto fetch_tile = [&]() {
+#pragma unroll
+            for (uint32_t c = 0; c < kDecChains; ++c)
+                zt[c] = *reinterpret_cast<const lds_u32*>(ch[c].tileb - hl + r4 * kLanes + q4);
+        };
+        auto finish = [&](uint32_t T, uint2 (&pv)[kDecChains]) {
+            uint32_t ef[kDecChains];
+#pragma unroll
+            for (uint32_t c = 0; c < kDecChains; ++c) ef[c] = zero_bytes(zt[c] ^ np);
+            // the lane's 4 symbols as 16-bit values, two per dword
+            uint32_t zz[kDecChains][2];
+#pragma unroll
+            for (uint32_t c = 0; c < kDecChains; ++c) {
+                zz[c][0] = __builtin_amdgcn_perm(0u, zt[c], 0x0c010c00u);
+                zz[c][1] = __builtin_amdgcn_perm(0u, zt[c], 0x0c030c02u);
+            }
+            uint32_t efa = 0;
+#pragma unroll
+            for (uint32_t c = 0; c < kDecChains; ++c) efa |= ef[c];
+            if (__builtin_expect(__ballot(efa != 0) != 0, 0)) {
+#pragma unroll
+                for (uint32_t c = 0; c < kDecChains; ++c) {
+                    const uint64_t m1 = __ballot(ef[c] != 0);
+                    if (m1 == 0) continue;
+                    // index of the lane's first escaped value in the stream's escape region: the
+                    // half's count so far plus the values of lower lanes (usually one per lane)
+                    uint32_t E1 = 0;
+                    uint32_t eidx = __builtin_amdgcn_ubfe(st[c].E, L.fsh, 16) + half_rank(m1, E1, L.fsh, L.lowm);
+                    st[c].E += E1;
+                    uint32_t f = ef[c];
+                    if (__ballot((f & (f - 1u)) != 0) != 0) {
+                        const uint32_t cnt = __popc(f);
+                        for (uint32_t j = 1; j < 4; ++j) {
+                            const uint64_t m = __ballot(cnt > j);
+                            if (m == 0) break;
+                            uint32_t E = 0;
+                            eidx += half_rank(m, E, L.fsh, L.lowm);
+                            st[c].E += E;
+                        }
+                    }
+                    // the lane's escaped values in order (16 bits each); the first 128 bytes of a
+                    // stream's escape region come from the window register, later ones from memory
+                    do {
+                        const uint32_t kv = __builtin_ctz(f | 0x80000000u) >> 3;         // value 0..3
+                        const uint32_t pos = 2 * eidx + ea[c];
+                        const uint32_t wv = __builtin_amdgcn_ds_bpermute(
+                            int(((pos >> 2) + (upper ? 32u : 0u)) << 2), int(ew[c]));
+                        uint32_t e = (wv >> ((pos & 3u) * 8)) & 0xFFFFu;
+                        if (__ballot(f != 0 && pos >= kDecEscWin) != 0) {
+                            const uint32_t g = __builtin_amdgcn_raw_buffer_load_b16(
+                                L.rs, ch[c].woff + 2 * nw[c] + 2 * eidx, 0, 0);
+                            e = pos >= kDecEscWin ? g : e;
+                        }
+                        if (f != 0) {
+                            // a canonical encoder codes a value below n directly
+                            if (coded[c] && e < ((np >> (8 * kv)) & 0xFFu)) bad = true;
+                            const uint32_t sh = (kv & 1u) * 16;
+                            if (kv < 2) zz[c][0] = (zz[c][0] & ~(0xFFFFu << sh)) | (e << sh);
+                            else zz[c][1] = (zz[c][1] & ~(0xFFFFu << sh)) | (e << sh);
+                            f &= f - 1u;
+                            ++eidx;
+                        }
+                    } while (__ballot(f != 0) != 0);
+                }
+            }
+#pragma unroll
+            for (uint32_t c = 0; c < kDecChains; ++c) {
+                if (coded[c])
+                    st8(make_uint2(recon16x2(pv[c].x, zz[c][0]), recon16x2(pv[c].y, zz[c][1])), ors, rowo[c],
+                        T * kDecTile * rowb);
+                if (T + 2 < kTiles) pv[c] = ld8(prs, rowo[c], (T + 2) * kDecTile * rowb);
+            }
+        };
+        // one tile: its steps (with the previous tile's finish inside the first one), its symbols
+        // to the tile buffer, ring upkeep; pvp holds the previous tile's predictor row
+        auto tile_at = [&](uint32_t T, uint2 (&pvp)[kDecChains]) {
+            uint32_t sy[kDecChains][kDecTile];
+            DecState s0[kDecChains];
+#pragma unroll
+            for (uint32_t c = 0; c < kDecChains; ++c) s0[c] = st[c];
+            dec_tile_steps_bf16<false>(
+                st, L, ch, sy, [&] { if (T > 0) fetch_tile(); }, [&] { if (T > 0) finish(T - 1, pvp); });
+            // a half of a coded stream that read past the last chunk written (word count above
+            // 64 (wrk + 1) in its field) decodes the tile again from memory
+            uint32_t over = 0;
+#pragma unroll
+            for (uint32_t c = 0; c < kDecChains; ++c)
+                over |= ~((wrk[c] << 6) + 0x80408040u - st[c].P) & live[c];
+            if (__builtin_expect(over != 0, 0)) {
+                // the escape count keeps what the previous tile's finish added meanwhile
+#pragma unroll
+                for (uint32_t c = 0; c < kDecChains; ++c) {
+                    st[c].x = s0[c].x;
+                    st[c].P = s0[c].P;
+                }
+                dec_tile_steps_bf16<true>(st, L, ch, sy, [] {}, [] {});
+            }
+#pragma unroll
+            for (uint32_t c = 0; c < kDecChains; ++c)
+#pragma unroll
+                for (uint32_t r = 0; r < kDecTile; ++r)
+                    *reinterpret_cast<lds_u8*>(ch[c].tileb + r * kLanes) = uint8_t(sy[c][r]);
+#pragma unroll
+            for (uint32_t c = 0; c < kDecChains; ++c) {
+                // the chunk in cw goes into its slot; the next one is requested while the ring
+                // has a free slot (chunk ldk + 1 fits when ldk <= words consumed / 64 + slots - 2)
+                reinterpret_cast<lds_u32*>(ch[c].ringb)[__builtin_amdgcn_ubfe(ldk[c], L.fsh, 2) * (kBfChunk / 2) + hl] =
+                    cw[c];
+                wrk[c] = ldk[c];
+                const uint32_t room = ((st[c].P >> 6) & 0x03FF03FFu) + (0x8000u + kBfSlots - 2) * 0x00010001u - ldk[c];
+                ldk[c] += (room >> 15) & 0x00010001u;
+                cw[c] = __builtin_amdgcn_raw_buffer_load_b32(
+                    L.rs, ch[c].woff + 2 * kBfChunk * __builtin_amdgcn_ubfe(ldk[c], L.fsh, 16) + 4 * hl, 0, 0);
+            }
+            __builtin_amdgcn_wave_barrier();
+        };
+        for (uint32_t T = 0; T < kTiles; T += 2) {
+            tile_at(T, pvb);
+            tile_at(T + 1, pva);
+        }
+        fetch_tile();
+        finish(kTiles - 1, pvb);
+#pragma unroll
+        for (uint32_t c = 0; c < kDecChains; ++c) {
+            // ---- stream checks: states back at L, every word and escape consumed, zero pad
+            if (coded[c]) {
+                const uint32_t pc = __builtin_amdgcn_ubfe(st[c].P, L.fsh, 16);
+                const uint32_t ec = __builtin_amdgcn_ubfe(st[c].E, L.fsh, 16);
+                const uint32_t used = kStreamHead + 2 * nw[c] + 2 * ec;
+                if (st[c].x != kStateLow || pc != nw[c] || used > size[c]) bad = true;
+                else if (((used + 3) & ~3u) != size[c]) bad = true;
+                // the pad bytes are read now and checked at the next round's start
+                padv |= __builtin_amdgcn_raw_buffer_load_b8(L.rs, hl < size[c] - used ? rel[c] + used + hl : 0x80000000u,
+                                                            0, 0);
+            }
+            if (raw[c]) {
+                // raw stream: its 4096 values in (step, lane) order, copied row by row (the payload
+                // is only 4-byte aligned)
+                for (uint32_t T = 0; T < kTiles; ++T) {
+                    const uint32_t o = rel[c] + (T * kDecTile + r4) * 2 * kLanes + 2 * q4;
+                    st8(make_uint2(__builtin_amdgcn_raw_buffer_load_b32(L.rs, o, 0, 0),
+                                   __builtin_amdgcn_raw_buffer_load_b32(L.rs, o + 4, 0, 0)),
+                        ors, rowo[c], T * kDecTile * rowb);
                 }
             }
         }
@@ -1970,6 +2400,17 @@ hipError_t decode_all(const DecodeLaunch& a, const DevTables& t, hipStream_t st)
         if (e != hipSuccess) return e;
         timed("decode_streams", st, [&] {
             hipLaunchKernelGGL(k, dim3(lds_grid(lg)), dim3(kLdsThreads), lb, st, a, t, lg);
+        });
+        return hipGetLastError();
+    }
+    // the bf16 decoder moves predictor and output rows 8 bytes per lane
+    const bool aligned8 = (reinterpret_cast<uintptr_t>(a.aux) | reinterpret_cast<uintptr_t>(a.out)) % 8 == 0;
+    if (DT == SKV_BF16 && MODE == SKV_RESIDUAL && !g_force_v1 && v == 0 && aligned8 && dec_bf16_lds() <= kLdsLimit) {
+        const LdsGeo lg = lds_geometry(a.shape);
+        hipError_t e = allow_lds(decode_bf16, dec_bf16_lds());
+        if (e != hipSuccess) return e;
+        timed("decode_streams", st, [&] {
+            hipLaunchKernelGGL(decode_bf16, dim3(lds_grid(lg)), dim3(kLdsThreads), dec_bf16_lds(), st, a, t, lg);
         });
         return hipGetLastError();
     }
