@@ -159,6 +159,26 @@ def test_edge_inputs_e4m3(skv, orc, kind, channels):
     full_compare(skv, orc, t, p, tabs, oshape, f"edge e4m3 {kind} {channels}")
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "e4m3"])
+def test_word_bursts_after_escapes(skv, orc, dtype):
+    """Every token block escapes in its first 4 steps and codes rare direct
+    symbols (about 12 bits each) in the next 8, then repeats the predictor:
+    the tiles after the escapes need more words than the decoder's ring holds,
+    so they are decoded again from memory while the escapes of the tile before
+    are being resolved.  The streams stay coded (not raw)."""
+    cfg = gen.Config(93, f"burst-{dtype}", dtype, 1, 2, 512, 96)
+    t, p, tabs, oshape = residual_case(skv, orc, cfg)
+    step = (torch.arange(p.shape[2], device="cuda") % 128)[None, None, :, None]
+    if dtype == "e4m3":
+        far, rare, mask = 40, 20, 0xFF
+    else:
+        far, rare, mask = 300, 100, 0xFFFF
+    pi = p.to(torch.int32)
+    t = torch.where(step < 4, pi + far, torch.where(step < 12, pi + rare, pi)) & mask
+    t = t.to(torch.uint8) if dtype == "e4m3" else t.to(torch.int16)
+    full_compare(skv, orc, t, p, tabs, oshape, f"word bursts {dtype}")
+
+
 def test_corruption_and_wrong_tables(skv, orc):
     cfg = gen.Config(92, "corrupt-bf16", "bf16", 1, 2, 256, 64)
     t, p, tabs, oshape = residual_case(skv, orc, cfg)
