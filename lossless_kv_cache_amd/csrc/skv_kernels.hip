@@ -1348,6 +1348,201 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8))) void 
     }
 }
 
+// --------------------------------------------------------------- tiled bf16 encode
+// The tiled encoder for 16-bit elements: one channel group per workgroup, the
+// two half-waves of a wavefront on two token blocks, 8-step tiles.  A lane
+// loads 16 bytes of target and of predictor (8 channels of one token), forms
+// the 8 zigzag symbols with 16-bit packed arithmetic (order-preserving flips,
+// difference mod 2^16, zigzag) and stores them in the wavefront's LDS tile;
+// each lane then reads its own channel's symbols for the tile's 8 steps.
+// Emitted words go to a 128-word LDS ring per stream that stores each
+// completed 64-word chunk at once; escaped values (16 bits) are stored per
+// tile.  The tables of 256 symbols take 128 KB, so one workgroup runs per CU.
+constexpr uint32_t kBfTileLds = 2 * kTileSteps * kLanes * 2;            // symbols of both halves
+constexpr uint32_t kBfEncWaveLds = kBfTileLds + 2 * kPairRing * 2;
+__host__ __device__ constexpr uint32_t encode_bf16_lds(uint32_t fs) { return kLanes * fs * 16 + 16 * kBfEncWaveLds; }
+
+// v ^ 0x7FFF in each 16-bit half whose sign bit is set (the order-preserving
+// code of a bf16 pattern is this flip ^ 0x8000); v_perm selectors 8 and 9
+// spread the signs of bytes 1 and 3 over their halves
+__device__ __forceinline__ uint32_t sflip16x2(uint32_t v) {
+    return v ^ (__builtin_amdgcn_perm(v, v, 0x09090808u) & 0x7FFF7FFFu);
+}
+// zigzag symbols of two 16-bit residuals r (two's complement halves): 2r, or -2r - 1 when negative
+__device__ __forceinline__ uint32_t zig16x2(uint32_t r) {
+    typedef unsigned short us2 __attribute__((ext_vector_type(2)));
+    const us2 d = __builtin_bit_cast(us2, r) << us2{1, 1};
+    return __builtin_bit_cast(uint32_t, d) ^ __builtin_amdgcn_perm(r, r, 0x09090808u);
+}
+// zigzag symbols of target - predictor for two bf16 patterns each
+__device__ __forceinline__ uint32_t sym16x2(uint32_t t, uint32_t p) {
+    typedef unsigned short us2 __attribute__((ext_vector_type(2)));
+    const us2 d = __builtin_bit_cast(us2, sflip16x2(t)) - __builtin_bit_cast(us2, sflip16x2(p));
+    return zig16x2(__builtin_bit_cast(uint32_t, d));
+}
+
+__global__ __launch_bounds__(1024) void encode_bf16(EncodeLaunch a, DevTables t, uint32_t fs, LdsGeo lg) {
+    constexpr uint32_t RAW = 2 * kSyms;
+    constexpr uint32_t MAXE = (RAW - kStreamHead) / 2;
+    constexpr uint32_t kDrop = 0x80000000u;               // buffer offset past the range: the access is dropped
+    constexpr uint32_t kChunks = RAW / 128;                // 64-word chunks that fit the words region
+    extern __shared__ __align__(16) uint8_t lds[];
+    const Geo geo = geometry(a.shape);
+    const LdsPos ps = lds_position(geo, lg);
+    if (!ps.valid) return;
+    const uint32_t tab0 = ps.slab * geo.C + ps.cg * kLanes;
+    uint4* lenc = reinterpret_cast<uint4*>(lds);                            // [fs symbols][32 lanes]
+    for (uint32_t i = threadIdx.x; i < kLanes * fs; i += blockDim.x) {
+        const uint32_t sym = i / kLanes, j = i % kLanes;
+        lenc[i] = t.enc[size_t(tab0 + j) * 256 + sym];
+    }
+    __syncthreads();
+
+    const uint32_t wave = threadIdx.x >> 6, nwave = blockDim.x >> 6;
+    const uint32_t hl = threadIdx.x & 31u;
+    const bool upper = (threadIdx.x & 32u) != 0;
+    const uint32_t fsh = upper ? 16u : 0u;
+    const uint32_t lane = 31u - hl;                        // format lane (reversed within the half)
+    const uint32_t n = t.n[tab0 + lane];
+    uint8_t* tile = lds + size_t(kLanes) * fs * 16 + wave * kBfEncWaveLds;
+    uint8_t* ring = tile + kBfTileLds;
+    // tile: [half][step][32 channels] u16; this lane loads 8 channels of one step and reads its channel back
+    const uint32_t ld_row = hl >> 2, ld_q = hl & 3u;
+    constexpr uint32_t kHalfTile = kTileSteps * kLanes * 2;
+    uint4* tile_st = reinterpret_cast<uint4*>(tile + (upper ? kHalfTile : 0u) + ld_row * kLanes * 2 + ld_q * 16);
+    const uint16_t* tile_rd = reinterpret_cast<const uint16_t*>(tile + (upper ? kHalfTile : 0u)) + lane;
+    uint16_t* ring_h = reinterpret_cast<uint16_t*>(ring + (upper ? kPairRing * 2 : 0u));
+    const uint32_t* ring32 = reinterpret_cast<const uint32_t*>(ring_h);
+
+    const uint32_t rowb = geo.C * 2;
+    const size_t slab_b = size_t(ps.slab) * geo.T * rowb + size_t(ps.cg) * kLanes * 2;
+    const uint8_t* tgt = static_cast<const uint8_t*>(a.target) + slab_b + ld_q * 16;
+    const uint8_t* aux = static_cast<const uint8_t*>(a.aux) + slab_b + ld_q * 16;
+    const uint64_t sid0 = (uint64_t(ps.slab) * geo.ntb + ps.tb_begin) * geo.ncg + ps.cg;
+    uint8_t* wgs = a.scratch + sid0 * (2 * RAW);
+    const uint32_t sstride = geo.ncg * (2 * RAW);
+    const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
+        wgs, (short)0, int((ps.tb_end - ps.tb_begin - 1) * sstride + 2 * RAW), 0x00020000);
+
+    // symbols of one tile: 8 per lane into LDS, then each lane's channel for the tile's 8 steps
+    auto stage = [&](uint4 tv, uint4 pv, uint32_t* z) {
+        *tile_st = make_uint4(sym16x2(tv.x, pv.x), sym16x2(tv.y, pv.y), sym16x2(tv.z, pv.z), sym16x2(tv.w, pv.w));
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (uint32_t r = 0; r < kTileSteps; ++r) z[r] = tile_rd[r * kLanes];
+        __builtin_amdgcn_wave_barrier();
+    };
+
+    for (uint32_t r0 = ps.tb_begin + 2 * wave; r0 < ps.tb_end; r0 += 2 * nwave) {
+        const uint32_t tb = r0 + (upper ? 1u : 0u);
+        const bool act = tb < ps.tb_end;
+        const uint32_t tbs = act ? tb : r0;
+        const uint32_t ao = (tbs - ps.tb_begin) * sstride;
+        const uint32_t ebase = ao + kStreamHead - (upper ? 64u : 0u);   // upper-half slots carry a bias of 32 values
+        const uint32_t wreg = ao + RAW;
+        const uint8_t* tsrc = tgt + size_t(tbs * kSteps + ld_row) * rowb;
+        const uint8_t* psrc = aux + size_t(tbs * kSteps + ld_row) * rowb;
+        const size_t tstride = size_t(kTileSteps) * rowb;
+        constexpr int kTiles = kSteps / kTileSteps;
+
+        uint32_t zc[kTileSteps], zn[kTileSteps];
+        uint4 tv = *reinterpret_cast<const uint4*>(tsrc + (kTiles - 1) * tstride);
+        uint4 pv = *reinterpret_cast<const uint4*>(psrc + (kTiles - 1) * tstride);
+        stage(tv, pv, zc);
+        tv = *reinterpret_cast<const uint4*>(tsrc + (kTiles - 2) * tstride);
+        pv = *reinterpret_cast<const uint4*>(psrc + (kTiles - 2) * tstride);
+
+        uint32_t x = kStateLow;
+        uint32_t wp = 0;                                   // word counts: lower half | upper half << 16
+        uint32_t elo = 0, ehi = 0;                         // escape counts per half
+        uint4 ec = lenc[min(zc[kTileSteps - 1], n) * kLanes + lane];
+        for (int j = kTiles - 1; j >= 0; --j) {
+            if (j > 0) {
+                stage(tv, pv, zn);
+                if (j > 1) {
+                    tv = *reinterpret_cast<const uint4*>(tsrc + size_t(j - 2) * tstride);
+                    pv = *reinterpret_cast<const uint4*>(psrc + size_t(j - 2) * tstride);
+                }
+            }
+#pragma unroll
+            for (int r = kTileSteps - 1; r >= 0; --r) {
+                const uint4 e = ec;
+                const uint32_t znext = r > 0 ? zc[r - 1] : zn[kTileSteps - 1];
+                ec = lenc[min(znext, n) * kLanes + lane];
+                // words leave before the state absorbs the symbol (an idle half runs a copy of its
+                // partner's stream into its own ring and stores nothing)
+                uint32_t xs = x;
+                const bool emit = xs >= e.x;
+                const uint64_t mw = __ballot(emit);
+                const uint32_t mlo = uint32_t(mw), mhi = uint32_t(mw >> 32);
+                const uint32_t pp = __popc(mlo) | (__popc(mhi) << 16);
+                // ring slot: this half's count mod 128 plus the emitting lanes below (mbcnt_lo counts the
+                // entire lower half for an upper lane, which the packed base subtracts again)
+                const uint32_t pk = (wp - (pp << 16)) & 0x007F007Fu;
+                const uint32_t slot =
+                    __builtin_amdgcn_mbcnt_hi(mhi, __builtin_amdgcn_mbcnt_lo(mlo, __builtin_amdgcn_ubfe(pk, fsh, 16)));
+                if (emit) ring_h[slot & (kPairRing - 1)] = uint16_t(xs & 0xFFFFu);
+                xs = emit ? xs >> 16 : xs;
+                const uint32_t qt = __umulhi(xs + (e.z >> 24), e.y) >> (e.w & 31u);   // floor(xs / f)
+                // x = xs + qt (4096 - f) + start, the start taken from the high half of e.w
+                const uint32_t xq = __umul24(qt, e.z) + xs;
+                asm("v_add_u32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:WORD_1"
+                    : "=v"(x) : "v"(xq), "v"(e.w));
+                // a completed 64-word chunk leaves the ring (at most one per step and stream)
+                const uint32_t cross = ((wp & 0x003F003Fu) + pp) & 0x00400040u;
+                if (cross) {
+                    __builtin_amdgcn_wave_barrier();
+                    const uint32_t ck = __builtin_amdgcn_ubfe(wp >> 6, fsh, 10);
+                    const uint32_t w = ring32[(ck & 1u) * 32 + hl];
+                    const bool mine = act && __builtin_amdgcn_ubfe(cross, fsh + 6, 1) != 0;
+                    __builtin_amdgcn_raw_buffer_store_b32(
+                        w, wrs, mine && ck < kChunks ? wreg + ck * 128 + 4 * hl : kDrop, 0, 0);
+                    __builtin_amdgcn_wave_barrier();
+                }
+                wp += pp;
+            }
+            // escaped values of this tile, in emission order (rare: skipped by the whole wavefront)
+            uint32_t zm = zc[0];
+#pragma unroll
+            for (uint32_t r = 1; r < kTileSteps; ++r) zm = max(zm, zc[r]);
+            if (__ballot(zm >= n) != 0) {
+#pragma unroll
+                for (int r = kTileSteps - 1; r >= 0; --r) {
+                    const bool esc = zc[r] >= n;
+                    const uint64_t me = __ballot(esc);
+                    if (me == 0) continue;
+                    const uint32_t mlo = uint32_t(me), mhi = uint32_t(me >> 32), plo = __popc(mlo);
+                    const uint32_t pk = min(elo, MAXE) | ((min(ehi, MAXE) + 32u - plo) << 16);
+                    const uint32_t slot = __builtin_amdgcn_mbcnt_hi(
+                        mhi, __builtin_amdgcn_mbcnt_lo(mlo, __builtin_amdgcn_ubfe(pk, fsh, 16)));
+                    __builtin_amdgcn_raw_buffer_store_b16(uint16_t(zc[r]), wrs, act && esc ? ebase + 2 * slot : kDrop,
+                                                          0, 0);
+                    elo += plo;
+                    ehi += __popc(mhi);
+                }
+            }
+#pragma unroll
+            for (uint32_t r = 0; r < kTileSteps; ++r) zc[r] = zn[r];
+        }
+        // the partial last chunk, the final states and the stream's counts
+        __builtin_amdgcn_wave_barrier();
+        const uint32_t cnt = __builtin_amdgcn_ubfe(wp, fsh, 16), ecnt = upper ? ehi : elo;
+        const uint32_t ck = cnt >> 6;
+        const uint32_t w = ring32[(ck & 1u) * 32 + hl];
+        __builtin_amdgcn_raw_buffer_store_b32(
+            w, wrs, act && ck < kChunks && 2 * hl < (cnt & 63u) ? wreg + ck * 128 + 4 * hl : kDrop, 0, 0);
+        __builtin_amdgcn_wave_barrier();
+        if (act) {
+            reinterpret_cast<uint32_t*>(wgs + ao)[lane] = x;
+            if (hl == 0) {
+                const uint64_t sid = sid0 + uint64_t(tb - ps.tb_begin) * geo.ncg;
+                const uint32_t bytes = (kStreamHead + 2 * cnt + 2 * ecnt + 3) & ~3u;
+                a.meta[sid] = bytes >= RAW ? 0x80000000u : (cnt | (ecnt << 14));
+            }
+        }
+    }
+}
+
 // --------------------------------------------------------------- tiled e4m3 decode
 // One workgroup owns the 32 tables of a channel group: the complete
 // slot -> symbol maps (4096 bytes per table) and per symbol the 16-bit
@@ -1852,12 +2047,6 @@ __device__ __forceinline__ void st8(uint2 v, __amdgpu_buffer_rsrc_t r, uint32_t 
     const v2u w = {v.x, v.y};
     __builtin_amdgcn_raw_buffer_store_b64(w, r, off, soff, 0);
 }
-// v ^ 0x7FFF in each 16-bit half whose sign bit is set (the order-preserving
-// code of a bf16 pattern is this flip ^ 0x8000); v_perm selectors 8 and 9
-// spread the signs of bytes 1 and 3 over their halves
-__device__ __forceinline__ uint32_t sflip16x2(uint32_t v) {
-    return v ^ (__builtin_amdgcn_perm(v, v, 0x09090808u) & 0x7FFF7FFFu);
-}
 // targets of two predictor values and two zigzag symbols: ord(t) = ord(p) + r
 // mod 2^16 is flip(t) = flip(p) + r mod 2^16
 __device__ __forceinline__ uint32_t recon16x2(uint32_t p, uint32_t z) {
@@ -2333,7 +2522,17 @@ hipError_t encode_all(const EncodeLaunch& a, const DevTables& t, hipStream_t st)
     const size_t lt = size_t(kLanes) * fc_stride(t) * 16 + (kLdsThreads / 64) * kTileWaveLds;
     const bool aligned = (reinterpret_cast<uintptr_t>(a.target) | reinterpret_cast<uintptr_t>(a.aux)) % 8 == 0;
     const uint32_t ncg = a.shape.channels / kLanes;
-    if (DT == SKV_E4M3 && MODE == SKV_RESIDUAL && ncg % 4 == 0 && 2 * encode_pairs_lds(fc_stride(t)) + 512 <= kLdsLimit &&
+    const bool aligned16 = (reinterpret_cast<uintptr_t>(a.target) | reinterpret_cast<uintptr_t>(a.aux)) % 16 == 0;
+    if (DT == SKV_BF16 && MODE == SKV_RESIDUAL && aligned16 && encode_bf16_lds(fc_stride(t)) <= kLdsLimit &&
+        !g_force_v1 && variant().enc == 0) {
+        const LdsGeo lg = lds_geometry(a.shape);
+        const size_t lp = encode_bf16_lds(fc_stride(t));
+        hipError_t e = allow_lds(encode_bf16, lp);
+        if (e != hipSuccess) return e;
+        timed("encode_streams", st, [&] {
+            hipLaunchKernelGGL(encode_bf16, dim3(lds_grid(lg)), dim3(kLdsThreads), lp, st, a, t, fc_stride(t), lg);
+        });
+    } else if (DT == SKV_E4M3 && MODE == SKV_RESIDUAL && ncg % 4 == 0 && 2 * encode_pairs_lds(fc_stride(t)) + 512 <= kLdsLimit &&
         aligned && !g_force_v1 && variant().enc == 0) {
         const LdsGeo lg = lds_geometry(a.shape, 2);
         const size_t lp = encode_pairs_lds(fc_stride(t));
