@@ -144,9 +144,9 @@ def main() -> int:
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
         with open(TRAFFIC_FILE) as f:
-            tr = json.load(f)
-        ent = tr.get(dom)
-        if ent and ent.get("kernel_sha") == kernel_sha() and ent.get("workload") == cfg.name:
+            tr = json.load(f)                                   # {workload: {kernel: counters}}
+        ent = tr.get(cfg.name, {}).get(dom)
+        if ent and ent.get("kernel_sha") == kernel_sha():
             traffic = ent["bytes_per_launch"]
     roofline = {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
