@@ -179,6 +179,33 @@ def test_word_bursts_after_escapes(skv, orc, dtype):
     full_compare(skv, orc, t, p, tabs, oshape, f"word bursts {dtype}")
 
 
+def _offset_copy(x: torch.Tensor, k: int) -> torch.Tensor:
+    """A contiguous copy of x whose data starts k elements into a larger buffer."""
+    buf = torch.zeros(x.numel() + k, dtype=x.dtype, device=x.device)
+    v = buf[k:k + x.numel()].view(x.shape)
+    v.copy_(x)
+    return v
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "e4m3"])
+def test_unaligned_buffers(skv, orc, dtype):
+    """Target, predictor and output that are not 16-byte aligned take the
+    per-step kernels (the tiled ones move 8- and 16-byte pieces); their
+    containers and reconstructions are the same."""
+    cfg = gen.Config(94, f"unaligned-{dtype}", dtype, 1, 2, 384, 128)
+    t, p, tabs, oshape = residual_case(skv, orc, cfg)
+    tu, pu = _offset_copy(t, 1), _offset_copy(p, 3)
+    assert tu.data_ptr() % 8 != 0 and pu.data_ptr() % 8 != 0
+    say(f"[parity] unaligned {dtype}: encode on GPU")
+    cont = skv.encode(tabs, tu, pu)
+    torch.cuda.synchronize()
+    want = orc.encode(tabs.bytes(), oshape, t.cpu().numpy(), p.cpu().numpy(), threads=8)
+    assert cont.cpu().numpy().tobytes() == want
+    out = _offset_copy(torch.zeros_like(t), 1)
+    skv.decode_into(tabs, cont, pu, out)
+    assert torch.equal(out, t)
+
+
 def test_corruption_and_wrong_tables(skv, orc):
     cfg = gen.Config(92, "corrupt-bf16", "bf16", 1, 2, 256, 64)
     t, p, tabs, oshape = residual_case(skv, orc, cfg)
