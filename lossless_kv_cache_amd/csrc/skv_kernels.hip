@@ -91,8 +91,14 @@ __global__ __launch_bounds__(256) void expand_tables(const uint8_t* rec, uint32_
     // 2^l and down otherwise (then inc = 1); one of the two always holds
     // (Robison, "N-bit unsigned division via N-bit multiply-add").  Powers of
     // two shift, and f = 1 uses m = 2^32 - 1 with inc = 1.
+    // entries past n repeat the escape symbol's entry; escape entries carry bit 8 of w
+    // (a kernel may then look a symbol up by min(z, 255) without reading n)
+    const uint32_t se = min(tid, n);
+    const uint32_t fe = uint32_t(r[2 + 2 * se]) | (uint32_t(r[3 + 2 * se]) << 8);
+    const uint32_t ce = cum[se];
     uint4 e = make_uint4(0u, 0u, 0u, 0u);
-    if (tid <= n && f > 0) {
+    if (fe > 0) {
+        const uint32_t f = fe, c = ce;
         uint32_t m, inc = 0, l = 0;
         if ((f & (f - 1)) == 0) {
             while ((1u << (l + 1)) <= f) ++l;                   // f = 2^l
@@ -117,7 +123,7 @@ __global__ __launch_bounds__(256) void expand_tables(const uint8_t* rec, uint32_
         e.x = f << 20;
         e.y = m;
         e.z = (kM - f) | (inc << 24);
-        e.w = l | (c << 16);
+        e.w = l | (c << 16) | (tid >= n ? 0x100u : 0u);
     }
     enc[size_t(j) * 256 + tid] = e;
     fc[size_t(j) * 256 + tid] = f | (c << 16);
@@ -216,6 +222,116 @@ __global__ __launch_bounds__(256) void encode_streams(EncodeLaunch a, DevTables 
     reinterpret_cast<uint32_t*>(area)[lane] = x;
     if (lane == 0) {
         const uint32_t bytes = (kStreamHead + 2 * cnt + EB * ecnt + 3) & ~3u;
+        a.meta[sid] = bytes >= RAW ? 0x80000000u : (cnt | (ecnt << 14));
+    }
+}
+
+// Checkerboard encoder with the table reads taken off the state chain.  The
+// 32,768 tables (16 shifted tables per component) stay in device memory, so
+// every step reads a table entry from the L2; none of those reads depends on
+// the rANS state.  Each lane runs a software pipeline over the steps (which
+// go from 127 down to 0): a step's coefficient, side input and neighbours are
+// loaded 6 steps before the step is coded, its table entry 4 steps before
+// (one read: entries past a table's direct range repeat its escape entry,
+// flagged), its escaped value stored 2 steps before.  The state update then
+// waits on nothing but its own arithmetic.  Output order and format are those
+// of encode_streams.
+// kCbLag: steps between pipeline stages; P: register ring period (steps)
+template <int kCbLag, int P>
+__global__ __launch_bounds__(256) void encode_cb(EncodeLaunch a, DevTables t) {
+    constexpr uint32_t RAW = 2 * kSyms;
+    constexpr uint32_t MAXW = (RAW - kStreamHead) / 2;     // more words or escapes mean a raw stream
+    constexpr uint32_t MAXE = (RAW - kStreamHead) / 2;
+    const uint32_t tid = threadIdx.x;
+    const uint64_t sid = uint64_t(blockIdx.x) * kStreamsPerBlock + (tid >> 5);
+    if (sid >= a.n_streams) return;
+    const uint32_t lane = tid & 31u, half = tid & 32u;
+    const Geo g = geometry(a.shape);
+    const uint32_t cg = uint32_t(sid % g.ncg);
+    const uint32_t tb = uint32_t((sid / g.ncg) % g.ntb);
+    const uint32_t pass = uint32_t(sid / (uint64_t(g.ncg) * g.ntb));
+    const uint32_t ch = cg * kLanes + lane;
+    uint8_t* area = a.scratch + sid * (2 * RAW);
+    uint16_t* wfwd = reinterpret_cast<uint16_t*>(area + RAW);           // words, emission order
+    uint16_t* efwd = reinterpret_cast<uint16_t*>(area + kStreamHead);   // escaped values, emission order
+    const int16_t* coef = static_cast<const int16_t*>(a.target);
+    const int16_t* Gp = static_cast<const int16_t*>(a.aux);
+    const size_t C = g.C;
+
+    int32_t ic[P], ig[P], il[P], ir[P];                    // stage 1: raw inputs
+    uint32_t zz[P];                                        // stage 2: symbol
+    uint4 ee[P];                                           // stage 2: table entry
+    uint32_t x = kStateLow, cnt = 0, ecnt = 0;
+    constexpr int kIters = kSteps + 3 * kCbLag;
+    static_assert(P >= 3 * kCbLag + 1, "ring period covers the pipeline");
+    for (int it0 = 0; it0 < kIters; it0 += P) {
+#pragma unroll
+        for (int d = 0; d < P; ++d) {
+            const int it = it0 + d;
+            // stage 1: loads of step 127 - it
+            {
+                const int k = kSteps - 1 - it;
+                constexpr int slot_base = 0;
+                (void)slot_base;
+                const int sl = (kSteps - 1 - d + 8 * P) % P;      // (127 - it) mod P with it0 a multiple of P
+                if (k >= 0) {
+                    const uint32_t tok = 2u * (tb * kSteps + uint32_t(k)) + pass;
+                    const size_t r = size_t(tok) * C + ch;
+                    ic[sl] = coef[r];
+                    ig[sl] = Gp[r];
+                    if (pass) {
+                        il[sl] = coef[r - C];
+                        ir[sl] = tok + 1 < g.T ? int32_t(coef[r + C]) : int32_t(coef[r - C]);
+                    }
+                }
+            }
+            // stage 2: table, symbol and direct count of step 127 - (it - lag)
+            {
+                const int k = kSteps - 1 - (it - kCbLag);
+                const int sl = (kSteps - 1 - d + kCbLag + 8 * P) % P;
+                if (k >= 0 && k < kSteps) {
+                    int32_t mu = ig[sl];
+                    if (pass) mu += 8 * (il[sl] + ir[sl]);
+                    const int32_t kk = mu >> 4;
+                    const uint32_t table = ch * 16u + uint32_t(mu & 15);
+                    zz[sl] = zig16(uint32_t(ic[sl] - kk) & 0xFFFFu);
+                    // entries past the table's n repeat its escape entry, flagged in bit 8 of w
+                    ee[sl] = t.enc[size_t(table) * 256 + min(zz[sl], 255u)];
+                }
+            }
+            // stage 3: escapes of step 127 - (it - 2 lag), in step order
+            {
+                const int k = kSteps - 1 - (it - 2 * kCbLag);
+                const int sl = (kSteps - 1 - d + 2 * kCbLag + 8 * P) % P;
+                if (k >= 0 && k < kSteps) {
+                    const uint32_t z = zz[sl];
+                    const bool esc = (ee[sl].w & 0x100u) != 0;
+                    // escaped values keep decode order: ranked like the words, written backwards
+                    const uint64_t b = __ballot(esc);
+                    const uint32_t mine = uint32_t(b >> half);
+                    if (esc) {
+                        const uint32_t pos = ecnt + __popc(uint32_t(uint64_t(mine) >> (lane + 1)));
+                        if (pos < MAXE) efwd[pos] = uint16_t(z);
+                    }
+                    ecnt += __popc(mine);
+                }
+            }
+            // stage 4: the state update of step 127 - (it - 3 lag)
+            {
+                const int k = kSteps - 1 - (it - 3 * kCbLag);
+                const int sl = (kSteps - 1 - d + 3 * kCbLag + 8 * P) % P;
+                if (k >= 0 && k < kSteps) {
+                    const uint4 e = ee[sl];
+                    emit_words(x, cnt, x >= e.x, lane, half, wfwd, MAXW);
+                    const uint32_t qt = __umulhi(x + (e.z >> 24), e.y) >> (e.w & 31u);    // floor(x / f)
+                    x = x + (e.w >> 16) + __umul24(qt, e.z);
+                }
+            }
+        }
+    }
+    reinterpret_cast<uint32_t*>(area)[lane] = x;
+    if (lane == 0) {
+        const uint32_t bytes = (kStreamHead + 2 * cnt + 2 * ecnt + 3) & ~3u;
         a.meta[sid] = bytes >= RAW ? 0x80000000u : (cnt | (ecnt << 14));
     }
 }
@@ -2564,6 +2680,11 @@ hipError_t encode_all(const EncodeLaunch& a, const DevTables& t, hipStream_t st)
         if (e != hipSuccess) return e;
         timed("encode_streams", st, [&] {
             hipLaunchKernelGGL(k, dim3(lds_grid(lg)), dim3(kLdsThreads), lb, st, a, t, fc_stride(t), lg);
+        });
+    } else if (MODE == SKV_CHECKERBOARD && !g_force_v1 && variant().enc == 0) {
+        // two steps between stages: longer lags measured no faster (more registers, fewer waves)
+        timed("encode_streams", st, [&] {
+            hipLaunchKernelGGL((encode_cb<2, 8>), dim3(eg), dim3(256), 0, st, a, t);
         });
     } else {
         timed("encode_streams", st, [&] {
