@@ -57,6 +57,7 @@ struct DevTables {
     uint4* enc = nullptr;          // [n_tables][256] {freq<<20, divisor magic, 4096-freq, cum<<16 | shift}
     uint32_t* fc = nullptr;        // [n_tables][256] freq | cum<<16
     uint8_t* slot = nullptr;       // [n_tables][4096] slot -> symbol
+    uint8_t* half = nullptr;       // checkerboard blobs: [n_tables][2048] symbol of every even slot
 };
 
 struct EncodeLaunch {

@@ -67,7 +67,7 @@ __device__ __forceinline__ uint32_t unzig(uint32_t z) { return (z >> 1) ^ (0u - 
 
 // --------------------------------------------------------------- tables
 __global__ __launch_bounds__(256) void expand_tables(const uint8_t* rec, uint32_t* tn, uint4* enc, uint32_t* fc,
-                                                     uint8_t* slot) {
+                                                     uint8_t* slot, uint8_t* half) {
     __shared__ uint32_t cum[257];
     const uint32_t j = blockIdx.x, tid = threadIdx.x;
     const uint8_t* r = rec + size_t(j) * kTableRecord;
@@ -129,6 +129,10 @@ __global__ __launch_bounds__(256) void expand_tables(const uint8_t* rec, uint32_
     fc[size_t(j) * 256 + tid] = f | (c << 16);
     uint8_t* st = slot + size_t(j) * kM;
     for (uint32_t q = c; q < c + f; ++q) st[q] = uint8_t(tid);
+    if (half) {
+        uint8_t* sh = half + size_t(j) * (kM / 2);
+        for (uint32_t q = (c + 1) & ~1u; q < c + f; q += 2) sh[q / 2] = uint8_t(tid);
+    }
 }
 
 // --------------------------------------------------------------- encode
@@ -226,6 +230,23 @@ __global__ __launch_bounds__(256) void encode_streams(EncodeLaunch a, DevTables 
     }
 }
 
+// Stream of this half-wave in the checkerboard kernels: a block codes 8
+// token blocks of one channel group, and the blocks dispatched to one XCD
+// (round-robin over the 8 XCDs) sweep one channel group after another, so the
+// tables an XCD reads at a time (16 per component) stay in its L2.  Returns
+// false for a half-wave past the pass's last token block.
+__device__ __forceinline__ bool cb_stream(const Geo& g, uint64_t first, uint64_t& sid) {
+    const uint32_t bpc = (g.ntb + 7) / 8;                  // blocks per channel group
+    const uint32_t total = g.ncg * bpc;
+    const uint32_t b = blockIdx.x;
+    const uint32_t w = total % 8 == 0 ? (b % 8) * (total / 8) + b / 8 : b;
+    const uint32_t cg = w / bpc, tb = (w % bpc) * 8 + (threadIdx.x >> 5);
+    if (cg >= g.ncg || tb >= g.ntb) return false;
+    const uint64_t pass = first / (uint64_t(g.ncg) * g.ntb);
+    sid = (pass * g.ntb + tb) * g.ncg + cg;
+    return true;
+}
+
 // Checkerboard encoder with the table reads taken off the state chain.  The
 // 32,768 tables (16 shifted tables per component) stay in device memory, so
 // every step reads a table entry from the L2; none of those reads depends on
@@ -243,13 +264,14 @@ __global__ __launch_bounds__(256) void encode_cb(EncodeLaunch a, DevTables t) {
     constexpr uint32_t MAXW = (RAW - kStreamHead) / 2;     // more words or escapes mean a raw stream
     constexpr uint32_t MAXE = (RAW - kStreamHead) / 2;
     const uint32_t tid = threadIdx.x;
-    const uint64_t sid = uint64_t(blockIdx.x) * kStreamsPerBlock + (tid >> 5);
-    if (sid >= a.n_streams) return;
-    const uint32_t lane = tid & 31u, half = tid & 32u;
     const Geo g = geometry(a.shape);
+    const uint64_t per = uint64_t(g.ncg) * g.ntb;            // streams per pass
+    uint64_t sid;
+    if (!cb_stream(g, uint64_t(blockIdx.y) * per, sid)) return;
+    const uint32_t lane = tid & 31u, half = tid & 32u;
     const uint32_t cg = uint32_t(sid % g.ncg);
     const uint32_t tb = uint32_t((sid / g.ncg) % g.ntb);
-    const uint32_t pass = uint32_t(sid / (uint64_t(g.ncg) * g.ntb));
+    const uint32_t pass = uint32_t(sid / per);
     const uint32_t ch = cg * kLanes + lane;
     uint8_t* area = a.scratch + sid * (2 * RAW);
     uint16_t* wfwd = reinterpret_cast<uint16_t*>(area + RAW);           // words, emission order
@@ -654,6 +676,167 @@ __global__ __launch_bounds__(256) void decode_streams(DecodeLaunch a, DevTables 
     }
     if (x != kStateLow || p != nw) bad = true;
     const uint32_t used = kStreamHead + 2 * nw + EB * ep;
+    if (((used + 3) & ~3u) != size) bad = true;
+    else if (lane < size - used && sp[used + lane] != 0) bad = true;   // zero pad
+    if (bad) atomicOr(a.status, 1u);
+}
+
+// Checkerboard decoder with everything but the table lookups taken off the
+// state chain.  A step's side input and decoded neighbours (and from them its
+// table, mean and direct count) do not depend on the rANS state, so each lane
+// loads them 4 steps ahead and reads its table's direct count 2 steps ahead.
+// Words come from two 32-word windows of the stream held in registers (lane i
+// of a half holds word base + i and base + 32 + i); a refilling lane fetches
+// its word from the window lane with ds_bpermute, and a window that has been
+// used up is replaced by the next 32 words while the other one is consumed.
+// So a step waits on its slot-map byte and its (frequency, start) word, both
+// in device memory, and on nothing else.  Output and checks are those of
+// decode_streams.
+template <int kLag, int P>
+__global__ __launch_bounds__(256) void decode_cb(DecodeLaunch a, DevTables t, uint64_t first, uint64_t count) {
+    constexpr uint32_t RAW = 2 * kSyms;
+    const uint32_t tid = threadIdx.x;
+    const Geo g = geometry(a.shape);
+    uint64_t sid;
+    if (!cb_stream(g, first, sid)) return;
+    const uint32_t lane = tid & 31u, half = tid & 32u;
+    const uint32_t cg = uint32_t(sid % g.ncg);
+    const uint32_t tb = uint32_t((sid / g.ncg) % g.ntb);
+    const uint32_t pass = uint32_t(sid / (uint64_t(g.ncg) * g.ntb));
+    const uint32_t ch = cg * kLanes + lane;
+    const size_t C = g.C;
+    const uint64_t* index = reinterpret_cast<const uint64_t*>(a.in + kHeaderBytes);
+    const uint8_t* pay = a.in + kHeaderBytes + 8 * (a.n_streams + 1);
+    const uint64_t e0 = index[sid], e1 = index[sid + 1];
+    const uint64_t off = e0 & ~kRawBit, end = e1 & ~kRawBit;
+    int16_t* out = static_cast<int16_t*>(a.out);
+    const int16_t* Gp = static_cast<const int16_t*>(a.aux);
+    auto row_of = [&](uint32_t k) { return size_t(2u * (tb * kSteps + k) + pass) * C + ch; };
+    if (end < off || end > a.payload_bytes) {
+        if (lane == 0) atomicOr(a.status, 1u);
+        return;
+    }
+    const uint64_t size = end - off;
+    if (e0 & kRawBit) {
+        if (size != RAW) {
+            if (lane == 0) atomicOr(a.status, 1u);
+            return;
+        }
+        for (uint32_t k = 0; k < uint32_t(kSteps); ++k)
+            out[row_of(k)] = reinterpret_cast<const int16_t*>(pay + off)[k * kLanes + lane];
+        return;
+    }
+    const uint8_t* sp = pay + off;
+    if (size < kStreamHead || size % 4 != 0) {
+        if (lane == 0) atomicOr(a.status, 1u);
+        return;
+    }
+    const uint32_t nw = reinterpret_cast<const uint32_t*>(sp)[32];
+    if (nw > (size - kStreamHead) / 2) {
+        if (lane == 0) atomicOr(a.status, 1u);
+        return;
+    }
+    bool bad = false;
+    uint32_t x = reinterpret_cast<const uint32_t*>(sp)[lane];
+    if (x < kStateLow) bad = true;
+    const uint16_t* W = reinterpret_cast<const uint16_t*>(sp + kStreamHead);
+    const uint16_t* E = reinterpret_cast<const uint16_t*>(sp + kStreamHead + 2 * nw);
+    const uint32_t ecap = uint32_t((size - kStreamHead - 2 * nw) / 2);
+    // word windows: words past the stream's count read as 0 (a stream that needs them is corrupt)
+    auto word_at = [&](uint32_t i) -> uint32_t { return i < nw ? uint32_t(W[i]) : 0u; };
+    uint32_t base = 0, cur = word_at(lane), nxt = word_at(32 + lane);
+    uint32_t p = 0, ep = 0;
+    const uint32_t below = (1u << lane) - 1u;
+
+    int32_t ig[P], il[P], ir[P];                           // stage 1: side input and neighbours
+    int32_t kk[P];                                         // stage 2: mean cell
+    uint32_t tab[P], nn[P];                                // stage 2: table and direct count
+    constexpr int kIters = kSteps + 2 * kLag;
+    static_assert(P >= 2 * kLag + 1 && P % 2 == 0, "ring period covers the pipeline");
+    for (int it0 = 0; it0 < kIters; it0 += P) {
+#pragma unroll
+        for (int d = 0; d < P; ++d) {
+            const int it = it0 + d;
+            // stage 1: loads of step it
+            {
+                const int k = it;
+                const int sl = d % P;
+                if (k < kSteps) {
+                    const size_t r = row_of(uint32_t(k));
+                    ig[sl] = Gp[r];
+                    if (pass) {
+                        const uint32_t tok = 2u * (tb * kSteps + uint32_t(k)) + 1u;
+                        il[sl] = out[r - C];
+                        ir[sl] = tok + 1 < g.T ? int32_t(out[r + C]) : int32_t(out[r - C]);
+                    }
+                }
+            }
+            // stage 2: table, mean cell and direct count of step it - lag
+            {
+                const int k = it - kLag;
+                const int sl = (d - kLag + P) % P;
+                if (k >= 0 && k < kSteps) {
+                    int32_t mu = ig[sl];
+                    if (pass) mu += 8 * (il[sl] + ir[sl]);
+                    kk[sl] = mu >> 4;
+                    tab[sl] = ch * 16u + uint32_t(mu & 15);
+                    nn[sl] = t.n[tab[sl]];
+                }
+            }
+            // stage 3: the step it - 2 lag
+            {
+                const int k = it - 2 * kLag;
+                const int sl = (d - 2 * kLag + 2 * P) % P;
+                if (k >= 0 && k < kSteps) {
+                    const uint32_t table = tab[sl], n = nn[sl];
+                    const uint32_t slot = x & (kM - 1u);
+                    // the even slot's symbol, then the rows of it and of the next symbol: the odd slot
+                    // belongs to the next one when that one starts there (never past the escape symbol)
+                    const uint32_t s0 = t.half[size_t(table) * (kM / 2) + (slot >> 1)];
+                    const uint32_t* fr = t.fc + size_t(table) * 256 + s0;
+                    const uint32_t f0 = fr[0], f1 = fr[s0 < n ? 1 : 0];
+                    const bool adv = s0 < n && slot >= (f1 >> 16);
+                    const uint32_t s = s0 + (adv ? 1u : 0u);
+                    const uint32_t fcv = adv ? f1 : f0;
+                    x = (fcv & 0xFFFFu) * (x >> kProbBits) + slot - (fcv >> 16);
+                    // refill in lane order from the word windows
+                    const bool need = x < kStateLow;
+                    const uint32_t mine = uint32_t(__ballot(need) >> half);
+                    const uint32_t idx = p + __popc(mine & below) - base;                 // < 64
+                    const int src = int(((idx & 31u) + half) << 2);
+                    const uint32_t wc = __builtin_amdgcn_ds_bpermute(src, int(cur));
+                    const uint32_t wn = __builtin_amdgcn_ds_bpermute(src, int(nxt));
+                    if (need) {
+                        if (p + __popc(mine & below) >= nw) bad = true;
+                        x = (x << 16) | (idx < 32 ? wc : wn);
+                    }
+                    p += __popc(mine);
+                    if (p - base >= 32) {
+                        // the first window is used up: the second moves in and the next 32 words load
+                        base += 32;
+                        cur = nxt;
+                        nxt = word_at(base + 32 + lane);
+                    }
+                    // escaped values, in lane order, from the escape region
+                    const bool esc = s == n;
+                    const uint32_t me = uint32_t(__ballot(esc) >> half);
+                    uint32_t z = s;
+                    if (esc) {
+                        const uint32_t pos = ep + __popc(me & below);
+                        uint32_t v = 0;
+                        if (pos < ecap) v = E[pos];
+                        else bad = true;
+                        if (v < n) bad = true;                 // a canonical encoder codes such a value directly
+                        z = v;
+                    }
+                    ep += __popc(me);
+                    out[row_of(uint32_t(k))] = int16_t(uint16_t(uint32_t(kk[sl]) + unzig(z)));
+                }
+            }
+        }
+    }
+    if (x != kStateLow || p != nw) bad = true;
+    const uint32_t used = kStreamHead + 2 * nw + 2 * ep;
     if (((used + 3) & ~3u) != size) bad = true;
     else if (lane < size - used && sp[used + lane] != 0) bad = true;   // zero pad
     if (bad) atomicOr(a.status, 1u);
@@ -2683,8 +2866,10 @@ hipError_t encode_all(const EncodeLaunch& a, const DevTables& t, hipStream_t st)
         });
     } else if (MODE == SKV_CHECKERBOARD && !g_force_v1 && variant().enc == 0) {
         // two steps between stages: longer lags measured no faster (more registers, fewer waves)
+        const Geo g{a.shape.channels, a.shape.tokens, a.shape.channels / kLanes, a.shape.tokens / 2 / kSteps};
+        const dim3 grid(g.ncg * ((g.ntb + 7) / 8), 2);       // y: pass
         timed("encode_streams", st, [&] {
-            hipLaunchKernelGGL((encode_cb<2, 8>), dim3(eg), dim3(256), 0, st, a, t);
+            hipLaunchKernelGGL((encode_cb<2, 8>), grid, dim3(256), 0, st, a, t);
         });
     } else {
         timed("encode_streams", st, [&] {
@@ -2758,7 +2943,11 @@ hipError_t decode_all(const DecodeLaunch& a, const DevTables& t, hipStream_t st)
     const uint32_t grid = uint32_t((per + kStreamsPerBlock - 1) / kStreamsPerBlock);
     for (uint64_t ps = 0; ps < passes; ++ps)
         timed("decode_streams", st, [&] {
-            hipLaunchKernelGGL((decode_streams<DT, MODE>), dim3(grid), dim3(256), 0, st, a, t, ps * per, per);
+            if (MODE == SKV_CHECKERBOARD && !g_force_v1 && v == 0)
+                hipLaunchKernelGGL((decode_cb<2, 8>), dim3(a.shape.channels / kLanes * ((per / (a.shape.channels / kLanes) + 7) / 8)),
+                                   dim3(256), 0, st, a, t, ps * per, per);
+            else
+                hipLaunchKernelGGL((decode_streams<DT, MODE>), dim3(grid), dim3(256), 0, st, a, t, ps * per, per);
         });
     return hipGetLastError();
 }
@@ -2779,9 +2968,10 @@ hipError_t build_dev_tables(const uint8_t* blob, DevTables* t, hipStream_t st) {
     if (e == hipSuccess) e = hipMalloc(&t->enc, size_t(nt) * 256 * sizeof(uint4));
     if (e == hipSuccess) e = hipMalloc(&t->fc, size_t(nt) * 256 * 4);
     if (e == hipSuccess) e = hipMalloc(&t->slot, size_t(nt) * kM);
+    if (e == hipSuccess && blob[7] == SKV_CHECKERBOARD) e = hipMalloc(&t->half, size_t(nt) * (kM / 2));
     if (e == hipSuccess) e = hipMemcpyAsync(rec, blob + kHeaderBytes, size_t(nt) * kTableRecord, hipMemcpyHostToDevice, st);
     if (e == hipSuccess) {
-        hipLaunchKernelGGL(expand_tables, dim3(nt), dim3(256), 0, st, rec, t->n, t->enc, t->fc, t->slot);
+        hipLaunchKernelGGL(expand_tables, dim3(nt), dim3(256), 0, st, rec, t->n, t->enc, t->fc, t->slot, t->half);
         e = hipGetLastError();
     }
     if (e == hipSuccess) e = hipStreamSynchronize(st);
@@ -2798,6 +2988,7 @@ void free_dev_tables(DevTables* t) {
     if (t->enc) (void)hipFree(t->enc);
     if (t->fc) (void)hipFree(t->fc);
     if (t->slot) (void)hipFree(t->slot);
+    if (t->half) (void)hipFree(t->half);
     *t = DevTables{};
 }
 
