@@ -126,7 +126,8 @@ __global__ __launch_bounds__(256) void expand_tables(const uint8_t* rec, uint32_
         e.w = l | (c << 16) | (tid >= n ? 0x100u : 0u);
     }
     enc[size_t(j) * 256 + tid] = e;
-    fc[size_t(j) * 256 + tid] = f | (c << 16);
+    // checkerboard tables (the ones with half maps) flag their escape symbol in bit 15 (f < 4096)
+    fc[size_t(j) * 256 + tid] = f | (c << 16) | (half && tid == n ? 0x8000u : 0u);
     uint8_t* st = slot + size_t(j) * kM;
     for (uint32_t q = c; q < c + f; ++q) st[q] = uint8_t(tid);
     if (half) {
@@ -645,7 +646,7 @@ __global__ __launch_bounds__(256) void decode_streams(DecodeLaunch a, DevTables 
         const uint32_t slot = x & (kM - 1u);
         const uint32_t s = t.slot[size_t(table) * kM + slot];
         const uint32_t fcv = t.fc[size_t(table) * 256 + s];
-        x = (fcv & 0xFFFFu) * (x >> kProbBits) + slot - (fcv >> 16);
+        x = (fcv & 0x0FFFu) * (x >> kProbBits) + slot - (fcv >> 16);
         refill(x, p, x < kStateLow, lane, half, W, nw, bad);
         const bool esc = s == n;
         uint32_t z = s;
@@ -683,8 +684,8 @@ __global__ __launch_bounds__(256) void decode_streams(DecodeLaunch a, DevTables 
 
 // Checkerboard decoder with everything but the table lookups taken off the
 // state chain.  A step's side input and decoded neighbours (and from them its
-// table, mean and direct count) do not depend on the rANS state, so each lane
-// loads them 4 steps ahead and reads its table's direct count 2 steps ahead.
+// table and mean) do not depend on the rANS state, so each lane loads them
+// 4 steps ahead.
 // Words come from two 32-word windows of the stream held in registers (lane i
 // of a half holds word base + i and base + 32 + i); a refilling lane fetches
 // its word from the window lane with ds_bpermute, and a window that has been
@@ -750,7 +751,7 @@ __global__ __launch_bounds__(256) void decode_cb(DecodeLaunch a, DevTables t, ui
 
     int32_t ig[P], il[P], ir[P];                           // stage 1: side input and neighbours
     int32_t kk[P];                                         // stage 2: mean cell
-    uint32_t tab[P], nn[P];                                // stage 2: table and direct count
+    uint32_t tab[P];                                       // stage 2: table
     constexpr int kIters = kSteps + 2 * kLag;
     static_assert(P >= 2 * kLag + 1 && P % 2 == 0, "ring period covers the pipeline");
     for (int it0 = 0; it0 < kIters; it0 += P) {
@@ -780,7 +781,6 @@ __global__ __launch_bounds__(256) void decode_cb(DecodeLaunch a, DevTables t, ui
                     if (pass) mu += 8 * (il[sl] + ir[sl]);
                     kk[sl] = mu >> 4;
                     tab[sl] = ch * 16u + uint32_t(mu & 15);
-                    nn[sl] = t.n[tab[sl]];
                 }
             }
             // stage 3: the step it - 2 lag
@@ -788,17 +788,19 @@ __global__ __launch_bounds__(256) void decode_cb(DecodeLaunch a, DevTables t, ui
                 const int k = it - 2 * kLag;
                 const int sl = (d - 2 * kLag + 2 * P) % P;
                 if (k >= 0 && k < kSteps) {
-                    const uint32_t table = tab[sl], n = nn[sl];
+                    const uint32_t table = tab[sl];
                     const uint32_t slot = x & (kM - 1u);
-                    // the even slot's symbol, then the rows of it and of the next symbol: the odd slot
-                    // belongs to the next one when that one starts there (never past the escape symbol)
+                    // the even slot's symbol, then the rows of it and of the next symbol in one 8-byte read:
+                    // the odd slot belongs to the next one when that one starts there (never past the
+                    // escape symbol, whose row is flagged in bit 15)
                     const uint32_t s0 = t.half[size_t(table) * (kM / 2) + (slot >> 1)];
-                    const uint32_t* fr = t.fc + size_t(table) * 256 + s0;
-                    const uint32_t f0 = fr[0], f1 = fr[s0 < n ? 1 : 0];
-                    const bool adv = s0 < n && slot >= (f1 >> 16);
+                    uint2 fr;
+                    __builtin_memcpy(&fr, t.fc + size_t(table) * 256 + s0, 8);
+                    const bool last = (fr.x & 0x8000u) != 0;
+                    const bool adv = !last && slot >= (fr.y >> 16);
                     const uint32_t s = s0 + (adv ? 1u : 0u);
-                    const uint32_t fcv = adv ? f1 : f0;
-                    x = (fcv & 0xFFFFu) * (x >> kProbBits) + slot - (fcv >> 16);
+                    const uint32_t fcv = adv ? fr.y : fr.x;
+                    x = (fcv & 0x0FFFu) * (x >> kProbBits) + slot - (fcv >> 16);
                     // refill in lane order from the word windows
                     const bool need = x < kStateLow;
                     const uint32_t mine = uint32_t(__ballot(need) >> half);
@@ -818,7 +820,7 @@ __global__ __launch_bounds__(256) void decode_cb(DecodeLaunch a, DevTables t, ui
                         nxt = word_at(base + 32 + lane);
                     }
                     // escaped values, in lane order, from the escape region
-                    const bool esc = s == n;
+                    const bool esc = (fcv & 0x8000u) != 0;
                     const uint32_t me = uint32_t(__ballot(esc) >> half);
                     uint32_t z = s;
                     if (esc) {
@@ -826,7 +828,7 @@ __global__ __launch_bounds__(256) void decode_cb(DecodeLaunch a, DevTables t, ui
                         uint32_t v = 0;
                         if (pos < ecap) v = E[pos];
                         else bad = true;
-                        if (v < n) bad = true;                 // a canonical encoder codes such a value directly
+                        if (v < t.n[table]) bad = true;        // a canonical encoder codes such a value directly
                         z = v;
                     }
                     ep += __popc(me);
@@ -2966,7 +2968,7 @@ hipError_t build_dev_tables(const uint8_t* blob, DevTables* t, hipStream_t st) {
     hipError_t e = hipMalloc(&rec, size_t(nt) * kTableRecord);
     if (e == hipSuccess) e = hipMalloc(&t->n, size_t(nt) * 4);
     if (e == hipSuccess) e = hipMalloc(&t->enc, size_t(nt) * 256 * sizeof(uint4));
-    if (e == hipSuccess) e = hipMalloc(&t->fc, size_t(nt) * 256 * 4);
+    if (e == hipSuccess) e = hipMalloc(&t->fc, size_t(nt) * 256 * 4 + 16);   // + one entry read past the last row
     if (e == hipSuccess) e = hipMalloc(&t->slot, size_t(nt) * kM);
     if (e == hipSuccess && blob[7] == SKV_CHECKERBOARD) e = hipMalloc(&t->half, size_t(nt) * (kM / 2));
     if (e == hipSuccess) e = hipMemcpyAsync(rec, blob + kHeaderBytes, size_t(nt) * kTableRecord, hipMemcpyHostToDevice, st);
