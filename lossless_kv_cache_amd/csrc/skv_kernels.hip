@@ -1480,32 +1480,43 @@ __global__ __launch_bounds__(1024) void encode_tiles(EncodeLaunch a, DevTables t
     }
 }
 
-// The same coder with a workgroup on two adjacent channel groups: the two
-// half-waves of a wavefront code the two groups' streams of one token block,
-// so every row load covers 64 contiguous bytes of target and predictor.  The
-// tables of both groups sit in LDS ([symbols][64 lanes]); a stream's words
-// go through a 128-word ring that stores each completed 64-word chunk at
-// once, which keeps a workgroup's LDS small enough for two per CU.
-constexpr uint32_t kPairRing = 128;
-constexpr uint32_t kPairWaveLds = 2 * kTileSteps * kLanes + 2 * kPairRing * 2;
-__host__ __device__ constexpr uint32_t encode_pairs_lds(uint32_t fs) { return 2 * kLanes * fs * 16 + 16 * kPairWaveLds; }
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+typedef __attribute__((address_space(3))) uint16_t lds_u16;
+typedef __attribute__((address_space(3))) uint32_t lds_u32;
 
-template <uint32_t DT>
-__global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8))) void encode_pairs(EncodeLaunch a, DevTables t, uint32_t fs, LdsGeo lg) {
-    static_assert(DT == SKV_E4M3, "byte elements");
+// The same coder with a workgroup on 2 NC adjacent channel groups: chain c
+// of a lane codes channel group 2c + (upper half), so a wavefront codes the
+// 2 NC streams of one token block and every row load covers 64 NC contiguous
+// bytes of target and predictor.  With NC = 2 a load instruction reads whole
+// 128-byte lines, each line once; with NC = 1 the two workgroups sharing a
+// line run on one XCD and reach it through its L2.  The tables of the groups
+// sit in LDS ([symbols][64 NC columns]); a stream's words go through a
+// 128-word ring that stores each completed 64-word chunk at once.
+constexpr uint32_t kPairRing = 128;
+__host__ __device__ constexpr uint32_t encode_groups_lds(uint32_t nc, uint32_t fs) {
+    return 2 * nc * kLanes * fs * 16 + 16 * (kTileSteps * 2 * nc * kLanes + 2 * nc * kPairRing * 2);
+}
+
+template <uint32_t NC>
+__device__ __forceinline__ void encode_groups_body(const EncodeLaunch& a, const DevTables& t, uint32_t fs,
+                                                   const LdsGeo& lg) {
     constexpr uint32_t RAW = kSyms;
     constexpr uint32_t MAXE = RAW - kStreamHead;
     constexpr uint32_t kDrop = 0x80000000u;               // buffer offset past the range: the access is dropped
     constexpr uint32_t kChunks = RAW / 128;                // 64-word chunks that fit the words region
+    constexpr uint32_t NG = 2 * NC;                        // channel groups of the workgroup
+    constexpr uint32_t RL = NG * kLanes;                   // bytes of a tile row = table columns
+    constexpr uint32_t LW = RL / 8;                        // bytes a lane loads per row (8 lanes a row)
+    constexpr uint32_t WLDS = kTileSteps * RL + NG * kPairRing * 2;
     extern __shared__ __align__(16) uint8_t lds[];
     __shared__ uint8_t zig[256];
     const Geo geo = geometry(a.shape);
     const LdsPos ps = lds_position(geo, lg);
     if (!ps.valid) return;
-    const uint32_t tab0 = ps.slab * geo.C + ps.cg * kLanes;                 // first table of the pair
-    uint4* lenc = reinterpret_cast<uint4*>(lds);                            // [fs symbols][64 lanes]
-    for (uint32_t i = threadIdx.x; i < 2 * kLanes * fs; i += blockDim.x) {
-        const uint32_t sym = i / (2 * kLanes), j = i % (2 * kLanes);
+    const uint32_t tab0 = ps.slab * geo.C + ps.cg * kLanes;                 // first table of the groups
+    uint4* lenc = reinterpret_cast<uint4*>(lds);                            // [fs symbols][RL columns]
+    for (uint32_t i = threadIdx.x; i < RL * fs; i += blockDim.x) {
+        const uint32_t sym = i / RL, j = i % RL;
         lenc[i] = t.enc[size_t(tab0 + j) * 256 + sym];
     }
     for (uint32_t i = threadIdx.x; i < 256; i += blockDim.x) zig[i] = uint8_t(zig8(i));
@@ -1516,137 +1527,203 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8))) void 
     const bool upper = (threadIdx.x & 32u) != 0;
     const uint32_t fsh = upper ? 16u : 0u;
     const uint32_t lane = 31u - hl;                        // format lane (reversed within the half)
-    const uint32_t tl = (upper ? kLanes : 0u) + lane;      // table column of the lane's channel
-    const uint32_t n = t.n[tab0 + tl];
-    uint8_t* tile = lds + size_t(2 * kLanes) * fs * 16 + wave * kPairWaveLds;
-    uint8_t* ring = tile + 2 * kTileSteps * kLanes;
-    // tile: [half][step][32 channels]; this lane loads 8 channels of one step and reads its channel back
-    const uint32_t ld_row = hl >> 2, ld_q = hl & 3u;
-    uint2* tile_st = reinterpret_cast<uint2*>(tile + (upper ? kTileSteps * kLanes : 0u) + ld_row * kLanes + ld_q * 8);
-    const uint8_t* tile_rd = tile + (upper ? kTileSteps * kLanes : 0u) + lane;
-    uint16_t* ring_h = reinterpret_cast<uint16_t*>(ring + (upper ? kPairRing * 2 : 0u));
+    uint8_t* tile = lds + size_t(RL) * fs * 16 + wave * WLDS;
+    uint8_t* ring = tile + kTileSteps * RL;
+    // tile: [step][RL channels]; a lane loads LW channels of one step and reads its chains' channels back
+    const uint32_t ld_row = (threadIdx.x & 63u) >> 3, ld_q = (threadIdx.x & 7u) * LW;
+    uint8_t* tile_st = tile + ld_row * RL + ld_q;
+    uint32_t tl[NC], n[NC], ring_b[NC];
+    const uint8_t* tile_rd[NC];
+    const uint32_t* ring32[NC];
+#pragma unroll
+    for (uint32_t c = 0; c < NC; ++c) {
+        const uint32_t grp = 2 * c + (upper ? 1u : 0u);
+        tl[c] = grp * kLanes + lane;                       // table column of the chain's channel
+        n[c] = t.n[tab0 + tl[c]];
+        tile_rd[c] = tile + grp * kLanes + lane;
+        ring_b[c] = uint32_t(uintptr_t(ring)) + grp * kPairRing * 2;   // LDS byte offsets
+        ring32[c] = reinterpret_cast<const uint32_t*>(ring + grp * kPairRing * 2);
+    }
+    const uint32_t idle_b = uint32_t(uintptr_t(tile)) + 2 * (threadIdx.x & 63u);
+    uint32_t lowm = upper ? 0u : 0xFFFFFFFFu;
+    asm("" : "+v"(lowm));                                  // kept as a lane mask
 
     const uint32_t rowb = geo.C;
-    const size_t slab_b = size_t(ps.slab) * geo.T * rowb + size_t(ps.cg) * kLanes + (upper ? kLanes : 0u) + ld_q * 8;
-    const uint8_t* tgt = static_cast<const uint8_t*>(a.target) + slab_b;
-    const uint8_t* aux = static_cast<const uint8_t*>(a.aux) + slab_b;
+    // target and predictor rows of the slab's channel groups through one buffer resource each:
+    // the lane's row and byte offsets in a register, the tile's row offset in a scalar
+    const size_t slab_b = size_t(ps.slab) * geo.T * rowb + size_t(ps.cg) * kLanes;
+    const int slab_n = int(uint32_t(geo.T - 1) * rowb + RL);
+    const __amdgpu_buffer_rsrc_t trs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(static_cast<const uint8_t*>(a.target) + slab_b), (short)0, slab_n, 0x00020000);
+    const __amdgpu_buffer_rsrc_t prs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(static_cast<const uint8_t*>(a.aux) + slab_b), (short)0, slab_n, 0x00020000);
     const uint64_t sid0 = (uint64_t(ps.slab) * geo.ntb + ps.tb_begin) * geo.ncg + ps.cg;
     uint8_t* wgs = a.scratch + sid0 * (2 * RAW);
     const uint32_t sstride = geo.ncg * (2 * RAW);
     const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
-        wgs, (short)0, int((ps.tb_end - ps.tb_begin - 1) * sstride + 4 * RAW), 0x00020000);
+        wgs, (short)0, int((ps.tb_end - ps.tb_begin - 1) * sstride + NG * 2 * RAW), 0x00020000);
 
-    // z of one tile: difference bytes into LDS, then each lane's channel through the zigzag table
-    auto stage = [&](uint2 tv, uint2 pv, uint32_t* z) {
-        *tile_st = make_uint2(sub8x4(sflip8x4(tv.x), sflip8x4(pv.x)), sub8x4(sflip8x4(tv.y), sflip8x4(pv.y)));
+    typedef uint32_t Row[LW / 4];
+    // z of one tile: difference bytes into LDS, then each chain's channel through the zigzag table
+    auto stage = [&](const Row& tv, const Row& pv, uint32_t (&z)[NC][kTileSteps]) {
+        uint32_t d[LW / 4];
+#pragma unroll
+        for (uint32_t k = 0; k < LW / 4; ++k) d[k] = sub8x4(sflip8x4(tv[k]), sflip8x4(pv[k]));
+        if constexpr (LW == 8) *reinterpret_cast<uint2*>(tile_st) = make_uint2(d[0], d[1]);
+        else *reinterpret_cast<uint4*>(tile_st) = make_uint4(d[0], d[1], d[2], d[3]);
         __builtin_amdgcn_wave_barrier();
 #pragma unroll
-        for (uint32_t r = 0; r < kTileSteps; ++r) z[r] = zig[tile_rd[r * kLanes]];
+        for (uint32_t c = 0; c < NC; ++c)
+#pragma unroll
+            for (uint32_t r = 0; r < kTileSteps; ++r) z[c][r] = zig[tile_rd[c][r * RL]];
         __builtin_amdgcn_wave_barrier();
     };
-    const uint32_t* ring32 = reinterpret_cast<const uint32_t*>(ring_h);
 
     for (uint32_t tb = ps.tb_begin + wave; tb < ps.tb_end; tb += nwave) {
-        const uint32_t ao = (tb - ps.tb_begin) * sstride + (upper ? 2 * RAW : 0u);
-        const uint32_t ebase = ao + kStreamHead - (upper ? 32u : 0u);   // upper-half slots carry a bias of 32
-        const uint32_t wreg = ao + RAW;
-        const uint8_t* tsrc = tgt + size_t(tb * kSteps + ld_row) * rowb;
-        const uint8_t* psrc = aux + size_t(tb * kSteps + ld_row) * rowb;
-        const size_t tstride = size_t(kTileSteps) * rowb;
+        uint32_t ao[NC];
+#pragma unroll
+        for (uint32_t c = 0; c < NC; ++c) ao[c] = (tb - ps.tb_begin) * sstride + (2 * c + (upper ? 1u : 0u)) * (2 * RAW);
+        const uint32_t lo = (tb * kSteps + ld_row) * rowb + ld_q;
+        const uint32_t trow = kTileSteps * rowb;
+        auto load = [&](uint32_t j, Row& tv, Row& pv) {
+            if constexpr (LW == 8) {
+                const auto t2 = __builtin_amdgcn_raw_buffer_load_b64(trs, lo, j * trow, 0);
+                const auto p2 = __builtin_amdgcn_raw_buffer_load_b64(prs, lo, j * trow, 0);
+                tv[0] = t2[0], tv[1] = t2[1], pv[0] = p2[0], pv[1] = p2[1];
+            } else {
+                const auto t4 = __builtin_amdgcn_raw_buffer_load_b128(trs, lo, j * trow, 0);
+                const auto p4 = __builtin_amdgcn_raw_buffer_load_b128(prs, lo, j * trow, 0);
+#pragma unroll
+                for (uint32_t k = 0; k < 4; ++k) tv[k] = t4[k], pv[k] = p4[k];
+            }
+        };
         constexpr int kTiles = kSteps / kTileSteps;
+        static_assert(kTiles % 2 == 0, "tiles are taken in pairs");
 
-        uint32_t zc[kTileSteps], zn[kTileSteps];
-        uint2 tv = *reinterpret_cast<const uint2*>(tsrc + (kTiles - 1) * tstride);
-        uint2 pv = *reinterpret_cast<const uint2*>(psrc + (kTiles - 1) * tstride);
-        stage(tv, pv, zc);
-        tv = *reinterpret_cast<const uint2*>(tsrc + (kTiles - 2) * tstride);
-        pv = *reinterpret_cast<const uint2*>(psrc + (kTiles - 2) * tstride);
+        uint32_t za[NC][kTileSteps], zb[NC][kTileSteps];
+        Row tv, pv;
+        load(kTiles - 1, tv, pv);
+        stage(tv, pv, za);
+        load(kTiles - 2, tv, pv);
 
-        uint32_t x = kStateLow;
-        uint32_t wp = 0;                                   // word counts: lower half | upper half << 16
-        uint32_t elo = 0, ehi = 0;                         // escape counts per half
-        uint4 ec = lenc[min(zc[kTileSteps - 1], n) * (2 * kLanes) + tl];
-        for (int j = kTiles - 1; j >= 0; --j) {
+        uint32_t x[NC], wp[NC], elo[NC], ehi[NC];         // wp: word counts, lower half | upper half << 16
+        uint4 ec[NC];
+#pragma unroll
+        for (uint32_t c = 0; c < NC; ++c) {
+            x[c] = kStateLow;
+            wp[c] = elo[c] = ehi[c] = 0;
+            ec[c] = lenc[min(za[c][kTileSteps - 1], n[c]) * RL + tl[c]];
+        }
+        // one tile: zc holds its symbols, zn receives the next tile's (two arrays that trade roles, so
+        // no copy between tiles)
+        auto tile_pass = [&](int j, uint32_t (&zc)[NC][kTileSteps], uint32_t (&zn)[NC][kTileSteps]) {
             if (j > 0) {
                 stage(tv, pv, zn);
-                if (j > 1) {
-                    tv = *reinterpret_cast<const uint2*>(tsrc + size_t(j - 2) * tstride);
-                    pv = *reinterpret_cast<const uint2*>(psrc + size_t(j - 2) * tstride);
-                }
+                if (j > 1) load(uint32_t(j - 2), tv, pv);
             }
 #pragma unroll
             for (int r = kTileSteps - 1; r >= 0; --r) {
-                const uint4 e = ec;
-                const uint32_t znext = r > 0 ? zc[r - 1] : zn[kTileSteps - 1];
-                ec = lenc[min(znext, n) * (2 * kLanes) + tl];
-                // words leave before the state absorbs the symbol
-                uint32_t xs = x;
-                const bool emit = xs >= e.x;
-                const uint64_t mw = __ballot(emit);
-                const uint32_t mlo = uint32_t(mw), mhi = uint32_t(mw >> 32);
-                const uint32_t pp = __popc(mlo) | (__popc(mhi) << 16);
-                // ring slot: this half's count mod 128 plus the emitting lanes below (mbcnt_lo counts the
-                // entire lower half for an upper lane, which the packed base subtracts again)
-                const uint32_t pk = (wp - (pp << 16)) & 0x007F007Fu;
-                const uint32_t slot =
-                    __builtin_amdgcn_mbcnt_hi(mhi, __builtin_amdgcn_mbcnt_lo(mlo, __builtin_amdgcn_ubfe(pk, fsh, 16)));
-                if (emit) ring_h[slot & (kPairRing - 1)] = uint16_t(xs & 0xFFFFu);
-                xs = emit ? xs >> 16 : xs;
-                const uint32_t qt = __umulhi(xs + (e.z >> 24), e.y) >> (e.w & 31u);   // floor(xs / f)
-                // x = xs + qt (4096 - f) + start, the start taken from the high half of e.w
-                const uint32_t xq = __umul24(qt, e.z) + xs;
-                asm("v_add_u32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:WORD_1"
-                    : "=v"(x) : "v"(xq), "v"(e.w));
-                // a completed 64-word chunk leaves the ring (at most one per step and stream)
-                const uint32_t cross = ((wp & 0x003F003Fu) + pp) & 0x00400040u;
-                if (cross) {
-                    __builtin_amdgcn_wave_barrier();
-                    const uint32_t ck = __builtin_amdgcn_ubfe(wp >> 6, fsh, 10);
-                    const uint32_t w = ring32[(ck & 1u) * 32 + hl];
-                    const bool mine = __builtin_amdgcn_ubfe(cross, fsh + 6, 1) != 0;
-                    __builtin_amdgcn_raw_buffer_store_b32(
-                        w, wrs, mine && ck < kChunks ? wreg + ck * 128 + 4 * hl : kDrop, 0, 0);
-                    __builtin_amdgcn_wave_barrier();
+                uint32_t wn[NC], cross[NC];
+#pragma unroll
+                for (uint32_t c = 0; c < NC; ++c) {
+                    const uint4 e = ec[c];
+                    const uint32_t znext = r > 0 ? zc[c][r - 1] : zn[c][kTileSteps - 1];
+                    ec[c] = lenc[min(znext, n[c]) * RL + tl[c]];
+                    // words leave before the state absorbs the symbol
+                    uint32_t xs = x[c];
+                    const bool emit = xs >= e.x;
+                    const uint64_t mw = __ballot(emit);
+                    const uint32_t mlo = uint32_t(mw), mhi = uint32_t(mw >> 32);
+                    const uint32_t pp = __popc(mlo) | (__popc(mhi) << 16);
+                    // ring slot: this half's count mod 128 plus the emitting lanes below it in the half
+                    // (an upper lane's mbcnt_lo sees no lower-half flag through lowm); a lane that emits
+                    // nothing stores to its own slot of the idle tile instead, so the store needs no branch
+                    const uint32_t slot = __builtin_amdgcn_mbcnt_hi(
+                        mhi, __builtin_amdgcn_mbcnt_lo(mlo & lowm, __builtin_amdgcn_ubfe(wp[c], fsh, 7)));
+                    const uint32_t ra = ring_b[c] + 2 * (slot & (kPairRing - 1));
+                    uint32_t wa;
+                    asm("v_cndmask_b32_e64 %0, %1, %2, %3" : "=v"(wa) : "v"(idle_b), "v"(ra), "s"(mw));
+                    *reinterpret_cast<lds_u16*>(wa) = uint16_t(xs & 0xFFFFu);
+                    xs = emit ? xs >> 16 : xs;
+                    const uint32_t qt = __umulhi(xs + (e.z >> 24), e.y) >> (e.w & 31u);   // floor(xs / f)
+                    // x = xs + qt (4096 - f) + start, the start taken from the high half of e.w
+                    const uint32_t xq = __umul24(qt, e.z) + xs;
+                    asm("v_add_u32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD "
+                        "src1_sel:WORD_1"
+                        : "=v"(x[c]) : "v"(xq), "v"(e.w));
+                    // a completed 64-word chunk leaves the ring (at most one per step and stream: bit 6
+                    // of the half's count changes)
+                    wn[c] = wp[c] + pp;
+                    cross[c] = (wn[c] ^ wp[c]) & 0x00400040u;
                 }
-                wp += pp;
+#pragma unroll
+                for (uint32_t c = 0; c < NC; ++c) {
+                    if (cross[c]) {
+                        __builtin_amdgcn_wave_barrier();
+                        const uint32_t ck = __builtin_amdgcn_ubfe(wp[c] >> 6, fsh, 10);
+                        const uint32_t w = ring32[c][(ck & 1u) * 32 + hl];
+                        const bool mine = __builtin_amdgcn_ubfe(cross[c], fsh + 6, 1) != 0;
+                        __builtin_amdgcn_raw_buffer_store_b32(
+                            w, wrs, mine && ck < kChunks ? ao[c] + RAW + ck * 128 + 4 * hl : kDrop, 0, 0);
+                        __builtin_amdgcn_wave_barrier();
+                    }
+                    wp[c] = wn[c];
+                }
             }
             // escaped values of this tile, in emission order (rare: skipped by the whole wavefront)
-            uint32_t zm = zc[0];
 #pragma unroll
-            for (uint32_t r = 1; r < kTileSteps; ++r) zm = max(zm, zc[r]);
-            if (__ballot(zm >= n) != 0) {
+            for (uint32_t c = 0; c < NC; ++c) {
+                uint32_t zm = zc[c][0];
+#pragma unroll
+                for (uint32_t r = 1; r < kTileSteps; ++r) zm = max(zm, zc[c][r]);
+                if (__ballot(zm >= n[c]) == 0) continue;
+                // upper-half slots carry a bias of 32 (mbcnt_lo counts the whole lower half for them)
+                const uint32_t ebase = ao[c] + kStreamHead - (upper ? 32u : 0u);
 #pragma unroll
                 for (int r = kTileSteps - 1; r >= 0; --r) {
-                    const bool esc = zc[r] >= n;
+                    const bool esc = zc[c][r] >= n[c];
                     const uint64_t me = __ballot(esc);
                     if (me == 0) continue;
                     const uint32_t mlo = uint32_t(me), mhi = uint32_t(me >> 32), plo = __popc(mlo);
-                    const uint32_t pk = min(elo, MAXE) | ((min(ehi, MAXE) + 32u - plo) << 16);
+                    const uint32_t pk = min(elo[c], MAXE) | ((min(ehi[c], MAXE) + 32u - plo) << 16);
                     const uint32_t slot = __builtin_amdgcn_mbcnt_hi(
                         mhi, __builtin_amdgcn_mbcnt_lo(mlo, __builtin_amdgcn_ubfe(pk, fsh, 16)));
-                    __builtin_amdgcn_raw_buffer_store_b8(uint8_t(zc[r]), wrs, esc ? ebase + slot : kDrop, 0, 0);
-                    elo += plo;
-                    ehi += __popc(mhi);
+                    __builtin_amdgcn_raw_buffer_store_b8(uint8_t(zc[c][r]), wrs, esc ? ebase + slot : kDrop, 0, 0);
+                    elo[c] += plo;
+                    ehi[c] += __popc(mhi);
                 }
             }
+        };
+        for (int j = kTiles - 1; j > 0; j -= 2) {
+            tile_pass(j, za, zb);
+            tile_pass(j - 1, zb, za);
+        }
+        // the partial last chunk, the final states and the streams' counts
+        __builtin_amdgcn_wave_barrier();
 #pragma unroll
-            for (uint32_t r = 0; r < kTileSteps; ++r) zc[r] = zn[r];
+        for (uint32_t c = 0; c < NC; ++c) {
+            const uint32_t cnt = __builtin_amdgcn_ubfe(wp[c], fsh, 16), ecnt = upper ? ehi[c] : elo[c];
+            const uint32_t ck = cnt >> 6;
+            const uint32_t w = ring32[c][(ck & 1u) * 32 + hl];
+            __builtin_amdgcn_raw_buffer_store_b32(
+                w, wrs, ck < kChunks && 2 * hl < (cnt & 63u) ? ao[c] + RAW + ck * 128 + 4 * hl : kDrop, 0, 0);
+            reinterpret_cast<uint32_t*>(wgs + ao[c])[lane] = x[c];
+            if (hl == 0) {
+                const uint64_t sid = sid0 + uint64_t(tb - ps.tb_begin) * geo.ncg + 2 * c + (upper ? 1u : 0u);
+                const uint32_t bytes = (kStreamHead + 2 * cnt + ecnt + 3) & ~3u;
+                a.meta[sid] = bytes >= RAW ? 0x80000000u : (cnt | (ecnt << 14));
+            }
         }
-        // the partial last chunk, the final states and the stream's counts
         __builtin_amdgcn_wave_barrier();
-        const uint32_t cnt = __builtin_amdgcn_ubfe(wp, fsh, 16), ecnt = upper ? ehi : elo;
-        const uint32_t ck = cnt >> 6;
-        const uint32_t w = ring32[(ck & 1u) * 32 + hl];
-        __builtin_amdgcn_raw_buffer_store_b32(w, wrs, ck < kChunks && 2 * hl < (cnt & 63u) ? wreg + ck * 128 + 4 * hl : kDrop,
-                                              0, 0);
-        __builtin_amdgcn_wave_barrier();
-        reinterpret_cast<uint32_t*>(wgs + ao)[lane] = x;
-        if (hl == 0) {
-            const uint64_t sid = sid0 + uint64_t(tb - ps.tb_begin) * geo.ncg + (upper ? 1u : 0u);
-            const uint32_t bytes = (kStreamHead + 2 * cnt + ecnt + 3) & ~3u;
-            a.meta[sid] = bytes >= RAW ? 0x80000000u : (cnt | (ecnt << 14));
-        }
     }
+}
+
+// two channel groups, two workgroups per CU.  (Four groups, whole 128-byte lines read once by one
+// wavefront, fit one workgroup per CU and measured slower: 1.94 ms against 1.75 ms on a
+// 36 x 2 x 32768 x 1024 cache, the lost occupancy costing more than the line re-reads.)
+__global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8))) void encode_pairs(EncodeLaunch a, DevTables t,
+                                                                                          uint32_t fs, LdsGeo lg) {
+    encode_groups_body<1>(a, t, fs, lg);
 }
 
 // --------------------------------------------------------------- tiled bf16 encode
@@ -1882,10 +1959,6 @@ __host__ __device__ constexpr uint32_t dec_e4m3_rings(uint32_t fs) {
 __host__ __device__ constexpr uint32_t dec_e4m3_lds(uint32_t fs) {
     return dec_e4m3_rings(fs) + kDecStreams * (2 * kDecRing + kDecTile * kLanes);
 }
-
-typedef __attribute__((address_space(3))) uint8_t lds_u8;
-typedef __attribute__((address_space(3))) uint16_t lds_u16;
-typedef __attribute__((address_space(3))) uint32_t lds_u32;
 
 // bytewise helpers on 4 packed e4m3 codes / symbols
 __device__ __forceinline__ uint32_t add8x4(uint32_t a, uint32_t b) {
@@ -2801,6 +2874,12 @@ LdsGeo lds_geometry(const skv_shape& s, uint32_t cgw = 1) {
 }
 
 inline uint32_t lds_grid(const LdsGeo& g) { return ((g.groups + 7) / 8) * 8 * g.G; }
+// The tiled kernels address a slab's rows (a whole matrix in checkerboard mode)
+// with 32-bit byte offsets; larger slabs take the per-step kernels.
+inline bool slab_fits(const skv_shape& s) {
+    const uint64_t eb = s.dtype == SKV_E4M3 ? 1u : 2u;
+    return uint64_t(s.tokens) * s.channels * eb < (1ull << 31);
+}
 inline uint32_t fc_stride(const DevTables& t) { return (t.max_n + 1 + 3) & ~3u; }
 
 size_t decode_lds_bytes(const DevTables& t, uint32_t dtype, bool half) {
@@ -2824,7 +2903,8 @@ hipError_t encode_all(const EncodeLaunch& a, const DevTables& t, hipStream_t st)
     const bool aligned = (reinterpret_cast<uintptr_t>(a.target) | reinterpret_cast<uintptr_t>(a.aux)) % 8 == 0;
     const uint32_t ncg = a.shape.channels / kLanes;
     const bool aligned16 = (reinterpret_cast<uintptr_t>(a.target) | reinterpret_cast<uintptr_t>(a.aux)) % 16 == 0;
-    if (DT == SKV_BF16 && MODE == SKV_RESIDUAL && aligned16 && encode_bf16_lds(fc_stride(t)) <= kLdsLimit &&
+    const bool fits = slab_fits(a.shape);
+    if (DT == SKV_BF16 && MODE == SKV_RESIDUAL && fits && aligned16 && encode_bf16_lds(fc_stride(t)) <= kLdsLimit &&
         !g_force_v1 && variant().enc == 0) {
         const LdsGeo lg = lds_geometry(a.shape);
         const size_t lp = encode_bf16_lds(fc_stride(t));
@@ -2833,17 +2913,17 @@ hipError_t encode_all(const EncodeLaunch& a, const DevTables& t, hipStream_t st)
         timed("encode_streams", st, [&] {
             hipLaunchKernelGGL(encode_bf16, dim3(lds_grid(lg)), dim3(kLdsThreads), lp, st, a, t, fc_stride(t), lg);
         });
-    } else if (DT == SKV_E4M3 && MODE == SKV_RESIDUAL && ncg % 4 == 0 && 2 * encode_pairs_lds(fc_stride(t)) + 512 <= kLdsLimit &&
-        aligned && !g_force_v1 && variant().enc == 0) {
+    } else if (DT == SKV_E4M3 && MODE == SKV_RESIDUAL && fits && ncg % 4 == 0 &&
+               2 * encode_groups_lds(1, fc_stride(t)) + 512 <= kLdsLimit && aligned && !g_force_v1 &&
+               variant().enc == 0) {
         const LdsGeo lg = lds_geometry(a.shape, 2);
-        const size_t lp = encode_pairs_lds(fc_stride(t));
-        auto k = encode_pairs<SKV_E4M3>;
-        hipError_t e = allow_lds(k, lp);
+        const size_t lp = encode_groups_lds(1, fc_stride(t));
+        hipError_t e = allow_lds(encode_pairs, lp);
         if (e != hipSuccess) return e;
         timed("encode_streams", st, [&] {
-            hipLaunchKernelGGL(k, dim3(lds_grid(lg)), dim3(kLdsThreads), lp, st, a, t, fc_stride(t), lg);
+            hipLaunchKernelGGL(encode_pairs, dim3(lds_grid(lg)), dim3(kLdsThreads), lp, st, a, t, fc_stride(t), lg);
         });
-    } else if (DT == SKV_E4M3 && MODE == SKV_RESIDUAL && lt <= kLdsLimit && aligned && !g_force_v1 && variant().enc == 0) {
+    } else if (DT == SKV_E4M3 && MODE == SKV_RESIDUAL && fits && lt <= kLdsLimit && aligned && !g_force_v1 && variant().enc == 0) {
         const LdsGeo lg = lds_geometry(a.shape);
         auto k = encode_tiles<SKV_E4M3>;
         hipError_t e = allow_lds(k, lt);
@@ -2851,7 +2931,7 @@ hipError_t encode_all(const EncodeLaunch& a, const DevTables& t, hipStream_t st)
         timed("encode_streams", st, [&] {
             hipLaunchKernelGGL(k, dim3(lds_grid(lg)), dim3(kLdsThreads), lt, st, a, t, fc_stride(t), lg);
         });
-    } else if (MODE == SKV_RESIDUAL && lb <= kLdsLimit && !g_force_v1 && variant().enc >= 0) {
+    } else if (MODE == SKV_RESIDUAL && fits && lb <= kLdsLimit && !g_force_v1 && variant().enc >= 0) {
         const LdsGeo lg = lds_geometry(a.shape);
         auto k = encode_lds<DT, 1, 4>;
         switch (variant().enc) {
@@ -2866,7 +2946,7 @@ hipError_t encode_all(const EncodeLaunch& a, const DevTables& t, hipStream_t st)
         timed("encode_streams", st, [&] {
             hipLaunchKernelGGL(k, dim3(lds_grid(lg)), dim3(kLdsThreads), lb, st, a, t, fc_stride(t), lg);
         });
-    } else if (MODE == SKV_CHECKERBOARD && !g_force_v1 && variant().enc == 0) {
+    } else if (MODE == SKV_CHECKERBOARD && fits && !g_force_v1 && variant().enc == 0) {
         // two steps between stages: longer lags measured no faster (more registers, fewer waves)
         const Geo g{a.shape.channels, a.shape.tokens, a.shape.channels / kLanes, a.shape.tokens / 2 / kSteps};
         const dim3 grid(g.ncg * ((g.ntb + 7) / 8), 2);       // y: pass
@@ -2897,7 +2977,8 @@ hipError_t encode_all(const EncodeLaunch& a, const DevTables& t, hipStream_t st)
 template <uint32_t DT, uint32_t MODE>
 hipError_t decode_all(const DecodeLaunch& a, const DevTables& t, hipStream_t st) {
     const int v = variant().dec;
-    if (DT == SKV_E4M3 && MODE == SKV_RESIDUAL && !g_force_v1 && v == 0 && t.max_n + 1 <= 64 &&
+    const bool fits = slab_fits(a.shape);
+    if (DT == SKV_E4M3 && MODE == SKV_RESIDUAL && fits && !g_force_v1 && v == 0 && t.max_n + 1 <= 64 &&
         dec_e4m3_lds(64) <= kLdsLimit) {
         const LdsGeo lg = lds_geometry(a.shape);
         const bool small = t.max_n + 1 <= 32;
@@ -2912,7 +2993,7 @@ hipError_t decode_all(const DecodeLaunch& a, const DevTables& t, hipStream_t st)
     }
     // the bf16 decoder moves predictor and output rows 8 bytes per lane
     const bool aligned8 = (reinterpret_cast<uintptr_t>(a.aux) | reinterpret_cast<uintptr_t>(a.out)) % 8 == 0;
-    if (DT == SKV_BF16 && MODE == SKV_RESIDUAL && !g_force_v1 && v == 0 && aligned8 && dec_bf16_lds() <= kLdsLimit) {
+    if (DT == SKV_BF16 && MODE == SKV_RESIDUAL && fits && !g_force_v1 && v == 0 && aligned8 && dec_bf16_lds() <= kLdsLimit) {
         const LdsGeo lg = lds_geometry(a.shape);
         hipError_t e = allow_lds(decode_bf16, dec_bf16_lds());
         if (e != hipSuccess) return e;
@@ -2923,7 +3004,7 @@ hipError_t decode_all(const DecodeLaunch& a, const DevTables& t, hipStream_t st)
     }
     const bool half = v != 1 && v != 3;
     const size_t lb = decode_lds_bytes(t, DT, half);
-    if (MODE == SKV_RESIDUAL && lb <= kLdsLimit && !g_force_v1 && v >= 0) {
+    if (MODE == SKV_RESIDUAL && fits && lb <= kLdsLimit && !g_force_v1 && v >= 0) {
         const LdsGeo lg = lds_geometry(a.shape);
         auto k = decode_lds<DT, 1, 4, true>;
         switch (v) {
@@ -2945,7 +3026,7 @@ hipError_t decode_all(const DecodeLaunch& a, const DevTables& t, hipStream_t st)
     const uint32_t grid = uint32_t((per + kStreamsPerBlock - 1) / kStreamsPerBlock);
     for (uint64_t ps = 0; ps < passes; ++ps)
         timed("decode_streams", st, [&] {
-            if (MODE == SKV_CHECKERBOARD && !g_force_v1 && v == 0)
+            if (MODE == SKV_CHECKERBOARD && fits && !g_force_v1 && v == 0)
                 hipLaunchKernelGGL((decode_cb<2, 8>), dim3(a.shape.channels / kLanes * ((per / (a.shape.channels / kLanes) + 7) / 8)),
                                    dim3(256), 0, st, a, t, ps * per, per);
             else
