@@ -121,6 +121,27 @@ int skv_encode(const void* tables_blob, const skv_shape* s, const void* d_target
 int skv_decode(const void* tables_blob, const void* d_in, size_t in_bytes, const void* d_aux,
                void* d_out, size_t out_capacity, void* d_work, size_t* work_bytes, hipStream_t stream);
 
+/* Decode a token range (device).  A stored shared prefix, such as a system
+ * prompt, is reused by restoring the part of its cache that a request needs
+ * ("Speculative KV coding" page, section "Where it can be used": prefix
+ * caching; VeriCache page, "Application to remote prefix caching"); the
+ * container's offset index locates the streams of the range, so nothing
+ * outside it is read or decoded.  Residual containers only.
+ *   token_begin, token_end: the tokens [token_begin, token_end) of every
+ *     (layer, K|V) slab; both multiples of 128, token_begin < token_end <=
+ *     the container's tokens (else SKV_ERR_SHAPE, also for a checkerboard
+ *     container).
+ *   d_aux, d_out: device arrays [layers][kv][token_end - token_begin]
+ *     [channels] -- the predictor of the range and its reconstruction
+ *     (out_capacity bytes available).
+ * Header, blob and workspace rules as for skv_decode.  Every stream of the
+ * range is checked as in skv_decode (SKV_ERR_CORRUPT); streams outside the
+ * range are not read, so damage there goes unnoticed.  Blocks the host to
+ * read the header and the integrity word. */
+int skv_decode_range(const void* tables_blob, const void* d_in, size_t in_bytes, uint32_t token_begin,
+                     uint32_t token_end, const void* d_aux, void* d_out, size_t out_capacity, void* d_work,
+                     size_t* work_bytes, hipStream_t stream);
+
 /* Release a library-owned blob and its device copies.  NULL is a no-op. */
 void skv_free(void* tables_blob);
 

@@ -196,8 +196,11 @@ int skv_encode(const void* tables_blob, const skv_shape* s, const void* d_target
     return total > out_capacity ? SKV_ERR_CAPACITY : SKV_OK;
 }
 
-int skv_decode(const void* tables_blob, const void* d_in, size_t in_bytes, const void* d_aux, void* d_out,
-               size_t out_capacity, void* d_work, size_t* work_bytes, hipStream_t stream) {
+// Decode of token blocks [tb0, tb1) of every slab of a container (all of them
+// for skv_decode).  tb1 = 0 stands for the container's last token block + 1.
+static int decode_blocks(const void* tables_blob, const void* d_in, size_t in_bytes, bool range, uint32_t token_begin,
+                         uint32_t token_end, const void* d_aux, void* d_out, size_t out_capacity, void* d_work,
+                         size_t* work_bytes, hipStream_t stream) {
     if (!tables_blob || !work_bytes) return SKV_ERR_ARG;
     Blob* b = find_blob(tables_blob);
     if (!b) return SKV_ERR_ARG;
@@ -226,18 +229,31 @@ int skv_decode(const void* tables_blob, const void* d_in, size_t in_bytes, const
     const uint64_t payload = skv::rd64(h + 48);
     const uint64_t head = skv::kHeaderBytes + 8 * (n + 1);
     if (in_bytes < head || in_bytes - head < payload) return SKV_ERR_CORRUPT;
-    if (out_capacity < skv::element_count(s) * skv::elem_bytes(s.dtype)) return SKV_ERR_CAPACITY;
+    // the decoded part: whole token blocks of a residual container
+    skv_shape part = s;
+    uint32_t tb_base = 0;
+    if (range) {
+        if (s.mode != SKV_RESIDUAL || token_begin >= token_end || token_end > s.tokens ||
+            token_begin % skv::kSteps != 0 || token_end % skv::kSteps != 0)
+            return SKV_ERR_SHAPE;
+        part.tokens = token_end - token_begin;
+        tb_base = token_begin / skv::kSteps;
+    }
+    if (out_capacity < skv::element_count(part) * skv::elem_bytes(part.dtype)) return SKV_ERR_CAPACITY;
     const skv::DevTables* t = nullptr;
     int rc = device_tables(b, stream, &t);
     if (rc != SKV_OK) return rc;
     skv::DecodeLaunch a{};
-    a.in = static_cast<const uint8_t*>(d_in);
+    a.index = reinterpret_cast<const uint64_t*>(static_cast<const uint8_t*>(d_in) + skv::kHeaderBytes);
+    a.pay = static_cast<const uint8_t*>(d_in) + head;
     a.payload_bytes = payload;
     a.aux = d_aux;
     a.out = d_out;
     a.status = static_cast<uint32_t*>(d_work);
-    a.shape = s;
-    a.n_streams = n;
+    a.shape = part;
+    a.n_streams = skv::stream_count(part);
+    a.tb_base = tb_base;
+    a.ntb_index = s.tokens / skv::kSteps;
     if (skv::launch_clear_u32(a.status, 1, stream) != hipSuccess) return SKV_ERR_DEVICE;
     skv::timing_reset();
     if (skv::launch_decode(a, *t, stream) != hipSuccess) return SKV_ERR_DEVICE;
@@ -246,6 +262,19 @@ int skv_decode(const void* tables_blob, const void* d_in, size_t in_bytes, const
     if (hipStreamSynchronize(stream) != hipSuccess) return SKV_ERR_DEVICE;
     skv::timing_collect();
     return status ? SKV_ERR_CORRUPT : SKV_OK;
+}
+
+int skv_decode(const void* tables_blob, const void* d_in, size_t in_bytes, const void* d_aux, void* d_out,
+               size_t out_capacity, void* d_work, size_t* work_bytes, hipStream_t stream) {
+    return decode_blocks(tables_blob, d_in, in_bytes, false, 0, 0, d_aux, d_out, out_capacity, d_work, work_bytes,
+                         stream);
+}
+
+int skv_decode_range(const void* tables_blob, const void* d_in, size_t in_bytes, uint32_t token_begin,
+                     uint32_t token_end, const void* d_aux, void* d_out, size_t out_capacity, void* d_work,
+                     size_t* work_bytes, hipStream_t stream) {
+    return decode_blocks(tables_blob, d_in, in_bytes, true, token_begin, token_end, d_aux, d_out, out_capacity, d_work,
+                         work_bytes, stream);
 }
 
 int skv_kernel_timing(int enable) { return skv::timing_enable(enable != 0); }

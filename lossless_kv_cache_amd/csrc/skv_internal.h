@@ -76,13 +76,16 @@ struct EncodeLaunch {
 };
 
 struct DecodeLaunch {
-    const uint8_t* in;
+    const uint64_t* index;   // the container's stream offsets (n_streams + 1 of its own)
+    const uint8_t* pay;      // the container's payload
     uint64_t payload_bytes;
     const void* aux;
     void* out;
     uint32_t* status;
-    skv_shape shape;
-    uint64_t n_streams;
+    skv_shape shape;         // of the decoded range (aux and out layout)
+    uint64_t n_streams;      // streams decoded
+    uint32_t tb_base;        // first token block of the range in the container
+    uint32_t ntb_index;      // token blocks per slab in the container
 };
 
 hipError_t build_dev_tables(const uint8_t* blob, DevTables* t, hipStream_t stream);

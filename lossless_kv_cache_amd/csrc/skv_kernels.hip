@@ -567,6 +567,14 @@ __device__ __forceinline__ void refill(uint32_t& x, uint32_t& p, bool need, uint
     p += __popc(mine);
 }
 
+// Index position of stream (slab, tb, cg) of a decode.  The container numbers
+// its streams over its own token blocks (ntb_index per slab); a range decode
+// covers token blocks tb_base onwards of every slab, numbered from 0 here.
+__device__ __forceinline__ uint64_t index_pos(const DecodeLaunch& a, uint32_t slab, uint32_t tb, uint32_t cg,
+                                              uint32_t ncg) {
+    return (uint64_t(slab) * a.ntb_index + a.tb_base + tb) * ncg + cg;
+}
+
 template <uint32_t DT, uint32_t MODE>
 __global__ __launch_bounds__(256) void decode_streams(DecodeLaunch a, DevTables t, uint64_t first, uint64_t count) {
     const uint32_t tid = threadIdx.x;
@@ -581,9 +589,10 @@ __global__ __launch_bounds__(256) void decode_streams(DecodeLaunch a, DevTables 
     const uint32_t ch = cg * kLanes + lane;
     constexpr uint32_t EB = DT == SKV_E4M3 ? 1u : 2u;
     constexpr uint32_t RAW = kSyms * EB;
-    const uint64_t* index = reinterpret_cast<const uint64_t*>(a.in + kHeaderBytes);
-    const uint8_t* pay = a.in + kHeaderBytes + 8 * (a.n_streams + 1);
-    const uint64_t e0 = index[sid], e1 = index[sid + 1];
+    const uint64_t* index = a.index;
+    const uint8_t* pay = a.pay;
+    const uint64_t ip = MODE == SKV_RESIDUAL ? index_pos(a, slab, tb, cg, g.ncg) : sid;
+    const uint64_t e0 = index[ip], e1 = index[ip + 1];
     const uint64_t off = e0 & ~kRawBit, end = e1 & ~kRawBit;
     bool bad = false;
     if (end < off || end > a.payload_bytes) {
@@ -706,8 +715,8 @@ __global__ __launch_bounds__(256) void decode_cb(DecodeLaunch a, DevTables t, ui
     const uint32_t pass = uint32_t(sid / (uint64_t(g.ncg) * g.ntb));
     const uint32_t ch = cg * kLanes + lane;
     const size_t C = g.C;
-    const uint64_t* index = reinterpret_cast<const uint64_t*>(a.in + kHeaderBytes);
-    const uint8_t* pay = a.in + kHeaderBytes + 8 * (a.n_streams + 1);
+    const uint64_t* index = a.index;
+    const uint8_t* pay = a.pay;
     const uint64_t e0 = index[sid], e1 = index[sid + 1];
     const uint64_t off = e0 & ~kRawBit, end = e1 & ~kRawBit;
     int16_t* out = static_cast<int16_t*>(a.out);
@@ -898,8 +907,8 @@ __device__ __forceinline__ void decode_round(const DecodeLaunch& a, const LdsPos
     constexpr uint32_t RAW = kSyms * EB;
     const uint32_t lane = threadIdx.x & 31u, half = threadIdx.x & 32u;
     const uint32_t ltmask = (1u << lane) - 1u;
-    const uint64_t* index = reinterpret_cast<const uint64_t*>(a.in + kHeaderBytes);
-    const uint8_t* pay = a.in + kHeaderBytes + 8 * (a.n_streams + 1);
+    const uint64_t* index = a.index;
+    const uint8_t* pay = a.pay;
     const uint32_t rowb = geo.C * EB;                      // bytes per cache row
     // slab bases are uniform over the workgroup; lanes add 32-bit offsets
     const size_t slab_b = size_t(ps.slab) * geo.T * rowb + size_t(ps.cg) * kLanes * EB;
@@ -930,7 +939,7 @@ __device__ __forceinline__ void decode_round(const DecodeLaunch& a, const LdsPos
         E[s] = pay;
         act[s] = rawc[s] = false;
         if (!present) continue;
-        const uint64_t sid = (uint64_t(ps.slab) * geo.ntb + tb) * geo.ncg + ps.cg;
+        const uint64_t sid = index_pos(a, ps.slab, tb, ps.cg, geo.ncg);
         const uint64_t e0 = index[sid], e1 = index[sid + 1];
         const uint64_t o = e0 & ~kRawBit, end = e1 & ~kRawBit;
         const uint64_t size = end - o;
@@ -1040,7 +1049,7 @@ __device__ __forceinline__ void decode_round(const DecodeLaunch& a, const LdsPos
         }
         if (!act[s]) continue;
         if (x[s] != kStateLow || p[s] != nwc[s] || ep[s] > ecc[s]) bad = true;
-        const uint8_t* sp = pay + (index[(uint64_t(ps.slab) * geo.ntb + tb0 + s) * geo.ncg + ps.cg] & ~kRawBit);
+        const uint8_t* sp = pay + (index[index_pos(a, ps.slab, tb0 + s, ps.cg, geo.ncg)] & ~kRawBit);
         const uint32_t used = kStreamHead + 2 * nwc[s] + EB * ep[s];
         if (((used + 3) & ~3u) != sz[s]) bad = true;
         else if (lane < sz[s] - used && sp[used + lane] != 0) bad = true;   // zero pad
@@ -2107,10 +2116,10 @@ __global__ __launch_bounds__(1024, 1) void decode_e4m3(DecodeLaunch a, DevTables
     const uint32_t r4 = hl >> 3, q4 = (hl & 7u) * 4;               // tile-domain row and byte column
 
     const uint32_t rowb = geo.C;
-    const uint64_t* index = reinterpret_cast<const uint64_t*>(a.in + kHeaderBytes);
-    const uint8_t* pay = a.in + kHeaderBytes + 8 * (a.n_streams + 1);
-    const uint64_t sfirst = (uint64_t(ps.slab) * geo.ntb + ps.tb_begin) * geo.ncg + ps.cg;
-    const uint64_t slast = (uint64_t(ps.slab) * geo.ntb + ps.tb_end - 1) * geo.ncg + ps.cg;
+    const uint64_t* index = a.index;
+    const uint8_t* pay = a.pay;
+    const uint64_t sfirst = index_pos(a, ps.slab, ps.tb_begin, ps.cg, geo.ncg);
+    const uint64_t slast = index_pos(a, ps.slab, ps.tb_end - 1, ps.cg, geo.ncg);
     const uint64_t wlo = index[sfirst] & ~kRawBit, whi = index[slast + 1] & ~kRawBit;
     if (whi < wlo || whi > a.payload_bytes || whi - wlo >= (1ull << 31)) {
         if (tid == 0) atomicOr(a.status, 1u);
@@ -2149,7 +2158,7 @@ __global__ __launch_bounds__(1024, 1) void decode_e4m3(DecodeLaunch a, DevTables
 #pragma unroll
         for (uint32_t c = 0; c < kDecChains; ++c) {
             const uint32_t tbc = min(tb0 + 2 * c + (upper ? 1u : 0u), ps.tb_end - 1);
-            const uint64_t sid = (uint64_t(ps.slab) * geo.ntb + tbc) * geo.ncg + ps.cg;
+            const uint64_t sid = index_pos(a, ps.slab, tbc, ps.cg, geo.ncg);
             ix0[c] = index[sid];
             ix1[c] = index[sid + 1];
         }
@@ -2520,10 +2529,10 @@ __global__ __launch_bounds__(1024, 1) void decode_bf16(DecodeLaunch a, DevTables
     const uint32_t r4 = hl >> 3, q4 = (hl & 7u) * 4;               // tile-domain row and byte column
 
     const uint32_t rowb = geo.C * 2;
-    const uint64_t* index = reinterpret_cast<const uint64_t*>(a.in + kHeaderBytes);
-    const uint8_t* pay = a.in + kHeaderBytes + 8 * (a.n_streams + 1);
-    const uint64_t sfirst = (uint64_t(ps.slab) * geo.ntb + ps.tb_begin) * geo.ncg + ps.cg;
-    const uint64_t slast = (uint64_t(ps.slab) * geo.ntb + ps.tb_end - 1) * geo.ncg + ps.cg;
+    const uint64_t* index = a.index;
+    const uint8_t* pay = a.pay;
+    const uint64_t sfirst = index_pos(a, ps.slab, ps.tb_begin, ps.cg, geo.ncg);
+    const uint64_t slast = index_pos(a, ps.slab, ps.tb_end - 1, ps.cg, geo.ncg);
     const uint64_t wlo = index[sfirst] & ~kRawBit, whi = index[slast + 1] & ~kRawBit;
     if (whi < wlo || whi > a.payload_bytes || whi - wlo >= (1ull << 31)) {
         if (tid == 0) atomicOr(a.status, 1u);
@@ -2558,7 +2567,7 @@ __global__ __launch_bounds__(1024, 1) void decode_bf16(DecodeLaunch a, DevTables
 #pragma unroll
         for (uint32_t c = 0; c < kDecChains; ++c) {
             const uint32_t tbc = min(tb0 + 2 * c + (upper ? 1u : 0u), ps.tb_end - 1);
-            const uint64_t sid = (uint64_t(ps.slab) * geo.ntb + tbc) * geo.ncg + ps.cg;
+            const uint64_t sid = index_pos(a, ps.slab, tbc, ps.cg, geo.ncg);
             ix0[c] = index[sid];
             ix1[c] = index[sid + 1];
         }

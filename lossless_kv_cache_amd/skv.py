@@ -58,6 +58,8 @@ def lib():
         L.skv_encode.argtypes = [vp, sp, vp, vp, vp, sz, psz, vp, psz, vp]
         L.skv_decode.restype = ctypes.c_int
         L.skv_decode.argtypes = [vp, vp, sz, vp, vp, sz, vp, psz, vp]
+        L.skv_decode_range.restype = ctypes.c_int
+        L.skv_decode_range.argtypes = [vp, vp, sz, u32, u32, vp, vp, sz, vp, psz, vp]
         L.skv_free.restype = None
         L.skv_free.argtypes = [vp]
         L.skv_kernel_timing.restype = ctypes.c_int
@@ -210,6 +212,29 @@ def decode_into(tables: Tables, container: torch.Tensor, aux: torch.Tensor, out:
                           _stream())
     _check(rc, "skv_decode")
     return out
+
+
+def decode_range_into(tables: Tables, container: torch.Tensor, token_begin: int, token_end: int, aux: torch.Tensor,
+                      out: torch.Tensor) -> torch.Tensor:
+    """Decode tokens [token_begin, token_end) of every slab; aux and out hold that range only."""
+    key = container.device
+    work = _decode_work.get(key)
+    if work is None:
+        wb = ctypes.c_size_t()
+        _check(lib().skv_decode(tables.ptr, None, 0, None, None, 0, None, ctypes.byref(wb), None), "skv_decode(size)")
+        work = _decode_work[key] = torch.empty(wb.value, dtype=torch.uint8, device=key)
+    wb = ctypes.c_size_t(work.numel())
+    rc = lib().skv_decode_range(tables.ptr, _dev(container, "container"), container.numel(), token_begin, token_end,
+                                _dev(aux, "aux"), _dev(out, "out"), out.numel() * out.element_size(),
+                                work.data_ptr(), ctypes.byref(wb), _stream())
+    _check(rc, "skv_decode_range")
+    return out
+
+
+def decode_range(tables: Tables, container: torch.Tensor, token_begin: int, token_end: int,
+                 aux: torch.Tensor) -> torch.Tensor:
+    """Decode a token range against its predictor; returns a tensor shaped like aux."""
+    return decode_range_into(tables, container, token_begin, token_end, aux, torch.empty_like(aux))
 
 
 def kernel_timing(enable: bool) -> None:

@@ -26,7 +26,7 @@ def skv():
 def test_exports_every_declared_symbol(skv):
     text = open(os.path.join(ROOT, "include", "skv.h")).read()
     names = set(re.findall(r"^\s*(?:int|void|uint32_t|const char\*)\s+(skv_\w+)\s*\(", text, re.M))
-    assert {"skv_fit_tables", "skv_load_tables", "skv_encode", "skv_decode", "skv_free",
+    assert {"skv_fit_tables", "skv_load_tables", "skv_encode", "skv_decode", "skv_decode_range", "skv_free",
             "skv_version", "skv_strerror"} <= names
     L = ctypes.CDLL(skv.LIB_PATH)
     for n in sorted(names):
@@ -117,3 +117,9 @@ def test_size_queries_and_shape_errors(skv):
     s.abi_version = 2
     assert L.skv_encode(tabs.ptr, ctypes.byref(s), None, None, None, 0, ctypes.byref(ob), None,
                         ctypes.byref(wb), None) == skv.ERR_SHAPE
+    # decode workspace size queries (no device memory is touched)
+    wd, wr = ctypes.c_size_t(), ctypes.c_size_t()
+    assert L.skv_decode(tabs.ptr, None, 0, None, None, 0, None, ctypes.byref(wd), None) == 0
+    assert L.skv_decode_range(tabs.ptr, None, 0, 0, 128, None, None, 0, None, ctypes.byref(wr), None) == 0
+    assert wr.value == wd.value > 0
+    assert L.skv_decode_range(dummy, None, 0, 0, 128, None, None, 0, None, ctypes.byref(wr), None) == skv.ERR_ARG

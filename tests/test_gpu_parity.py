@@ -206,6 +206,74 @@ def test_unaligned_buffers(skv, orc, dtype):
     assert torch.equal(out, t)
 
 
+RANGES = [(0, 1024), (0, 128), (896, 1024), (256, 640), (128, 1024)]
+
+
+@pytest.mark.parametrize("dtype,aligned", [("e4m3", True), ("bf16", True), ("bf16", False)])
+def test_decode_range(skv, orc, dtype, aligned):
+    """A token range decoded through the offset index equals the same tokens
+    of the oracle's decode of the whole container (e4m3: decode_e4m3; bf16:
+    decode_bf16, or the per-table LDS decoder for unaligned buffers)."""
+    cfg = gen.Config(95, f"range-{dtype}", dtype, 2, 2, 1024, 256)
+    t, p, tabs, oshape = residual_case(skv, orc, cfg)
+    cont = skv.encode(tabs, t, p)
+    torch.cuda.synchronize()
+    pn = p.cpu().numpy()
+    say(f"[parity] range {dtype}: oracle decode of the whole container")
+    want = orc.decode(tabs.bytes(), cont.cpu().numpy().tobytes(), pn, pn, threads=8)
+    assert np.array_equal(want, t.cpu().numpy())
+    for a, b in RANGES:
+        say(f"[parity] range {dtype} aligned={aligned}: tokens [{a}, {b})")
+        pr = p[:, :, a:b].contiguous()
+        out = torch.zeros_like(pr)
+        if not aligned:
+            pr, out = _offset_copy(pr, 1), _offset_copy(out, 1)
+        skv.decode_range_into(tabs, cont, a, b, pr, out)
+        assert np.array_equal(out.cpu().numpy(), want[:, :, a:b]), (a, b)
+
+
+def test_decode_range_errors(skv, orc):
+    cfg = gen.Config(96, "range-errors", "e4m3", 1, 2, 512, 64)
+    t, p, tabs, oshape = residual_case(skv, orc, cfg)
+    cont = skv.encode(tabs, t, p)
+    for a, b in [(0, 100), (64, 192), (256, 256), (384, 128), (0, 640)]:
+        with pytest.raises(skv.SkvError) as e:
+            skv.decode_range(tabs, cont, a, b, p[:, :, :128].contiguous())
+        assert e.value.status == skv.ERR_SHAPE, (a, b)
+    with pytest.raises(skv.SkvError) as e:
+        skv.decode_range_into(tabs, cont, 128, 384, p, torch.empty(10, dtype=torch.uint8, device="cuda"))
+    assert e.value.status == skv.ERR_CAPACITY
+    # a damaged stream inside the range is found; one outside it is not read
+    good = cont.cpu().numpy()
+    n, idx, head = _parse(good.tobytes())
+    ntb, ncg = 512 // 128, 64 // 32
+    for tb, inside in [(1, True), (3, False)]:
+        s = (0 * ntb + tb) * ncg + 1                       # slab 0, channel group 1
+        assert not (idx[s] >> np.uint64(63))
+        a = int(idx[s] & np.uint64((1 << 63) - 1))
+        bad = good.copy()
+        bad[head + a + 5] ^= np.uint8(0x40)                # a final state byte
+        pr = p[:, :, 128:256].contiguous()
+        say(f"[parity] range damage in token block {tb}")
+        if inside:
+            bad_cont = torch.from_numpy(bad).cuda()
+            with pytest.raises(skv.SkvError) as e:
+                skv.decode_range(tabs, bad_cont, 128, 256, pr)
+            assert e.value.status == skv.ERR_CORRUPT
+        else:
+            out = skv.decode_range(tabs, torch.from_numpy(bad).cuda(), 128, 256, pr)
+            assert torch.equal(out, t[:, :, 128:256])
+    # checkerboard containers have no range decode
+    cb = gen.CONFIGS[4].with_tokens(512, channels=64)
+    coef, G = gen.dckv_draw(cb, device="cuda")
+    cc, cgl = gen.dckv_draw(cb, gen.CALIB, tokens=256, device="cuda")
+    ctabs = skv.fit_tables(skv.INT16, skv.CHECKERBOARD, 1, 1, 64, cc.cpu().numpy(), cgl.cpu().numpy(), 256)
+    ccont = skv.encode(ctabs, coef, G)
+    with pytest.raises(skv.SkvError) as e:
+        skv.decode_range(ctabs, ccont, 0, 256, G[:256].contiguous())
+    assert e.value.status == skv.ERR_SHAPE
+
+
 def test_corruption_and_wrong_tables(skv, orc):
     cfg = gen.Config(92, "corrupt-bf16", "bf16", 1, 2, 256, 64)
     t, p, tabs, oshape = residual_case(skv, orc, cfg)
