@@ -389,6 +389,41 @@ def test_full_size_residual(skv, orc, cid):
     say(f"[parity] cfg{cid}: round trip exact")
 
 
+def test_slab_over_2gib(skv, orc):
+    """A (layer, K|V) slab of 2 GiB (2^21 tokens x 1024 e4m3 channels) is past
+    the tiled kernels' 32-bit row offsets, so it takes the per-step encoder and
+    decoder; sampled streams match the oracle, the round trip is exact, and a
+    range at the slab's end decodes through the tiled decoder."""
+    cfg = gen.Config(97, "slab-2gib-e4m3", "e4m3", 1, 1, 1 << 21, 1024, outliers=False)
+    say(f"[parity] 2 GiB slab: generating {cfg.values} values on GPU")
+    t, p, tabs, oshape = residual_case(skv, orc, cfg)
+    say("[parity] 2 GiB slab: encode")
+    cont = skv.encode(tabs, t, p)
+    torch.cuda.synchronize()
+    n = orc.n_streams(oshape)
+    head = 64 + 8 * (n + 1)
+    host_head = cont[:head].cpu().numpy().tobytes()
+    idx = np.frombuffer(host_head[64:], dtype=np.uint64)
+    offs = idx & np.uint64((1 << 63) - 1)
+    assert int(offs[-1]) == cont.numel() - head
+    ncg, blob = cfg.channels // 32, tabs.bytes()
+    for s in _sample_ids(n, 24, 97):
+        cg, tb = s % ncg, s // ncg
+        sl = (0, 0, slice(tb * 128, tb * 128 + 128), slice(cg * 32, cg * 32 + 32))
+        lanes = np.arange(32, dtype=np.uint32) + cg * 32
+        data, raw = orc.encode_tile(blob, oshape, t[sl].cpu().numpy(), p[sl].cpu().numpy(), lanes)
+        assert bool(int(idx[s]) >> 63) == raw, s
+        assert cont[head + int(offs[s]):head + int(offs[s + 1])].cpu().numpy().tobytes() == data, s
+    say("[parity] 2 GiB slab: sampled streams identical; decoding")
+    back = skv.decode(tabs, cont, p)
+    assert torch.equal(back, t)
+    del back
+    a = cfg.tokens - 256
+    part = skv.decode_range(tabs, cont, a, cfg.tokens, p[:, :, a:].contiguous())
+    assert torch.equal(part, t[:, :, a:])
+    say("[parity] 2 GiB slab: round trip and end range exact")
+
+
 def test_full_size_checkerboard(skv, orc):
     cfg = gen.CONFIGS[4]
     say("[parity] cfg4: generating")
