@@ -21,6 +21,8 @@
 #include <cstdio>
 #include <cstdlib>
 
+#include <hip/hip_ext.h>
+
 #include "skv_internal.h"
 
 namespace skv {
@@ -2823,8 +2825,8 @@ __global__ void clear_u32(uint32_t* p, uint32_t n) {
     if (i < n) p[i] = 0u;
 }
 
-// Optional per-kernel timing: a HIP event pair around each launch on the
-// caller's stream, read back after the call's final synchronization.
+// Optional per-kernel timing: a HIP event pair on each launch on the caller's
+// stream, read back after the call's final synchronization.
 struct KernelTiming {
     bool on = false;
     int count = 0;
@@ -2836,16 +2838,17 @@ struct KernelTiming {
 KernelTiming g_timing;
 bool g_force_v1 = false;     // use the one-stream-per-half-wave kernels (diagnostics)
 
+// `launch` dispatches one kernel with hipExtLaunchKernelGGL and the event pair it
+// is given (null when timing is off): the events take the kernel's own start
+// and end times, with no marker packets between the launches.
 template <class F>
 void timed(const char* name, hipStream_t st, F&& launch) {
     KernelTiming& T = g_timing;
     if (T.on && T.count < kMaxTimedKernels) {
-        (void)hipEventRecord(T.ev[2 * T.count], st);
-        launch();
-        (void)hipEventRecord(T.ev[2 * T.count + 1], st);
+        launch(T.ev[2 * T.count], T.ev[2 * T.count + 1]);
         T.name[T.count++] = name;
     } else {
-        launch();
+        launch(nullptr, nullptr);
     }
 }
 
@@ -2919,8 +2922,8 @@ hipError_t encode_all(const EncodeLaunch& a, const DevTables& t, hipStream_t st)
         const size_t lp = encode_bf16_lds(fc_stride(t));
         hipError_t e = allow_lds(encode_bf16, lp);
         if (e != hipSuccess) return e;
-        timed("encode_streams", st, [&] {
-            hipLaunchKernelGGL(encode_bf16, dim3(lds_grid(lg)), dim3(kLdsThreads), lp, st, a, t, fc_stride(t), lg);
+        timed("encode_streams", st, [&](hipEvent_t e0, hipEvent_t e1) {
+            hipExtLaunchKernelGGL(encode_bf16, dim3(lds_grid(lg)), dim3(kLdsThreads), lp, st, e0, e1, 0, a, t, fc_stride(t), lg);
         });
     } else if (DT == SKV_E4M3 && MODE == SKV_RESIDUAL && fits && ncg % 4 == 0 &&
                2 * encode_groups_lds(1, fc_stride(t)) + 512 <= kLdsLimit && aligned && !g_force_v1 &&
@@ -2929,16 +2932,16 @@ hipError_t encode_all(const EncodeLaunch& a, const DevTables& t, hipStream_t st)
         const size_t lp = encode_groups_lds(1, fc_stride(t));
         hipError_t e = allow_lds(encode_pairs, lp);
         if (e != hipSuccess) return e;
-        timed("encode_streams", st, [&] {
-            hipLaunchKernelGGL(encode_pairs, dim3(lds_grid(lg)), dim3(kLdsThreads), lp, st, a, t, fc_stride(t), lg);
+        timed("encode_streams", st, [&](hipEvent_t e0, hipEvent_t e1) {
+            hipExtLaunchKernelGGL(encode_pairs, dim3(lds_grid(lg)), dim3(kLdsThreads), lp, st, e0, e1, 0, a, t, fc_stride(t), lg);
         });
     } else if (DT == SKV_E4M3 && MODE == SKV_RESIDUAL && fits && lt <= kLdsLimit && aligned && !g_force_v1 && variant().enc == 0) {
         const LdsGeo lg = lds_geometry(a.shape);
         auto k = encode_tiles<SKV_E4M3>;
         hipError_t e = allow_lds(k, lt);
         if (e != hipSuccess) return e;
-        timed("encode_streams", st, [&] {
-            hipLaunchKernelGGL(k, dim3(lds_grid(lg)), dim3(kLdsThreads), lt, st, a, t, fc_stride(t), lg);
+        timed("encode_streams", st, [&](hipEvent_t e0, hipEvent_t e1) {
+            hipExtLaunchKernelGGL(k, dim3(lds_grid(lg)), dim3(kLdsThreads), lt, st, e0, e1, 0, a, t, fc_stride(t), lg);
         });
     } else if (MODE == SKV_RESIDUAL && fits && lb <= kLdsLimit && !g_force_v1 && variant().enc >= 0) {
         const LdsGeo lg = lds_geometry(a.shape);
@@ -2952,33 +2955,33 @@ hipError_t encode_all(const EncodeLaunch& a, const DevTables& t, hipStream_t st)
         }
         hipError_t e = allow_lds(k, lb);
         if (e != hipSuccess) return e;
-        timed("encode_streams", st, [&] {
-            hipLaunchKernelGGL(k, dim3(lds_grid(lg)), dim3(kLdsThreads), lb, st, a, t, fc_stride(t), lg);
+        timed("encode_streams", st, [&](hipEvent_t e0, hipEvent_t e1) {
+            hipExtLaunchKernelGGL(k, dim3(lds_grid(lg)), dim3(kLdsThreads), lb, st, e0, e1, 0, a, t, fc_stride(t), lg);
         });
     } else if (MODE == SKV_CHECKERBOARD && fits && !g_force_v1 && variant().enc == 0) {
         // two steps between stages: longer lags measured no faster (more registers, fewer waves)
         const Geo g{a.shape.channels, a.shape.tokens, a.shape.channels / kLanes, a.shape.tokens / 2 / kSteps};
         const dim3 grid(g.ncg * ((g.ntb + 7) / 8), 2);       // y: pass
-        timed("encode_streams", st, [&] {
-            hipLaunchKernelGGL((encode_cb<2, 8>), grid, dim3(256), 0, st, a, t);
+        timed("encode_streams", st, [&](hipEvent_t e0, hipEvent_t e1) {
+            hipExtLaunchKernelGGL((encode_cb<2, 8>), grid, dim3(256), 0, st, e0, e1, 0, a, t);
         });
     } else {
-        timed("encode_streams", st, [&] {
-            hipLaunchKernelGGL((encode_streams<DT, MODE>), dim3(eg), dim3(256), 0, st, a, t);
+        timed("encode_streams", st, [&](hipEvent_t e0, hipEvent_t e1) {
+            hipExtLaunchKernelGGL((encode_streams<DT, MODE>), dim3(eg), dim3(256), 0, st, e0, e1, 0, a, t);
         });
     }
-    timed("stream_block_sums", st, [&] {
-        hipLaunchKernelGGL(stream_block_sums, dim3(nb), dim3(kScanBlock), 0, st, a.meta, n,
+    timed("stream_block_sums", st, [&](hipEvent_t e0, hipEvent_t e1) {
+        hipExtLaunchKernelGGL(stream_block_sums, dim3(nb), dim3(kScanBlock), 0, st, e0, e1, 0, a.meta, n,
                            kSyms * (DT == SKV_E4M3 ? 1u : 2u), a.block_sum);
     });
-    timed("stream_block_scan", st, [&] {
-        hipLaunchKernelGGL(stream_block_scan, dim3(1), dim3(kScanBlock), 0, st, a.block_sum, nb, a.block_off, a.total);
+    timed("stream_block_scan", st, [&](hipEvent_t e0, hipEvent_t e1) {
+        hipExtLaunchKernelGGL(stream_block_scan, dim3(1), dim3(kScanBlock), 0, st, e0, e1, 0, a.block_sum, nb, a.block_off, a.total);
     });
-    timed("place_streams", st, [&] {
-        hipLaunchKernelGGL((place_streams<DT, MODE>), dim3(nb), dim3(kScanBlock), 0, st, a, a.block_off);
+    timed("place_streams", st, [&](hipEvent_t e0, hipEvent_t e1) {
+        hipExtLaunchKernelGGL((place_streams<DT, MODE>), dim3(nb), dim3(kScanBlock), 0, st, e0, e1, 0, a, a.block_off);
     });
-    timed("copy_streams", st, [&] {
-        hipLaunchKernelGGL((copy_streams<DT, MODE>), dim3(uint32_t((n + 3) / 4)), dim3(256), 0, st, a);
+    timed("copy_streams", st, [&](hipEvent_t e0, hipEvent_t e1) {
+        hipExtLaunchKernelGGL((copy_streams<DT, MODE>), dim3(uint32_t((n + 3) / 4)), dim3(256), 0, st, e0, e1, 0, a);
     });
     return hipGetLastError();
 }
@@ -2995,8 +2998,8 @@ hipError_t decode_all(const DecodeLaunch& a, const DevTables& t, hipStream_t st)
         const size_t lb = small ? dec_e4m3_lds(32) : dec_e4m3_lds(64);
         hipError_t e = allow_lds(k, lb);
         if (e != hipSuccess) return e;
-        timed("decode_streams", st, [&] {
-            hipLaunchKernelGGL(k, dim3(lds_grid(lg)), dim3(kLdsThreads), lb, st, a, t, lg);
+        timed("decode_streams", st, [&](hipEvent_t e0, hipEvent_t e1) {
+            hipExtLaunchKernelGGL(k, dim3(lds_grid(lg)), dim3(kLdsThreads), lb, st, e0, e1, 0, a, t, lg);
         });
         return hipGetLastError();
     }
@@ -3006,8 +3009,8 @@ hipError_t decode_all(const DecodeLaunch& a, const DevTables& t, hipStream_t st)
         const LdsGeo lg = lds_geometry(a.shape);
         hipError_t e = allow_lds(decode_bf16, dec_bf16_lds());
         if (e != hipSuccess) return e;
-        timed("decode_streams", st, [&] {
-            hipLaunchKernelGGL(decode_bf16, dim3(lds_grid(lg)), dim3(kLdsThreads), dec_bf16_lds(), st, a, t, lg);
+        timed("decode_streams", st, [&](hipEvent_t e0, hipEvent_t e1) {
+            hipExtLaunchKernelGGL(decode_bf16, dim3(lds_grid(lg)), dim3(kLdsThreads), dec_bf16_lds(), st, e0, e1, 0, a, t, lg);
         });
         return hipGetLastError();
     }
@@ -3025,8 +3028,8 @@ hipError_t decode_all(const DecodeLaunch& a, const DevTables& t, hipStream_t st)
         }
         hipError_t e = allow_lds(k, lb);
         if (e != hipSuccess) return e;
-        timed("decode_streams", st, [&] {
-            hipLaunchKernelGGL(k, dim3(lds_grid(lg)), dim3(kLdsThreads), lb, st, a, t, fc_stride(t), lg);
+        timed("decode_streams", st, [&](hipEvent_t e0, hipEvent_t e1) {
+            hipExtLaunchKernelGGL(k, dim3(lds_grid(lg)), dim3(kLdsThreads), lb, st, e0, e1, 0, a, t, fc_stride(t), lg);
         });
         return hipGetLastError();
     }
@@ -3034,12 +3037,12 @@ hipError_t decode_all(const DecodeLaunch& a, const DevTables& t, hipStream_t st)
     const uint64_t per = a.n_streams / passes;
     const uint32_t grid = uint32_t((per + kStreamsPerBlock - 1) / kStreamsPerBlock);
     for (uint64_t ps = 0; ps < passes; ++ps)
-        timed("decode_streams", st, [&] {
+        timed("decode_streams", st, [&](hipEvent_t e0, hipEvent_t e1) {
             if (MODE == SKV_CHECKERBOARD && fits && !g_force_v1 && v == 0)
-                hipLaunchKernelGGL((decode_cb<2, 8>), dim3(a.shape.channels / kLanes * ((per / (a.shape.channels / kLanes) + 7) / 8)),
-                                   dim3(256), 0, st, a, t, ps * per, per);
+                hipExtLaunchKernelGGL((decode_cb<2, 8>), dim3(a.shape.channels / kLanes * ((per / (a.shape.channels / kLanes) + 7) / 8)),
+                                   dim3(256), 0, st, e0, e1, 0, a, t, ps * per, per);
             else
-                hipLaunchKernelGGL((decode_streams<DT, MODE>), dim3(grid), dim3(256), 0, st, a, t, ps * per, per);
+                hipExtLaunchKernelGGL((decode_streams<DT, MODE>), dim3(grid), dim3(256), 0, st, e0, e1, 0, a, t, ps * per, per);
         });
     return hipGetLastError();
 }
