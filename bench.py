@@ -67,19 +67,26 @@ def main() -> int:
         return 1
     torch.cuda.set_device(0)
     cfg = gen.CONFIGS[args.config]
-    if cfg.dtype == "int16":
-        raise SystemExit("the checkerboard workload is a parity case; bench times the residual workloads")
-    dt = skv.E4M3 if cfg.dtype == "e4m3" else skv.BF16
+    cb = cfg.dtype == "int16"                  # DCKV coefficients (checkerboard mode)
 
     log(f"generating {cfg.name}: {cfg.values} values on the GPU")
     t0 = time.perf_counter()
-    tgt, prd = gen.residual_array(cfg, device="cuda")
-    ct, cp = gen.residual_array(cfg, gen.CALIB, tokens=gen.CALIB_TOKENS, device="cuda")
+    if cb:
+        tgt, prd = gen.dckv_draw(cfg, device="cuda")
+        ct, cp = gen.dckv_draw(cfg, gen.CALIB, tokens=gen.CALIB_TOKENS, device="cuda")
+    else:
+        tgt, prd = gen.residual_array(cfg, device="cuda")
+        ct, cp = gen.residual_array(cfg, gen.CALIB, tokens=gen.CALIB_TOKENS, device="cuda")
     torch.cuda.synchronize()
     log(f"generated in {time.perf_counter() - t0:.1f} s; fitting tables")
     t0 = time.perf_counter()
-    tabs = skv.fit_tables(dt, skv.RESIDUAL, cfg.layers, cfg.kv, cfg.channels, ct.cpu().numpy(), cp.cpu().numpy(),
-                          gen.CALIB_TOKENS)
+    if cb:
+        tabs = skv.fit_tables(skv.INT16, skv.CHECKERBOARD, 1, 1, cfg.channels, ct.cpu().numpy(), cp.cpu().numpy(),
+                              gen.CALIB_TOKENS)
+    else:
+        dt = skv.E4M3 if cfg.dtype == "e4m3" else skv.BF16
+        tabs = skv.fit_tables(dt, skv.RESIDUAL, cfg.layers, cfg.kv, cfg.channels, ct.cpu().numpy(),
+                              cp.cpu().numpy(), gen.CALIB_TOKENS)
     fit_s = time.perf_counter() - t0
     del ct, cp
     log(f"fit {tabs.nbytes} B of tables in {fit_s:.2f} s")
@@ -120,7 +127,7 @@ def main() -> int:
     # partial decode: the first half of every slab's tokens through the container's offset index
     part = None
     t1 = (cfg.tokens // 2) // 128 * 128
-    if t1 > 0:
+    if t1 > 0 and not cb:
         cont = enc(tgt, prd)
         pr = prd[:, :, :t1].contiguous()
         orr = torch.empty_like(pr)
@@ -155,7 +162,8 @@ def main() -> int:
         "encode_streams": 2 * raw_bytes + payload,               # target + predictor read, coded streams out
         "place_streams": 8 * (n_streams + 1) + 64,              # index + header written
         "copy_streams": payload,                                 # the stream payload written
-        "decode_streams": raw_bytes + cont_bytes + raw_bytes,    # predictor + container read, reconstruction out
+        # predictor (or G) + container read, reconstruction out; checkerboard decodes in two launches
+        "decode_streams": (raw_bytes + cont_bytes + raw_bytes) // (2 if cb else 1),
         "stream_block_sums": 0, "stream_block_scan": 0,
     }
     dom = max(ktot, key=lambda k: ktot[k] / args.steps)
@@ -195,7 +203,7 @@ def main() -> int:
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(cfg, tabs, tgt, prd, args.cpu_seconds)
+        cpu = (cpu_baseline_cb if cb else cpu_baseline)(cfg, tabs, tgt, prd, args.cpu_seconds)
 
     res = {
         "metric": METRIC,
@@ -267,6 +275,37 @@ def cpu_baseline(cfg, tabs, tgt, prd, seconds):
     return {"value": round(done_bytes / spent / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
             "sample": f"encode + decode of {layers} of {cfg.layers} layers (K and V, {done_bytes} B of "
                       f"{cfg.dtype} codes) of the same workload and tables, {threads} OpenMP threads",
+            "seconds": round(spent, 2)}
+
+
+def cpu_baseline_cb(cfg, tabs, coef, G, seconds):
+    """The oracle on the host for the checkerboard workload: encode + decode of
+    leading token spans of the same matrix (same tables) until about `seconds`."""
+    import numpy as np
+    import oracle
+
+    threads = max(1, min(16, len(os.sched_getaffinity(0))))
+    blob = tabs.bytes()
+    span = min(cfg.tokens, 8192)
+    done_bytes, spent, spans = 0, 0.0, 0
+    for a in range(0, cfg.tokens, span):
+        c = coef[a:a + span].cpu().numpy()
+        g = G[a:a + span].cpu().numpy()
+        shape = oracle.make_shape(oracle.INT16, oracle.CHECKERBOARD, 1, 1, span, cfg.channels)
+        t0 = time.perf_counter()
+        cont = oracle.encode(blob, shape, c, g, threads=threads)
+        back = oracle.decode(blob, cont, g, c, threads=threads)
+        spent += time.perf_counter() - t0
+        if not np.array_equal(back, c):
+            raise RuntimeError("oracle round trip failed")
+        done_bytes += c.nbytes
+        spans += 1
+        log(f"cpu oracle: span {spans} done, {spent:.1f} s so far")
+        if spent >= seconds:
+            break
+    return {"value": round(done_bytes / spent / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"encode + decode of {spans} spans of {span} tokens x {cfg.channels} int16 coefficients "
+                      f"({done_bytes} B) of the same matrix and tables, {threads} OpenMP threads",
             "seconds": round(spent, 2)}
 
 
