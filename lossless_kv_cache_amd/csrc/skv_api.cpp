@@ -9,6 +9,7 @@
 #include <cstring>
 #include <map>
 #include <mutex>
+#include <thread>
 #include <unordered_map>
 
 #include "skv_internal.h"
@@ -73,6 +74,46 @@ bool same_geometry(const skv_shape& blob, const skv_shape& s) {
 }
 
 uint64_t align256(uint64_t v) { return (v + 255) & ~uint64_t(255); }
+
+// Small device-to-host reads on the caller's stream (the container size, a
+// header, the integrity word).  They go through a pinned staging buffer and
+// an event that the calling thread polls, so the host sees the value as soon
+// as the copy lands: a blocking stream synchronization wakes the thread
+// noticeably later, and the decoder's header read and integrity check sit
+// between kernels.  Each thread keeps one staging buffer and event per
+// device for its lifetime.
+constexpr size_t kStagingBytes = 256;
+struct Staging {
+    void* host = nullptr;
+    hipEvent_t ev = nullptr;
+};
+
+int read_back(void* dst, const void* src, size_t n, hipStream_t st) {
+    thread_local std::map<int, Staging> staging;
+    if (n > kStagingBytes) return SKV_ERR_ARG;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return SKV_ERR_DEVICE;
+    Staging& sg = staging[dev];
+    if (!sg.host) {
+        if (hipHostMalloc(&sg.host, kStagingBytes, hipHostMallocDefault) != hipSuccess) {
+            sg.host = nullptr;
+            return SKV_ERR_NOMEM;
+        }
+        if (hipEventCreateWithFlags(&sg.ev, hipEventDisableTiming) != hipSuccess) {
+            (void)hipHostFree(sg.host);
+            sg.host = nullptr;
+            sg.ev = nullptr;
+            return SKV_ERR_DEVICE;
+        }
+    }
+    if (hipMemcpyAsync(sg.host, src, n, hipMemcpyDeviceToHost, st) != hipSuccess) return SKV_ERR_DEVICE;
+    if (hipEventRecord(sg.ev, st) != hipSuccess) return SKV_ERR_DEVICE;
+    hipError_t e;
+    while ((e = hipEventQuery(sg.ev)) == hipErrorNotReady) std::this_thread::yield();
+    if (e != hipSuccess) return SKV_ERR_DEVICE;
+    std::memcpy(dst, sg.host, n);
+    return SKV_OK;
+}
 
 }  // namespace
 
@@ -188,8 +229,8 @@ int skv_encode(const void* tables_blob, const skv_shape* s, const void* d_target
     skv::timing_reset();
     if (skv::launch_encode(a, *t, stream) != hipSuccess) return SKV_ERR_DEVICE;
     uint64_t payload = 0;
-    if (hipMemcpyAsync(&payload, a.total, 8, hipMemcpyDeviceToHost, stream) != hipSuccess) return SKV_ERR_DEVICE;
-    if (hipStreamSynchronize(stream) != hipSuccess) return SKV_ERR_DEVICE;
+    rc = read_back(&payload, a.total, 8, stream);
+    if (rc != SKV_OK) return rc;
     skv::timing_collect();
     const uint64_t total = skv::kHeaderBytes + 8 * (n + 1) + payload;
     *out_bytes = total;
@@ -216,8 +257,8 @@ static int decode_blocks(const void* tables_blob, const void* d_in, size_t in_by
     if (!d_in || !d_aux || !d_out) return SKV_ERR_ARG;
     if (in_bytes < skv::kHeaderBytes) return SKV_ERR_CORRUPT;
     uint8_t h[skv::kHeaderBytes];
-    if (hipMemcpyAsync(h, d_in, sizeof h, hipMemcpyDeviceToHost, stream) != hipSuccess) return SKV_ERR_DEVICE;
-    if (hipStreamSynchronize(stream) != hipSuccess) return SKV_ERR_DEVICE;
+    int rc = read_back(h, d_in, sizeof h, stream);
+    if (rc != SKV_OK) return rc;
     if (std::memcmp(h, "SKV1", 4) != 0 || skv::rd16(h + 4) != 1) return SKV_ERR_CORRUPT;
     if (h[8] != skv::kProbBits || h[9] != skv::kLanes || skv::rd16(h + 10) != skv::kSteps) return SKV_ERR_CORRUPT;
     skv_shape s{SKV_ABI_VERSION, h[6], h[7], skv::rd32(h + 12), skv::rd32(h + 16), skv::rd32(h + 20),
@@ -241,7 +282,7 @@ static int decode_blocks(const void* tables_blob, const void* d_in, size_t in_by
     }
     if (out_capacity < skv::element_count(part) * skv::elem_bytes(part.dtype)) return SKV_ERR_CAPACITY;
     const skv::DevTables* t = nullptr;
-    int rc = device_tables(b, stream, &t);
+    rc = device_tables(b, stream, &t);
     if (rc != SKV_OK) return rc;
     skv::DecodeLaunch a{};
     a.index = reinterpret_cast<const uint64_t*>(static_cast<const uint8_t*>(d_in) + skv::kHeaderBytes);
@@ -258,8 +299,8 @@ static int decode_blocks(const void* tables_blob, const void* d_in, size_t in_by
     skv::timing_reset();
     if (skv::launch_decode(a, *t, stream) != hipSuccess) return SKV_ERR_DEVICE;
     uint32_t status = 0;
-    if (hipMemcpyAsync(&status, a.status, 4, hipMemcpyDeviceToHost, stream) != hipSuccess) return SKV_ERR_DEVICE;
-    if (hipStreamSynchronize(stream) != hipSuccess) return SKV_ERR_DEVICE;
+    rc = read_back(&status, a.status, 4, stream);
+    if (rc != SKV_OK) return rc;
     skv::timing_collect();
     return status ? SKV_ERR_CORRUPT : SKV_OK;
 }
