@@ -18,7 +18,7 @@ _SRC = os.path.join(_HERE, "skv_oracle.c")
 _LIB = os.path.join(_HERE, "libskv_oracle.so")
 
 BF16, E4M3, INT16 = 1, 2, 3
-RESIDUAL, CHECKERBOARD = 0, 1
+RESIDUAL, CHECKERBOARD, RESIDUAL_EXP = 0, 1, 2
 OK, E_ARG, E_SHAPE, E_CAPACITY, E_CORRUPT, E_TABLES = 0, -1, -2, -3, -4, -5
 
 
@@ -55,6 +55,7 @@ def lib():
             "skvo_zigzag": (u32, [i32]),
             "skvo_unzigzag": (i32, [u32]),
             "skvo_reconstruct": (u32, [u32, i32, ctypes.c_int]),
+            "skvo_exp_class": (u32, [u32, ctypes.c_int, u32]),
             "skvo_dckv_split": (None, [i32, ctypes.POINTER(i32), ctypes.POINTER(i32)]),
             "skvo_dckv_symbol": (u32, [i32, i32, ctypes.POINTER(i32)]),
             "skvo_dckv_reconstruct": (i32, [u32, i32]),
@@ -108,6 +109,16 @@ def residual(t: int, p: int, nbits: int) -> int:
 
 def zigzag(r: int) -> int:
     return lib().skvo_zigzag(r)
+
+
+def exp_class(p: int, dtype: int, base: int) -> int:
+    return lib().skvo_exp_class(p, dtype, base)
+
+
+def blob_bases(blob: bytes) -> np.ndarray:
+    """Class bases (one per slab) of an exponent-mode blob."""
+    nt = int.from_bytes(blob[8:12], "little")
+    return np.frombuffer(blob[64 + 514 * nt:], dtype=np.uint8).copy()
 
 
 def unzigzag(z: int) -> int:

@@ -56,7 +56,7 @@
 #define SKVO_TAB_BYTES 514    /* u16 n + u16 freq[256] */
 
 enum { DT_BF16 = 1, DT_E4M3 = 2, DT_INT16 = 3 };
-enum { MODE_RESIDUAL = 0, MODE_CHECKERBOARD = 1 };
+enum { MODE_RESIDUAL = 0, MODE_CHECKERBOARD = 1, MODE_RESIDUAL_EXP = 2 };
 enum { E_OK = 0, E_ARG = -1, E_SHAPE = -2, E_CAPACITY = -3, E_CORRUPT = -4, E_TABLES = -5 };
 
 /* ------------------------------------------------------------------ */
@@ -136,6 +136,19 @@ uint32_t skvo_reconstruct(uint32_t p, int32_t r, int nbits) {
     int64_t o = ((int64_t)skvo_ord(p, nbits) + r) % span;
     if (o < 0) o += span;
     return skvo_inv_ord((uint32_t)o, nbits);
+}
+
+/* Exponent class of a predictor element (exponent-conditioned residual
+ * tables).  [DCKV] "How it differs": the static per-component model gives way
+ * to models conditioned on what the decoder already knows; [SKC] "Early
+ * results" leaves a finer residual model open.  Reading: the residual of a
+ * value is modelled by a table chosen by its predictor's exponent field
+ * (bf16: bits 14..7, e4m3: bits 6..3), as the class E - base clamped to
+ * [0, 15], with base fixed per (layer, K|V) slab at fit time. */
+uint32_t skvo_exp_class(uint32_t p, int dtype, uint32_t base) {
+    uint32_t e = (dtype == DT_E4M3) ? ((p >> 3) & 0xFu) : ((p >> 7) & 0xFFu);
+    uint32_t c = e < base ? 0u : e - base;
+    return c > 15u ? 15u : c;
 }
 
 /* [DCKV] "How it differs": a predicted mean shifts the Laplace.  Reading:
@@ -344,12 +357,14 @@ typedef struct {
 } skvo_shape;
 
 static int elem_bytes(uint32_t dtype) { return dtype == DT_E4M3 ? 1 : 2; }
+/* Modes that code [layers][kv][tokens][channels] residuals against a predictor. */
+static int residual_like(uint32_t mode) { return mode == MODE_RESIDUAL || mode == MODE_RESIDUAL_EXP; }
 static int elem_bits(uint32_t dtype) { return dtype == DT_E4M3 ? 8 : 16; }
 
 static int shape_ok(const skvo_shape* s) {
     if (s->dtype < DT_BF16 || s->dtype > DT_INT16) return 0;
     if (s->channels == 0 || s->channels % SKVO_LANES) return 0;
-    if (s->mode == MODE_RESIDUAL) {
+    if (residual_like(s->mode)) {
         if (s->dtype == DT_INT16) return 0;
         if (s->layers == 0 || s->kv == 0 || s->tokens == 0) return 0;
         return s->tokens % SKVO_STEPS == 0;
@@ -363,22 +378,29 @@ static int shape_ok(const skvo_shape* s) {
 
 static uint64_t n_tables_of(const skvo_shape* s) {
     if (s->mode == MODE_RESIDUAL) return (uint64_t)s->layers * s->kv * s->channels;
+    if (s->mode == MODE_RESIDUAL_EXP) return (uint64_t)s->layers * s->kv * 16;
     return (uint64_t)s->channels * 16;
+}
+
+/* Bytes after the table records: one class base per slab (exponent mode). */
+static uint64_t n_bases_of(const skvo_shape* s) {
+    return s->mode == MODE_RESIDUAL_EXP ? (uint64_t)s->layers * s->kv : 0;
 }
 
 static uint64_t n_streams_of(const skvo_shape* s) {
     uint64_t cg = s->channels / SKVO_LANES;
-    if (s->mode == MODE_RESIDUAL)
+    if (residual_like(s->mode))
         return (uint64_t)s->layers * s->kv * (s->tokens / SKVO_STEPS) * cg;
     return 2ull * (s->tokens / 2 / SKVO_STEPS) * cg;
 }
 
-uint64_t skvo_blob_bytes(const skvo_shape* s) { return SKVO_HDR + n_tables_of(s) * SKVO_TAB_BYTES; }
+uint64_t skvo_blob_bytes(const skvo_shape* s) { return SKVO_HDR + n_tables_of(s) * SKVO_TAB_BYTES + n_bases_of(s); }
 
 /* Parse a table blob: header fields must match the shape, every table must
  * hold 1..255 direct symbols plus ESC, positive frequencies summing to 2^12
  * and zeros beyond ESC. */
-static int parse_blob(const uint8_t* blob, size_t nbytes, const skvo_shape* s, skvo_table** out) {
+static int parse_blob(const uint8_t* blob, size_t nbytes, const skvo_shape* s, skvo_table** out,
+                      const uint8_t** bases) {
     if (nbytes < SKVO_HDR || memcmp(blob, "SKVT", 4) != 0 || get16(blob + 4) != 1) return E_TABLES;
     if (blob[6] != s->dtype || blob[7] != s->mode) return E_TABLES;
     uint64_t nt = n_tables_of(s);
@@ -402,6 +424,7 @@ static int parse_blob(const uint8_t* blob, size_t nbytes, const skvo_shape* s, s
         table_cum(&t[j]);
     }
     *out = t;
+    *bases = blob + SKVO_HDR + nt * SKVO_TAB_BYTES;   /* n_bases_of(s) bytes */
     return E_OK;
 }
 
@@ -412,7 +435,7 @@ typedef struct { uint64_t slab, tb, cg; } stream_pos;
 
 static stream_pos stream_at(const skvo_shape* s, uint64_t id) {
     uint64_t ncg = s->channels / SKVO_LANES;
-    uint64_t ntb = (s->mode == MODE_RESIDUAL ? s->tokens : s->tokens / 2) / SKVO_STEPS;
+    uint64_t ntb = (residual_like(s->mode) ? s->tokens : s->tokens / 2) / SKVO_STEPS;
     stream_pos sp;
     sp.cg = id % ncg;
     sp.tb = (id / ncg) % ntb;
@@ -423,7 +446,7 @@ static stream_pos stream_at(const skvo_shape* s, uint64_t id) {
 /* Token (row) coded at step k of a stream. */
 static uint64_t token_of(const skvo_shape* s, stream_pos sp, int k) {
     uint64_t j = sp.tb * SKVO_STEPS + (uint64_t)k;
-    if (s->mode == MODE_RESIDUAL) return j;
+    if (residual_like(s->mode)) return j;
     return 2 * j + sp.slab;   /* pass 0: even tokens, pass 1: odd tokens */
 }
 
@@ -441,17 +464,21 @@ static void store_elem(void* a, int dtype, size_t idx, uint32_t v) {
  * residual: aux = predictor cache; checkerboard: aux = side input G and the
  * neighbours come from `tgt` (the true coefficients on the encode side, the
  * already decoded even tokens on the decode side). */
-static void gather_stream(const skvo_shape* s, const skvo_table* tabs, const void* tgt, const void* aux,
-                          uint64_t id, uint32_t* z, const skvo_table** tp, int with_z) {
+static void gather_stream(const skvo_shape* s, const skvo_table* tabs, const uint8_t* bases, const void* tgt,
+                          const void* aux, uint64_t id, uint32_t* z, const skvo_table** tp, int with_z) {
     stream_pos sp = stream_at(s, id);
     size_t C = s->channels;
     for (int k = 0; k < SKVO_STEPS; ++k) {
         uint64_t tok = token_of(s, sp, k);
         for (int i = 0; i < SKVO_LANES; ++i) {
             size_t ch = sp.cg * SKVO_LANES + (size_t)i;
-            if (s->mode == MODE_RESIDUAL) {
+            if (residual_like(s->mode)) {
                 size_t idx = ((size_t)sp.slab * s->tokens + tok) * C + ch;
-                tp[k * SKVO_LANES + i] = &tabs[sp.slab * C + ch];
+                if (s->mode == MODE_RESIDUAL)
+                    tp[k * SKVO_LANES + i] = &tabs[sp.slab * C + ch];
+                else
+                    tp[k * SKVO_LANES + i] =
+                        &tabs[sp.slab * 16 + skvo_exp_class(load_elem(aux, s->dtype, idx), (int)s->dtype, bases[sp.slab])];
                 if (with_z)
                     z[k * SKVO_LANES + i] = skvo_zigzag(skvo_residual(load_elem(tgt, s->dtype, idx),
                                                                       load_elem(aux, s->dtype, idx),
@@ -497,13 +524,13 @@ uint64_t skvo_bound(const skvo_shape* s) {
 
 /* Encode one stream of the arrays into `out` (capacity raw size).  Returns
  * the stream's byte count; *raw is set when the stream is stored raw. */
-static size_t encode_one(const skvo_shape* s, const skvo_table* tabs, const void* tgt, const void* aux,
-                         uint64_t id, uint8_t* out, int* raw) {
+static size_t encode_one(const skvo_shape* s, const skvo_table* tabs, const uint8_t* bases, const void* tgt,
+                         const void* aux, uint64_t id, uint8_t* out, int* raw) {
     uint32_t z[SKVO_SYMS];
     const skvo_table* tp[SKVO_SYMS];
     int eb = elem_bytes(s->dtype);
     size_t rawb = (size_t)SKVO_SYMS * eb;
-    gather_stream(s, tabs, tgt, aux, id, z, tp, 1);
+    gather_stream(s, tabs, bases, tgt, aux, id, z, tp, 1);
     const size_t tcap = 4 * SKVO_LANES + 4 + 4 * (size_t)SKVO_SYMS + 4;
     uint8_t* tmp = (uint8_t*)malloc(tcap);
     size_t nb = skvo_stream_encode(SKVO_STEPS, eb, z, tp, tmp, tcap);
@@ -514,8 +541,8 @@ static size_t encode_one(const skvo_shape* s, const skvo_table* tabs, const void
             uint64_t tok = token_of(s, sp, k);
             for (int i = 0; i < SKVO_LANES; ++i) {
                 size_t ch = sp.cg * SKVO_LANES + (size_t)i;
-                size_t idx = (s->mode == MODE_RESIDUAL) ? ((size_t)sp.slab * s->tokens + tok) * s->channels + ch
-                                                        : tok * s->channels + ch;
+                size_t idx = residual_like(s->mode) ? ((size_t)sp.slab * s->tokens + tok) * s->channels + ch
+                                                    : tok * s->channels + ch;
                 uint32_t v = load_elem(tgt, s->dtype, idx);
                 if (eb == 1) out[k * SKVO_LANES + i] = (uint8_t)v;
                 else put16(out + 2 * (k * SKVO_LANES + i), v);
@@ -539,7 +566,8 @@ int64_t skvo_encode(const uint8_t* blob, size_t blob_bytes, const skvo_shape* s,
     if (!blob || !s || !tgt || !aux) return E_ARG;
     if (!shape_ok(s)) return E_SHAPE;
     skvo_table* tabs = NULL;
-    int rc = parse_blob(blob, blob_bytes, s, &tabs);
+    const uint8_t* bases = NULL;
+    int rc = parse_blob(blob, blob_bytes, s, &tabs, &bases);
     if (rc) return rc;
     uint64_t n = n_streams_of(s);
     size_t rawb = (size_t)SKVO_SYMS * elem_bytes(s->dtype);
@@ -549,7 +577,7 @@ int64_t skvo_encode(const uint8_t* blob, size_t blob_bytes, const skvo_shape* s,
     if (nthreads < 1) nthreads = 1;
 #pragma omp parallel for schedule(dynamic, 64) num_threads(nthreads)
     for (int64_t id = 0; id < (int64_t)n; ++id)
-        size[id] = encode_one(s, tabs, tgt, aux, (uint64_t)id, tmp + (size_t)id * rawb, &raw[id]);
+        size[id] = encode_one(s, tabs, bases, tgt, aux, (uint64_t)id, tmp + (size_t)id * rawb, &raw[id]);
     uint64_t payload = 0;
     for (uint64_t id = 0; id < n; ++id) payload += size[id];
     uint64_t total = SKVO_HDR + 8 * (n + 1) + payload;
@@ -584,8 +612,8 @@ int skvo_container_shape(const uint8_t* in, uint64_t in_bytes, skvo_shape* s) {
     return E_OK;
 }
 
-static int decode_one(const skvo_shape* s, const skvo_table* tabs, const uint8_t* src, uint64_t nb, int raw,
-                      const void* aux, void* out, uint64_t id) {
+static int decode_one(const skvo_shape* s, const skvo_table* tabs, const uint8_t* bases, const uint8_t* src,
+                      uint64_t nb, int raw, const void* aux, void* out, uint64_t id) {
     uint32_t z[SKVO_SYMS];
     const skvo_table* tp[SKVO_SYMS];
     int eb = elem_bytes(s->dtype), nbits = elem_bits(s->dtype);
@@ -595,7 +623,7 @@ static int decode_one(const skvo_shape* s, const skvo_table* tabs, const uint8_t
         if (nb != (uint64_t)SKVO_SYMS * eb) return E_CORRUPT;
     } else {
         /* tables first: in checkerboard mode they depend on the decoded even tokens */
-        gather_stream(s, tabs, out, aux, id, NULL, tp, 0);
+        gather_stream(s, tabs, bases, out, aux, id, NULL, tp, 0);
         int rc = skvo_stream_decode(SKVO_STEPS, eb, src, nb, tp, z);
         if (rc) return rc;
     }
@@ -603,11 +631,11 @@ static int decode_one(const skvo_shape* s, const skvo_table* tabs, const uint8_t
         uint64_t tok = token_of(s, sp, k);
         for (int i = 0; i < SKVO_LANES; ++i) {
             size_t ch = sp.cg * SKVO_LANES + (size_t)i;
-            size_t idx = (s->mode == MODE_RESIDUAL) ? ((size_t)sp.slab * s->tokens + tok) * C + ch : tok * C + ch;
+            size_t idx = residual_like(s->mode) ? ((size_t)sp.slab * s->tokens + tok) * C + ch : tok * C + ch;
             uint32_t v;
             if (raw) {
                 v = (eb == 1) ? src[k * SKVO_LANES + i] : get16(src + 2 * (k * SKVO_LANES + i));
-            } else if (s->mode == MODE_RESIDUAL) {
+            } else if (residual_like(s->mode)) {
                 v = skvo_reconstruct(load_elem(aux, s->dtype, idx), skvo_unzigzag(z[k * SKVO_LANES + i]), nbits);
             } else {
                 int32_t mu = skvo_dckv_mean((const int16_t*)out, (const int16_t*)aux, s->tokens, (uint32_t)C,
@@ -632,11 +660,12 @@ int skvo_decode(const uint8_t* blob, size_t blob_bytes, const uint8_t* in, uint6
     if (!shape_ok(&s)) return E_CORRUPT;
     uint64_t n = n_streams_of(&s);
     if (get64(in + 32) != n) return E_CORRUPT;
-    uint64_t elems = (uint64_t)s.tokens * s.channels * (s.mode == MODE_RESIDUAL ? (uint64_t)s.layers * s.kv : 1);
+    uint64_t elems = (uint64_t)s.tokens * s.channels * (residual_like(s.mode) ? (uint64_t)s.layers * s.kv : 1);
     if (out_bytes < elems * elem_bytes(s.dtype)) return E_CAPACITY;
     if (get64(in + 40) != skvo_fnv1a64(blob, blob_bytes)) return E_TABLES;
     skvo_table* tabs = NULL;
-    rc = parse_blob(blob, blob_bytes, &s, &tabs);
+    const uint8_t* bases = NULL;
+    rc = parse_blob(blob, blob_bytes, &s, &tabs, &bases);
     if (rc) return rc;
     uint64_t payload = get64(in + 48);
     uint64_t head = SKVO_HDR + 8 * (n + 1);
@@ -650,7 +679,7 @@ int skvo_decode(const uint8_t* blob, size_t blob_bytes, const uint8_t* in, uint6
         if (b < a || b > payload) { free(tabs); return E_CORRUPT; }
     }
     if (nthreads < 1) nthreads = 1;
-    int passes = (s.mode == MODE_RESIDUAL) ? 1 : 2;
+    int passes = residual_like(s.mode) ? 1 : 2;
     uint64_t per = n / passes;
     int bad = 0;
     for (int ps = 0; ps < passes; ++ps) {
@@ -660,7 +689,7 @@ int skvo_decode(const uint8_t* blob, size_t blob_bytes, const uint8_t* in, uint6
             uint64_t id = (uint64_t)ps * per + (uint64_t)j;
             uint64_t e = get64(idx + 8 * id);
             uint64_t a = e & mask, b = get64(idx + 8 * (id + 1)) & mask;
-            int r = decode_one(&s, tabs, pay + a, b - a, (int)(e >> 63), aux, out, id);
+            int r = decode_one(&s, tabs, bases, pay + a, b - a, (int)(e >> 63), aux, out, id);
             if (r) bad = 1;
         }
         if (bad) break;
@@ -782,7 +811,7 @@ int skvo_fit_tables(const skvo_shape* s, const void* calib_t, const void* calib_
                     uint8_t* blob, uint64_t cap, uint64_t* blob_bytes) {
     if (!s || !calib_t || !calib_a || !blob_bytes) return E_ARG;
     skvo_shape cs = *s;
-    cs.tokens = (s->mode == MODE_RESIDUAL) ? SKVO_STEPS : 2 * SKVO_STEPS;   /* tokens do not matter here */
+    cs.tokens = residual_like(s->mode) ? SKVO_STEPS : 2 * SKVO_STEPS;   /* tokens do not matter here */
     if (!shape_ok(&cs) || calib_tokens == 0) return E_SHAPE;
     if (s->mode == MODE_CHECKERBOARD && (calib_tokens % 2)) return E_SHAPE;
     uint64_t total = skvo_blob_bytes(s);
@@ -791,6 +820,74 @@ int skvo_fit_tables(const skvo_shape* s, const void* calib_t, const void* calib_
     blob_header(blob, s, calib_tokens, total);
     size_t C = s->channels;
     double p[255];
+    if (s->mode == MODE_RESIDUAL_EXP) {
+        /* Exponent-conditioned tables: per slab, the class base is the first of
+         * the 16 consecutive exponents that hold the most calibration
+         * predictors (the smallest such base on ties); the table of class q
+         * is a Laplace fitted to the slab's calibration values of class q
+         * (the slab's pooled scale when fewer than 64 of them are within
+         * |r| <= 127), with the slab's tail floor and the class's own escape
+         * rate.  Sums run over the slab's values in element order. */
+        int nbits = elem_bits(s->dtype);
+        uint32_t emax = s->dtype == DT_E4M3 ? 15u : 255u;
+        uint64_t slabs = (uint64_t)s->layers * s->kv;
+        uint64_t per_slab = (uint64_t)calib_tokens * C;
+        uint32_t* zs = (uint32_t*)malloc(per_slab * sizeof(uint32_t));
+        int32_t* rs = (int32_t*)malloc(per_slab * sizeof(int32_t));
+        uint8_t* cls = (uint8_t*)malloc(per_slab);
+        if (!zs || !rs || !cls) { free(zs); free(rs); free(cls); return E_ARG; }
+        uint8_t* bases = blob + SKVO_HDR + n_tables_of(s) * SKVO_TAB_BYTES;
+        for (uint64_t sl = 0; sl < slabs; ++sl) {
+            uint64_t hist[256] = {0};
+            for (uint64_t i = 0; i < per_slab; ++i) {
+                size_t idx = (size_t)sl * per_slab + i;
+                uint32_t pv = load_elem(calib_a, s->dtype, idx);
+                rs[i] = skvo_residual(load_elem(calib_t, s->dtype, idx), pv, nbits);
+                zs[i] = skvo_zigzag(rs[i]);
+                hist[(s->dtype == DT_E4M3) ? ((pv >> 3) & 0xFu) : ((pv >> 7) & 0xFFu)] += 1;
+            }
+            uint32_t zq = tail_count(zs, per_slab);
+            uint32_t base = 0;
+            uint64_t best = 0;
+            for (uint32_t b0 = 0; b0 + 15 <= emax; ++b0) {
+                uint64_t cnt = 0;
+                for (uint32_t e = b0; e <= b0 + 15; ++e) cnt += hist[e];
+                if (b0 == 0 || cnt > best) { best = cnt; base = b0; }
+            }
+            bases[sl] = (uint8_t)base;
+            double sum_all = 0.0;
+            uint64_t cnt_all = 0;
+            for (uint64_t i = 0; i < per_slab; ++i) {
+                cls[i] = (uint8_t)skvo_exp_class(load_elem(calib_a, s->dtype, (size_t)sl * per_slab + i), (int)s->dtype, base);
+                if (rs[i] <= 127 && rs[i] >= -127) { sum_all += (double)(rs[i] < 0 ? -rs[i] : rs[i]); ++cnt_all; }
+            }
+            double b_all = cnt_all ? sum_all / (double)cnt_all : 0.0;
+            if (b_all < 0.05) b_all = 0.05;
+            for (uint32_t q = 0; q < 16; ++q) {
+                double sum = 0.0;
+                uint64_t cnt = 0, members = 0;
+                for (uint64_t i = 0; i < per_slab; ++i) {
+                    if (cls[i] != q) continue;
+                    ++members;
+                    if (rs[i] <= 127 && rs[i] >= -127) { sum += (double)(rs[i] < 0 ? -rs[i] : rs[i]); ++cnt; }
+                }
+                double b = cnt >= 64 ? sum / (double)cnt : b_all;
+                if (b < 0.05) b = 0.05;
+                for (uint32_t z = 0; z < 255; ++z) p[z] = skvo_cell_mass((double)skvo_unzigzag(z), 0.0, b);
+                uint32_t n = direct_count(p);
+                if (n < zq) n = zq;
+                uint64_t esc = 0;
+                for (uint64_t i = 0; i < per_slab; ++i)
+                    if (cls[i] == q && zs[i] >= n) ++esc;
+                double pe = ((double)esc + 1.0) / ((double)members + 2.0);
+                build_table(p, n, pe, blob + SKVO_HDR + (sl * 16 + q) * SKVO_TAB_BYTES);
+            }
+        }
+        free(zs);
+        free(rs);
+        free(cls);
+        return E_OK;
+    }
     if (s->mode == MODE_RESIDUAL) {
         int nbits = elem_bits(s->dtype);
         uint64_t slabs = (uint64_t)s->layers * s->kv;
@@ -876,15 +973,19 @@ int64_t skvo_encode_tile(const uint8_t* blob, size_t blob_bytes, const skvo_shap
                          const void* tile_a, const int16_t* nb_l, const int16_t* nb_r, const uint32_t* lane_ids,
                          uint8_t* out, int* raw) {
     skvo_table* tabs = NULL;
-    int rc = parse_blob(blob, blob_bytes, s, &tabs);
+    const uint8_t* bases = NULL;
+    int rc = parse_blob(blob, blob_bytes, s, &tabs, &bases);
     if (rc) return rc;
     uint32_t z[SKVO_SYMS];
     const skvo_table* tp[SKVO_SYMS];
     int eb = elem_bytes(s->dtype), nbits = elem_bits(s->dtype);
     for (int j = 0; j < SKVO_SYMS; ++j) {
         uint32_t lane = lane_ids[j % SKVO_LANES];
-        if (s->mode == MODE_RESIDUAL) {
-            tp[j] = &tabs[lane];
+        if (residual_like(s->mode)) {
+            /* exponent mode: every lane id is the stream's slab */
+            tp[j] = s->mode == MODE_RESIDUAL
+                        ? &tabs[lane]
+                        : &tabs[(size_t)lane * 16 + skvo_exp_class(load_elem(tile_a, s->dtype, j), (int)s->dtype, bases[lane])];
             z[j] = skvo_zigzag(skvo_residual(load_elem(tile_t, s->dtype, j), load_elem(tile_a, s->dtype, j), nbits));
         } else {
             int32_t mu = ((const int16_t*)tile_a)[j], f;
