@@ -51,13 +51,15 @@ typedef enum {
 } skv_status;
 
 typedef enum { SKV_BF16 = 1, SKV_E4M3 = 2, SKV_INT16 = 3 } skv_dtype;
-typedef enum { SKV_RESIDUAL = 0, SKV_CHECKERBOARD = 1 } skv_mode;
+typedef enum { SKV_RESIDUAL = 0, SKV_CHECKERBOARD = 1, SKV_RESIDUAL_EXP = 2 } skv_mode;
 
 /* Cache shape.  Residual mode: arrays are [layers][kv][tokens][channels]
  * of bf16 bit patterns (2 B) or e4m3 codes (1 B), channel fastest; tokens a
  * multiple of 128, channels a multiple of 32.  Checkerboard mode: dtype
  * SKV_INT16, layers = kv = 1, arrays are [tokens][channels] int16 with
- * tokens a multiple of 256.  abi_version must be SKV_ABI_VERSION. */
+ * tokens a multiple of 256.  SKV_RESIDUAL_EXP codes the same arrays as
+ * SKV_RESIDUAL with tables conditioned on the predictor instead of the
+ * channel (see skv_fit_tables).  abi_version must be SKV_ABI_VERSION. */
 typedef struct {
     uint32_t abi_version;
     uint32_t dtype;      /* skv_dtype */
@@ -77,6 +79,17 @@ typedef struct {
  * range of 1..255 symbols (all with cell mass >= 2^-12) and an escape symbol
  * whose probability is the smoothed calibration escape rate, quantized to
  * 12-bit frequencies >= 1 summing to 4096.
+ * SKV_RESIDUAL_EXP (a finer residual model, "Speculative KV coding" page,
+ * "Early results"; conditional models, DCKV page, "How it differs"): one
+ * table per (layer, K|V) slab and predictor exponent class -- the class of a
+ * value is its predictor's exponent field (bf16 bits 14..7, e4m3 bits 6..3)
+ * minus the slab's base, clamped to [0, 15]; the base starts the window of
+ * 16 exponents that holds the most calibration predictors (the lowest such
+ * window); each table is the Laplace above fitted to the slab's calibration
+ * values of its class (the slab's pooled scale when fewer than 64 of them
+ * have |residual| <= 127), with the slab's tail floor and the class's escape
+ * rate.  Its blob has layers * kv * 16 records followed by one base byte per
+ * slab.
  * On success *tables_blob points to a library-owned, immutable blob of
  * *blob_bytes bytes (layout: 64 B header "SKVT" | u16 version | u8 dtype |
  * u8 mode | u32 n_tables | u32 layers | u32 kv | u32 channels | u32
@@ -126,7 +139,8 @@ int skv_decode(const void* tables_blob, const void* d_in, size_t in_bytes, const
  * ("Speculative KV coding" page, section "Where it can be used": prefix
  * caching; VeriCache page, "Application to remote prefix caching"); the
  * container's offset index locates the streams of the range, so nothing
- * outside it is read or decoded.  Residual containers only.
+ * outside it is read or decoded.  Residual-mode containers (either table
+ * kind) only.
  *   token_begin, token_end: the tokens [token_begin, token_end) of every
  *     (layer, K|V) slab; both multiples of 128, token_begin < token_end <=
  *     the container's tokens (else SKV_ERR_SHAPE, also for a checkerboard

@@ -140,7 +140,7 @@ int skv_fit_tables(const skv_shape* s, const void* calib_target, const void* cal
     if (!s || !calib_target || !calib_aux || !tables_blob || !blob_bytes) return SKV_ERR_ARG;
     if (!skv::shape_supported(*s, false) || calib_tokens == 0) return SKV_ERR_SHAPE;
     if (s->mode == SKV_CHECKERBOARD && calib_tokens % 2 != 0) return SKV_ERR_SHAPE;
-    const size_t size = skv::kHeaderBytes + skv::table_count(*s) * skv::kTableRecord;
+    const size_t size = skv::blob_size(*s);
     uint8_t* bytes = static_cast<uint8_t*>(std::malloc(size));
     if (!bytes) return SKV_ERR_NOMEM;
     const int rc = skv::fit_tables_host(*s, calib_target, calib_aux, calib_tokens, bytes, size);
@@ -274,7 +274,7 @@ static int decode_blocks(const void* tables_blob, const void* d_in, size_t in_by
     skv_shape part = s;
     uint32_t tb_base = 0;
     if (range) {
-        if (s.mode != SKV_RESIDUAL || token_begin >= token_end || token_end > s.tokens ||
+        if (s.mode == SKV_CHECKERBOARD || token_begin >= token_end || token_end > s.tokens ||
             token_begin % skv::kSteps != 0 || token_end % skv::kSteps != 0)
             return SKV_ERR_SHAPE;
         part.tokens = token_end - token_begin;

@@ -24,7 +24,7 @@ namespace skv {
 bool shape_supported(const skv_shape& s, bool need_tokens) {
     if (s.abi_version != SKV_ABI_VERSION) return false;
     if (s.channels == 0 || s.channels % kLanes != 0) return false;
-    if (s.mode == SKV_RESIDUAL) {
+    if (s.mode == SKV_RESIDUAL || s.mode == SKV_RESIDUAL_EXP) {
         if (s.dtype != SKV_BF16 && s.dtype != SKV_E4M3) return false;
         if (s.layers == 0 || s.kv == 0) return false;
         return !need_tokens || (s.tokens > 0 && s.tokens % kSteps == 0);
@@ -37,12 +37,19 @@ bool shape_supported(const skv_shape& s, bool need_tokens) {
 }
 
 uint64_t table_count(const skv_shape& s) {
-    return s.mode == SKV_RESIDUAL ? uint64_t(s.layers) * s.kv * s.channels : uint64_t(s.channels) * 16;
+    if (s.mode == SKV_RESIDUAL) return uint64_t(s.layers) * s.kv * s.channels;
+    if (s.mode == SKV_RESIDUAL_EXP) return uint64_t(s.layers) * s.kv * kExpClasses;
+    return uint64_t(s.channels) * 16;
+}
+
+uint64_t blob_size(const skv_shape& s) {
+    const uint64_t bases = s.mode == SKV_RESIDUAL_EXP ? uint64_t(s.layers) * s.kv : 0;
+    return kHeaderBytes + table_count(s) * kTableRecord + bases;
 }
 
 uint64_t stream_count(const skv_shape& s) {
     uint64_t groups = s.channels / kLanes;
-    if (s.mode == SKV_RESIDUAL) return uint64_t(s.layers) * s.kv * (s.tokens / kSteps) * groups;
+    if (s.mode != SKV_CHECKERBOARD) return uint64_t(s.layers) * s.kv * (s.tokens / kSteps) * groups;
     return 2 * uint64_t(s.tokens / (2 * kSteps)) * groups;
 }
 
@@ -172,7 +179,7 @@ uint32_t slab_tail_floor(const std::vector<uint64_t>& above_count_by_z, uint64_t
 int fit_tables_host(const skv_shape& s, const void* calib_t, const void* calib_a, uint32_t calib_tokens,
                     uint8_t* blob, size_t blob_bytes) {
     const uint64_t nt = table_count(s);
-    if (blob_bytes != kHeaderBytes + nt * kTableRecord) return SKV_ERR_ARG;
+    if (blob_bytes != blob_size(s)) return SKV_ERR_ARG;
     std::memset(blob, 0, kHeaderBytes);
     std::memcpy(blob, "SKVT", 4);
     wr16(blob + 4, 1);
@@ -187,6 +194,80 @@ int fit_tables_host(const skv_shape& s, const void* calib_t, const void* calib_a
     uint8_t* rec = blob + kHeaderBytes;
     const uint32_t C = s.channels, N = calib_tokens;
     double mass[255];
+
+    if (s.mode == SKV_RESIDUAL_EXP) {
+        // One table per (slab, predictor exponent class).  The class base of a
+        // slab starts the window of 16 exponents that holds the most
+        // calibration predictors (the lowest such window); the table of a
+        // class is the Laplace of the class's calibration residuals (the
+        // slab's pooled scale below 64 in-range values), with the slab's
+        // tail floor and the class's escape rate.  Sums run in element order.
+        const int nbits = s.dtype == SKV_E4M3 ? 8 : 16;
+        const uint32_t emax = s.dtype == SKV_E4M3 ? 15u : 255u;
+        const uint64_t slabs = uint64_t(s.layers) * s.kv;
+        const size_t per = size_t(N) * C;
+        auto elem = [&](const void* a, size_t i) -> uint32_t {
+            return nbits == 8 ? static_cast<const uint8_t*>(a)[i] : static_cast<const uint16_t*>(a)[i];
+        };
+        std::vector<int32_t> r(per);
+        std::vector<uint8_t> cls(per);
+        std::vector<uint64_t> above(257);
+        uint8_t* bases = blob + kHeaderBytes + nt * kTableRecord;
+        for (uint64_t sl = 0; sl < slabs; ++sl) {
+            std::fill(above.begin(), above.end(), 0ull);
+            uint64_t hist[256] = {};
+            for (size_t i = 0; i < per; ++i) {
+                const uint32_t pv = elem(calib_a, sl * per + i);
+                r[i] = ordered_residual(elem(calib_t, sl * per + i), pv, nbits);
+                above[std::min<uint32_t>(zig_of(r[i], nbits), 255u)] += 1;
+                hist[exp_field(pv, s.dtype)] += 1;
+            }
+            for (int z = 254; z >= 0; --z) above[size_t(z)] += above[size_t(z) + 1];
+            const uint32_t floor_n = slab_tail_floor(above, per);
+            uint32_t base = 0;
+            uint64_t best = 0, win = 0;
+            for (uint32_t e = 0; e < 16; ++e) win += hist[e];
+            best = win;
+            for (uint32_t b0 = 1; b0 + 15 <= emax; ++b0) {
+                win += hist[b0 + 15] - hist[b0 - 1];
+                if (win > best) {
+                    best = win;
+                    base = b0;
+                }
+            }
+            bases[sl] = uint8_t(base);
+            double acc_all = 0.0;
+            uint64_t used_all = 0;
+            for (size_t i = 0; i < per; ++i) {
+                cls[i] = uint8_t(exp_class(elem(calib_a, sl * per + i), s.dtype, base));
+                if (std::abs(r[i]) <= 127) {
+                    acc_all += double(std::abs(r[i]));
+                    ++used_all;
+                }
+            }
+            const double b_all = std::max(used_all ? acc_all / double(used_all) : 0.0, 0.05);
+            for (uint32_t q = 0; q < kExpClasses; ++q) {
+                double acc = 0.0;
+                uint64_t used = 0, members = 0;
+                for (size_t i = 0; i < per; ++i) {
+                    if (cls[i] != q) continue;
+                    ++members;
+                    if (std::abs(r[i]) <= 127) {
+                        acc += double(std::abs(r[i]));
+                        ++used;
+                    }
+                }
+                const double b = std::max(used >= 64 ? acc / double(used) : b_all, 0.05);
+                masses_for(0.0, b, mass);
+                const Record R = make_record(mass, 0.0, floor_n);
+                uint64_t esc = 0;
+                for (size_t i = 0; i < per; ++i) esc += cls[i] == q && zig_of(r[i], nbits) >= R.n;
+                const double pe = (double(esc) + 1.0) / (double(members) + 2.0);
+                put_record(rec + (sl * kExpClasses + q) * kTableRecord, make_record(mass, pe, floor_n));
+            }
+        }
+        return SKV_OK;
+    }
 
     if (s.mode == SKV_RESIDUAL) {
         const int nbits = s.dtype == SKV_E4M3 ? 8 : 16;
@@ -268,7 +349,7 @@ int validate_blob(const uint8_t* b, size_t bytes) {
     skv_shape s{SKV_ABI_VERSION, b[6], b[7], rd32(b + 12), rd32(b + 16), 0, rd32(b + 20)};
     if (!shape_supported(s, false)) return SKV_ERR_TABLES;
     const uint64_t nt = table_count(s);
-    if (rd32(b + 8) != nt || rd64(b + 32) != bytes || bytes != kHeaderBytes + nt * kTableRecord) return SKV_ERR_TABLES;
+    if (rd32(b + 8) != nt || rd64(b + 32) != bytes || bytes != blob_size(s)) return SKV_ERR_TABLES;
     for (uint64_t j = 0; j < nt; ++j) {
         const uint8_t* r = b + kHeaderBytes + j * kTableRecord;
         const uint32_t n = rd16(r);

@@ -29,9 +29,23 @@ constexpr int kMaxTimedKernels = 16;
 
 inline uint32_t elem_bytes(uint32_t dtype) { return dtype == SKV_E4M3 ? 1u : 2u; }
 
+// Exponent-conditioned mode: a value's table is chosen by its predictor's
+// exponent field (bf16 bits 14..7, e4m3 bits 6..3) as the class E - base,
+// clamped to [0, 15], with one base per (layer, K|V) slab.
+constexpr uint32_t kExpClasses = 16;
+__host__ __device__ inline uint32_t exp_field(uint32_t p, uint32_t dtype) {
+    return dtype == SKV_E4M3 ? (p >> 3) & 0xFu : (p >> 7) & 0xFFu;
+}
+__host__ __device__ inline uint32_t exp_class(uint32_t p, uint32_t dtype, uint32_t base) {
+    const uint32_t e = exp_field(p, dtype);
+    const uint32_t c = e < base ? 0u : e - base;
+    return c < kExpClasses - 1 ? c : kExpClasses - 1;
+}
+
 // Shape checks shared by fit / encode / decode.
 bool shape_supported(const skv_shape& s, bool need_tokens);
 uint64_t table_count(const skv_shape& s);
+uint64_t blob_size(const skv_shape& s);      // header + records (+ class bases)
 uint64_t stream_count(const skv_shape& s);
 uint64_t element_count(const skv_shape& s);
 
@@ -58,6 +72,7 @@ struct DevTables {
     uint32_t* fc = nullptr;        // [n_tables][256] freq | cum<<16
     uint8_t* slot = nullptr;       // [n_tables][4096] slot -> symbol
     uint8_t* half = nullptr;       // checkerboard blobs: [n_tables][2048] symbol of every even slot
+    uint8_t* base = nullptr;       // exponent-mode blobs: [slabs] class base
 };
 
 struct EncodeLaunch {

@@ -40,7 +40,7 @@ __device__ __forceinline__ Geo geometry(const skv_shape& s) {
     g.C = s.channels;
     g.T = s.tokens;
     g.ncg = s.channels / kLanes;
-    g.ntb = (s.mode == SKV_RESIDUAL ? s.tokens : s.tokens / 2) / kSteps;
+    g.ntb = (s.mode != SKV_CHECKERBOARD ? s.tokens : s.tokens / 2) / kSteps;
     return g;
 }
 
@@ -179,18 +179,19 @@ __global__ __launch_bounds__(256) void encode_streams(EncodeLaunch a, DevTables 
     uint32_t x = kStateLow, cnt = 0, ecnt = 0;
     for (int k = kSteps - 1; k >= 0; --k) {
         uint32_t z, table;
-        if (MODE == SKV_RESIDUAL) {
+        if (MODE != SKV_CHECKERBOARD) {
             const size_t idx = (size_t(slab) * g.T + size_t(tb) * kSteps + k) * g.C + ch;
+            uint32_t pv;
             if (DT == SKV_E4M3) {
                 const uint32_t tv = static_cast<const uint8_t*>(a.target)[idx];
-                const uint32_t pv = static_cast<const uint8_t*>(a.aux)[idx];
+                pv = static_cast<const uint8_t*>(a.aux)[idx];
                 z = zig8((ord8(tv) - ord8(pv)) & 0xFFu);
             } else {
                 const uint32_t tv = static_cast<const uint16_t*>(a.target)[idx];
-                const uint32_t pv = static_cast<const uint16_t*>(a.aux)[idx];
+                pv = static_cast<const uint16_t*>(a.aux)[idx];
                 z = zig16((ord16(tv) - ord16(pv)) & 0xFFFFu);
             }
-            table = res_table;
+            table = MODE == SKV_RESIDUAL ? res_table : slab * kExpClasses + exp_class(pv, DT, t.base[slab]);
         } else {
             const uint32_t tok = 2u * (tb * kSteps + uint32_t(k)) + slab;
             const int16_t* coef = static_cast<const int16_t*>(a.target);
@@ -482,8 +483,8 @@ __global__ __launch_bounds__(256) void copy_streams(EncodeLaunch a) {
         constexpr uint32_t PER_ROW = kLanes * EB / 16;          // 16-byte pieces per row segment
         for (uint32_t e = lane; e < kSteps * PER_ROW; e += 64) {
             const uint32_t k = e / PER_ROW, piece = e % PER_ROW;
-            const uint32_t tok = MODE == SKV_RESIDUAL ? tb * kSteps + k : 2u * (tb * kSteps + k) + slab;
-            const size_t idx = MODE == SKV_RESIDUAL ? (size_t(slab) * g.T + tok) * g.C + cg * kLanes
+            const uint32_t tok = MODE != SKV_CHECKERBOARD ? tb * kSteps + k : 2u * (tb * kSteps + k) + slab;
+            const size_t idx = MODE != SKV_CHECKERBOARD ? (size_t(slab) * g.T + tok) * g.C + cg * kLanes
                                                     : size_t(tok) * g.C + cg * kLanes;
             const uint4 v = *reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(a.target) + idx * EB + piece * 16);
             *reinterpret_cast<uint4*>(dst + e * 16) = v;
@@ -593,7 +594,7 @@ __global__ __launch_bounds__(256) void decode_streams(DecodeLaunch a, DevTables 
     constexpr uint32_t RAW = kSyms * EB;
     const uint64_t* index = a.index;
     const uint8_t* pay = a.pay;
-    const uint64_t ip = MODE == SKV_RESIDUAL ? index_pos(a, slab, tb, cg, g.ncg) : sid;
+    const uint64_t ip = MODE != SKV_CHECKERBOARD ? index_pos(a, slab, tb, cg, g.ncg) : sid;
     const uint64_t e0 = index[ip], e1 = index[ip + 1];
     const uint64_t off = e0 & ~kRawBit, end = e1 & ~kRawBit;
     bool bad = false;
@@ -603,7 +604,7 @@ __global__ __launch_bounds__(256) void decode_streams(DecodeLaunch a, DevTables 
     }
     const uint64_t size = end - off;
     auto out_index = [&](uint32_t k) -> size_t {
-        if (MODE == SKV_RESIDUAL) return (size_t(slab) * g.T + size_t(tb) * kSteps + k) * g.C + ch;
+        if (MODE != SKV_CHECKERBOARD) return (size_t(slab) * g.T + size_t(tb) * kSteps + k) * g.C + ch;
         return size_t(2u * (tb * kSteps + k) + slab) * g.C + ch;
     };
     if (e0 & kRawBit) {
@@ -641,6 +642,10 @@ __global__ __launch_bounds__(256) void decode_streams(DecodeLaunch a, DevTables 
         int32_t kk = 0;
         if (MODE == SKV_RESIDUAL) {
             table = res_table;
+        } else if (MODE == SKV_RESIDUAL_EXP) {
+            const uint32_t pv = DT == SKV_E4M3 ? uint32_t(static_cast<const uint8_t*>(a.aux)[oi])
+                                               : uint32_t(static_cast<const uint16_t*>(a.aux)[oi]);
+            table = slab * kExpClasses + exp_class(pv, DT, t.base[slab]);
         } else {
             const uint32_t tok = 2u * (tb * kSteps + k) + slab;
             const int16_t* dec = static_cast<const int16_t*>(a.out);
@@ -674,7 +679,7 @@ __global__ __launch_bounds__(256) void decode_streams(DecodeLaunch a, DevTables 
             }
             ep += __popc(mine);
         }
-        if (MODE == SKV_RESIDUAL) {
+        if (MODE != SKV_CHECKERBOARD) {
             if (DT == SKV_E4M3) {
                 const uint32_t pv = static_cast<const uint8_t*>(a.aux)[oi];
                 static_cast<uint8_t*>(a.out)[oi] = uint8_t(unord8((ord8(pv) + unzig(z)) & 0xFFu));
@@ -3033,7 +3038,7 @@ hipError_t decode_all(const DecodeLaunch& a, const DevTables& t, hipStream_t st)
         });
         return hipGetLastError();
     }
-    const uint64_t passes = MODE == SKV_RESIDUAL ? 1 : 2;
+    const uint64_t passes = MODE == SKV_CHECKERBOARD ? 2 : 1;
     const uint64_t per = a.n_streams / passes;
     const uint32_t grid = uint32_t((per + kStreamsPerBlock - 1) / kStreamsPerBlock);
     for (uint64_t ps = 0; ps < passes; ++ps)
@@ -3064,6 +3069,10 @@ hipError_t build_dev_tables(const uint8_t* blob, DevTables* t, hipStream_t st) {
     if (e == hipSuccess) e = hipMalloc(&t->fc, size_t(nt) * 256 * 4 + 16);   // + one entry read past the last row
     if (e == hipSuccess) e = hipMalloc(&t->slot, size_t(nt) * kM);
     if (e == hipSuccess && blob[7] == SKV_CHECKERBOARD) e = hipMalloc(&t->half, size_t(nt) * (kM / 2));
+    const size_t nbase = blob[7] == SKV_RESIDUAL_EXP ? size_t(rd32(blob + 12)) * rd32(blob + 16) : 0;
+    if (e == hipSuccess && nbase) e = hipMalloc(&t->base, nbase);
+    if (e == hipSuccess && nbase)
+        e = hipMemcpyAsync(t->base, blob + kHeaderBytes + size_t(nt) * kTableRecord, nbase, hipMemcpyHostToDevice, st);
     if (e == hipSuccess) e = hipMemcpyAsync(rec, blob + kHeaderBytes, size_t(nt) * kTableRecord, hipMemcpyHostToDevice, st);
     if (e == hipSuccess) {
         hipLaunchKernelGGL(expand_tables, dim3(nt), dim3(256), 0, st, rec, t->n, t->enc, t->fc, t->slot, t->half);
@@ -3084,17 +3093,24 @@ void free_dev_tables(DevTables* t) {
     if (t->fc) (void)hipFree(t->fc);
     if (t->slot) (void)hipFree(t->slot);
     if (t->half) (void)hipFree(t->half);
+    if (t->base) (void)hipFree(t->base);
     *t = DevTables{};
 }
 
 hipError_t launch_encode(const EncodeLaunch& a, const DevTables& t, hipStream_t st) {
     if (a.shape.mode == SKV_CHECKERBOARD) return encode_all<SKV_INT16, SKV_CHECKERBOARD>(a, t, st);
+    if (a.shape.mode == SKV_RESIDUAL_EXP)
+        return a.shape.dtype == SKV_E4M3 ? encode_all<SKV_E4M3, SKV_RESIDUAL_EXP>(a, t, st)
+                                         : encode_all<SKV_BF16, SKV_RESIDUAL_EXP>(a, t, st);
     if (a.shape.dtype == SKV_E4M3) return encode_all<SKV_E4M3, SKV_RESIDUAL>(a, t, st);
     return encode_all<SKV_BF16, SKV_RESIDUAL>(a, t, st);
 }
 
 hipError_t launch_decode(const DecodeLaunch& a, const DevTables& t, hipStream_t st) {
     if (a.shape.mode == SKV_CHECKERBOARD) return decode_all<SKV_INT16, SKV_CHECKERBOARD>(a, t, st);
+    if (a.shape.mode == SKV_RESIDUAL_EXP)
+        return a.shape.dtype == SKV_E4M3 ? decode_all<SKV_E4M3, SKV_RESIDUAL_EXP>(a, t, st)
+                                         : decode_all<SKV_BF16, SKV_RESIDUAL_EXP>(a, t, st);
     if (a.shape.dtype == SKV_E4M3) return decode_all<SKV_E4M3, SKV_RESIDUAL>(a, t, st);
     return decode_all<SKV_BF16, SKV_RESIDUAL>(a, t, st);
 }

@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(_HERE, "libskv.so")
 
 ABI_VERSION = 1
 BF16, E4M3, INT16 = 1, 2, 3
-RESIDUAL, CHECKERBOARD = 0, 1
+RESIDUAL, CHECKERBOARD, RESIDUAL_EXP = 0, 1, 2
 OK, ERR_ARG, ERR_SHAPE, ERR_CAPACITY, ERR_CORRUPT, ERR_TABLES, ERR_DEVICE, ERR_NOMEM = 0, -1, -2, -3, -4, -5, -6, -7
 
 

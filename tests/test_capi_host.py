@@ -52,6 +52,19 @@ def test_fit_matches_oracle_residual(skv, orc, cid, layers):
     assert got == want
 
 
+@pytest.mark.parametrize("cid,layers", [(0, 1), (1, 2), (2, 2), (3, 1)])
+def test_fit_matches_oracle_exponent_mode(skv, orc, cid, layers):
+    cfg = gen.CONFIGS[cid].with_tokens(256, layers=layers)
+    ct, cp = _residual_calib(cfg)
+    dt = skv.E4M3 if cfg.dtype == "e4m3" else skv.BF16
+    tabs = skv.fit_tables(dt, skv.RESIDUAL_EXP, cfg.layers, cfg.kv, cfg.channels, ct, cp, 256)
+    shape = orc.make_shape(dt, orc.RESIDUAL_EXP, cfg.layers, cfg.kv, 128, cfg.channels)
+    assert tabs.bytes() == orc.fit_tables(shape, ct, cp, 256)
+    # the blob loads back through validation
+    again = skv.load_tables(tabs.bytes())
+    assert again.bytes() == tabs.bytes()
+
+
 def test_fit_matches_oracle_checkerboard(skv, orc):
     cfg = gen.CONFIGS[4].with_tokens(256, channels=256)
     cc, cg = gen.dckv_draw(cfg, gen.CALIB, tokens=256)

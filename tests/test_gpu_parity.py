@@ -206,6 +206,61 @@ def test_unaligned_buffers(skv, orc, dtype):
     assert torch.equal(out, t)
 
 
+def exp_case(skv, orc, cfg):
+    t, p = gen.residual_array(cfg, device="cuda")
+    ct, cp = gen.residual_array(cfg, gen.CALIB, tokens=256)
+    dt = _dt(cfg, skv)
+    tabs = skv.fit_tables(dt, skv.RESIDUAL_EXP, cfg.layers, cfg.kv, cfg.channels, ct.numpy(), cp.numpy(), 256)
+    oshape = orc.make_shape(dt, orc.RESIDUAL_EXP, cfg.layers, cfg.kv, cfg.tokens, cfg.channels)
+    return t, p, tabs, oshape
+
+
+@pytest.mark.parametrize("cid", [0, 2])
+def test_exponent_mode_small(skv, orc, cid):
+    """Exponent-conditioned tables: containers byte-identical to the oracle's,
+    exact decode of both, and a range decode."""
+    cfg = gen.CONFIGS[cid].with_tokens(640, layers=2, channels=192)
+    t, p, tabs, oshape = exp_case(skv, orc, cfg)
+    want = full_compare(skv, orc, t, p, tabs, oshape, f"exponent mode {cfg.dtype}")
+    assert want[7] == orc.RESIDUAL_EXP
+    cont = torch.from_numpy(np.frombuffer(want, dtype=np.uint8).copy()).cuda()
+    part = skv.decode_range(tabs, cont, 256, 512, p[:, :, 256:512].contiguous())
+    assert torch.equal(part, t[:, :, 256:512])
+
+
+def test_exponent_mode_full_size_e4m3(skv, orc):
+    """The Qwen3-8B-shaped e4m3 cache with exponent-conditioned tables: sampled
+    streams equal the oracle's, the round trip is exact, and the container is
+    smaller than with per-channel tables."""
+    cfg = gen.CONFIGS[2]
+    say(f"[parity] exponent mode cfg2: generating {cfg.values} values on GPU")
+    t, p, tabs, oshape = exp_case(skv, orc, cfg)
+    cont = skv.encode(tabs, t, p)
+    torch.cuda.synchronize()
+    n = orc.n_streams(oshape)
+    head = 64 + 8 * (n + 1)
+    host_head = cont[:head].cpu().numpy().tobytes()
+    idx = np.frombuffer(host_head[64:], dtype=np.uint64)
+    offs = idx & np.uint64((1 << 63) - 1)
+    assert int(offs[-1]) == cont.numel() - head
+    ratio = cfg.raw_bytes / cont.numel()
+    say(f"[parity] exponent mode cfg2: ratio {ratio:.4f}")
+    assert ratio > 4.5
+    ncg, ntb, blob = cfg.channels // 32, cfg.tokens // 128, tabs.bytes()
+    for s in _sample_ids(n, 32, 2):
+        cg, rest = s % ncg, s // ncg
+        tb, slab = rest % ntb, rest // ntb
+        l, k = divmod(slab, cfg.kv)
+        sl = (l, k, slice(tb * 128, tb * 128 + 128), slice(cg * 32, cg * 32 + 32))
+        lanes = np.full(32, slab, dtype=np.uint32)            # exponent mode: the stream's slab
+        data, raw = orc.encode_tile(blob, oshape, t[sl].cpu().numpy(), p[sl].cpu().numpy(), lanes)
+        assert bool(int(idx[s]) >> 63) == raw, s
+        assert cont[head + int(offs[s]):head + int(offs[s + 1])].cpu().numpy().tobytes() == data, s
+    say("[parity] exponent mode cfg2: sampled streams identical; decoding")
+    back = skv.decode(tabs, cont, p)
+    assert torch.equal(back, t)
+
+
 RANGES = [(0, 1024), (0, 128), (896, 1024), (256, 640), (128, 1024)]
 
 
