@@ -47,6 +47,8 @@ def main() -> int:
     ap.add_argument("--config", type=int, default=2, help="workload id (2 = Qwen3-8B-shaped e4m3)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target length of the CPU-oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--tables", choices=["channel", "exponent"], default="channel",
+                    help="residual tables per channel (default) or per slab and predictor exponent class")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also time a plain device copy of the cache (HBM ceiling; counter scale reference)")
     args = ap.parse_args()
@@ -69,6 +71,7 @@ def main() -> int:
     cfg = gen.CONFIGS[args.config]
     cb = cfg.dtype == "int16"                  # DCKV coefficients (checkerboard mode)
 
+    wl = cfg.name + ("-exponent-tables" if args.tables == "exponent" and not cb else "")
     log(f"generating {cfg.name}: {cfg.values} values on the GPU")
     t0 = time.perf_counter()
     if cb:
@@ -85,7 +88,8 @@ def main() -> int:
                               gen.CALIB_TOKENS)
     else:
         dt = skv.E4M3 if cfg.dtype == "e4m3" else skv.BF16
-        tabs = skv.fit_tables(dt, skv.RESIDUAL, cfg.layers, cfg.kv, cfg.channels, ct.cpu().numpy(),
+        mode = skv.RESIDUAL_EXP if args.tables == "exponent" else skv.RESIDUAL
+        tabs = skv.fit_tables(dt, mode, cfg.layers, cfg.kv, cfg.channels, ct.cpu().numpy(),
                               cp.cpu().numpy(), gen.CALIB_TOKENS)
     fit_s = time.perf_counter() - t0
     del ct, cp
@@ -173,7 +177,7 @@ def main() -> int:
     if os.path.exists(TRAFFIC_FILE):
         with open(TRAFFIC_FILE) as f:
             tr = json.load(f)                                   # {workload: {kernel: counters}}
-        ent = tr.get(cfg.name, {}).get(dom)
+        ent = tr.get(wl, {}).get(dom)
         if ent and ent.get("kernel_sha") == kernel_sha():
             traffic = ent["bytes_per_launch"]
     roofline = {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
@@ -218,7 +222,7 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": "u32",
         "data": "synthetic",
-        "config": {"workload": cfg.name, "shape": f"[{cfg.layers}][{cfg.kv}][{cfg.tokens}][{cfg.channels}]",
+        "config": {"workload": wl, "tables": None if cb else args.tables, "shape": f"[{cfg.layers}][{cfg.kv}][{cfg.tokens}][{cfg.channels}]",
                    "element": cfg.dtype, "values": cfg.values, "raw_bytes": raw_bytes, "streams": n_streams,
                    "step": "encode + decode of the whole cache", "container_bytes": cont_bytes},
         "ratio": round(ratio, 4),
@@ -247,20 +251,26 @@ def cpu_baseline(cfg, tabs, tgt, prd, seconds):
 
     threads = max(1, min(16, len(os.sched_getaffinity(0))))
     blob = tabs.bytes()
-    per_layer_tables = cfg.kv * cfg.channels
+    exp = tabs.mode == oracle.RESIDUAL_EXP
+    per_layer_tables = cfg.kv * (16 if exp else cfg.channels)
     rec = 514
+    n_tables = cfg.layers * per_layer_tables
     done_bytes, spent, layers = 0, 0.0, 0
     for layer in range(cfg.layers):
         hdr = bytearray(blob[:64])
         hdr[8:12] = per_layer_tables.to_bytes(4, "little")
         hdr[12:16] = (1).to_bytes(4, "little")
-        total = 64 + per_layer_tables * rec
+        total = 64 + per_layer_tables * rec + (cfg.kv if exp else 0)
         hdr[32:40] = total.to_bytes(8, "little")
         sub = bytes(hdr) + blob[64 + layer * per_layer_tables * rec:64 + (layer + 1) * per_layer_tables * rec]
+        if exp:                                                   # the layer's class bases
+            b0 = 64 + n_tables * rec + layer * cfg.kv
+            sub += blob[b0:b0 + cfg.kv]
         t = tgt[layer:layer + 1].cpu().numpy()
         p = prd[layer:layer + 1].cpu().numpy()
         dt = oracle.E4M3 if cfg.dtype == "e4m3" else oracle.BF16
-        shape = oracle.make_shape(dt, oracle.RESIDUAL, 1, cfg.kv, cfg.tokens, cfg.channels)
+        shape = oracle.make_shape(dt, oracle.RESIDUAL_EXP if exp else oracle.RESIDUAL, 1, cfg.kv, cfg.tokens,
+                                  cfg.channels)
         a = time.perf_counter()
         c = oracle.encode(sub, shape, t, p, threads=threads)
         back = oracle.decode(sub, c, p, t, threads=threads)

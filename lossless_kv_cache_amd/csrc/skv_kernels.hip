@@ -1975,6 +1975,17 @@ __host__ __device__ constexpr uint32_t dec_e4m3_rings(uint32_t fs) {
 __host__ __device__ constexpr uint32_t dec_e4m3_lds(uint32_t fs) {
     return dec_e4m3_rings(fs) + kDecStreams * (2 * kDecRing + kDecTile * kLanes);
 }
+// Exponent-class tables: maps [16 classes][4096] | 4096 - f [16][128] u16 | start [16][128] u16 | rings |
+// tiles | class tiles [streams][32 lanes][4 steps] | n [16].  Rows cover residual bytes 64..191: byte 64
+// (residual -64, zigzag 127) holds the escape symbol, which with at most 126 direct symbols is never a
+// direct one, so escaped positions read 0x40 in every class.
+constexpr uint32_t kExpRows = 128;
+constexpr uint32_t kExpRowBytes = kExpClasses * kExpRows * 2;
+constexpr uint32_t kExpEscByte = 128u - kExpRows / 2;
+__host__ __device__ constexpr uint32_t dec_exp_rings() { return (kExpClasses * kM + 2 * kExpRowBytes + 255) & ~255u; }
+__host__ __device__ constexpr uint32_t dec_exp_lds() {
+    return dec_exp_rings() + kDecStreams * (2 * kDecRing + 2 * kDecTile * kLanes) + kExpClasses;
+}
 
 // bytewise helpers on 4 packed e4m3 codes / symbols
 __device__ __forceinline__ uint32_t add8x4(uint32_t a, uint32_t b) {
@@ -2031,27 +2042,44 @@ struct DecChain {
 // which keeps the ring read unconditional.  `pre` runs before the first
 // step's map reads and `post` right after them, so work on the previous tile
 // fills the wait for those reads.
-template <bool GLOBAL, uint32_t FS, class Pre, class Post>
+//
+// EXP (exponent-class tables): the maps and rows belong to the step's class,
+// taken from cw (the lane's class byte of every step, class << 4): the map
+// of class q sits at q * 4096 from mapb and its rows at q * 256 from gb.
+template <bool GLOBAL, uint32_t FS, bool EXP = false, class Pre, class Post>
 __device__ __forceinline__ void dec_tile_steps(DecState (&st)[kDecChains], const DecLane& L,
                                                const DecChain (&ch)[kDecChains], uint32_t (&sy)[kDecChains][kDecTile],
-                                               Pre&& pre, Post&& post) {
+                                               Pre&& pre, Post&& post, const uint32_t (&cw)[kDecChains] = {}) {
 #pragma unroll
     for (uint32_t r = 0; r < kDecTile; ++r) {
         uint32_t sym[kDecChains], g[kDecChains], cu[kDecChains], xn[kDecChains], idx[kDecChains], w[kDecChains];
+        uint32_t mb[kDecChains], rb[kDecChains];
         uint64_t mw[kDecChains];
+#pragma unroll
+        for (uint32_t c = 0; c < kDecChains; ++c) {
+            if constexpr (EXP) {
+                const uint32_t q = __builtin_amdgcn_ubfe(cw[c], 8 * r + 4, 4);
+                mb[c] = (q << 12) + L.mapb;
+                rb[c] = q * (kExpRows * 2) + L.gb;
+            } else {
+                mb[c] = L.mapb;
+                rb[c] = L.gb;
+            }
+        }
         if (r == 0) pre();
 #pragma unroll
         for (uint32_t c = 0; c < kDecChains; ++c)
-            sym[c] = *reinterpret_cast<const lds_u8*>((st[c].x & (kM - 1u)) | L.mapb);
+            sym[c] = *reinterpret_cast<const lds_u8*>((st[c].x & (kM - 1u)) | mb[c]);
         if (r == 0) post();
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (uint32_t c = 0; c < kDecChains; ++c) {
             // the byte load already zero-extends; an empty asm hides the extension from the compiler
             asm("" : "+v"(sym[c]));
-            const uint32_t ga = (sym[c] << 6) + L.gb;
-            g[c] = *reinterpret_cast<const lds_u16*>(ga);                         // 4096 - f
-            cu[c] = *reinterpret_cast<const lds_u16*>(ga + FS * kLanes * 2);       // start
+            // rows: [residual byte][32 lanes] per lane, or [class][128 residual bytes] shared
+            const uint32_t ga = EXP ? (sym[c] << 1) + rb[c] : (sym[c] << 6) + rb[c];
+            g[c] = *reinterpret_cast<const lds_u16*>(ga);                                       // 4096 - f
+            cu[c] = *reinterpret_cast<const lds_u16*>(ga + (EXP ? kExpRowBytes : FS * kLanes * 2));  // start
         }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -2074,12 +2102,15 @@ __device__ __forceinline__ void dec_tile_steps(DecState (&st)[kDecChains], const
     }
 }
 
-template <uint32_t FS>
+template <uint32_t FS, bool EXP = false>
 __global__ __launch_bounds__(1024, 1) void decode_e4m3(DecodeLaunch a, DevTables t, LdsGeo lg) {
-    constexpr uint32_t OFF_G = kLanes * kM;
-    constexpr uint32_t OFF_C = OFF_G + FS * kLanes * 2;
-    constexpr uint32_t OFF_R = dec_e4m3_rings(FS);
+    static_assert(!EXP || FS == kExpRows, "exponent-class rows cover 128 residual bytes");
+    constexpr uint32_t OFF_G = EXP ? kExpClasses * kM : kLanes * kM;
+    constexpr uint32_t OFF_C = EXP ? OFF_G + kExpRowBytes : OFF_G + FS * kLanes * 2;
+    constexpr uint32_t OFF_R = EXP ? dec_exp_rings() : dec_e4m3_rings(FS);
     constexpr uint32_t OFF_T = OFF_R + kDecStreams * 2 * kDecRing;
+    constexpr uint32_t OFF_K = OFF_T + kDecStreams * kDecTile * kLanes;     // class tiles (EXP)
+    constexpr uint32_t OFF_N = OFF_K + kDecStreams * kDecTile * kLanes;     // n of each class (EXP)
     constexpr uint32_t kTiles = kSteps / kDecTile;
     extern __shared__ __align__(16) uint8_t lds[];
     const uint32_t lb = uint32_t(uintptr_t(lds));                  // LDS offset of the dynamic block
@@ -2087,20 +2118,53 @@ __global__ __launch_bounds__(1024, 1) void decode_e4m3(DecodeLaunch a, DevTables
     const LdsPos ps = lds_position(geo, lg);
     if (!ps.valid) return;
     const uint32_t tid = threadIdx.x;
-    const uint32_t tab0 = ps.slab * geo.C + ps.cg * kLanes;
+    const uint32_t tab0 = EXP ? ps.slab * kExpClasses : ps.slab * geo.C + ps.cg * kLanes;
     // rows by residual byte: row = r + FS/2 for the symbol of residual r (|r| < FS/2 when n < FS)
     constexpr uint32_t RB = 128u - FS / 2;                        // residual byte of row 0
-    uint16_t* lg16 = reinterpret_cast<uint16_t*>(lds + OFF_G);    // [FS rows][32 lanes]
+    uint16_t* lg16 = reinterpret_cast<uint16_t*>(lds + OFF_G);    // [FS rows][32 lanes] or [16 classes][64 rows]
     uint16_t* lc16 = reinterpret_cast<uint16_t*>(lds + OFF_C);
-    for (uint32_t i = tid; i < FS * kLanes; i += blockDim.x) {
-        const uint32_t row = i / kLanes;
-        const uint32_t z = zig8((row + RB - 128u) & 0xFFu);         // symbol of the row's residual
-        const uint32_t fc = t.fc[size_t(tab0 + i % kLanes) * 256 + z];
-        lg16[i] = uint16_t(kM - (fc & 0xFFFFu));
-        lc16[i] = uint16_t(fc >> 16);                             // symbols past n: start 4096
+    if constexpr (EXP) {
+        for (uint32_t i = tid; i < kExpClasses * kExpRows; i += blockDim.x) {
+            const uint32_t q = i / kExpRows, row = i % kExpRows;
+            const uint32_t n = t.n[tab0 + q];
+            // row 0 (residual byte 64) is the class's escape symbol
+            const uint32_t z = row == 0 ? n : zig8((row + RB - 128u) & 0xFFu);
+            const uint32_t fc = t.fc[size_t(tab0 + q) * 256 + z];
+            lg16[i] = uint16_t(kM - (fc & 0xFFFFu));
+            lc16[i] = uint16_t(fc >> 16);
+        }
+        if (tid < kExpClasses) lds[OFF_N + tid] = uint8_t(t.n[tab0 + tid]);
+    } else {
+        for (uint32_t i = tid; i < FS * kLanes; i += blockDim.x) {
+            const uint32_t row = i / kLanes;
+            const uint32_t z = zig8((row + RB - 128u) & 0xFFu);     // symbol of the row's residual
+            const uint32_t fc = t.fc[size_t(tab0 + i % kLanes) * 256 + z];
+            lg16[i] = uint16_t(kM - (fc & 0xFFFFu));
+            lc16[i] = uint16_t(fc >> 16);                         // symbols past n: start 4096
+        }
     }
     __syncthreads();
-    {
+    if constexpr (EXP) {
+        // the 16 class maps of the slab, contiguous in memory; a byte becomes the residual byte of its
+        // symbol, the escape symbol's becomes 0x40
+        const uint4* src = reinterpret_cast<const uint4*>(t.slot + size_t(tab0) * kM);
+        uint4* dst = reinterpret_cast<uint4*>(lds);
+        auto rb4 = [](uint32_t z) {
+            const uint32_t l = z & 0x01010101u;
+            return ((z >> 1) & 0x7F7F7F7Fu) ^ ((l << 8) - l) ^ 0x80808080u;
+        };
+#pragma unroll
+        for (uint32_t k = 0; k < kExpClasses * kM / 16 / 1024; ++k) {
+            const uint32_t e = k * 1024 + tid;
+            const uint32_t n4 = (t.n[tab0 + e / (kM / 16)] & 0xFFu) * 0x01010101u;
+            const uint4 v = src[e];
+            auto cv = [&](uint32_t z) {
+                const uint32_t m = (zero_bytes(z ^ n4) >> 7) * 0xFFu;   // bytes holding the escape symbol
+                return (rb4(z) & ~m) | (kExpEscByte * 0x01010101u & m);
+            };
+            dst[e] = make_uint4(cv(v.x), cv(v.y), cv(v.z), cv(v.w));
+        }
+    } else {
         // maps: the 32 slot -> symbol tables of the group are contiguous in memory; each byte
         // becomes the residual byte of its symbol, unzig(z) + 128 = unzig(z) ^ 0x80, 4 at a time
         const uint4* src = reinterpret_cast<const uint4*>(t.slot + size_t(tab0) * kM);
@@ -2133,18 +2197,24 @@ __global__ __launch_bounds__(1024, 1) void decode_e4m3(DecodeLaunch a, DevTables
         return;
     }
     DecLane L;
-    L.mapb = lb + hl * kM;
-    L.gb = lb + OFF_G + hl * 2 - RB * kLanes * 2;                  // row of residual byte b at b * 64 + gb
+    if constexpr (EXP) {
+        L.mapb = lb;                                               // class q's map at q * 4096
+        L.gb = lb + OFF_G - RB * 2;                                // class q, residual byte b at q * 256 + b * 2 + gb
+    } else {
+        L.mapb = lb + hl * kM;
+        L.gb = lb + OFF_G + hl * 2 - RB * kLanes * 2;              // row of residual byte b at b * 64 + gb
+    }
     L.fsh = upper ? 16u : 0u;
     L.lowm = upper ? 0u : 0xFFFFFFFFu;
     // every payload read of the workgroup goes through one range-checked resource
     L.rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(pay + wlo), (short)0, int(whi - wlo), 0x00020000);
-    // tile-domain bytes: the escape symbol's map byte and n of the lane's 4 channels
+    // tile-domain bytes: the escape symbol's map byte and n of the lane's 4 channels (exponent
+    // classes: 0x40 in every class; n by the position's class)
     uint32_t escp = 0, np = 0;
 #pragma unroll
     for (uint32_t k = 0; k < 4; ++k) {
-        const uint32_t nk = t.n[tab0 + q4 + k];
-        escp |= rbyte(nk) << (8 * k);
+        const uint32_t nk = EXP ? 0u : t.n[tab0 + q4 + k];
+        escp |= (EXP ? kExpEscByte : rbyte(nk)) << (8 * k);
         np |= min(nk, 255u) << (8 * k);
     }
     // predictor and output rows of the slab's channel group, 32-bit offsets from one base each
@@ -2183,6 +2253,7 @@ __global__ __launch_bounds__(1024, 1) void decode_e4m3(DecodeLaunch a, DevTables
         // wrk = last chunk written to the ring, live = 0x8000 in the field of a half with
         // a coded stream
         uint32_t ldk[kDecChains], wrk[kDecChains], live[kDecChains];
+        uint32_t ktb[kDecChains], cls[kDecChains];                 // class tile base, class word (EXP)
         bool coded[kDecChains], raw[kDecChains];
         uint64_t e0[kDecChains], e1[kDecChains];
         uint32_t x0[kDecChains], c0[kDecChains], c1[kDecChains];
@@ -2214,6 +2285,7 @@ __global__ __launch_bounds__(1024, 1) void decode_e4m3(DecodeLaunch a, DevTables
             const uint32_t hs = (tid >> 5) * kDecChains + c;          // stream slot in the workgroup
             ch[c].ringb = lb + OFF_R + hs * 2 * kDecRing;             // 256-byte aligned
             ch[c].tileb = lb + OFF_T + hs * kDecTile * kLanes + hl;
+            ktb[c] = lb + OFF_K + hs * kDecTile * kLanes;
             // ---- stream header checks (every lane of the half holds the same entries)
             uint32_t x = kStateLow;
             size[c] = 0;
@@ -2262,6 +2334,26 @@ __global__ __launch_bounds__(1024, 1) void decode_e4m3(DecodeLaunch a, DevTables
         // step reads them back transposed (lane hl: step r4, lanes q4..q4+3 of its half, so the
         // lanes of a half and the bytes of a lane run in decode order), resolves escaped values,
         // reconstructs and stores the rows and reloads pv with the row two tiles ahead.
+        // EXP: the classes of a tile go through the class tile (the lane's predictor row r4, bytes q4..q4+3
+        // in, the lane's own channel's 4 steps out); a class byte holds class << 4
+        auto put_classes = [&](const uint32_t (&pv)[kDecChains]) {
+            if constexpr (EXP) {
+#pragma unroll
+                for (uint32_t c = 0; c < kDecChains; ++c) {
+                    const uint32_t v = (pv[c] << 1) & 0xF0F0F0F0u;
+#pragma unroll
+                    for (uint32_t j = 0; j < 4; ++j)
+                        *reinterpret_cast<lds_u8*>(ktb[c] + (q4 + j) * kDecTile + r4) = uint8_t(v >> (8 * j));
+                }
+            }
+        };
+        auto get_classes = [&]() {
+            if constexpr (EXP) {
+#pragma unroll
+                for (uint32_t c = 0; c < kDecChains; ++c)
+                    cls[c] = *reinterpret_cast<const lds_u32*>(ktb[c] + hl * kDecTile);
+            }
+        };
         uint32_t zt[kDecChains];
         auto fetch_tile = [&]() {
 #pragma unroll
@@ -2311,7 +2403,10 @@ __global__ __launch_bounds__(1024, 1) void decode_e4m3(DecodeLaunch a, DevTables
                         }
                         if (f != 0) {
                             // a canonical encoder codes a value below n directly
-                            if (coded[c] && e < ((np >> sh) & 0xFFu)) bad = true;
+                            const uint32_t nv = EXP ? uint32_t(*reinterpret_cast<const lds_u8*>(
+                                                          lb + OFF_N + ((pv[c] >> (sh + 3)) & 0xFu)))
+                                                    : (np >> sh) & 0xFFu;
+                            if (coded[c] && e < nv) bad = true;
                             v = (v & ~(0xFFu << sh)) | (rbyte(e) << sh);
                             f &= f - 1u;
                             ++eidx;
@@ -2335,8 +2430,10 @@ __global__ __launch_bounds__(1024, 1) void decode_e4m3(DecodeLaunch a, DevTables
             DecState s0[kDecChains];
 #pragma unroll
             for (uint32_t c = 0; c < kDecChains; ++c) s0[c] = st[c];
-            dec_tile_steps<false, FS>(
-                st, L, ch, sy, [&] { if (T > 0) fetch_tile(); }, [&] { if (T > 0) finish(T - 1, pvp); });
+            get_classes();
+            __builtin_amdgcn_wave_barrier();
+            dec_tile_steps<false, FS, EXP>(
+                st, L, ch, sy, [&] { if (T > 0) fetch_tile(); }, [&] { if (T > 0) finish(T - 1, pvp); }, cls);
             // a half of a coded stream that read past the last chunk written (word count above
             // 32 (wrk + 1) in its field) decodes the tile again from memory
             uint32_t over = 0;
@@ -2350,13 +2447,16 @@ __global__ __launch_bounds__(1024, 1) void decode_e4m3(DecodeLaunch a, DevTables
                     st[c].x = s0[c].x;
                     st[c].P = s0[c].P;
                 }
-                dec_tile_steps<true, FS>(st, L, ch, sy, [] {}, [] {});
+                dec_tile_steps<true, FS, EXP>(st, L, ch, sy, [] {}, [] {}, cls);
             }
 #pragma unroll
             for (uint32_t c = 0; c < kDecChains; ++c)
 #pragma unroll
                 for (uint32_t r = 0; r < kDecTile; ++r)
                     *reinterpret_cast<lds_u8*>(ch[c].tileb + r * kLanes) = uint8_t(sy[c][r]);
+            // the next tile's classes: its predictor row is in pvp (the initial load after tile 0, the
+            // reload of the finish above after later tiles)
+            if (T + 1 < kTiles) put_classes(pvp);
 #pragma unroll
             for (uint32_t c = 0; c < kDecChains; ++c) {
                 // the chunk in cw goes into its slot; the next one is requested while the ring
@@ -2371,6 +2471,8 @@ __global__ __launch_bounds__(1024, 1) void decode_e4m3(DecodeLaunch a, DevTables
             }
             __builtin_amdgcn_wave_barrier();
         };
+        put_classes(pva);
+        __builtin_amdgcn_wave_barrier();
         for (uint32_t T = 0; T < kTiles; T += 2) {
             tile_at(T, pvb);
             tile_at(T + 1, pva);
@@ -3005,6 +3107,17 @@ hipError_t decode_all(const DecodeLaunch& a, const DevTables& t, hipStream_t st)
         if (e != hipSuccess) return e;
         timed("decode_streams", st, [&](hipEvent_t e0, hipEvent_t e1) {
             hipExtLaunchKernelGGL(k, dim3(lds_grid(lg)), dim3(kLdsThreads), lb, st, e0, e1, 0, a, t, lg);
+        });
+        return hipGetLastError();
+    }
+    if (DT == SKV_E4M3 && MODE == SKV_RESIDUAL_EXP && fits && !g_force_v1 && v == 0 &&
+        t.max_n + 2 <= kExpRows && dec_exp_lds() <= kLdsLimit) {
+        const LdsGeo lg = lds_geometry(a.shape);
+        auto k = decode_e4m3<kExpRows, true>;
+        hipError_t e = allow_lds(k, dec_exp_lds());
+        if (e != hipSuccess) return e;
+        timed("decode_streams", st, [&](hipEvent_t e0, hipEvent_t e1) {
+            hipExtLaunchKernelGGL(k, dim3(lds_grid(lg)), dim3(kLdsThreads), dec_exp_lds(), st, e0, e1, 0, a, t, lg);
         });
         return hipGetLastError();
     }
