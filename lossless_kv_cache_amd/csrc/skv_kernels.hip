@@ -1512,10 +1512,23 @@ constexpr uint32_t kPairRing = 128;
 __host__ __device__ constexpr uint32_t encode_groups_lds(uint32_t nc, uint32_t fs) {
     return 2 * nc * kLanes * fs * 16 + 16 * (kTileSteps * 2 * nc * kLanes + 2 * nc * kPairRing * 2);
 }
+// Exponent-class tables ([16 classes][fs] entries and the classes' n) with 16-bit tile entries
+__host__ __device__ constexpr uint32_t encode_exp_lds(uint32_t fs) {
+    return kExpClasses * fs * 16 + kExpClasses + 8 * (kTileSteps * 2 * kLanes * 2 + 2 * kPairRing * 2) + 16;
+}
 
-template <uint32_t NC>
+// Z8(d): zigzag symbols of 4 signed residual bytes, (d << 1) per byte with the
+// byte's sign spread over it (v_perm selectors 8..11 give a byte's sign)
+__device__ __forceinline__ uint32_t zig8x4(uint32_t d) {
+    return ((d << 1) & 0xFEFEFEFEu) ^ __builtin_amdgcn_perm(d << 8, d, 0x090B080Au);
+}
+
+// EXP: exponent-class tables (one table per slab and predictor exponent class);
+// a tile entry is 16 bits, the symbol and the class of one position.
+template <uint32_t NC, bool EXP = false>
 __device__ __forceinline__ void encode_groups_body(const EncodeLaunch& a, const DevTables& t, uint32_t fs,
                                                    const LdsGeo& lg) {
+    static_assert(!EXP || NC == 1, "exponent classes: two channel groups");
     constexpr uint32_t RAW = kSyms;
     constexpr uint32_t MAXE = RAW - kStreamHead;
     constexpr uint32_t kDrop = 0x80000000u;               // buffer offset past the range: the access is dropped
@@ -1523,18 +1536,28 @@ __device__ __forceinline__ void encode_groups_body(const EncodeLaunch& a, const 
     constexpr uint32_t NG = 2 * NC;                        // channel groups of the workgroup
     constexpr uint32_t RL = NG * kLanes;                   // bytes of a tile row = table columns
     constexpr uint32_t LW = RL / 8;                        // bytes a lane loads per row (8 lanes a row)
-    constexpr uint32_t WLDS = kTileSteps * RL + NG * kPairRing * 2;
+    constexpr uint32_t TE = EXP ? 2 : 1;                   // bytes of a tile entry
+    constexpr uint32_t WLDS = kTileSteps * RL * TE + NG * kPairRing * 2;
     extern __shared__ __align__(16) uint8_t lds[];
     __shared__ uint8_t zig[256];
     const Geo geo = geometry(a.shape);
     const LdsPos ps = lds_position(geo, lg);
     if (!ps.valid) return;
-    const uint32_t tab0 = ps.slab * geo.C + ps.cg * kLanes;                 // first table of the groups
-    uint4* lenc = reinterpret_cast<uint4*>(lds);                            // [fs symbols][RL columns]
-    for (uint32_t i = threadIdx.x; i < RL * fs; i += blockDim.x) {
-        const uint32_t sym = i / RL, j = i % RL;
-        lenc[i] = t.enc[size_t(tab0 + j) * 256 + sym];
+    // first table of the groups (EXP: of the slab's classes)
+    const uint32_t tab0 = EXP ? ps.slab * kExpClasses : ps.slab * geo.C + ps.cg * kLanes;
+    constexpr uint32_t NT = EXP ? kExpClasses : RL;        // tables held
+    uint4* lenc = reinterpret_cast<uint4*>(lds);           // [fs symbols][RL columns] or [16 classes][fs symbols]
+    for (uint32_t i = threadIdx.x; i < NT * fs; i += blockDim.x) {
+        if constexpr (EXP) {
+            const uint32_t q = i / fs, sym = i % fs;       // entries past n repeat the escape entry, flagged
+            lenc[i] = t.enc[size_t(tab0 + q) * 256 + sym];
+        } else {
+            const uint32_t sym = i / RL, j = i % RL;
+            lenc[i] = t.enc[size_t(tab0 + j) * 256 + sym];
+        }
     }
+    uint8_t* nq = lds + size_t(NT) * fs * 16;              // EXP: n of each class
+    if (EXP && threadIdx.x < kExpClasses) nq[threadIdx.x] = uint8_t(t.n[tab0 + threadIdx.x]);
     for (uint32_t i = threadIdx.x; i < 256; i += blockDim.x) zig[i] = uint8_t(zig8(i));
     __syncthreads();
 
@@ -1543,11 +1566,11 @@ __device__ __forceinline__ void encode_groups_body(const EncodeLaunch& a, const 
     const bool upper = (threadIdx.x & 32u) != 0;
     const uint32_t fsh = upper ? 16u : 0u;
     const uint32_t lane = 31u - hl;                        // format lane (reversed within the half)
-    uint8_t* tile = lds + size_t(RL) * fs * 16 + wave * WLDS;
-    uint8_t* ring = tile + kTileSteps * RL;
+    uint8_t* tile = lds + ((size_t(NT) * fs * 16 + (EXP ? 16 : 0)) + wave * WLDS);
+    uint8_t* ring = tile + kTileSteps * RL * TE;
     // tile: [step][RL channels]; a lane loads LW channels of one step and reads its chains' channels back
     const uint32_t ld_row = (threadIdx.x & 63u) >> 3, ld_q = (threadIdx.x & 7u) * LW;
-    uint8_t* tile_st = tile + ld_row * RL + ld_q;
+    uint8_t* tile_st = tile + (ld_row * RL + ld_q) * TE;
     uint32_t tl[NC], n[NC], ring_b[NC];
     const uint8_t* tile_rd[NC];
     const uint32_t* ring32[NC];
@@ -1555,8 +1578,8 @@ __device__ __forceinline__ void encode_groups_body(const EncodeLaunch& a, const 
     for (uint32_t c = 0; c < NC; ++c) {
         const uint32_t grp = 2 * c + (upper ? 1u : 0u);
         tl[c] = grp * kLanes + lane;                       // table column of the chain's channel
-        n[c] = t.n[tab0 + tl[c]];
-        tile_rd[c] = tile + grp * kLanes + lane;
+        n[c] = EXP ? 0u : t.n[tab0 + tl[c]];
+        tile_rd[c] = tile + (grp * kLanes + lane) * TE;
         ring_b[c] = uint32_t(uintptr_t(ring)) + grp * kPairRing * 2;   // LDS byte offsets
         ring32[c] = reinterpret_cast<const uint32_t*>(ring + grp * kPairRing * 2);
     }
@@ -1581,18 +1604,39 @@ __device__ __forceinline__ void encode_groups_body(const EncodeLaunch& a, const 
 
     typedef uint32_t Row[LW / 4];
     // z of one tile: difference bytes into LDS, then each chain's channel through the zigzag table
+    // (EXP: symbol | class << 8 per position, formed in registers)
     auto stage = [&](const Row& tv, const Row& pv, uint32_t (&z)[NC][kTileSteps]) {
         uint32_t d[LW / 4];
 #pragma unroll
         for (uint32_t k = 0; k < LW / 4; ++k) d[k] = sub8x4(sflip8x4(tv[k]), sflip8x4(pv[k]));
-        if constexpr (LW == 8) *reinterpret_cast<uint2*>(tile_st) = make_uint2(d[0], d[1]);
-        else *reinterpret_cast<uint4*>(tile_st) = make_uint4(d[0], d[1], d[2], d[3]);
+        if constexpr (EXP) {
+            uint32_t w[LW / 2];
+#pragma unroll
+            for (uint32_t k = 0; k < LW / 4; ++k) {
+                const uint32_t zz = zig8x4(d[k]), cc = (pv[k] >> 3) & 0x0F0F0F0Fu;
+                w[2 * k] = __builtin_amdgcn_perm(cc, zz, 0x05010400u);
+                w[2 * k + 1] = __builtin_amdgcn_perm(cc, zz, 0x07030602u);
+            }
+            *reinterpret_cast<uint4*>(tile_st) = make_uint4(w[0], w[1], w[2], w[3]);
+        } else if constexpr (LW == 8) {
+            *reinterpret_cast<uint2*>(tile_st) = make_uint2(d[0], d[1]);
+        } else {
+            *reinterpret_cast<uint4*>(tile_st) = make_uint4(d[0], d[1], d[2], d[3]);
+        }
         __builtin_amdgcn_wave_barrier();
 #pragma unroll
         for (uint32_t c = 0; c < NC; ++c)
 #pragma unroll
-            for (uint32_t r = 0; r < kTileSteps; ++r) z[c][r] = zig[tile_rd[c][r * RL]];
+            for (uint32_t r = 0; r < kTileSteps; ++r) {
+                if constexpr (EXP) z[c][r] = *reinterpret_cast<const uint16_t*>(tile_rd[c] + r * RL * 2);
+                else z[c][r] = zig[tile_rd[c][r * RL]];
+            }
         __builtin_amdgcn_wave_barrier();
+    };
+    // table entry of a position (EXP: class table, symbols past the table's n read its escape entry)
+    auto entry = [&](uint32_t c, uint32_t zv) -> uint4 {
+        if constexpr (EXP) return lenc[(zv >> 8) * fs + min(zv & 0xFFu, fs - 1)];
+        else return lenc[min(zv, n[c]) * RL + tl[c]];
     };
 
     for (uint32_t tb = ps.tb_begin + wave; tb < ps.tb_end; tb += nwave) {
@@ -1623,12 +1667,13 @@ __device__ __forceinline__ void encode_groups_body(const EncodeLaunch& a, const 
         load(kTiles - 2, tv, pv);
 
         uint32_t x[NC], wp[NC], elo[NC], ehi[NC];         // wp: word counts, lower half | upper half << 16
+        uint32_t escf[NC];                                 // EXP: entries' flags of the tile (bit 8: escape)
         uint4 ec[NC];
 #pragma unroll
         for (uint32_t c = 0; c < NC; ++c) {
             x[c] = kStateLow;
             wp[c] = elo[c] = ehi[c] = 0;
-            ec[c] = lenc[min(za[c][kTileSteps - 1], n[c]) * RL + tl[c]];
+            ec[c] = entry(c, za[c][kTileSteps - 1]);
         }
         // one tile: zc holds its symbols, zn receives the next tile's (two arrays that trade roles, so
         // no copy between tiles)
@@ -1644,7 +1689,8 @@ __device__ __forceinline__ void encode_groups_body(const EncodeLaunch& a, const 
                 for (uint32_t c = 0; c < NC; ++c) {
                     const uint4 e = ec[c];
                     const uint32_t znext = r > 0 ? zc[c][r - 1] : zn[c][kTileSteps - 1];
-                    ec[c] = lenc[min(znext, n[c]) * RL + tl[c]];
+                    ec[c] = entry(c, znext);
+                    if constexpr (EXP) escf[c] = (r == kTileSteps - 1 ? 0u : escf[c]) | e.w;
                     // words leave before the state absorbs the symbol
                     uint32_t xs = x[c];
                     const bool emit = xs >= e.x;
@@ -1689,15 +1735,19 @@ __device__ __forceinline__ void encode_groups_body(const EncodeLaunch& a, const 
             // escaped values of this tile, in emission order (rare: skipped by the whole wavefront)
 #pragma unroll
             for (uint32_t c = 0; c < NC; ++c) {
-                uint32_t zm = zc[c][0];
+                if constexpr (EXP) {
+                    if (__ballot((escf[c] & 0x100u) != 0) == 0) continue;
+                } else {
+                    uint32_t zm = zc[c][0];
 #pragma unroll
-                for (uint32_t r = 1; r < kTileSteps; ++r) zm = max(zm, zc[c][r]);
-                if (__ballot(zm >= n[c]) == 0) continue;
+                    for (uint32_t r = 1; r < kTileSteps; ++r) zm = max(zm, zc[c][r]);
+                    if (__ballot(zm >= n[c]) == 0) continue;
+                }
                 // upper-half slots carry a bias of 32 (mbcnt_lo counts the whole lower half for them)
                 const uint32_t ebase = ao[c] + kStreamHead - (upper ? 32u : 0u);
 #pragma unroll
                 for (int r = kTileSteps - 1; r >= 0; --r) {
-                    const bool esc = zc[c][r] >= n[c];
+                    const bool esc = EXP ? (zc[c][r] & 0xFFu) >= nq[zc[c][r] >> 8] : zc[c][r] >= n[c];
                     const uint64_t me = __ballot(esc);
                     if (me == 0) continue;
                     const uint32_t mlo = uint32_t(me), mhi = uint32_t(me >> 32), plo = __popc(mlo);
@@ -1734,6 +1784,13 @@ __device__ __forceinline__ void encode_groups_body(const EncodeLaunch& a, const 
     }
 }
 
+// two channel groups with the slab's exponent-class tables; 512-thread workgroups, three per CU
+// (the class bookkeeping needs more than the 64 registers of eight waves per SIMD)
+constexpr uint32_t kExpEncThreads = 512;
+__global__ __launch_bounds__(kExpEncThreads) __attribute__((amdgpu_waves_per_eu(6))) void encode_pairs_exp(
+    EncodeLaunch a, DevTables t, uint32_t fs, LdsGeo lg) {
+    encode_groups_body<1, true>(a, t, fs, lg);
+}
 // two channel groups, two workgroups per CU.  (Four groups, whole 128-byte lines read once by one
 // wavefront, fit one workgroup per CU and measured slower: 1.94 ms against 1.75 ms on a
 // 36 x 2 x 32768 x 1024 cache, the lost occupancy costing more than the line re-reads.)
@@ -3031,6 +3088,16 @@ hipError_t encode_all(const EncodeLaunch& a, const DevTables& t, hipStream_t st)
         if (e != hipSuccess) return e;
         timed("encode_streams", st, [&](hipEvent_t e0, hipEvent_t e1) {
             hipExtLaunchKernelGGL(encode_bf16, dim3(lds_grid(lg)), dim3(kLdsThreads), lp, st, e0, e1, 0, a, t, fc_stride(t), lg);
+        });
+    } else if (DT == SKV_E4M3 && MODE == SKV_RESIDUAL_EXP && fits && ncg % 4 == 0 && aligned &&
+               3 * (encode_exp_lds(fc_stride(t)) + 256) <= kLdsLimit && !g_force_v1 && variant().enc == 0) {
+        const LdsGeo lg = lds_geometry(a.shape, 2);
+        const size_t lp = encode_exp_lds(fc_stride(t));
+        hipError_t e = allow_lds(encode_pairs_exp, lp);
+        if (e != hipSuccess) return e;
+        timed("encode_streams", st, [&](hipEvent_t e0, hipEvent_t e1) {
+            hipExtLaunchKernelGGL(encode_pairs_exp, dim3(lds_grid(lg)), dim3(kExpEncThreads), lp, st, e0, e1, 0, a, t,
+                                  fc_stride(t), lg);
         });
     } else if (DT == SKV_E4M3 && MODE == SKV_RESIDUAL && fits && ncg % 4 == 0 &&
                2 * encode_groups_lds(1, fc_stride(t)) + 512 <= kLdsLimit && aligned && !g_force_v1 &&
