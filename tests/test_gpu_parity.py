@@ -228,6 +228,28 @@ def test_exponent_mode_small(skv, orc, cid):
     assert torch.equal(part, t[:, :, 256:512])
 
 
+def test_exponent_mode_escapes_and_unaligned(skv, orc):
+    """Exponent mode through every kernel path: rare far residuals (escapes in
+    every class, with bursts of words), the tiled kernels on aligned buffers and
+    the per-step ones on unaligned buffers; all containers equal the oracle's."""
+    cfg = gen.Config(99, "exp-escapes", "e4m3", 1, 2, 512, 128)
+    t, p, tabs, oshape = exp_case(skv, orc, cfg)
+    rng = np.random.default_rng(21)
+    tn = t.cpu().numpy()
+    flat = tn.reshape(-1)
+    pos = rng.choice(flat.size, size=flat.size // 200, replace=False)
+    flat[pos] = rng.integers(0, 256, size=pos.size, dtype=np.uint8)
+    t = torch.from_numpy(tn).cuda()
+    want = full_compare(skv, orc, t, p, tabs, oshape, "exponent mode escapes")
+    tu, pu = _offset_copy(t, 1), _offset_copy(p, 3)
+    cont = skv.encode(tabs, tu, pu)
+    torch.cuda.synchronize()
+    assert cont.cpu().numpy().tobytes() == want
+    out = _offset_copy(torch.zeros_like(t), 1)
+    skv.decode_into(tabs, cont, pu, out)
+    assert torch.equal(out, t)
+
+
 def test_exponent_mode_full_size_e4m3(skv, orc):
     """The Qwen3-8B-shaped e4m3 cache with exponent-conditioned tables: sampled
     streams equal the oracle's, the round trip is exact, and the container is
