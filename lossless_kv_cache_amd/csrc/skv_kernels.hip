@@ -1514,7 +1514,7 @@ __host__ __device__ constexpr uint32_t encode_groups_lds(uint32_t nc, uint32_t f
 }
 // Exponent-class tables ([16 classes][fs] entries and the classes' n) with 16-bit tile entries
 __host__ __device__ constexpr uint32_t encode_exp_lds(uint32_t fs) {
-    return kExpClasses * fs * 16 + kExpClasses + 8 * (kTileSteps * 2 * kLanes * 2 + 2 * kPairRing * 2) + 16;
+    return kExpClasses * (fs + 1) * 16 + kExpClasses + 8 * (kTileSteps * 2 * kLanes * 2 + 2 * kPairRing * 2) + 16;
 }
 
 // Z8(d): zigzag symbols of 4 signed residual bytes, (d << 1) per byte with the
@@ -1546,17 +1546,20 @@ __device__ __forceinline__ void encode_groups_body(const EncodeLaunch& a, const 
     // first table of the groups (EXP: of the slab's classes)
     const uint32_t tab0 = EXP ? ps.slab * kExpClasses : ps.slab * geo.C + ps.cg * kLanes;
     constexpr uint32_t NT = EXP ? kExpClasses : RL;        // tables held
-    uint4* lenc = reinterpret_cast<uint4*>(lds);           // [fs symbols][RL columns] or [16 classes][fs symbols]
+    // EXP: a class takes fs + 1 entries (an odd number of 16-byte entries), so that the same symbol of
+    // different classes falls in different LDS banks
+    const uint32_t cstride = EXP ? fs + 1 : fs;
+    uint4* lenc = reinterpret_cast<uint4*>(lds);           // [fs symbols][RL columns] or [16 classes][fs + 1]
     for (uint32_t i = threadIdx.x; i < NT * fs; i += blockDim.x) {
         if constexpr (EXP) {
             const uint32_t q = i / fs, sym = i % fs;       // entries past n repeat the escape entry, flagged
-            lenc[i] = t.enc[size_t(tab0 + q) * 256 + sym];
+            lenc[q * cstride + sym] = t.enc[size_t(tab0 + q) * 256 + sym];
         } else {
             const uint32_t sym = i / RL, j = i % RL;
             lenc[i] = t.enc[size_t(tab0 + j) * 256 + sym];
         }
     }
-    uint8_t* nq = lds + size_t(NT) * fs * 16;              // EXP: n of each class
+    uint8_t* nq = lds + size_t(NT) * cstride * 16;         // EXP: n of each class
     if (EXP && threadIdx.x < kExpClasses) nq[threadIdx.x] = uint8_t(t.n[tab0 + threadIdx.x]);
     for (uint32_t i = threadIdx.x; i < 256; i += blockDim.x) zig[i] = uint8_t(zig8(i));
     __syncthreads();
@@ -1566,7 +1569,7 @@ __device__ __forceinline__ void encode_groups_body(const EncodeLaunch& a, const 
     const bool upper = (threadIdx.x & 32u) != 0;
     const uint32_t fsh = upper ? 16u : 0u;
     const uint32_t lane = 31u - hl;                        // format lane (reversed within the half)
-    uint8_t* tile = lds + ((size_t(NT) * fs * 16 + (EXP ? 16 : 0)) + wave * WLDS);
+    uint8_t* tile = lds + ((size_t(NT) * cstride * 16 + (EXP ? 16 : 0)) + wave * WLDS);
     uint8_t* ring = tile + kTileSteps * RL * TE;
     // tile: [step][RL channels]; a lane loads LW channels of one step and reads its chains' channels back
     const uint32_t ld_row = (threadIdx.x & 63u) >> 3, ld_q = (threadIdx.x & 7u) * LW;
@@ -1635,7 +1638,7 @@ __device__ __forceinline__ void encode_groups_body(const EncodeLaunch& a, const 
     };
     // table entry of a position (EXP: class table, symbols past the table's n read its escape entry)
     auto entry = [&](uint32_t c, uint32_t zv) -> uint4 {
-        if constexpr (EXP) return lenc[(zv >> 8) * fs + min(zv & 0xFFu, fs - 1)];
+        if constexpr (EXP) return lenc[(zv >> 8) * cstride + min(zv & 0xFFu, fs - 1)];
         else return lenc[min(zv, n[c]) * RL + tl[c]];
     };
 
@@ -2037,7 +2040,10 @@ __host__ __device__ constexpr uint32_t dec_e4m3_lds(uint32_t fs) {
 // (residual -64, zigzag 127) holds the escape symbol, which with at most 126 direct symbols is never a
 // direct one, so escaped positions read 0x40 in every class.
 constexpr uint32_t kExpRows = 128;
-constexpr uint32_t kExpRowBytes = kExpClasses * kExpRows * 2;
+// a class's rows take 260 bytes, so that the same residual byte of different classes falls in
+// different LDS banks
+constexpr uint32_t kExpRowStride = kExpRows * 2 + 4;
+constexpr uint32_t kExpRowBytes = kExpClasses * kExpRowStride;
 constexpr uint32_t kExpEscByte = 128u - kExpRows / 2;
 __host__ __device__ constexpr uint32_t dec_exp_rings() { return (kExpClasses * kM + 2 * kExpRowBytes + 255) & ~255u; }
 __host__ __device__ constexpr uint32_t dec_exp_lds() {
@@ -2102,7 +2108,7 @@ struct DecChain {
 //
 // EXP (exponent-class tables): the maps and rows belong to the step's class,
 // taken from cw (the lane's class byte of every step, class << 4): the map
-// of class q sits at q * 4096 from mapb and its rows at q * 256 from gb.
+// of class q sits at q * 4096 from mapb and its rows at q * kExpRowStride from gb.
 template <bool GLOBAL, uint32_t FS, bool EXP = false, class Pre, class Post>
 __device__ __forceinline__ void dec_tile_steps(DecState (&st)[kDecChains], const DecLane& L,
                                                const DecChain (&ch)[kDecChains], uint32_t (&sy)[kDecChains][kDecTile],
@@ -2117,7 +2123,7 @@ __device__ __forceinline__ void dec_tile_steps(DecState (&st)[kDecChains], const
             if constexpr (EXP) {
                 const uint32_t q = __builtin_amdgcn_ubfe(cw[c], 8 * r + 4, 4);
                 mb[c] = (q << 12) + L.mapb;
-                rb[c] = q * (kExpRows * 2) + L.gb;
+                rb[c] = q * kExpRowStride + L.gb;
             } else {
                 mb[c] = L.mapb;
                 rb[c] = L.gb;
@@ -2187,8 +2193,8 @@ __global__ __launch_bounds__(1024, 1) void decode_e4m3(DecodeLaunch a, DevTables
             // row 0 (residual byte 64) is the class's escape symbol
             const uint32_t z = row == 0 ? n : zig8((row + RB - 128u) & 0xFFu);
             const uint32_t fc = t.fc[size_t(tab0 + q) * 256 + z];
-            lg16[i] = uint16_t(kM - (fc & 0xFFFFu));
-            lc16[i] = uint16_t(fc >> 16);
+            lg16[q * (kExpRowStride / 2) + row] = uint16_t(kM - (fc & 0xFFFFu));
+            lc16[q * (kExpRowStride / 2) + row] = uint16_t(fc >> 16);
         }
         if (tid < kExpClasses) lds[OFF_N + tid] = uint8_t(t.n[tab0 + tid]);
     } else {
@@ -2256,7 +2262,7 @@ __global__ __launch_bounds__(1024, 1) void decode_e4m3(DecodeLaunch a, DevTables
     DecLane L;
     if constexpr (EXP) {
         L.mapb = lb;                                               // class q's map at q * 4096
-        L.gb = lb + OFF_G - RB * 2;                                // class q, residual byte b at q * 256 + b * 2 + gb
+        L.gb = lb + OFF_G - RB * 2;                                // class q, residual byte b at q * 260 + b * 2 + gb
     } else {
         L.mapb = lb + hl * kM;
         L.gb = lb + OFF_G + hl * 2 - RB * kLanes * 2;              // row of residual byte b at b * 64 + gb
