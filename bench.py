@@ -54,7 +54,7 @@ def main() -> int:
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the coding path has no multi-GPU part "
-              "(streams are independent; sharding is described in DESIGN.md). Run with --gpus 1.",
+              "(streams are independent, so a cache shards by slab with no exchange). Run with --gpus 1.",
               flush=True)
         return 2
 
