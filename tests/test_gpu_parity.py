@@ -250,6 +250,54 @@ def test_exponent_mode_escapes_and_unaligned(skv, orc):
     assert torch.equal(out, t)
 
 
+def test_exponent_mode_corruption(skv, orc):
+    """Damaged exponent-mode containers: the class-table decoder reaches the
+    oracle's verdict on every bit flip in the coded part of a stream (a flip
+    can leave a consistent stream, which both then decode alike), and refuses
+    an index past the payload and another blob."""
+    cfg = gen.Config(100, "exp-corrupt", "e4m3", 1, 2, 512, 128)
+    t, p, tabs, oshape = exp_case(skv, orc, cfg)
+    cont = skv.encode(tabs, t, p)
+    good = cont.cpu().numpy()
+    n, idx, head = _parse(good.tobytes())
+    rng = np.random.default_rng(8)
+    pn, tn = p.cpu().numpy(), t.cpu().numpy()
+    trials = refused = 0
+    while trials < 24:
+        st = int(rng.integers(0, n))
+        if idx[st] >> np.uint64(63):
+            continue
+        a = int(idx[st] & np.uint64((1 << 63) - 1))
+        nw = int.from_bytes(good[head + a + 128:head + a + 132].tobytes(), "little")
+        bad = good.copy()
+        pos = head + int(rng.integers(a, a + 132 + 2 * nw))
+        bad[pos] ^= np.uint8(1 << int(rng.integers(0, 8)))
+        say(f"[parity] exponent corrupt trial {trials}: stream {st} byte {pos}")
+        want = np.zeros_like(tn)
+        rc = orc.decode_rc(tabs.bytes(), bad.tobytes(), pn, want)
+        if rc == orc.E_CORRUPT:
+            with pytest.raises(skv.SkvError) as e:
+                skv.decode(tabs, torch.from_numpy(bad).cuda(), p)
+            assert e.value.status == skv.ERR_CORRUPT
+            refused += 1
+        else:
+            assert rc == orc.OK
+            assert np.array_equal(skv.decode(tabs, torch.from_numpy(bad).cuda(), p).cpu().numpy(), want)
+        trials += 1
+    assert refused >= 20
+    bad = good.copy()
+    bad[64 + 8 * 3:64 + 8 * 4] = np.frombuffer(struct.pack("<Q", 1 << 40), np.uint8)
+    with pytest.raises(skv.SkvError) as e:
+        skv.decode(tabs, torch.from_numpy(bad).cuda(), p)
+    assert e.value.status == skv.ERR_CORRUPT
+    ct, cp = gen.residual_array(cfg, gen.CALIB, tokens=256)
+    per_channel = skv.fit_tables(skv.E4M3, skv.RESIDUAL, 1, 2, 128, ct.numpy(), cp.numpy(), 256)
+    with pytest.raises(skv.SkvError) as e:
+        skv.decode(per_channel, cont, p)
+    assert e.value.status == skv.ERR_TABLES
+    assert torch.equal(skv.decode(tabs, cont, p), t)
+
+
 def test_exponent_mode_full_size_e4m3(skv, orc):
     """The Qwen3-8B-shaped e4m3 cache with exponent-conditioned tables: sampled
     streams equal the oracle's, the round trip is exact, and the container is
