@@ -250,13 +250,14 @@ def test_exponent_mode_escapes_and_unaligned(skv, orc):
     assert torch.equal(out, t)
 
 
-def test_exponent_mode_corruption(skv, orc):
-    """Damaged exponent-mode containers: the class-table decoder reaches the
-    oracle's verdict on every bit flip in the coded part of a stream (a flip
-    can leave a consistent stream, which both then decode alike), and refuses
-    an index past the payload and another blob."""
+@pytest.mark.parametrize("exp", [True, False])
+def test_e4m3_corruption_verdicts(skv, orc, exp):
+    """Damaged e4m3 containers (per-channel or exponent-class tables): the
+    decoder reaches the oracle's verdict on every bit flip in the coded part of
+    a stream (a flip can leave a consistent stream, which both then decode
+    alike), and refuses an index past the payload and another blob."""
     cfg = gen.Config(100, "exp-corrupt", "e4m3", 1, 2, 512, 128)
-    t, p, tabs, oshape = exp_case(skv, orc, cfg)
+    t, p, tabs, oshape = exp_case(skv, orc, cfg) if exp else residual_case(skv, orc, cfg)
     cont = skv.encode(tabs, t, p)
     good = cont.cpu().numpy()
     n, idx, head = _parse(good.tobytes())
@@ -272,7 +273,7 @@ def test_exponent_mode_corruption(skv, orc):
         bad = good.copy()
         pos = head + int(rng.integers(a, a + 132 + 2 * nw))
         bad[pos] ^= np.uint8(1 << int(rng.integers(0, 8)))
-        say(f"[parity] exponent corrupt trial {trials}: stream {st} byte {pos}")
+        say(f"[parity] e4m3 corrupt trial {trials} (exponent tables {exp}): stream {st} byte {pos}")
         want = np.zeros_like(tn)
         rc = orc.decode_rc(tabs.bytes(), bad.tobytes(), pn, want)
         if rc == orc.E_CORRUPT:
@@ -291,9 +292,9 @@ def test_exponent_mode_corruption(skv, orc):
         skv.decode(tabs, torch.from_numpy(bad).cuda(), p)
     assert e.value.status == skv.ERR_CORRUPT
     ct, cp = gen.residual_array(cfg, gen.CALIB, tokens=256)
-    per_channel = skv.fit_tables(skv.E4M3, skv.RESIDUAL, 1, 2, 128, ct.numpy(), cp.numpy(), 256)
+    other = skv.fit_tables(skv.E4M3, skv.RESIDUAL if exp else skv.RESIDUAL_EXP, 1, 2, 128, ct.numpy(), cp.numpy(), 256)
     with pytest.raises(skv.SkvError) as e:
-        skv.decode(per_channel, cont, p)
+        skv.decode(other, cont, p)
     assert e.value.status == skv.ERR_TABLES
     assert torch.equal(skv.decode(tabs, cont, p), t)
 
