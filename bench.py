@@ -49,6 +49,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--tables", choices=["channel", "exponent"], default="channel",
                     help="residual tables per channel (default) or per slab and predictor exponent class")
+    ap.add_argument("--transfer-layers", type=int, default=4,
+                    help="layers per chunk of the transfer-pipeline measurement (0 = skip it)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also time a plain device copy of the cache (HBM ceiling; counter scale reference)")
     args = ap.parse_args()
@@ -205,6 +207,11 @@ def main() -> int:
                 "GBps_read_plus_write": round(2 * src.numel() / (ms / 1e3) / 1e9, 1)}
         del dst
 
+    xfer = None
+    if not cb and args.transfer_layers > 0:
+        del out
+        xfer = transfer_probe(skv, cfg, tabs, tgt, prd, min(args.transfer_layers, cfg.layers))
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = (cpu_baseline_cb if cb else cpu_baseline)(cfg, tabs, tgt, prd, args.cpu_seconds)
@@ -237,10 +244,51 @@ def main() -> int:
         "kernels_roofline": per_kernel,
         "copy_ceiling": copy,
         "range_decode": part,
+        "transfer": xfer,
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)
     return 0 if ok else 1
+
+
+def transfer_probe(skv, cfg, tabs, tgt, prd, layers_per_chunk, reps=3):
+    """Wall time of the transfer pipeline (chunked encode -> page-locked host
+    -> device -> decode, overlapped on separate streams) against moving the
+    raw cache the same way (device -> page-locked host -> device, one copy
+    each way); both read the cache from and write it back to HBM."""
+    import torch
+
+    tr = skv.Transfer(tabs, cfg.tokens, layers_per_chunk)
+    out = torch.empty_like(tgt)
+    wire, offs = tr(tgt, prd, prd, out)                       # warm: tables of every chunk, buffers
+    ok = bool(torch.equal(out, tgt))
+    times = []
+    for _ in range(reps):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        wire, offs = tr(tgt, prd, prd, out)
+        torch.cuda.synchronize()
+        times.append((time.perf_counter() - t0) * 1e3)
+    ok = ok and bool(torch.equal(out, tgt))
+    raw = tgt.numel() * tgt.element_size()
+    host = torch.empty(raw, dtype=torch.uint8, pin_memory=True)
+    src = tgt.view(-1).view(torch.uint8)
+    dst = out.view(-1).view(torch.uint8)
+    raw_times = []
+    for _ in range(reps + 1):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        host.copy_(src, non_blocking=True)
+        dst.copy_(host, non_blocking=True)
+        torch.cuda.synchronize()
+        raw_times.append((time.perf_counter() - t0) * 1e3)
+    raw_ms = min(raw_times[1:])
+    ms = min(times)
+    del host, tr
+    return {"layers_per_chunk": layers_per_chunk, "chunks": len(offs) - 1, "wire_bytes": int(wire.numel()),
+            "ms": round(ms, 3), "GBps": round(raw / (ms / 1e3) / 1e9, 2),
+            "raw_copy_ms": round(raw_ms, 3), "raw_copy_GBps": round(raw / (raw_ms / 1e3) / 1e9, 2),
+            "speedup_vs_raw_copy": round(raw_ms / ms, 3), "verified": ok}
 
 
 def cpu_baseline(cfg, tabs, tgt, prd, seconds):

@@ -156,6 +156,46 @@ int skv_decode_range(const void* tables_blob, const void* d_in, size_t in_bytes,
                      uint32_t token_end, const void* d_aux, void* d_out, size_t out_capacity, void* d_work,
                      size_t* work_bytes, hipStream_t stream);
 
+/* Transfer pipeline (device -> host -> device).  Moving a prefilled cache
+ * to the server that decodes ("Speculative KV coding" page, section "Where
+ * it can be used": disaggregated prefill over a slow link) with its copies
+ * and the GPU work on separate streams so that they overlap (VeriCache page,
+ * "Hardware basis of the parallel execution").  The cache is cut into chunks
+ * of layers_per_chunk whole layers (the last chunk may be shorter); chunk c
+ * is encoded into a container of its own (the tables of its layers, as a
+ * blob of those layers that skv_free releases with tables_blob), copied to
+ * the host buffer h_wire, copied back to the device and decoded into d_out,
+ * while chunk c + 1 is being encoded.  The sender encodes on the calling
+ * thread; a receiver thread started and joined by this call copies back and
+ * decodes.  Residual-mode shapes (either table kind) only, else
+ * SKV_ERR_SHAPE.
+ *   d_target, d_aux_send: the sender's cache and predictor, device arrays of
+ *     shape s.
+ *   h_wire: host memory of wire_capacity bytes (page-locked, e.g. from
+ *     hipHostMalloc, for the copies to overlap; pageable memory works but
+ *     serializes them).  Receives the chunk containers back to back;
+ *     chunk_offsets (host, ceil(layers / layers_per_chunk) + 1 entries)
+ *     receives each one's byte offset and, last, the total, also stored in
+ *     *wire_bytes.  Each chunk container decodes on its own with
+ *     skv_decode and the tables of its layers.
+ *   d_aux_recv, d_out: the receiver's predictor (shape s) and the
+ *     reconstruction (out_capacity bytes available).
+ *   d_work: device workspace of *work_bytes bytes: two container buffers on
+ *     each side plus the encoder's and decoder's workspaces.
+ * Two-phase sizing as in skv_encode: h_wire == NULL sets *wire_bytes to the
+ * bound (every stream raw), d_work == NULL sets *work_bytes to the need.
+ * layers_per_chunk must be 1..layers (SKV_ERR_ARG).  Per-kernel timing must
+ * be off (SKV_ERR_ARG), since its state is process-wide.  A chunk that does
+ * not fit in the rest of h_wire stops the pipeline with SKV_ERR_CAPACITY and
+ * *wire_bytes = the bound; any encode or decode error stops it with that
+ * status; either way d_out is then unspecified.  The caller's stream is
+ * ordered before the pipeline's streams; the call returns once every copy
+ * and kernel it queued has finished. */
+int skv_transfer(const void* tables_blob, const skv_shape* s, uint32_t layers_per_chunk, const void* d_target,
+                 const void* d_aux_send, void* h_wire, size_t wire_capacity, size_t* wire_bytes,
+                 uint64_t* chunk_offsets, const void* d_aux_recv, void* d_out, size_t out_capacity, void* d_work,
+                 size_t* work_bytes, hipStream_t stream);
+
 /* Release a library-owned blob and its device copies.  NULL is a no-op. */
 void skv_free(void* tables_blob);
 

@@ -5,12 +5,17 @@
 // header validation, and the launches on the caller's stream.  The encoder
 // is deterministic, as a compressor feeding exact reconstruction must be
 // (VeriCache page, section "Compressor interface").
+#include <algorithm>
+#include <atomic>
+#include <condition_variable>
 #include <cstdlib>
 #include <cstring>
 #include <map>
 #include <mutex>
 #include <thread>
 #include <unordered_map>
+#include <utility>
+#include <vector>
 
 #include "skv_internal.h"
 
@@ -23,7 +28,11 @@ struct Blob {
     skv_shape shape{};                       // tokens = 0
     std::mutex dev_mu;
     std::map<int, skv::DevTables> dev;       // device ordinal -> expanded tables
+    std::mutex part_mu;
+    std::map<std::pair<uint32_t, uint32_t>, void*> parts;   // (first layer, layers) -> registered sub-blob
 };
+
+std::atomic<bool> g_timing_on{false};
 
 std::mutex g_mu;
 std::unordered_map<const void*, Blob*> g_blobs;
@@ -88,12 +97,27 @@ struct Staging {
     hipEvent_t ev = nullptr;
 };
 
+// Worker threads that the library starts and joins itself release their
+// staging buffers when they end; a caller's thread keeps its own until the
+// process exits.
+thread_local bool t_release_staging = false;
+struct StagingSet {
+    std::map<int, Staging> per_dev;
+    ~StagingSet() {
+        if (!t_release_staging) return;
+        for (auto& kv : per_dev) {
+            if (kv.second.ev) (void)hipEventDestroy(kv.second.ev);
+            if (kv.second.host) (void)hipHostFree(kv.second.host);
+        }
+    }
+};
+
 int read_back(void* dst, const void* src, size_t n, hipStream_t st) {
-    thread_local std::map<int, Staging> staging;
+    thread_local StagingSet staging;
     if (n > kStagingBytes) return SKV_ERR_ARG;
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return SKV_ERR_DEVICE;
-    Staging& sg = staging[dev];
+    Staging& sg = staging.per_dev[dev];
     if (!sg.host) {
         if (hipHostMalloc(&sg.host, kStagingBytes, hipHostMallocDefault) != hipSuccess) {
             sg.host = nullptr;
@@ -172,6 +196,7 @@ void skv_free(void* tables_blob) {
         b = it->second;
         g_blobs.erase(it);
     }
+    for (auto& kv : b->parts) skv_free(kv.second);
     int cur = 0;
     const bool have = hipGetDevice(&cur) == hipSuccess;
     for (auto& kv : b->dev) {
@@ -182,8 +207,9 @@ void skv_free(void* tables_blob) {
     delete b;
 }
 
-int skv_encode(const void* tables_blob, const skv_shape* s, const void* d_target, const void* d_aux, void* d_out,
-               size_t out_capacity, size_t* out_bytes, void* d_work, size_t* work_bytes, hipStream_t stream) {
+static int encode_impl(const void* tables_blob, const skv_shape* s, const void* d_target, const void* d_aux,
+                       void* d_out, size_t out_capacity, size_t* out_bytes, void* d_work, size_t* work_bytes,
+                       hipStream_t stream, bool timing) {
     if (!tables_blob || !s || !out_bytes || !work_bytes) return SKV_ERR_ARG;
     if (!skv::shape_supported(*s, true)) return SKV_ERR_SHAPE;
     Blob* b = find_blob(tables_blob);
@@ -226,22 +252,28 @@ int skv_encode(const void* tables_blob, const skv_shape* s, const void* d_target
     a.blob_hash = b->hash;
     a.shape = *s;
     a.n_streams = n;
-    skv::timing_reset();
+    if (timing) skv::timing_reset();
     if (skv::launch_encode(a, *t, stream) != hipSuccess) return SKV_ERR_DEVICE;
     uint64_t payload = 0;
     rc = read_back(&payload, a.total, 8, stream);
     if (rc != SKV_OK) return rc;
-    skv::timing_collect();
+    if (timing) skv::timing_collect();
     const uint64_t total = skv::kHeaderBytes + 8 * (n + 1) + payload;
     *out_bytes = total;
     return total > out_capacity ? SKV_ERR_CAPACITY : SKV_OK;
+}
+
+int skv_encode(const void* tables_blob, const skv_shape* s, const void* d_target, const void* d_aux, void* d_out,
+               size_t out_capacity, size_t* out_bytes, void* d_work, size_t* work_bytes, hipStream_t stream) {
+    return encode_impl(tables_blob, s, d_target, d_aux, d_out, out_capacity, out_bytes, d_work, work_bytes, stream,
+                       true);
 }
 
 // Decode of token blocks [tb0, tb1) of every slab of a container (all of them
 // for skv_decode).  tb1 = 0 stands for the container's last token block + 1.
 static int decode_blocks(const void* tables_blob, const void* d_in, size_t in_bytes, bool range, uint32_t token_begin,
                          uint32_t token_end, const void* d_aux, void* d_out, size_t out_capacity, void* d_work,
-                         size_t* work_bytes, hipStream_t stream) {
+                         size_t* work_bytes, hipStream_t stream, bool timing = true) {
     if (!tables_blob || !work_bytes) return SKV_ERR_ARG;
     Blob* b = find_blob(tables_blob);
     if (!b) return SKV_ERR_ARG;
@@ -296,12 +328,12 @@ static int decode_blocks(const void* tables_blob, const void* d_in, size_t in_by
     a.tb_base = tb_base;
     a.ntb_index = s.tokens / skv::kSteps;
     if (skv::launch_clear_u32(a.status, 1, stream) != hipSuccess) return SKV_ERR_DEVICE;
-    skv::timing_reset();
+    if (timing) skv::timing_reset();
     if (skv::launch_decode(a, *t, stream) != hipSuccess) return SKV_ERR_DEVICE;
     uint32_t status = 0;
     rc = read_back(&status, a.status, 4, stream);
     if (rc != SKV_OK) return rc;
-    skv::timing_collect();
+    if (timing) skv::timing_collect();
     return status ? SKV_ERR_CORRUPT : SKV_OK;
 }
 
@@ -318,7 +350,241 @@ int skv_decode_range(const void* tables_blob, const void* d_in, size_t in_bytes,
                          work_bytes, stream);
 }
 
-int skv_kernel_timing(int enable) { return skv::timing_enable(enable != 0); }
+// The tables of layers [l0, l0 + nl) of a residual-mode blob as a blob of
+// their own (header with the part's layer and table counts, the part's
+// records, and in exponent mode its slabs' base bytes), registered once and
+// kept with the parent until skv_free releases both.
+static int layer_part(Blob* b, uint32_t l0, uint32_t nl, Blob** out) {
+    std::lock_guard<std::mutex> lk(b->part_mu);
+    auto key = std::make_pair(l0, nl);
+    auto it = b->parts.find(key);
+    if (it == b->parts.end()) {
+        skv_shape one = b->shape, part = b->shape;
+        one.layers = 1;
+        part.layers = nl;
+        const uint64_t per_layer = skv::table_count(one);
+        const size_t size = skv::blob_size(part);
+        uint8_t* bytes = static_cast<uint8_t*>(std::malloc(size));
+        if (!bytes) return SKV_ERR_NOMEM;
+        std::memcpy(bytes, b->bytes, skv::kHeaderBytes);
+        skv::wr32(bytes + 8, uint32_t(per_layer * nl));
+        skv::wr32(bytes + 12, nl);
+        skv::wr64(bytes + 32, size);
+        std::memcpy(bytes + skv::kHeaderBytes, b->bytes + skv::kHeaderBytes + l0 * per_layer * skv::kTableRecord,
+                    nl * per_layer * skv::kTableRecord);
+        if (b->shape.mode == SKV_RESIDUAL_EXP) {
+            const size_t bases = skv::kHeaderBytes + skv::table_count(b->shape) * skv::kTableRecord;
+            std::memcpy(bytes + skv::kHeaderBytes + nl * per_layer * skv::kTableRecord,
+                        b->bytes + bases + size_t(l0) * b->shape.kv, size_t(nl) * b->shape.kv);
+        }
+        int rc = skv::validate_blob(bytes, size);
+        void* handle = nullptr;
+        if (rc == SKV_OK) {
+            rc = register_blob(bytes, size, &handle);
+        } else {
+            std::free(bytes);
+        }
+        if (rc != SKV_OK) return rc;
+        it = b->parts.emplace(key, handle).first;
+    }
+    *out = find_blob(it->second);
+    return *out ? SKV_OK : SKV_ERR_TABLES;
+}
+
+int skv_transfer(const void* tables_blob, const skv_shape* s, uint32_t layers_per_chunk, const void* d_target,
+                 const void* d_aux_send, void* h_wire, size_t wire_capacity, size_t* wire_bytes,
+                 uint64_t* chunk_offsets, const void* d_aux_recv, void* d_out, size_t out_capacity, void* d_work,
+                 size_t* work_bytes, hipStream_t stream) {
+    if (!tables_blob || !s || !wire_bytes || !work_bytes) return SKV_ERR_ARG;
+    if (!skv::shape_supported(*s, true) || s->mode == SKV_CHECKERBOARD) return SKV_ERR_SHAPE;
+    Blob* b = find_blob(tables_blob);
+    if (!b) return SKV_ERR_ARG;
+    if (!same_geometry(b->shape, *s)) return SKV_ERR_TABLES;
+    if (layers_per_chunk == 0 || layers_per_chunk > s->layers) return SKV_ERR_ARG;
+
+    const uint32_t nc = (s->layers + layers_per_chunk - 1) / layers_per_chunk;
+    skv_shape cs = *s;
+    cs.layers = layers_per_chunk;
+    const uint32_t raw = skv::kSyms * skv::elem_bytes(s->dtype);
+    const uint64_t n_chunk = skv::stream_count(cs);
+    const uint64_t bound_chunk = skv::kHeaderBytes + 8 * (n_chunk + 1) + n_chunk * raw;
+    const uint64_t n_all = skv::stream_count(*s);
+    const uint64_t wire_bound = uint64_t(nc) * (skv::kHeaderBytes + 8) + 8 * n_all + n_all * raw;
+    const uint64_t enc_need = skv::encode_work_bytes(n_chunk, raw);
+    const uint64_t dec_need = 256;
+    const uint64_t slot = align256(bound_chunk);
+    const uint64_t need = 4 * slot + align256(enc_need) + dec_need;
+    if (!h_wire || !d_work) {
+        if (!h_wire) *wire_bytes = wire_bound;
+        if (!d_work) *work_bytes = need;
+        return SKV_OK;
+    }
+    if (*work_bytes < need) {
+        *work_bytes = need;
+        return SKV_ERR_CAPACITY;
+    }
+    if (!d_target || !d_aux_send || !d_aux_recv || !d_out || !chunk_offsets) return SKV_ERR_ARG;
+    if (g_timing_on) return SKV_ERR_ARG;
+    const uint64_t layer_bytes = uint64_t(s->kv) * s->tokens * s->channels * skv::elem_bytes(s->dtype);
+    if (out_capacity < layer_bytes * s->layers) return SKV_ERR_CAPACITY;
+
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return SKV_ERR_DEVICE;
+    std::vector<Blob*> part(nc);
+    std::vector<skv_shape> shp(nc);
+    for (uint32_t c = 0; c < nc; ++c) {
+        const uint32_t l0 = c * layers_per_chunk;
+        shp[c] = *s;
+        shp[c].layers = std::min(layers_per_chunk, s->layers - l0);
+        const int rc = layer_part(b, l0, shp[c].layers, &part[c]);
+        if (rc != SKV_OK) return rc;
+    }
+
+    // streams (default priority) and per-chunk events
+    hipStream_t s_enc = nullptr, s_d2h = nullptr, s_h2d = nullptr, s_dec = nullptr;
+    hipEvent_t ev_start = nullptr;
+    std::vector<hipEvent_t> ev_enc(nc, nullptr), ev_d2h(nc, nullptr), ev_h2d(nc, nullptr);
+    bool ok = hipStreamCreateWithFlags(&s_enc, hipStreamNonBlocking) == hipSuccess &&
+              hipStreamCreateWithFlags(&s_d2h, hipStreamNonBlocking) == hipSuccess &&
+              hipStreamCreateWithFlags(&s_h2d, hipStreamNonBlocking) == hipSuccess &&
+              hipStreamCreateWithFlags(&s_dec, hipStreamNonBlocking) == hipSuccess &&
+              hipEventCreateWithFlags(&ev_start, hipEventDisableTiming) == hipSuccess;
+    for (uint32_t c = 0; ok && c < nc; ++c)
+        ok = hipEventCreateWithFlags(&ev_enc[c], hipEventDisableTiming) == hipSuccess &&
+             hipEventCreateWithFlags(&ev_d2h[c], hipEventDisableTiming) == hipSuccess &&
+             hipEventCreateWithFlags(&ev_h2d[c], hipEventDisableTiming) == hipSuccess;
+    // the caller's earlier work on its stream (inputs, outputs) comes first
+    ok = ok && hipEventRecord(ev_start, stream) == hipSuccess &&
+         hipStreamWaitEvent(s_enc, ev_start, 0) == hipSuccess &&
+         hipStreamWaitEvent(s_dec, ev_start, 0) == hipSuccess;
+    // device tables of every part before either side starts
+    const skv::DevTables* dt = nullptr;
+    for (uint32_t c = 0; ok && c < nc; ++c) ok = device_tables(part[c], s_enc, &dt) == SKV_OK;
+
+    uint8_t* w = static_cast<uint8_t*>(d_work);
+    uint8_t* cont[2] = {w, w + slot};
+    uint8_t* recv[2] = {w + 2 * slot, w + 3 * slot};
+    uint8_t* enc_work = w + 4 * slot;
+    uint8_t* dec_work = enc_work + align256(enc_need);
+    uint8_t* wire = static_cast<uint8_t*>(h_wire);
+    const uint8_t* tgt = static_cast<const uint8_t*>(d_target);
+    const uint8_t* aux_s = static_cast<const uint8_t*>(d_aux_send);
+    const uint8_t* aux_r = static_cast<const uint8_t*>(d_aux_recv);
+    uint8_t* out = static_cast<uint8_t*>(d_out);
+
+    std::mutex mu;
+    std::condition_variable cv;
+    uint32_t produced = 0;                    // chunks whose device-to-host copy is queued
+    bool stop = false;
+    int send_rc = ok ? SKV_OK : SKV_ERR_DEVICE, recv_rc = SKV_OK;
+    std::vector<uint64_t> size(nc, 0);
+
+    // Receiver: host-to-device copy of each chunk as it arrives (the next
+    // chunk's copy queued before the current chunk's decode), then decode.
+    auto receiver = [&] {
+        t_release_staging = true;
+        if (hipSetDevice(dev) != hipSuccess) {
+            std::lock_guard<std::mutex> lk(mu);
+            recv_rc = SKV_ERR_DEVICE;
+            stop = true;
+            cv.notify_all();
+            return;
+        }
+        uint32_t next = 0;
+        for (uint32_t c = 0; c < nc; ++c) {
+            uint32_t avail;
+            {
+                std::unique_lock<std::mutex> lk(mu);
+                cv.wait(lk, [&] { return produced > c || stop; });
+                if (produced <= c) return;
+                avail = produced;
+            }
+            int rc = SKV_OK;
+            for (; rc == SKV_OK && next < avail && next <= c + 1; ++next) {
+                // recv[next & 1] last held chunk next - 2, decoded before this point
+                if (hipStreamWaitEvent(s_h2d, ev_d2h[next], 0) != hipSuccess ||
+                    hipMemcpyAsync(recv[next & 1], wire + chunk_offsets[next], size[next], hipMemcpyHostToDevice,
+                                   s_h2d) != hipSuccess ||
+                    hipEventRecord(ev_h2d[next], s_h2d) != hipSuccess)
+                    rc = SKV_ERR_DEVICE;
+            }
+            if (rc == SKV_OK && hipStreamWaitEvent(s_dec, ev_h2d[c], 0) != hipSuccess) rc = SKV_ERR_DEVICE;
+            const uint64_t off = uint64_t(c) * layers_per_chunk * layer_bytes;
+            size_t wb = dec_need;
+            if (rc == SKV_OK)
+                rc = decode_blocks(part[c]->bytes, recv[c & 1], size[c], false, 0, 0, aux_r + off, out + off,
+                                   shp[c].layers * layer_bytes, dec_work, &wb, s_dec, false);
+            if (rc != SKV_OK) {
+                std::lock_guard<std::mutex> lk(mu);
+                recv_rc = rc;
+                stop = true;
+                cv.notify_all();
+                return;
+            }
+        }
+    };
+    std::thread rx;
+    if (send_rc == SKV_OK) rx = std::thread(receiver);
+
+    // Sender (this thread): encode chunk c into cont[c & 1] while the copies
+    // and the decode of earlier chunks proceed on their own streams.
+    uint64_t wire_off = 0;
+    for (uint32_t c = 0; send_rc == SKV_OK && c < nc; ++c) {
+        {
+            std::lock_guard<std::mutex> lk(mu);
+            if (stop) break;
+        }
+        int rc = SKV_OK;
+        if (c >= 2 && hipStreamWaitEvent(s_enc, ev_d2h[c - 2], 0) != hipSuccess) rc = SKV_ERR_DEVICE;
+        const uint64_t off = uint64_t(c) * layers_per_chunk * layer_bytes;
+        size_t bytes = 0, wb = enc_need;
+        if (rc == SKV_OK)
+            rc = encode_impl(part[c]->bytes, &shp[c], tgt + off, aux_s + off, cont[c & 1], bound_chunk, &bytes, enc_work,
+                             &wb, s_enc, false);
+        if (rc == SKV_OK && bytes > wire_capacity - wire_off) rc = SKV_ERR_CAPACITY;
+        if (rc == SKV_OK &&
+            (hipEventRecord(ev_enc[c], s_enc) != hipSuccess || hipStreamWaitEvent(s_d2h, ev_enc[c], 0) != hipSuccess ||
+             hipMemcpyAsync(wire + wire_off, cont[c & 1], bytes, hipMemcpyDeviceToHost, s_d2h) != hipSuccess ||
+             hipEventRecord(ev_d2h[c], s_d2h) != hipSuccess))
+            rc = SKV_ERR_DEVICE;
+        std::lock_guard<std::mutex> lk(mu);
+        if (rc != SKV_OK) {
+            send_rc = rc;
+            stop = true;
+        } else {
+            chunk_offsets[c] = wire_off;
+            size[c] = bytes;
+            wire_off += bytes;
+            produced = c + 1;
+        }
+        cv.notify_all();
+    }
+    if (rx.joinable()) rx.join();
+    // nothing queued by this call may still run once it returns
+    for (hipStream_t st : {s_enc, s_d2h, s_h2d, s_dec})
+        if (st && hipStreamSynchronize(st) != hipSuccess && send_rc == SKV_OK) send_rc = SKV_ERR_DEVICE;
+    for (uint32_t c = 0; c < nc; ++c)
+        for (hipEvent_t e : {ev_enc[c], ev_d2h[c], ev_h2d[c]})
+            if (e) (void)hipEventDestroy(e);
+    if (ev_start) (void)hipEventDestroy(ev_start);
+    for (hipStream_t st : {s_enc, s_d2h, s_h2d, s_dec})
+        if (st) (void)hipStreamDestroy(st);
+    if (send_rc == SKV_ERR_CAPACITY) {
+        *wire_bytes = wire_bound;
+        return send_rc;
+    }
+    if (send_rc != SKV_OK) return send_rc;
+    if (recv_rc != SKV_OK) return recv_rc;
+    chunk_offsets[nc] = wire_off;
+    *wire_bytes = wire_off;
+    return SKV_OK;
+}
+
+int skv_kernel_timing(int enable) {
+    const int rc = skv::timing_enable(enable != 0);
+    if (rc == SKV_OK) g_timing_on = enable != 0;
+    return rc;
+}
 
 int skv_kernel_times(const char** names, float* ms, int capacity) {
     if (capacity < 0) return SKV_ERR_ARG;

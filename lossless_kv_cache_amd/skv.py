@@ -61,6 +61,9 @@ def lib():
         L.skv_decode_range.restype = ctypes.c_int
         L.skv_decode_range.argtypes = [vp, vp, sz, u32, u32, vp, vp, sz, vp, psz, vp]
         L.skv_free.restype = None
+        L.skv_transfer.argtypes = [vp, sp, u32, vp, vp, vp, sz, psz, ctypes.POINTER(ctypes.c_uint64), vp, vp, sz,
+                                   vp, psz, vp]
+        L.skv_transfer.restype = ctypes.c_int
         L.skv_free.argtypes = [vp]
         L.skv_kernel_timing.restype = ctypes.c_int
         L.skv_kernel_timing.argtypes = [ctypes.c_int]
@@ -235,6 +238,47 @@ def decode_range(tables: Tables, container: torch.Tensor, token_begin: int, toke
                  aux: torch.Tensor) -> torch.Tensor:
     """Decode a token range against its predictor; returns a tensor shaped like aux."""
     return decode_range_into(tables, container, token_begin, token_end, aux, torch.empty_like(aux))
+
+
+class Transfer:
+    """Chunked encode -> host -> decode pipeline with reusable buffers: a
+    device workspace and a page-locked host wire buffer sized for the bound."""
+
+    def __init__(self, tables: Tables, tokens: int, layers_per_chunk: int, device=None):
+        self.tables = tables
+        self.shape = tables.shape(tokens)
+        self.layers_per_chunk = layers_per_chunk
+        dev = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
+        wire, wb = ctypes.c_size_t(), ctypes.c_size_t()
+        _check(lib().skv_transfer(tables.ptr, ctypes.byref(self.shape), layers_per_chunk, None, None, None, 0,
+                                  ctypes.byref(wire), None, None, None, 0, None, ctypes.byref(wb), None),
+               "skv_transfer(size query)")
+        self.n_chunks = -(-self.shape.layers // layers_per_chunk)
+        self.work = torch.empty(wb.value, dtype=torch.uint8, device=dev)
+        self.wire = torch.empty(wire.value, dtype=torch.uint8, pin_memory=True)
+        self.offsets = (ctypes.c_uint64 * (self.n_chunks + 1))()
+
+    def __call__(self, target: torch.Tensor, aux_send: torch.Tensor, aux_recv: torch.Tensor,
+                 out: torch.Tensor) -> tuple[torch.Tensor, list[int]]:
+        """Moves target through the pipeline into out; returns (wire bytes view, chunk offsets)."""
+        nbytes = ctypes.c_size_t()
+        wb = ctypes.c_size_t(self.work.numel())
+        rc = lib().skv_transfer(self.tables.ptr, ctypes.byref(self.shape), self.layers_per_chunk,
+                                _dev(target, "target"), _dev(aux_send, "aux_send"), self.wire.data_ptr(),
+                                self.wire.numel(), ctypes.byref(nbytes), self.offsets, _dev(aux_recv, "aux_recv"),
+                                _dev(out, "out"), out.numel() * out.element_size(), self.work.data_ptr(),
+                                ctypes.byref(wb), _stream())
+        _check(rc, "skv_transfer")
+        return self.wire[: nbytes.value], list(self.offsets)
+
+
+def transfer(tables: Tables, target: torch.Tensor, aux_send: torch.Tensor, aux_recv: torch.Tensor,
+             layers_per_chunk: int) -> tuple[torch.Tensor, torch.Tensor, list[int]]:
+    """Move a residual-mode cache through the pipeline; returns (reconstruction, wire bytes, chunk offsets)."""
+    tr = Transfer(tables, tokens_of(tables, target), layers_per_chunk, target.device)
+    out = torch.empty_like(aux_recv)
+    wire, offsets = tr(target, aux_send, aux_recv, out)
+    return out, wire.clone(), offsets
 
 
 def kernel_timing(enable: bool) -> None:

@@ -26,8 +26,8 @@ def skv():
 def test_exports_every_declared_symbol(skv):
     text = open(os.path.join(ROOT, "include", "skv.h")).read()
     names = set(re.findall(r"^\s*(?:int|void|uint32_t|const char\*)\s+(skv_\w+)\s*\(", text, re.M))
-    assert {"skv_fit_tables", "skv_load_tables", "skv_encode", "skv_decode", "skv_decode_range", "skv_free",
-            "skv_version", "skv_strerror"} <= names
+    assert {"skv_fit_tables", "skv_load_tables", "skv_encode", "skv_decode", "skv_decode_range", "skv_transfer",
+            "skv_free", "skv_version", "skv_strerror"} <= names
     L = ctypes.CDLL(skv.LIB_PATH)
     for n in sorted(names):
         assert hasattr(L, n), n
@@ -136,3 +136,40 @@ def test_size_queries_and_shape_errors(skv):
     assert L.skv_decode_range(tabs.ptr, None, 0, 0, 128, None, None, 0, None, ctypes.byref(wr), None) == 0
     assert wr.value == wd.value > 0
     assert L.skv_decode_range(dummy, None, 0, 0, 128, None, None, 0, None, ctypes.byref(wr), None) == skv.ERR_ARG
+
+
+def test_transfer_size_queries_and_argument_errors(skv):
+    """skv_transfer's two-phase sizing: the wire bound is the sum of the
+    chunk containers' bounds (every stream raw), and the workspace holds two
+    container buffers per side; no device memory is touched."""
+    L = skv.lib()
+    cfg = gen.CONFIGS[0].with_tokens(256, layers=3, channels=64)
+    ct, cp = _residual_calib(cfg)
+    tabs = skv.fit_tables(skv.BF16, skv.RESIDUAL, 3, 2, 64, ct, cp, 256)
+    s = tabs.shape(1024)
+    wire, work = ctypes.c_size_t(), ctypes.c_size_t()
+
+    def query(lpc, shape=s, t=tabs):
+        return L.skv_transfer(t.ptr, ctypes.byref(shape), lpc, None, None, None, 0, ctypes.byref(wire), None, None,
+                              None, 0, None, ctypes.byref(work), None)
+
+    def bound(layers):
+        n = layers * 2 * (1024 // 128) * (64 // 32)
+        return 64 + 8 * (n + 1) + n * 4096 * 2
+
+    for lpc, chunks in ((1, [1, 1, 1]), (2, [2, 1]), (3, [3])):
+        assert query(lpc) == 0
+        assert wire.value == sum(bound(c) for c in chunks)
+        assert work.value >= 4 * bound(lpc) + 256
+    assert query(0) == skv.ERR_ARG and query(4) == skv.ERR_ARG
+    dummy = ctypes.c_void_p(12345)
+    assert L.skv_transfer(dummy, ctypes.byref(s), 1, None, None, None, 0, ctypes.byref(wire), None, None, None, 0,
+                          None, ctypes.byref(work), None) == skv.ERR_ARG
+    other = skv.make_shape(skv.BF16, skv.RESIDUAL, 2, 2, 1024, 64)
+    assert query(1, other) == skv.ERR_TABLES
+    ragged = skv.make_shape(skv.BF16, skv.RESIDUAL, 3, 2, 1000, 64)
+    assert query(1, ragged) == skv.ERR_SHAPE
+    cb_cfg = gen.CONFIGS[4].with_tokens(256, channels=64)
+    cc, cg = gen.dckv_draw(cb_cfg, gen.CALIB, tokens=256)
+    cb = skv.fit_tables(skv.INT16, skv.CHECKERBOARD, 1, 1, 64, cc.numpy(), cg.numpy(), 256)
+    assert query(1, cb.shape(1024), cb) == skv.ERR_SHAPE

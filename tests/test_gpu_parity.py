@@ -586,3 +586,78 @@ def test_full_size_checkerboard(skv, orc):
     back = skv.decode(tabs, cont, G)
     assert torch.equal(back, coef)
     say("[parity] cfg4: sampled streams identical, round trip exact")
+
+
+@pytest.mark.parametrize("cid,exp,layers,lpc", [(0, False, 5, 2), (2, True, 3, 1), (2, False, 4, 4)])
+def test_transfer_pipeline(skv, orc, cid, exp, layers, lpc):
+    """Chunked encode -> host -> decode: every chunk on the wire is
+    byte-identical to the oracle's container of those layers, with tables the
+    oracle fits on those layers' calibration alone; the reconstruction is
+    exact; a chunk container decodes on its own."""
+    cfg = gen.CONFIGS[cid].with_tokens(384, layers=layers, channels=160)
+    dt = _dt(cfg, skv)
+    mode, omode = (skv.RESIDUAL_EXP, orc.RESIDUAL_EXP) if exp else (skv.RESIDUAL, orc.RESIDUAL)
+    t, p = gen.residual_array(cfg, device="cuda")
+    ct, cp = [a.numpy() for a in gen.residual_array(cfg, gen.CALIB, tokens=256)]
+    tabs = skv.fit_tables(dt, mode, layers, cfg.kv, cfg.channels, ct, cp, 256)
+    say(f"[parity] transfer {cfg.dtype} exp={exp} layers={layers} per chunk={lpc}")
+    recv_p = p.clone()
+    out, wire, offs = skv.transfer(tabs, t, p, recv_p, lpc)
+    assert torch.equal(out, t)
+    wire = wire.numpy().tobytes()
+    nc = -(-layers // lpc)
+    assert len(offs) == nc + 1 and offs[0] == 0 and offs[-1] == len(wire)
+    tn, pn = t.cpu().numpy(), p.cpu().numpy()
+    for c in range(nc):
+        l0, l1 = c * lpc, min(layers, (c + 1) * lpc)
+        oshape = orc.make_shape(dt, omode, l1 - l0, cfg.kv, cfg.tokens, cfg.channels)
+        blob = orc.fit_tables(oshape, np.ascontiguousarray(ct[l0:l1]), np.ascontiguousarray(cp[l0:l1]), 256)
+        want = orc.encode(blob, oshape, np.ascontiguousarray(tn[l0:l1]), np.ascontiguousarray(pn[l0:l1]), threads=8)
+        assert wire[offs[c]:offs[c + 1]] == want, c
+        if c == nc - 1:
+            part = skv.load_tables(blob)
+            chunk = torch.from_numpy(np.frombuffer(want, dtype=np.uint8).copy()).cuda()
+            assert torch.equal(skv.decode(part, chunk, p[l0:l1].contiguous()), t[l0:l1])
+
+
+def test_transfer_wire_too_small(skv, orc):
+    """A wire buffer that cannot hold the first chunk stops the pipeline with
+    SKV_ERR_CAPACITY; the same object then runs with a buffer of the bound."""
+    cfg = gen.CONFIGS[0].with_tokens(256, layers=3, channels=64)
+    t, p = gen.residual_array(cfg, device="cuda")
+    ct, cp = [a.numpy() for a in gen.residual_array(cfg, gen.CALIB, tokens=256)]
+    tabs = skv.fit_tables(skv.BF16, skv.RESIDUAL, 3, cfg.kv, cfg.channels, ct, cp, 256)
+    tr = skv.Transfer(tabs, cfg.tokens, 1)
+    full = tr.wire
+    tr.wire = full[:1000]
+    out = torch.zeros_like(t)
+    with pytest.raises(skv.SkvError) as e:
+        tr(t, p, p, out)
+    assert e.value.status == skv.ERR_CAPACITY
+    tr.wire = full
+    tr(t, p, p, out)
+    assert torch.equal(out, t)
+
+
+def test_transfer_full_size_e4m3(skv, orc):
+    """The Qwen3-8B-shaped e4m3 cache in chunks of 4 layers: exact
+    reconstruction, and the first and last chunk containers equal the
+    one-shot encoder's containers of those layers."""
+    cfg = gen.CONFIGS[2]
+    say(f"[parity] transfer cfg2: generating {cfg.values} values on GPU")
+    t, p = gen.residual_array(cfg, device="cuda")
+    ct, cp = [a.numpy() for a in gen.residual_array(cfg, gen.CALIB, tokens=256)]
+    tabs = skv.fit_tables(skv.E4M3, skv.RESIDUAL, cfg.layers, cfg.kv, cfg.channels, ct, cp, 256)
+    tr = skv.Transfer(tabs, cfg.tokens, 4)
+    out = torch.empty_like(t)
+    wire, offs = tr(t, p, p, out)
+    assert torch.equal(out, t)
+    ratio = cfg.raw_bytes / wire.numel()
+    say(f"[parity] transfer cfg2: {len(offs) - 1} chunks, ratio {ratio:.4f}")
+    assert ratio > 3.5
+    for c in (0, len(offs) - 2):
+        l0, l1 = 4 * c, min(cfg.layers, 4 * c + 4)
+        part = skv.fit_tables(skv.E4M3, skv.RESIDUAL, l1 - l0, cfg.kv, cfg.channels,
+                              np.ascontiguousarray(ct[l0:l1]), np.ascontiguousarray(cp[l0:l1]), 256)
+        want = skv.encode(part, t[l0:l1].contiguous(), p[l0:l1].contiguous())
+        assert torch.equal(wire[offs[c]:offs[c + 1]], want.cpu()), c
