@@ -145,3 +145,27 @@ def test_expmode_roundtrip_and_ratio(orc, cid):
     # the synthetic predictor's error grows with magnitude (e4m3 rounding), so the
     # exponent classes separate narrow and wide residuals
     assert sizes[orc.RESIDUAL_EXP] < sizes[orc.RESIDUAL]
+
+
+@pytest.mark.parametrize("exp", [False, True])
+def test_layer_slice_of_a_blob_is_the_fit_of_those_layers(orc, exp):
+    """Tables are fitted per (layer, K|V) slab from that slab's calibration
+    alone, so the blob fitted on a run of layers holds exactly the parent
+    blob's records (and, with exponent classes, base bytes) of those layers;
+    the transfer pipeline's per-chunk containers rely on this."""
+    cfg = gen.CONFIGS[0].with_tokens(256, layers=3, channels=64)
+    mode = orc.RESIDUAL_EXP if exp else orc.RESIDUAL
+    ct, cp = [a.numpy() for a in gen.residual_array(cfg, gen.CALIB, tokens=256)]
+    full = orc.fit_tables(orc.make_shape(orc.BF16, mode, 3, cfg.kv, 128, cfg.channels), ct, cp, 256)
+    part = orc.fit_tables(orc.make_shape(orc.BF16, mode, 2, cfg.kv, 128, cfg.channels),
+                          np.ascontiguousarray(ct[1:]), np.ascontiguousarray(cp[1:]), 256)
+    per_layer = cfg.kv * (16 if exp else cfg.channels)
+    rec = 514
+    assert part[64 + 0:64 + 2 * per_layer * rec] == full[64 + per_layer * rec:64 + 3 * per_layer * rec]
+    if exp:
+        assert list(orc.blob_bases(part)) == list(orc.blob_bases(full))[cfg.kv:]
+    assert int.from_bytes(part[12:16], "little") == 2
+    assert int.from_bytes(part[8:12], "little") == 2 * per_layer
+    assert int.from_bytes(part[32:40], "little") == len(part)
+    # everything else in the header is the parent's
+    assert part[:8] == full[:8] and part[16:32] == full[16:32] and part[40:64] == full[40:64]
