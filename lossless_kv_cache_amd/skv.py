@@ -159,6 +159,50 @@ def _stream() -> int:
     return torch.cuda.current_stream().cuda_stream
 
 
+def elem_bytes(dtype: int) -> int:
+    return 1 if dtype == E4M3 else 2
+
+
+def _layout(tables: "Tables", tokens: int) -> tuple:
+    if tables.mode == CHECKERBOARD:
+        return (tokens, tables.channels)
+    return (tables.layers, tables.kv, tokens, tables.channels)
+
+
+def _check_cache(t: torch.Tensor, name: str, tables: "Tables", tokens: int) -> int:
+    """A contiguous device array in the tables' layout with `tokens` tokens and
+    elements of the tables' width; the kernels read or write exactly that many
+    bytes, so anything else is refused here before the library is called."""
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a device tensor")
+    eb = elem_bytes(tables.dtype)
+    if t.element_size() != eb:
+        raise ValueError(f"{name}: {t.element_size()}-byte elements, the tables code {eb}-byte elements")
+    want = _layout(tables, tokens)
+    if tuple(t.shape) != want:
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {want}")
+    return _dev(t, name)
+
+
+def _decode_buffers(aux: torch.Tensor, out: torch.Tensor, tables: "Tables", tokens=None) -> tuple[int, int, int]:
+    """Decode: the predictor (or G) in the tables' layout (with `tokens`
+    tokens when given) and an output of the same element width.  The library
+    checks the capacity it is given against the container header; the
+    capacity passed is the smaller of the output's and the predictor's sizes,
+    so neither is read or written past its end.  Returns (aux, out, capacity)."""
+    nd = len(_layout(tables, 0))
+    if not isinstance(aux, torch.Tensor) or aux.dim() != nd:
+        raise ValueError(f"aux must be a {nd}-D device tensor in the tables' layout")
+    if tokens is None:
+        tokens = aux.shape[0] if tables.mode == CHECKERBOARD else aux.shape[2]
+    if not isinstance(out, torch.Tensor) or out.element_size() != aux.element_size():
+        raise ValueError(f"out must be a device tensor of {aux.element_size()}-byte elements")
+    pa = _check_cache(aux, "aux", tables, tokens)
+    po = _dev(out, "out")
+    cap = min(out.numel() * out.element_size(), aux.numel() * aux.element_size())
+    return pa, po, cap
+
+
 def tokens_of(tables: Tables, target: torch.Tensor) -> int:
     if tables.mode == CHECKERBOARD:
         if target.dim() != 2:
@@ -184,9 +228,13 @@ class Encoder:
 
     def __call__(self, target: torch.Tensor, aux: torch.Tensor) -> torch.Tensor:
         """Returns a view of the container (valid until the next call)."""
+        pt = _check_cache(target, "target", self.tables, self.shape.tokens)
+        pa = _check_cache(aux, "aux", self.tables, self.shape.tokens)
+        if target.device != self.out.device or aux.device != self.out.device:
+            raise ValueError("target and aux must be on the encoder's device")
         ob = ctypes.c_size_t()
         wb = ctypes.c_size_t(self.work.numel())
-        rc = lib().skv_encode(self.tables.ptr, ctypes.byref(self.shape), _dev(target, "target"), _dev(aux, "aux"),
+        rc = lib().skv_encode(self.tables.ptr, ctypes.byref(self.shape), pt, pa,
                               self.out.data_ptr(), self.out.numel(), ctypes.byref(ob), self.work.data_ptr(),
                               ctypes.byref(wb), _stream())
         _check(rc, "skv_encode")
@@ -202,7 +250,16 @@ def encode(tables: Tables, target: torch.Tensor, aux: torch.Tensor) -> torch.Ten
 _decode_work = {}
 
 
+def _check_container(container: torch.Tensor) -> int:
+    ptr = _dev(container, "container")
+    if container.element_size() != 1:
+        raise ValueError("container must be a uint8 device tensor")
+    return ptr
+
+
 def decode_into(tables: Tables, container: torch.Tensor, aux: torch.Tensor, out: torch.Tensor) -> torch.Tensor:
+    pc = _check_container(container)
+    pa, po, cap = _decode_buffers(aux, out, tables)
     key = container.device
     work = _decode_work.get(key)
     if work is None:
@@ -210,8 +267,7 @@ def decode_into(tables: Tables, container: torch.Tensor, aux: torch.Tensor, out:
         _check(lib().skv_decode(tables.ptr, None, 0, None, None, 0, None, ctypes.byref(wb), None), "skv_decode(size)")
         work = _decode_work[key] = torch.empty(wb.value, dtype=torch.uint8, device=key)
     wb = ctypes.c_size_t(work.numel())
-    rc = lib().skv_decode(tables.ptr, _dev(container, "container"), container.numel(), _dev(aux, "aux"),
-                          _dev(out, "out"), out.numel() * out.element_size(), work.data_ptr(), ctypes.byref(wb),
+    rc = lib().skv_decode(tables.ptr, pc, container.numel(), pa, po, cap, work.data_ptr(), ctypes.byref(wb),
                           _stream())
     _check(rc, "skv_decode")
     return out
@@ -220,6 +276,11 @@ def decode_into(tables: Tables, container: torch.Tensor, aux: torch.Tensor, out:
 def decode_range_into(tables: Tables, container: torch.Tensor, token_begin: int, token_end: int, aux: torch.Tensor,
                       out: torch.Tensor) -> torch.Tensor:
     """Decode tokens [token_begin, token_end) of every slab; aux and out hold that range only."""
+    # the library's range rules first (same status), then the buffers of the range
+    if (tables.mode == CHECKERBOARD or not 0 <= token_begin < token_end or token_begin % 128 or token_end % 128):
+        raise SkvError(ERR_SHAPE, "skv_decode_range")
+    pc = _check_container(container)
+    pa, po, cap = _decode_buffers(aux, out, tables, token_end - token_begin)
     key = container.device
     work = _decode_work.get(key)
     if work is None:
@@ -227,8 +288,7 @@ def decode_range_into(tables: Tables, container: torch.Tensor, token_begin: int,
         _check(lib().skv_decode(tables.ptr, None, 0, None, None, 0, None, ctypes.byref(wb), None), "skv_decode(size)")
         work = _decode_work[key] = torch.empty(wb.value, dtype=torch.uint8, device=key)
     wb = ctypes.c_size_t(work.numel())
-    rc = lib().skv_decode_range(tables.ptr, _dev(container, "container"), container.numel(), token_begin, token_end,
-                                _dev(aux, "aux"), _dev(out, "out"), out.numel() * out.element_size(),
+    rc = lib().skv_decode_range(tables.ptr, pc, container.numel(), token_begin, token_end, pa, po, cap,
                                 work.data_ptr(), ctypes.byref(wb), _stream())
     _check(rc, "skv_decode_range")
     return out
@@ -261,13 +321,16 @@ class Transfer:
     def __call__(self, target: torch.Tensor, aux_send: torch.Tensor, aux_recv: torch.Tensor,
                  out: torch.Tensor) -> tuple[torch.Tensor, list[int]]:
         """Moves target through the pipeline into out; returns (wire bytes view, chunk offsets)."""
+        T = self.shape.tokens
+        pt = _check_cache(target, "target", self.tables, T)
+        ps = _check_cache(aux_send, "aux_send", self.tables, T)
+        pr = _check_cache(aux_recv, "aux_recv", self.tables, T)
+        po = _check_cache(out, "out", self.tables, T)
         nbytes = ctypes.c_size_t()
         wb = ctypes.c_size_t(self.work.numel())
-        rc = lib().skv_transfer(self.tables.ptr, ctypes.byref(self.shape), self.layers_per_chunk,
-                                _dev(target, "target"), _dev(aux_send, "aux_send"), self.wire.data_ptr(),
-                                self.wire.numel(), ctypes.byref(nbytes), self.offsets, _dev(aux_recv, "aux_recv"),
-                                _dev(out, "out"), out.numel() * out.element_size(), self.work.data_ptr(),
-                                ctypes.byref(wb), _stream())
+        rc = lib().skv_transfer(self.tables.ptr, ctypes.byref(self.shape), self.layers_per_chunk, pt, ps,
+                                self.wire.data_ptr(), self.wire.numel(), ctypes.byref(nbytes), self.offsets, pr, po,
+                                out.numel() * out.element_size(), self.work.data_ptr(), ctypes.byref(wb), _stream())
         _check(rc, "skv_transfer")
         return self.wire[: nbytes.value], list(self.offsets)
 

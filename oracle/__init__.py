@@ -242,7 +242,8 @@ def n_streams(shape: Shape) -> int:
     return lib().skvo_n_streams(ctypes.byref(shape))
 
 
-def encode(blob: bytes, shape: Shape, target: np.ndarray, aux: np.ndarray, threads: int = 1) -> bytes:
+def encode_array(blob: bytes, shape: Shape, target: np.ndarray, aux: np.ndarray, threads: int = 1) -> np.ndarray:
+    """The container as a uint8 array (no copy of large outputs)."""
     b = np.frombuffer(blob, dtype=np.uint8).copy()
     t = np.ascontiguousarray(target)
     a = np.ascontiguousarray(aux)
@@ -252,7 +253,11 @@ def encode(blob: bytes, shape: Shape, target: np.ndarray, aux: np.ndarray, threa
     rc = lib().skvo_encode(_ptr(b), len(b), ctypes.byref(shape), _ptr(t), _ptr(a), _ptr(out), cap, ctypes.byref(need), threads)
     if rc < 0:
         raise RuntimeError(f"oracle encode failed: {rc}")
-    return out[:rc].tobytes()
+    return out[:rc]
+
+
+def encode(blob: bytes, shape: Shape, target: np.ndarray, aux: np.ndarray, threads: int = 1) -> bytes:
+    return encode_array(blob, shape, target, aux, threads).tobytes()
 
 
 def decode_rc(blob: bytes, container: bytes, aux: np.ndarray, out: np.ndarray, threads: int = 1) -> int:

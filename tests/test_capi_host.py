@@ -173,3 +173,56 @@ def test_transfer_size_queries_and_argument_errors(skv):
     cc, cg = gen.dckv_draw(cb_cfg, gen.CALIB, tokens=256)
     cb = skv.fit_tables(skv.INT16, skv.CHECKERBOARD, 1, 1, 64, cc.numpy(), cg.numpy(), 256)
     assert query(1, cb.shape(1024), cb) == skv.ERR_SHAPE
+
+
+def _small_tables(skv, dtype, mode, layers=1, kv=2, channels=64):
+    if mode == skv.CHECKERBOARD:
+        cfg = gen.CONFIGS[4].with_tokens(256, channels=channels)
+        cc, cg = gen.dckv_draw(cfg, gen.CALIB, tokens=256)
+        return skv.fit_tables(skv.INT16, skv.CHECKERBOARD, 1, 1, channels, cc.numpy(), cg.numpy(), 256)
+    cfg = gen.CONFIGS[0 if dtype == skv.BF16 else 2].with_tokens(256, layers=layers, channels=channels)
+    ct, cp = _residual_calib(cfg)
+    return skv.fit_tables(dtype, mode, layers, kv, channels, ct, cp, 256)
+
+
+def test_binding_refuses_mis_sized_device_inputs(skv):
+    """The binding checks every array the kernels read or write against the
+    tables' layout before calling the library: wrong shapes and element
+    widths raise ValueError, and the decode capacity passed to the library is
+    the smaller of the output's and the predictor's sizes.  (Host tensors of
+    the right layout are refused as not device tensors; nothing is launched.)"""
+    import torch
+
+    tabs = _small_tables(skv, skv.E4M3, skv.RESIDUAL)
+    good = torch.zeros((1, 2, 256, 64), dtype=torch.uint8)
+    for bad, what in [(torch.zeros((1, 2, 256, 32), dtype=torch.uint8), "shape"),
+                      (torch.zeros((2, 2, 256, 64), dtype=torch.uint8), "shape"),
+                      (torch.zeros((1, 2, 128, 64), dtype=torch.uint8), "shape"),
+                      (torch.zeros((1, 2, 256, 64), dtype=torch.int16), "byte elements"),
+                      (np.zeros((1, 2, 256, 64), dtype=np.uint8), "device tensor")]:
+        with pytest.raises(ValueError, match=what):
+            skv._check_cache(bad, "target", tabs, 256)
+    with pytest.raises(ValueError, match="device tensor"):
+        skv._check_cache(good, "target", tabs, 256)
+    # decode: out of another element width, and an aux of the wrong rank
+    with pytest.raises(ValueError, match="byte elements"):
+        skv._decode_buffers(good, torch.zeros(good.shape, dtype=torch.int16), tabs)
+    with pytest.raises(ValueError, match="4-D"):
+        skv._decode_buffers(good.view(-1), good, tabs)
+    with pytest.raises(ValueError, match="shape"):
+        skv._decode_buffers(good, good, tabs, tokens=128)
+    # the public entry points refuse before reaching the library
+    with pytest.raises(ValueError):
+        skv.decode_into(tabs, torch.zeros(100, dtype=torch.uint8), good, good)
+    with pytest.raises(skv.SkvError) as e:
+        skv.decode_range_into(tabs, torch.zeros(100, dtype=torch.uint8), 0, 100, good, good)
+    assert e.value.status == skv.ERR_SHAPE
+    # bf16 tables take 2-byte elements; checkerboard arrays are [tokens][channels]
+    tb = _small_tables(skv, skv.BF16, skv.RESIDUAL)
+    with pytest.raises(ValueError, match="byte elements"):
+        skv._check_cache(good, "aux", tb, 256)
+    tc = _small_tables(skv, skv.INT16, skv.CHECKERBOARD)
+    with pytest.raises(ValueError, match="shape"):
+        skv._check_cache(torch.zeros((1, 1, 256, 64), dtype=torch.int16), "target", tc, 256)
+    with pytest.raises(ValueError, match="device tensor"):
+        skv._check_cache(torch.zeros((256, 64), dtype=torch.int16), "target", tc, 256)

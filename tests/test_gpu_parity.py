@@ -5,10 +5,11 @@ The coding path is integer end to end, so there is no tolerance: container
 bytes must equal the oracle's byte for byte and the decode must return the
 target exactly (lossless reconstruction, Speculative KV coding summary,
 'Core idea'; checkerboard decoding in two passes, DCKV page, 'How it
-differs').  Small cases compare whole containers; full-size workloads
-compare sampled streams (the oracle encodes them one by one from the
-gathered tiles) plus the exact GPU round trip.
+differs').  Every case, the full-size workloads included, compares the
+whole container (header, index, payload) with the oracle's, byte for byte,
+and checks the exact GPU round trip.
 """
+import os
 import struct
 import sys
 
@@ -19,6 +20,9 @@ import torch
 from workloads import gen
 
 pytestmark = pytest.mark.gpu
+
+# host threads for the oracle: the CPU share of one GPU on the test machines
+ORACLE_THREADS = max(1, min(16, os.cpu_count() or 1))
 
 
 def say(msg):
@@ -45,6 +49,31 @@ def _parse(c: bytes):
     return n, idx, 64 + 8 * (n + 1)
 
 
+def host_u8(x: torch.Tensor) -> np.ndarray:
+    return x.cpu().numpy().reshape(-1).view(np.uint8)
+
+
+def assert_same_container(got: np.ndarray, want: np.ndarray, what: str):
+    """Byte-for-byte equality of two containers; a mismatch names the first
+    differing part (header, index entry or stream)."""
+    if got.size == want.size and np.array_equal(got, want):
+        return
+    m = min(got.size, want.size)
+    diff = np.nonzero(got[:m] != want[:m])[0]
+    first = int(diff[0]) if diff.size else m
+    n = int(want[32:40].view(np.uint64)[0])
+    head = 64 + 8 * (n + 1)
+    if first < 64:
+        where = f"header byte {first}"
+    elif first < head:
+        where = f"index entry {(first - 64) // 8}"
+    else:
+        offs = want[64:head].view(np.uint64) & np.uint64((1 << 63) - 1)
+        where = f"stream {int(np.searchsorted(offs, np.uint64(first - head), side='right')) - 1}"
+    raise AssertionError(f"{what}: container differs from the oracle's (sizes {got.size} / {want.size}; "
+                         f"first difference at byte {first}, {where})")
+
+
 def residual_case(skv, orc, cfg, device="cuda"):
     t, p = gen.residual_array(cfg, device=device)
     ct, cp = gen.residual_array(cfg, gen.CALIB, tokens=256, device=device)
@@ -61,19 +90,14 @@ def full_compare(skv, orc, t, p, tabs, oshape, what):
     torch.cuda.synchronize()
     tn, pn = t.cpu().numpy(), p.cpu().numpy()
     say(f"[parity] {what}: encode with oracle")
-    want = orc.encode(tabs.bytes(), oshape, tn, pn, threads=8)
-    got = cont.cpu().numpy().tobytes()
-    assert len(got) == len(want), (len(got), len(want))
-    if got != want:
-        n, idx, head = _parse(want)
-        gi = np.frombuffer(got[64:head], dtype=np.uint64)
-        bad = np.nonzero(gi != idx)[0]
-        raise AssertionError(f"container differs; first index mismatch {bad[:5]}")
+    want_a = orc.encode_array(tabs.bytes(), oshape, tn, pn, threads=ORACLE_THREADS)
+    assert_same_container(host_u8(cont), want_a, what)
+    want = want_a.tobytes()
     say(f"[parity] {what}: decode on GPU")
     back = skv.decode(tabs, cont, p)
     assert torch.equal(back, t)
     # the GPU decodes the oracle's container as well
-    back2 = skv.decode(tabs, torch.from_numpy(np.frombuffer(want, dtype=np.uint8).copy()).cuda(), p)
+    back2 = skv.decode(tabs, torch.from_numpy(want_a.copy()).cuda(), p)
     assert torch.equal(back2, t)
     return want
 
@@ -300,36 +324,13 @@ def test_e4m3_corruption_verdicts(skv, orc, exp):
 
 
 def test_exponent_mode_full_size_e4m3(skv, orc):
-    """The Qwen3-8B-shaped e4m3 cache with exponent-conditioned tables: sampled
-    streams equal the oracle's, the round trip is exact, and the container is
-    smaller than with per-channel tables."""
+    """The Qwen3-8B-shaped e4m3 cache with exponent-conditioned tables: the
+    whole container equals the oracle's, the round trip is exact, and the
+    container is smaller than with per-channel tables."""
     cfg = gen.CONFIGS[2]
     say(f"[parity] exponent mode cfg2: generating {cfg.values} values on GPU")
     t, p, tabs, oshape = exp_case(skv, orc, cfg)
-    cont = skv.encode(tabs, t, p)
-    torch.cuda.synchronize()
-    n = orc.n_streams(oshape)
-    head = 64 + 8 * (n + 1)
-    host_head = cont[:head].cpu().numpy().tobytes()
-    idx = np.frombuffer(host_head[64:], dtype=np.uint64)
-    offs = idx & np.uint64((1 << 63) - 1)
-    assert int(offs[-1]) == cont.numel() - head
-    ratio = cfg.raw_bytes / cont.numel()
-    say(f"[parity] exponent mode cfg2: ratio {ratio:.4f}")
-    assert ratio > 4.5
-    ncg, ntb, blob = cfg.channels // 32, cfg.tokens // 128, tabs.bytes()
-    for s in _sample_ids(n, 32, 2):
-        cg, rest = s % ncg, s // ncg
-        tb, slab = rest % ntb, rest // ntb
-        l, k = divmod(slab, cfg.kv)
-        sl = (l, k, slice(tb * 128, tb * 128 + 128), slice(cg * 32, cg * 32 + 32))
-        lanes = np.full(32, slab, dtype=np.uint32)            # exponent mode: the stream's slab
-        data, raw = orc.encode_tile(blob, oshape, t[sl].cpu().numpy(), p[sl].cpu().numpy(), lanes)
-        assert bool(int(idx[s]) >> 63) == raw, s
-        assert cont[head + int(offs[s]):head + int(offs[s + 1])].cpu().numpy().tobytes() == data, s
-    say("[parity] exponent mode cfg2: sampled streams identical; decoding")
-    back = skv.decode(tabs, cont, p)
-    assert torch.equal(back, t)
+    big_compare(skv, orc, t, p, tabs, oshape, "exponent mode cfg2", min_ratio=4.5)
 
 
 RANGES = [(0, 1024), (0, 128), (896, 1024), (256, 640), (128, 1024)]
@@ -363,11 +364,18 @@ def test_decode_range_errors(skv, orc):
     t, p, tabs, oshape = residual_case(skv, orc, cfg)
     cont = skv.encode(tabs, t, p)
     for a, b in [(0, 100), (64, 192), (256, 256), (384, 128), (0, 640)]:
+        pr = torch.zeros((1, 2, max(b - a, 128), 64), dtype=p.dtype, device="cuda")
         with pytest.raises(skv.SkvError) as e:
-            skv.decode_range(tabs, cont, a, b, p[:, :, :128].contiguous())
+            skv.decode_range(tabs, cont, a, b, pr)
         assert e.value.status == skv.ERR_SHAPE, (a, b)
     with pytest.raises(skv.SkvError) as e:
-        skv.decode_range_into(tabs, cont, 128, 384, p, torch.empty(10, dtype=torch.uint8, device="cuda"))
+        skv.decode_range_into(tabs, cont, 128, 384, p[:, :, 128:384].contiguous(),
+                              torch.empty(10, dtype=torch.uint8, device="cuda"))
+    assert e.value.status == skv.ERR_CAPACITY
+    # a predictor shorter than the container's tokens: the capacity passed is
+    # the smaller of the two buffers, so the library refuses it
+    with pytest.raises(skv.SkvError) as e:
+        skv.decode_into(tabs, cont, p[:, :, :256].contiguous(), torch.empty_like(p))
     assert e.value.status == skv.ERR_CAPACITY
     # a damaged stream inside the range is found; one outside it is not read
     good = cont.cpu().numpy()
@@ -447,26 +455,29 @@ def test_corruption_and_wrong_tables(skv, orc):
 
 
 # ------------------------------------------------------------------ full-size workloads
-def _sample_ids(n, k, seed):
-    rng = np.random.default_rng(seed)
-    ids = set(rng.choice(n, size=min(k, n), replace=False).tolist())
-    ids.update({0, n - 1})
-    return sorted(ids)
-
-
-def _check_sampled_streams(orc, blob, oshape, cont_host, tile_fn, lane_fn, n, ids, what):
-    head = 64 + 8 * (n + 1)
-    idx = np.frombuffer(cont_host[64:head], dtype=np.uint64)
-    mask = np.uint64((1 << 63) - 1)
-    offs = idx & mask
-    assert offs[0] == 0 and np.all(offs[1:] >= offs[:-1])
-    assert int(offs[-1]) == len(cont_host) - head
-    for s in ids:
-        tt, ta, nl, nr = tile_fn(s)
-        data, raw = orc.encode_tile(blob, oshape, tt, ta, lane_fn(s), nl, nr)
-        a, b = int(offs[s]), int(offs[s + 1])
-        assert bool(int(idx[s]) >> 63) == raw, (what, s)
-        assert cont_host[head + a:head + b] == data, (what, s)
+def big_compare(skv, orc, t, p, tabs, oshape, what, min_ratio=None):
+    """Whole-container parity at full size: the GPU container equals the
+    oracle's byte for byte (every index entry and stream), then the GPU
+    decodes it and the reconstruction is compared with the target in HBM."""
+    say(f"[parity] {what}: encode on GPU")
+    cont = skv.encode(tabs, t, p)
+    torch.cuda.synchronize()
+    raw_bytes = t.numel() * t.element_size()
+    say(f"[parity] {what}: container {cont.numel()} B, ratio {raw_bytes / cont.numel():.4f}")
+    if min_ratio is not None:
+        assert raw_bytes / cont.numel() > min_ratio
+    got = host_u8(cont)
+    tn, pn = t.cpu().numpy(), p.cpu().numpy()
+    say(f"[parity] {what}: oracle encode on {ORACLE_THREADS} threads")
+    want = orc.encode_array(tabs.bytes(), oshape, tn, pn, threads=ORACLE_THREADS)
+    del tn, pn
+    assert_same_container(got, want, what)
+    del got, want
+    say(f"[parity] {what}: containers identical; decoding on GPU")
+    back = skv.decode(tabs, cont, p)
+    assert torch.equal(back, t)
+    say(f"[parity] {what}: round trip exact")
+    return cont
 
 
 @pytest.mark.parametrize("cid", [1, 2, 3])
@@ -474,80 +485,22 @@ def test_full_size_residual(skv, orc, cid):
     cfg = gen.CONFIGS[cid]
     say(f"[parity] cfg{cid} {cfg.name}: generating {cfg.values} values on GPU")
     t, p, tabs, oshape = residual_case(skv, orc, cfg)
-    say(f"[parity] cfg{cid}: encode")
-    cont = skv.encode(tabs, t, p)
-    torch.cuda.synchronize()
-    n = orc.n_streams(oshape)
-    ratio = cfg.raw_bytes / cont.numel()
-    say(f"[parity] cfg{cid}: {n} streams, container {cont.numel()} B, ratio {ratio:.3f}")
-    head = 64 + 8 * (n + 1)
-    ids = _sample_ids(n, 48, cid)
-    # copy back only the header+index and the sampled streams' bytes
-    host_head = cont[:head].cpu().numpy().tobytes()
-    idx = np.frombuffer(host_head[64:], dtype=np.uint64) & np.uint64((1 << 63) - 1)
-    assert int(idx[-1]) == cont.numel() - head
-    ncg, ntb = cfg.channels // 32, cfg.tokens // 128
-    blob = tabs.bytes()
-
-    def tile(s):
-        cg, rest = s % ncg, s // ncg
-        tb, slab = rest % ntb, rest // ntb
-        l, k = divmod(slab, cfg.kv)
-        sl = (l, k, slice(tb * 128, tb * 128 + 128), slice(cg * 32, cg * 32 + 32))
-        return t[sl].cpu().numpy(), p[sl].cpu().numpy(), None, None
-
-    def lanes(s):
-        cg, slab = s % ncg, s // (ncg * ntb)
-        return np.arange(32, dtype=np.uint32) + slab * cfg.channels + cg * 32
-
-    head_raw = np.frombuffer(host_head[64:], dtype=np.uint64)
-    for s in ids:
-        tt, ta, _, _ = tile(s)
-        data, raw = orc.encode_tile(blob, oshape, tt, ta, lanes(s))
-        a, b = int(idx[s]), int(idx[s + 1])
-        assert bool(int(head_raw[s]) >> 63) == raw, s
-        got = cont[head + a:head + b].cpu().numpy().tobytes()
-        assert got == data, (cid, s)
-    say(f"[parity] cfg{cid}: {len(ids)} sampled streams identical; decoding")
-    del cont
-    back = skv.decode(tabs, skv.encode(tabs, t, p), p)
-    assert torch.equal(back, t)
-    say(f"[parity] cfg{cid}: round trip exact")
+    big_compare(skv, orc, t, p, tabs, oshape, f"cfg{cid}")
 
 
 def test_slab_over_2gib(skv, orc):
     """A (layer, K|V) slab of 2 GiB (2^21 tokens x 1024 e4m3 channels) is past
     the tiled kernels' 32-bit row offsets, so it takes the per-step encoder and
-    decoder; sampled streams match the oracle, the round trip is exact, and a
-    range at the slab's end decodes through the tiled decoder."""
+    decoder; the whole container equals the oracle's, the round trip is exact,
+    and a range at the slab's end decodes through the tiled decoder."""
     cfg = gen.Config(97, "slab-2gib-e4m3", "e4m3", 1, 1, 1 << 21, 1024, outliers=False)
     say(f"[parity] 2 GiB slab: generating {cfg.values} values on GPU")
     t, p, tabs, oshape = residual_case(skv, orc, cfg)
-    say("[parity] 2 GiB slab: encode")
-    cont = skv.encode(tabs, t, p)
-    torch.cuda.synchronize()
-    n = orc.n_streams(oshape)
-    head = 64 + 8 * (n + 1)
-    host_head = cont[:head].cpu().numpy().tobytes()
-    idx = np.frombuffer(host_head[64:], dtype=np.uint64)
-    offs = idx & np.uint64((1 << 63) - 1)
-    assert int(offs[-1]) == cont.numel() - head
-    ncg, blob = cfg.channels // 32, tabs.bytes()
-    for s in _sample_ids(n, 24, 97):
-        cg, tb = s % ncg, s // ncg
-        sl = (0, 0, slice(tb * 128, tb * 128 + 128), slice(cg * 32, cg * 32 + 32))
-        lanes = np.arange(32, dtype=np.uint32) + cg * 32
-        data, raw = orc.encode_tile(blob, oshape, t[sl].cpu().numpy(), p[sl].cpu().numpy(), lanes)
-        assert bool(int(idx[s]) >> 63) == raw, s
-        assert cont[head + int(offs[s]):head + int(offs[s + 1])].cpu().numpy().tobytes() == data, s
-    say("[parity] 2 GiB slab: sampled streams identical; decoding")
-    back = skv.decode(tabs, cont, p)
-    assert torch.equal(back, t)
-    del back
+    cont = big_compare(skv, orc, t, p, tabs, oshape, "2 GiB slab")
     a = cfg.tokens - 256
     part = skv.decode_range(tabs, cont, a, cfg.tokens, p[:, :, a:].contiguous())
     assert torch.equal(part, t[:, :, a:])
-    say("[parity] 2 GiB slab: round trip and end range exact")
+    say("[parity] 2 GiB slab: end range exact")
 
 
 def test_full_size_checkerboard(skv, orc):
@@ -557,35 +510,7 @@ def test_full_size_checkerboard(skv, orc):
     cc, cg = gen.dckv_draw(cfg, gen.CALIB, tokens=256, device="cuda")
     tabs = skv.fit_tables(skv.INT16, skv.CHECKERBOARD, 1, 1, cfg.channels, cc.cpu().numpy(), cg.cpu().numpy(), 256)
     oshape = orc.make_shape(orc.INT16, orc.CHECKERBOARD, 1, 1, cfg.tokens, cfg.channels)
-    cont = skv.encode(tabs, coef, G)
-    torch.cuda.synchronize()
-    n = orc.n_streams(oshape)
-    head = 64 + 8 * (n + 1)
-    say(f"[parity] cfg4: {n} streams, ratio {cfg.raw_bytes / cont.numel():.3f}")
-    idx_raw = np.frombuffer(cont[:head].cpu().numpy().tobytes()[64:], dtype=np.uint64)
-    idx = idx_raw & np.uint64((1 << 63) - 1)
-    ncg, ntb = cfg.channels // 32, cfg.tokens // 2 // 128
-    T = cfg.tokens
-    blob = tabs.bytes()
-    for s in _sample_ids(n, 48, 4):
-        cgi, rest = s % ncg, s // ncg
-        tb, ps = rest % ntb, rest // ntb
-        toks = torch.arange(128, device="cuda") * 2 + 2 * 128 * tb + ps
-        cols = slice(cgi * 32, cgi * 32 + 32)
-        tt = coef[toks, cols].cpu().numpy()
-        ta = G[toks, cols].cpu().numpy()
-        nl = nr = None
-        if ps == 1:
-            nl = coef[toks - 1, cols].cpu().numpy()
-            right = torch.where(toks + 1 < T, toks + 1, toks - 1)
-            nr = coef[right, cols].cpu().numpy()
-        data, raw = orc.encode_tile(blob, oshape, tt, ta, np.arange(32, dtype=np.uint32) + cgi * 32, nl, nr)
-        a, b = int(idx[s]), int(idx[s + 1])
-        assert bool(int(idx_raw[s]) >> 63) == raw
-        assert cont[head + a:head + b].cpu().numpy().tobytes() == data, s
-    back = skv.decode(tabs, cont, G)
-    assert torch.equal(back, coef)
-    say("[parity] cfg4: sampled streams identical, round trip exact")
+    big_compare(skv, orc, coef, G, tabs, oshape, "cfg4 checkerboard")
 
 
 @pytest.mark.parametrize("cid,exp,layers,lpc", [(0, False, 5, 2), (2, True, 3, 1), (2, False, 4, 4)])
@@ -641,8 +566,9 @@ def test_transfer_wire_too_small(skv, orc):
 
 def test_transfer_full_size_e4m3(skv, orc):
     """The Qwen3-8B-shaped e4m3 cache in chunks of 4 layers: exact
-    reconstruction, and the first and last chunk containers equal the
-    one-shot encoder's containers of those layers."""
+    reconstruction, and every chunk container on the wire equals the oracle's
+    container of those layers, coded with tables the oracle fits on those
+    layers' calibration alone."""
     cfg = gen.CONFIGS[2]
     say(f"[parity] transfer cfg2: generating {cfg.values} values on GPU")
     t, p = gen.residual_array(cfg, device="cuda")
@@ -655,9 +581,12 @@ def test_transfer_full_size_e4m3(skv, orc):
     ratio = cfg.raw_bytes / wire.numel()
     say(f"[parity] transfer cfg2: {len(offs) - 1} chunks, ratio {ratio:.4f}")
     assert ratio > 3.5
-    for c in (0, len(offs) - 2):
+    w = wire.numpy()
+    tn, pn = t.cpu().numpy(), p.cpu().numpy()
+    for c in range(len(offs) - 1):
         l0, l1 = 4 * c, min(cfg.layers, 4 * c + 4)
-        part = skv.fit_tables(skv.E4M3, skv.RESIDUAL, l1 - l0, cfg.kv, cfg.channels,
-                              np.ascontiguousarray(ct[l0:l1]), np.ascontiguousarray(cp[l0:l1]), 256)
-        want = skv.encode(part, t[l0:l1].contiguous(), p[l0:l1].contiguous())
-        assert torch.equal(wire[offs[c]:offs[c + 1]], want.cpu()), c
+        oshape = orc.make_shape(orc.E4M3, orc.RESIDUAL, l1 - l0, cfg.kv, cfg.tokens, cfg.channels)
+        blob = orc.fit_tables(oshape, np.ascontiguousarray(ct[l0:l1]), np.ascontiguousarray(cp[l0:l1]), 256)
+        want = orc.encode_array(blob, oshape, tn[l0:l1], pn[l0:l1], threads=ORACLE_THREADS)
+        assert_same_container(w[offs[c]:offs[c + 1]], want, f"transfer chunk {c}")
+        say(f"[parity] transfer cfg2: chunk {c} identical to the oracle's")
