@@ -51,8 +51,8 @@ def main() -> int:
                     help="residual tables per channel (default) or per slab and predictor exponent class")
     ap.add_argument("--transfer-layers", type=int, default=4,
                     help="layers per chunk of the transfer-pipeline measurement (0 = skip it)")
-    ap.add_argument("--copy-probe", action="store_true",
-                    help="also time a plain device copy of the cache (HBM ceiling; counter scale reference)")
+    ap.add_argument("--no-copy-probe", action="store_true",
+                    help="skip timing a plain device copy of the cache (HBM ceiling; counter scale reference)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the coding path has no multi-GPU part "
@@ -185,13 +185,24 @@ def main() -> int:
     roofline = {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
                 "algorithmic_bytes": alg.get(dom, 0), "avg_ms": round(kavg[dom], 4)}
+    # whole calls (every kernel of the op and its host read-backs), against HBM peak
+    enc_alg = 2 * raw_bytes + cont_bytes
+    dec_alg = 2 * raw_bytes + cont_bytes
+    op_roofline = {
+        "encode": {"ms": round(enc_ms, 4), "algorithmic_bytes": enc_alg,
+                   "achieved_GBps": round(enc_alg / (enc_ms / 1e3) / 1e9, 1),
+                   "frac": round(enc_alg / (enc_ms / 1e3) / 1e9 / HBM_PEAK_GBPS, 4)},
+        "decode": {"ms": round(dec_ms, 4), "algorithmic_bytes": dec_alg,
+                   "achieved_GBps": round(dec_alg / (dec_ms / 1e3) / 1e9, 1),
+                   "frac": round(dec_alg / (dec_ms / 1e3) / 1e9 / HBM_PEAK_GBPS, 4)},
+    }
     per_kernel = {k: {"avg_ms": round(kavg[k], 4), "algorithmic_bytes": alg.get(k, 0),
                       "achieved_GBps": round(alg.get(k, 0) / (kavg[k] / 1e3) / 1e9, 1),
                       "frac": round(alg.get(k, 0) / (kavg[k] / 1e3) / 1e9 / HBM_PEAK_GBPS, 4)}
                   for k in kavg if alg.get(k, 0)}
 
     copy = None
-    if args.copy_probe:
+    if not args.no_copy_probe:
         src = tgt.view(-1).view(torch.uint8)
         dst = torch.empty_like(src)
         for _ in range(2):
@@ -203,8 +214,10 @@ def main() -> int:
         e1.record()
         torch.cuda.synchronize()
         ms = e0.elapsed_time(e1) / 5
-        copy = {"bytes_copied": src.numel(), "ms": round(ms, 4),
-                "GBps_read_plus_write": round(2 * src.numel() / (ms / 1e3) / 1e9, 1)}
+        cgbps = 2 * src.numel() / (ms / 1e3) / 1e9
+        copy = {"bytes_copied": src.numel(), "ms": round(ms, 4), "GBps_read_plus_write": round(cgbps, 1),
+                "frac_of_peak": round(cgbps / HBM_PEAK_GBPS, 4),
+                "decode_kernel_frac_of_copy": round(achieved / cgbps, 4) if dom.startswith("decode") else None}
         del dst
 
     xfer = None
@@ -241,6 +254,7 @@ def main() -> int:
         "table_fit_s": round(fit_s, 3),
         "verified_roundtrip": ok,
         "roofline": roofline,
+        "op_roofline": op_roofline,
         "kernels_roofline": per_kernel,
         "copy_ceiling": copy,
         "range_decode": part,
@@ -318,19 +332,48 @@ def transfer_probe(skv, cfg, tabs, tgt, prd, layers_per_chunk, reps=3):
             "speedup_vs_raw_overlapped_copy": round(piped_ms / ms, 3), "verified": ok}
 
 
+def host_cpus() -> dict:
+    """The host's CPU inventory: logical CPUs, the ones this process may run
+    on, and lscpu's sockets, cores per socket and threads per core."""
+    import subprocess
+
+    info = {"nproc": os.cpu_count(), "affinity": len(os.sched_getaffinity(0))}
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        keys = {"Socket(s)": "sockets", "Core(s) per socket": "cores_per_socket",
+                "Thread(s) per core": "threads_per_core", "Model name": "model"}
+        for line in out.splitlines():
+            k, _, v = line.partition(":")
+            if k.strip() in keys:
+                v = v.strip()
+                info[keys[k.strip()]] = int(v) if v.isdigit() else v
+    except (OSError, subprocess.SubprocessError):
+        pass
+    return info
+
+
+def oracle_threads() -> int:
+    """OpenMP threads for the oracle: every CPU this process may use, up to
+    the 16-CPU share of one GPU on the test machines (OMP_NUM_THREADS there)."""
+    cap = int(os.environ.get("OMP_NUM_THREADS", "16") or 16)
+    return max(1, min(cap, 16, len(os.sched_getaffinity(0))))
+
+
 def cpu_baseline(cfg, tabs, tgt, prd, seconds):
     """The oracle (plain C, OpenMP over streams) on the host: encode + decode
-    of whole layers of the same workload until about `seconds` of work."""
+    of whole layers of the same workload until about `seconds` of work, on
+    every thread it may use, then the first layer again on one thread."""
     import numpy as np
     import oracle
 
-    threads = max(1, min(16, len(os.sched_getaffinity(0))))
+    threads = oracle_threads()
     blob = tabs.bytes()
     exp = tabs.mode == oracle.RESIDUAL_EXP
     per_layer_tables = cfg.kv * (16 if exp else cfg.channels)
     rec = 514
     n_tables = cfg.layers * per_layer_tables
     done_bytes, spent, layers = 0, 0.0, 0
+    one = None
     for layer in range(cfg.layers):
         hdr = bytearray(blob[:64])
         hdr[8:12] = per_layer_tables.to_bytes(4, "little")
@@ -352,6 +395,14 @@ def cpu_baseline(cfg, tabs, tgt, prd, seconds):
         spent += time.perf_counter() - a
         if not np.array_equal(back, t):
             raise RuntimeError("oracle round trip failed")
+        if one is None:                                           # the same layer on one thread
+            a = time.perf_counter()
+            c1 = oracle.encode(sub, shape, t, p, threads=1)
+            oracle.decode(sub, c1, p, t, threads=1)
+            s1 = time.perf_counter() - a
+            one = {"value": round(t.nbytes / s1 / 1e9, 4), "unit": "GB/s", "threads": 1,
+                   "sample": f"encode + decode of layer 0 ({t.nbytes} B)", "seconds": round(s1, 2)}
+            log(f"cpu oracle: layer 0 on one thread in {s1:.1f} s")
         done_bytes += t.nbytes
         layers += 1
         log(f"cpu oracle: layer {layer} done, {spent:.1f} s so far")
@@ -360,7 +411,7 @@ def cpu_baseline(cfg, tabs, tgt, prd, seconds):
     return {"value": round(done_bytes / spent / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
             "sample": f"encode + decode of {layers} of {cfg.layers} layers (K and V, {done_bytes} B of "
                       f"{cfg.dtype} codes) of the same workload and tables, {threads} OpenMP threads",
-            "seconds": round(spent, 2)}
+            "seconds": round(spent, 2), "one_thread": one, "host": host_cpus()}
 
 
 def cpu_baseline_cb(cfg, tabs, coef, G, seconds):
@@ -369,10 +420,11 @@ def cpu_baseline_cb(cfg, tabs, coef, G, seconds):
     import numpy as np
     import oracle
 
-    threads = max(1, min(16, len(os.sched_getaffinity(0))))
+    threads = oracle_threads()
     blob = tabs.bytes()
     span = min(cfg.tokens, 8192)
     done_bytes, spent, spans = 0, 0.0, 0
+    one = None
     for a in range(0, cfg.tokens, span):
         c = coef[a:a + span].cpu().numpy()
         g = G[a:a + span].cpu().numpy()
@@ -383,6 +435,13 @@ def cpu_baseline_cb(cfg, tabs, coef, G, seconds):
         spent += time.perf_counter() - t0
         if not np.array_equal(back, c):
             raise RuntimeError("oracle round trip failed")
+        if one is None:                                           # the same span on one thread
+            t0 = time.perf_counter()
+            cont1 = oracle.encode(blob, shape, c, g, threads=1)
+            oracle.decode(blob, cont1, g, c, threads=1)
+            s1 = time.perf_counter() - t0
+            one = {"value": round(c.nbytes / s1 / 1e9, 4), "unit": "GB/s", "threads": 1,
+                   "sample": f"encode + decode of the first span ({c.nbytes} B)", "seconds": round(s1, 2)}
         done_bytes += c.nbytes
         spans += 1
         log(f"cpu oracle: span {spans} done, {spent:.1f} s so far")
@@ -391,7 +450,7 @@ def cpu_baseline_cb(cfg, tabs, coef, G, seconds):
     return {"value": round(done_bytes / spent / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
             "sample": f"encode + decode of {spans} spans of {span} tokens x {cfg.channels} int16 coefficients "
                       f"({done_bytes} B) of the same matrix and tables, {threads} OpenMP threads",
-            "seconds": round(spent, 2)}
+            "seconds": round(spent, 2), "one_thread": one, "host": host_cpus()}
 
 
 if __name__ == "__main__":

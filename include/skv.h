@@ -76,9 +76,14 @@ typedef struct {
  * Each table is a Laplace integrated over unit cells (location 0, or f/16
  * for shifted table f in checkerboard mode; scale = mean |residual| over
  * calibration values with |residual| <= 127, floored at 0.05), with a direct
- * range of 1..255 symbols (all with cell mass >= 2^-12) and an escape symbol
- * whose probability is the smoothed calibration escape rate, quantized to
- * 12-bit frequencies >= 1 summing to 4096.
+ * range of n symbols z = 0..n-1 and an escape symbol (index n) whose
+ * probability is the smoothed calibration escape rate (#z >= n + 1) / (N + 2),
+ * quantized to 12-bit frequencies >= 1 summing to 4096 (largest remainder,
+ * ties to the smaller index).  n is 1 + the largest z <= 254 whose cell mass
+ * is at least 2^-12, raised in residual modes to the slab's calibration tail
+ * floor -- the smallest z in [1, 255] such that at most floor(N / 1024) of the
+ * N calibration symbols of the table's (layer, K|V) slab are z or larger --
+ * and at most 255.
  * SKV_RESIDUAL_EXP (a finer residual model, "Speculative KV coding" page,
  * "Early results"; conditional models, DCKV page, "How it differs"): one
  * table per (layer, K|V) slab and predictor exponent class -- the class of a
@@ -103,16 +108,31 @@ int skv_fit_tables(const skv_shape* s, const void* calib_target, const void* cal
  * summing to 4096 and zeros beyond.  Release with skv_free. */
 int skv_load_tables(const void* blob, size_t blob_bytes, void** tables_blob);
 
-/* Encode (device).  d_target and d_aux (predictor, or G in checkerboard mode)
- * are device arrays of the shape's layout.  The container written to d_out:
+/* Encode (device).  The sender codes the residual of the target cache
+ * against the predictor's cache with an entropy coder ("Speculative KV
+ * coding" page, section "Core idea", flow steps 1-2: the sender has the
+ * target and predictor caches and entropy-codes their difference); the coder is rANS
+ * against the fitted tables (DCKV page, "How it differs").  d_target and
+ * d_aux (predictor, or G in checkerboard mode) are device arrays of the
+ * shape's layout; neither is written.  Residual of a value: r = (ord t - ord
+ * p) mod 2^N read as signed (N = 16 for bf16, 8 for e4m3; ord maps a sign-
+ * magnitude pattern to an order-preserving integer), symbol z = zigzag(r).
+ * Stream s = (slab * token blocks + token block) * channel groups + channel
+ * group; lane i codes channel 32 * group + i, step k token 128 * block + k
+ * (checkerboard: the slab is the pass, token 2 * (128 * block + k) + pass).
+ * The container written to d_out:
  *   64 B header: "SKV1" | u16 1 | u8 dtype | u8 mode | u8 12 | u8 32 | u16 128 |
  *                u32 layers | u32 kv | u32 tokens | u32 channels | u32 0 |
  *                u64 n_streams | u64 FNV-1a-64 of the blob | u64 payload bytes | u64 0
  *   index: (n_streams+1) u64 payload offsets, bit 63 = stream stored raw,
  *          last entry = payload bytes
- *   payload: streams (32 lanes x 128 steps) in id order; coded streams are
- *          32 u32 final rANS states, the u16 words, a zero u16 if their
- *          count is odd; raw streams are the 4096 target elements.
+ *   payload: streams (32 lanes x 128 steps) in id order.  A coded stream is
+ *          32 u32 final rANS states (lane order) | u32 word count W | W u16
+ *          words in decode order (by step, then lane) | the escaped values
+ *          (z >= the lane's direct count: u16 for 16-bit elements, u8 for
+ *          e4m3) in decode order | zero bytes up to a multiple of 4.  A stream
+ *          whose coded size would reach its raw size is stored raw: its 4096
+ *          target elements in (step, lane) order.
  * Two-phase sizing: with d_out == NULL, *out_bytes receives the bound (every
  * stream raw); with d_work == NULL, *work_bytes receives the workspace need.
  * Otherwise out_capacity must hold the container (else SKV_ERR_CAPACITY and
@@ -122,8 +142,12 @@ int skv_encode(const void* tables_blob, const skv_shape* s, const void* d_target
                void* d_out, size_t out_capacity, size_t* out_bytes,
                void* d_work, size_t* work_bytes, hipStream_t stream);
 
-/* Decode (device).  d_in holds in_bytes of container; d_aux is the
- * predictor (or G) in the shape's layout; d_out receives the reconstruction
+/* Decode (device).  The receiver replays the predictor, decodes the
+ * residual and adds it back, which returns the original bytes exactly
+ * ("Speculative KV coding" page, section "Core idea", flow steps 3-4; the stored
+ * cache is restored in full before use, DCKV page, "How it works").  d_in holds in_bytes of container;
+ * d_aux is the predictor (or G) in the shape's layout, with at least
+ * out_capacity bytes readable; d_out receives the reconstruction
  * (out_capacity bytes available).  The shape comes from the header, which is
  * validated against the blob (hash, dtype, mode, layers, kv, channels).
  * With d_work == NULL, *work_bytes receives the workspace need.  Every

@@ -207,6 +207,33 @@ void skv_free(void* tables_blob) {
     delete b;
 }
 
+// The encoder's launch arguments, its workspace carved from w
+// (skv::encode_work_bytes(n, raw) bytes, 256-byte aligned).
+static skv::EncodeLaunch encode_launch(const Blob* b, const skv_shape& s, const void* d_target, const void* d_aux,
+                                       void* d_out, size_t out_capacity, uint8_t* w) {
+    const uint64_t n = skv::stream_count(s);
+    const uint32_t raw = skv::kSyms * skv::elem_bytes(s.dtype);
+    skv::EncodeLaunch a{};
+    a.target = d_target;
+    a.aux = d_aux;
+    a.scratch = w;
+    w += align256(2 * n * raw);
+    a.meta = reinterpret_cast<uint32_t*>(w);
+    w += align256(4 * n);
+    const uint64_t nb = (n + 1023) / 1024;
+    a.block_sum = reinterpret_cast<uint32_t*>(w);
+    w += align256(4 * nb);
+    a.block_off = reinterpret_cast<uint64_t*>(w);
+    w += align256(8 * nb);
+    a.total = reinterpret_cast<uint64_t*>(w);
+    a.out = static_cast<uint8_t*>(d_out);
+    a.out_capacity = out_capacity;
+    a.blob_hash = b->hash;
+    a.shape = s;
+    a.n_streams = n;
+    return a;
+}
+
 static int encode_impl(const void* tables_blob, const skv_shape* s, const void* d_target, const void* d_aux,
                        void* d_out, size_t out_capacity, size_t* out_bytes, void* d_work, size_t* work_bytes,
                        hipStream_t stream, bool timing) {
@@ -233,25 +260,7 @@ static int encode_impl(const void* tables_blob, const skv_shape* s, const void* 
     int rc = device_tables(b, stream, &t);
     if (rc != SKV_OK) return rc;
 
-    uint8_t* w = static_cast<uint8_t*>(d_work);
-    skv::EncodeLaunch a{};
-    a.target = d_target;
-    a.aux = d_aux;
-    a.scratch = w;
-    w += align256(2 * n * raw);
-    a.meta = reinterpret_cast<uint32_t*>(w);
-    w += align256(4 * n);
-    const uint64_t nb = (n + 1023) / 1024;
-    a.block_sum = reinterpret_cast<uint32_t*>(w);
-    w += align256(4 * nb);
-    a.block_off = reinterpret_cast<uint64_t*>(w);
-    w += align256(8 * nb);
-    a.total = reinterpret_cast<uint64_t*>(w);
-    a.out = static_cast<uint8_t*>(d_out);
-    a.out_capacity = out_capacity;
-    a.blob_hash = b->hash;
-    a.shape = *s;
-    a.n_streams = n;
+    skv::EncodeLaunch a = encode_launch(b, *s, d_target, d_aux, d_out, out_capacity, static_cast<uint8_t*>(d_work));
     if (timing) skv::timing_reset();
     if (skv::launch_encode(a, *t, stream) != hipSuccess) return SKV_ERR_DEVICE;
     uint64_t payload = 0;

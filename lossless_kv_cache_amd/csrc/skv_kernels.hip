@@ -3006,7 +3006,6 @@ struct KernelTiming {
     int done = 0;
 };
 KernelTiming g_timing;
-bool g_force_v1 = false;     // use the one-stream-per-half-wave kernels (diagnostics)
 
 // `launch` dispatches one kernel with hipExtLaunchKernelGGL and the event pair it
 // is given (null when timing is off): the events take the kernel's own start
@@ -3024,18 +3023,6 @@ void timed(const char* name, hipStream_t st, F&& launch) {
 
 constexpr uint32_t kLdsThreads = 1024;
 
-// Kernel variant selection for tuning runs: SKV_VARIANT="<enc>,<dec>" (0 = default).
-struct Variant {
-    int enc = 0, dec = 0;
-};
-const Variant& variant() {
-    static const Variant v = [] {
-        Variant r;
-        if (const char* e = std::getenv("SKV_VARIANT")) std::sscanf(e, "%d,%d", &r.enc, &r.dec);
-        return r;
-    }();
-    return v;
-}
 constexpr size_t kLdsLimit = 160 * 1024;
 
 // Work decomposition of the LDS kernels for a residual-mode shape.
@@ -3086,8 +3073,7 @@ hipError_t encode_all(const EncodeLaunch& a, const DevTables& t, hipStream_t st)
     const uint32_t ncg = a.shape.channels / kLanes;
     const bool aligned16 = (reinterpret_cast<uintptr_t>(a.target) | reinterpret_cast<uintptr_t>(a.aux)) % 16 == 0;
     const bool fits = slab_fits(a.shape);
-    if (DT == SKV_BF16 && MODE == SKV_RESIDUAL && fits && aligned16 && encode_bf16_lds(fc_stride(t)) <= kLdsLimit &&
-        !g_force_v1 && variant().enc == 0) {
+    if (DT == SKV_BF16 && MODE == SKV_RESIDUAL && fits && aligned16 && encode_bf16_lds(fc_stride(t)) <= kLdsLimit ) {
         const LdsGeo lg = lds_geometry(a.shape);
         const size_t lp = encode_bf16_lds(fc_stride(t));
         hipError_t e = allow_lds(encode_bf16, lp);
@@ -3096,7 +3082,7 @@ hipError_t encode_all(const EncodeLaunch& a, const DevTables& t, hipStream_t st)
             hipExtLaunchKernelGGL(encode_bf16, dim3(lds_grid(lg)), dim3(kLdsThreads), lp, st, e0, e1, 0, a, t, fc_stride(t), lg);
         });
     } else if (DT == SKV_E4M3 && MODE == SKV_RESIDUAL_EXP && fits && ncg % 4 == 0 && aligned &&
-               3 * (encode_exp_lds(fc_stride(t)) + 256) <= kLdsLimit && !g_force_v1 && variant().enc == 0) {
+               3 * (encode_exp_lds(fc_stride(t)) + 256) <= kLdsLimit) {
         const LdsGeo lg = lds_geometry(a.shape, 2);
         const size_t lp = encode_exp_lds(fc_stride(t));
         hipError_t e = allow_lds(encode_pairs_exp, lp);
@@ -3106,8 +3092,7 @@ hipError_t encode_all(const EncodeLaunch& a, const DevTables& t, hipStream_t st)
                                   fc_stride(t), lg);
         });
     } else if (DT == SKV_E4M3 && MODE == SKV_RESIDUAL && fits && ncg % 4 == 0 &&
-               2 * encode_groups_lds(1, fc_stride(t)) + 512 <= kLdsLimit && aligned && !g_force_v1 &&
-               variant().enc == 0) {
+               2 * encode_groups_lds(1, fc_stride(t)) + 512 <= kLdsLimit && aligned) {
         const LdsGeo lg = lds_geometry(a.shape, 2);
         const size_t lp = encode_groups_lds(1, fc_stride(t));
         hipError_t e = allow_lds(encode_pairs, lp);
@@ -3115,7 +3100,7 @@ hipError_t encode_all(const EncodeLaunch& a, const DevTables& t, hipStream_t st)
         timed("encode_streams", st, [&](hipEvent_t e0, hipEvent_t e1) {
             hipExtLaunchKernelGGL(encode_pairs, dim3(lds_grid(lg)), dim3(kLdsThreads), lp, st, e0, e1, 0, a, t, fc_stride(t), lg);
         });
-    } else if (DT == SKV_E4M3 && MODE == SKV_RESIDUAL && fits && lt <= kLdsLimit && aligned && !g_force_v1 && variant().enc == 0) {
+    } else if (DT == SKV_E4M3 && MODE == SKV_RESIDUAL && fits && lt <= kLdsLimit && aligned) {
         const LdsGeo lg = lds_geometry(a.shape);
         auto k = encode_tiles<SKV_E4M3>;
         hipError_t e = allow_lds(k, lt);
@@ -3123,22 +3108,15 @@ hipError_t encode_all(const EncodeLaunch& a, const DevTables& t, hipStream_t st)
         timed("encode_streams", st, [&](hipEvent_t e0, hipEvent_t e1) {
             hipExtLaunchKernelGGL(k, dim3(lds_grid(lg)), dim3(kLdsThreads), lt, st, e0, e1, 0, a, t, fc_stride(t), lg);
         });
-    } else if (MODE == SKV_RESIDUAL && fits && lb <= kLdsLimit && !g_force_v1 && variant().enc >= 0) {
+    } else if (MODE == SKV_RESIDUAL && fits && lb <= kLdsLimit) {
         const LdsGeo lg = lds_geometry(a.shape);
         auto k = encode_lds<DT, 1, 4>;
-        switch (variant().enc) {
-            case 1: k = encode_lds<DT, 2, 4>; break;
-            case 2: k = encode_lds<DT, 1, 8>; break;
-            case 3: k = encode_lds<DT, 2, 8>; break;
-            case 4: k = encode_lds<DT, 1, 16>; break;
-            default: break;
-        }
         hipError_t e = allow_lds(k, lb);
         if (e != hipSuccess) return e;
         timed("encode_streams", st, [&](hipEvent_t e0, hipEvent_t e1) {
             hipExtLaunchKernelGGL(k, dim3(lds_grid(lg)), dim3(kLdsThreads), lb, st, e0, e1, 0, a, t, fc_stride(t), lg);
         });
-    } else if (MODE == SKV_CHECKERBOARD && fits && !g_force_v1 && variant().enc == 0) {
+    } else if (MODE == SKV_CHECKERBOARD && fits) {
         // two steps between stages: longer lags measured no faster (more registers, fewer waves)
         const Geo g{a.shape.channels, a.shape.tokens, a.shape.channels / kLanes, a.shape.tokens / 2 / kSteps};
         const dim3 grid(g.ncg * ((g.ntb + 7) / 8), 2);       // y: pass
@@ -3168,9 +3146,8 @@ hipError_t encode_all(const EncodeLaunch& a, const DevTables& t, hipStream_t st)
 
 template <uint32_t DT, uint32_t MODE>
 hipError_t decode_all(const DecodeLaunch& a, const DevTables& t, hipStream_t st) {
-    const int v = variant().dec;
     const bool fits = slab_fits(a.shape);
-    if (DT == SKV_E4M3 && MODE == SKV_RESIDUAL && fits && !g_force_v1 && v == 0 && t.max_n + 1 <= 64 &&
+    if (DT == SKV_E4M3 && MODE == SKV_RESIDUAL && fits && t.max_n + 1 <= 64 &&
         dec_e4m3_lds(64) <= kLdsLimit) {
         const LdsGeo lg = lds_geometry(a.shape);
         const bool small = t.max_n + 1 <= 32;
@@ -3183,7 +3160,7 @@ hipError_t decode_all(const DecodeLaunch& a, const DevTables& t, hipStream_t st)
         });
         return hipGetLastError();
     }
-    if (DT == SKV_E4M3 && MODE == SKV_RESIDUAL_EXP && fits && !g_force_v1 && v == 0 &&
+    if (DT == SKV_E4M3 && MODE == SKV_RESIDUAL_EXP && fits &&
         t.max_n + 2 <= kExpRows && dec_exp_lds() <= kLdsLimit) {
         const LdsGeo lg = lds_geometry(a.shape);
         auto k = decode_e4m3<kExpRows, true>;
@@ -3196,7 +3173,7 @@ hipError_t decode_all(const DecodeLaunch& a, const DevTables& t, hipStream_t st)
     }
     // the bf16 decoder moves predictor and output rows 8 bytes per lane
     const bool aligned8 = (reinterpret_cast<uintptr_t>(a.aux) | reinterpret_cast<uintptr_t>(a.out)) % 8 == 0;
-    if (DT == SKV_BF16 && MODE == SKV_RESIDUAL && fits && !g_force_v1 && v == 0 && aligned8 && dec_bf16_lds() <= kLdsLimit) {
+    if (DT == SKV_BF16 && MODE == SKV_RESIDUAL && fits && aligned8 && dec_bf16_lds() <= kLdsLimit) {
         const LdsGeo lg = lds_geometry(a.shape);
         hipError_t e = allow_lds(decode_bf16, dec_bf16_lds());
         if (e != hipSuccess) return e;
@@ -3205,18 +3182,10 @@ hipError_t decode_all(const DecodeLaunch& a, const DevTables& t, hipStream_t st)
         });
         return hipGetLastError();
     }
-    const bool half = v != 1 && v != 3;
-    const size_t lb = decode_lds_bytes(t, DT, half);
-    if (MODE == SKV_RESIDUAL && fits && lb <= kLdsLimit && !g_force_v1 && v >= 0) {
+    const size_t lb = decode_lds_bytes(t, DT, true);
+    if (MODE == SKV_RESIDUAL && fits && lb <= kLdsLimit) {
         const LdsGeo lg = lds_geometry(a.shape);
         auto k = decode_lds<DT, 1, 4, true>;
-        switch (v) {
-            case 1: k = decode_lds<DT, 1, 4, false>; break;
-            case 2: k = decode_lds<DT, 1, 8, true>; break;
-            case 3: k = decode_lds<DT, 2, 2, false>; break;
-            case 4: k = decode_lds<DT, 2, 2, true>; break;
-            default: break;
-        }
         hipError_t e = allow_lds(k, lb);
         if (e != hipSuccess) return e;
         timed("decode_streams", st, [&](hipEvent_t e0, hipEvent_t e1) {
@@ -3229,7 +3198,7 @@ hipError_t decode_all(const DecodeLaunch& a, const DevTables& t, hipStream_t st)
     const uint32_t grid = uint32_t((per + kStreamsPerBlock - 1) / kStreamsPerBlock);
     for (uint64_t ps = 0; ps < passes; ++ps)
         timed("decode_streams", st, [&](hipEvent_t e0, hipEvent_t e1) {
-            if (MODE == SKV_CHECKERBOARD && fits && !g_force_v1 && v == 0)
+            if (MODE == SKV_CHECKERBOARD && fits)
                 hipExtLaunchKernelGGL((decode_cb<2, 8>), dim3(a.shape.channels / kLanes * ((per / (a.shape.channels / kLanes) + 7) / 8)),
                                    dim3(256), 0, st, e0, e1, 0, a, t, ps * per, per);
             else

@@ -6,8 +6,11 @@ kernels. There is no CPU fallback: a missing library or GPU raises.
 """
 from __future__ import annotations
 
+import atexit
 import ctypes
 import os
+import sys
+import weakref
 
 import numpy as np
 import torch
@@ -84,12 +87,17 @@ def make_shape(dtype: int, mode: int, layers: int, kv: int, tokens: int, channel
     return Shape(ABI_VERSION, dtype, mode, layers, kv, tokens, channels)
 
 
+# Every open blob, so that the exit hook below can release them.
+_live_tables = weakref.WeakSet()
+
+
 class Tables:
     """A library-owned table blob (host), uploaded to each device on first use."""
 
     def __init__(self, ptr: int, nbytes: int):
         self._ptr = ctypes.c_void_p(ptr)
         self.nbytes = nbytes
+        _live_tables.add(self)
         b = self.bytes()[:64]
         self.dtype, self.mode = b[6], b[7]
         self.layers = int.from_bytes(b[12:16], "little")
@@ -111,9 +119,26 @@ class Tables:
             _lib.skv_free(self._ptr)
         self._ptr = ctypes.c_void_p(None)
 
-    def __del__(self):
+    def __del__(self, _finalizing=sys.is_finalizing):
+        # During interpreter shutdown the exit hook has already released every
+        # blob; a finalizer running later (module globals may be gone by then)
+        # must not make HIP calls.
+        if _finalizing():
+            return
         try:
             self.close()
+        except Exception:
+            pass
+
+
+@atexit.register
+def _release_tables():
+    """Release every open blob and its device tables at interpreter exit,
+    while torch and the HIP runtime are still whole: exit hooks run before
+    module teardown, and long before the runtime's own static destructors."""
+    for t in list(_live_tables):
+        try:
+            t.close()
         except Exception:
             pass
 
