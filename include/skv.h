@@ -142,6 +142,31 @@ int skv_encode(const void* tables_blob, const skv_shape* s, const void* d_target
                void* d_out, size_t out_capacity, size_t* out_bytes,
                void* d_work, size_t* work_bytes, hipStream_t stream);
 
+/* Encode without allocating (device), for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  Same container as skv_encode for the
+ * same inputs and blob; the workspace is a fixed array of
+ * SKV_NOALLOC_WORK_BYTES that the library keeps on every device it runs on
+ * until the process ends, so no workspace argument is taken and nothing is
+ * allocated or freed by the call.
+ *   - A shape whose workspace (the size skv_encode reports in *work_bytes)
+ *     exceeds SKV_NOALLOC_WORK_BYTES returns SKV_ERR_SHAPE (64 MiB holds
+ *     about 8,000 e4m3 or 4,000 bf16 / int16 streams of 4096 values).
+ *   - The blob's device tables must already be on the current device (any
+ *     earlier skv_encode, skv_decode, skv_decode_range or skv_transfer with
+ *     this blob on this device puts them there; building them allocates),
+ *     else SKV_ERR_ARG.
+ *   - d_out == NULL sets *out_bytes to the bound; else out_capacity must
+ *     hold the container (SKV_ERR_CAPACITY, *out_bytes = the size needed).
+ *   - Calls on one device share its array.  The library runs them one at a
+ *     time (each returns only after its kernels have finished with the
+ *     array), so calls from several threads do not race; the array keeps the
+ *     last call's contents, none of which a call reads before writing it.
+ * Blocks the host until the container size is known. */
+#define SKV_NOALLOC_WORK_BYTES (64u << 20)
+int skv_encode_noalloc(const void* tables_blob, const skv_shape* s, const void* d_target, const void* d_aux,
+                       void* d_out, size_t out_capacity, size_t* out_bytes, hipStream_t stream);
+
 /* Decode (device).  The receiver replays the predictor, decodes the
  * residual and adds it back, which returns the original bytes exactly
  * ("Speculative KV coding" page, section "Core idea", flow steps 3-4; the stored

@@ -278,6 +278,51 @@ int skv_encode(const void* tables_blob, const skv_shape* s, const void* d_target
                        true);
 }
 
+int skv_encode_noalloc(const void* tables_blob, const skv_shape* s, const void* d_target, const void* d_aux,
+                       void* d_out, size_t out_capacity, size_t* out_bytes, hipStream_t stream) {
+    if (!tables_blob || !s || !out_bytes) return SKV_ERR_ARG;
+    if (!skv::shape_supported(*s, true)) return SKV_ERR_SHAPE;
+    Blob* b = find_blob(tables_blob);
+    if (!b) return SKV_ERR_ARG;
+    if (!same_geometry(b->shape, *s)) return SKV_ERR_TABLES;
+    const uint64_t n = skv::stream_count(*s);
+    const uint32_t raw = skv::kSyms * skv::elem_bytes(s->dtype);
+    const uint64_t bound = skv::kHeaderBytes + 8 * (n + 1) + n * raw;
+    if (skv::encode_work_bytes(n, raw) > skv::kNoAllocWorkBytes) return SKV_ERR_SHAPE;
+    if (!d_out) {
+        *out_bytes = bound;
+        return SKV_OK;
+    }
+    if (!d_target || !d_aux) return SKV_ERR_ARG;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return SKV_ERR_DEVICE;
+    const skv::DevTables* t = nullptr;
+    {
+        // resident tables only: building them would allocate
+        std::lock_guard<std::mutex> lk(b->dev_mu);
+        auto it = b->dev.find(dev);
+        if (it == b->dev.end()) return SKV_ERR_ARG;
+        t = &it->second;
+    }
+    if (dev < 0 || dev >= 64) return SKV_ERR_DEVICE;
+    std::lock_guard<std::mutex> lk(skv::noalloc_lock(dev));
+    uint8_t* w = nullptr;
+    if (skv::noalloc_workspace(dev, &w) != hipSuccess) return SKV_ERR_DEVICE;
+    skv::EncodeLaunch a = encode_launch(b, *s, d_target, d_aux, d_out, out_capacity, w);
+    skv::timing_reset();
+    if (skv::launch_encode(a, *t, stream) != hipSuccess) return SKV_ERR_DEVICE;
+    // the size through a plain copy and a stream synchronization (the pinned
+    // staging buffer of the other calls is allocated on a thread's first use)
+    uint64_t payload = 0;
+    if (hipMemcpyAsync(&payload, a.total, 8, hipMemcpyDeviceToHost, stream) != hipSuccess ||
+        hipStreamSynchronize(stream) != hipSuccess)
+        return SKV_ERR_DEVICE;
+    skv::timing_collect();
+    const uint64_t total = skv::kHeaderBytes + 8 * (n + 1) + payload;
+    *out_bytes = total;
+    return total > out_capacity ? SKV_ERR_CAPACITY : SKV_OK;
+}
+
 // Decode of token blocks [tb0, tb1) of every slab of a container (all of them
 // for skv_decode).  tb1 = 0 stands for the container's last token block + 1.
 static int decode_blocks(const void* tables_blob, const void* d_in, size_t in_bytes, bool range, uint32_t token_begin,

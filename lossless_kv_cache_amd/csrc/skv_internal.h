@@ -7,6 +7,7 @@
 
 #include <cstddef>
 #include <cstdint>
+#include <mutex>
 #include <hip/hip_runtime.h>
 
 #include "../../include/skv.h"
@@ -109,6 +110,14 @@ hipError_t launch_encode(const EncodeLaunch& a, const DevTables& t, hipStream_t 
 hipError_t launch_decode(const DecodeLaunch& a, const DevTables& t, hipStream_t stream);
 hipError_t launch_clear_u32(uint32_t* p, uint32_t n, hipStream_t stream);
 uint64_t encode_work_bytes(uint64_t n_streams, uint32_t raw_bytes);
+
+// Fixed device workspace of skv_encode_noalloc (SKV_NOALLOC_WORK_BYTES).
+// noalloc_workspace: the current device's address of it (dev = the current
+// device, 0 <= dev < 64), looked up once per device; call it holding
+// noalloc_lock(dev), which also serializes the calls that use it.
+constexpr size_t kNoAllocWorkBytes = size_t(SKV_NOALLOC_WORK_BYTES);
+hipError_t noalloc_workspace(int dev, uint8_t** ptr);
+std::mutex& noalloc_lock(int dev);
 
 // per-kernel timing diagnostics (process-wide, not for concurrent callers)
 int timing_enable(bool on);

@@ -20,12 +20,44 @@
 #include <algorithm>
 #include <cstdio>
 #include <cstdlib>
+#include <mutex>
 
 #include <hip/hip_ext.h>
 
 #include "skv_internal.h"
 
+// Workspace of skv_encode_noalloc, for callers that cannot allocate device
+// memory: one fixed array, of which the runtime holds a copy on every GPU
+// the library runs on until the process ends.  Host code never uses this
+// name as an address (on the host it stands for the symbol, not for device
+// memory): it asks the runtime for the current device's address of it once
+// per device (noalloc_workspace below) and passes that address to kernels.
+static __device__ __align__(256) uint8_t scratch[skv::kNoAllocWorkBytes];
+
 namespace skv {
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_noalloc_mu[kMaxDevices];     // one call at a time per device
+uint8_t* g_noalloc_ptr[kMaxDevices] = {};
+}  // namespace
+
+hipError_t noalloc_workspace(int dev, uint8_t** ptr) {
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    if (!g_noalloc_ptr[dev]) {
+        // the caller holds g_noalloc_mu[dev] and has made `dev` current
+        void* p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        g_noalloc_ptr[dev] = static_cast<uint8_t*>(p);
+    }
+    *ptr = g_noalloc_ptr[dev];
+    return hipSuccess;
+}
+
+std::mutex& noalloc_lock(int dev) { return g_noalloc_mu[dev]; }
+
 namespace {
 
 constexpr uint32_t kStreamsPerBlock = 8;    // 256 threads = 4 wavefronts x 2 streams

@@ -59,6 +59,8 @@ def lib():
         L.skv_load_tables.argtypes = [vp, sz, ctypes.POINTER(vp)]
         L.skv_encode.restype = ctypes.c_int
         L.skv_encode.argtypes = [vp, sp, vp, vp, vp, sz, psz, vp, psz, vp]
+        L.skv_encode_noalloc.restype = ctypes.c_int
+        L.skv_encode_noalloc.argtypes = [vp, sp, vp, vp, vp, sz, psz, vp]
         L.skv_decode.restype = ctypes.c_int
         L.skv_decode.argtypes = [vp, vp, sz, vp, vp, sz, vp, psz, vp]
         L.skv_decode_range.restype = ctypes.c_int
@@ -270,6 +272,35 @@ def encode(tables: Tables, target: torch.Tensor, aux: torch.Tensor) -> torch.Ten
     """Encode a device cache; returns a fresh uint8 device tensor (the container)."""
     enc = Encoder(tables, tokens_of(tables, target), target.device)
     return enc(target, aux).clone()
+
+
+NOALLOC_WORK_BYTES = 64 << 20
+
+
+def encode_noalloc(tables: Tables, target: torch.Tensor, aux: torch.Tensor, out: torch.Tensor) -> torch.Tensor:
+    """Encode into the caller's uint8 device tensor `out` through the entry
+    point that allocates nothing (its workspace is the library's fixed
+    per-device array); returns the view of `out` that holds the container.
+    The tables must have been used on this device before (see
+    skv_encode_noalloc)."""
+    shape = tables.shape(tokens_of(tables, target))
+    pt = _check_cache(target, "target", tables, shape.tokens)
+    pa = _check_cache(aux, "aux", tables, shape.tokens)
+    po = _check_container(out)
+    ob = ctypes.c_size_t()
+    _check(lib().skv_encode_noalloc(tables.ptr, ctypes.byref(shape), pt, pa, po, out.numel(), ctypes.byref(ob),
+                                    _stream()), "skv_encode_noalloc")
+    return out[: ob.value]
+
+
+def encode_noalloc_bound(tables: Tables, tokens: int) -> int:
+    """Container bound for encode_noalloc (raises SkvError(ERR_SHAPE) when the
+    shape's workspace exceeds the fixed array)."""
+    shape = tables.shape(tokens)
+    ob = ctypes.c_size_t()
+    _check(lib().skv_encode_noalloc(tables.ptr, ctypes.byref(shape), None, None, None, 0, ctypes.byref(ob), None),
+           "skv_encode_noalloc(size query)")
+    return ob.value
 
 
 _decode_work = {}

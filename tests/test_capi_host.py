@@ -226,3 +226,21 @@ def test_binding_refuses_mis_sized_device_inputs(skv):
         skv._check_cache(torch.zeros((1, 1, 256, 64), dtype=torch.int16), "target", tc, 256)
     with pytest.raises(ValueError, match="device tensor"):
         skv._check_cache(torch.zeros((256, 64), dtype=torch.int16), "target", tc, 256)
+
+
+def test_noalloc_size_limits_on_host(skv):
+    """skv_encode_noalloc's size checks need no device: a shape whose
+    workspace fits the fixed array reports the same bound as skv_encode, a
+    larger one is refused with SKV_ERR_SHAPE."""
+    tabs = _small_tables(skv, skv.E4M3, skv.RESIDUAL, layers=1, channels=1024)
+    for tokens in (128, 1024, 4096):
+        s = tabs.shape(tokens)
+        ob, wb = ctypes.c_size_t(), ctypes.c_size_t()
+        assert skv.lib().skv_encode(tabs.ptr, ctypes.byref(s), None, None, None, 0, ctypes.byref(ob), None,
+                                    ctypes.byref(wb), None) == 0
+        assert wb.value <= skv.NOALLOC_WORK_BYTES
+        assert skv.encode_noalloc_bound(tabs, tokens) == ob.value
+    # 32768 tokens x 1024 channels x K,V: 16384 streams of 8 KiB scratch each
+    with pytest.raises(skv.SkvError) as e:
+        skv.encode_noalloc_bound(tabs, 32768)
+    assert e.value.status == skv.ERR_SHAPE
