@@ -18,7 +18,7 @@ _SRC = os.path.join(_HERE, "skv_oracle.c")
 _LIB = os.path.join(_HERE, "libskv_oracle.so")
 
 BF16, E4M3, INT16 = 1, 2, 3
-RESIDUAL, CHECKERBOARD, RESIDUAL_EXP = 0, 1, 2
+RESIDUAL, CHECKERBOARD, RESIDUAL_EXP, CHECKERBOARD_MAP = 0, 1, 2, 3
 OK, E_ARG, E_SHAPE, E_CAPACITY, E_CORRUPT, E_TABLES = 0, -1, -2, -3, -4, -5
 
 
@@ -66,6 +66,10 @@ def lib():
             "skvo_quantize": (None, [vp, ctypes.c_int, vp]),
             "skvo_fnv1a64": (u64, [vp, ctypes.c_size_t]),
             "skvo_blob_bytes": (u64, [sp]),
+            "skvo_blob_bytes_map": (u64, [sp, u32]),
+            "skvo_dckv_map": (ctypes.c_int, [vp, vp, u32, u32, u32, u32, u32, vp, vp, vp, ctypes.c_int]),
+            "skvo_fit_tables_map": (ctypes.c_int, [sp, vp, vp, u32, u32, u32, u32, vp, vp, vp, u64,
+                                                   ctypes.POINTER(u64)]),
             "skvo_bound": (u64, [sp]),
             "skvo_n_streams": (u64, [sp]),
             "skvo_fit_tables": (ctypes.c_int, [sp, vp, vp, u32, vp, u64, ctypes.POINTER(u64)]),
@@ -225,6 +229,42 @@ def fit_tables(shape: Shape, calib_t: np.ndarray, calib_a: np.ndarray, calib_tok
     rc = lib().skvo_fit_tables(ctypes.byref(shape), _ptr(ct), _ptr(ca), calib_tokens, _ptr(out), need, ctypes.byref(nb))
     if rc:
         raise RuntimeError(f"oracle fit_tables failed: {rc}")
+    return out[: nb.value].tobytes()
+
+
+def dckv_map(coef: np.ndarray, G: np.ndarray, V: np.ndarray, U: np.ndarray, sh1: int, sh2: int,
+             threads: int = 1) -> np.ndarray:
+    """Side input with the decoded-neighbour map applied (odd rows G', even
+    rows G) for [T][C] int16 coefficients and G; V int8 [k][2C], U int8 [C][k]."""
+    c = np.ascontiguousarray(coef, dtype=np.int16)
+    g = np.ascontiguousarray(G, dtype=np.int16)
+    v = np.ascontiguousarray(V, dtype=np.int8)
+    u = np.ascontiguousarray(U, dtype=np.int8)
+    T, C = c.shape
+    k = v.shape[0]
+    assert g.shape == (T, C) and v.shape == (k, 2 * C) and u.shape == (C, k)
+    out = np.zeros_like(g)
+    rc = lib().skvo_dckv_map(_ptr(c), _ptr(g), T, C, k, sh1, sh2, _ptr(v), _ptr(u), _ptr(out), threads)
+    if rc:
+        raise RuntimeError(f"oracle dckv_map failed: {rc}")
+    return out
+
+
+def fit_tables_map(shape: Shape, calib_coef: np.ndarray, calib_G: np.ndarray, calib_tokens: int, V: np.ndarray,
+                   U: np.ndarray, sh1: int, sh2: int) -> bytes:
+    """Tables of the decoded-neighbour-map mode (checkerboard fit on G', then the map)."""
+    v = np.ascontiguousarray(V, dtype=np.int8)
+    u = np.ascontiguousarray(U, dtype=np.int8)
+    k = v.shape[0]
+    need = lib().skvo_blob_bytes_map(ctypes.byref(shape), k)
+    out = np.zeros(need, dtype=np.uint8)
+    nb = ctypes.c_uint64()
+    c = np.ascontiguousarray(calib_coef, dtype=np.int16)
+    g = np.ascontiguousarray(calib_G, dtype=np.int16)
+    rc = lib().skvo_fit_tables_map(ctypes.byref(shape), _ptr(c), _ptr(g), calib_tokens, k, sh1, sh2, _ptr(v), _ptr(u),
+                                   _ptr(out), need, ctypes.byref(nb))
+    if rc:
+        raise RuntimeError(f"oracle fit_tables_map failed: {rc}")
     return out[: nb.value].tobytes()
 
 

@@ -56,7 +56,7 @@
 #define SKVO_TAB_BYTES 514    /* u16 n + u16 freq[256] */
 
 enum { DT_BF16 = 1, DT_E4M3 = 2, DT_INT16 = 3 };
-enum { MODE_RESIDUAL = 0, MODE_CHECKERBOARD = 1, MODE_RESIDUAL_EXP = 2 };
+enum { MODE_RESIDUAL = 0, MODE_CHECKERBOARD = 1, MODE_RESIDUAL_EXP = 2, MODE_CHECKERBOARD_MAP = 3 };
 enum { E_OK = 0, E_ARG = -1, E_SHAPE = -2, E_CAPACITY = -3, E_CORRUPT = -4, E_TABLES = -5 };
 
 /* ------------------------------------------------------------------ */
@@ -197,6 +197,86 @@ int32_t skvo_dckv_mean(const int16_t* coef, const int16_t* G, uint32_t T, uint32
         mu += 8 * (left + right);
     }
     return mu;
+}
+
+/* Decoded-neighbour map.  [DCKV] "How it differs": an odd position is
+ * predicted from both of its already decoded neighbours and its own token
+ * embedding through a low-rank linear map.  Reading: the embedding part is
+ * the side input G (as above); the neighbour part is a rank-k map applied to
+ * the two decoded neighbour rows in exact integer arithmetic, whose output,
+ * in 1/16 cells, is added to the odd token's side input:
+ *   n        the left row then the right row of the odd token (2C values;
+ *            the last odd token repeats its left row), each value saturated
+ *            to at most 32639
+ *   h_j      = sum over i < 2C of V[j][i] * n_i               (exact)
+ *   q_j      = h_j / 2^sh1 rounded half up, clamped to [-128, 127]
+ *   m_c      = (sum over j < k of U[c][j] * q_j) / 2^sh2 rounded half up
+ *   G'[t][c] = G[t][c] + m_c clamped to [-32768, 32767]
+ * V is int8 [k][2C] and U int8 [C][k], both row-major.  Even tokens keep
+ * G.  The mean of an odd coefficient is then G' + 8 * (left + right), as in
+ * the checkerboard mode, which the map reduces to when U is zero. */
+typedef struct {
+    uint32_t k, sh1, sh2;
+    const int8_t* V;
+    const int8_t* U;
+} skvo_map;
+
+/* v / 2^s rounded half up: floor((v + 2^(s-1)) / 2^s). */
+static int64_t round_shift(int64_t v, uint32_t s) {
+    if (s == 0) return v;
+    int64_t d = (int64_t)1 << s;
+    int64_t a = v + d / 2;
+    int64_t q = a / d;
+    if (a % d != 0 && a < 0) q -= 1;   /* C division truncates toward zero */
+    return q;
+}
+
+static int64_t clamp64(int64_t v, int64_t lo, int64_t hi) { return v < lo ? lo : (v > hi ? hi : v); }
+
+/* Side input with the map applied: Gout[t] = G[t] on even tokens, G'[t] on
+ * odd ones, computed from the even rows of `coef`. */
+static void dckv_map_side(const int16_t* coef, const int16_t* G, uint32_t T, uint32_t C, const skvo_map* m,
+                          int16_t* Gout, int nthreads) {
+    if (nthreads < 1) nthreads = 1;
+#pragma omp parallel for schedule(dynamic, 8) num_threads(nthreads)
+    for (int64_t tt = 0; tt < (int64_t)T; ++tt) {
+        uint32_t t = (uint32_t)tt;
+        const int16_t* g = G + (size_t)t * C;
+        int16_t* o = Gout + (size_t)t * C;
+        if (!(t & 1u)) {
+            memcpy(o, g, (size_t)C * sizeof(int16_t));
+            continue;
+        }
+        uint32_t left = t - 1, right = (t + 1 < T) ? t + 1 : t - 1;
+        int64_t* n = (int64_t*)malloc(2 * (size_t)C * sizeof(int64_t));
+        int64_t* q = (int64_t*)malloc((size_t)m->k * sizeof(int64_t));
+        for (uint32_t i = 0; i < C; ++i) {
+            int64_t a = coef[(size_t)left * C + i], b = coef[(size_t)right * C + i];
+            n[i] = a > 32639 ? 32639 : a;
+            n[C + i] = b > 32639 ? 32639 : b;
+        }
+        for (uint32_t j = 0; j < m->k; ++j) {
+            int64_t h = 0;
+            for (uint32_t i = 0; i < 2 * C; ++i) h += (int64_t)m->V[(size_t)j * 2 * C + i] * n[i];
+            q[j] = clamp64(round_shift(h, m->sh1), -128, 127);
+        }
+        for (uint32_t c = 0; c < C; ++c) {
+            int64_t acc = 0;
+            for (uint32_t j = 0; j < m->k; ++j) acc += (int64_t)m->U[(size_t)c * m->k + j] * q[j];
+            o[c] = (int16_t)clamp64((int64_t)g[c] + round_shift(acc, m->sh2), -32768, 32767);
+        }
+        free(n);
+        free(q);
+    }
+}
+
+/* The map on caller-supplied arrays (tests): coef, G and Gout are [T][C]. */
+int skvo_dckv_map(const int16_t* coef, const int16_t* G, uint32_t T, uint32_t C, uint32_t k, uint32_t sh1,
+                  uint32_t sh2, const int8_t* V, const int8_t* U, int16_t* Gout, int nthreads) {
+    if (!coef || !G || !V || !U || !Gout || k == 0 || sh1 > 40 || sh2 > 30) return E_ARG;
+    skvo_map m = {k, sh1, sh2, V, U};
+    dckv_map_side(coef, G, T, C, &m, Gout, nthreads);
+    return E_OK;
 }
 
 /* ------------------------------------------------------------------ */
@@ -359,6 +439,8 @@ typedef struct {
 static int elem_bytes(uint32_t dtype) { return dtype == DT_E4M3 ? 1 : 2; }
 /* Modes that code [layers][kv][tokens][channels] residuals against a predictor. */
 static int residual_like(uint32_t mode) { return mode == MODE_RESIDUAL || mode == MODE_RESIDUAL_EXP; }
+/* Modes that code [tokens][channels] coefficients in two checkerboard passes. */
+static int checkerboard_like(uint32_t mode) { return mode == MODE_CHECKERBOARD || mode == MODE_CHECKERBOARD_MAP; }
 static int elem_bits(uint32_t dtype) { return dtype == DT_E4M3 ? 8 : 16; }
 
 static int shape_ok(const skvo_shape* s) {
@@ -369,7 +451,7 @@ static int shape_ok(const skvo_shape* s) {
         if (s->layers == 0 || s->kv == 0 || s->tokens == 0) return 0;
         return s->tokens % SKVO_STEPS == 0;
     }
-    if (s->mode == MODE_CHECKERBOARD) {
+    if (checkerboard_like(s->mode)) {
         if (s->dtype != DT_INT16 || s->layers != 1 || s->kv != 1) return 0;
         return s->tokens > 0 && s->tokens % (2 * SKVO_STEPS) == 0;
     }
@@ -396,18 +478,45 @@ static uint64_t n_streams_of(const skvo_shape* s) {
 
 uint64_t skvo_blob_bytes(const skvo_shape* s) { return SKVO_HDR + n_tables_of(s) * SKVO_TAB_BYTES + n_bases_of(s); }
 
+/* Map section after the records of a decoded-neighbour-map blob:
+ * u32 k | u32 sh1 | u32 sh2 | u32 0 | int8 V[k][2C] | int8 U[C][k]. */
+#define SKVO_MAP_HDR 16
+static uint64_t map_bytes(uint32_t k, uint32_t C) { return SKVO_MAP_HDR + 3ull * k * C; }
+uint64_t skvo_blob_bytes_map(const skvo_shape* s, uint32_t k) { return skvo_blob_bytes(s) + map_bytes(k, s->channels); }
+
+/* Map parameters accepted in a blob: rank a multiple of 16 up to 256. */
+static int map_params_ok(uint32_t k, uint32_t sh1, uint32_t sh2) {
+    return k >= 16 && k <= 256 && k % 16 == 0 && sh1 <= 40 && sh2 <= 30;
+}
+
 /* Parse a table blob: header fields must match the shape, every table must
  * hold 1..255 direct symbols plus ESC, positive frequencies summing to 2^12
  * and zeros beyond ESC. */
-static int parse_blob(const uint8_t* blob, size_t nbytes, const skvo_shape* s, skvo_table** out,
-                      const uint8_t** bases) {
+static int parse_blob_map(const uint8_t* blob, size_t nbytes, const skvo_shape* s, skvo_table** out,
+                          const uint8_t** bases, skvo_map* map) {
     if (nbytes < SKVO_HDR || memcmp(blob, "SKVT", 4) != 0 || get16(blob + 4) != 1) return E_TABLES;
     if (blob[6] != s->dtype || blob[7] != s->mode) return E_TABLES;
     uint64_t nt = n_tables_of(s);
     if (get32(blob + 8) != nt || get32(blob + 12) != s->layers || get32(blob + 16) != s->kv ||
         get32(blob + 20) != s->channels)
         return E_TABLES;
-    if (get64(blob + 32) != nbytes || nbytes != skvo_blob_bytes(s)) return E_TABLES;
+    if (s->mode == MODE_CHECKERBOARD_MAP) {
+        uint64_t at = skvo_blob_bytes(s);
+        if (nbytes < at + SKVO_MAP_HDR) return E_TABLES;
+        const uint8_t* mh = blob + at;
+        uint32_t k = get32(mh), sh1 = get32(mh + 4), sh2 = get32(mh + 8);
+        if (!map_params_ok(k, sh1, sh2) || get32(mh + 12) != 0) return E_TABLES;
+        if (get64(blob + 32) != nbytes || nbytes != at + map_bytes(k, s->channels)) return E_TABLES;
+        if (map) {
+            map->k = k;
+            map->sh1 = sh1;
+            map->sh2 = sh2;
+            map->V = (const int8_t*)(mh + SKVO_MAP_HDR);
+            map->U = map->V + 2ull * k * s->channels;
+        }
+    } else if (get64(blob + 32) != nbytes || nbytes != skvo_blob_bytes(s)) {
+        return E_TABLES;
+    }
     skvo_table* t = (skvo_table*)malloc(nt * sizeof(skvo_table));
     for (uint64_t j = 0; j < nt; ++j) {
         const uint8_t* p = blob + SKVO_HDR + j * SKVO_TAB_BYTES;
@@ -426,6 +535,11 @@ static int parse_blob(const uint8_t* blob, size_t nbytes, const skvo_shape* s, s
     *out = t;
     *bases = blob + SKVO_HDR + nt * SKVO_TAB_BYTES;   /* n_bases_of(s) bytes */
     return E_OK;
+}
+
+static int parse_blob(const uint8_t* blob, size_t nbytes, const skvo_shape* s, skvo_table** out,
+                      const uint8_t** bases) {
+    return parse_blob_map(blob, nbytes, s, out, bases, NULL);
 }
 
 /* Stream id -> (slab, token block, channel group); see the container layout:
@@ -567,8 +681,16 @@ int64_t skvo_encode(const uint8_t* blob, size_t blob_bytes, const skvo_shape* s,
     if (!shape_ok(s)) return E_SHAPE;
     skvo_table* tabs = NULL;
     const uint8_t* bases = NULL;
-    int rc = parse_blob(blob, blob_bytes, s, &tabs, &bases);
+    skvo_map map;
+    int rc = parse_blob_map(blob, blob_bytes, s, &tabs, &bases, &map);
     if (rc) return rc;
+    int16_t* gmap = NULL;
+    if (s->mode == MODE_CHECKERBOARD_MAP) {
+        /* odd tokens take the side input with the map of their true (= decoded) even neighbours */
+        gmap = (int16_t*)malloc((size_t)s->tokens * s->channels * sizeof(int16_t));
+        dckv_map_side((const int16_t*)tgt, (const int16_t*)aux, s->tokens, s->channels, &map, gmap, nthreads);
+        aux = gmap;
+    }
     uint64_t n = n_streams_of(s);
     size_t rawb = (size_t)SKVO_SYMS * elem_bytes(s->dtype);
     uint8_t* tmp = (uint8_t*)malloc(n * rawb);
@@ -582,6 +704,7 @@ int64_t skvo_encode(const uint8_t* blob, size_t blob_bytes, const skvo_shape* s,
     for (uint64_t id = 0; id < n; ++id) payload += size[id];
     uint64_t total = SKVO_HDR + 8 * (n + 1) + payload;
     if (need) *need = total;
+    free(gmap);
     if (!out || cap < total) {
         free(tmp); free(size); free(raw); free(tabs);
         return out ? E_CAPACITY : (int64_t)total;
@@ -665,7 +788,8 @@ int skvo_decode(const uint8_t* blob, size_t blob_bytes, const uint8_t* in, uint6
     if (get64(in + 40) != skvo_fnv1a64(blob, blob_bytes)) return E_TABLES;
     skvo_table* tabs = NULL;
     const uint8_t* bases = NULL;
-    rc = parse_blob(blob, blob_bytes, &s, &tabs, &bases);
+    skvo_map map;
+    rc = parse_blob_map(blob, blob_bytes, &s, &tabs, &bases, &map);
     if (rc) return rc;
     uint64_t payload = get64(in + 48);
     uint64_t head = SKVO_HDR + 8 * (n + 1);
@@ -682,18 +806,27 @@ int skvo_decode(const uint8_t* blob, size_t blob_bytes, const uint8_t* in, uint6
     int passes = residual_like(s.mode) ? 1 : 2;
     uint64_t per = n / passes;
     int bad = 0;
+    int16_t* gmap = NULL;
+    const void* pass_aux = aux;
     for (int ps = 0; ps < passes; ++ps) {
+        if (ps == 1 && s.mode == MODE_CHECKERBOARD_MAP) {
+            /* the map reads the decoded even tokens */
+            gmap = (int16_t*)malloc((size_t)s.tokens * s.channels * sizeof(int16_t));
+            dckv_map_side((const int16_t*)out, (const int16_t*)aux, s.tokens, s.channels, &map, gmap, nthreads);
+            pass_aux = gmap;
+        }
         /* checkerboard: the odd pass starts only once every even token is decoded */
 #pragma omp parallel for schedule(dynamic, 64) num_threads(nthreads) reduction(| : bad)
         for (int64_t j = 0; j < (int64_t)per; ++j) {
             uint64_t id = (uint64_t)ps * per + (uint64_t)j;
             uint64_t e = get64(idx + 8 * id);
             uint64_t a = e & mask, b = get64(idx + 8 * (id + 1)) & mask;
-            int r = decode_one(&s, tabs, bases, pay + a, b - a, (int)(e >> 63), aux, out, id);
+            int r = decode_one(&s, tabs, bases, pay + a, b - a, (int)(e >> 63), pass_aux, out, id);
             if (r) bad = 1;
         }
         if (bad) break;
     }
+    free(gmap);
     free(tabs);
     return bad ? E_CORRUPT : E_OK;
 }
@@ -807,9 +940,12 @@ static void blob_header(uint8_t* h, const skvo_shape* s, uint32_t calib_tokens, 
  *   checkerboard mode: calib_t = int16 coefficients, calib_a = int16 G,
  *                      [calib_tokens][channels], calib_tokens even
  * Writes skvo_blob_bytes(s) bytes to blob (when cap allows). */
+static void fit_checkerboard(const int16_t* coef, const int16_t* G, uint32_t calib_tokens, size_t C, uint8_t* rec);
+
 int skvo_fit_tables(const skvo_shape* s, const void* calib_t, const void* calib_a, uint32_t calib_tokens,
                     uint8_t* blob, uint64_t cap, uint64_t* blob_bytes) {
     if (!s || !calib_t || !calib_a || !blob_bytes) return E_ARG;
+    if (s->mode == MODE_CHECKERBOARD_MAP) return E_SHAPE;   /* takes skvo_fit_tables_map */
     skvo_shape cs = *s;
     cs.tokens = residual_like(s->mode) ? SKVO_STEPS : 2 * SKVO_STEPS;   /* tokens do not matter here */
     if (!shape_ok(&cs) || calib_tokens == 0) return E_SHAPE;
@@ -926,8 +1062,14 @@ int skvo_fit_tables(const skvo_shape* s, const void* calib_t, const void* calib_
         free(zs);
         return E_OK;
     }
-    const int16_t* coef = (const int16_t*)calib_t;
-    const int16_t* G = (const int16_t*)calib_a;
+    if (s->mode != MODE_CHECKERBOARD) return E_SHAPE;   /* the map mode takes skvo_fit_tables_map */
+    fit_checkerboard((const int16_t*)calib_t, (const int16_t*)calib_a, calib_tokens, C, blob + SKVO_HDR);
+    return E_OK;
+}
+
+/* Checkerboard tables (16 shifted tables per component) from calibration
+ * coefficients and their side input G, [N][C], N even. */
+static void fit_checkerboard(const int16_t* coef, const int16_t* G, uint32_t calib_tokens, size_t C, uint8_t* rec) {
     for (size_t ch = 0; ch < C; ++ch) {
         double sum = 0.0;
         uint64_t cnt = 0;
@@ -953,8 +1095,39 @@ int skvo_fit_tables(const skvo_shape* s, const void* calib_t, const void* calib_
         }
         double pe = ((double)esc + 1.0) / ((double)calib_tokens + 2.0);
         for (int f = 0; f < 16; ++f)
-            build_table(pf[f], nf[f], pe, blob + SKVO_HDR + (ch * 16 + (size_t)f) * SKVO_TAB_BYTES);
+            build_table(pf[f], nf[f], pe, rec + (ch * 16 + (size_t)f) * SKVO_TAB_BYTES);
     }
+}
+
+/* Tables of the decoded-neighbour-map mode: the checkerboard fit on the
+ * calibration rows with their side input G' (the map applied to the
+ * calibration's own even rows), then the map itself after the records. */
+int skvo_fit_tables_map(const skvo_shape* s, const int16_t* calib_coef, const int16_t* calib_G,
+                        uint32_t calib_tokens, uint32_t k, uint32_t sh1, uint32_t sh2, const int8_t* V,
+                        const int8_t* U, uint8_t* blob, uint64_t cap, uint64_t* blob_bytes) {
+    if (!s || !calib_coef || !calib_G || !V || !U || !blob_bytes) return E_ARG;
+    if (s->mode != MODE_CHECKERBOARD_MAP) return E_SHAPE;
+    skvo_shape cs = *s;
+    cs.tokens = 2 * SKVO_STEPS;
+    if (!shape_ok(&cs) || calib_tokens == 0 || (calib_tokens % 2)) return E_SHAPE;
+    if (!map_params_ok(k, sh1, sh2)) return E_ARG;
+    uint64_t total = skvo_blob_bytes_map(s, k);
+    *blob_bytes = total;
+    if (!blob || cap < total) return E_CAPACITY;
+    size_t C = s->channels;
+    blob_header(blob, s, calib_tokens, total);
+    skvo_map m = {k, sh1, sh2, V, U};
+    int16_t* gmap = (int16_t*)malloc((size_t)calib_tokens * C * sizeof(int16_t));
+    dckv_map_side(calib_coef, calib_G, calib_tokens, (uint32_t)C, &m, gmap, 1);
+    fit_checkerboard(calib_coef, gmap, calib_tokens, C, blob + SKVO_HDR);
+    free(gmap);
+    uint8_t* mh = blob + skvo_blob_bytes(s);
+    memset(mh, 0, SKVO_MAP_HDR);
+    put32(mh, k);
+    put32(mh + 4, sh1);
+    put32(mh + 8, sh2);
+    memcpy(mh + SKVO_MAP_HDR, V, 2ull * k * C);
+    memcpy(mh + SKVO_MAP_HDR + 2ull * k * C, U, (size_t)k * C);
     return E_OK;
 }
 

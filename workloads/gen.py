@@ -155,7 +155,25 @@ def dckv_params(cfg: Config, device="cpu"):
     return b.to(**f32), emb.to(**f32), E.to(**f32), (U @ V).to(**f32)
 
 
-def dckv_draw(cfg: Config, purpose: int = EVAL, tokens: int | None = None, device="cpu"):
+MAP_RANK, MAP_SH1, MAP_SH2 = 64, 11, 4
+
+
+def dckv_map_weights(cfg: Config, rank: int = MAP_RANK):
+    """Seeded weights of a rank-`rank` linear map over an odd token's two
+    even neighbour rows: V int8 [rank][2C] (entries N(0, 40^2), clipped),
+    U int8 [C][rank] (row c ~ N(0, (2 b_c)^2), clipped), and the two shifts
+    (MAP_SH1, MAP_SH2) that scale them.  These are inputs of the workload,
+    like the codec weights of a trained model."""
+    g = _gen("cpu", _seed(cfg.cid, PARAMS, 1))
+    b, _, _, _ = dckv_params(cfg)
+    C = cfg.channels
+    V = (torch.randn((rank, 2 * C), generator=g, dtype=torch.float64) * 40.0).round().clamp(-127, 127)
+    U = (torch.randn((C, rank), generator=g, dtype=torch.float64) * (2.0 * b.double())[:, None]).round()
+    U = U.clamp(-127, 127)
+    return V.to(torch.int8).numpy(), U.to(torch.int8).numpy(), MAP_SH1, MAP_SH2
+
+
+def dckv_draw(cfg: Config, purpose: int = EVAL, tokens: int | None = None, device="cpu", nbr_map=None):
     """Coefficients and side input for the checkerboard configuration.
 
     Returns (coef, G): int16 tensors [tokens][channels].  G holds each
@@ -163,7 +181,9 @@ def dckv_draw(cfg: Config, purpose: int = EVAL, tokens: int | None = None, devic
     even tokens E*emb(token); odd tokens the rank-64 map UV*emb(token).  The
     coefficient of an even token is round(E*emb + Laplace(b_c)); of an odd
     token round(mean of its two even neighbours + UV*emb + Laplace(b_c)) (the
-    last odd token repeats its left neighbour).
+    last odd token repeats its left neighbour).  With nbr_map = (V, U, sh1,
+    sh2) the odd mean also adds the real-valued map of the two neighbour
+    rows n, (U (V n) / 2^sh1) / 2^sh2 / 16 cells.
     """
     T = cfg.tokens if tokens is None else tokens
     assert T % 2 == 0
@@ -182,5 +202,13 @@ def dckv_draw(cfg: Config, purpose: int = EVAL, tokens: int | None = None, devic
     coef[0::2] = torch.round(G[0::2] / 16.0 + lap[0::2]).clamp(-32768, 32767)
     left = coef[0::2]
     right = torch.cat([coef[2::2], coef[-2:-1]], dim=0)
-    coef[1::2] = torch.round((left + right) * 0.5 + G[1::2] / 16.0 + lap[1::2]).clamp(-32768, 32767)
+    odd = (left + right) * 0.5 + G[1::2] / 16.0 + lap[1::2]
+    if nbr_map is not None:
+        V, U, sh1, sh2 = nbr_map
+        C = cfg.channels
+        Vf = torch.as_tensor(V, dtype=torch.float32, device=device)
+        Uf = torch.as_tensor(U, dtype=torch.float32, device=device)
+        h = left @ Vf[:, :C].T.contiguous() + right @ Vf[:, C:].T.contiguous()
+        odd = odd + (h / 2.0 ** sh1) @ Uf.T.contiguous() / (2.0 ** sh2 * 16.0)
+    coef[1::2] = torch.round(odd).clamp(-32768, 32767)
     return coef.to(torch.int16), G.to(torch.int16)
