@@ -47,8 +47,9 @@ def main() -> int:
     ap.add_argument("--config", type=int, default=2, help="workload id (2 = Qwen3-8B-shaped e4m3)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target length of the CPU-oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--tables", choices=["channel", "exponent"], default="channel",
-                    help="residual tables per channel (default) or per slab and predictor exponent class")
+    ap.add_argument("--tables", choices=["channel", "exponent", "map"], default="channel",
+                    help="residual tables per channel (default) or per slab and predictor exponent class; "
+                         "for the DCKV workload, 'map' adds the rank-64 decoded-neighbour map")
     ap.add_argument("--transfer-layers", type=int, default=4,
                     help="layers per chunk of the transfer-pipeline measurement (0 = skip it)")
     ap.add_argument("--no-copy-probe", action="store_true",
@@ -73,19 +74,28 @@ def main() -> int:
     cfg = gen.CONFIGS[args.config]
     cb = cfg.dtype == "int16"                  # DCKV coefficients (checkerboard mode)
 
-    wl = cfg.name + ("-exponent-tables" if args.tables == "exponent" and not cb else "")
+    use_map = cb and args.tables == "map"
+    if args.tables == "map" and not cb:
+        print("--tables map applies to the DCKV coefficient workload (--config 4)", flush=True)
+        return 2
+    wl = cfg.name + ("-exponent-tables" if args.tables == "exponent" and not cb else "") + \
+        ("-neighbour-map" if use_map else "")
     log(f"generating {cfg.name}: {cfg.values} values on the GPU")
     t0 = time.perf_counter()
+    nmap = gen.dckv_map_weights(cfg) if use_map else None
     if cb:
-        tgt, prd = gen.dckv_draw(cfg, device="cuda")
-        ct, cp = gen.dckv_draw(cfg, gen.CALIB, tokens=gen.CALIB_TOKENS, device="cuda")
+        tgt, prd = gen.dckv_draw(cfg, device="cuda", nbr_map=nmap)
+        ct, cp = gen.dckv_draw(cfg, gen.CALIB, tokens=gen.CALIB_TOKENS, device="cuda", nbr_map=nmap)
     else:
         tgt, prd = gen.residual_array(cfg, device="cuda")
         ct, cp = gen.residual_array(cfg, gen.CALIB, tokens=gen.CALIB_TOKENS, device="cuda")
     torch.cuda.synchronize()
     log(f"generated in {time.perf_counter() - t0:.1f} s; fitting tables")
     t0 = time.perf_counter()
-    if cb:
+    if use_map:
+        V, U, sh_h, sh_m = nmap
+        tabs = skv.fit_tables_map(cfg.channels, ct.cpu().numpy(), cp.cpu().numpy(), gen.CALIB_TOKENS, V, U, sh_h, sh_m)
+    elif cb:
         tabs = skv.fit_tables(skv.INT16, skv.CHECKERBOARD, 1, 1, cfg.channels, ct.cpu().numpy(), cp.cpu().numpy(),
                               gen.CALIB_TOKENS)
     else:
@@ -171,6 +181,9 @@ def main() -> int:
         # predictor (or G) + container read, reconstruction out; checkerboard decodes in two launches
         "decode_streams": (raw_bytes + cont_bytes + raw_bytes) // (2 if cb else 1),
         "stream_block_sums": 0, "stream_block_scan": 0,
+        # decoded-neighbour map (once per encode, once per decode): the even rows read, the odd
+        # rows' side input read and their mapped side input written
+        "nbr_map": 3 * (raw_bytes // 2) if use_map else 0,
     }
     dom = max(ktot, key=lambda k: ktot[k] / args.steps)
     dur_s = kavg[dom] / 1e3
@@ -242,7 +255,7 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": "u32",
         "data": "synthetic",
-        "config": {"workload": wl, "tables": None if cb else args.tables, "shape": f"[{cfg.layers}][{cfg.kv}][{cfg.tokens}][{cfg.channels}]",
+        "config": {"workload": wl, "tables": ("neighbour-map rank 64" if use_map else None) if cb else args.tables, "shape": f"[{cfg.layers}][{cfg.kv}][{cfg.tokens}][{cfg.channels}]",
                    "element": cfg.dtype, "values": cfg.values, "raw_bytes": raw_bytes, "streams": n_streams,
                    "step": "encode + decode of the whole cache", "container_bytes": cont_bytes},
         "ratio": round(ratio, 4),
@@ -428,7 +441,7 @@ def cpu_baseline_cb(cfg, tabs, coef, G, seconds):
     for a in range(0, cfg.tokens, span):
         c = coef[a:a + span].cpu().numpy()
         g = G[a:a + span].cpu().numpy()
-        shape = oracle.make_shape(oracle.INT16, oracle.CHECKERBOARD, 1, 1, span, cfg.channels)
+        shape = oracle.make_shape(oracle.INT16, tabs.mode, 1, 1, span, cfg.channels)
         t0 = time.perf_counter()
         cont = oracle.encode(blob, shape, c, g, threads=threads)
         back = oracle.decode(blob, cont, g, c, threads=threads)

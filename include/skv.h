@@ -51,13 +51,13 @@ typedef enum {
 } skv_status;
 
 typedef enum { SKV_BF16 = 1, SKV_E4M3 = 2, SKV_INT16 = 3 } skv_dtype;
-typedef enum { SKV_RESIDUAL = 0, SKV_CHECKERBOARD = 1, SKV_RESIDUAL_EXP = 2 } skv_mode;
+typedef enum { SKV_RESIDUAL = 0, SKV_CHECKERBOARD = 1, SKV_RESIDUAL_EXP = 2, SKV_CHECKERBOARD_MAP = 3 } skv_mode;
 
 /* Cache shape.  Residual mode: arrays are [layers][kv][tokens][channels]
  * of bf16 bit patterns (2 B) or e4m3 codes (1 B), channel fastest; tokens a
- * multiple of 128, channels a multiple of 32.  Checkerboard mode: dtype
- * SKV_INT16, layers = kv = 1, arrays are [tokens][channels] int16 with
- * tokens a multiple of 256.  SKV_RESIDUAL_EXP codes the same arrays as
+ * multiple of 128, channels a multiple of 32.  Checkerboard modes
+ * (SKV_CHECKERBOARD, SKV_CHECKERBOARD_MAP): dtype SKV_INT16, layers = kv = 1,
+ * arrays are [tokens][channels] int16 with tokens a multiple of 256.  SKV_RESIDUAL_EXP codes the same arrays as
  * SKV_RESIDUAL with tables conditioned on the predictor instead of the
  * channel (see skv_fit_tables).  abi_version must be SKV_ABI_VERSION. */
 typedef struct {
@@ -103,9 +103,47 @@ typedef struct {
 int skv_fit_tables(const skv_shape* s, const void* calib_target, const void* calib_aux,
                    uint32_t calib_tokens, void** tables_blob, size_t* blob_bytes);
 
+/* Tables of SKV_CHECKERBOARD_MAP, the checkerboard mode with a map over the
+ * decoded neighbours (DCKV page, "How it differs": an odd position is
+ * predicted from both decoded neighbours and its own token embedding through
+ * a low-rank linear map).  The embedding part is the side input G, as in
+ * SKV_CHECKERBOARD; the neighbour part is a rank-k map in exact integer
+ * arithmetic whose output, in 1/16 cells, is added to an odd token's side
+ * input before its mean is formed:
+ *   n      = the token's left row then its right row (2 * channels values;
+ *            the last odd token repeats its left row), each saturated to
+ *            at most 32639
+ *   q_j    = sum_i V[j][i] n_i / 2^shift_h rounded half up, clamped to
+ *            [-128, 127]                                       (j < rank)
+ *   m_c    = sum_j U[c][j] q_j / 2^shift_m rounded half up
+ *   G'[t][c] = G[t][c] + m_c clamped to [-32768, 32767]
+ * and the odd token's mean (1/16 cells) is G' + 8 * (left + right), as in
+ * SKV_CHECKERBOARD, which this mode equals when U is zero.  The tables are
+ * those of skv_fit_tables fitted with G' in place of G on the odd
+ * calibration tokens (the map applied to the calibration's own even rows).
+ *   calib_coef, calib_G (host): [calib_tokens][channels] int16, calib_tokens even.
+ *   map (host): rank a power of two from 16 to 256, shift_h <= 40,
+ *     shift_m <= 30 (else SKV_ERR_ARG); V int8 [rank][2 * channels] and U
+ *     int8 [channels][rank], row-major, copied into the blob.
+ * The blob is that of skv_fit_tables (mode byte 3) followed by the map:
+ * u32 rank | u32 shift_h | u32 shift_m | u32 0 | V | U.  The codec computes
+ * the map between its two passes on the GPU's int8 matrix units (exact:
+ * 32-bit sums); encoding needs tokens * channels * 2 more workspace bytes,
+ * decoding writes G' into the output's odd rows before decoding them. */
+typedef struct {
+    uint32_t rank;
+    uint32_t shift_h;
+    uint32_t shift_m;
+    const int8_t* V;
+    const int8_t* U;
+} skv_nbr_map;
+int skv_fit_tables_map(const skv_shape* s, const void* calib_coef, const void* calib_G, uint32_t calib_tokens,
+                       const skv_nbr_map* map, void** tables_blob, size_t* blob_bytes);
+
 /* Copy a blob produced elsewhere (same layout as above) into a library-owned
  * blob after validating it: every table has 1 <= n <= 255, freq[0..n] >= 1
- * summing to 4096 and zeros beyond.  Release with skv_free. */
+ * summing to 4096 and zeros beyond (and, for SKV_CHECKERBOARD_MAP, a valid
+ * map section).  Release with skv_free. */
 int skv_load_tables(const void* blob, size_t blob_bytes, void** tables_blob);
 
 /* Encode (device).  The sender codes the residual of the target cache

@@ -84,6 +84,13 @@ bool same_geometry(const skv_shape& blob, const skv_shape& s) {
 
 uint64_t align256(uint64_t v) { return (v + 255) & ~uint64_t(255); }
 
+// Encoder workspace of a shape: the kernels' scratch, plus the mapped side
+// input of the odd tokens in the decoded-neighbour-map mode.
+uint64_t encode_need(const skv_shape& s) {
+    const uint64_t need = skv::encode_work_bytes(skv::stream_count(s), skv::kSyms * skv::elem_bytes(s.dtype));
+    return s.mode == SKV_CHECKERBOARD_MAP ? need + align256(uint64_t(s.tokens) * s.channels * 2) : need;
+}
+
 // Small device-to-host reads on the caller's stream (the container size, a
 // header, the integrity word).  They go through a pinned staging buffer and
 // an event that the calling thread polls, so the host sees the value as soon
@@ -163,11 +170,33 @@ int skv_fit_tables(const skv_shape* s, const void* calib_target, const void* cal
                    void** tables_blob, size_t* blob_bytes) {
     if (!s || !calib_target || !calib_aux || !tables_blob || !blob_bytes) return SKV_ERR_ARG;
     if (!skv::shape_supported(*s, false) || calib_tokens == 0) return SKV_ERR_SHAPE;
+    if (s->mode == SKV_CHECKERBOARD_MAP) return SKV_ERR_SHAPE;       // its tables need the map: skv_fit_tables_map
     if (s->mode == SKV_CHECKERBOARD && calib_tokens % 2 != 0) return SKV_ERR_SHAPE;
     const size_t size = skv::blob_size(*s);
     uint8_t* bytes = static_cast<uint8_t*>(std::malloc(size));
     if (!bytes) return SKV_ERR_NOMEM;
     const int rc = skv::fit_tables_host(*s, calib_target, calib_aux, calib_tokens, bytes, size);
+    if (rc != SKV_OK) {
+        std::free(bytes);
+        return rc;
+    }
+    *blob_bytes = size;
+    return register_blob(bytes, size, tables_blob);
+}
+
+int skv_fit_tables_map(const skv_shape* s, const void* calib_coef, const void* calib_G, uint32_t calib_tokens,
+                       const skv_nbr_map* map, void** tables_blob, size_t* blob_bytes) {
+    if (!s || !calib_coef || !calib_G || !map || !map->V || !map->U || !tables_blob || !blob_bytes)
+        return SKV_ERR_ARG;
+    if (s->mode != SKV_CHECKERBOARD_MAP || !skv::shape_supported(*s, false) || calib_tokens == 0 ||
+        calib_tokens % 2 != 0)
+        return SKV_ERR_SHAPE;
+    if (!skv::map_params_ok(map->rank, map->shift_h, map->shift_m)) return SKV_ERR_ARG;
+    const size_t size = skv::blob_size(*s) + skv::map_section_bytes(map->rank, s->channels);
+    uint8_t* bytes = static_cast<uint8_t*>(std::malloc(size));
+    if (!bytes) return SKV_ERR_NOMEM;
+    const int rc = skv::fit_tables_map_host(*s, static_cast<const int16_t*>(calib_coef),
+                                            static_cast<const int16_t*>(calib_G), calib_tokens, *map, bytes, size);
     if (rc != SKV_OK) {
         std::free(bytes);
         return rc;
@@ -208,7 +237,7 @@ void skv_free(void* tables_blob) {
 }
 
 // The encoder's launch arguments, its workspace carved from w
-// (skv::encode_work_bytes(n, raw) bytes, 256-byte aligned).
+// (encode_need(s) bytes, 256-byte aligned).
 static skv::EncodeLaunch encode_launch(const Blob* b, const skv_shape& s, const void* d_target, const void* d_aux,
                                        void* d_out, size_t out_capacity, uint8_t* w) {
     const uint64_t n = skv::stream_count(s);
@@ -216,6 +245,7 @@ static skv::EncodeLaunch encode_launch(const Blob* b, const skv_shape& s, const 
     skv::EncodeLaunch a{};
     a.target = d_target;
     a.aux = d_aux;
+    a.aux_odd = d_aux;
     a.scratch = w;
     w += align256(2 * n * raw);
     a.meta = reinterpret_cast<uint32_t*>(w);
@@ -226,6 +256,11 @@ static skv::EncodeLaunch encode_launch(const Blob* b, const skv_shape& s, const 
     a.block_off = reinterpret_cast<uint64_t*>(w);
     w += align256(8 * nb);
     a.total = reinterpret_cast<uint64_t*>(w);
+    w += 256;
+    if (s.mode == SKV_CHECKERBOARD_MAP) {
+        a.map_side = reinterpret_cast<int16_t*>(w);                    // odd rows written by the map
+        a.aux_odd = a.map_side;
+    }
     a.out = static_cast<uint8_t*>(d_out);
     a.out_capacity = out_capacity;
     a.blob_hash = b->hash;
@@ -245,7 +280,7 @@ static int encode_impl(const void* tables_blob, const skv_shape* s, const void* 
     const uint64_t n = skv::stream_count(*s);
     const uint32_t raw = skv::kSyms * skv::elem_bytes(s->dtype);
     const uint64_t bound = skv::kHeaderBytes + 8 * (n + 1) + n * raw;
-    const uint64_t need = skv::encode_work_bytes(n, raw);
+    const uint64_t need = encode_need(*s);
     if (!d_out || !d_work) {
         if (!d_out) *out_bytes = bound;
         if (!d_work) *work_bytes = need;
@@ -288,7 +323,7 @@ int skv_encode_noalloc(const void* tables_blob, const skv_shape* s, const void* 
     const uint64_t n = skv::stream_count(*s);
     const uint32_t raw = skv::kSyms * skv::elem_bytes(s->dtype);
     const uint64_t bound = skv::kHeaderBytes + 8 * (n + 1) + n * raw;
-    if (skv::encode_work_bytes(n, raw) > skv::kNoAllocWorkBytes) return SKV_ERR_SHAPE;
+    if (encode_need(*s) > skv::kNoAllocWorkBytes) return SKV_ERR_SHAPE;
     if (!d_out) {
         *out_bytes = bound;
         return SKV_OK;
@@ -360,7 +395,7 @@ static int decode_blocks(const void* tables_blob, const void* d_in, size_t in_by
     skv_shape part = s;
     uint32_t tb_base = 0;
     if (range) {
-        if (s.mode == SKV_CHECKERBOARD || token_begin >= token_end || token_end > s.tokens ||
+        if (skv::is_checkerboard(s.mode) || token_begin >= token_end || token_end > s.tokens ||
             token_begin % skv::kSteps != 0 || token_end % skv::kSteps != 0)
             return SKV_ERR_SHAPE;
         part.tokens = token_end - token_begin;
@@ -375,6 +410,9 @@ static int decode_blocks(const void* tables_blob, const void* d_in, size_t in_by
     a.pay = static_cast<const uint8_t*>(d_in) + head;
     a.payload_bytes = payload;
     a.aux = d_aux;
+    // decoded-neighbour map: the odd pass reads its side input from the output's odd rows,
+    // where the map of the decoded even rows is written between the passes
+    a.aux_odd = s.mode == SKV_CHECKERBOARD_MAP ? d_out : d_aux;
     a.out = d_out;
     a.status = static_cast<uint32_t*>(d_work);
     a.shape = part;
@@ -450,7 +488,7 @@ int skv_transfer(const void* tables_blob, const skv_shape* s, uint32_t layers_pe
                  uint64_t* chunk_offsets, const void* d_aux_recv, void* d_out, size_t out_capacity, void* d_work,
                  size_t* work_bytes, hipStream_t stream) {
     if (!tables_blob || !s || !wire_bytes || !work_bytes) return SKV_ERR_ARG;
-    if (!skv::shape_supported(*s, true) || s->mode == SKV_CHECKERBOARD) return SKV_ERR_SHAPE;
+    if (!skv::shape_supported(*s, true) || skv::is_checkerboard(s->mode)) return SKV_ERR_SHAPE;
     Blob* b = find_blob(tables_blob);
     if (!b) return SKV_ERR_ARG;
     if (!same_geometry(b->shape, *s)) return SKV_ERR_TABLES;

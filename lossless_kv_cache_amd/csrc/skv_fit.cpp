@@ -29,7 +29,7 @@ bool shape_supported(const skv_shape& s, bool need_tokens) {
         if (s.layers == 0 || s.kv == 0) return false;
         return !need_tokens || (s.tokens > 0 && s.tokens % kSteps == 0);
     }
-    if (s.mode == SKV_CHECKERBOARD) {
+    if (is_checkerboard(s.mode)) {
         if (s.dtype != SKV_INT16 || s.layers != 1 || s.kv != 1) return false;
         return !need_tokens || (s.tokens > 0 && s.tokens % (2 * kSteps) == 0);
     }
@@ -49,7 +49,7 @@ uint64_t blob_size(const skv_shape& s) {
 
 uint64_t stream_count(const skv_shape& s) {
     uint64_t groups = s.channels / kLanes;
-    if (s.mode != SKV_CHECKERBOARD) return uint64_t(s.layers) * s.kv * (s.tokens / kSteps) * groups;
+    if (!is_checkerboard(s.mode)) return uint64_t(s.layers) * s.kv * (s.tokens / kSteps) * groups;
     return 2 * uint64_t(s.tokens / (2 * kSteps)) * groups;
 }
 
@@ -173,6 +173,8 @@ uint32_t slab_tail_floor(const std::vector<uint64_t>& above_count_by_z, uint64_t
     while (z < 255 && above_count_by_z[z] > budget) ++z;
     return z;
 }
+
+void fit_checkerboard(const int16_t* coef, const int16_t* G, uint32_t N, uint32_t C, uint8_t* rec);
 
 }  // namespace
 
@@ -309,8 +311,16 @@ int fit_tables_host(const skv_shape& s, const void* calib_t, const void* calib_a
         return SKV_OK;
     }
 
-    const int16_t* coef = static_cast<const int16_t*>(calib_t);
-    const int16_t* G = static_cast<const int16_t*>(calib_a);
+    if (s.mode != SKV_CHECKERBOARD) return SKV_ERR_SHAPE;     // the map mode fits through fit_tables_map_host
+    fit_checkerboard(static_cast<const int16_t*>(calib_t), static_cast<const int16_t*>(calib_a), N, C, rec);
+    return SKV_OK;
+}
+
+namespace {
+
+// Checkerboard records (16 shifted tables per component) from calibration
+// coefficients and their side input, [N][C].
+void fit_checkerboard(const int16_t* coef, const int16_t* G, uint32_t N, uint32_t C, uint8_t* rec) {
     std::vector<int32_t> mu(N);
     for (uint32_t c = 0; c < C; ++c) {
         double acc = 0.0;
@@ -341,6 +351,67 @@ int fit_tables_host(const skv_shape& s, const void* calib_t, const void* calib_a
         const double pe = (double(esc) + 1.0) / (double(N) + 2.0);
         for (int f = 0; f < 16; ++f) put_record(rec + (size_t(c) * 16 + f) * kTableRecord, make_record(shifted[f], pe));
     }
+}
+
+// floor((v + 2^(s-1)) / 2^s): v / 2^s rounded half up (arithmetic shift).
+inline int64_t round_half_up(int64_t v, uint32_t s) { return s ? (v + (int64_t(1) << (s - 1))) >> s : v; }
+
+}  // namespace
+
+void nbr_map_host(const int16_t* coef, const int16_t* G, uint32_t T, uint32_t C, const skv_nbr_map& map,
+                  int16_t* Gout) {
+    const uint32_t K = map.rank, W = 2 * C;
+    std::vector<int64_t> in(W), q(K);
+    for (uint32_t t = 0; t < T; ++t) {
+        std::memcpy(Gout + size_t(t) * C, G + size_t(t) * C, size_t(C) * 2);
+        if (t % 2 == 0) continue;
+        const int16_t* l = coef + size_t(t - 1) * C;
+        const int16_t* r = t + 1 < T ? coef + size_t(t + 1) * C : l;
+        for (uint32_t i = 0; i < C; ++i) {
+            in[i] = std::min<int64_t>(l[i], 32639);
+            in[C + i] = std::min<int64_t>(r[i], 32639);
+        }
+        for (uint32_t j = 0; j < K; ++j) {
+            const int8_t* v = map.V + size_t(j) * W;
+            int64_t h = 0;
+            for (uint32_t i = 0; i < W; ++i) h += int64_t(v[i]) * in[i];
+            q[j] = std::clamp<int64_t>(round_half_up(h, map.shift_h), -128, 127);
+        }
+        for (uint32_t c = 0; c < C; ++c) {
+            const int8_t* u = map.U + size_t(c) * K;
+            int64_t m = 0;
+            for (uint32_t j = 0; j < K; ++j) m += int64_t(u[j]) * q[j];
+            const int64_t g = int64_t(G[size_t(t) * C + c]) + round_half_up(m, map.shift_m);
+            Gout[size_t(t) * C + c] = int16_t(std::clamp<int64_t>(g, -32768, 32767));
+        }
+    }
+}
+
+int fit_tables_map_host(const skv_shape& s, const int16_t* calib_coef, const int16_t* calib_G,
+                        uint32_t calib_tokens, const skv_nbr_map& map, uint8_t* blob, size_t blob_bytes) {
+    const uint32_t C = s.channels;
+    if (blob_bytes != blob_size(s) + map_section_bytes(map.rank, C)) return SKV_ERR_ARG;
+    std::memset(blob, 0, kHeaderBytes);
+    std::memcpy(blob, "SKVT", 4);
+    wr16(blob + 4, 1);
+    blob[6] = uint8_t(s.dtype);
+    blob[7] = uint8_t(s.mode);
+    wr32(blob + 8, uint32_t(table_count(s)));
+    wr32(blob + 12, s.layers);
+    wr32(blob + 16, s.kv);
+    wr32(blob + 20, C);
+    wr32(blob + 24, calib_tokens);
+    wr64(blob + 32, blob_bytes);
+    std::vector<int16_t> g2(size_t(calib_tokens) * C);
+    nbr_map_host(calib_coef, calib_G, calib_tokens, C, map, g2.data());
+    fit_checkerboard(calib_coef, g2.data(), calib_tokens, C, blob + kHeaderBytes);
+    uint8_t* m = blob + blob_size(s);
+    std::memset(m, 0, kMapHeader);
+    wr32(m, map.rank);
+    wr32(m + 4, map.shift_h);
+    wr32(m + 8, map.shift_m);
+    std::memcpy(m + kMapHeader, map.V, size_t(map.rank) * 2 * C);
+    std::memcpy(m + kMapHeader + size_t(map.rank) * 2 * C, map.U, size_t(map.rank) * C);
     return SKV_OK;
 }
 
@@ -349,7 +420,14 @@ int validate_blob(const uint8_t* b, size_t bytes) {
     skv_shape s{SKV_ABI_VERSION, b[6], b[7], rd32(b + 12), rd32(b + 16), 0, rd32(b + 20)};
     if (!shape_supported(s, false)) return SKV_ERR_TABLES;
     const uint64_t nt = table_count(s);
-    if (rd32(b + 8) != nt || rd64(b + 32) != bytes || bytes != blob_size(s)) return SKV_ERR_TABLES;
+    uint64_t want = blob_size(s);
+    if (s.mode == SKV_CHECKERBOARD_MAP) {
+        if (bytes < want + kMapHeader) return SKV_ERR_TABLES;
+        const uint8_t* m = b + want;
+        if (!map_params_ok(rd32(m), rd32(m + 4), rd32(m + 8)) || rd32(m + 12) != 0) return SKV_ERR_TABLES;
+        want += map_section_bytes(rd32(m), s.channels);
+    }
+    if (rd32(b + 8) != nt || rd64(b + 32) != bytes || bytes != want) return SKV_ERR_TABLES;
     for (uint64_t j = 0; j < nt; ++j) {
         const uint8_t* r = b + kHeaderBytes + j * kTableRecord;
         const uint32_t n = rd16(r);

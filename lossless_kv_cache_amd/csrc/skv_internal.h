@@ -29,6 +29,19 @@ constexpr uint64_t kRawBit = 1ull << 63;
 constexpr int kMaxTimedKernels = 16;
 
 inline uint32_t elem_bytes(uint32_t dtype) { return dtype == SKV_E4M3 ? 1u : 2u; }
+// Modes that code [tokens][channels] coefficients in two passes (even, odd tokens).
+__host__ __device__ inline bool is_checkerboard(uint32_t mode) {
+    return mode == SKV_CHECKERBOARD || mode == SKV_CHECKERBOARD_MAP;
+}
+// Map section of an SKV_CHECKERBOARD_MAP blob, after the records:
+// u32 rank | u32 shift_h | u32 shift_m | u32 0 | int8 V[rank][2C] | int8 U[C][rank].
+constexpr size_t kMapHeader = 16;
+inline uint64_t map_section_bytes(uint32_t rank, uint32_t channels) {
+    return kMapHeader + 3ull * rank * channels;
+}
+inline bool map_params_ok(uint32_t rank, uint32_t sh_h, uint32_t sh_m) {
+    return rank >= 16 && rank <= 256 && (rank & (rank - 1)) == 0 && sh_h <= 40 && sh_m <= 30;
+}
 
 // Exponent-conditioned mode: a value's table is chosen by its predictor's
 // exponent field (bf16 bits 14..7, e4m3 bits 6..3) as the class E - base,
@@ -53,6 +66,13 @@ uint64_t element_count(const skv_shape& s);
 // Host table fit (fp64).  Writes a complete blob (header + records).
 int fit_tables_host(const skv_shape& s, const void* calib_t, const void* calib_a, uint32_t calib_tokens,
                     uint8_t* blob, size_t blob_bytes);
+// SKV_CHECKERBOARD_MAP: the fit with the map applied to the calibration rows,
+// then the map section (blob_bytes = blob_size(s) + map_section_bytes).
+int fit_tables_map_host(const skv_shape& s, const int16_t* calib_coef, const int16_t* calib_G,
+                        uint32_t calib_tokens, const skv_nbr_map& map, uint8_t* blob, size_t blob_bytes);
+// Side input with the map applied, on the host: Gout = G on even tokens, G' on odd ones.
+void nbr_map_host(const int16_t* coef, const int16_t* G, uint32_t T, uint32_t C, const skv_nbr_map& map,
+                  int16_t* Gout);
 int validate_blob(const uint8_t* blob, size_t bytes);
 uint64_t fnv1a64(const uint8_t* p, size_t n);
 
@@ -74,11 +94,17 @@ struct DevTables {
     uint8_t* slot = nullptr;       // [n_tables][4096] slot -> symbol
     uint8_t* half = nullptr;       // checkerboard blobs: [n_tables][2048] symbol of every even slot
     uint8_t* base = nullptr;       // exponent-mode blobs: [slabs] class base
+    // decoded-neighbour-map blobs: the map (rank 0 otherwise)
+    uint32_t map_rank = 0, map_sh_h = 0, map_sh_m = 0;
+    int8_t* map_v = nullptr;       // [rank][2C]
+    int8_t* map_u = nullptr;       // [C][rank]
 };
 
 struct EncodeLaunch {
     const void* target;
     const void* aux;
+    const void* aux_odd;    // side input of the odd pass (checkerboard modes): aux, or the mapped side input
+    int16_t* map_side;      // decoded-neighbour map: [tokens][channels] workspace for the mapped side input
     uint8_t* scratch;       // [n_streams][2 * raw_bytes]: states, escapes (back of 1st half), words (back of 2nd)
     uint32_t* meta;         // [n_streams] bytes | raw<<31
     uint32_t* block_sum;    // [n_blocks]
@@ -96,6 +122,7 @@ struct DecodeLaunch {
     const uint8_t* pay;      // the container's payload
     uint64_t payload_bytes;
     const void* aux;
+    const void* aux_odd;     // side input of the odd pass (checkerboard modes): aux, or out (mapped in place)
     void* out;
     uint32_t* status;
     skv_shape shape;         // of the decoded range (aux and out layout)
@@ -109,6 +136,10 @@ void free_dev_tables(DevTables* t);
 hipError_t launch_encode(const EncodeLaunch& a, const DevTables& t, hipStream_t stream);
 hipError_t launch_decode(const DecodeLaunch& a, const DevTables& t, hipStream_t stream);
 hipError_t launch_clear_u32(uint32_t* p, uint32_t n, hipStream_t stream);
+// Decoded-neighbour map on the device: out[t] = G'[t] for every odd token t,
+// from the even rows of coef (out may be coef itself: only odd rows are written).
+hipError_t launch_nbr_map(const int16_t* coef, const int16_t* G, int16_t* out, uint32_t tokens, uint32_t channels,
+                          const DevTables& t, hipStream_t stream);
 uint64_t encode_work_bytes(uint64_t n_streams, uint32_t raw_bytes);
 
 // Fixed device workspace of skv_encode_noalloc (SKV_NOALLOC_WORK_BYTES).

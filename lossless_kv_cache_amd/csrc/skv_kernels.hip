@@ -72,7 +72,7 @@ __device__ __forceinline__ Geo geometry(const skv_shape& s) {
     g.C = s.channels;
     g.T = s.tokens;
     g.ncg = s.channels / kLanes;
-    g.ntb = (s.mode != SKV_CHECKERBOARD ? s.tokens : s.tokens / 2) / kSteps;
+    g.ntb = (!is_checkerboard(s.mode) ? s.tokens : s.tokens / 2) / kSteps;
     return g;
 }
 
@@ -227,7 +227,7 @@ __global__ __launch_bounds__(256) void encode_streams(EncodeLaunch a, DevTables 
         } else {
             const uint32_t tok = 2u * (tb * kSteps + uint32_t(k)) + slab;
             const int16_t* coef = static_cast<const int16_t*>(a.target);
-            const int16_t* G = static_cast<const int16_t*>(a.aux);
+            const int16_t* G = static_cast<const int16_t*>(slab ? a.aux_odd : a.aux);
             int32_t mu = G[size_t(tok) * g.C + ch];
             if (slab == 1) {
                 const int32_t l = coef[size_t(tok - 1) * g.C + ch];
@@ -313,7 +313,7 @@ __global__ __launch_bounds__(256) void encode_cb(EncodeLaunch a, DevTables t) {
     uint16_t* wfwd = reinterpret_cast<uint16_t*>(area + RAW);           // words, emission order
     uint16_t* efwd = reinterpret_cast<uint16_t*>(area + kStreamHead);   // escaped values, emission order
     const int16_t* coef = static_cast<const int16_t*>(a.target);
-    const int16_t* Gp = static_cast<const int16_t*>(a.aux);
+    const int16_t* Gp = static_cast<const int16_t*>(pass ? a.aux_odd : a.aux);
     const size_t C = g.C;
 
     int32_t ic[P], ig[P], il[P], ir[P];                    // stage 1: raw inputs
@@ -681,7 +681,8 @@ __global__ __launch_bounds__(256) void decode_streams(DecodeLaunch a, DevTables 
         } else {
             const uint32_t tok = 2u * (tb * kSteps + k) + slab;
             const int16_t* dec = static_cast<const int16_t*>(a.out);
-            int32_t mu = static_cast<const int16_t*>(a.aux)[oi];
+            // the odd pass's side input may be the output's odd rows (mapped in place): read before the store
+            int32_t mu = static_cast<const int16_t*>(slab ? a.aux_odd : a.aux)[oi];
             if (slab == 1) {
                 const int32_t l = dec[size_t(tok - 1) * g.C + ch];
                 const int32_t r = (tok + 1 < g.T) ? int32_t(dec[size_t(tok + 1) * g.C + ch]) : l;
@@ -759,7 +760,9 @@ __global__ __launch_bounds__(256) void decode_cb(DecodeLaunch a, DevTables t, ui
     const uint64_t e0 = index[sid], e1 = index[sid + 1];
     const uint64_t off = e0 & ~kRawBit, end = e1 & ~kRawBit;
     int16_t* out = static_cast<int16_t*>(a.out);
-    const int16_t* Gp = static_cast<const int16_t*>(a.aux);
+    // the odd pass's side input may be the output's odd rows (mapped in place): a lane reads
+    // each element's side input in an earlier pipeline stage than it stores the element
+    const int16_t* Gp = static_cast<const int16_t*>(pass ? a.aux_odd : a.aux);
     auto row_of = [&](uint32_t k) { return size_t(2u * (tb * kSteps + k) + pass) * C + ch; };
     if (end < off || end > a.payload_bytes) {
         if (lane == 0) atomicOr(a.status, 1u);
@@ -3022,6 +3025,143 @@ __global__ __launch_bounds__(1024, 1) void decode_bf16(DecodeLaunch a, DevTables
     if (bad || padv != 0) atomicOr(a.status, 1u);
 }
 
+// --------------------------------------------------------------- decoded-neighbour map
+// Side input of the odd tokens with the neighbour map applied (checkerboard
+// mode with a decoded-neighbour map; DCKV page, "How it differs": an odd
+// position is predicted from both decoded neighbours through a low-rank
+// linear map).  For each odd token t, with n its left row then its right row
+// (the last odd token repeats its left row), each value saturated to at most
+// 32639:  q = clamp(round(V n / 2^sh_h), -128, 127),
+//         out[t] = clamp16(G[t] + round(U q / 2^sh_m)),
+// rounding half up.  Both products run on the int8 matrix units
+// (v_mfma_i32_16x16x64_i8), whose 32-bit sums are exact here:
+//   1. H = N V^T for a block of 16 tokens per wavefront.  An int16 input
+//      splits into int8 halves, n = 256 hi + lo with lo in [-128, 127] and
+//      hi in [-128, 127] (this is why inputs saturate at 32639), so H =
+//      256 (N_hi V^T) + N_lo V^T, each sum at most 4096 * 2^14 < 2^31, put
+//      together in 64 bits.
+//   2. q, rounded and clamped, goes to LDS (the wavefront's 16 rows, rank
+//      padded with zeros to a multiple of 64), and Q U^T runs over 16-channel
+//      tiles, added to G and stored.
+// A lane's operand bytes are 16 consecutive k of its row (A) or column (B);
+// the product pairs the same byte positions of A and B, so any order the
+// hardware gives k within a 64-wide step sums the same terms.  Output tile:
+// lane l, element r holds row 4 (l / 16) + r, column l % 16.
+typedef int v4i __attribute__((ext_vector_type(4)));
+constexpr uint32_t kMapTok = 64;                 // odd tokens per workgroup, 16 per wavefront
+
+__device__ __forceinline__ int64_t round_half_up(int64_t v, uint32_t s) {
+    return s ? (v + (int64_t(1) << (s - 1))) >> s : v;
+}
+
+// 16 consecutive int16 of a row: vector loads when the row is 16-byte aligned
+template <bool VEC>
+__device__ __forceinline__ void load16(const int16_t* p, int32_t (&v)[16]) {
+    if (VEC) {
+        const int4 a = reinterpret_cast<const int4*>(p)[0], b = reinterpret_cast<const int4*>(p)[1];
+        const int32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            v[2 * i] = int32_t(int16_t(uint32_t(w[i]) & 0xFFFFu));
+            v[2 * i + 1] = w[i] >> 16;
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) v[i] = p[i];
+    }
+}
+
+template <uint32_t KT, bool VEC>   // KT: rank / 16
+__global__ __launch_bounds__(256) void nbr_map(const int16_t* coef, const int16_t* G, int16_t* out, uint32_t T,
+                                               uint32_t C, const int8_t* __restrict__ V, const int8_t* __restrict__ U,
+                                               uint32_t sh_h, uint32_t sh_m) {
+    constexpr uint32_t K = 16 * KT;
+    constexpr uint32_t KP = (K + 63) / 64 * 64;             // rank padded to whole 64-wide steps
+    __shared__ __align__(16) int8_t qs[kMapTok * KP];
+    const uint32_t lane = threadIdx.x & 63u, w = threadIdx.x >> 6;
+    const uint32_t g4 = lane >> 4, r16 = lane & 15u;
+    const uint32_t u0 = blockIdx.x * kMapTok + w * 16;      // first odd index of this wavefront
+    const uint32_t nodd = T / 2;
+    const uint32_t W2 = 2 * C;
+
+    // 1. H = N V^T: this lane's A row is odd token u0 + r16
+    v4i hi[KT], lo[KT];
+#pragma unroll
+    for (uint32_t j = 0; j < KT; ++j) hi[j] = lo[j] = v4i{0, 0, 0, 0};
+    {
+        const uint32_t u = min(u0 + r16, nodd - 1);           // rows past the end repeat the last (not stored)
+        const uint32_t t = 2 * u + 1;
+        const int16_t* lrow = coef + size_t(t - 1) * C;
+        const int16_t* rrow = t + 1 < T ? coef + size_t(t + 1) * C : lrow;
+        for (uint32_t kb = 0; kb < W2; kb += 64) {
+            const uint32_t kk = kb + 16 * g4;
+            int32_t v[16];
+            load16<VEC>(kk < C ? lrow + kk : rrow + (kk - C), v);
+            uint32_t ph[4], pl[4];
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+                uint32_t h4 = 0, l4 = 0;
+#pragma unroll
+                for (int b = 0; b < 4; ++b) {
+                    const int32_t x = v[4 * d + b] > 32639 ? 32639 : v[4 * d + b];
+                    const int32_t l8 = ((x + 128) & 255) - 128;
+                    const int32_t h8 = (x - l8) >> 8;
+                    l4 |= (uint32_t(l8) & 0xFFu) << (8 * b);
+                    h4 |= (uint32_t(h8) & 0xFFu) << (8 * b);
+                }
+                ph[d] = h4;
+                pl[d] = l4;
+            }
+            const v4i ah = {int(ph[0]), int(ph[1]), int(ph[2]), int(ph[3])};
+            const v4i al = {int(pl[0]), int(pl[1]), int(pl[2]), int(pl[3])};
+#pragma unroll
+            for (uint32_t j = 0; j < KT; ++j) {
+                const v4i bv = *reinterpret_cast<const v4i*>(V + size_t(j * 16 + r16) * W2 + kk);
+                hi[j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(ah, bv, hi[j], 0, 0, 0);
+                lo[j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(al, bv, lo[j], 0, 0, 0);
+            }
+        }
+    }
+    // 2. q to LDS: element r of tile j is token 4 g4 + r of the wavefront, rank column 16 j + r16
+    int8_t* qw = qs + size_t(w) * 16 * KP;
+#pragma unroll
+    for (uint32_t j = 0; j < KT; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int64_t h = int64_t(hi[j][r]) * 256 + int64_t(lo[j][r]);
+            const int64_t q0 = round_half_up(h, sh_h);
+            const int64_t q = q0 < -128 ? -128 : (q0 > 127 ? 127 : q0);
+            qw[(4 * g4 + r) * KP + j * 16 + r16] = int8_t(q);
+        }
+    if (KP > K)
+        for (uint32_t i = lane; i < 16 * (KP - K); i += 64) qw[(i / (KP - K)) * KP + K + i % (KP - K)] = 0;
+    __syncthreads();
+
+    // 3. out = G + round(Q U^T): A = the wavefront's q rows, B = U rows (channels)
+    v4i aq[KP / 64];
+#pragma unroll
+    for (uint32_t kb = 0; kb < KP / 64; ++kb)
+        aq[kb] = *reinterpret_cast<const v4i*>(qw + r16 * KP + kb * 64 + 16 * g4);
+    for (uint32_t c0 = 0; c0 < C; c0 += 16) {
+        v4i acc = {0, 0, 0, 0};
+#pragma unroll
+        for (uint32_t kb = 0; kb < KP / 64; ++kb) {
+            const uint32_t kk = kb * 64 + 16 * g4;
+            const v4i bv = kk < K ? *reinterpret_cast<const v4i*>(U + size_t(c0 + r16) * K + kk) : v4i{0, 0, 0, 0};
+            acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(aq[kb], bv, acc, 0, 0, 0);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const uint32_t u = u0 + 4 * g4 + r;
+            if (u < nodd) {
+                const size_t e = size_t(2 * u + 1) * C + c0 + r16;
+                const int32_t v = int32_t(G[e]) + int32_t(round_half_up(acc[r], sh_m));
+                out[e] = int16_t(v < -32768 ? -32768 : (v > 32767 ? 32767 : v));
+            }
+        }
+    }
+}
+
 __global__ void clear_u32(uint32_t* p, uint32_t n) {
     const uint32_t i = blockIdx.x * blockDim.x + threadIdx.x;
     if (i < n) p[i] = 0u;
@@ -3094,9 +3234,31 @@ hipError_t allow_lds(K kernel, size_t bytes) {
                                int(bytes));
 }
 
+template <uint32_t KT>
+hipError_t nbr_map_kt(const int16_t* coef, const int16_t* G, int16_t* out, uint32_t T, uint32_t C,
+                      const DevTables& t, hipStream_t st) {
+    const bool vec = reinterpret_cast<uintptr_t>(coef) % 16 == 0;
+    timed("nbr_map", st, [&](hipEvent_t e0, hipEvent_t e1) {
+        const dim3 grid(T / 2 / kMapTok), block(256);
+        if (vec)
+            hipExtLaunchKernelGGL((nbr_map<KT, true>), grid, block, 0, st, e0, e1, 0, coef, G, out, T, C, t.map_v,
+                                  t.map_u, t.map_sh_h, t.map_sh_m);
+        else
+            hipExtLaunchKernelGGL((nbr_map<KT, false>), grid, block, 0, st, e0, e1, 0, coef, G, out, T, C, t.map_v,
+                                  t.map_u, t.map_sh_h, t.map_sh_m);
+    });
+    return hipGetLastError();
+}
+
 template <uint32_t DT, uint32_t MODE>
 hipError_t encode_all(const EncodeLaunch& a, const DevTables& t, hipStream_t st) {
     const uint64_t n = a.n_streams;
+    if (MODE == SKV_CHECKERBOARD && a.shape.mode == SKV_CHECKERBOARD_MAP) {
+        // the odd pass codes against the side input mapped from the true (= decoded) even rows
+        const hipError_t e = launch_nbr_map(static_cast<const int16_t*>(a.target), static_cast<const int16_t*>(a.aux),
+                                            a.map_side, a.shape.tokens, a.shape.channels, t, st);
+        if (e != hipSuccess) return e;
+    }
     const uint32_t nb = uint32_t((n + kScanBlock - 1) / kScanBlock);
     const uint32_t eg = uint32_t((n + kStreamsPerBlock - 1) / kStreamsPerBlock);
     const size_t lb = encode_lds_bytes(t, DT);
@@ -3228,7 +3390,14 @@ hipError_t decode_all(const DecodeLaunch& a, const DevTables& t, hipStream_t st)
     const uint64_t passes = MODE == SKV_CHECKERBOARD ? 2 : 1;
     const uint64_t per = a.n_streams / passes;
     const uint32_t grid = uint32_t((per + kStreamsPerBlock - 1) / kStreamsPerBlock);
-    for (uint64_t ps = 0; ps < passes; ++ps)
+    for (uint64_t ps = 0; ps < passes; ++ps) {
+        if (ps == 1 && a.shape.mode == SKV_CHECKERBOARD_MAP) {
+            // the map of the decoded even rows, written into the output's odd rows (the odd pass's side input)
+            int16_t* o = static_cast<int16_t*>(a.out);
+            const hipError_t e = launch_nbr_map(o, static_cast<const int16_t*>(a.aux), o, a.shape.tokens,
+                                                a.shape.channels, t, st);
+            if (e != hipSuccess) return e;
+        }
         timed("decode_streams", st, [&](hipEvent_t e0, hipEvent_t e1) {
             if (MODE == SKV_CHECKERBOARD && fits)
                 hipExtLaunchKernelGGL((decode_cb<2, 8>), dim3(a.shape.channels / kLanes * ((per / (a.shape.channels / kLanes) + 7) / 8)),
@@ -3236,6 +3405,7 @@ hipError_t decode_all(const DecodeLaunch& a, const DevTables& t, hipStream_t st)
             else
                 hipExtLaunchKernelGGL((decode_streams<DT, MODE>), dim3(grid), dim3(256), 0, st, e0, e1, 0, a, t, ps * per, per);
         });
+    }
     return hipGetLastError();
 }
 
@@ -3255,7 +3425,20 @@ hipError_t build_dev_tables(const uint8_t* blob, DevTables* t, hipStream_t st) {
     if (e == hipSuccess) e = hipMalloc(&t->enc, size_t(nt) * 256 * sizeof(uint4));
     if (e == hipSuccess) e = hipMalloc(&t->fc, size_t(nt) * 256 * 4 + 16);   // + one entry read past the last row
     if (e == hipSuccess) e = hipMalloc(&t->slot, size_t(nt) * kM);
-    if (e == hipSuccess && blob[7] == SKV_CHECKERBOARD) e = hipMalloc(&t->half, size_t(nt) * (kM / 2));
+    if (e == hipSuccess && is_checkerboard(blob[7])) e = hipMalloc(&t->half, size_t(nt) * (kM / 2));
+    if (e == hipSuccess && blob[7] == SKV_CHECKERBOARD_MAP) {
+        // the map section follows the records (validated with the blob)
+        const uint8_t* m = blob + kHeaderBytes + size_t(nt) * kTableRecord;
+        const uint32_t C = rd32(blob + 20);
+        t->map_rank = rd32(m);
+        t->map_sh_h = rd32(m + 4);
+        t->map_sh_m = rd32(m + 8);
+        const size_t nv = size_t(t->map_rank) * 2 * C, nu = size_t(t->map_rank) * C;
+        e = hipMalloc(&t->map_v, nv);
+        if (e == hipSuccess) e = hipMalloc(&t->map_u, nu);
+        if (e == hipSuccess) e = hipMemcpyAsync(t->map_v, m + kMapHeader, nv, hipMemcpyHostToDevice, st);
+        if (e == hipSuccess) e = hipMemcpyAsync(t->map_u, m + kMapHeader + nv, nu, hipMemcpyHostToDevice, st);
+    }
     const size_t nbase = blob[7] == SKV_RESIDUAL_EXP ? size_t(rd32(blob + 12)) * rd32(blob + 16) : 0;
     if (e == hipSuccess && nbase) e = hipMalloc(&t->base, nbase);
     if (e == hipSuccess && nbase)
@@ -3281,11 +3464,25 @@ void free_dev_tables(DevTables* t) {
     if (t->slot) (void)hipFree(t->slot);
     if (t->half) (void)hipFree(t->half);
     if (t->base) (void)hipFree(t->base);
+    if (t->map_v) (void)hipFree(t->map_v);
+    if (t->map_u) (void)hipFree(t->map_u);
     *t = DevTables{};
 }
 
+hipError_t launch_nbr_map(const int16_t* coef, const int16_t* G, int16_t* out, uint32_t T, uint32_t C,
+                          const DevTables& t, hipStream_t st) {
+    switch (t.map_rank) {
+        case 16: return nbr_map_kt<1>(coef, G, out, T, C, t, st);
+        case 32: return nbr_map_kt<2>(coef, G, out, T, C, t, st);
+        case 64: return nbr_map_kt<4>(coef, G, out, T, C, t, st);
+        case 128: return nbr_map_kt<8>(coef, G, out, T, C, t, st);
+        case 256: return nbr_map_kt<16>(coef, G, out, T, C, t, st);
+        default: return hipErrorInvalidValue;
+    }
+}
+
 hipError_t launch_encode(const EncodeLaunch& a, const DevTables& t, hipStream_t st) {
-    if (a.shape.mode == SKV_CHECKERBOARD) return encode_all<SKV_INT16, SKV_CHECKERBOARD>(a, t, st);
+    if (is_checkerboard(a.shape.mode)) return encode_all<SKV_INT16, SKV_CHECKERBOARD>(a, t, st);
     if (a.shape.mode == SKV_RESIDUAL_EXP)
         return a.shape.dtype == SKV_E4M3 ? encode_all<SKV_E4M3, SKV_RESIDUAL_EXP>(a, t, st)
                                          : encode_all<SKV_BF16, SKV_RESIDUAL_EXP>(a, t, st);
@@ -3294,7 +3491,7 @@ hipError_t launch_encode(const EncodeLaunch& a, const DevTables& t, hipStream_t 
 }
 
 hipError_t launch_decode(const DecodeLaunch& a, const DevTables& t, hipStream_t st) {
-    if (a.shape.mode == SKV_CHECKERBOARD) return decode_all<SKV_INT16, SKV_CHECKERBOARD>(a, t, st);
+    if (is_checkerboard(a.shape.mode)) return decode_all<SKV_INT16, SKV_CHECKERBOARD>(a, t, st);
     if (a.shape.mode == SKV_RESIDUAL_EXP)
         return a.shape.dtype == SKV_E4M3 ? decode_all<SKV_E4M3, SKV_RESIDUAL_EXP>(a, t, st)
                                          : decode_all<SKV_BF16, SKV_RESIDUAL_EXP>(a, t, st);

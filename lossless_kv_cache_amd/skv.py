@@ -20,7 +20,7 @@ LIB_PATH = os.path.join(_HERE, "libskv.so")
 
 ABI_VERSION = 1
 BF16, E4M3, INT16 = 1, 2, 3
-RESIDUAL, CHECKERBOARD, RESIDUAL_EXP = 0, 1, 2
+RESIDUAL, CHECKERBOARD, RESIDUAL_EXP, CHECKERBOARD_MAP = 0, 1, 2, 3
 OK, ERR_ARG, ERR_SHAPE, ERR_CAPACITY, ERR_CORRUPT, ERR_TABLES, ERR_DEVICE, ERR_NOMEM = 0, -1, -2, -3, -4, -5, -6, -7
 
 
@@ -34,6 +34,11 @@ class Shape(ctypes.Structure):
     _fields_ = [("abi_version", ctypes.c_uint32), ("dtype", ctypes.c_uint32), ("mode", ctypes.c_uint32),
                 ("layers", ctypes.c_uint32), ("kv", ctypes.c_uint32), ("tokens", ctypes.c_uint32),
                 ("channels", ctypes.c_uint32)]
+
+
+class NbrMap(ctypes.Structure):
+    _fields_ = [("rank", ctypes.c_uint32), ("shift_h", ctypes.c_uint32), ("shift_m", ctypes.c_uint32),
+                ("V", ctypes.c_void_p), ("U", ctypes.c_void_p)]
 
 
 _lib = None
@@ -55,6 +60,8 @@ def lib():
         L.skv_strerror.argtypes = [ctypes.c_int]
         L.skv_fit_tables.restype = ctypes.c_int
         L.skv_fit_tables.argtypes = [sp, vp, vp, u32, ctypes.POINTER(vp), psz]
+        L.skv_fit_tables_map.restype = ctypes.c_int
+        L.skv_fit_tables_map.argtypes = [sp, vp, vp, u32, ctypes.POINTER(NbrMap), ctypes.POINTER(vp), psz]
         L.skv_load_tables.restype = ctypes.c_int
         L.skv_load_tables.argtypes = [vp, sz, ctypes.POINTER(vp)]
         L.skv_encode.restype = ctypes.c_int
@@ -167,6 +174,24 @@ def fit_tables(dtype: int, mode: int, layers: int, kv: int, channels: int, calib
     return Tables(out.value, nb.value)
 
 
+def fit_tables_map(channels: int, calib_coef, calib_G, calib_tokens: int, V, U, shift_h: int,
+                   shift_m: int) -> Tables:
+    """Tables of the checkerboard mode with a decoded-neighbour map (see
+    skv_fit_tables_map): V int8 [rank][2 * channels], U int8 [channels][rank]."""
+    s = make_shape(INT16, CHECKERBOARD_MAP, 1, 1, 0, channels)
+    v = np.ascontiguousarray(V, dtype=np.int8)
+    u = np.ascontiguousarray(U, dtype=np.int8)
+    if v.ndim != 2 or u.shape != (channels, v.shape[0]) or v.shape[1] != 2 * channels:
+        raise ValueError("V must be [rank][2 * channels] and U [channels][rank]")
+    m = NbrMap(v.shape[0], shift_h, shift_m, v.ctypes.data, u.ctypes.data)
+    pt, keep_t = _host_ptr(calib_coef)
+    pa, keep_a = _host_ptr(calib_G)
+    out, nb = ctypes.c_void_p(), ctypes.c_size_t()
+    _check(lib().skv_fit_tables_map(ctypes.byref(s), pt, pa, calib_tokens, ctypes.byref(m), ctypes.byref(out),
+                                    ctypes.byref(nb)), "skv_fit_tables_map")
+    return Tables(out.value, nb.value)
+
+
 def load_tables(blob: bytes) -> Tables:
     buf = ctypes.create_string_buffer(bytes(blob), len(blob))
     out = ctypes.c_void_p()
@@ -190,8 +215,12 @@ def elem_bytes(dtype: int) -> int:
     return 1 if dtype == E4M3 else 2
 
 
+def is_checkerboard(mode: int) -> bool:
+    return mode in (CHECKERBOARD, CHECKERBOARD_MAP)
+
+
 def _layout(tables: "Tables", tokens: int) -> tuple:
-    if tables.mode == CHECKERBOARD:
+    if is_checkerboard(tables.mode):
         return (tokens, tables.channels)
     return (tables.layers, tables.kv, tokens, tables.channels)
 
@@ -221,7 +250,7 @@ def _decode_buffers(aux: torch.Tensor, out: torch.Tensor, tables: "Tables", toke
     if not isinstance(aux, torch.Tensor) or aux.dim() != nd:
         raise ValueError(f"aux must be a {nd}-D device tensor in the tables' layout")
     if tokens is None:
-        tokens = aux.shape[0] if tables.mode == CHECKERBOARD else aux.shape[2]
+        tokens = aux.shape[0] if is_checkerboard(tables.mode) else aux.shape[2]
     if not isinstance(out, torch.Tensor) or out.element_size() != aux.element_size():
         raise ValueError(f"out must be a device tensor of {aux.element_size()}-byte elements")
     pa = _check_cache(aux, "aux", tables, tokens)
@@ -231,7 +260,7 @@ def _decode_buffers(aux: torch.Tensor, out: torch.Tensor, tables: "Tables", toke
 
 
 def tokens_of(tables: Tables, target: torch.Tensor) -> int:
-    if tables.mode == CHECKERBOARD:
+    if is_checkerboard(tables.mode):
         if target.dim() != 2:
             raise ValueError("checkerboard arrays are [tokens][channels]")
         return target.shape[0]
@@ -333,7 +362,7 @@ def decode_range_into(tables: Tables, container: torch.Tensor, token_begin: int,
                       out: torch.Tensor) -> torch.Tensor:
     """Decode tokens [token_begin, token_end) of every slab; aux and out hold that range only."""
     # the library's range rules first (same status), then the buffers of the range
-    if (tables.mode == CHECKERBOARD or not 0 <= token_begin < token_end or token_begin % 128 or token_end % 128):
+    if (is_checkerboard(tables.mode) or not 0 <= token_begin < token_end or token_begin % 128 or token_end % 128):
         raise SkvError(ERR_SHAPE, "skv_decode_range")
     pc = _check_container(container)
     pa, po, cap = _decode_buffers(aux, out, tables, token_end - token_begin)

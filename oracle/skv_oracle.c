@@ -484,9 +484,9 @@ uint64_t skvo_blob_bytes(const skvo_shape* s) { return SKVO_HDR + n_tables_of(s)
 static uint64_t map_bytes(uint32_t k, uint32_t C) { return SKVO_MAP_HDR + 3ull * k * C; }
 uint64_t skvo_blob_bytes_map(const skvo_shape* s, uint32_t k) { return skvo_blob_bytes(s) + map_bytes(k, s->channels); }
 
-/* Map parameters accepted in a blob: rank a multiple of 16 up to 256. */
+/* Map parameters accepted in a blob: rank a power of two from 16 to 256. */
 static int map_params_ok(uint32_t k, uint32_t sh1, uint32_t sh2) {
-    return k >= 16 && k <= 256 && k % 16 == 0 && sh1 <= 40 && sh2 <= 30;
+    return k >= 16 && k <= 256 && (k & (k - 1)) == 0 && sh1 <= 40 && sh2 <= 30;
 }
 
 /* Parse a table blob: header fields must match the shape, every table must

@@ -244,3 +244,34 @@ def test_noalloc_size_limits_on_host(skv):
     with pytest.raises(skv.SkvError) as e:
         skv.encode_noalloc_bound(tabs, 32768)
     assert e.value.status == skv.ERR_SHAPE
+
+
+@pytest.mark.parametrize("rank,channels", [(16, 64), (64, 256), (256, 32)])
+def test_fit_matches_oracle_neighbour_map(skv, orc, rank, channels):
+    """The decoded-neighbour-map fit (the library's own host map applied to
+    the calibration rows, then the checkerboard fit, then the map section)
+    equals the oracle's blob byte for byte; the plain fit refuses the mode and
+    the map fit refuses ranks that are not powers of two from 16 to 256."""
+    cfg = gen.CONFIGS[4].with_tokens(512, channels=channels)
+    V, U, sh1, sh2 = gen.dckv_map_weights(cfg, rank)
+    cc, cg = (a.numpy() for a in gen.dckv_draw(cfg, gen.CALIB, tokens=256, nbr_map=(V, U, sh1, sh2)))
+    tabs = skv.fit_tables_map(channels, cc, cg, 256, V, U, sh1, sh2)
+    shape = orc.make_shape(orc.INT16, orc.CHECKERBOARD_MAP, 1, 1, 512, channels)
+    want = orc.fit_tables_map(shape, cc, cg, 256, V, U, sh1, sh2)
+    assert tabs.bytes() == want
+    assert tabs.mode == skv.CHECKERBOARD_MAP
+    # the blob loads back (validation of the map section)
+    assert skv.load_tables(want).bytes() == want
+    with pytest.raises(skv.SkvError) as e:
+        skv.fit_tables(skv.INT16, skv.CHECKERBOARD_MAP, 1, 1, channels, cc, cg, 256)
+    assert e.value.status == skv.ERR_SHAPE
+    with pytest.raises(skv.SkvError) as e:
+        skv.fit_tables_map(channels, cc, cg, 256, np.zeros((24, 2 * channels), np.int8),
+                           np.zeros((channels, 24), np.int8), sh1, sh2)
+    assert e.value.status == skv.ERR_ARG
+    # a damaged map header is refused on load
+    bad = bytearray(want)
+    bad[64 + 514 * 16 * channels] = 48                     # rank 48
+    with pytest.raises(skv.SkvError) as e:
+        skv.load_tables(bytes(bad))
+    assert e.value.status == skv.ERR_TABLES

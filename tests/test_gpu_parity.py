@@ -137,6 +137,67 @@ def test_checkerboard_small(skv, orc):
     full_compare(skv, orc, coef, G, tabs, oshape, "checkerboard 1280x192")
 
 
+def map_case(skv, orc, T, C, rank, device="cuda"):
+    """Checkerboard data with a decoded-neighbour map of the given rank, its
+    tables (fitted by the library) and the oracle's shape."""
+    cfg = gen.CONFIGS[4].with_tokens(T, channels=C)
+    V, U, sh1, sh2 = gen.dckv_map_weights(cfg, rank)
+    coef, G = gen.dckv_draw(cfg, device=device, nbr_map=(V, U, sh1, sh2))
+    cc, cg = gen.dckv_draw(cfg, gen.CALIB, tokens=256, nbr_map=(V, U, sh1, sh2))
+    tabs = skv.fit_tables_map(C, cc.numpy(), cg.numpy(), 256, V, U, sh1, sh2)
+    oshape = orc.make_shape(orc.INT16, orc.CHECKERBOARD_MAP, 1, 1, T, C)
+    return coef, G, tabs, oshape, (V, U, sh1, sh2)
+
+
+@pytest.mark.parametrize("rank", [16, 32, 64, 128, 256])
+def test_checkerboard_map_small(skv, orc, rank):
+    """The decoded-neighbour map on the int8 matrix units (every rank the blob
+    allows): containers equal the oracle's, both decode exactly."""
+    coef, G, tabs, oshape, _ = map_case(skv, orc, 1280, 192, rank)
+    full_compare(skv, orc, coef, G, tabs, oshape, f"checkerboard map rank {rank}")
+
+
+def test_checkerboard_map_extremes_and_unaligned(skv, orc):
+    """Coefficients at the ends of int16 (the map's input saturation and both
+    halves of the int8 split at their limits), side inputs at the ends of
+    int16 (the clamp of G'), escapes; then the same through unaligned buffers
+    (the map's element-load path)."""
+    coef, G, tabs, oshape, _ = map_case(skv, orc, 768, 128, 64)
+    c, g = coef.cpu().numpy().copy(), G.cpu().numpy().copy()
+    rng = np.random.default_rng(23)
+    for v in (32767, 32640, 32639, -32768, -32767, 255, -129):
+        pos = rng.choice(c.size // 2, size=40, replace=False)
+        rows, cols = np.divmod(pos, c.shape[1])
+        c[2 * rows, cols] = v                              # even rows: the map's inputs
+    pos = rng.choice(g.size // 2, size=60, replace=False)
+    rows, cols = np.divmod(pos, g.shape[1])
+    g[2 * rows + 1, cols] = rng.choice([32767, -32768, 32700, -32700], size=60)
+    coef, G = torch.from_numpy(c).cuda(), torch.from_numpy(g).cuda()
+    want = full_compare(skv, orc, coef, G, tabs, oshape, "checkerboard map extremes")
+    cu, gu = _offset_copy(coef, 1), _offset_copy(G, 3)
+    cont = skv.encode(tabs, cu, gu)
+    torch.cuda.synchronize()
+    assert cont.cpu().numpy().tobytes() == want
+    out = _offset_copy(torch.zeros_like(coef), 1)
+    skv.decode_into(tabs, cont, gu, out)
+    assert torch.equal(out, coef)
+
+
+def test_checkerboard_map_zero_equals_checkerboard(skv, orc):
+    """U = 0 on the GPU: the map mode's index and payload equal the plain
+    checkerboard mode's for the same data."""
+    cfg = gen.CONFIGS[4].with_tokens(1024, channels=96)
+    V, U, sh1, sh2 = gen.dckv_map_weights(cfg, 32)
+    U = np.zeros_like(U)
+    coef, G = gen.dckv_draw(cfg, device="cuda")
+    cc, cg = gen.dckv_draw(cfg, gen.CALIB, tokens=256)
+    tm = skv.fit_tables_map(96, cc.numpy(), cg.numpy(), 256, V, U, sh1, sh2)
+    t1 = skv.fit_tables(skv.INT16, skv.CHECKERBOARD, 1, 1, 96, cc.numpy(), cg.numpy(), 256)
+    cm, c1 = skv.encode(tm, coef, G), skv.encode(t1, coef, G)
+    assert torch.equal(cm[64:], c1[64:])
+    assert torch.equal(skv.decode(tm, cm, G), coef)
+
+
 @pytest.mark.parametrize("kind", ["equal", "random", "maxz", "escapes"])
 def test_edge_inputs(skv, orc, kind):
     """Degenerate inputs: target == predictor; incompressible (raw
@@ -511,6 +572,21 @@ def test_full_size_checkerboard(skv, orc):
     tabs = skv.fit_tables(skv.INT16, skv.CHECKERBOARD, 1, 1, cfg.channels, cc.cpu().numpy(), cg.cpu().numpy(), 256)
     oshape = orc.make_shape(orc.INT16, orc.CHECKERBOARD, 1, 1, cfg.tokens, cfg.channels)
     big_compare(skv, orc, coef, G, tabs, oshape, "cfg4 checkerboard")
+
+
+def test_full_size_checkerboard_map(skv, orc):
+    """The DCKV coefficient workload (131072 tokens x 2048 coefficients) with a
+    rank-64 decoded-neighbour map: whole container equal to the oracle's,
+    exact round trip, smaller than the plain checkerboard container."""
+    cfg = gen.CONFIGS[4]
+    say("[parity] cfg4 with the neighbour map: generating")
+    coef, G, tabs, oshape, _ = map_case(skv, orc, cfg.tokens, cfg.channels, 64)
+    cont = big_compare(skv, orc, coef, G, tabs, oshape, "cfg4 neighbour map")
+    cc, cg = gen.dckv_draw(cfg, gen.CALIB, tokens=256, nbr_map=gen.dckv_map_weights(cfg, 64))
+    plain = skv.fit_tables(skv.INT16, skv.CHECKERBOARD, 1, 1, cfg.channels, cc.numpy(), cg.numpy(), 256)
+    c1 = skv.encode(plain, coef, G)
+    say(f"[parity] cfg4 neighbour map: {cont.numel()} B against {c1.numel()} B without the map")
+    assert cont.numel() < c1.numel()
 
 
 @pytest.mark.parametrize("cid,exp,layers,lpc", [(0, False, 5, 2), (2, True, 3, 1), (2, False, 4, 4)])

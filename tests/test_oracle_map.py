@@ -126,12 +126,12 @@ def test_map_mode_tiles_equal_container_streams(orc):
 
 def test_map_blob_checks(orc):
     """The plain fit refuses the map mode; the map fit refuses ranks the
-    blob cannot hold (not a multiple of 16, or above 256)."""
+    blob cannot hold (not a power of two from 16 to 256)."""
     cfg = gen.CONFIGS[4].with_tokens(512, channels=32)
     cc, cg = (a.numpy() for a in gen.dckv_draw(cfg, gen.CALIB, tokens=256))
     shape = orc.make_shape(orc.INT16, orc.CHECKERBOARD_MAP, 1, 1, 512, 32)
     with pytest.raises(RuntimeError):
         orc.fit_tables(shape, cc, cg, 256)
-    for k in (8, 24, 272):
+    for k in (8, 24, 48, 512):
         with pytest.raises(RuntimeError):
             orc.fit_tables_map(shape, cc, cg, 256, np.zeros((k, 64), np.int8), np.zeros((32, k), np.int8), 0, 0)
