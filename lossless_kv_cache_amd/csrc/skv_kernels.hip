@@ -3054,29 +3054,42 @@ __device__ __forceinline__ int64_t round_half_up(int64_t v, uint32_t s) {
     return s ? (v + (int64_t(1) << (s - 1))) >> s : v;
 }
 
-// 16 consecutive int16 of a row: vector loads when the row is 16-byte aligned
+typedef short s16x2 __attribute__((ext_vector_type(2)));
+
+// int8 halves of four int16 inputs (two dwords of two values, the first in
+// the low half), each saturated to at most 32639: lo is x mod 256 as a signed
+// byte, and hi = (x - lo) / 256 is byte 1 of the 16-bit x + 128 (no carry out
+// after the saturation).  Packed 16-bit min and add, then byte permutes.
+__device__ __forceinline__ void split4(uint32_t d0, uint32_t d1, uint32_t& lo, uint32_t& hi) {
+    const s16x2 cap = {32639, 32639}, half = {128, 128};
+    const s16x2 a = __builtin_elementwise_min(__builtin_bit_cast(s16x2, d0), cap);
+    const s16x2 b = __builtin_elementwise_min(__builtin_bit_cast(s16x2, d1), cap);
+    lo = __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, b), __builtin_bit_cast(uint32_t, a), 0x06040200u);
+    hi = __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, b + half), __builtin_bit_cast(uint32_t, a + half),
+                               0x07050301u);
+}
+
+// 16 consecutive int16 of a row as 8 dwords: two 16-byte loads when VEC (the
+// arrays are 16-byte aligned), else element loads
 template <bool VEC>
-__device__ __forceinline__ void load16(const int16_t* p, int32_t (&v)[16]) {
+__device__ __forceinline__ void load16(const int16_t* p, uint32_t (&d)[8]) {
     if (VEC) {
-        const int4 a = reinterpret_cast<const int4*>(p)[0], b = reinterpret_cast<const int4*>(p)[1];
-        const int32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            v[2 * i] = int32_t(int16_t(uint32_t(w[i]) & 0xFFFFu));
-            v[2 * i + 1] = w[i] >> 16;
-        }
+        const uint4 a = reinterpret_cast<const uint4*>(p)[0], b = reinterpret_cast<const uint4*>(p)[1];
+        d[0] = a.x; d[1] = a.y; d[2] = a.z; d[3] = a.w;
+        d[4] = b.x; d[5] = b.y; d[6] = b.z; d[7] = b.w;
     } else {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) v[i] = p[i];
+        for (int i = 0; i < 8; ++i) d[i] = uint32_t(uint16_t(p[2 * i])) | (uint32_t(uint16_t(p[2 * i + 1])) << 16);
     }
 }
 
-template <uint32_t KT, bool VEC>   // KT: rank / 16
-__global__ __launch_bounds__(256) void nbr_map(const int16_t* coef, const int16_t* G, int16_t* out, uint32_t T,
-                                               uint32_t C, const int8_t* __restrict__ V, const int8_t* __restrict__ U,
-                                               uint32_t sh_h, uint32_t sh_m) {
+template <uint32_t KT, bool VEC>   // KT: rank / 16; VEC: coef, G and out 16-byte aligned
+__global__ __launch_bounds__(256) void nbr_map(const int16_t* coef, const int16_t* __restrict__ G, int16_t* out,
+                                               uint32_t T, uint32_t C, const int8_t* __restrict__ V,
+                                               const int8_t* __restrict__ U, uint32_t sh_h, uint32_t sh_m) {
     constexpr uint32_t K = 16 * KT;
     constexpr uint32_t KP = (K + 63) / 64 * 64;             // rank padded to whole 64-wide steps
+    constexpr uint32_t KB = KP / 64;
     __shared__ __align__(16) int8_t qs[kMapTok * KP];
     const uint32_t lane = threadIdx.x & 63u, w = threadIdx.x >> 6;
     const uint32_t g4 = lane >> 4, r16 = lane & 15u;
@@ -3084,42 +3097,40 @@ __global__ __launch_bounds__(256) void nbr_map(const int16_t* coef, const int16_
     const uint32_t nodd = T / 2;
     const uint32_t W2 = 2 * C;
 
-    // 1. H = N V^T: this lane's A row is odd token u0 + r16
+    // 1. H = N V^T: this lane's A row is odd token u0 + r16 (inputs k < C
+    //    from its left row, k >= C from its right row; 2C is a multiple of
+    //    64 and no 16-wide piece straddles C); the next 64-wide step's inputs
+    //    are loaded while the current one multiplies
     v4i hi[KT], lo[KT];
 #pragma unroll
     for (uint32_t j = 0; j < KT; ++j) hi[j] = lo[j] = v4i{0, 0, 0, 0};
     {
-        const uint32_t u = min(u0 + r16, nodd - 1);           // rows past the end repeat the last (not stored)
+        const uint32_t u = min(u0 + r16, nodd - 1);           // (always u0 + r16: the grid covers T / 2 exactly)
         const uint32_t t = 2 * u + 1;
         const int16_t* lrow = coef + size_t(t - 1) * C;
         const int16_t* rrow = t + 1 < T ? coef + size_t(t + 1) * C : lrow;
+        auto src = [&](uint32_t kk) { return kk < C ? lrow + kk : rrow + (kk - C); };
+        uint32_t cur[8], nxt[8];
+        load16<VEC>(src(16 * g4), cur);
         for (uint32_t kb = 0; kb < W2; kb += 64) {
             const uint32_t kk = kb + 16 * g4;
-            int32_t v[16];
-            load16<VEC>(kk < C ? lrow + kk : rrow + (kk - C), v);
-            uint32_t ph[4], pl[4];
+            if (kb + 64 < W2) load16<VEC>(src(kk + 64), nxt);
+            v4i bv[KT];
 #pragma unroll
-            for (int d = 0; d < 4; ++d) {
-                uint32_t h4 = 0, l4 = 0;
+            for (uint32_t j = 0; j < KT; ++j)
+                bv[j] = *reinterpret_cast<const v4i*>(V + size_t(j * 16 + r16) * W2 + kk);
+            uint32_t pl[4], ph[4];
 #pragma unroll
-                for (int b = 0; b < 4; ++b) {
-                    const int32_t x = v[4 * d + b] > 32639 ? 32639 : v[4 * d + b];
-                    const int32_t l8 = ((x + 128) & 255) - 128;
-                    const int32_t h8 = (x - l8) >> 8;
-                    l4 |= (uint32_t(l8) & 0xFFu) << (8 * b);
-                    h4 |= (uint32_t(h8) & 0xFFu) << (8 * b);
-                }
-                ph[d] = h4;
-                pl[d] = l4;
-            }
+            for (int d = 0; d < 4; ++d) split4(cur[2 * d], cur[2 * d + 1], pl[d], ph[d]);
             const v4i ah = {int(ph[0]), int(ph[1]), int(ph[2]), int(ph[3])};
             const v4i al = {int(pl[0]), int(pl[1]), int(pl[2]), int(pl[3])};
 #pragma unroll
             for (uint32_t j = 0; j < KT; ++j) {
-                const v4i bv = *reinterpret_cast<const v4i*>(V + size_t(j * 16 + r16) * W2 + kk);
-                hi[j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(ah, bv, hi[j], 0, 0, 0);
-                lo[j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(al, bv, lo[j], 0, 0, 0);
+                hi[j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(ah, bv[j], hi[j], 0, 0, 0);
+                lo[j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(al, bv[j], lo[j], 0, 0, 0);
             }
+#pragma unroll
+            for (int i = 0; i < 8; ++i) cur[i] = nxt[i];
         }
     }
     // 2. q to LDS: element r of tile j is token 4 g4 + r of the wavefront, rank column 16 j + r16
@@ -3137,26 +3148,60 @@ __global__ __launch_bounds__(256) void nbr_map(const int16_t* coef, const int16_
         for (uint32_t i = lane; i < 16 * (KP - K); i += 64) qw[(i / (KP - K)) * KP + K + i % (KP - K)] = 0;
     __syncthreads();
 
-    // 3. out = G + round(Q U^T): A = the wavefront's q rows, B = U rows (channels)
-    v4i aq[KP / 64];
+    // 3. out = G + round(U Q^T), transposed so that a lane holds 4 consecutive
+    //    channels of one token: A = U rows (channels), B = the wavefront's q
+    //    rows (tokens); element r of a tile is channel 4 g4 + r of token r16.
+    //    Up to four 16-channel tiles per round (channels are a multiple of 32,
+    //    not always of 64), their loads issued together.
+    v4i bq[KB];
 #pragma unroll
-    for (uint32_t kb = 0; kb < KP / 64; ++kb)
-        aq[kb] = *reinterpret_cast<const v4i*>(qw + r16 * KP + kb * 64 + 16 * g4);
-    for (uint32_t c0 = 0; c0 < C; c0 += 16) {
-        v4i acc = {0, 0, 0, 0};
+    for (uint32_t kb = 0; kb < KB; ++kb)
+        bq[kb] = *reinterpret_cast<const v4i*>(qw + r16 * KP + kb * 64 + 16 * g4);
+    const uint32_t u = u0 + r16;
+    const size_t row = size_t(2 * min(u, nodd - 1) + 1) * C;
+    for (uint32_t c0 = 0; c0 < C; c0 += 64) {
+        v4i au[4][KB];
+        uint2 gv[4];
+        const uint32_t ntile = min(4u, (C - c0) / 16);       // 2 or 4
 #pragma unroll
-        for (uint32_t kb = 0; kb < KP / 64; ++kb) {
-            const uint32_t kk = kb * 64 + 16 * g4;
-            const v4i bv = kk < K ? *reinterpret_cast<const v4i*>(U + size_t(c0 + r16) * K + kk) : v4i{0, 0, 0, 0};
-            acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(aq[kb], bv, acc, 0, 0, 0);
+        for (uint32_t tt = 0; tt < 4; ++tt) {
+            if (tt >= ntile) break;
+            const uint32_t c = c0 + 16 * tt;
+#pragma unroll
+            for (uint32_t kb = 0; kb < KB; ++kb) {
+                const uint32_t kk = kb * 64 + 16 * g4;
+                au[tt][kb] = kk < K ? *reinterpret_cast<const v4i*>(U + size_t(c + r16) * K + kk) : v4i{0, 0, 0, 0};
+            }
+            const int16_t* gp = G + row + c + 4 * g4;
+            if (VEC) {
+                gv[tt] = *reinterpret_cast<const uint2*>(gp);
+            } else {
+                gv[tt].x = uint32_t(uint16_t(gp[0])) | (uint32_t(uint16_t(gp[1])) << 16);
+                gv[tt].y = uint32_t(uint16_t(gp[2])) | (uint32_t(uint16_t(gp[3])) << 16);
+            }
         }
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const uint32_t u = u0 + 4 * g4 + r;
+        for (uint32_t tt = 0; tt < 4; ++tt) {
+            if (tt >= ntile) break;
+            v4i acc = {0, 0, 0, 0};
+#pragma unroll
+            for (uint32_t kb = 0; kb < KB; ++kb) acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(au[tt][kb], bq[kb], acc, 0, 0, 0);
+            const int32_t gq[4] = {int32_t(int16_t(gv[tt].x & 0xFFFFu)), int32_t(gv[tt].x) >> 16,
+                                   int32_t(int16_t(gv[tt].y & 0xFFFFu)), int32_t(gv[tt].y) >> 16};
+            uint32_t o[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int32_t v = gq[r] + int32_t(round_half_up(acc[r], sh_m));
+                o[r] = uint32_t(uint16_t(int16_t(v < -32768 ? -32768 : (v > 32767 ? 32767 : v))));
+            }
             if (u < nodd) {
-                const size_t e = size_t(2 * u + 1) * C + c0 + r16;
-                const int32_t v = int32_t(G[e]) + int32_t(round_half_up(acc[r], sh_m));
-                out[e] = int16_t(v < -32768 ? -32768 : (v > 32767 ? 32767 : v));
+                int16_t* op = out + row + c0 + 16 * tt + 4 * g4;
+                if (VEC) {
+                    *reinterpret_cast<uint2*>(op) = uint2{o[0] | (o[1] << 16), o[2] | (o[3] << 16)};
+                } else {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) op[r] = int16_t(uint16_t(o[r]));
+                }
             }
         }
     }
@@ -3237,7 +3282,8 @@ hipError_t allow_lds(K kernel, size_t bytes) {
 template <uint32_t KT>
 hipError_t nbr_map_kt(const int16_t* coef, const int16_t* G, int16_t* out, uint32_t T, uint32_t C,
                       const DevTables& t, hipStream_t st) {
-    const bool vec = reinterpret_cast<uintptr_t>(coef) % 16 == 0;
+    const bool vec = (reinterpret_cast<uintptr_t>(coef) | reinterpret_cast<uintptr_t>(G) |
+                      reinterpret_cast<uintptr_t>(out)) % 16 == 0;
     timed("nbr_map", st, [&](hipEvent_t e0, hipEvent_t e1) {
         const dim3 grid(T / 2 / kMapTok), block(256);
         if (vec)
