@@ -3387,12 +3387,14 @@ hipError_t encode_all(const EncodeLaunch& a, const DevTables& t, hipStream_t st)
 template <uint32_t DT, uint32_t MODE>
 hipError_t decode_all(const DecodeLaunch& a, const DevTables& t, hipStream_t st) {
     const bool fits = slab_fits(a.shape);
-    if (DT == SKV_E4M3 && MODE == SKV_RESIDUAL && fits && t.max_n + 1 <= 64 &&
-        dec_e4m3_lds(64) <= kLdsLimit) {
+    // rows by residual byte: FS rows hold every symbol of tables with fewer than FS direct symbols
+    // (FS = 128: 156 KB of LDS); wider tables take the per-table LDS decoder
+    static_assert(dec_e4m3_lds(128) <= kLdsLimit, "128-row tables fit in LDS");
+    if (DT == SKV_E4M3 && MODE == SKV_RESIDUAL && fits && t.max_n + 1 <= 128) {
         const LdsGeo lg = lds_geometry(a.shape);
-        const bool small = t.max_n + 1 <= 32;
-        auto k = small ? decode_e4m3<32> : decode_e4m3<64>;
-        const size_t lb = small ? dec_e4m3_lds(32) : dec_e4m3_lds(64);
+        const uint32_t fs = t.max_n + 1 <= 32 ? 32u : (t.max_n + 1 <= 64 ? 64u : 128u);
+        auto k = fs == 32 ? decode_e4m3<32> : (fs == 64 ? decode_e4m3<64> : decode_e4m3<128>);
+        const size_t lb = dec_e4m3_lds(fs);
         hipError_t e = allow_lds(k, lb);
         if (e != hipSuccess) return e;
         timed("decode_streams", st, [&](hipEvent_t e0, hipEvent_t e1) {

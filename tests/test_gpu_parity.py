@@ -244,6 +244,34 @@ def test_edge_inputs_e4m3(skv, orc, kind, channels):
     full_compare(skv, orc, t, p, tabs, oshape, f"edge e4m3 {kind} {channels}")
 
 
+def _ordered_noise(x: torch.Tensor, noise: float, seed: int) -> torch.Tensor:
+    """e4m3 codes moved by N(0, noise^2) steps in value order (clamped at the
+    ends), so residuals stay near the noise without sign-crossing jumps."""
+    g = torch.Generator(device=x.device)
+    g.manual_seed(seed)
+    u = x.to(torch.int32)
+    o = torch.where(u < 128, u ^ 0x80, u ^ 0xFF)
+    o = (o + (torch.randn(x.shape, generator=g, device=x.device) * noise).round().to(torch.int32)).clamp(0, 255)
+    return torch.where(o >= 128, o ^ 0x80, o ^ 0xFF).to(torch.uint8)
+
+
+@pytest.mark.parametrize("noise,lo,hi", [(10, 64, 127), (24, 128, 255)])
+def test_e4m3_wide_tables(skv, orc, noise, lo, hi):
+    """Predictors noisier than the workload's widen the tables: 64 to 127
+    direct symbols take the tiled e4m3 decoder with 128-row tables, 128 or
+    more the per-table LDS decoder.  Containers equal the oracle's."""
+    cfg = gen.Config(98, "wide-e4m3", "e4m3", 2, 2, 640, 128)
+    t, _ = gen.residual_array(cfg, device="cuda")
+    ct, _ = gen.residual_array(cfg, gen.CALIB, tokens=256)
+    p, cp = _ordered_noise(t, noise, 1), _ordered_noise(ct, noise, 2)
+    tabs = skv.fit_tables(skv.E4M3, skv.RESIDUAL, 2, 2, 128, ct.numpy(), cp.numpy(), 256)
+    blob = tabs.bytes()
+    ns = [int.from_bytes(blob[64 + 514 * j:66 + 514 * j], "little") for j in range(2 * 2 * 128)]
+    assert lo <= max(ns) <= hi, (min(ns), max(ns))
+    oshape = orc.make_shape(orc.E4M3, orc.RESIDUAL, 2, 2, 640, 128)
+    full_compare(skv, orc, t, p, tabs, oshape, f"e4m3 tables up to {max(ns)} symbols")
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "e4m3"])
 def test_word_bursts_after_escapes(skv, orc, dtype):
     """Every token block escapes in its first 4 steps and codes rare direct
