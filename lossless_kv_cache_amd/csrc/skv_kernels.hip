@@ -1847,9 +1847,19 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8))) void 
 // Emitted words go to a 128-word LDS ring per stream that stores each
 // completed 64-word chunk at once; escaped values (16 bits) are stored per
 // tile.  The tables of 256 symbols take 128 KB, so one workgroup runs per CU.
+// EXP (exponent-class tables): the slab's 16 class tables in LDS, [class]
+// [fs + 1] entries (an odd count, so the same symbol of different classes
+// falls in different banks; entries past a table's n repeat its flagged
+// escape entry), and 32-bit tile entries z | class << 16, the class formed
+// from the predictor with packed 16-bit arithmetic.
 constexpr uint32_t kBfTileLds = 2 * kTileSteps * kLanes * 2;            // symbols of both halves
 constexpr uint32_t kBfEncWaveLds = kBfTileLds + 2 * kPairRing * 2;
 __host__ __device__ constexpr uint32_t encode_bf16_lds(uint32_t fs) { return kLanes * fs * 16 + 16 * kBfEncWaveLds; }
+constexpr uint32_t kBfTileLdsExp = 2 * kTileSteps * kLanes * 4;         // 32-bit entries of both halves
+constexpr uint32_t kBfEncWaveLdsExp = kBfTileLdsExp + 2 * kPairRing * 2;
+__host__ __device__ constexpr uint32_t encode_bf16_exp_lds(uint32_t fs) {
+    return kExpClasses * (fs + 1) * 16 + 16 + 16 * kBfEncWaveLdsExp;
+}
 
 // v ^ 0x7FFF in each 16-bit half whose sign bit is set (the order-preserving
 // code of a bf16 pattern is this flip ^ 0x8000); v_perm selectors 8 and 9
@@ -1869,7 +1879,16 @@ __device__ __forceinline__ uint32_t sym16x2(uint32_t t, uint32_t p) {
     const us2 d = __builtin_bit_cast(us2, sflip16x2(t)) - __builtin_bit_cast(us2, sflip16x2(p));
     return zig16x2(__builtin_bit_cast(uint32_t, d));
 }
+// exponent classes of two bf16 predictors: min(max(E - base, 0), 15) per 16-bit half, E the
+// exponent field (bits 14..7); base2 = base in both halves
+__device__ __forceinline__ uint32_t cls16x2(uint32_t p, uint32_t base2) {
+    typedef unsigned short us2 __attribute__((ext_vector_type(2)));
+    const us2 e = __builtin_bit_cast(us2, (p >> 7) & 0x00FF00FFu);
+    const us2 c = __builtin_elementwise_sub_sat(e, __builtin_bit_cast(us2, base2));
+    return __builtin_bit_cast(uint32_t, __builtin_elementwise_min(c, us2{15, 15}));
+}
 
+template <bool EXP>
 __global__ __launch_bounds__(1024) void encode_bf16(EncodeLaunch a, DevTables t, uint32_t fs, LdsGeo lg) {
     constexpr uint32_t RAW = 2 * kSyms;
     constexpr uint32_t MAXE = (RAW - kStreamHead) / 2;
@@ -1879,11 +1898,22 @@ __global__ __launch_bounds__(1024) void encode_bf16(EncodeLaunch a, DevTables t,
     const Geo geo = geometry(a.shape);
     const LdsPos ps = lds_position(geo, lg);
     if (!ps.valid) return;
-    const uint32_t tab0 = ps.slab * geo.C + ps.cg * kLanes;
-    uint4* lenc = reinterpret_cast<uint4*>(lds);                            // [fs symbols][32 lanes]
-    for (uint32_t i = threadIdx.x; i < kLanes * fs; i += blockDim.x) {
-        const uint32_t sym = i / kLanes, j = i % kLanes;
-        lenc[i] = t.enc[size_t(tab0 + j) * 256 + sym];
+    const uint32_t tab0 = EXP ? ps.slab * kExpClasses : ps.slab * geo.C + ps.cg * kLanes;
+    // tables: [fs symbols][32 lanes], or (EXP) [16 classes][fs + 1] then n of each class
+    const uint32_t cstride = fs + 1;
+    uint4* lenc = reinterpret_cast<uint4*>(lds);
+    uint8_t* nq = lds + size_t(kExpClasses) * cstride * 16;
+    if constexpr (EXP) {
+        for (uint32_t i = threadIdx.x; i < kExpClasses * cstride; i += blockDim.x) {
+            const uint32_t q = i / cstride, sym = i % cstride;
+            lenc[i] = t.enc[size_t(tab0 + q) * 256 + min(sym, 255u)];
+        }
+        if (threadIdx.x < kExpClasses) nq[threadIdx.x] = uint8_t(t.n[tab0 + threadIdx.x]);
+    } else {
+        for (uint32_t i = threadIdx.x; i < kLanes * fs; i += blockDim.x) {
+            const uint32_t sym = i / kLanes, j = i % kLanes;
+            lenc[i] = t.enc[size_t(tab0 + j) * 256 + sym];
+        }
     }
     __syncthreads();
 
@@ -1892,14 +1922,17 @@ __global__ __launch_bounds__(1024) void encode_bf16(EncodeLaunch a, DevTables t,
     const bool upper = (threadIdx.x & 32u) != 0;
     const uint32_t fsh = upper ? 16u : 0u;
     const uint32_t lane = 31u - hl;                        // format lane (reversed within the half)
-    const uint32_t n = t.n[tab0 + lane];
-    uint8_t* tile = lds + size_t(kLanes) * fs * 16 + wave * kBfEncWaveLds;
-    uint8_t* ring = tile + kBfTileLds;
-    // tile: [half][step][32 channels] u16; this lane loads 8 channels of one step and reads its channel back
+    const uint32_t n = EXP ? 0u : t.n[tab0 + lane];
+    constexpr uint32_t TE = EXP ? 4 : 2;                   // bytes of a tile entry
+    constexpr uint32_t WLDS = EXP ? kBfEncWaveLdsExp : kBfEncWaveLds;
+    uint8_t* tile = lds + (EXP ? size_t(kExpClasses) * cstride * 16 + 16 : size_t(kLanes) * fs * 16) + wave * WLDS;
+    uint8_t* ring = tile + 2 * kTileSteps * kLanes * TE;
+    // tile: [half][step][32 channels] entries; this lane loads 8 channels of one step and reads its channel back
     const uint32_t ld_row = hl >> 2, ld_q = hl & 3u;
-    constexpr uint32_t kHalfTile = kTileSteps * kLanes * 2;
-    uint4* tile_st = reinterpret_cast<uint4*>(tile + (upper ? kHalfTile : 0u) + ld_row * kLanes * 2 + ld_q * 16);
-    const uint16_t* tile_rd = reinterpret_cast<const uint16_t*>(tile + (upper ? kHalfTile : 0u)) + lane;
+    constexpr uint32_t kHalfTile = kTileSteps * kLanes * TE;
+    uint4* tile_st = reinterpret_cast<uint4*>(tile + (upper ? kHalfTile : 0u) + ld_row * kLanes * TE + ld_q * 8 * TE);
+    const uint8_t* tile_rd = tile + (upper ? kHalfTile : 0u) + lane * TE;
+    const uint32_t base2 = EXP ? uint32_t(t.base[ps.slab]) * 0x00010001u : 0u;
     uint16_t* ring_h = reinterpret_cast<uint16_t*>(ring + (upper ? kPairRing * 2 : 0u));
     const uint32_t* ring32 = reinterpret_cast<const uint32_t*>(ring_h);
 
@@ -1914,12 +1947,34 @@ __global__ __launch_bounds__(1024) void encode_bf16(EncodeLaunch a, DevTables t,
         wgs, (short)0, int((ps.tb_end - ps.tb_begin - 1) * sstride + 2 * RAW), 0x00020000);
 
     // symbols of one tile: 8 per lane into LDS, then each lane's channel for the tile's 8 steps
+    // (EXP: entries z | class << 16)
     auto stage = [&](uint4 tv, uint4 pv, uint32_t* z) {
-        *tile_st = make_uint4(sym16x2(tv.x, pv.x), sym16x2(tv.y, pv.y), sym16x2(tv.z, pv.z), sym16x2(tv.w, pv.w));
+        const uint4 zz = make_uint4(sym16x2(tv.x, pv.x), sym16x2(tv.y, pv.y), sym16x2(tv.z, pv.z), sym16x2(tv.w, pv.w));
+        if constexpr (EXP) {
+            const uint4 cc = make_uint4(cls16x2(pv.x, base2), cls16x2(pv.y, base2), cls16x2(pv.z, base2),
+                                        cls16x2(pv.w, base2));
+            tile_st[0] = make_uint4(__builtin_amdgcn_perm(cc.x, zz.x, 0x05040100u),
+                                    __builtin_amdgcn_perm(cc.x, zz.x, 0x07060302u),
+                                    __builtin_amdgcn_perm(cc.y, zz.y, 0x05040100u),
+                                    __builtin_amdgcn_perm(cc.y, zz.y, 0x07060302u));
+            tile_st[1] = make_uint4(__builtin_amdgcn_perm(cc.z, zz.z, 0x05040100u),
+                                    __builtin_amdgcn_perm(cc.z, zz.z, 0x07060302u),
+                                    __builtin_amdgcn_perm(cc.w, zz.w, 0x05040100u),
+                                    __builtin_amdgcn_perm(cc.w, zz.w, 0x07060302u));
+        } else {
+            *tile_st = zz;
+        }
         __builtin_amdgcn_wave_barrier();
 #pragma unroll
-        for (uint32_t r = 0; r < kTileSteps; ++r) z[r] = tile_rd[r * kLanes];
+        for (uint32_t r = 0; r < kTileSteps; ++r)
+            z[r] = EXP ? *reinterpret_cast<const uint32_t*>(tile_rd + r * kLanes * TE)
+                       : *reinterpret_cast<const uint16_t*>(tile_rd + r * kLanes * TE);
         __builtin_amdgcn_wave_barrier();
+    };
+    // table entry of a position (EXP: the class table's, symbols past its n reading its escape entry)
+    auto entry = [&](uint32_t zv) -> uint4 {
+        if constexpr (EXP) return lenc[(zv >> 16) * cstride + min(zv & 0xFFFFu, fs - 1)];
+        return lenc[min(zv, n) * kLanes + lane];
     };
 
     for (uint32_t r0 = ps.tb_begin + 2 * wave; r0 < ps.tb_end; r0 += 2 * nwave) {
@@ -1944,8 +1999,9 @@ __global__ __launch_bounds__(1024) void encode_bf16(EncodeLaunch a, DevTables t,
         uint32_t x = kStateLow;
         uint32_t wp = 0;                                   // word counts: lower half | upper half << 16
         uint32_t elo = 0, ehi = 0;                         // escape counts per half
-        uint4 ec = lenc[min(zc[kTileSteps - 1], n) * kLanes + lane];
+        uint4 ec = entry(zc[kTileSteps - 1]);
         for (int j = kTiles - 1; j >= 0; --j) {
+            uint32_t escf = 0;                             // EXP: the tile's entry flags (bit 8: escape)
             if (j > 0) {
                 stage(tv, pv, zn);
                 if (j > 1) {
@@ -1957,7 +2013,8 @@ __global__ __launch_bounds__(1024) void encode_bf16(EncodeLaunch a, DevTables t,
             for (int r = kTileSteps - 1; r >= 0; --r) {
                 const uint4 e = ec;
                 const uint32_t znext = r > 0 ? zc[r - 1] : zn[kTileSteps - 1];
-                ec = lenc[min(znext, n) * kLanes + lane];
+                ec = entry(znext);
+                if constexpr (EXP) escf |= e.w;
                 // words leave before the state absorbs the symbol (an idle half runs a copy of its
                 // partner's stream into its own ring and stores nothing)
                 uint32_t xs = x;
@@ -1991,21 +2048,27 @@ __global__ __launch_bounds__(1024) void encode_bf16(EncodeLaunch a, DevTables t,
                 wp += pp;
             }
             // escaped values of this tile, in emission order (rare: skipped by the whole wavefront)
-            uint32_t zm = zc[0];
+            bool any;
+            if constexpr (EXP) {
+                any = (escf & 0x100u) != 0;
+            } else {
+                uint32_t zm = zc[0];
 #pragma unroll
-            for (uint32_t r = 1; r < kTileSteps; ++r) zm = max(zm, zc[r]);
-            if (__ballot(zm >= n) != 0) {
+                for (uint32_t r = 1; r < kTileSteps; ++r) zm = max(zm, zc[r]);
+                any = zm >= n;
+            }
+            if (__ballot(any) != 0) {
 #pragma unroll
                 for (int r = kTileSteps - 1; r >= 0; --r) {
-                    const bool esc = zc[r] >= n;
+                    const bool esc = EXP ? (zc[r] & 0xFFFFu) >= nq[zc[r] >> 16] : zc[r] >= n;
                     const uint64_t me = __ballot(esc);
                     if (me == 0) continue;
                     const uint32_t mlo = uint32_t(me), mhi = uint32_t(me >> 32), plo = __popc(mlo);
                     const uint32_t pk = min(elo, MAXE) | ((min(ehi, MAXE) + 32u - plo) << 16);
                     const uint32_t slot = __builtin_amdgcn_mbcnt_hi(
                         mhi, __builtin_amdgcn_mbcnt_lo(mlo, __builtin_amdgcn_ubfe(pk, fsh, 16)));
-                    __builtin_amdgcn_raw_buffer_store_b16(uint16_t(zc[r]), wrs, act && esc ? ebase + 2 * slot : kDrop,
-                                                          0, 0);
+                    __builtin_amdgcn_raw_buffer_store_b16(uint16_t(zc[r] & 0xFFFFu), wrs,
+                                                          act && esc ? ebase + 2 * slot : kDrop, 0, 0);
                     elo += plo;
                     ehi += __popc(mhi);
                 }
@@ -2626,6 +2689,15 @@ __host__ __device__ constexpr uint32_t dec_bf16_rings() { return (kLanes * (kM /
 __host__ __device__ constexpr uint32_t dec_bf16_lds() {
     return dec_bf16_rings() + kDecStreams * (2 * kBfRing + kDecTile * kLanes);
 }
+// Exponent-class tables: half maps [16 classes][2048] | rows [16 classes][257] u32 | rings | tiles |
+// class tiles [streams][32 channels][4 steps] | n [16]
+constexpr uint32_t kBfExpRowStride = kBf16Rows * 4;     // 1028 bytes: a class's rows start one bank further
+__host__ __device__ constexpr uint32_t dec_bf16_exp_rings() {
+    return (kExpClasses * (kM / 2) + kExpClasses * kBfExpRowStride + 511) & ~511u;
+}
+__host__ __device__ constexpr uint32_t dec_bf16_exp_lds() {
+    return dec_bf16_exp_rings() + kDecStreams * (2 * kBfRing + 2 * kDecTile * kLanes) + kExpClasses;
+}
 
 __device__ __forceinline__ uint2 ld8(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t soff) {
     typedef uint32_t v2u __attribute__((ext_vector_type(2)));
@@ -2647,27 +2719,42 @@ __device__ __forceinline__ uint32_t recon16x2(uint32_t p, uint32_t z) {
 }
 
 // The steps of one tile (see dec_tile_steps); the map lookup reads the rows of
-// the even slot's symbol and of the next symbol.
-template <bool GLOBAL, class Pre, class Post>
+// the even slot's symbol and of the next symbol.  EXP: a step's class (from
+// the class word, class << 4 per step byte) picks the half map and the rows.
+template <bool GLOBAL, bool EXP = false, class Pre, class Post>
 __device__ __forceinline__ void dec_tile_steps_bf16(DecState (&st)[kDecChains], const DecLane& L,
                                                     const DecChain (&ch)[kDecChains],
-                                                    uint32_t (&sy)[kDecChains][kDecTile], Pre&& pre, Post&& post) {
+                                                    uint32_t (&sy)[kDecChains][kDecTile], Pre&& pre, Post&& post,
+                                                    const uint32_t (&cw)[kDecChains] = {}) {
 #pragma unroll
     for (uint32_t r = 0; r < kDecTile; ++r) {
         uint32_t s0[kDecChains], e0[kDecChains], e1[kDecChains], xn[kDecChains], idx[kDecChains], w[kDecChains];
+        uint32_t mb[kDecChains], rb[kDecChains];
         uint64_t mw[kDecChains];
+#pragma unroll
+        for (uint32_t c = 0; c < kDecChains; ++c) {
+            if constexpr (EXP) {
+                const uint32_t q = __builtin_amdgcn_ubfe(cw[c], 8 * r + 4, 4);
+                mb[c] = (q << 11) + L.mapb;
+                rb[c] = q * kBfExpRowStride + L.gb;
+            } else {
+                mb[c] = L.mapb;
+                rb[c] = L.gb;
+            }
+        }
         if (r == 0) pre();
 #pragma unroll
         for (uint32_t c = 0; c < kDecChains; ++c)
-            s0[c] = *reinterpret_cast<const lds_u8*>(__builtin_amdgcn_ubfe(st[c].x, 1, 11) | L.mapb);
+            s0[c] = *reinterpret_cast<const lds_u8*>(__builtin_amdgcn_ubfe(st[c].x, 1, 11) | mb[c]);
         if (r == 0) post();
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (uint32_t c = 0; c < kDecChains; ++c) {
             asm("" : "+v"(s0[c]));
-            const uint32_t ra = (s0[c] << 7) + L.gb;
+            // rows: [symbol][32 lanes] per lane, or [class][257 symbols] shared
+            const uint32_t ra = EXP ? (s0[c] << 2) + rb[c] : (s0[c] << 7) + rb[c];
             e0[c] = *reinterpret_cast<const lds_u32*>(ra);
-            e1[c] = *reinterpret_cast<const lds_u32*>(ra + kLanes * 4);
+            e1[c] = *reinterpret_cast<const lds_u32*>(ra + (EXP ? 4u : kLanes * 4));
         }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -2697,10 +2784,14 @@ __device__ __forceinline__ void dec_tile_steps_bf16(DecState (&st)[kDecChains], 
     }
 }
 
+template <bool EXP>
 __global__ __launch_bounds__(1024, 1) void decode_bf16(DecodeLaunch a, DevTables t, LdsGeo lg) {
-    constexpr uint32_t OFF_G = kLanes * (kM / 2);
-    constexpr uint32_t OFF_R = dec_bf16_rings();
+    constexpr uint32_t NT = EXP ? kExpClasses : kLanes;           // tables held
+    constexpr uint32_t OFF_G = NT * (kM / 2);
+    constexpr uint32_t OFF_R = EXP ? dec_bf16_exp_rings() : dec_bf16_rings();
     constexpr uint32_t OFF_T = OFF_R + kDecStreams * 2 * kBfRing;
+    constexpr uint32_t OFF_K = OFF_T + kDecStreams * kDecTile * kLanes;     // class tiles (EXP)
+    constexpr uint32_t OFF_N = OFF_K + kDecStreams * kDecTile * kLanes;     // n of each class (EXP)
     constexpr uint32_t kTiles = kSteps / kDecTile;
     extern __shared__ __align__(16) uint8_t lds[];
     const uint32_t lb = uint32_t(uintptr_t(lds));                  // LDS offset of the dynamic block
@@ -2708,21 +2799,23 @@ __global__ __launch_bounds__(1024, 1) void decode_bf16(DecodeLaunch a, DevTables
     const LdsPos ps = lds_position(geo, lg);
     if (!ps.valid) return;
     const uint32_t tid = threadIdx.x;
-    const uint32_t tab0 = ps.slab * geo.C + ps.cg * kLanes;
+    const uint32_t tab0 = EXP ? ps.slab * kExpClasses : ps.slab * geo.C + ps.cg * kLanes;
     // rows by symbol: (4096 - f) | start << 16; symbols past n and the sentinel row 256 start at 4096
-    uint32_t* lrow = reinterpret_cast<uint32_t*>(lds + OFF_G);           // [257 rows][32 lanes]
-    for (uint32_t i = tid; i < kBf16Rows * kLanes; i += blockDim.x) {
-        const uint32_t row = i / kLanes;
-        const uint32_t fc = row < 256 ? t.fc[size_t(tab0 + i % kLanes) * 256 + row] : (kM << 16);
+    uint32_t* lrow = reinterpret_cast<uint32_t*>(lds + OFF_G);           // [257 rows][32 lanes] or [16][257]
+    for (uint32_t i = tid; i < kBf16Rows * NT; i += blockDim.x) {
+        const uint32_t row = EXP ? i % kBf16Rows : i / kLanes, tq = EXP ? i / kBf16Rows : i % kLanes;
+        const uint32_t fc = row < 256 ? t.fc[size_t(tab0 + tq) * 256 + row] : (kM << 16);
         lrow[i] = (kM - (fc & 0xFFFFu)) | (fc & 0xFFFF0000u);
     }
+    if (EXP && tid < kExpClasses) lds[OFF_N + tid] = uint8_t(min(t.n[tab0 + tid], 255u));
     {
         // half maps: the symbol of every even slot (the odd slot belongs to the same symbol or
-        // to the next one, which then starts there), from the group's contiguous slot maps
+        // to the next one, which then starts there), from the group's (or the slab's class
+        // tables') contiguous slot maps
         const uint4* src = reinterpret_cast<const uint4*>(t.slot + size_t(tab0) * kM);
         uint2* dst = reinterpret_cast<uint2*>(lds);
 #pragma unroll
-        for (uint32_t q = 0; q < kLanes * kM / 16 / 1024; ++q) {
+        for (uint32_t q = 0; q < NT * kM / 16 / 1024; ++q) {
             const uint4 v = src[q * 1024 + tid];
             dst[q * 1024 + tid] = make_uint2(__builtin_amdgcn_perm(v.y, v.x, 0x06040200u),
                                              __builtin_amdgcn_perm(v.w, v.z, 0x06040200u));
@@ -2746,16 +2839,20 @@ __global__ __launch_bounds__(1024, 1) void decode_bf16(DecodeLaunch a, DevTables
         return;
     }
     DecLane L;
-    L.mapb = lb + hl * (kM / 2);
-    L.gb = lb + OFF_G + hl * 4;                                     // row of symbol z at z * 128 + gb
+    L.mapb = EXP ? lb : lb + hl * (kM / 2);                        // EXP: class q's half map at q * 2048
+    L.gb = EXP ? lb + OFF_G : lb + OFF_G + hl * 4;                  // row z at z * 128 + gb (EXP: q * 1028 + z * 4)
     L.fsh = upper ? 16u : 0u;
     L.lowm = upper ? 0u : 0xFFFFFFFFu;
     // every payload read of the workgroup goes through one range-checked resource
     L.rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(pay + wlo), (short)0, int(whi - wlo), 0x00020000);
-    // tile-domain bytes: n (the escape symbol) of the lane's 4 channels
+    // tile-domain bytes: n (the escape symbol) of the lane's 4 channels (EXP: by each position's
+    // class, formed per tile from its predictors)
     uint32_t np = 0;
+    if constexpr (!EXP) {
 #pragma unroll
-    for (uint32_t k = 0; k < 4; ++k) np |= min(t.n[tab0 + q4 + k], 255u) << (8 * k);
+        for (uint32_t k = 0; k < 4; ++k) np |= min(t.n[tab0 + q4 + k], 255u) << (8 * k);
+    }
+    const uint32_t base2 = EXP ? uint32_t(t.base[ps.slab]) * 0x00010001u : 0u;
     // predictor and output rows of the slab's channel group, 32-bit offsets from one base each
     const size_t slab_b = size_t(ps.slab) * geo.T * rowb + size_t(ps.cg) * kLanes * 2;
     const __amdgpu_buffer_rsrc_t prs = __builtin_amdgcn_make_buffer_rsrc(
@@ -2793,6 +2890,7 @@ __global__ __launch_bounds__(1024, 1) void decode_bf16(DecodeLaunch a, DevTables
         // wrk = last chunk written to the ring, live = 0x8000 in the field of a half with
         // a coded stream
         uint32_t ldk[kDecChains], wrk[kDecChains], live[kDecChains];
+        uint32_t ktb[kDecChains], cls[kDecChains];                 // class tile base, class word (EXP)
         bool coded[kDecChains], raw[kDecChains];
         uint64_t e0[kDecChains], e1[kDecChains];
         uint32_t x0[kDecChains], c0[kDecChains], c1[kDecChains];
@@ -2824,6 +2922,7 @@ __global__ __launch_bounds__(1024, 1) void decode_bf16(DecodeLaunch a, DevTables
             const uint32_t hs = (tid >> 5) * kDecChains + c;          // stream slot in the workgroup
             ch[c].ringb = lb + OFF_R + hs * 2 * kBfRing;              // 512-byte aligned
             ch[c].tileb = lb + OFF_T + hs * kDecTile * kLanes + hl;
+            ktb[c] = lb + OFF_K + hs * kDecTile * kLanes;
             // ---- stream header checks (every lane of the half holds the same entries)
             uint32_t x = kStateLow;
             size[c] = 0;
@@ -2873,6 +2972,27 @@ __global__ __launch_bounds__(1024, 1) void decode_bf16(DecodeLaunch a, DevTables
         // step reads them back transposed (lane hl: step r4, lanes q4..q4+3 of its half, so the
         // lanes of a half and the bytes of a lane run in decode order), resolves escaped values,
         // reconstructs and stores the rows and reloads pv with the row two tiles ahead.
+        // EXP: the classes of a tile go through the class tile (the lane's predictor row r4, channels
+        // q4..q4+3 in, the lane's own channel's 4 steps out); a class byte holds class << 4
+        auto put_classes = [&](const uint2 (&pv)[kDecChains]) {
+            if constexpr (EXP) {
+#pragma unroll
+                for (uint32_t c = 0; c < kDecChains; ++c) {
+                    const uint32_t ca = cls16x2(pv[c].x, base2) << 4, cb = cls16x2(pv[c].y, base2) << 4;
+                    const uint32_t v = __builtin_amdgcn_perm(cb, ca, 0x06040200u);   // 4 class bytes, channel order
+#pragma unroll
+                    for (uint32_t j = 0; j < 4; ++j)
+                        *reinterpret_cast<lds_u8*>(ktb[c] + (q4 + j) * kDecTile + r4) = uint8_t(v >> (8 * j));
+                }
+            }
+        };
+        auto get_classes = [&]() {
+            if constexpr (EXP) {
+#pragma unroll
+                for (uint32_t c = 0; c < kDecChains; ++c)
+                    cls[c] = *reinterpret_cast<const lds_u32*>(ktb[c] + hl * kDecTile);
+            }
+        };
         uint32_t zt[kDecChains];
         auto fetch_tile = [&]() {
 #pragma unroll
@@ -2880,9 +3000,22 @@ __global__ __launch_bounds__(1024, 1) void decode_bf16(DecodeLaunch a, DevTables
                 zt[c] = *reinterpret_cast<const lds_u32*>(ch[c].tileb - hl + r4 * kLanes + q4);
         };
         auto finish = [&](uint32_t T, uint2 (&pv)[kDecChains]) {
-            uint32_t ef[kDecChains];
+            uint32_t ef[kDecChains], npc[kDecChains];
 #pragma unroll
-            for (uint32_t c = 0; c < kDecChains; ++c) ef[c] = zero_bytes(zt[c] ^ np);
+            for (uint32_t c = 0; c < kDecChains; ++c) {
+                if constexpr (EXP) {
+                    // n of each position's class
+                    const uint32_t ca = cls16x2(pv[c].x, base2), cb = cls16x2(pv[c].y, base2);
+                    const uint32_t nl = lb + OFF_N;
+                    npc[c] = uint32_t(*reinterpret_cast<const lds_u8*>(nl + (ca & 0xFu))) |
+                             (uint32_t(*reinterpret_cast<const lds_u8*>(nl + (ca >> 16))) << 8) |
+                             (uint32_t(*reinterpret_cast<const lds_u8*>(nl + (cb & 0xFu))) << 16) |
+                             (uint32_t(*reinterpret_cast<const lds_u8*>(nl + (cb >> 16))) << 24);
+                } else {
+                    npc[c] = np;
+                }
+                ef[c] = zero_bytes(zt[c] ^ npc[c]);
+            }
             // the lane's 4 symbols as 16-bit values, two per dword
             uint32_t zz[kDecChains][2];
 #pragma unroll
@@ -2929,7 +3062,7 @@ __global__ __launch_bounds__(1024, 1) void decode_bf16(DecodeLaunch a, DevTables
                         }
                         if (f != 0) {
                             // a canonical encoder codes a value below n directly
-                            if (coded[c] && e < ((np >> (8 * kv)) & 0xFFu)) bad = true;
+                            if (coded[c] && e < ((npc[c] >> (8 * kv)) & 0xFFu)) bad = true;
                             const uint32_t sh = (kv & 1u) * 16;
                             if (kv < 2) zz[c][0] = (zz[c][0] & ~(0xFFFFu << sh)) | (e << sh);
                             else zz[c][1] = (zz[c][1] & ~(0xFFFFu << sh)) | (e << sh);
@@ -2954,8 +3087,10 @@ __global__ __launch_bounds__(1024, 1) void decode_bf16(DecodeLaunch a, DevTables
             DecState s0[kDecChains];
 #pragma unroll
             for (uint32_t c = 0; c < kDecChains; ++c) s0[c] = st[c];
-            dec_tile_steps_bf16<false>(
-                st, L, ch, sy, [&] { if (T > 0) fetch_tile(); }, [&] { if (T > 0) finish(T - 1, pvp); });
+            get_classes();
+            __builtin_amdgcn_wave_barrier();
+            dec_tile_steps_bf16<false, EXP>(
+                st, L, ch, sy, [&] { if (T > 0) fetch_tile(); }, [&] { if (T > 0) finish(T - 1, pvp); }, cls);
             // a half of a coded stream that read past the last chunk written (word count above
             // 64 (wrk + 1) in its field) decodes the tile again from memory
             uint32_t over = 0;
@@ -2969,13 +3104,16 @@ __global__ __launch_bounds__(1024, 1) void decode_bf16(DecodeLaunch a, DevTables
                     st[c].x = s0[c].x;
                     st[c].P = s0[c].P;
                 }
-                dec_tile_steps_bf16<true>(st, L, ch, sy, [] {}, [] {});
+                dec_tile_steps_bf16<true, EXP>(st, L, ch, sy, [] {}, [] {}, cls);
             }
 #pragma unroll
             for (uint32_t c = 0; c < kDecChains; ++c)
 #pragma unroll
                 for (uint32_t r = 0; r < kDecTile; ++r)
                     *reinterpret_cast<lds_u8*>(ch[c].tileb + r * kLanes) = uint8_t(sy[c][r]);
+            // the next tile's classes: its predictor row is in pvp (the initial load after tile 0, the
+            // reload of the finish above after later tiles)
+            if (T + 1 < kTiles) put_classes(pvp);
 #pragma unroll
             for (uint32_t c = 0; c < kDecChains; ++c) {
                 // the chunk in cw goes into its slot; the next one is requested while the ring
@@ -2990,6 +3128,8 @@ __global__ __launch_bounds__(1024, 1) void decode_bf16(DecodeLaunch a, DevTables
             }
             __builtin_amdgcn_wave_barrier();
         };
+        put_classes(pva);
+        __builtin_amdgcn_wave_barrier();
         for (uint32_t T = 0; T < kTiles; T += 2) {
             tile_at(T, pvb);
             tile_at(T + 1, pva);
@@ -3144,7 +3284,7 @@ __global__ __launch_bounds__(256) void nbr_map(const int16_t* coef, const int16_
             const int64_t q = q0 < -128 ? -128 : (q0 > 127 ? 127 : q0);
             qw[(4 * g4 + r) * KP + j * 16 + r16] = int8_t(q);
         }
-    if (KP > K)
+    if constexpr (KP > K)
         for (uint32_t i = lane; i < 16 * (KP - K); i += 64) qw[(i / (KP - K)) * KP + K + i % (KP - K)] = 0;
     __syncthreads();
 
@@ -3313,13 +3453,24 @@ hipError_t encode_all(const EncodeLaunch& a, const DevTables& t, hipStream_t st)
     const uint32_t ncg = a.shape.channels / kLanes;
     const bool aligned16 = (reinterpret_cast<uintptr_t>(a.target) | reinterpret_cast<uintptr_t>(a.aux)) % 16 == 0;
     const bool fits = slab_fits(a.shape);
-    if (DT == SKV_BF16 && MODE == SKV_RESIDUAL && fits && aligned16 && encode_bf16_lds(fc_stride(t)) <= kLdsLimit ) {
+    if (DT == SKV_BF16 && MODE == SKV_RESIDUAL && fits && aligned16 && encode_bf16_lds(fc_stride(t)) <= kLdsLimit) {
         const LdsGeo lg = lds_geometry(a.shape);
         const size_t lp = encode_bf16_lds(fc_stride(t));
-        hipError_t e = allow_lds(encode_bf16, lp);
+        hipError_t e = allow_lds(encode_bf16<false>, lp);
         if (e != hipSuccess) return e;
         timed("encode_streams", st, [&](hipEvent_t e0, hipEvent_t e1) {
-            hipExtLaunchKernelGGL(encode_bf16, dim3(lds_grid(lg)), dim3(kLdsThreads), lp, st, e0, e1, 0, a, t, fc_stride(t), lg);
+            hipExtLaunchKernelGGL(encode_bf16<false>, dim3(lds_grid(lg)), dim3(kLdsThreads), lp, st, e0, e1, 0, a, t,
+                                  fc_stride(t), lg);
+        });
+    } else if (DT == SKV_BF16 && MODE == SKV_RESIDUAL_EXP && fits && aligned16 &&
+               encode_bf16_exp_lds(fc_stride(t)) <= kLdsLimit) {
+        const LdsGeo lg = lds_geometry(a.shape);
+        const size_t lp = encode_bf16_exp_lds(fc_stride(t));
+        hipError_t e = allow_lds(encode_bf16<true>, lp);
+        if (e != hipSuccess) return e;
+        timed("encode_streams", st, [&](hipEvent_t e0, hipEvent_t e1) {
+            hipExtLaunchKernelGGL(encode_bf16<true>, dim3(lds_grid(lg)), dim3(kLdsThreads), lp, st, e0, e1, 0, a, t,
+                                  fc_stride(t), lg);
         });
     } else if (DT == SKV_E4M3 && MODE == SKV_RESIDUAL_EXP && fits && ncg % 4 == 0 && aligned &&
                3 * (encode_exp_lds(fc_stride(t)) + 256) <= kLdsLimit) {
@@ -3417,10 +3568,21 @@ hipError_t decode_all(const DecodeLaunch& a, const DevTables& t, hipStream_t st)
     const bool aligned8 = (reinterpret_cast<uintptr_t>(a.aux) | reinterpret_cast<uintptr_t>(a.out)) % 8 == 0;
     if (DT == SKV_BF16 && MODE == SKV_RESIDUAL && fits && aligned8 && dec_bf16_lds() <= kLdsLimit) {
         const LdsGeo lg = lds_geometry(a.shape);
-        hipError_t e = allow_lds(decode_bf16, dec_bf16_lds());
+        hipError_t e = allow_lds(decode_bf16<false>, dec_bf16_lds());
         if (e != hipSuccess) return e;
         timed("decode_streams", st, [&](hipEvent_t e0, hipEvent_t e1) {
-            hipExtLaunchKernelGGL(decode_bf16, dim3(lds_grid(lg)), dim3(kLdsThreads), dec_bf16_lds(), st, e0, e1, 0, a, t, lg);
+            hipExtLaunchKernelGGL(decode_bf16<false>, dim3(lds_grid(lg)), dim3(kLdsThreads), dec_bf16_lds(), st, e0, e1,
+                                  0, a, t, lg);
+        });
+        return hipGetLastError();
+    }
+    if (DT == SKV_BF16 && MODE == SKV_RESIDUAL_EXP && fits && aligned8 && dec_bf16_exp_lds() <= kLdsLimit) {
+        const LdsGeo lg = lds_geometry(a.shape);
+        hipError_t e = allow_lds(decode_bf16<true>, dec_bf16_exp_lds());
+        if (e != hipSuccess) return e;
+        timed("decode_streams", st, [&](hipEvent_t e0, hipEvent_t e1) {
+            hipExtLaunchKernelGGL(decode_bf16<true>, dim3(lds_grid(lg)), dim3(kLdsThreads), dec_bf16_exp_lds(), st, e0,
+                                  e1, 0, a, t, lg);
         });
         return hipGetLastError();
     }

@@ -272,15 +272,17 @@ def test_e4m3_wide_tables(skv, orc, noise, lo, hi):
     full_compare(skv, orc, t, p, tabs, oshape, f"e4m3 tables up to {max(ns)} symbols")
 
 
+@pytest.mark.parametrize("exp", [False, True])
 @pytest.mark.parametrize("dtype", ["bf16", "e4m3"])
-def test_word_bursts_after_escapes(skv, orc, dtype):
+def test_word_bursts_after_escapes(skv, orc, dtype, exp):
     """Every token block escapes in its first 4 steps and codes rare direct
     symbols (about 12 bits each) in the next 8, then repeats the predictor:
     the tiles after the escapes need more words than the decoder's ring holds,
     so they are decoded again from memory while the escapes of the tile before
-    are being resolved.  The streams stay coded (not raw)."""
-    cfg = gen.Config(93, f"burst-{dtype}", dtype, 1, 2, 512, 96)
-    t, p, tabs, oshape = residual_case(skv, orc, cfg)
+    are being resolved.  The streams stay coded (not raw).  Per-channel and
+    exponent-class tables."""
+    cfg = gen.Config(93, f"burst-{dtype}", dtype, 1, 2, 512, 128 if exp else 96)
+    t, p, tabs, oshape = exp_case(skv, orc, cfg) if exp else residual_case(skv, orc, cfg)
     step = (torch.arange(p.shape[2], device="cuda") % 128)[None, None, :, None]
     if dtype == "e4m3":
         far, rare, mask = 40, 20, 0xFF
@@ -341,17 +343,19 @@ def test_exponent_mode_small(skv, orc, cid):
     assert torch.equal(part, t[:, :, 256:512])
 
 
-def test_exponent_mode_escapes_and_unaligned(skv, orc):
+@pytest.mark.parametrize("dtype", ["e4m3", "bf16"])
+def test_exponent_mode_escapes_and_unaligned(skv, orc, dtype):
     """Exponent mode through every kernel path: rare far residuals (escapes in
     every class, with bursts of words), the tiled kernels on aligned buffers and
     the per-step ones on unaligned buffers; all containers equal the oracle's."""
-    cfg = gen.Config(99, "exp-escapes", "e4m3", 1, 2, 512, 128)
+    cfg = gen.Config(99, "exp-escapes", dtype, 1, 2, 512, 128)
     t, p, tabs, oshape = exp_case(skv, orc, cfg)
     rng = np.random.default_rng(21)
     tn = t.cpu().numpy()
     flat = tn.reshape(-1)
     pos = rng.choice(flat.size, size=flat.size // 200, replace=False)
-    flat[pos] = rng.integers(0, 256, size=pos.size, dtype=np.uint8)
+    hi = 256 if dtype == "e4m3" else 65536
+    flat[pos] = rng.integers(0, hi, size=pos.size).astype(np.int64).astype(flat.dtype)
     t = torch.from_numpy(tn).cuda()
     want = full_compare(skv, orc, t, p, tabs, oshape, "exponent mode escapes")
     tu, pu = _offset_copy(t, 1), _offset_copy(p, 3)
@@ -420,6 +424,16 @@ def test_exponent_mode_full_size_e4m3(skv, orc):
     say(f"[parity] exponent mode cfg2: generating {cfg.values} values on GPU")
     t, p, tabs, oshape = exp_case(skv, orc, cfg)
     big_compare(skv, orc, t, p, tabs, oshape, "exponent mode cfg2", min_ratio=4.5)
+
+
+def test_exponent_mode_full_size_bf16(skv, orc):
+    """The Qwen3-0.6B-shaped bf16 cache with exponent-conditioned tables (the
+    tiled bf16 kernels with the slab's 16 class tables): whole container equal
+    to the oracle's, exact round trip."""
+    cfg = gen.CONFIGS[1]
+    say(f"[parity] exponent mode cfg1: generating {cfg.values} values on GPU")
+    t, p, tabs, oshape = exp_case(skv, orc, cfg)
+    big_compare(skv, orc, t, p, tabs, oshape, "exponent mode cfg1", min_ratio=2.5)
 
 
 RANGES = [(0, 1024), (0, 128), (896, 1024), (256, 640), (128, 1024)]
