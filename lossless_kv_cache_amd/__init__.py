@@ -5,5 +5,6 @@ The C ABI lives in ``include/skv.h`` (``libskv.so``); ``skv`` is its thin
 ctypes binding.
 """
 from . import skv  # noqa: F401
-from .skv import (BF16, CHECKERBOARD, E4M3, INT16, RESIDUAL, Encoder, SkvError, Tables,  # noqa: F401
-                  decode, decode_into, encode, fit_tables, load_tables, make_shape)
+from .skv import (BF16, CHECKERBOARD, CHECKERBOARD_MAP, E4M3, INT16, RESIDUAL, RESIDUAL_EXP, Encoder,  # noqa: F401
+                  SkvError, Tables, decode, decode_into, decode_range, encode, encode_noalloc, fit_tables,
+                  fit_tables_map, load_tables, make_shape, transfer)
