@@ -47,7 +47,8 @@ typedef enum {
     SKV_ERR_TABLES = -5,   /* table blob malformed, or not the one a container
                               was coded with (hash mismatch), or shape mismatch  */
     SKV_ERR_DEVICE = -6,   /* a HIP runtime call failed                           */
-    SKV_ERR_NOMEM = -7     /* host or device allocation failed                   */
+    SKV_ERR_NOMEM = -7,    /* host or device allocation failed                   */
+    SKV_ERR_BUSY = -8      /* a store entry is pinned (in use)                   */
 } skv_status;
 
 typedef enum { SKV_BF16 = 1, SKV_E4M3 = 2, SKV_INT16 = 3 } skv_dtype;
@@ -282,6 +283,98 @@ int skv_transfer(const void* tables_blob, const skv_shape* s, uint32_t layers_pe
                  const void* d_aux_send, void* h_wire, size_t wire_capacity, size_t* wire_bytes,
                  uint64_t* chunk_offsets, const void* d_aux_recv, void* d_out, size_t out_capacity, void* d_work,
                  size_t* work_bytes, hipStream_t stream);
+
+/* Prefix-cache store.  Keeping the caches of shared prefixes (system
+ * prompts, retrieved documents) compressed lets the same memory hold more of
+ * them, which raises the hit rate ("Speculative KV coding" page, section
+ * "Where it can be used": prefix caching; VeriCache page, "Application to
+ * remote prefix caching"); a request restores only the prefix it shares
+ * through skv_decode_range.  A store keeps containers in an arena the caller
+ * owns and allocates no device memory itself (the arena outlives the store;
+ * the store never reads or writes arena bytes except through skv_store_put
+ * and skv_store_decode).
+ *
+ * Entries are keyed by block hashes: hashes[b] identifies tokens
+ * [128 b, 128 b + 128) together with everything before them (a chained hash
+ * of the token ids, for instance), so two caches share their first m blocks
+ * exactly when their first m hashes are equal.  A lookup returns the entry
+ * holding the longest leading run of the query's hashes (ties: the most
+ * recently used), checking all of that run's hashes, not only the last.
+ *
+ * Space: the arena is cut into 256-byte granules; an entry takes its
+ * container rounded up, at the lowest free offset where it fits.  When no
+ * free run is long enough, entries are evicted least recently used first
+ * (use = commit or lookup hit) until one is; pinned entries and open
+ * reservations are never evicted, and if evicting every other entry still
+ * would not make room, nothing is evicted and the call returns
+ * SKV_ERR_CAPACITY.  Entry ids start at 1 and are never reused.  Calls on
+ * one store may come from several threads (a mutex serializes the
+ * bookkeeping; skv_store_put and skv_store_decode run their GPU work
+ * outside it).
+ *
+ *   skv_store_create: arena (256-byte aligned, else SKV_ERR_ARG) of
+ *     arena_bytes (a multiple of 256, at least 256).  *store receives the
+ *     handle; release it with skv_store_destroy (entries are dropped, the
+ *     arena is not touched).
+ *   skv_store_reserve: room for a container of `bytes` that the caller
+ *     writes itself (for instance one received from another server); *entry
+ *     and *addr receive the id and the arena address.  The entry stays out
+ *     of lookups and eviction until skv_store_commit (the caller has
+ *     finished writing) or skv_store_abort.  nblocks 1..2^20 hashes are
+ *     copied (SKV_ERR_ARG otherwise).
+ *   skv_store_commit: the reservation holds `bytes` (at most the reserved
+ *     size) of container; the unused granules return to the free space and
+ *     the entry becomes visible and most recently used.
+ *   skv_store_abort: drop a reservation.
+ *   skv_store_put (device): encode a cache into the store -- skv_encode's
+ *     arguments, the container placed once its size is known (the streams
+ *     are coded into d_work, the space reserved, then the container written
+ *     there) -- and commit it with nblocks = tokens / 128 hashes (else
+ *     SKV_ERR_ARG).  d_work == NULL sets *work_bytes to the need
+ *     (skv_encode's).  Blocks until the entry is committed; *entry and
+ *     *container_bytes receive its id and size.
+ *   skv_store_lookup: *hit receives the best entry for the query (entry 0
+ *     and matched_blocks 0 on a miss).  A hit pins the entry (it cannot be
+ *     evicted or erased) until skv_store_release.
+ *   skv_store_decode (device): decode tokens [token_begin, token_end) of an
+ *     entry through skv_decode_range (token_end == 0: the whole container
+ *     through skv_decode), with that call's arguments and rules; the entry
+ *     is pinned during the call.
+ *   skv_store_erase: remove an entry now (SKV_ERR_BUSY while pinned).
+ *   Unknown or already removed ids return SKV_ERR_ARG. */
+typedef struct skv_store skv_store;
+typedef struct {
+    uint64_t entry;            /* 0 on a miss                               */
+    uint32_t matched_blocks;   /* leading query blocks the entry holds      */
+    uint32_t entry_blocks;     /* blocks the entry holds                    */
+    const void* container;     /* its container in the arena                */
+    uint64_t container_bytes;
+} skv_store_hit;
+typedef struct {
+    uint64_t arena_bytes;
+    uint64_t used_bytes;       /* granules held by entries and reservations */
+    uint64_t largest_free;     /* longest free run                          */
+    uint64_t container_bytes;  /* committed entries' container bytes        */
+    uint64_t entries;          /* committed entries                         */
+    uint64_t pinned;           /* committed entries pinned by lookups       */
+    uint64_t inserts, evictions, hits, misses, hit_blocks;
+} skv_store_info;
+int skv_store_create(void* arena, uint64_t arena_bytes, skv_store** store);
+void skv_store_destroy(skv_store* store);
+int skv_store_reserve(skv_store* store, const uint64_t* hashes, uint32_t nblocks, uint64_t bytes, uint64_t* entry,
+                      void** addr);
+int skv_store_commit(skv_store* store, uint64_t entry, uint64_t bytes);
+int skv_store_abort(skv_store* store, uint64_t entry);
+int skv_store_put(skv_store* store, const uint64_t* hashes, uint32_t nblocks, const void* tables_blob,
+                  const skv_shape* s, const void* d_target, const void* d_aux, void* d_work, size_t* work_bytes,
+                  hipStream_t stream, uint64_t* entry, uint64_t* container_bytes);
+int skv_store_lookup(skv_store* store, const uint64_t* hashes, uint32_t nblocks, skv_store_hit* hit);
+int skv_store_release(skv_store* store, uint64_t entry);
+int skv_store_decode(skv_store* store, const void* tables_blob, uint64_t entry, uint32_t token_begin,
+                     uint32_t token_end, const void* d_aux, void* d_out, size_t out_capacity, void* d_work,
+                     size_t* work_bytes, hipStream_t stream);
+int skv_store_erase(skv_store* store, uint64_t entry);
+int skv_store_stats(skv_store* store, skv_store_info* stats);
 
 /* Release a library-owned blob and its device copies.  NULL is a no-op. */
 void skv_free(void* tables_blob);

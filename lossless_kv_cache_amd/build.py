@@ -30,7 +30,8 @@ def build(verbose: bool = False) -> str:
     os.makedirs(out_dir, exist_ok=True)
     common = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wextra", "-Wno-unused-parameter"]
     objs = []
-    for src, device in (("skv_fit.cpp", False), ("skv_api.cpp", False), ("skv_kernels.hip", True)):
+    for src, device in (("skv_fit.cpp", False), ("skv_api.cpp", False), ("skv_store.cpp", False),
+                        ("skv_kernels.hip", True)):
         obj = os.path.join(out_dir, src + ".o")
         cmd = [hipcc, *common, "-c", os.path.join(CSRC, src), "-o", obj]
         if device:

@@ -162,6 +162,7 @@ const char* skv_strerror(int status) {
         case SKV_ERR_TABLES: return "table blob invalid or mismatched";
         case SKV_ERR_DEVICE: return "HIP runtime error";
         case SKV_ERR_NOMEM: return "out of memory";
+        case SKV_ERR_BUSY: return "store entry in use";
         default: return "unknown status";
     }
 }
@@ -684,3 +685,41 @@ int skv_kernel_times(const char** names, float* ms, int capacity) {
 }
 
 }  // extern "C"
+
+namespace skv {
+
+int encode_begin(const void* tables_blob, const skv_shape* s, const void* d_target, const void* d_aux, void* d_work,
+                 size_t work_bytes, hipStream_t stream, PendingEncode* pe) {
+    if (!tables_blob || !s || !pe || !d_target || !d_aux || !d_work) return SKV_ERR_ARG;
+    if (!shape_supported(*s, true)) return SKV_ERR_SHAPE;
+    Blob* b = find_blob(tables_blob);
+    if (!b) return SKV_ERR_ARG;
+    if (!same_geometry(b->shape, *s)) return SKV_ERR_TABLES;
+    if (work_bytes < encode_need(*s)) return SKV_ERR_CAPACITY;
+    const DevTables* t = nullptr;
+    int rc = device_tables(b, stream, &t);
+    if (rc != SKV_OK) return rc;
+    pe->a = encode_launch(b, *s, d_target, d_aux, nullptr, 0, static_cast<uint8_t*>(d_work));
+    pe->t = t;
+    if (launch_encode(pe->a, *t, stream, kEncodeCode) != hipSuccess) return SKV_ERR_DEVICE;
+    uint64_t payload = 0;
+    rc = read_back(&payload, pe->a.total, 8, stream);
+    if (rc != SKV_OK) return rc;
+    pe->container_bytes = kHeaderBytes + 8 * (pe->a.n_streams + 1) + payload;
+    return SKV_OK;
+}
+
+int encode_finish(PendingEncode* pe, void* d_out, size_t out_capacity, hipStream_t stream) {
+    if (!pe || !d_out) return SKV_ERR_ARG;
+    if (out_capacity < pe->container_bytes) return SKV_ERR_CAPACITY;
+    pe->a.out = static_cast<uint8_t*>(d_out);
+    pe->a.out_capacity = out_capacity;
+    if (launch_encode(pe->a, *pe->t, stream, kEncodePack) != hipSuccess) return SKV_ERR_DEVICE;
+    // the read of the magic waits for the pack kernels
+    uint8_t magic[4];
+    const int rc = read_back(magic, d_out, sizeof magic, stream);
+    if (rc != SKV_OK) return rc;
+    return std::memcmp(magic, "SKV1", 4) == 0 ? SKV_OK : SKV_ERR_DEVICE;
+}
+
+}  // namespace skv

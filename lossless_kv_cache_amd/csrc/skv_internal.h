@@ -133,8 +133,28 @@ struct DecodeLaunch {
 
 hipError_t build_dev_tables(const uint8_t* blob, DevTables* t, hipStream_t stream);
 void free_dev_tables(DevTables* t);
-hipError_t launch_encode(const EncodeLaunch& a, const DevTables& t, hipStream_t stream);
+// Encoder phases: kEncodeCode codes the streams into the workspace and sums
+// their sizes (the payload size lands in *a.total); kEncodePack writes the
+// header, index and streams into a.out.  Between the two, a.out and
+// a.out_capacity may change.
+constexpr uint32_t kEncodeCode = 1, kEncodePack = 2, kEncodeAll = 3;
+hipError_t launch_encode(const EncodeLaunch& a, const DevTables& t, hipStream_t stream, uint32_t phases = kEncodeAll);
 hipError_t launch_decode(const DecodeLaunch& a, const DevTables& t, hipStream_t stream);
+
+// The encoder in two calls, for callers that place the container once its
+// size is known (the prefix-cache store).  encode_begin validates as
+// skv_encode does, codes the streams into d_work (encode workspace size) and
+// blocks until pe->container_bytes is known; encode_finish writes the
+// container to d_out and returns once it is there.  The blob and d_work must
+// stay alive between the two calls, on the same stream.
+struct PendingEncode {
+    EncodeLaunch a;
+    const DevTables* t;
+    uint64_t container_bytes;
+};
+int encode_begin(const void* tables_blob, const skv_shape* s, const void* d_target, const void* d_aux, void* d_work,
+                 size_t work_bytes, hipStream_t stream, PendingEncode* pe);
+int encode_finish(PendingEncode* pe, void* d_out, size_t out_capacity, hipStream_t stream);
 hipError_t launch_clear_u32(uint32_t* p, uint32_t n, hipStream_t stream);
 // Decoded-neighbour map on the device: out[t] = G'[t] for every odd token t,
 // from the even rows of coef (out may be coef itself: only odd rows are written).

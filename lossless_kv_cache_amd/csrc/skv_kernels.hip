@@ -3436,16 +3436,17 @@ hipError_t nbr_map_kt(const int16_t* coef, const int16_t* G, int16_t* out, uint3
     return hipGetLastError();
 }
 
+// Encoder phase 1: the streams into the workspace, their sizes summed.
 template <uint32_t DT, uint32_t MODE>
-hipError_t encode_all(const EncodeLaunch& a, const DevTables& t, hipStream_t st) {
+hipError_t encode_code(const EncodeLaunch& a, const DevTables& t, hipStream_t st) {
     const uint64_t n = a.n_streams;
+    const uint32_t nb = uint32_t((n + kScanBlock - 1) / kScanBlock);
     if (MODE == SKV_CHECKERBOARD && a.shape.mode == SKV_CHECKERBOARD_MAP) {
         // the odd pass codes against the side input mapped from the true (= decoded) even rows
         const hipError_t e = launch_nbr_map(static_cast<const int16_t*>(a.target), static_cast<const int16_t*>(a.aux),
                                             a.map_side, a.shape.tokens, a.shape.channels, t, st);
         if (e != hipSuccess) return e;
     }
-    const uint32_t nb = uint32_t((n + kScanBlock - 1) / kScanBlock);
     const uint32_t eg = uint32_t((n + kStreamsPerBlock - 1) / kStreamsPerBlock);
     const size_t lb = encode_lds_bytes(t, DT);
     const size_t lt = size_t(kLanes) * fc_stride(t) * 16 + (kLdsThreads / 64) * kTileWaveLds;
@@ -3526,6 +3527,14 @@ hipError_t encode_all(const EncodeLaunch& a, const DevTables& t, hipStream_t st)
     timed("stream_block_scan", st, [&](hipEvent_t e0, hipEvent_t e1) {
         hipExtLaunchKernelGGL(stream_block_scan, dim3(1), dim3(kScanBlock), 0, st, e0, e1, 0, a.block_sum, nb, a.block_off, a.total);
     });
+    return hipGetLastError();
+}
+
+// Encoder phase 2: header, index and streams into a.out.
+template <uint32_t DT, uint32_t MODE>
+hipError_t encode_pack(const EncodeLaunch& a, hipStream_t st) {
+    const uint64_t n = a.n_streams;
+    const uint32_t nb = uint32_t((n + kScanBlock - 1) / kScanBlock);
     timed("place_streams", st, [&](hipEvent_t e0, hipEvent_t e1) {
         hipExtLaunchKernelGGL((place_streams<DT, MODE>), dim3(nb), dim3(kScanBlock), 0, st, e0, e1, 0, a, a.block_off);
     });
@@ -3533,6 +3542,15 @@ hipError_t encode_all(const EncodeLaunch& a, const DevTables& t, hipStream_t st)
         hipExtLaunchKernelGGL((copy_streams<DT, MODE>), dim3(uint32_t((n + 3) / 4)), dim3(256), 0, st, e0, e1, 0, a);
     });
     return hipGetLastError();
+}
+
+template <uint32_t DT, uint32_t MODE>
+hipError_t encode_all(const EncodeLaunch& a, const DevTables& t, hipStream_t st, uint32_t phases) {
+    if (phases & kEncodeCode) {
+        const hipError_t e = encode_code<DT, MODE>(a, t, st);
+        if (e != hipSuccess) return e;
+    }
+    return phases & kEncodePack ? encode_pack<DT, MODE>(a, st) : hipSuccess;
 }
 
 template <uint32_t DT, uint32_t MODE>
@@ -3691,13 +3709,13 @@ hipError_t launch_nbr_map(const int16_t* coef, const int16_t* G, int16_t* out, u
     }
 }
 
-hipError_t launch_encode(const EncodeLaunch& a, const DevTables& t, hipStream_t st) {
-    if (is_checkerboard(a.shape.mode)) return encode_all<SKV_INT16, SKV_CHECKERBOARD>(a, t, st);
+hipError_t launch_encode(const EncodeLaunch& a, const DevTables& t, hipStream_t st, uint32_t phases) {
+    if (is_checkerboard(a.shape.mode)) return encode_all<SKV_INT16, SKV_CHECKERBOARD>(a, t, st, phases);
     if (a.shape.mode == SKV_RESIDUAL_EXP)
-        return a.shape.dtype == SKV_E4M3 ? encode_all<SKV_E4M3, SKV_RESIDUAL_EXP>(a, t, st)
-                                         : encode_all<SKV_BF16, SKV_RESIDUAL_EXP>(a, t, st);
-    if (a.shape.dtype == SKV_E4M3) return encode_all<SKV_E4M3, SKV_RESIDUAL>(a, t, st);
-    return encode_all<SKV_BF16, SKV_RESIDUAL>(a, t, st);
+        return a.shape.dtype == SKV_E4M3 ? encode_all<SKV_E4M3, SKV_RESIDUAL_EXP>(a, t, st, phases)
+                                         : encode_all<SKV_BF16, SKV_RESIDUAL_EXP>(a, t, st, phases);
+    if (a.shape.dtype == SKV_E4M3) return encode_all<SKV_E4M3, SKV_RESIDUAL>(a, t, st, phases);
+    return encode_all<SKV_BF16, SKV_RESIDUAL>(a, t, st, phases);
 }
 
 hipError_t launch_decode(const DecodeLaunch& a, const DevTables& t, hipStream_t st) {

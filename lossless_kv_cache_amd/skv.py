@@ -8,6 +8,7 @@ from __future__ import annotations
 
 import atexit
 import ctypes
+import hashlib
 import os
 import sys
 import weakref
@@ -22,6 +23,8 @@ ABI_VERSION = 1
 BF16, E4M3, INT16 = 1, 2, 3
 RESIDUAL, CHECKERBOARD, RESIDUAL_EXP, CHECKERBOARD_MAP = 0, 1, 2, 3
 OK, ERR_ARG, ERR_SHAPE, ERR_CAPACITY, ERR_CORRUPT, ERR_TABLES, ERR_DEVICE, ERR_NOMEM = 0, -1, -2, -3, -4, -5, -6, -7
+ERR_BUSY = -8
+BLOCK_TOKENS = 128
 
 
 class SkvError(RuntimeError):
@@ -39,6 +42,17 @@ class Shape(ctypes.Structure):
 class NbrMap(ctypes.Structure):
     _fields_ = [("rank", ctypes.c_uint32), ("shift_h", ctypes.c_uint32), ("shift_m", ctypes.c_uint32),
                 ("V", ctypes.c_void_p), ("U", ctypes.c_void_p)]
+
+
+class StoreHit(ctypes.Structure):
+    _fields_ = [("entry", ctypes.c_uint64), ("matched_blocks", ctypes.c_uint32), ("entry_blocks", ctypes.c_uint32),
+                ("container", ctypes.c_void_p), ("container_bytes", ctypes.c_uint64)]
+
+
+class StoreInfo(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_uint64) for n in ("arena_bytes", "used_bytes", "largest_free", "container_bytes",
+                                               "entries", "pinned", "inserts", "evictions", "hits", "misses",
+                                               "hit_blocks")]
 
 
 _lib = None
@@ -79,6 +93,30 @@ def lib():
         L.skv_free.argtypes = [vp]
         L.skv_kernel_timing.restype = ctypes.c_int
         L.skv_kernel_timing.argtypes = [ctypes.c_int]
+        u64 = ctypes.c_uint64
+        pu64 = ctypes.POINTER(u64)
+        L.skv_store_create.restype = ctypes.c_int
+        L.skv_store_create.argtypes = [vp, u64, ctypes.POINTER(vp)]
+        L.skv_store_destroy.restype = None
+        L.skv_store_destroy.argtypes = [vp]
+        L.skv_store_reserve.restype = ctypes.c_int
+        L.skv_store_reserve.argtypes = [vp, vp, u32, u64, pu64, ctypes.POINTER(vp)]
+        L.skv_store_commit.restype = ctypes.c_int
+        L.skv_store_commit.argtypes = [vp, u64, u64]
+        L.skv_store_abort.restype = ctypes.c_int
+        L.skv_store_abort.argtypes = [vp, u64]
+        L.skv_store_put.restype = ctypes.c_int
+        L.skv_store_put.argtypes = [vp, vp, u32, vp, sp, vp, vp, vp, psz, vp, pu64, pu64]
+        L.skv_store_lookup.restype = ctypes.c_int
+        L.skv_store_lookup.argtypes = [vp, vp, u32, ctypes.POINTER(StoreHit)]
+        L.skv_store_release.restype = ctypes.c_int
+        L.skv_store_release.argtypes = [vp, u64]
+        L.skv_store_decode.restype = ctypes.c_int
+        L.skv_store_decode.argtypes = [vp, vp, u64, u32, u32, vp, vp, sz, vp, psz, vp]
+        L.skv_store_erase.restype = ctypes.c_int
+        L.skv_store_erase.argtypes = [vp, u64]
+        L.skv_store_stats.restype = ctypes.c_int
+        L.skv_store_stats.argtypes = [vp, ctypes.POINTER(StoreInfo)]
         L.skv_kernel_times.restype = ctypes.c_int
         L.skv_kernel_times.argtypes = [ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(ctypes.c_float), ctypes.c_int]
         if L.skv_version() != ABI_VERSION:
@@ -447,3 +485,168 @@ def decode(tables: Tables, container: torch.Tensor, aux: torch.Tensor) -> torch.
     """Decode a container against the predictor (or G); returns a tensor shaped like aux."""
     out = torch.empty_like(aux)
     return decode_into(tables, container, aux, out)
+
+
+# ------------------------------------------------------------------ prefix-cache store
+def block_hashes(token_ids, block: int = BLOCK_TOKENS) -> np.ndarray:
+    """Chained 64-bit hashes of the whole blocks of a token-id sequence: the
+    hash of block b covers tokens [0, block * (b + 1)) (BLAKE2b of the
+    previous block's hash and the block's ids as int64), so two sequences
+    share their first m hashes exactly when they share their first m blocks."""
+    ids = np.ascontiguousarray(np.asarray(token_ids, dtype=np.int64).reshape(-1))
+    out = np.empty(len(ids) // block, dtype=np.uint64)
+    h = b""
+    for b in range(len(out)):
+        h = hashlib.blake2b(h + ids[b * block:(b + 1) * block].tobytes(), digest_size=8).digest()
+        out[b] = int.from_bytes(h, "little")
+    return out
+
+
+def _hash_arg(hashes) -> tuple[int, int, np.ndarray]:
+    h = np.ascontiguousarray(np.asarray(hashes, dtype=np.uint64).reshape(-1))
+    return h.ctypes.data, len(h), h
+
+
+class Store:
+    """Prefix-cache store (skv_store_*) over an arena tensor the store keeps
+    alive.  put / decode need a device arena; reserve, commit, lookup, erase
+    and stats are bookkeeping only and take any contiguous uint8 tensor."""
+
+    def __init__(self, arena_bytes: int | None = None, arena: torch.Tensor | None = None, device=None):
+        if arena is None:
+            dev = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
+            arena = torch.empty(arena_bytes, dtype=torch.uint8, device=dev)
+        if not isinstance(arena, torch.Tensor) or arena.dtype != torch.uint8 or not arena.is_contiguous():
+            raise ValueError("arena must be a contiguous uint8 tensor")
+        self.arena = arena
+        self._h = ctypes.c_void_p()
+        _check(lib().skv_store_create(arena.data_ptr(), arena.numel(), ctypes.byref(self._h)), "skv_store_create")
+        self._work = None
+
+    def _handle(self):
+        if not self._h.value:
+            raise ValueError("store is closed")
+        return self._h
+
+    def _view(self, addr: int, nbytes: int) -> torch.Tensor:
+        off = addr - self.arena.data_ptr()
+        return self.arena[off:off + nbytes]
+
+    def _workspace(self, need: int) -> torch.Tensor:
+        if self._work is None or self._work.numel() < need:
+            self._work = None
+            self._work = torch.empty(need, dtype=torch.uint8, device=self.arena.device)
+        return self._work
+
+    def reserve(self, nbytes: int, hashes) -> tuple[int, torch.Tensor]:
+        """Room for a container written by the caller: (entry id, arena view of nbytes)."""
+        hp, n, _keep = _hash_arg(hashes)
+        eid, addr = ctypes.c_uint64(), ctypes.c_void_p()
+        _check(lib().skv_store_reserve(self._handle(), hp, n, nbytes, ctypes.byref(eid), ctypes.byref(addr)),
+               "skv_store_reserve")
+        return eid.value, self._view(addr.value, nbytes)
+
+    def commit(self, entry: int, nbytes: int) -> None:
+        _check(lib().skv_store_commit(self._handle(), entry, nbytes), "skv_store_commit")
+
+    def abort(self, entry: int) -> None:
+        _check(lib().skv_store_abort(self._handle(), entry), "skv_store_abort")
+
+    def insert(self, container: torch.Tensor, hashes) -> int:
+        """Store an existing container (copied into the arena on the current stream)."""
+        if not isinstance(container, torch.Tensor) or container.dtype != torch.uint8 or container.dim() != 1:
+            raise ValueError("container must be a 1-D uint8 tensor")
+        eid, view = self.reserve(container.numel(), hashes)
+        try:
+            view.copy_(container)
+            if view.is_cuda:
+                torch.cuda.current_stream().synchronize()
+        except Exception:
+            self.abort(eid)
+            raise
+        self.commit(eid, container.numel())
+        return eid
+
+    def put(self, tables: Tables, target: torch.Tensor, aux: torch.Tensor, hashes) -> tuple[int, int]:
+        """Encode target against aux into the store; returns (entry id, container bytes)."""
+        if not self.arena.is_cuda:
+            raise ValueError("put needs a device arena")
+        tokens = tokens_of(tables, target)
+        pt = _check_cache(target, "target", tables, tokens)
+        pa = _check_cache(aux, "aux", tables, tokens)
+        if target.device != self.arena.device or aux.device != self.arena.device:
+            raise ValueError("target and aux must be on the arena's device")
+        hp, n, _keep = _hash_arg(hashes)
+        if tokens % BLOCK_TOKENS or n != tokens // BLOCK_TOKENS:
+            raise ValueError(f"{tokens} tokens take {tokens // BLOCK_TOKENS} block hashes of whole 128-token blocks")
+        shape = tables.shape(tokens)
+        wb = ctypes.c_size_t()
+        _check(lib().skv_store_put(self._handle(), None, 0, tables.ptr, ctypes.byref(shape), None, None, None,
+                                   ctypes.byref(wb), None, None, None), "skv_store_put(size query)")
+        work = self._workspace(wb.value)
+        wb = ctypes.c_size_t(work.numel())
+        eid, nbytes = ctypes.c_uint64(), ctypes.c_uint64()
+        rc = lib().skv_store_put(self._handle(), hp, n, tables.ptr, ctypes.byref(shape), pt, pa, work.data_ptr(),
+                                 ctypes.byref(wb), _stream(), ctypes.byref(eid), ctypes.byref(nbytes))
+        _check(rc, "skv_store_put")
+        return eid.value, nbytes.value
+
+    def lookup(self, hashes) -> StoreHit:
+        """Entry holding the longest leading run of the hashes (entry 0 on a miss); a hit is pinned until release."""
+        hp, n, _keep = _hash_arg(hashes)
+        hit = StoreHit()
+        _check(lib().skv_store_lookup(self._handle(), hp if n else None, n, ctypes.byref(hit)), "skv_store_lookup")
+        return hit
+
+    def container(self, hit: StoreHit) -> torch.Tensor:
+        """Arena view of a hit's container (valid while the hit is pinned)."""
+        return self._view(hit.container, hit.container_bytes)
+
+    def release(self, entry: int) -> None:
+        _check(lib().skv_store_release(self._handle(), entry), "skv_store_release")
+
+    def erase(self, entry: int) -> None:
+        _check(lib().skv_store_erase(self._handle(), entry), "skv_store_erase")
+
+    def decode_into(self, tables: Tables, entry: int, aux: torch.Tensor, out: torch.Tensor, token_begin: int = 0,
+                    token_end: int = 0) -> torch.Tensor:
+        """Decode tokens [token_begin, token_end) of an entry (token_end 0: the whole container)."""
+        if token_end:
+            if is_checkerboard(tables.mode) or not 0 <= token_begin < token_end or token_begin % 128 or token_end % 128:
+                raise SkvError(ERR_SHAPE, "skv_store_decode")
+            pa, po, cap = _decode_buffers(aux, out, tables, token_end - token_begin)
+        else:
+            if token_begin:
+                raise ValueError("a whole-container decode starts at token 0")
+            pa, po, cap = _decode_buffers(aux, out, tables)
+        if aux.device != self.arena.device or out.device != self.arena.device:
+            raise ValueError("aux and out must be on the arena's device")
+        wb = ctypes.c_size_t()
+        _check(lib().skv_store_decode(self._handle(), tables.ptr, entry, 0, 0, None, None, 0, None, ctypes.byref(wb),
+                                      None), "skv_store_decode(size query)")
+        work = self._workspace(wb.value)
+        wb = ctypes.c_size_t(work.numel())
+        rc = lib().skv_store_decode(self._handle(), tables.ptr, entry, token_begin, token_end, pa, po, cap,
+                                    work.data_ptr(), ctypes.byref(wb), _stream())
+        _check(rc, "skv_store_decode")
+        return out
+
+    def decode(self, tables: Tables, entry: int, aux: torch.Tensor, token_begin: int = 0,
+               token_end: int = 0) -> torch.Tensor:
+        return self.decode_into(tables, entry, aux, torch.empty_like(aux), token_begin, token_end)
+
+    def stats(self) -> dict:
+        info = StoreInfo()
+        _check(lib().skv_store_stats(self._handle(), ctypes.byref(info)), "skv_store_stats")
+        return {name: getattr(info, name) for name, _ in StoreInfo._fields_}
+
+    def close(self) -> None:
+        if self._h.value and _lib is not None:
+            _lib.skv_store_destroy(self._h)
+        self._h = ctypes.c_void_p(None)
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -1,0 +1,153 @@
+"""GPU: the prefix-cache store (skv_store_*) over a device arena.  A cache put
+into the store is the oracle's container byte for byte; a request that shares
+the first m blocks of a stored prefix finds it and decodes exactly those
+tokens (and any other whole-block range, or the whole cache) through the
+container's offset index; least recently used entries make room, pinned ones
+stay ("Speculative KV coding" page, "Where it can be used": prefix caching)."""
+import os
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from workloads import gen
+
+pytestmark = pytest.mark.gpu
+
+ORACLE_THREADS = max(1, min(16, os.cpu_count() or 1))
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def skv():
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible")
+    from lossless_kv_cache_amd import skv as m
+    m.lib()
+    return m
+
+
+def residual_tables(skv, cfg, mode):
+    ct, cp = gen.residual_array(cfg, gen.CALIB, tokens=256)
+    dt = skv.E4M3 if cfg.dtype == "e4m3" else skv.BF16
+    return skv.fit_tables(dt, mode, cfg.layers, cfg.kv, cfg.channels, ct.numpy(), cp.numpy(), 256)
+
+
+def token_ids(seed, n):
+    return np.random.default_rng(seed).integers(0, 150000, n)
+
+
+@pytest.mark.parametrize("dtype,mode", [("bf16", 0), ("e4m3", 0), ("bf16", 2), ("e4m3", 2)])
+def test_put_lookup_prefix_decode(skv, orc, dtype, mode):
+    cfg = gen.Config(110 + mode, f"store-{dtype}", dtype, 2, 2, 640, 256, outliers=dtype == "bf16")
+    say(f"[store] {dtype} mode {mode}: put")
+    t, p = gen.residual_array(cfg, device="cuda")
+    tabs = residual_tables(skv, cfg, mode)
+    st = skv.Store(arena_bytes=32 << 20)
+    ids = token_ids(1, cfg.tokens)
+    h = skv.block_hashes(ids)
+    assert len(h) == 5
+    entry, nbytes = st.put(tabs, t, p, h)
+    oshape = orc.make_shape(skv.E4M3 if dtype == "e4m3" else skv.BF16, mode, cfg.layers, cfg.kv, cfg.tokens,
+                            cfg.channels)
+    want = orc.encode_array(tabs.bytes(), oshape, t.cpu().numpy(), p.cpu().numpy(), threads=ORACLE_THREADS)
+    hit = st.lookup(h)
+    assert (hit.entry, hit.matched_blocks, hit.entry_blocks, hit.container_bytes) == (entry, 5, 5, nbytes)
+    got = st.container(hit).cpu().numpy()
+    assert nbytes == want.size and np.array_equal(got, want), "stored container differs from the oracle's"
+    st.release(entry)
+    # a request sharing the first 3 blocks (token 389 differs)
+    ids2 = ids.copy()
+    ids2[389] += 1
+    hit = st.lookup(skv.block_hashes(ids2))
+    assert (hit.entry, hit.matched_blocks) == (entry, 3)
+    T3 = 128 * hit.matched_blocks
+    say(f"[store] {dtype} mode {mode}: prefix decode of {T3} tokens")
+    part = st.decode(tabs, entry, p[:, :, :T3].contiguous(), 0, T3)
+    assert torch.equal(part, t[:, :, :T3])
+    st.release(entry)
+    mid = st.decode(tabs, entry, p[:, :, 128:512].contiguous(), 128, 512)
+    assert torch.equal(mid, t[:, :, 128:512])
+    assert torch.equal(st.decode(tabs, entry, p), t)
+    s = st.stats()
+    assert (s["entries"], s["hits"], s["pinned"], s["container_bytes"]) == (1, 2, 0, nbytes)
+
+
+def test_eviction_and_pins_on_device(skv):
+    """Room for two caches: a third put evicts the least recently used one; a
+    pinned entry is passed over; every surviving entry still decodes."""
+    cfgs = [gen.Config(120 + k, f"store-evict-{k}", "e4m3", 2, 2, 512, 256, outliers=False) for k in range(4)]
+    data = [gen.residual_array(c, device="cuda") for c in cfgs]
+    tabs = residual_tables(skv, cfgs[0], 0)
+    sizes = [skv.encode(tabs, t, p).numel() for t, p in data]
+    # largest first, so that every later cache fits where one evicted entry was
+    order = sorted(range(4), key=lambda k: -sizes[k])
+    data, sizes = [data[k] for k in order], [sizes[k] for k in order]
+    gran = lambda n: -(-n // 256) * 256
+    st = skv.Store(arena_bytes=2 * gran(max(sizes)) + 256)
+    hs = [skv.block_hashes(token_ids(10 + k, 512)) for k in range(4)]
+    e0, _ = st.put(tabs, *data[0], hs[0])
+    e1, _ = st.put(tabs, *data[1], hs[1])
+    assert st.stats()["evictions"] == 0
+    e2, _ = st.put(tabs, *data[2], hs[2])                # evicts e0
+    s = st.stats()
+    assert (s["entries"], s["evictions"]) == (2, 1)
+    assert st.lookup(hs[0]).entry == 0
+    hit = st.lookup(hs[1])                               # e1: pinned and most recent
+    assert hit.entry == e1
+    e3, _ = st.put(tabs, *data[3], hs[3])                # e2 is the only evictable entry
+    assert st.lookup(hs[2]).entry == 0
+    assert st.stats()["evictions"] == 2
+    assert torch.equal(st.decode(tabs, e1, data[1][1]), data[1][0])
+    assert torch.equal(st.decode(tabs, e3, data[3][1]), data[3][0])
+    with pytest.raises(skv.SkvError) as ei:
+        st.erase(e1)
+    assert ei.value.status == skv.ERR_BUSY
+    st.release(e1)
+    st.erase(e1)
+    with pytest.raises(skv.SkvError) as ei:
+        st.decode(tabs, e1, data[1][1])
+    assert ei.value.status == skv.ERR_ARG
+    # a cache larger than the arena: refused before anything is evicted
+    small = skv.Store(arena_bytes=gran(sizes[0]) // 2 // 256 * 256)
+    with pytest.raises(skv.SkvError) as ei:
+        small.put(tabs, *data[0], hs[0])
+    assert ei.value.status == skv.ERR_CAPACITY
+    assert small.stats()["entries"] == 0 and small.stats()["used_bytes"] == 0
+
+
+def test_insert_and_checkerboard_entries(skv, orc):
+    """A container coded elsewhere goes in through reserve/commit (insert); a
+    checkerboard cache is stored and decoded whole, and its ranges are refused."""
+    cfg = gen.Config(130, "store-insert", "bf16", 1, 2, 384, 128)
+    t, p = gen.residual_array(cfg, device="cuda")
+    tabs = residual_tables(skv, cfg, 0)
+    cont = skv.encode(tabs, t, p).clone()
+    st = skv.Store(arena_bytes=8 << 20)
+    e = st.insert(cont, skv.block_hashes(token_ids(3, 384)))
+    assert torch.equal(st.decode(tabs, e, p), t)
+    assert torch.equal(st.decode(tabs, e, p[:, :, 256:].contiguous(), 256, 384), t[:, :, 256:])
+
+    cb = gen.CONFIGS[4].with_tokens(1280, channels=192)
+    coef, G = gen.dckv_draw(cb, device="cuda")
+    cc, cg = gen.dckv_draw(cb, gen.CALIB, tokens=256)
+    ctabs = skv.fit_tables(skv.INT16, skv.CHECKERBOARD, 1, 1, 192, cc.numpy(), cg.numpy(), 256)
+    hc = skv.block_hashes(token_ids(4, 1280))
+    ec, nb = st.put(ctabs, coef, G, hc)
+    oshape = orc.make_shape(orc.INT16, orc.CHECKERBOARD, 1, 1, 1280, 192)
+    want = orc.encode_array(ctabs.bytes(), oshape, coef.cpu().numpy(), G.cpu().numpy(), threads=ORACLE_THREADS)
+    hit = st.lookup(hc)
+    assert hit.entry == ec and np.array_equal(st.container(hit).cpu().numpy(), want)
+    st.release(ec)
+    assert torch.equal(st.decode(ctabs, ec, G), coef)
+    with pytest.raises(skv.SkvError) as ei:
+        st.decode(ctabs, ec, G[:256].contiguous(), 0, 256)
+    assert ei.value.status == skv.ERR_SHAPE
+    with pytest.raises(ValueError):
+        st.put(ctabs, coef, G, hc[:9])                   # one hash per 128-token block
+    assert st.stats()["entries"] == 2
