@@ -227,19 +227,25 @@ int skv_decode(const void* tables_blob, const void* d_in, size_t in_bytes, const
  * ("Speculative KV coding" page, section "Where it can be used": prefix
  * caching; VeriCache page, "Application to remote prefix caching"); the
  * container's offset index locates the streams of the range, so nothing
- * outside it is read or decoded.  Residual-mode containers (either table
- * kind) only.
- *   token_begin, token_end: the tokens [token_begin, token_end) of every
- *     (layer, K|V) slab; both multiples of 128, token_begin < token_end <=
- *     the container's tokens (else SKV_ERR_SHAPE, also for a checkerboard
- *     container).
- *   d_aux, d_out: device arrays [layers][kv][token_end - token_begin]
- *     [channels] -- the predictor of the range and its reconstruction
- *     (out_capacity bytes available).
- * Header, blob and workspace rules as for skv_decode.  Every stream of the
- * range is checked as in skv_decode (SKV_ERR_CORRUPT); streams outside the
- * range are not read, so damage there goes unnoticed.  Blocks the host to
- * read the header and the integrity word. */
+ * outside it is read or decoded.
+ *   token_begin, token_end: the tokens [token_begin, token_end), with
+ *     token_begin < token_end <= the container's tokens (else SKV_ERR_SHAPE).
+ *   Residual modes (either table kind): both multiples of 128, the range of
+ *     every (layer, K|V) slab; d_aux and d_out are device arrays
+ *     [layers][kv][token_end - token_begin][channels] -- the predictor of the
+ *     range and its reconstruction (out_capacity bytes available).
+ *   Checkerboard modes: both multiples of 256 (a block of 128 even and 128
+ *     odd tokens), the range under 2 GiB; d_out is [token_end - token_begin]
+ *     [channels].  The last odd token of the range needs the even token
+ *     token_end, whose stream is decoded whole, so unless token_end is the
+ *     container's last token d_aux holds the side input G of tokens
+ *     [token_begin, token_end + 256) -- the range then the next block --
+ *     else of [token_begin, token_end).  The workspace need is 256 +
+ *     512 * channels bytes (the next block's even rows).
+ * Header and blob rules as for skv_decode.  Every stream decoded is checked
+ * as in skv_decode (SKV_ERR_CORRUPT); streams outside the range are not
+ * read, so damage there goes unnoticed.  Blocks the host to read the header
+ * and the integrity word. */
 int skv_decode_range(const void* tables_blob, const void* d_in, size_t in_bytes, uint32_t token_begin,
                      uint32_t token_end, const void* d_aux, void* d_out, size_t out_capacity, void* d_work,
                      size_t* work_bytes, hipStream_t stream);
@@ -338,8 +344,8 @@ int skv_transfer(const void* tables_blob, const skv_shape* s, uint32_t layers_pe
  *     evicted or erased) until skv_store_release.
  *   skv_store_decode (device): decode tokens [token_begin, token_end) of an
  *     entry through skv_decode_range (token_end == 0: the whole container
- *     through skv_decode), with that call's arguments and rules; the entry
- *     is pinned during the call.
+ *     through skv_decode), with that call's arguments and rules (workspace
+ *     sizing included); the entry is pinned during the call.
  *   skv_store_erase: remove an entry now (SKV_ERR_BUSY while pinned).
  *   Unknown or already removed ids return SKV_ERR_ARG. */
 typedef struct skv_store skv_store;

@@ -367,7 +367,10 @@ static int decode_blocks(const void* tables_blob, const void* d_in, size_t in_by
     if (!tables_blob || !work_bytes) return SKV_ERR_ARG;
     Blob* b = find_blob(tables_blob);
     if (!b) return SKV_ERR_ARG;
-    const uint64_t need = 256;
+    // the status word; a checkerboard range also decodes the even tokens of
+    // the block after it (256 rows) into the workspace
+    const bool cb = skv::is_checkerboard(b->shape.mode);
+    const uint64_t need = 256 + (cb && range ? align256(2ull * skv::kSteps * b->shape.channels * 2) : 0);
     if (!d_work) {
         *work_bytes = need;
         return SKV_OK;
@@ -392,15 +395,17 @@ static int decode_blocks(const void* tables_blob, const void* d_in, size_t in_by
     const uint64_t payload = skv::rd64(h + 48);
     const uint64_t head = skv::kHeaderBytes + 8 * (n + 1);
     if (in_bytes < head || in_bytes - head < payload) return SKV_ERR_CORRUPT;
-    // the decoded part: whole token blocks of a residual container
+    // the decoded part: whole token blocks (128 tokens; checkerboard: 128 even and 128 odd)
     skv_shape part = s;
     uint32_t tb_base = 0;
+    const uint32_t blk = cb ? 2 * skv::kSteps : skv::kSteps;
     if (range) {
-        if (skv::is_checkerboard(s.mode) || token_begin >= token_end || token_end > s.tokens ||
-            token_begin % skv::kSteps != 0 || token_end % skv::kSteps != 0)
+        if (token_begin >= token_end || token_end > s.tokens || token_begin % blk != 0 || token_end % blk != 0)
             return SKV_ERR_SHAPE;
+        // checkerboard ranges take the per-stream decoder, which keeps a range under 2 GiB
+        if (cb && uint64_t(token_end - token_begin) * s.channels * 2 >= (1ull << 31)) return SKV_ERR_SHAPE;
         part.tokens = token_end - token_begin;
-        tb_base = token_begin / skv::kSteps;
+        tb_base = token_begin / blk;
     }
     if (out_capacity < skv::element_count(part) * skv::elem_bytes(part.dtype)) return SKV_ERR_CAPACITY;
     const skv::DevTables* t = nullptr;
@@ -419,7 +424,11 @@ static int decode_blocks(const void* tables_blob, const void* d_in, size_t in_by
     a.shape = part;
     a.n_streams = skv::stream_count(part);
     a.tb_base = tb_base;
-    a.ntb_index = s.tokens / skv::kSteps;
+    a.ntb_index = s.tokens / blk;
+    // a checkerboard range before the container's end: the next block's even rows after the status word
+    a.next_rows = cb && range && token_end < s.tokens
+                      ? reinterpret_cast<int16_t*>(static_cast<uint8_t*>(d_work) + 256)
+                      : nullptr;
     if (skv::launch_clear_u32(a.status, 1, stream) != hipSuccess) return SKV_ERR_DEVICE;
     if (timing) skv::timing_reset();
     if (skv::launch_decode(a, *t, stream) != hipSuccess) return SKV_ERR_DEVICE;

@@ -129,6 +129,11 @@ struct DecodeLaunch {
     uint64_t n_streams;      // streams decoded
     uint32_t tb_base;        // first token block of the range in the container
     uint32_t ntb_index;      // token blocks per slab in the container
+    // checkerboard range that stops before the container's end: 256 rows for
+    // the token block after the range, whose even tokens are decoded first
+    // (its first row is the right neighbour of the range's last odd token);
+    // aux then continues with that block's side input.  Null otherwise.
+    int16_t* next_rows;
 };
 
 hipError_t build_dev_tables(const uint8_t* blob, DevTables* t, hipStream_t stream);
@@ -158,8 +163,10 @@ int encode_finish(PendingEncode* pe, void* d_out, size_t out_capacity, hipStream
 hipError_t launch_clear_u32(uint32_t* p, uint32_t n, hipStream_t stream);
 // Decoded-neighbour map on the device: out[t] = G'[t] for every odd token t,
 // from the even rows of coef (out may be coef itself: only odd rows are written).
+// right: the row after coef's last (a range's next even token, 16-byte
+// aligned like the others), or null at the end of the cache.
 hipError_t launch_nbr_map(const int16_t* coef, const int16_t* G, int16_t* out, uint32_t tokens, uint32_t channels,
-                          const DevTables& t, hipStream_t stream);
+                          const DevTables& t, hipStream_t stream, const int16_t* right = nullptr);
 uint64_t encode_work_bytes(uint64_t n_streams, uint32_t raw_bytes);
 
 // Fixed device workspace of skv_encode_noalloc (SKV_NOALLOC_WORK_BYTES).

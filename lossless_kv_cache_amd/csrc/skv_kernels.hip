@@ -742,7 +742,10 @@ __global__ __launch_bounds__(256) void decode_streams(DecodeLaunch a, DevTables 
 // So a step waits on its slot-map byte and its (frequency, start) word, both
 // in device memory, and on nothing else.  Output and checks are those of
 // decode_streams.
-template <int kLag, int P>
+// RANGE: token blocks tb_base onwards of the container (the shape is the
+// range's, rows are numbered from its start), and the range's last odd token
+// takes its right neighbour from next_rows when the range stops early.
+template <int kLag, int P, bool RANGE = false>
 __global__ __launch_bounds__(256) void decode_cb(DecodeLaunch a, DevTables t, uint64_t first, uint64_t count) {
     constexpr uint32_t RAW = 2 * kSyms;
     const uint32_t tid = threadIdx.x;
@@ -757,7 +760,8 @@ __global__ __launch_bounds__(256) void decode_cb(DecodeLaunch a, DevTables t, ui
     const size_t C = g.C;
     const uint64_t* index = a.index;
     const uint8_t* pay = a.pay;
-    const uint64_t e0 = index[sid], e1 = index[sid + 1];
+    const uint64_t xid = RANGE ? index_pos(a, pass, tb, cg, g.ncg) : sid;
+    const uint64_t e0 = index[xid], e1 = index[xid + 1];
     const uint64_t off = e0 & ~kRawBit, end = e1 & ~kRawBit;
     int16_t* out = static_cast<int16_t*>(a.out);
     // the odd pass's side input may be the output's odd rows (mapped in place): a lane reads
@@ -819,7 +823,11 @@ __global__ __launch_bounds__(256) void decode_cb(DecodeLaunch a, DevTables t, ui
                     if (pass) {
                         const uint32_t tok = 2u * (tb * kSteps + uint32_t(k)) + 1u;
                         il[sl] = out[r - C];
-                        ir[sl] = tok + 1 < g.T ? int32_t(out[r + C]) : int32_t(out[r - C]);
+                        if constexpr (RANGE)
+                            ir[sl] = tok + 1 < g.T ? int32_t(out[r + C])
+                                                   : int32_t(a.next_rows ? a.next_rows[ch] : out[r - C]);
+                        else
+                            ir[sl] = tok + 1 < g.T ? int32_t(out[r + C]) : int32_t(out[r - C]);
                     }
                 }
             }
@@ -3223,10 +3231,14 @@ __device__ __forceinline__ void load16(const int16_t* p, uint32_t (&d)[8]) {
     }
 }
 
-template <uint32_t KT, bool VEC>   // KT: rank / 16; VEC: coef, G and out 16-byte aligned
+// KT: rank / 16; VEC: coef, G and out 16-byte aligned.  right: the row after
+// the last one (the last odd token's right neighbour), or null for the end of
+// the cache (the last odd token repeats its left row).
+template <uint32_t KT, bool VEC>
 __global__ __launch_bounds__(256) void nbr_map(const int16_t* coef, const int16_t* __restrict__ G, int16_t* out,
                                                uint32_t T, uint32_t C, const int8_t* __restrict__ V,
-                                               const int8_t* __restrict__ U, uint32_t sh_h, uint32_t sh_m) {
+                                               const int8_t* __restrict__ U, uint32_t sh_h, uint32_t sh_m,
+                                               const int16_t* right) {
     constexpr uint32_t K = 16 * KT;
     constexpr uint32_t KP = (K + 63) / 64 * 64;             // rank padded to whole 64-wide steps
     constexpr uint32_t KB = KP / 64;
@@ -3248,7 +3260,7 @@ __global__ __launch_bounds__(256) void nbr_map(const int16_t* coef, const int16_
         const uint32_t u = min(u0 + r16, nodd - 1);           // (always u0 + r16: the grid covers T / 2 exactly)
         const uint32_t t = 2 * u + 1;
         const int16_t* lrow = coef + size_t(t - 1) * C;
-        const int16_t* rrow = t + 1 < T ? coef + size_t(t + 1) * C : lrow;
+        const int16_t* rrow = t + 1 < T ? coef + size_t(t + 1) * C : (right ? right : lrow);
         auto src = [&](uint32_t kk) { return kk < C ? lrow + kk : rrow + (kk - C); };
         uint32_t cur[8], nxt[8];
         load16<VEC>(src(16 * g4), cur);
@@ -3421,17 +3433,17 @@ hipError_t allow_lds(K kernel, size_t bytes) {
 
 template <uint32_t KT>
 hipError_t nbr_map_kt(const int16_t* coef, const int16_t* G, int16_t* out, uint32_t T, uint32_t C,
-                      const DevTables& t, hipStream_t st) {
+                      const DevTables& t, hipStream_t st, const int16_t* right) {
     const bool vec = (reinterpret_cast<uintptr_t>(coef) | reinterpret_cast<uintptr_t>(G) |
-                      reinterpret_cast<uintptr_t>(out)) % 16 == 0;
+                      reinterpret_cast<uintptr_t>(out) | reinterpret_cast<uintptr_t>(right)) % 16 == 0;
     timed("nbr_map", st, [&](hipEvent_t e0, hipEvent_t e1) {
         const dim3 grid(T / 2 / kMapTok), block(256);
         if (vec)
             hipExtLaunchKernelGGL((nbr_map<KT, true>), grid, block, 0, st, e0, e1, 0, coef, G, out, T, C, t.map_v,
-                                  t.map_u, t.map_sh_h, t.map_sh_m);
+                                  t.map_u, t.map_sh_h, t.map_sh_m, right);
         else
             hipExtLaunchKernelGGL((nbr_map<KT, false>), grid, block, 0, st, e0, e1, 0, coef, G, out, T, C, t.map_v,
-                                  t.map_u, t.map_sh_h, t.map_sh_m);
+                                  t.map_u, t.map_sh_h, t.map_sh_m, right);
     });
     return hipGetLastError();
 }
@@ -3444,7 +3456,7 @@ hipError_t encode_code(const EncodeLaunch& a, const DevTables& t, hipStream_t st
     if (MODE == SKV_CHECKERBOARD && a.shape.mode == SKV_CHECKERBOARD_MAP) {
         // the odd pass codes against the side input mapped from the true (= decoded) even rows
         const hipError_t e = launch_nbr_map(static_cast<const int16_t*>(a.target), static_cast<const int16_t*>(a.aux),
-                                            a.map_side, a.shape.tokens, a.shape.channels, t, st);
+                                            a.map_side, a.shape.tokens, a.shape.channels, t, st, nullptr);
         if (e != hipSuccess) return e;
     }
     const uint32_t eg = uint32_t((n + kStreamsPerBlock - 1) / kStreamsPerBlock);
@@ -3618,18 +3630,40 @@ hipError_t decode_all(const DecodeLaunch& a, const DevTables& t, hipStream_t st)
     const uint64_t passes = MODE == SKV_CHECKERBOARD ? 2 : 1;
     const uint64_t per = a.n_streams / passes;
     const uint32_t grid = uint32_t((per + kStreamsPerBlock - 1) / kStreamsPerBlock);
+    const uint32_t ncg = a.shape.channels / kLanes;
+    auto cb_grid = [&](uint64_t streams) { return dim3(uint32_t(ncg * ((streams / ncg + 7) / 8))); };
+    // a checkerboard range (token blocks from tb_base, or fewer than the container's)
+    const bool range = MODE == SKV_CHECKERBOARD && (a.tb_base != 0 || a.ntb_index != a.shape.tokens / 2 / kSteps);
+    if (range && !fits) return hipErrorInvalidValue;
+    if (range && a.next_rows) {
+        // the even tokens of the block after the range, into next_rows; the block's side input
+        // follows the range's in aux
+        DecodeLaunch x = a;
+        x.shape.tokens = 2 * kSteps;
+        x.n_streams = 2 * uint64_t(ncg);
+        x.tb_base = a.tb_base + a.shape.tokens / (2 * kSteps);
+        x.aux = static_cast<const int16_t*>(a.aux) + size_t(a.shape.tokens) * a.shape.channels;
+        x.aux_odd = x.aux;
+        x.out = a.next_rows;
+        x.next_rows = nullptr;
+        timed("decode_streams", st, [&](hipEvent_t e0, hipEvent_t e1) {
+            hipExtLaunchKernelGGL((decode_cb<2, 8, true>), cb_grid(ncg), dim3(256), 0, st, e0, e1, 0, x, t, 0, ncg);
+        });
+    }
     for (uint64_t ps = 0; ps < passes; ++ps) {
         if (ps == 1 && a.shape.mode == SKV_CHECKERBOARD_MAP) {
             // the map of the decoded even rows, written into the output's odd rows (the odd pass's side input)
             int16_t* o = static_cast<int16_t*>(a.out);
             const hipError_t e = launch_nbr_map(o, static_cast<const int16_t*>(a.aux), o, a.shape.tokens,
-                                                a.shape.channels, t, st);
+                                                a.shape.channels, t, st, a.next_rows);
             if (e != hipSuccess) return e;
         }
         timed("decode_streams", st, [&](hipEvent_t e0, hipEvent_t e1) {
-            if (MODE == SKV_CHECKERBOARD && fits)
-                hipExtLaunchKernelGGL((decode_cb<2, 8>), dim3(a.shape.channels / kLanes * ((per / (a.shape.channels / kLanes) + 7) / 8)),
-                                   dim3(256), 0, st, e0, e1, 0, a, t, ps * per, per);
+            if (MODE == SKV_CHECKERBOARD && range)
+                hipExtLaunchKernelGGL((decode_cb<2, 8, true>), cb_grid(per), dim3(256), 0, st, e0, e1, 0, a, t,
+                                      ps * per, per);
+            else if (MODE == SKV_CHECKERBOARD && fits)
+                hipExtLaunchKernelGGL((decode_cb<2, 8>), cb_grid(per), dim3(256), 0, st, e0, e1, 0, a, t, ps * per, per);
             else
                 hipExtLaunchKernelGGL((decode_streams<DT, MODE>), dim3(grid), dim3(256), 0, st, e0, e1, 0, a, t, ps * per, per);
         });
@@ -3698,13 +3732,13 @@ void free_dev_tables(DevTables* t) {
 }
 
 hipError_t launch_nbr_map(const int16_t* coef, const int16_t* G, int16_t* out, uint32_t T, uint32_t C,
-                          const DevTables& t, hipStream_t st) {
+                          const DevTables& t, hipStream_t st, const int16_t* right) {
     switch (t.map_rank) {
-        case 16: return nbr_map_kt<1>(coef, G, out, T, C, t, st);
-        case 32: return nbr_map_kt<2>(coef, G, out, T, C, t, st);
-        case 64: return nbr_map_kt<4>(coef, G, out, T, C, t, st);
-        case 128: return nbr_map_kt<8>(coef, G, out, T, C, t, st);
-        case 256: return nbr_map_kt<16>(coef, G, out, T, C, t, st);
+        case 16: return nbr_map_kt<1>(coef, G, out, T, C, t, st, right);
+        case 32: return nbr_map_kt<2>(coef, G, out, T, C, t, st, right);
+        case 64: return nbr_map_kt<4>(coef, G, out, T, C, t, st, right);
+        case 128: return nbr_map_kt<8>(coef, G, out, T, C, t, st, right);
+        case 256: return nbr_map_kt<16>(coef, G, out, T, C, t, st, right);
         default: return hipErrorInvalidValue;
     }
 }

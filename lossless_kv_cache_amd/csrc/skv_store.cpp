@@ -296,7 +296,11 @@ int skv_store_decode(skv_store* store, const void* tables_blob, uint64_t entry, 
                      uint32_t token_end, const void* d_aux, void* d_out, size_t out_capacity, void* d_work,
                      size_t* work_bytes, hipStream_t stream) {
     if (!store || !work_bytes) return SKV_ERR_ARG;
-    if (!d_work) return skv_decode(tables_blob, nullptr, 0, nullptr, nullptr, 0, nullptr, work_bytes, stream);
+    if (!d_work)
+        return token_end == 0 && token_begin == 0
+                   ? skv_decode(tables_blob, nullptr, 0, nullptr, nullptr, 0, nullptr, work_bytes, stream)
+                   : skv_decode_range(tables_blob, nullptr, 0, token_begin, token_end, nullptr, nullptr, 0, nullptr,
+                                      work_bytes, stream);
     const void* cont = nullptr;
     uint64_t bytes = 0;
     {

@@ -396,20 +396,65 @@ def decode_into(tables: Tables, container: torch.Tensor, aux: torch.Tensor, out:
     return out
 
 
+def container_tokens(container: torch.Tensor) -> int:
+    """Tokens per slab in a container's header (a small device-to-host read)."""
+    _check_container(container)
+    if container.numel() < 64:
+        raise SkvError(ERR_CORRUPT, "container header")
+    return int.from_bytes(container[20:24].cpu().numpy().tobytes(), "little")
+
+
+def range_aux_tokens(tables: Tables, tokens: int, token_begin: int, token_end: int) -> int:
+    """Tokens of side input / predictor a range decode reads: the range, and
+    for a checkerboard range that stops before the container's `tokens`, the
+    256-token block after it (its even tokens are decoded for the range's
+    last odd token)."""
+    if is_checkerboard(tables.mode):
+        return min(tokens, token_end + 256) - token_begin
+    return token_end - token_begin
+
+
+def _range_buffers(tables: Tables, tokens: int | None, token_begin: int, token_end: int, aux, out, what: str,
+                   rules_only: bool = False):
+    """The library's range rules (same status), then the buffers of the
+    range: aux with range_aux_tokens tokens, out of the range's elements."""
+    cb = is_checkerboard(tables.mode)
+    blk = 256 if cb else 128
+    if (not 0 <= token_begin < token_end or token_begin % blk or token_end % blk or
+            (tokens is not None and token_end > tokens)):
+        raise SkvError(ERR_SHAPE, what)
+    if rules_only:
+        return None
+    if not cb:
+        return _decode_buffers(aux, out, tables, token_end - token_begin)
+    pa = _check_cache(aux, "aux", tables, range_aux_tokens(tables, tokens, token_begin, token_end))
+    if not isinstance(out, torch.Tensor) or out.element_size() != 2:
+        raise ValueError("out must be a device tensor of 2-byte elements")
+    po = _dev(out, "out")
+    cap = min(out.numel(), (token_end - token_begin) * tables.channels) * 2
+    return pa, po, cap
+
+
+def _range_work(tables: Tables, token_begin: int, token_end: int, device) -> torch.Tensor:
+    wb = ctypes.c_size_t()
+    _check(lib().skv_decode_range(tables.ptr, None, 0, token_begin, token_end, None, None, 0, None, ctypes.byref(wb),
+                                  None), "skv_decode_range(size)")
+    work = _decode_work.get(device)
+    if work is None or work.numel() < wb.value:
+        _decode_work[device] = None
+        work = _decode_work[device] = torch.empty(wb.value, dtype=torch.uint8, device=device)
+    return work
+
+
 def decode_range_into(tables: Tables, container: torch.Tensor, token_begin: int, token_end: int, aux: torch.Tensor,
                       out: torch.Tensor) -> torch.Tensor:
-    """Decode tokens [token_begin, token_end) of every slab; aux and out hold that range only."""
-    # the library's range rules first (same status), then the buffers of the range
-    if (is_checkerboard(tables.mode) or not 0 <= token_begin < token_end or token_begin % 128 or token_end % 128):
-        raise SkvError(ERR_SHAPE, "skv_decode_range")
+    """Decode tokens [token_begin, token_end) of every slab; out holds that
+    range, aux range_aux_tokens(...) tokens from token_begin."""
+    _range_buffers(tables, None, token_begin, token_end, None, None, "skv_decode_range", rules_only=True)
     pc = _check_container(container)
-    pa, po, cap = _decode_buffers(aux, out, tables, token_end - token_begin)
-    key = container.device
-    work = _decode_work.get(key)
-    if work is None:
-        wb = ctypes.c_size_t()
-        _check(lib().skv_decode(tables.ptr, None, 0, None, None, 0, None, ctypes.byref(wb), None), "skv_decode(size)")
-        work = _decode_work[key] = torch.empty(wb.value, dtype=torch.uint8, device=key)
+    T = container_tokens(container) if is_checkerboard(tables.mode) else None
+    pa, po, cap = _range_buffers(tables, T, token_begin, token_end, aux, out, "skv_decode_range")
+    work = _range_work(tables, token_begin, token_end, container.device)
     wb = ctypes.c_size_t(work.numel())
     rc = lib().skv_decode_range(tables.ptr, pc, container.numel(), token_begin, token_end, pa, po, cap,
                                 work.data_ptr(), ctypes.byref(wb), _stream())
@@ -419,8 +464,10 @@ def decode_range_into(tables: Tables, container: torch.Tensor, token_begin: int,
 
 def decode_range(tables: Tables, container: torch.Tensor, token_begin: int, token_end: int,
                  aux: torch.Tensor) -> torch.Tensor:
-    """Decode a token range against its predictor; returns a tensor shaped like aux."""
-    return decode_range_into(tables, container, token_begin, token_end, aux, torch.empty_like(aux))
+    """Decode a token range against its predictor (or side input); returns the range's reconstruction."""
+    _range_buffers(tables, None, token_begin, token_end, None, None, "skv_decode_range", rules_only=True)
+    out = torch.empty(_layout(tables, token_end - token_begin), dtype=aux.dtype, device=aux.device)
+    return decode_range_into(tables, container, token_begin, token_end, aux, out)
 
 
 class Transfer:
@@ -522,6 +569,8 @@ class Store:
         self._h = ctypes.c_void_p()
         _check(lib().skv_store_create(arena.data_ptr(), arena.numel(), ctypes.byref(self._h)), "skv_store_create")
         self._work = None
+        self._tokens = {}          # entry id -> the container's tokens (ids are never reused)
+        self._reserved = {}        # open reservation id -> arena address
 
     def _handle(self):
         if not self._h.value:
@@ -544,13 +593,21 @@ class Store:
         eid, addr = ctypes.c_uint64(), ctypes.c_void_p()
         _check(lib().skv_store_reserve(self._handle(), hp, n, nbytes, ctypes.byref(eid), ctypes.byref(addr)),
                "skv_store_reserve")
+        self._reserved[eid.value] = addr.value
         return eid.value, self._view(addr.value, nbytes)
 
-    def commit(self, entry: int, nbytes: int) -> None:
+    def commit(self, entry: int, nbytes: int, tokens: int | None = None) -> None:
+        """Make a reservation visible; tokens (read from the container header
+        when not given) sizes the checks of later range decodes."""
         _check(lib().skv_store_commit(self._handle(), entry, nbytes), "skv_store_commit")
+        addr = self._reserved.pop(entry, None)
+        if tokens is None and addr is not None and nbytes >= 64:
+            tokens = int.from_bytes(self._view(addr, 24)[20:24].cpu().numpy().tobytes(), "little")
+        self._tokens[entry] = tokens
 
     def abort(self, entry: int) -> None:
         _check(lib().skv_store_abort(self._handle(), entry), "skv_store_abort")
+        self._reserved.pop(entry, None)
 
     def insert(self, container: torch.Tensor, hashes) -> int:
         """Store an existing container (copied into the arena on the current stream)."""
@@ -564,7 +621,7 @@ class Store:
         except Exception:
             self.abort(eid)
             raise
-        self.commit(eid, container.numel())
+        self.commit(eid, container.numel(), container_tokens(container) if container.is_cuda else None)
         return eid
 
     def put(self, tables: Tables, target: torch.Tensor, aux: torch.Tensor, hashes) -> tuple[int, int]:
@@ -589,6 +646,7 @@ class Store:
         rc = lib().skv_store_put(self._handle(), hp, n, tables.ptr, ctypes.byref(shape), pt, pa, work.data_ptr(),
                                  ctypes.byref(wb), _stream(), ctypes.byref(eid), ctypes.byref(nbytes))
         _check(rc, "skv_store_put")
+        self._tokens[eid.value] = tokens
         return eid.value, nbytes.value
 
     def lookup(self, hashes) -> StoreHit:
@@ -612,9 +670,10 @@ class Store:
                     token_end: int = 0) -> torch.Tensor:
         """Decode tokens [token_begin, token_end) of an entry (token_end 0: the whole container)."""
         if token_end:
-            if is_checkerboard(tables.mode) or not 0 <= token_begin < token_end or token_begin % 128 or token_end % 128:
-                raise SkvError(ERR_SHAPE, "skv_store_decode")
-            pa, po, cap = _decode_buffers(aux, out, tables, token_end - token_begin)
+            T = self._tokens.get(entry)
+            if T is None and is_checkerboard(tables.mode):
+                raise SkvError(ERR_ARG, "skv_store_decode")
+            pa, po, cap = _range_buffers(tables, T, token_begin, token_end, aux, out, "skv_store_decode")
         else:
             if token_begin:
                 raise ValueError("a whole-container decode starts at token 0")
@@ -622,8 +681,8 @@ class Store:
         if aux.device != self.arena.device or out.device != self.arena.device:
             raise ValueError("aux and out must be on the arena's device")
         wb = ctypes.c_size_t()
-        _check(lib().skv_store_decode(self._handle(), tables.ptr, entry, 0, 0, None, None, 0, None, ctypes.byref(wb),
-                                      None), "skv_store_decode(size query)")
+        _check(lib().skv_store_decode(self._handle(), tables.ptr, entry, token_begin, token_end, None, None, 0, None,
+                                      ctypes.byref(wb), None), "skv_store_decode(size query)")
         work = self._workspace(wb.value)
         wb = ctypes.c_size_t(work.numel())
         rc = lib().skv_store_decode(self._handle(), tables.ptr, entry, token_begin, token_end, pa, po, cap,
@@ -633,7 +692,11 @@ class Store:
 
     def decode(self, tables: Tables, entry: int, aux: torch.Tensor, token_begin: int = 0,
                token_end: int = 0) -> torch.Tensor:
-        return self.decode_into(tables, entry, aux, torch.empty_like(aux), token_begin, token_end)
+        if not token_end:
+            return self.decode_into(tables, entry, aux, torch.empty_like(aux))
+        _range_buffers(tables, None, token_begin, token_end, None, None, "skv_store_decode", rules_only=True)
+        out = torch.empty(_layout(tables, token_end - token_begin), dtype=aux.dtype, device=aux.device)
+        return self.decode_into(tables, entry, aux, out, token_begin, token_end)
 
     def stats(self) -> dict:
         info = StoreInfo()

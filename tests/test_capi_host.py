@@ -275,3 +275,19 @@ def test_fit_matches_oracle_neighbour_map(skv, orc, rank, channels):
     with pytest.raises(skv.SkvError) as e:
         skv.load_tables(bytes(bad))
     assert e.value.status == skv.ERR_TABLES
+
+
+def test_range_workspace_sizing_on_host(skv):
+    """The workspace a range decode asks for needs no device: the status word,
+    plus for a checkerboard blob one 256-token block of rows (the even tokens
+    after the range); a whole decode needs only the status word."""
+    for dtype, mode, channels, extra in [(skv.E4M3, skv.RESIDUAL, 64, 0), (skv.BF16, skv.RESIDUAL_EXP, 64, 0),
+                                         (skv.INT16, skv.CHECKERBOARD, 64, 512 * 64)]:
+        tabs = _small_tables(skv, dtype, mode, channels=channels)
+        wb = ctypes.c_size_t()
+        assert skv.lib().skv_decode_range(tabs.ptr, None, 0, 0, 256, None, None, 0, None, ctypes.byref(wb), None) == 0
+        assert wb.value == 256 + extra
+        assert skv.lib().skv_decode(tabs.ptr, None, 0, None, None, 0, None, ctypes.byref(wb), None) == 0
+        assert wb.value == 256
+        assert skv.range_aux_tokens(tabs, 1024, 256, 512) == (512 if extra else 256)
+        assert skv.range_aux_tokens(tabs, 1024, 512, 1024) == 512

@@ -500,15 +500,64 @@ def test_decode_range_errors(skv, orc):
         else:
             out = skv.decode_range(tabs, torch.from_numpy(bad).cuda(), 128, 256, pr)
             assert torch.equal(out, t[:, :, 128:256])
-    # checkerboard containers have no range decode
+    # checkerboard ranges: whole 256-token blocks, and the side input of the block after the range
     cb = gen.CONFIGS[4].with_tokens(512, channels=64)
     coef, G = gen.dckv_draw(cb, device="cuda")
     cc, cgl = gen.dckv_draw(cb, gen.CALIB, tokens=256, device="cuda")
     ctabs = skv.fit_tables(skv.INT16, skv.CHECKERBOARD, 1, 1, 64, cc.cpu().numpy(), cgl.cpu().numpy(), 256)
     ccont = skv.encode(ctabs, coef, G)
-    with pytest.raises(skv.SkvError) as e:
-        skv.decode_range(ctabs, ccont, 0, 256, G[:256].contiguous())
-    assert e.value.status == skv.ERR_SHAPE
+    for a, b in [(0, 128), (128, 384), (256, 256), (0, 768)]:
+        with pytest.raises(skv.SkvError) as e:
+            skv.decode_range(ctabs, ccont, a, b, G[:256].contiguous())
+        assert e.value.status == skv.ERR_SHAPE, (a, b)
+    with pytest.raises(ValueError, match="shape"):
+        skv.decode_range(ctabs, ccont, 0, 256, G[:256].contiguous())      # the next block's G is missing
+    assert torch.equal(skv.decode_range(ctabs, ccont, 0, 256, G), coef[:256])
+    assert torch.equal(skv.decode_range(ctabs, ccont, 256, 512, G[256:].contiguous()), coef[256:])
+
+
+@pytest.mark.parametrize("mapped", [False, True])
+def test_decode_range_checkerboard(skv, orc, mapped):
+    """Checkerboard ranges (with and without the decoded-neighbour map) equal
+    the same tokens of the oracle's decode of the whole container.  A range
+    that stops early decodes the even stream of the next block too: damage
+    there is found, damage in that block's odd stream is not read."""
+    T, C = 2048, 192
+    if mapped:
+        coef, G, tabs, oshape, _ = map_case(skv, orc, T, C, 64)
+    else:
+        cfg = gen.CONFIGS[4].with_tokens(T, channels=C)
+        coef, G = gen.dckv_draw(cfg, device="cuda")
+        cc, cgl = gen.dckv_draw(cfg, gen.CALIB, tokens=256)
+        tabs = skv.fit_tables(skv.INT16, skv.CHECKERBOARD, 1, 1, C, cc.numpy(), cgl.numpy(), 256)
+    cont = skv.encode(tabs, coef, G)
+    torch.cuda.synchronize()
+    Gn = G.cpu().numpy()
+    want = orc.decode(tabs.bytes(), cont.cpu().numpy().tobytes(), Gn, Gn, threads=8)
+    assert np.array_equal(want, coef.cpu().numpy())
+    for a, b in [(0, 256), (0, T), (256, 768), (T - 256, T), (512, 1536), (1536, 1792), (0, T - 256)]:
+        say(f"[parity] checkerboard range mapped={mapped}: tokens [{a}, {b})")
+        aux = G[a:min(T, b + 256)].contiguous()
+        out = skv.decode_range(tabs, cont, a, b, aux)
+        assert np.array_equal(out.cpu().numpy(), want[a:b]), (a, b)
+    good = cont.cpu().numpy()
+    n, idx, head = _parse(good.tobytes())
+    ntb, ncg = T // 256, C // 32
+    for ps, detected in [(0, True), (1, False)]:
+        s_ = (ps * ntb + 3) * ncg + 1                     # block 3 (after the range [256, 768)), group 1
+        assert not (idx[s_] >> np.uint64(63))
+        off = int(idx[s_] & np.uint64((1 << 63) - 1))
+        bad = good.copy()
+        bad[head + off + 5] ^= np.uint8(0x40)               # a final state byte
+        say(f"[parity] checkerboard range damage in pass {ps} of the next block")
+        bad_cont = torch.from_numpy(bad).cuda()
+        if detected:
+            with pytest.raises(skv.SkvError) as e:
+                skv.decode_range(tabs, bad_cont, 256, 768, G[256:1024].contiguous())
+            assert e.value.status == skv.ERR_CORRUPT
+        else:
+            out = skv.decode_range(tabs, bad_cont, 256, 768, G[256:1024].contiguous())
+            assert np.array_equal(out.cpu().numpy(), want[256:768])
 
 
 def test_corruption_and_wrong_tables(skv, orc):

@@ -123,7 +123,7 @@ def test_eviction_and_pins_on_device(skv):
 
 def test_insert_and_checkerboard_entries(skv, orc):
     """A container coded elsewhere goes in through reserve/commit (insert); a
-    checkerboard cache is stored and decoded whole, and its ranges are refused."""
+    checkerboard cache is stored, then decoded whole and by 256-token blocks."""
     cfg = gen.Config(130, "store-insert", "bf16", 1, 2, 384, 128)
     t, p = gen.residual_array(cfg, device="cuda")
     tabs = residual_tables(skv, cfg, 0)
@@ -145,9 +145,14 @@ def test_insert_and_checkerboard_entries(skv, orc):
     assert hit.entry == ec and np.array_equal(st.container(hit).cpu().numpy(), want)
     st.release(ec)
     assert torch.equal(st.decode(ctabs, ec, G), coef)
+    # a checkerboard prefix: the side input runs one 256-token block past it
+    assert torch.equal(st.decode(ctabs, ec, G[:768].contiguous(), 0, 512), coef[:512])
+    assert torch.equal(st.decode(ctabs, ec, G[1024:].contiguous(), 1024, 1280), coef[1024:])
     with pytest.raises(skv.SkvError) as ei:
-        st.decode(ctabs, ec, G[:256].contiguous(), 0, 256)
+        st.decode(ctabs, ec, G[:256].contiguous(), 0, 128)
     assert ei.value.status == skv.ERR_SHAPE
+    with pytest.raises(ValueError, match="shape"):
+        st.decode(ctabs, ec, G[:512].contiguous(), 0, 512)
     with pytest.raises(ValueError):
         st.put(ctabs, coef, G, hc[:9])                   # one hash per 128-token block
     assert st.stats()["entries"] == 2
