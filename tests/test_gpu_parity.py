@@ -426,14 +426,15 @@ def test_exponent_mode_full_size_e4m3(skv, orc):
     big_compare(skv, orc, t, p, tabs, oshape, "exponent mode cfg2", min_ratio=4.5)
 
 
-def test_exponent_mode_full_size_bf16(skv, orc):
-    """The Qwen3-0.6B-shaped bf16 cache with exponent-conditioned tables (the
-    tiled bf16 kernels with the slab's 16 class tables): whole container equal
-    to the oracle's, exact round trip."""
-    cfg = gen.CONFIGS[1]
-    say(f"[parity] exponent mode cfg1: generating {cfg.values} values on GPU")
+@pytest.mark.parametrize("cid", [1, 3])
+def test_exponent_mode_full_size_bf16(skv, orc, cid):
+    """The Qwen3-0.6B- and Qwen3-32B-shaped bf16 caches with exponent-conditioned
+    tables (the tiled bf16 kernels with the slab's 16 class tables): whole
+    container equal to the oracle's, exact round trip."""
+    cfg = gen.CONFIGS[cid]
+    say(f"[parity] exponent mode cfg{cid}: generating {cfg.values} values on GPU")
     t, p, tabs, oshape = exp_case(skv, orc, cfg)
-    big_compare(skv, orc, t, p, tabs, oshape, "exponent mode cfg1", min_ratio=2.5)
+    big_compare(skv, orc, t, p, tabs, oshape, f"exponent mode cfg{cid}", min_ratio=2.5)
 
 
 RANGES = [(0, 1024), (0, 128), (896, 1024), (256, 640), (128, 1024)]
