@@ -173,13 +173,26 @@ int skv_load_tables(const void* blob, size_t blob_bytes, void** tables_blob);
  *          whose coded size would reach its raw size is stored raw: its 4096
  *          target elements in (step, lane) order.
  * Two-phase sizing: with d_out == NULL, *out_bytes receives the bound (every
- * stream raw); with d_work == NULL, *work_bytes receives the workspace need.
- * Otherwise out_capacity must hold the container (else SKV_ERR_CAPACITY and
- * *out_bytes = the size needed) and *work_bytes the need.  Blocks the host
+ * stream raw); with d_work == NULL, *work_bytes receives the workspace need
+ * of a single pass over the cache.  Otherwise out_capacity must hold the
+ * container (else SKV_ERR_CAPACITY and *out_bytes = the size needed).  A
+ * workspace smaller than the single-pass need codes the cache in passes of
+ * whole (layer, K|V) slabs, or of whole token blocks of one slab, that fit
+ * in it, one after another into the same workspace; the container is the
+ * same.  Below one token block's need (and, for checkerboard shapes, below
+ * the single-pass need) the call returns SKV_ERR_CAPACITY with *work_bytes
+ * = the smallest workable size (see skv_encode_workspace).  Blocks the host
  * until the container size is known (one stream synchronization). */
 int skv_encode(const void* tables_blob, const skv_shape* s, const void* d_target, const void* d_aux,
                void* d_out, size_t out_capacity, size_t* out_bytes,
                void* d_work, size_t* work_bytes, hipStream_t stream);
+
+/* Encoder workspace for a memory budget (host only; no device call): with
+ * max_bytes == 0 or at least the single-pass need, *work_bytes = that need
+ * and *passes = 1; below it, the workspace skv_encode uses when given
+ * max_bytes and the number of passes it then makes; below the smallest
+ * workable size, SKV_ERR_CAPACITY with *work_bytes = that size. */
+int skv_encode_workspace(const skv_shape* s, uint64_t max_bytes, size_t* work_bytes, uint32_t* passes);
 
 /* Encode without allocating (device), for callers that cannot allocate
  * device memory: code under HIP graph capture, tight serving loops,
@@ -188,9 +201,11 @@ int skv_encode(const void* tables_blob, const skv_shape* s, const void* d_target
  * SKV_NOALLOC_WORK_BYTES that the library keeps on every device it runs on
  * until the process ends, so no workspace argument is taken and nothing is
  * allocated or freed by the call.
- *   - A shape whose workspace (the size skv_encode reports in *work_bytes)
- *     exceeds SKV_NOALLOC_WORK_BYTES returns SKV_ERR_SHAPE (64 MiB holds
- *     about 8,000 e4m3 or 4,000 bf16 / int16 streams of 4096 values).
+ *   - The cache is coded in as many passes as the array needs (as
+ *     skv_encode does with a workspace of SKV_NOALLOC_WORK_BYTES: 64 MiB
+ *     holds about 8,000 e4m3 or 4,000 bf16 streams of 4096 values per
+ *     pass); a checkerboard shape, which takes one pass, whose workspace
+ *     exceeds the array returns SKV_ERR_SHAPE.
  *   - The blob's device tables must already be on the current device (any
  *     earlier skv_encode, skv_decode, skv_decode_range or skv_transfer with
  *     this blob on this device puts them there; building them allocates),

@@ -237,21 +237,23 @@ void skv_free(void* tables_blob) {
     delete b;
 }
 
-// The encoder's launch arguments, its workspace carved from w
-// (encode_need(s) bytes, 256-byte aligned).
+// The encoder's launch arguments for the streams of shape s, its workspace
+// carved from w for `carve` streams (encode_need-sized for all of them,
+// 256-byte aligned).  Set up as a single pass over the whole container.
 static skv::EncodeLaunch encode_launch(const Blob* b, const skv_shape& s, const void* d_target, const void* d_aux,
-                                       void* d_out, size_t out_capacity, uint8_t* w) {
+                                       void* d_out, size_t out_capacity, uint8_t* w, uint64_t carve = 0) {
     const uint64_t n = skv::stream_count(s);
+    const uint64_t m = carve ? carve : n;
     const uint32_t raw = skv::kSyms * skv::elem_bytes(s.dtype);
     skv::EncodeLaunch a{};
     a.target = d_target;
     a.aux = d_aux;
     a.aux_odd = d_aux;
     a.scratch = w;
-    w += align256(2 * n * raw);
+    w += align256(2 * m * raw);
     a.meta = reinterpret_cast<uint32_t*>(w);
-    w += align256(4 * n);
-    const uint64_t nb = (n + 1023) / 1024;
+    w += align256(4 * m);
+    const uint64_t nb = (m + 1023) / 1024;
     a.block_sum = reinterpret_cast<uint32_t*>(w);
     w += align256(4 * nb);
     a.block_off = reinterpret_cast<uint64_t*>(w);
@@ -267,7 +269,133 @@ static skv::EncodeLaunch encode_launch(const Blob* b, const skv_shape& s, const 
     a.blob_hash = b->hash;
     a.shape = s;
     a.n_streams = n;
+    a.sid_base = 0;
+    a.n_total = n;
+    a.pay_base = nullptr;
+    a.last = 1;
+    a.container = s;
     return a;
+}
+
+// A pass of the encoder: whole slabs [slab0, slab0 + nslab) (slab = layer x
+// K|V), or token blocks [tb0, tb0 + ntb) of slab slab0.  Either way a
+// contiguous run of the container's streams.
+struct Pass {
+    uint32_t slab0, nslab, tb0, ntb;
+};
+
+// How a cache is cut into passes: one pass; `step` whole slabs per pass; or
+// `step` token blocks of one slab per pass.  per_pass: the streams a pass's
+// workspace is carved for.
+struct Plan {
+    enum { kOne, kSlabs, kBlocks } kind;
+    uint32_t step, passes;
+    uint64_t per_pass;
+};
+
+static uint32_t token_blocks(const skv_shape& s) {
+    return skv::is_checkerboard(s.mode) ? s.tokens / (2 * skv::kSteps) : s.tokens / skv::kSteps;
+}
+
+static Pass pass_at(const Plan& pl, const skv_shape& s, uint32_t c) {
+    const uint32_t slabs = s.layers * s.kv, ntb = token_blocks(s);
+    if (pl.kind == Plan::kOne) return Pass{0, slabs, 0, ntb};
+    if (pl.kind == Plan::kSlabs) return Pass{c * pl.step, std::min(pl.step, slabs - c * pl.step), 0, ntb};
+    const uint32_t per_slab = (ntb + pl.step - 1) / pl.step;
+    const uint32_t t0 = (c % per_slab) * pl.step;
+    return Pass{c / per_slab, 1, t0, std::min(pl.step, ntb - t0)};
+}
+
+// The fewest passes whose workspace fits in `budget` bytes (0: no limit):
+// one pass when the whole cache fits, else as many whole slabs per pass as
+// fit, else as many token blocks of a slab.  Checkerboard shapes take one
+// pass (the odd tokens are coded against the even ones).  Returns false, with
+// *min_bytes the smallest workspace that works, when nothing fits.
+static bool plan_passes(const skv_shape& s, uint64_t budget, Plan* pl, uint64_t* min_bytes) {
+    const uint64_t n = skv::stream_count(s);
+    const uint32_t raw = skv::kSyms * skv::elem_bytes(s.dtype);
+    const uint32_t slabs = s.layers * s.kv, ncg = s.channels / skv::kLanes, ntb = token_blocks(s);
+    if (budget == 0 || budget >= encode_need(s)) {
+        *pl = Plan{Plan::kOne, 0, 1, n};
+        return true;
+    }
+    *min_bytes = skv::is_checkerboard(s.mode) ? encode_need(s) : skv::encode_work_bytes(ncg, raw);
+    if (skv::is_checkerboard(s.mode)) return false;
+    // the largest stream count whose workspace fits (the size grows with the count)
+    uint64_t lo = 0, hi = n;
+    while (lo < hi) {
+        const uint64_t mid = (lo + hi + 1) / 2;
+        if (skv::encode_work_bytes(mid, raw) <= budget) lo = mid;
+        else hi = mid - 1;
+    }
+    const uint64_t per_slab = uint64_t(ntb) * ncg;
+    if (lo >= per_slab) {
+        const uint32_t k = uint32_t(std::min<uint64_t>(lo / per_slab, slabs));
+        *pl = Plan{Plan::kSlabs, k, (slabs + k - 1) / k, uint64_t(k) * per_slab};
+        return true;
+    }
+    const uint32_t j = uint32_t(lo / ncg);
+    if (j == 0) return false;
+    *pl = Plan{Plan::kBlocks, j, slabs * ((ntb + j - 1) / j), uint64_t(j) * ncg};
+    return true;
+}
+
+// The device tables seen from slab slab0 on (a pass's slab 0).
+static skv::DevTables tables_from_slab(const skv::DevTables& t, const skv_shape& s, uint32_t slab0) {
+    skv::DevTables u = t;
+    if (slab0 == 0) return u;
+    const uint64_t off = uint64_t(slab0) * (s.mode == SKV_RESIDUAL_EXP ? skv::kExpClasses : s.channels);
+    u.n_tables -= uint32_t(off);
+    if (u.n) u.n += off;
+    if (u.enc) u.enc += off * 256;
+    if (u.fc) u.fc += off * 256;
+    if (u.slot) u.slot += off * skv::kM;
+    if (u.base) u.base += slab0;
+    return u;
+}
+
+// Code the cache in the planned passes, each into the same workspace, and
+// pack every pass's streams into d_out; *payload receives the payload size.
+// A pass's payload offset carries over on the device (two running totals,
+// alternating), so the host waits once, at the end: through the pinned
+// staging buffer, or (plain) a plain copy and a stream synchronization, which
+// allocate nothing.
+static int encode_passes(const Blob* b, const skv_shape& s, const skv::DevTables& t, const Plan& plan,
+                         const void* d_target, const void* d_aux, void* d_out, size_t out_capacity, uint8_t* w,
+                         hipStream_t stream, uint64_t* payload, bool plain = false) {
+    const uint32_t eb = skv::elem_bytes(s.dtype);
+    const uint32_t ncg = s.channels / skv::kLanes, ntb = token_blocks(s);
+    const uint64_t n = skv::stream_count(s);
+    const uint64_t* slots = nullptr;
+    for (uint32_t c = 0; c < plan.passes; ++c) {
+        const Pass p = pass_at(plan, s, c);
+        skv_shape ps = s;
+        if (plan.kind != Plan::kOne) {
+            ps.layers = p.nslab;
+            ps.kv = 1;
+            ps.tokens = p.ntb * skv::kSteps;
+        }
+        const size_t off = (size_t(p.slab0) * s.tokens + size_t(p.tb0) * skv::kSteps) * s.channels * eb;
+        skv::EncodeLaunch a = encode_launch(b, ps, static_cast<const uint8_t*>(d_target) + off,
+                                            static_cast<const uint8_t*>(d_aux) + off, d_out, out_capacity, w,
+                                            plan.per_pass);
+        uint64_t* tot = a.total;
+        slots = tot;
+        a.total = tot + ((c + 1) & 1);
+        a.pay_base = c ? tot + (c & 1) : nullptr;
+        a.sid_base = (uint64_t(p.slab0) * ntb + p.tb0) * ncg;
+        a.n_total = n;
+        a.last = c + 1 == plan.passes;
+        a.container = s;
+        const skv::DevTables u = tables_from_slab(t, s, p.slab0);
+        if (skv::launch_encode(a, u, stream) != hipSuccess) return SKV_ERR_DEVICE;
+    }
+    const uint64_t* fin = slots + (plan.passes & 1);
+    if (!plain) return read_back(payload, fin, 8, stream);
+    if (hipMemcpyAsync(payload, fin, 8, hipMemcpyDeviceToHost, stream) != hipSuccess ||
+        hipStreamSynchronize(stream) != hipSuccess)
+        return SKV_ERR_DEVICE;
+    return SKV_OK;
 }
 
 static int encode_impl(const void* tables_blob, const skv_shape* s, const void* d_target, const void* d_aux,
@@ -287,8 +415,10 @@ static int encode_impl(const void* tables_blob, const skv_shape* s, const void* 
         if (!d_work) *work_bytes = need;
         return SKV_OK;
     }
-    if (*work_bytes < need) {
-        *work_bytes = need;
+    Plan plan{};
+    uint64_t min_bytes = 0;
+    if (!plan_passes(*s, *work_bytes, &plan, &min_bytes)) {
+        *work_bytes = min_bytes;
         return SKV_ERR_CAPACITY;
     }
     if (!d_target || !d_aux) return SKV_ERR_ARG;
@@ -296,11 +426,10 @@ static int encode_impl(const void* tables_blob, const skv_shape* s, const void* 
     int rc = device_tables(b, stream, &t);
     if (rc != SKV_OK) return rc;
 
-    skv::EncodeLaunch a = encode_launch(b, *s, d_target, d_aux, d_out, out_capacity, static_cast<uint8_t*>(d_work));
     if (timing) skv::timing_reset();
-    if (skv::launch_encode(a, *t, stream) != hipSuccess) return SKV_ERR_DEVICE;
     uint64_t payload = 0;
-    rc = read_back(&payload, a.total, 8, stream);
+    rc = encode_passes(b, *s, *t, plan, d_target, d_aux, d_out, out_capacity, static_cast<uint8_t*>(d_work), stream,
+                       &payload);
     if (rc != SKV_OK) return rc;
     if (timing) skv::timing_collect();
     const uint64_t total = skv::kHeaderBytes + 8 * (n + 1) + payload;
@@ -314,6 +443,21 @@ int skv_encode(const void* tables_blob, const skv_shape* s, const void* d_target
                        true);
 }
 
+int skv_encode_workspace(const skv_shape* s, uint64_t max_bytes, size_t* work_bytes, uint32_t* passes) {
+    if (!s || !work_bytes || !passes) return SKV_ERR_ARG;
+    if (!skv::shape_supported(*s, true)) return SKV_ERR_SHAPE;
+    Plan plan{};
+    uint64_t min_bytes = 0;
+    if (!plan_passes(*s, max_bytes, &plan, &min_bytes)) {
+        *work_bytes = min_bytes;
+        return SKV_ERR_CAPACITY;
+    }
+    *work_bytes = plan.kind == Plan::kOne ? encode_need(*s)
+                                          : skv::encode_work_bytes(plan.per_pass, skv::kSyms * skv::elem_bytes(s->dtype));
+    *passes = plan.passes;
+    return SKV_OK;
+}
+
 int skv_encode_noalloc(const void* tables_blob, const skv_shape* s, const void* d_target, const void* d_aux,
                        void* d_out, size_t out_capacity, size_t* out_bytes, hipStream_t stream) {
     if (!tables_blob || !s || !out_bytes) return SKV_ERR_ARG;
@@ -324,7 +468,9 @@ int skv_encode_noalloc(const void* tables_blob, const skv_shape* s, const void* 
     const uint64_t n = skv::stream_count(*s);
     const uint32_t raw = skv::kSyms * skv::elem_bytes(s->dtype);
     const uint64_t bound = skv::kHeaderBytes + 8 * (n + 1) + n * raw;
-    if (encode_need(*s) > skv::kNoAllocWorkBytes) return SKV_ERR_SHAPE;
+    Plan plan{};
+    uint64_t min_bytes = 0;
+    if (!plan_passes(*s, skv::kNoAllocWorkBytes, &plan, &min_bytes)) return SKV_ERR_SHAPE;
     if (!d_out) {
         *out_bytes = bound;
         return SKV_OK;
@@ -344,15 +490,10 @@ int skv_encode_noalloc(const void* tables_blob, const skv_shape* s, const void* 
     std::lock_guard<std::mutex> lk(skv::noalloc_lock(dev));
     uint8_t* w = nullptr;
     if (skv::noalloc_workspace(dev, &w) != hipSuccess) return SKV_ERR_DEVICE;
-    skv::EncodeLaunch a = encode_launch(b, *s, d_target, d_aux, d_out, out_capacity, w);
     skv::timing_reset();
-    if (skv::launch_encode(a, *t, stream) != hipSuccess) return SKV_ERR_DEVICE;
-    // the size through a plain copy and a stream synchronization (the pinned
-    // staging buffer of the other calls is allocated on a thread's first use)
     uint64_t payload = 0;
-    if (hipMemcpyAsync(&payload, a.total, 8, hipMemcpyDeviceToHost, stream) != hipSuccess ||
-        hipStreamSynchronize(stream) != hipSuccess)
-        return SKV_ERR_DEVICE;
+    const int rc = encode_passes(b, *s, *t, plan, d_target, d_aux, d_out, out_capacity, w, stream, &payload, true);
+    if (rc != SKV_OK) return rc;
     skv::timing_collect();
     const uint64_t total = skv::kHeaderBytes + 8 * (n + 1) + payload;
     *out_bytes = total;

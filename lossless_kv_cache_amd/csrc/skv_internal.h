@@ -113,8 +113,18 @@ struct EncodeLaunch {
     uint8_t* out;           // container
     uint64_t out_capacity;
     uint64_t blob_hash;
-    skv_shape shape;
+    skv_shape shape;         // of the streams coded by this launch (a chunk of the container's)
     uint64_t n_streams;
+    // A cache coded a chunk at a time (a contiguous run of its streams per launch):
+    // the chunk's first stream in the container, the container's stream count and
+    // shape, the payload offset of the chunk's first stream (device; null = 0; the
+    // chunk's running total lands in *total), and whether the chunk is the last
+    // (which writes the header and the final index entry).
+    uint64_t sid_base;
+    uint64_t n_total;
+    const uint64_t* pay_base;
+    uint32_t last;
+    skv_shape container;
 };
 
 struct DecodeLaunch {

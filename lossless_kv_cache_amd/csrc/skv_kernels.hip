@@ -417,12 +417,13 @@ __global__ __launch_bounds__(kScanBlock) void stream_block_sums(const uint32_t* 
     }
 }
 
-// Exclusive scan of the block sums by one workgroup, chunk by chunk.
+// Exclusive scan of the block sums by one workgroup, a kScanBlock run at a
+// time, starting from *base (the payload before this chunk of streams; null: 0).
 __global__ __launch_bounds__(kScanBlock) void stream_block_scan(const uint32_t* bsum, uint32_t nb, uint64_t* boff,
-                                                               uint64_t* total) {
+                                                               uint64_t* total, const uint64_t* base0) {
     __shared__ uint64_t wsum[kScanBlock / 64];
     __shared__ uint64_t carry;
-    if (threadIdx.x == 0) carry = 0;
+    if (threadIdx.x == 0) carry = base0 ? *base0 : 0ull;
     __syncthreads();
     const uint32_t lane = threadIdx.x & 63u, w = threadIdx.x >> 6;
     for (uint32_t base = 0; base < nb; base += kScanBlock) {
@@ -450,8 +451,8 @@ __global__ __launch_bounds__(kScanBlock) void place_streams(EncodeLaunch a, cons
     __shared__ uint32_t wsum[kScanBlock / 64];
     constexpr uint32_t EB = DT == SKV_E4M3 ? 1u : 2u;
     constexpr uint32_t RAW = kSyms * EB;
-    const uint64_t n = a.n_streams;
-    const uint64_t head = kHeaderBytes + 8 * (n + 1);
+    const uint64_t n = a.n_streams, N = a.n_total;
+    const uint64_t head = kHeaderBytes + 8 * (N + 1);
     const uint64_t total = *a.total;
     if (head + total > a.out_capacity) return;        // caller reports SKV_ERR_CAPACITY
     const uint32_t lane = threadIdx.x & 63u, w = threadIdx.x >> 6;
@@ -469,17 +470,18 @@ __global__ __launch_bounds__(kScanBlock) void place_streams(EncodeLaunch a, cons
     uint64_t off = boff[blockIdx.x];
     for (uint32_t q = 0; q < w; ++q) off += wsum[q];
     off += incl - v;
-    uint64_t* index = reinterpret_cast<uint64_t*>(a.out + kHeaderBytes);
+    uint64_t* index = reinterpret_cast<uint64_t*>(a.out + kHeaderBytes) + a.sid_base;
     if (i < n) index[i] = off | (uint64_t(m >> 31) << 63);
-    if (i == n - 1) index[n] = total;
-    if (i == 0) {
+    if (a.last && i == n - 1) index[n] = total;
+    if (a.last && i == 0) {
         uint8_t* h = a.out;
+        const skv_shape& cs = a.container;
         const uint32_t words[16] = {
             0x31564B53u,                                                    // "SKV1"
-            1u | (a.shape.dtype << 16) | (a.shape.mode << 24),
+            1u | (cs.dtype << 16) | (cs.mode << 24),
             kProbBits | (uint32_t(kLanes) << 8) | (uint32_t(kSteps) << 16),
-            a.shape.layers, a.shape.kv, a.shape.tokens, a.shape.channels, 0u,
-            uint32_t(n), uint32_t(n >> 32),
+            cs.layers, cs.kv, cs.tokens, cs.channels, 0u,
+            uint32_t(N), uint32_t(N >> 32),
             uint32_t(a.blob_hash), uint32_t(a.blob_hash >> 32),
             uint32_t(total), uint32_t(total >> 32), 0u, 0u};
         for (int q = 0; q < 16; ++q) reinterpret_cast<uint32_t*>(h)[q] = words[q];
@@ -499,10 +501,10 @@ __global__ __launch_bounds__(256) void copy_streams(EncodeLaunch a) {
     const uint64_t n = a.n_streams;
     const uint64_t sid = uint64_t(blockIdx.x) * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     if (sid >= n) return;
-    const uint64_t head = kHeaderBytes + 8 * (n + 1);
+    const uint64_t head = kHeaderBytes + 8 * (a.n_total + 1);
     if (head + *a.total > a.out_capacity) return;        // caller reports SKV_ERR_CAPACITY
     const uint32_t lane = threadIdx.x & 63u;
-    const uint64_t* index = reinterpret_cast<const uint64_t*>(a.out + kHeaderBytes);
+    const uint64_t* index = reinterpret_cast<const uint64_t*>(a.out + kHeaderBytes) + a.sid_base;
     uint8_t* dst = a.out + head + (index[sid] & ~kRawBit);
     const uint32_t ms = a.meta[sid];
     const uint8_t* src = a.scratch + sid * (2 * RAW);
@@ -3537,7 +3539,8 @@ hipError_t encode_code(const EncodeLaunch& a, const DevTables& t, hipStream_t st
                            kSyms * (DT == SKV_E4M3 ? 1u : 2u), a.block_sum);
     });
     timed("stream_block_scan", st, [&](hipEvent_t e0, hipEvent_t e1) {
-        hipExtLaunchKernelGGL(stream_block_scan, dim3(1), dim3(kScanBlock), 0, st, e0, e1, 0, a.block_sum, nb, a.block_off, a.total);
+        hipExtLaunchKernelGGL(stream_block_scan, dim3(1), dim3(kScanBlock), 0, st, e0, e1, 0, a.block_sum, nb, a.block_off,
+                              a.total, a.pay_base);
     });
     return hipGetLastError();
 }

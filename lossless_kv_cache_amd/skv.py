@@ -80,6 +80,8 @@ def lib():
         L.skv_load_tables.argtypes = [vp, sz, ctypes.POINTER(vp)]
         L.skv_encode.restype = ctypes.c_int
         L.skv_encode.argtypes = [vp, sp, vp, vp, vp, sz, psz, vp, psz, vp]
+        L.skv_encode_workspace.restype = ctypes.c_int
+        L.skv_encode_workspace.argtypes = [sp, ctypes.c_uint64, psz, ctypes.POINTER(u32)]
         L.skv_encode_noalloc.restype = ctypes.c_int
         L.skv_encode_noalloc.argtypes = [vp, sp, vp, vp, vp, sz, psz, vp]
         L.skv_decode.restype = ctypes.c_int
@@ -307,18 +309,31 @@ def tokens_of(tables: Tables, target: torch.Tensor) -> int:
     return target.shape[2]
 
 
-class Encoder:
-    """Encodes repeatedly with one set of tables, reusing its buffers."""
+def encode_workspace(tables: Tables, tokens: int, max_bytes: int = 0) -> tuple[int, int]:
+    """(workspace bytes, passes) of an encode of `tokens` tokens within
+    max_bytes of workspace (0: a single pass)."""
+    shape = tables.shape(tokens)
+    wb, ps = ctypes.c_size_t(), ctypes.c_uint32()
+    _check(lib().skv_encode_workspace(ctypes.byref(shape), max_bytes, ctypes.byref(wb), ctypes.byref(ps)),
+           "skv_encode_workspace")
+    return wb.value, ps.value
 
-    def __init__(self, tables: Tables, tokens: int, device=None):
+
+class Encoder:
+    """Encodes repeatedly with one set of tables, reusing its buffers; with
+    max_work_bytes the workspace stays within that budget (the cache is then
+    coded in passes)."""
+
+    def __init__(self, tables: Tables, tokens: int, device=None, max_work_bytes: int = 0):
         self.tables = tables
         self.shape = tables.shape(tokens)
         dev = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
         ob, wb = ctypes.c_size_t(), ctypes.c_size_t()
         _check(lib().skv_encode(tables.ptr, ctypes.byref(self.shape), None, None, None, 0, ctypes.byref(ob), None,
                                 ctypes.byref(wb), None), "skv_encode(size query)")
+        work_bytes, self.passes = encode_workspace(tables, tokens, max_work_bytes)
         self.out = torch.empty(ob.value, dtype=torch.uint8, device=dev)
-        self.work = torch.empty(wb.value, dtype=torch.uint8, device=dev)
+        self.work = torch.empty(work_bytes, dtype=torch.uint8, device=dev)
 
     def __call__(self, target: torch.Tensor, aux: torch.Tensor) -> torch.Tensor:
         """Returns a view of the container (valid until the next call)."""
@@ -361,8 +376,8 @@ def encode_noalloc(tables: Tables, target: torch.Tensor, aux: torch.Tensor, out:
 
 
 def encode_noalloc_bound(tables: Tables, tokens: int) -> int:
-    """Container bound for encode_noalloc (raises SkvError(ERR_SHAPE) when the
-    shape's workspace exceeds the fixed array)."""
+    """Container bound for encode_noalloc (raises SkvError(ERR_SHAPE) for a
+    checkerboard shape whose single-pass workspace exceeds the fixed array)."""
     shape = tables.shape(tokens)
     ob = ctypes.c_size_t()
     _check(lib().skv_encode_noalloc(tables.ptr, ctypes.byref(shape), None, None, None, 0, ctypes.byref(ob), None),

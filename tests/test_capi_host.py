@@ -229,9 +229,9 @@ def test_binding_refuses_mis_sized_device_inputs(skv):
 
 
 def test_noalloc_size_limits_on_host(skv):
-    """skv_encode_noalloc's size checks need no device: a shape whose
-    workspace fits the fixed array reports the same bound as skv_encode, a
-    larger one is refused with SKV_ERR_SHAPE."""
+    """skv_encode_noalloc's size checks need no device: any residual shape
+    reports the same bound as skv_encode (larger ones are coded in passes); a
+    checkerboard shape past the fixed array is refused with SKV_ERR_SHAPE."""
     tabs = _small_tables(skv, skv.E4M3, skv.RESIDUAL, layers=1, channels=1024)
     for tokens in (128, 1024, 4096):
         s = tabs.shape(tokens)
@@ -240,9 +240,17 @@ def test_noalloc_size_limits_on_host(skv):
                                     ctypes.byref(wb), None) == 0
         assert wb.value <= skv.NOALLOC_WORK_BYTES
         assert skv.encode_noalloc_bound(tabs, tokens) == ob.value
-    # 32768 tokens x 1024 channels x K,V: 16384 streams of 8 KiB scratch each
+    # 32768 tokens x 1024 channels x K,V: 16384 streams of 8 KiB scratch each, coded in passes
+    s = tabs.shape(32768)
+    ob = ctypes.c_size_t()
+    assert skv.lib().skv_encode(tabs.ptr, ctypes.byref(s), None, None, None, 0, ctypes.byref(ob), None,
+                                ctypes.byref(ctypes.c_size_t()), None) == 0
+    assert skv.encode_noalloc_bound(tabs, 32768) == ob.value
+    assert skv.encode_workspace(tabs, 32768, skv.NOALLOC_WORK_BYTES)[1] == 4
+    # a checkerboard shape takes one pass: past the array it is refused
+    tc = _small_tables(skv, skv.INT16, skv.CHECKERBOARD, channels=2048)
     with pytest.raises(skv.SkvError) as e:
-        skv.encode_noalloc_bound(tabs, 32768)
+        skv.encode_noalloc_bound(tc, 32768)
     assert e.value.status == skv.ERR_SHAPE
 
 
@@ -291,3 +299,37 @@ def test_range_workspace_sizing_on_host(skv):
         assert wb.value == 256
         assert skv.range_aux_tokens(tabs, 1024, 256, 512) == (512 if extra else 256)
         assert skv.range_aux_tokens(tabs, 1024, 512, 1024) == 512
+
+
+def test_encode_workspace_plans(skv):
+    """Workspace budgets (host only): at or above the single-pass need, one
+    pass of that size; below it, passes of whole slabs, then of token blocks
+    of one slab, each within the budget and more of them as it shrinks;
+    below one token block (or, for checkerboard shapes, below one pass)
+    SKV_ERR_CAPACITY with the smallest workable size."""
+    tabs = _small_tables(skv, skv.E4M3, skv.RESIDUAL, layers=2, channels=256)   # 4 slabs of 16 blocks x 8 groups
+    T = 2048
+    full, p1 = skv.encode_workspace(tabs, T)
+    assert p1 == 1 and skv.encode_workspace(tabs, T, full) == (full, 1)
+    raw = 4096
+    per_stream = 2 * raw + 4                              # scratch and size word per stream
+    seen = []
+    for budget in (full - 1, full // 2, full // 4 + 4096, full // 5, full // 16, full // 40, 9 * per_stream):
+        wb, passes = skv.encode_workspace(tabs, T, budget)
+        assert wb <= budget and passes > 1, budget
+        seen.append(passes)
+    assert seen == sorted(seen)
+    assert skv.encode_workspace(tabs, T, full // 4 + 4096)[1] == 4          # one slab per pass
+    assert skv.encode_workspace(tabs, T, full // 5)[1] == 4 * 2             # 12 + 4 token blocks
+    smallest = skv.encode_workspace(tabs, T, 1 << 30)[0]
+    with pytest.raises(skv.SkvError) as e:
+        skv.encode_workspace(tabs, T, 8 * per_stream - 1)
+    assert e.value.status == skv.ERR_CAPACITY
+    wb, passes = skv.encode_workspace(tabs, T, 8 * per_stream + 2048)
+    assert passes == 4 * 16 and wb <= 8 * per_stream + 2048                # one token block per pass
+    assert smallest == full
+    tc = _small_tables(skv, skv.INT16, skv.CHECKERBOARD, channels=64)
+    cfull, _ = skv.encode_workspace(tc, 2048)
+    with pytest.raises(skv.SkvError) as e:
+        skv.encode_workspace(tc, 2048, cfull - 1)
+    assert e.value.status == skv.ERR_CAPACITY

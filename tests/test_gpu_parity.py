@@ -9,6 +9,7 @@ differs').  Every case, the full-size workloads included, compares the
 whole container (header, index, payload) with the oracle's, byte for byte,
 and checks the exact GPU round trip.
 """
+import ctypes
 import os
 import struct
 import sys
@@ -758,3 +759,41 @@ def test_transfer_full_size_e4m3(skv, orc):
         want = orc.encode_array(blob, oshape, tn[l0:l1], pn[l0:l1], threads=ORACLE_THREADS)
         assert_same_container(w[offs[c]:offs[c + 1]], want, f"transfer chunk {c}")
         say(f"[parity] transfer cfg2: chunk {c} identical to the oracle's")
+
+
+@pytest.mark.parametrize("dtype,mode", [("e4m3", 0), ("bf16", 0), ("e4m3", 2), ("bf16", 2)])
+def test_encode_in_passes(skv, orc, dtype, mode):
+    """A workspace below the single-pass need codes the cache in passes (whole
+    slabs, with a ragged last pass; token blocks of one slab; one block per
+    pass), each into the same workspace: every container equals the oracle's
+    byte for byte, and an output too small is refused with the size needed."""
+    cfg = gen.Config(98, f"passes-{dtype}", dtype, 3, 2, 2048, 256, outliers=dtype == "bf16")
+    t, p = gen.residual_array(cfg, device="cuda")
+    ct, cp = gen.residual_array(cfg, gen.CALIB, tokens=256)
+    dt = _dt(cfg, skv)
+    tabs = skv.fit_tables(dt, mode, cfg.layers, cfg.kv, cfg.channels, ct.numpy(), cp.numpy(), 256)
+    oshape = orc.make_shape(dt, mode, cfg.layers, cfg.kv, cfg.tokens, cfg.channels)
+    want = orc.encode_array(tabs.bytes(), oshape, t.cpu().numpy(), p.cpu().numpy(), threads=ORACLE_THREADS)
+    T = cfg.tokens
+    full, _ = skv.encode_workspace(tabs, T)
+    per_block = 8 * 2 * 4096 * cfg.elem_bytes + 4096       # 8 channel groups of scratch, with room for the rest
+    seen = set()
+    for budget in (0, full * 2 // 3 + 4096, full // 2, full // 4, full // 7, full // 20, per_block):
+        wb, passes = skv.encode_workspace(tabs, T, budget)
+        enc = skv.Encoder(tabs, T, max_work_bytes=budget)
+        assert enc.passes == passes and enc.work.numel() == wb
+        say(f"[parity] {dtype} mode {mode}: {passes} passes in {wb} B of workspace")
+        got = enc(t, p)
+        assert_same_container(host_u8(got), want, f"{dtype} mode {mode}, {passes} passes")
+        seen.add(passes)
+        if passes > 1:
+            with pytest.raises(skv.SkvError) as e:
+                lib_out = torch.empty(1000, dtype=torch.uint8, device="cuda")
+                ob, wbuf = ctypes.c_size_t(), ctypes.c_size_t(enc.work.numel())
+                shape = tabs.shape(T)
+                skv._check(skv.lib().skv_encode(tabs.ptr, ctypes.byref(shape), t.data_ptr(), p.data_ptr(),
+                                                lib_out.data_ptr(), lib_out.numel(), ctypes.byref(ob),
+                                                enc.work.data_ptr(), ctypes.byref(wbuf), skv._stream()), "skv_encode")
+            assert e.value.status == skv.ERR_CAPACITY and ob.value == want.size
+    assert len(seen) >= 6, seen
+    assert torch.equal(skv.decode(tabs, got, p), t)

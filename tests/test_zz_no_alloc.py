@@ -3,8 +3,9 @@ callers that cannot allocate device memory.  Called through the C ABI, its
 container equals skv_encode's byte for byte and decodes exactly, on two
 calls in a row with the second input smaller and different (the fixed
 workspace keeps the first call's contents, which the second must not
-read); shapes past the fixed workspace and tables not yet on the device are
-refused before anything is launched.
+read); shapes larger than one pass of the fixed workspace are coded in
+several passes; a checkerboard shape past it and tables not yet on the
+device are refused before anything is launched.
 """
 import sys
 
@@ -59,8 +60,12 @@ def _inputs(skv, kind, tokens, purpose):
     return gen.residual_array(cfg, purpose, device="cuda")
 
 
-# (kind, tokens of the first call, tokens of the second, smaller call)
-CASES = [("bf16", 1024, 256), ("e4m3", 1024, 384), ("exp-e4m3", 896, 128), ("checkerboard", 4096, 1024)]
+# (kind, tokens of the first call, tokens of the second, smaller call).  The
+# first calls of the last two exceed one pass of the fixed array: 8192 bf16
+# tokens take one whole slab per pass, 32768 e4m3 tokens 255 + 1 token blocks
+# of each slab.
+CASES = [("bf16", 1024, 256), ("e4m3", 1024, 384), ("exp-e4m3", 896, 128), ("checkerboard", 4096, 1024),
+         ("bf16", 8192, 1024), ("e4m3", 32768, 512)]
 
 
 @pytest.mark.parametrize("kind,big,small", CASES)
@@ -84,8 +89,8 @@ def test_noalloc_equals_encode(skv, kind, big, small):
 
 
 def test_noalloc_refusals(skv):
-    # a shape whose workspace exceeds the fixed array
-    tabs = _tables(skv, "e4m3")
+    # a checkerboard shape (one pass) whose workspace exceeds the fixed array
+    tabs = _tables(skv, "checkerboard")
     with pytest.raises(skv.SkvError) as e:
         skv.encode_noalloc_bound(tabs, 32768)
     assert e.value.status == skv.ERR_SHAPE
