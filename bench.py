@@ -54,6 +54,8 @@ def main() -> int:
                     help="layers per chunk of the transfer-pipeline measurement (0 = skip it)")
     ap.add_argument("--no-copy-probe", action="store_true",
                     help="skip timing a plain device copy of the cache (HBM ceiling; counter scale reference)")
+    ap.add_argument("--no-store-probe", action="store_true",
+                    help="skip the prefix-cache store measurement (put, shared-prefix decode, hit-rate trace)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the coding path has no multi-GPU part "
@@ -238,6 +240,12 @@ def main() -> int:
         del out
         xfer = transfer_probe(skv, cfg, tabs, tgt, prd, min(args.transfer_layers, cfg.layers))
 
+    store = None
+    if not cb and not args.no_store_probe:
+        store = store_probe(skv, cfg, tabs, tgt, prd)
+        log(f"prefix store: put {store['put_ms']} ms, shared-prefix decode {store['lookup_and_decode_ms']} ms, "
+            f"hit rate coded {store['trace']['coded']['hit_rate']} vs raw {store['trace']['raw']['hit_rate']}")
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = (cpu_baseline_cb if cb else cpu_baseline)(cfg, tabs, tgt, prd, args.cpu_seconds)
@@ -272,10 +280,11 @@ def main() -> int:
         "copy_ceiling": copy,
         "range_decode": part,
         "transfer": xfer,
+        "prefix_store": store,
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)
-    return 0 if ok else 1
+    return 0 if ok and (store is None or store["verified"]) else 1
 
 
 def transfer_probe(skv, cfg, tabs, tgt, prd, layers_per_chunk, reps=3):
@@ -343,6 +352,96 @@ def transfer_probe(skv, cfg, tabs, tgt, prd, layers_per_chunk, reps=3):
             "raw_overlapped_copy_GBps": round(raw / (piped_ms / 1e3) / 1e9, 2),
             "speedup_vs_raw_copy": round(raw_ms / ms, 3),
             "speedup_vs_raw_overlapped_copy": round(piped_ms / ms, 3), "verified": ok}
+
+
+def store_probe(skv, cfg, tabs, tgt, prd, prefix_tokens=4096, prompts=64, requests=2000, zipf=1.0, seed=7,
+                reps=5):
+    """The prefix-cache store on the same cache: putting a prefix of
+    `prefix_tokens` tokens (encode straight into the arena), looking up and
+    decoding the part of it a new request shares (half its blocks), and a
+    seeded request trace -- `prompts` prefixes drawn with Zipf popularity,
+    a miss inserting the prefix -- replayed against two arenas of the same
+    size (four raw prefixes), one holding coded prefixes and one holding raw
+    ones (bookkeeping only), for the hit rate each reaches."""
+    import numpy as np
+    import torch
+
+    T = min(prefix_tokens, cfg.tokens)
+    t = tgt[:, :, :T].contiguous()
+    p = prd[:, :, :T].contiguous()
+    raw = t.numel() * t.element_size()
+    rng = np.random.default_rng(seed)
+    ids = rng.integers(0, 150000, T)
+    h = skv.block_hashes(ids)
+    arena_bytes = -(-4 * raw // 256) * 256
+    st = skv.Store(arena_bytes=arena_bytes)
+    put_ms = []
+    for _ in range(reps + 1):
+        torch.cuda.synchronize()
+        a = time.perf_counter()
+        entry, nbytes = st.put(tabs, t, p, h)
+        put_ms.append((time.perf_counter() - a) * 1e3)
+        if len(put_ms) <= reps:
+            st.erase(entry)
+    put = sorted(put_ms[1:])[len(put_ms[1:]) // 2]
+    # a request sharing the first half of the prefix's blocks
+    q = ids.copy()
+    q[T // 2 + 5] += 1
+    half = T // 2
+    pr = p[:, :, :half].contiguous()
+    out = torch.empty_like(pr)
+    dec_ms = []
+    ok = True
+    for _ in range(reps + 1):
+        torch.cuda.synchronize()
+        a = time.perf_counter()
+        hit = st.lookup(skv.block_hashes(q))
+        st.decode_into(tabs, hit.entry, pr, out, 0, 128 * hit.matched_blocks)
+        st.release(hit.entry)
+        torch.cuda.synchronize()
+        dec_ms.append((time.perf_counter() - a) * 1e3)
+        ok = ok and hit.matched_blocks == half // 128
+    ok = ok and bool(torch.equal(out, t[:, :, :half]))
+    dec = sorted(dec_ms[1:])[len(dec_ms[1:]) // 2]
+    cont = st.container(st.lookup(h)).clone()
+    # the trace: the same requests against coded and raw prefixes in arenas of one size
+    ranks = np.arange(1, prompts + 1, dtype=np.float64)
+    pop = ranks ** -zipf
+    pop /= pop.sum()
+    draws = rng.choice(prompts, size=requests, p=pop)
+    keys = [skv.block_hashes(rng.integers(0, 150000, T)) for _ in range(prompts)]
+    coded = skv.Store(arena_bytes=arena_bytes)
+    base = torch.empty(arena_bytes + 256, dtype=torch.uint8)
+    off = (-base.data_ptr()) % 256
+    rawst = skv.Store(arena=base[off:off + arena_bytes])
+    res = {}
+    for name, store in (("coded", coded), ("raw", rawst)):
+        hits = 0
+        for k in draws:
+            hit = store.lookup(keys[k])
+            if hit.matched_blocks == len(keys[k]):
+                hits += 1
+                store.release(hit.entry)
+                continue
+            if hit.entry:
+                store.release(hit.entry)
+            if name == "coded":
+                store.insert(cont, keys[k])
+            else:
+                e, _ = store.reserve(raw, keys[k])
+                store.commit(e, raw, tokens=T)
+        res[name] = {"hit_rate": round(hits / requests, 4), "entries_resident": store.stats()["entries"],
+                     "evictions": store.stats()["evictions"]}
+    st.close()
+    coded.close()
+    rawst.close()
+    return {"prefix_tokens": T, "prefix_raw_bytes": raw, "container_bytes": int(nbytes),
+            "put_ms": round(put, 3), "put_GBps": round(raw / (put / 1e3) / 1e9, 1),
+            "shared_prefix_tokens": half, "lookup_and_decode_ms": round(dec, 3),
+            "lookup_and_decode_GBps": round(t.numel() * t.element_size() / 2 / (dec / 1e3) / 1e9, 1),
+            "verified": ok,
+            "trace": {"arena_bytes": arena_bytes, "prompts": prompts, "requests": requests, "zipf": zipf,
+                      "coded": res["coded"], "raw": res["raw"]}}
 
 
 def host_cpus() -> dict:
