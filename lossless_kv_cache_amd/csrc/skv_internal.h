@@ -93,6 +93,8 @@ struct DevTables {
     uint32_t* fc = nullptr;        // [n_tables][256] freq | cum<<16
     uint8_t* slot = nullptr;       // [n_tables][4096] slot -> symbol
     uint8_t* half = nullptr;       // checkerboard blobs: [n_tables][2048] symbol of every even slot
+    uint2* enc8 = nullptr;         // checkerboard blobs: [n_tables][256] encode entries packed in 8 bytes:
+                                   // {magic, f | start << 12 | shift << 24 | inc << 29 | escape << 30}
     uint8_t* base = nullptr;       // exponent-mode blobs: [slabs] class base
     // decoded-neighbour-map blobs: the map (rank 0 otherwise)
     uint32_t map_rank = 0, map_sh_h = 0, map_sh_m = 0;

@@ -101,7 +101,7 @@ __device__ __forceinline__ uint32_t unzig(uint32_t z) { return (z >> 1) ^ (0u - 
 
 // --------------------------------------------------------------- tables
 __global__ __launch_bounds__(256) void expand_tables(const uint8_t* rec, uint32_t* tn, uint4* enc, uint32_t* fc,
-                                                     uint8_t* slot, uint8_t* half) {
+                                                     uint8_t* slot, uint8_t* half, uint2* enc8) {
     __shared__ uint32_t cum[257];
     const uint32_t j = blockIdx.x, tid = threadIdx.x;
     const uint8_t* r = rec + size_t(j) * kTableRecord;
@@ -160,6 +160,10 @@ __global__ __launch_bounds__(256) void expand_tables(const uint8_t* rec, uint32_
         e.w = l | (c << 16) | (tid >= n ? 0x100u : 0u);
     }
     enc[size_t(j) * 256 + tid] = e;
+    // the same entry in 8 bytes (checkerboard tables: f < 4096, start < 4096, shift < 12)
+    if (enc8)
+        enc8[size_t(j) * 256 + tid] = make_uint2(e.y, (e.x >> 20) | ((e.w >> 16) << 12) | ((e.w & 31u) << 24) |
+                                                          ((e.z >> 24) << 29) | (((e.w >> 8) & 1u) << 30));
     // checkerboard tables (the ones with half maps) flag their escape symbol in bit 15 (f < 4096)
     fc[size_t(j) * 256 + tid] = f | (c << 16) | (half && tid == n ? 0x8000u : 0u);
     uint8_t* st = slot + size_t(j) * kM;
@@ -271,12 +275,23 @@ __global__ __launch_bounds__(256) void encode_streams(EncodeLaunch a, DevTables 
 // (round-robin over the 8 XCDs) sweep one channel group after another, so the
 // tables an XCD reads at a time (16 per component) stay in its L2.  Returns
 // false for a half-wave past the pass's last token block.
-__device__ __forceinline__ bool cb_stream(const Geo& g, uint64_t first, uint64_t& sid) {
-    const uint32_t bpc = (g.ntb + 7) / 8;                  // blocks per channel group
+// HW: half-waves (streams) per block.
+template <uint32_t HW = 8>
+__device__ __forceinline__ uint32_t cb_block(const Geo& g) {
+    const uint32_t bpc = (g.ntb + HW - 1) / HW;            // blocks per channel group
     const uint32_t total = g.ncg * bpc;
     const uint32_t b = blockIdx.x;
-    const uint32_t w = total % 8 == 0 ? (b % 8) * (total / 8) + b / 8 : b;
-    const uint32_t cg = w / bpc, tb = (w % bpc) * 8 + (threadIdx.x >> 5);
+    return total % 8 == 0 ? (b % 8) * (total / 8) + b / 8 : b;
+}
+// The channel group of this block (the same for all its half-waves; ncg or
+// more for a block past the last one).
+template <uint32_t HW = 8>
+__device__ __forceinline__ uint32_t cb_group(const Geo& g) { return cb_block<HW>(g) / ((g.ntb + HW - 1) / HW); }
+template <uint32_t HW = 8>
+__device__ __forceinline__ bool cb_stream(const Geo& g, uint64_t first, uint64_t& sid) {
+    const uint32_t bpc = (g.ntb + HW - 1) / HW;
+    const uint32_t w = cb_block<HW>(g);
+    const uint32_t cg = w / bpc, tb = (w % bpc) * HW + (threadIdx.x >> 5);
     if (cg >= g.ncg || tb >= g.ntb) return false;
     const uint64_t pass = first / (uint64_t(g.ncg) * g.ntb);
     sid = (pass * g.ntb + tb) * g.ncg + cg;
@@ -293,17 +308,30 @@ __device__ __forceinline__ bool cb_stream(const Geo& g, uint64_t first, uint64_t
 // flagged), its escaped value stored 2 steps before.  The state update then
 // waits on nothing but its own arithmetic.  Output order and format are those
 // of encode_streams.
+// A block's 16 streams share one channel group: the packed entries of
+// symbols 0..11 of its 32 x 16 tables sit in LDS, and only larger symbols
+// read their entry from device memory.
 // kCbLag: steps between pipeline stages; P: register ring period (steps)
+constexpr uint32_t kCbEncHead = 12;                      // symbols per table whose entries stay in LDS
+constexpr uint32_t kCbEncStreams = 16;                   // streams (half-waves) per block
 template <int kCbLag, int P>
-__global__ __launch_bounds__(256) void encode_cb(EncodeLaunch a, DevTables t) {
+__global__ __launch_bounds__(kCbEncStreams * 32) void encode_cb(EncodeLaunch a, DevTables t) {
     constexpr uint32_t RAW = 2 * kSyms;
     constexpr uint32_t MAXW = (RAW - kStreamHead) / 2;     // more words or escapes mean a raw stream
     constexpr uint32_t MAXE = (RAW - kStreamHead) / 2;
+    __shared__ uint2 ehead[kLanes * 16 * kCbEncHead];       // [lane][shift][symbol 0..11]
     const uint32_t tid = threadIdx.x;
     const Geo g = geometry(a.shape);
     const uint64_t per = uint64_t(g.ncg) * g.ntb;            // streams per pass
+    {
+        const uint32_t bcg = cb_group<kCbEncStreams>(g);
+        if (bcg >= g.ncg) return;                              // the whole block
+        for (uint32_t i = tid; i < kLanes * 16 * kCbEncHead; i += blockDim.x)
+            ehead[i] = t.enc8[(size_t(bcg) * (kLanes * 16) + i / kCbEncHead) * 256 + i % kCbEncHead];
+        __syncthreads();
+    }
     uint64_t sid;
-    if (!cb_stream(g, uint64_t(blockIdx.y) * per, sid)) return;
+    if (!cb_stream<kCbEncStreams>(g, uint64_t(blockIdx.y) * per, sid)) return;
     const uint32_t lane = tid & 31u, half = tid & 32u;
     const uint32_t cg = uint32_t(sid % g.ncg);
     const uint32_t tb = uint32_t((sid / g.ncg) % g.ntb);
@@ -318,7 +346,7 @@ __global__ __launch_bounds__(256) void encode_cb(EncodeLaunch a, DevTables t) {
 
     int32_t ic[P], ig[P], il[P], ir[P];                    // stage 1: raw inputs
     uint32_t zz[P];                                        // stage 2: symbol
-    uint4 ee[P];                                           // stage 2: table entry
+    uint2 ee[P];                                           // stage 2: packed table entry
     uint32_t x = kStateLow, cnt = 0, ecnt = 0;
     constexpr int kIters = kSteps + 3 * kCbLag;
     static_assert(P >= 3 * kCbLag + 1, "ring period covers the pipeline");
@@ -353,8 +381,9 @@ __global__ __launch_bounds__(256) void encode_cb(EncodeLaunch a, DevTables t) {
                     const int32_t kk = mu >> 4;
                     const uint32_t table = ch * 16u + uint32_t(mu & 15);
                     zz[sl] = zig16(uint32_t(ic[sl] - kk) & 0xFFFFu);
-                    // entries past the table's n repeat its escape entry, flagged in bit 8 of w
-                    ee[sl] = t.enc[size_t(table) * 256 + min(zz[sl], 255u)];
+                    // entries past the table's n repeat its escape entry, flagged in bit 30
+                    if (zz[sl] < kCbEncHead) ee[sl] = ehead[(lane * 16u + uint32_t(mu & 15)) * kCbEncHead + zz[sl]];
+                    else ee[sl] = t.enc8[size_t(table) * 256 + min(zz[sl], 255u)];
                 }
             }
             // stage 3: escapes of step 127 - (it - 2 lag), in step order
@@ -363,7 +392,7 @@ __global__ __launch_bounds__(256) void encode_cb(EncodeLaunch a, DevTables t) {
                 const int sl = (kSteps - 1 - d + 2 * kCbLag + 8 * P) % P;
                 if (k >= 0 && k < kSteps) {
                     const uint32_t z = zz[sl];
-                    const bool esc = (ee[sl].w & 0x100u) != 0;
+                    const bool esc = (ee[sl].y & 0x40000000u) != 0;
                     // escaped values keep decode order: ranked like the words, written backwards
                     const uint64_t b = __ballot(esc);
                     const uint32_t mine = uint32_t(b >> half);
@@ -379,10 +408,12 @@ __global__ __launch_bounds__(256) void encode_cb(EncodeLaunch a, DevTables t) {
                 const int k = kSteps - 1 - (it - 3 * kCbLag);
                 const int sl = (kSteps - 1 - d + 3 * kCbLag + 8 * P) % P;
                 if (k >= 0 && k < kSteps) {
-                    const uint4 e = ee[sl];
-                    emit_words(x, cnt, x >= e.x, lane, half, wfwd, MAXW);
-                    const uint32_t qt = __umulhi(x + (e.z >> 24), e.y) >> (e.w & 31u);    // floor(x / f)
-                    x = x + (e.w >> 16) + __umul24(qt, e.z);
+                    const uint32_t m = ee[sl].x, w = ee[sl].y;
+                    const uint32_t f = w & 0xFFFu;
+                    emit_words(x, cnt, x >= (f << 20), lane, half, wfwd, MAXW);
+                    const uint32_t qt = __umulhi(x + __builtin_amdgcn_ubfe(w, 29, 1), m) >>
+                                        __builtin_amdgcn_ubfe(w, 24, 5);                    // floor(x / f)
+                    x = x + __builtin_amdgcn_ubfe(w, 12, 12) + qt * (kM - f);
                 }
             }
         }
@@ -747,13 +778,35 @@ __global__ __launch_bounds__(256) void decode_streams(DecodeLaunch a, DevTables 
 // RANGE: token blocks tb_base onwards of the container (the shape is the
 // range's, rows are numbered from its start), and the range's last odd token
 // takes its right neighbour from next_rows when the range stops early.
+//
+// The block's streams share one channel group, whose 32 x 16 tables the block
+// reads throughout; the starts of each table's first 32 symbols (and of the
+// 33rd) sit in LDS, so a slot below the 33rd start finds its symbol by binary
+// search there (start and frequency from neighbouring starts) and only the
+// other lanes read the half slot map and rows from device memory.
+constexpr uint32_t kCbHead = 32;                         // symbols per table whose starts stay in LDS
+constexpr uint32_t kCbDecStreams = 16;                   // streams (half-waves) per block
+constexpr uint32_t kCbHeadRow = kCbHead + 1;
 template <int kLag, int P, bool RANGE = false>
-__global__ __launch_bounds__(256) void decode_cb(DecodeLaunch a, DevTables t, uint64_t first, uint64_t count) {
+__global__ __launch_bounds__(kCbDecStreams * 32) __attribute__((amdgpu_waves_per_eu(6))) void decode_cb(
+    DecodeLaunch a, DevTables t, uint64_t first, uint64_t count) {
     constexpr uint32_t RAW = 2 * kSyms;
+    __shared__ uint16_t head[kLanes * 16 * kCbHeadRow];       // [lane][shift][symbol 0..32] starts
     const uint32_t tid = threadIdx.x;
     const Geo g = geometry(a.shape);
+    {
+        const uint32_t bcg = cb_group<kCbDecStreams>(g);
+        if (bcg >= g.ncg) return;                              // the whole block
+        // starts of symbols 0..32 of each table, those past a table's escape symbol repeating its start
+        for (uint32_t i = tid; i < kLanes * 16 * kCbHeadRow; i += blockDim.x) {
+            const uint32_t table = bcg * (kLanes * 16) + i / kCbHeadRow, z = i % kCbHeadRow;
+            const uint32_t rt = min(kCbHead, t.n[table]);
+            head[i] = uint16_t(t.fc[size_t(table) * 256 + min(z, rt)] >> 16);
+        }
+        __syncthreads();
+    }
     uint64_t sid;
-    if (!cb_stream(g, first, sid)) return;
+    if (!cb_stream<kCbDecStreams>(g, first, sid)) return;
     const uint32_t lane = tid & 31u, half = tid & 32u;
     const uint32_t cg = uint32_t(sid % g.ncg);
     const uint32_t tb = uint32_t((sid / g.ncg) % g.ntb);
@@ -851,16 +904,26 @@ __global__ __launch_bounds__(256) void decode_cb(DecodeLaunch a, DevTables t, ui
                 if (k >= 0 && k < kSteps) {
                     const uint32_t table = tab[sl];
                     const uint32_t slot = x & (kM - 1u);
-                    // the even slot's symbol, then the rows of it and of the next symbol in one 8-byte read:
-                    // the odd slot belongs to the next one when that one starts there (never past the
-                    // escape symbol, whose row is flagged in bit 15)
-                    const uint32_t s0 = t.half[size_t(table) * (kM / 2) + (slot >> 1)];
-                    uint2 fr;
-                    __builtin_memcpy(&fr, t.fc + size_t(table) * 256 + s0, 8);
+                    // symbols 0..31: binary search of the starts in LDS
+                    const uint32_t hb = (lane * 16u + (table & 15u)) * kCbHeadRow;
+                    const bool hit = slot < head[hb + kCbHead];
+                    uint32_t zc = 0;
+#pragma unroll
+                    for (uint32_t step = kCbHead / 2; step; step >>= 1) zc += head[hb + zc + step] <= slot ? step : 0u;
+                    const uint32_t c0 = head[hb + zc], c1 = head[hb + zc + 1];
+                    // other slots: the even slot's symbol, then the rows of it and of the next symbol in one
+                    // 8-byte read: the odd slot belongs to the next one when that one starts there (never
+                    // past the escape symbol, whose row is flagged in bit 15)
+                    uint32_t s0 = 0;
+                    uint2 fr = make_uint2(0u, 0u);
+                    if (!hit) {
+                        s0 = t.half[size_t(table) * (kM / 2) + (slot >> 1)];
+                        __builtin_memcpy(&fr, t.fc + size_t(table) * 256 + s0, 8);
+                    }
                     const bool last = (fr.x & 0x8000u) != 0;
                     const bool adv = !last && slot >= (fr.y >> 16);
-                    const uint32_t s = s0 + (adv ? 1u : 0u);
-                    const uint32_t fcv = adv ? fr.y : fr.x;
+                    const uint32_t s = hit ? zc : s0 + (adv ? 1u : 0u);
+                    const uint32_t fcv = hit ? (c1 - c0) | (c0 << 16) : (adv ? fr.y : fr.x);
                     x = (fcv & 0x0FFFu) * (x >> kProbBits) + slot - (fcv >> 16);
                     // refill in lane order from the word windows
                     const bool need = x < kStateLow;
@@ -3525,9 +3588,9 @@ hipError_t encode_code(const EncodeLaunch& a, const DevTables& t, hipStream_t st
     } else if (MODE == SKV_CHECKERBOARD && fits) {
         // two steps between stages: longer lags measured no faster (more registers, fewer waves)
         const Geo g{a.shape.channels, a.shape.tokens, a.shape.channels / kLanes, a.shape.tokens / 2 / kSteps};
-        const dim3 grid(g.ncg * ((g.ntb + 7) / 8), 2);       // y: pass
+        const dim3 grid(g.ncg * ((g.ntb + kCbEncStreams - 1) / kCbEncStreams), 2);       // y: pass
         timed("encode_streams", st, [&](hipEvent_t e0, hipEvent_t e1) {
-            hipExtLaunchKernelGGL((encode_cb<2, 8>), grid, dim3(256), 0, st, e0, e1, 0, a, t);
+            hipExtLaunchKernelGGL((encode_cb<2, 7>), grid, dim3(kCbEncStreams * 32), 0, st, e0, e1, 0, a, t);
         });
     } else {
         timed("encode_streams", st, [&](hipEvent_t e0, hipEvent_t e1) {
@@ -3634,7 +3697,9 @@ hipError_t decode_all(const DecodeLaunch& a, const DevTables& t, hipStream_t st)
     const uint64_t per = a.n_streams / passes;
     const uint32_t grid = uint32_t((per + kStreamsPerBlock - 1) / kStreamsPerBlock);
     const uint32_t ncg = a.shape.channels / kLanes;
-    auto cb_grid = [&](uint64_t streams) { return dim3(uint32_t(ncg * ((streams / ncg + 7) / 8))); };
+    auto cb_grid = [&](uint64_t streams) {
+        return dim3(uint32_t(ncg * ((streams / ncg + kCbDecStreams - 1) / kCbDecStreams)));
+    };
     // a checkerboard range (token blocks from tb_base, or fewer than the container's)
     const bool range = MODE == SKV_CHECKERBOARD && (a.tb_base != 0 || a.ntb_index != a.shape.tokens / 2 / kSteps);
     if (range && !fits) return hipErrorInvalidValue;
@@ -3650,7 +3715,8 @@ hipError_t decode_all(const DecodeLaunch& a, const DevTables& t, hipStream_t st)
         x.out = a.next_rows;
         x.next_rows = nullptr;
         timed("decode_streams", st, [&](hipEvent_t e0, hipEvent_t e1) {
-            hipExtLaunchKernelGGL((decode_cb<2, 8, true>), cb_grid(ncg), dim3(256), 0, st, e0, e1, 0, x, t, 0, ncg);
+            hipExtLaunchKernelGGL((decode_cb<2, 6, true>), cb_grid(ncg), dim3(kCbDecStreams * 32), 0, st, e0, e1, 0, x,
+                                  t, 0, ncg);
         });
     }
     for (uint64_t ps = 0; ps < passes; ++ps) {
@@ -3663,10 +3729,11 @@ hipError_t decode_all(const DecodeLaunch& a, const DevTables& t, hipStream_t st)
         }
         timed("decode_streams", st, [&](hipEvent_t e0, hipEvent_t e1) {
             if (MODE == SKV_CHECKERBOARD && range)
-                hipExtLaunchKernelGGL((decode_cb<2, 8, true>), cb_grid(per), dim3(256), 0, st, e0, e1, 0, a, t,
+                hipExtLaunchKernelGGL((decode_cb<2, 6, true>), cb_grid(per), dim3(kCbDecStreams * 32), 0, st, e0, e1, 0, a, t,
                                       ps * per, per);
             else if (MODE == SKV_CHECKERBOARD && fits)
-                hipExtLaunchKernelGGL((decode_cb<2, 8>), cb_grid(per), dim3(256), 0, st, e0, e1, 0, a, t, ps * per, per);
+                hipExtLaunchKernelGGL((decode_cb<2, 6>), cb_grid(per), dim3(kCbDecStreams * 32), 0, st, e0, e1, 0, a, t,
+                                      ps * per, per);
             else
                 hipExtLaunchKernelGGL((decode_streams<DT, MODE>), dim3(grid), dim3(256), 0, st, e0, e1, 0, a, t, ps * per, per);
         });
@@ -3691,6 +3758,7 @@ hipError_t build_dev_tables(const uint8_t* blob, DevTables* t, hipStream_t st) {
     if (e == hipSuccess) e = hipMalloc(&t->fc, size_t(nt) * 256 * 4 + 16);   // + one entry read past the last row
     if (e == hipSuccess) e = hipMalloc(&t->slot, size_t(nt) * kM);
     if (e == hipSuccess && is_checkerboard(blob[7])) e = hipMalloc(&t->half, size_t(nt) * (kM / 2));
+    if (e == hipSuccess && is_checkerboard(blob[7])) e = hipMalloc(&t->enc8, size_t(nt) * 256 * sizeof(uint2));
     if (e == hipSuccess && blob[7] == SKV_CHECKERBOARD_MAP) {
         // the map section follows the records (validated with the blob)
         const uint8_t* m = blob + kHeaderBytes + size_t(nt) * kTableRecord;
@@ -3710,7 +3778,8 @@ hipError_t build_dev_tables(const uint8_t* blob, DevTables* t, hipStream_t st) {
         e = hipMemcpyAsync(t->base, blob + kHeaderBytes + size_t(nt) * kTableRecord, nbase, hipMemcpyHostToDevice, st);
     if (e == hipSuccess) e = hipMemcpyAsync(rec, blob + kHeaderBytes, size_t(nt) * kTableRecord, hipMemcpyHostToDevice, st);
     if (e == hipSuccess) {
-        hipLaunchKernelGGL(expand_tables, dim3(nt), dim3(256), 0, st, rec, t->n, t->enc, t->fc, t->slot, t->half);
+        hipLaunchKernelGGL(expand_tables, dim3(nt), dim3(256), 0, st, rec, t->n, t->enc, t->fc, t->slot, t->half,
+                           t->enc8);
         e = hipGetLastError();
     }
     if (e == hipSuccess) e = hipStreamSynchronize(st);
@@ -3728,6 +3797,7 @@ void free_dev_tables(DevTables* t) {
     if (t->fc) (void)hipFree(t->fc);
     if (t->slot) (void)hipFree(t->slot);
     if (t->half) (void)hipFree(t->half);
+    if (t->enc8) (void)hipFree(t->enc8);
     if (t->base) (void)hipFree(t->base);
     if (t->map_v) (void)hipFree(t->map_v);
     if (t->map_u) (void)hipFree(t->map_u);
