@@ -314,20 +314,25 @@ __device__ __forceinline__ bool cb_stream(const Geo& g, uint64_t first, uint64_t
 // kCbLag: steps between pipeline stages; P: register ring period (steps)
 constexpr uint32_t kCbEncHead = 12;                      // symbols per table whose entries stay in LDS
 constexpr uint32_t kCbEncStreams = 16;                   // streams (half-waves) per block
+constexpr uint32_t kCbEncLane = 16 * kCbEncHead + 1;     // entries per lane: an odd count spreads the lanes'
+                                                         // 8-byte reads over the bank pairs
 template <int kCbLag, int P>
 __global__ __launch_bounds__(kCbEncStreams * 32) void encode_cb(EncodeLaunch a, DevTables t) {
     constexpr uint32_t RAW = 2 * kSyms;
     constexpr uint32_t MAXW = (RAW - kStreamHead) / 2;     // more words or escapes mean a raw stream
     constexpr uint32_t MAXE = (RAW - kStreamHead) / 2;
-    __shared__ uint2 ehead[kLanes * 16 * kCbEncHead];       // [lane][shift][symbol 0..11]
+    __shared__ uint2 ehead[kLanes * kCbEncLane];            // [lane][shift][symbol 0..11]
     const uint32_t tid = threadIdx.x;
     const Geo g = geometry(a.shape);
     const uint64_t per = uint64_t(g.ncg) * g.ntb;            // streams per pass
     {
         const uint32_t bcg = cb_group<kCbEncStreams>(g);
         if (bcg >= g.ncg) return;                              // the whole block
-        for (uint32_t i = tid; i < kLanes * 16 * kCbEncHead; i += blockDim.x)
-            ehead[i] = t.enc8[(size_t(bcg) * (kLanes * 16) + i / kCbEncHead) * 256 + i % kCbEncHead];
+        for (uint32_t i = tid; i < kLanes * 16 * kCbEncHead; i += blockDim.x) {
+            const uint32_t j = i / kCbEncHead, z = i % kCbEncHead;     // j = lane * 16 + shift
+            ehead[(j / 16) * kCbEncLane + (j % 16) * kCbEncHead + z] =
+                t.enc8[(size_t(bcg) * (kLanes * 16) + j) * 256 + z];
+        }
         __syncthreads();
     }
     uint64_t sid;
@@ -382,7 +387,7 @@ __global__ __launch_bounds__(kCbEncStreams * 32) void encode_cb(EncodeLaunch a, 
                     const uint32_t table = ch * 16u + uint32_t(mu & 15);
                     zz[sl] = zig16(uint32_t(ic[sl] - kk) & 0xFFFFu);
                     // entries past the table's n repeat its escape entry, flagged in bit 30
-                    if (zz[sl] < kCbEncHead) ee[sl] = ehead[(lane * 16u + uint32_t(mu & 15)) * kCbEncHead + zz[sl]];
+                    if (zz[sl] < kCbEncHead) ee[sl] = ehead[lane * kCbEncLane + uint32_t(mu & 15) * kCbEncHead + zz[sl]];
                     else ee[sl] = t.enc8[size_t(table) * 256 + min(zz[sl], 255u)];
                 }
             }
@@ -787,11 +792,13 @@ __global__ __launch_bounds__(256) void decode_streams(DecodeLaunch a, DevTables 
 constexpr uint32_t kCbHead = 32;                         // symbols per table whose starts stay in LDS
 constexpr uint32_t kCbDecStreams = 16;                   // streams (half-waves) per block
 constexpr uint32_t kCbHeadRow = kCbHead + 1;
+// a lane's 16 rows take an odd number of dwords, so lanes start on different banks
+constexpr uint32_t kCbHeadLane = 16 * kCbHeadRow + 2;
 template <int kLag, int P, bool RANGE = false>
 __global__ __launch_bounds__(kCbDecStreams * 32) __attribute__((amdgpu_waves_per_eu(6))) void decode_cb(
     DecodeLaunch a, DevTables t, uint64_t first, uint64_t count) {
     constexpr uint32_t RAW = 2 * kSyms;
-    __shared__ uint16_t head[kLanes * 16 * kCbHeadRow];       // [lane][shift][symbol 0..32] starts
+    __shared__ uint16_t head[kLanes * kCbHeadLane];            // [lane][shift][symbol 0..32] starts
     const uint32_t tid = threadIdx.x;
     const Geo g = geometry(a.shape);
     {
@@ -799,9 +806,11 @@ __global__ __launch_bounds__(kCbDecStreams * 32) __attribute__((amdgpu_waves_per
         if (bcg >= g.ncg) return;                              // the whole block
         // starts of symbols 0..32 of each table, those past a table's escape symbol repeating its start
         for (uint32_t i = tid; i < kLanes * 16 * kCbHeadRow; i += blockDim.x) {
-            const uint32_t table = bcg * (kLanes * 16) + i / kCbHeadRow, z = i % kCbHeadRow;
+            const uint32_t j = i / kCbHeadRow, z = i % kCbHeadRow;     // j = lane * 16 + shift
+            const uint32_t table = bcg * (kLanes * 16) + j;
             const uint32_t rt = min(kCbHead, t.n[table]);
-            head[i] = uint16_t(t.fc[size_t(table) * 256 + min(z, rt)] >> 16);
+            head[(j / 16) * kCbHeadLane + (j % 16) * kCbHeadRow + z] =
+                uint16_t(t.fc[size_t(table) * 256 + min(z, rt)] >> 16);
         }
         __syncthreads();
     }
@@ -905,7 +914,7 @@ __global__ __launch_bounds__(kCbDecStreams * 32) __attribute__((amdgpu_waves_per
                     const uint32_t table = tab[sl];
                     const uint32_t slot = x & (kM - 1u);
                     // symbols 0..31: binary search of the starts in LDS
-                    const uint32_t hb = (lane * 16u + (table & 15u)) * kCbHeadRow;
+                    const uint32_t hb = lane * kCbHeadLane + (table & 15u) * kCbHeadRow;
                     const bool hit = slot < head[hb + kCbHead];
                     uint32_t zc = 0;
 #pragma unroll
