@@ -797,3 +797,37 @@ def test_encode_in_passes(skv, orc, dtype, mode):
             assert e.value.status == skv.ERR_CAPACITY and ob.value == want.size
     assert len(seen) >= 6, seen
     assert torch.equal(skv.decode(tabs, got, p), t)
+
+
+@pytest.mark.parametrize("dtype", ["e4m3", "bf16"])
+def test_encode_in_passes_raw_and_escapes(skv, orc, dtype):
+    """Passes over a cache whose token blocks alternate between incompressible
+    values (stored raw: the compaction copies them from the pass's own part of
+    the target), values that all escape, and ordinary ones: whole-slab and
+    token-block passes give the oracle's container."""
+    cfg = gen.Config(99, f"passes-mixed-{dtype}", dtype, 2, 2, 1536, 128, outliers=False)
+    t, p, tabs, oshape = residual_case(skv, orc, cfg)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(23)
+    t = t.clone()
+    bits = 8 if dtype == "e4m3" else 16
+    for b in range(cfg.tokens // 128):
+        sl = slice(128 * b, 128 * b + 128)
+        if b % 3 == 0:
+            hi = 1 << bits
+            r = torch.randint(0, hi, t[:, :, sl].shape, generator=g, device="cuda", dtype=torch.int32)
+            t[:, :, sl] = (r - (hi // 2 if dtype == "bf16" else 0)).to(t.dtype)
+        elif b % 3 == 1:
+            off = 100 if dtype == "e4m3" else 300
+            t[:, :, sl] = (p[:, :, sl].to(torch.int32) + off).to(t.dtype)
+    want = orc.encode_array(tabs.bytes(), oshape, t.cpu().numpy(), p.cpu().numpy(), threads=ORACLE_THREADS)
+    n, idx, _ = _parse(want.tobytes())
+    assert (idx[:-1] >> np.uint64(63)).any(), "some streams are stored raw"
+    full, _ = skv.encode_workspace(tabs, cfg.tokens)
+    for budget in (0, full // 3, full // 9):
+        wb, passes = skv.encode_workspace(tabs, cfg.tokens, budget)
+        enc = skv.Encoder(tabs, cfg.tokens, max_work_bytes=budget)
+        say(f"[parity] mixed {dtype}: {passes} passes")
+        got = enc(t, p)
+        assert_same_container(host_u8(got), want, f"mixed {dtype}, {passes} passes")
+    assert torch.equal(skv.decode(tabs, got, p), t)
