@@ -298,30 +298,136 @@ __device__ __forceinline__ bool cb_stream(const Geo& g, uint64_t first, uint64_t
     return true;
 }
 
-// Checkerboard encoder with the table reads taken off the state chain.  The
-// 32,768 tables (16 shifted tables per component) stay in device memory, so
-// every step reads a table entry from the L2; none of those reads depends on
-// the rANS state.  Each lane runs a software pipeline over the steps (which
-// go from 127 down to 0): a step's coefficient, side input and neighbours are
-// loaded 6 steps before the step is coded, its table entry 4 steps before
-// (one read: entries past a table's direct range repeat its escape entry,
-// flagged), its escaped value stored 2 steps before.  The state update then
-// waits on nothing but its own arithmetic.  Output order and format are those
-// of encode_streams.
-// A block's 16 streams share one channel group: the packed entries of
-// symbols 0..11 of its 32 x 16 tables sit in LDS, and only larger symbols
-// read their entry from device memory.
-// kCbLag: steps between pipeline stages; P: register ring period (steps)
+// Checkerboard encoder.  The 32,768 tables (16 shifted tables per
+// component) stay in device memory; a block's 16 streams share one channel
+// group, and the packed entries of symbols 0..11 of its 32 x 16 tables sit in
+// LDS, so only larger symbols read their entry from device memory.  None of a
+// step's reads depends on the rANS state, so they are all issued ahead of the
+// state chain, in batches of 8 steps (steps run from 127 down to 0):
+//   * the coefficients, side inputs and neighbours of batch j + 1 are loaded
+//     while batch j is coded;
+//   * the table entries of batch j are requested before batch j + 1's loads,
+//     so waiting for them never waits for those;
+//   * words and escaped values go to per-stream LDS rings and out to the
+//     workspace once per batch, so no store is pending while the batch waits
+//     on its loads (loads and stores share one counter and complete out of
+//     order with respect to each other, so a pending store turns every wait
+//     into a wait for everything).
+// Every load is issued unconditionally (a lane without a device-memory entry
+// reads the first entry), so the number of loads in flight is the same on
+// every path and each wait names exactly the loads it needs.  Output order
+// and format are those of encode_streams.
 constexpr uint32_t kCbEncHead = 12;                      // symbols per table whose entries stay in LDS
 constexpr uint32_t kCbEncStreams = 16;                   // streams (half-waves) per block
 constexpr uint32_t kCbEncLane = 16 * kCbEncHead + 1;     // entries per lane: an odd count spreads the lanes'
                                                          // 8-byte reads over the bank pairs
-template <int kCbLag, int P>
-__global__ __launch_bounds__(kCbEncStreams * 32) void encode_cb(EncodeLaunch a, DevTables t) {
+constexpr uint32_t kCbEncBatch = 8;                      // steps per batch
+constexpr uint32_t kCbEncRing = kCbEncBatch * kLanes;    // words a stream can emit in one batch
+constexpr uint32_t kCbEncEsc = 64;                       // escaped values per batch kept in LDS (more go out at once)
+
+template <bool PASS>
+__device__ __forceinline__ void encode_cb_stream(const EncodeLaunch& a, const DevTables& t, const Geo& g,
+                                                 uint64_t sid, const uint2* ehead, uint16_t* wring,
+                                                 uint16_t* ering) {
     constexpr uint32_t RAW = 2 * kSyms;
     constexpr uint32_t MAXW = (RAW - kStreamHead) / 2;     // more words or escapes mean a raw stream
     constexpr uint32_t MAXE = (RAW - kStreamHead) / 2;
+    constexpr uint32_t B = kCbEncBatch, NB = kSteps / kCbEncBatch;
+    const uint32_t lane = threadIdx.x & 31u, half = threadIdx.x & 32u;
+    const uint32_t cg = uint32_t(sid % g.ncg);
+    const uint32_t tb = uint32_t((sid / g.ncg) % g.ntb);
+    const uint32_t ch = cg * kLanes + lane;
+    uint8_t* area = a.scratch + sid * (2 * RAW);
+    uint16_t* wfwd = reinterpret_cast<uint16_t*>(area + RAW);           // words, emission order
+    uint16_t* efwd = reinterpret_cast<uint16_t*>(area + kStreamHead);   // escaped values, emission order
+    const int16_t* coef = static_cast<const int16_t*>(a.target);
+    const int16_t* Gp = static_cast<const int16_t*>(PASS ? a.aux_odd : a.aux);
+    const size_t C = g.C;
+    const uint2* lhead = ehead + lane * kCbEncLane;
+
+    // inputs of batch j: step 127 - B j - i in slot i (j = NB loads step 0 again, unused)
+    int32_t ic[B], ig[B], il[B], ir[B];
+    auto load_batch = [&](uint32_t j) {
+#pragma unroll
+        for (uint32_t i = 0; i < B; ++i) {
+            const uint32_t k = j < NB ? kSteps - 1 - B * j - i : 0u;
+            const uint32_t tok = 2u * (tb * kSteps + k) + (PASS ? 1u : 0u);
+            const size_t r = size_t(tok) * C + ch;
+            ic[i] = coef[r];
+            ig[i] = Gp[r];
+            if constexpr (PASS) {
+                il[i] = coef[r - C];
+                ir[i] = coef[tok + 1 < g.T ? r + C : r - C];
+            }
+        }
+    };
+    uint32_t x = kStateLow, cnt = 0, ecnt = 0, wdone = 0, edone = 0;
+    load_batch(0);
+    for (uint32_t j = 0; j < NB; ++j) {
+        // symbols and table entries of batch j
+        uint32_t zs[B];                                    // symbol | shift << 16
+        uint2 ge[B];                                       // device-memory entry (symbols past the LDS head)
+#pragma unroll
+        for (uint32_t i = 0; i < B; ++i) {
+            int32_t mu = ig[i];
+            if constexpr (PASS) mu += 8 * (il[i] + ir[i]);
+            const int32_t kk = mu >> 4;
+            const uint32_t sh = uint32_t(mu & 15);
+            const uint32_t z = zig16(uint32_t(ic[i] - kk) & 0xFFFFu);
+            zs[i] = z | (sh << 16);
+            // entries past the table's n repeat its escape entry, flagged in bit 30
+            const uint2* gp = z < kCbEncHead ? t.enc8 : t.enc8 + (size_t(ch) * 16u + sh) * 256 + min(z, 255u);
+            ge[i] = *gp;
+        }
+        load_batch(j + 1);
+#pragma unroll
+        for (uint32_t i = 0; i < B; ++i) {
+            const uint32_t z = zs[i] & 0xFFFFu, sh = zs[i] >> 16;
+            const uint2 le = lhead[sh * kCbEncHead + min(z, kCbEncHead - 1)];
+            const uint2 e = z < kCbEncHead ? le : ge[i];
+            // escaped values keep decode order: ranked like the words, written backwards
+            const bool esc = (e.y & 0x40000000u) != 0;
+            const uint32_t me = uint32_t(__ballot(esc) >> half);
+            if (esc) {
+                const uint32_t pos = ecnt + __popc(uint32_t(uint64_t(me) >> (lane + 1)));
+                if (pos - edone < kCbEncEsc) ering[pos % kCbEncEsc] = uint16_t(z);
+                else if (pos < MAXE) efwd[pos] = uint16_t(z);
+            }
+            ecnt += __popc(me);
+            // the state update
+            const uint32_t m = e.x, w = e.y;
+            const uint32_t f = w & 0xFFFu;
+            const bool emit = x >= (f << 20);
+            const uint32_t mw = uint32_t(__ballot(emit) >> half);
+            if (emit) {
+                const uint32_t pos = cnt + __popc(uint32_t(uint64_t(mw) >> (lane + 1)));
+                wring[pos % kCbEncRing] = uint16_t(x & 0xFFFFu);
+                x >>= 16;
+            }
+            cnt += __popc(mw);
+            const uint32_t qt = __umulhi(x + __builtin_amdgcn_ubfe(w, 29, 1), m) >>
+                                __builtin_amdgcn_ubfe(w, 24, 5);                    // floor(x / f)
+            x = x + __builtin_amdgcn_ubfe(w, 12, 12) + qt * (kM - f);
+        }
+        // the batch's words and escaped values out to the workspace (the lanes of this stream wrote
+        // them; LDS operations of one wavefront complete in order)
+        for (uint32_t i = wdone + lane; i < min(cnt, MAXW); i += kLanes) wfwd[i] = wring[i % kCbEncRing];
+        wdone = cnt;
+        const uint32_t eend = min(min(ecnt, edone + kCbEncEsc), MAXE);
+        for (uint32_t i = edone + lane; i < eend; i += kLanes) efwd[i] = ering[i % kCbEncEsc];
+        edone = ecnt;
+    }
+    reinterpret_cast<uint32_t*>(area)[lane] = x;
+    if (lane == 0) {
+        const uint32_t bytes = (kStreamHead + 2 * cnt + 2 * ecnt + 3) & ~3u;
+        a.meta[sid] = bytes >= RAW ? 0x80000000u : (cnt | (ecnt << 14));
+    }
+}
+
+__global__ __launch_bounds__(kCbEncStreams * 32) void encode_cb(EncodeLaunch a, DevTables t) {
     __shared__ uint2 ehead[kLanes * kCbEncLane];            // [lane][shift][symbol 0..11]
+    __shared__ uint16_t wring[kCbEncStreams * kCbEncRing];  // [stream][word position mod kCbEncRing]
+    __shared__ uint16_t ering[kCbEncStreams * kCbEncEsc];   // [stream][escape position mod kCbEncEsc]
     const uint32_t tid = threadIdx.x;
     const Geo g = geometry(a.shape);
     const uint64_t per = uint64_t(g.ncg) * g.ntb;            // streams per pass
@@ -337,97 +443,11 @@ __global__ __launch_bounds__(kCbEncStreams * 32) void encode_cb(EncodeLaunch a, 
     }
     uint64_t sid;
     if (!cb_stream<kCbEncStreams>(g, uint64_t(blockIdx.y) * per, sid)) return;
-    const uint32_t lane = tid & 31u, half = tid & 32u;
-    const uint32_t cg = uint32_t(sid % g.ncg);
-    const uint32_t tb = uint32_t((sid / g.ncg) % g.ntb);
-    const uint32_t pass = uint32_t(sid / per);
-    const uint32_t ch = cg * kLanes + lane;
-    uint8_t* area = a.scratch + sid * (2 * RAW);
-    uint16_t* wfwd = reinterpret_cast<uint16_t*>(area + RAW);           // words, emission order
-    uint16_t* efwd = reinterpret_cast<uint16_t*>(area + kStreamHead);   // escaped values, emission order
-    const int16_t* coef = static_cast<const int16_t*>(a.target);
-    const int16_t* Gp = static_cast<const int16_t*>(pass ? a.aux_odd : a.aux);
-    const size_t C = g.C;
-
-    int32_t ic[P], ig[P], il[P], ir[P];                    // stage 1: raw inputs
-    uint32_t zz[P];                                        // stage 2: symbol
-    uint2 ee[P];                                           // stage 2: packed table entry
-    uint32_t x = kStateLow, cnt = 0, ecnt = 0;
-    constexpr int kIters = kSteps + 3 * kCbLag;
-    static_assert(P >= 3 * kCbLag + 1, "ring period covers the pipeline");
-    for (int it0 = 0; it0 < kIters; it0 += P) {
-#pragma unroll
-        for (int d = 0; d < P; ++d) {
-            const int it = it0 + d;
-            // stage 1: loads of step 127 - it
-            {
-                const int k = kSteps - 1 - it;
-                constexpr int slot_base = 0;
-                (void)slot_base;
-                const int sl = (kSteps - 1 - d + 8 * P) % P;      // (127 - it) mod P with it0 a multiple of P
-                if (k >= 0) {
-                    const uint32_t tok = 2u * (tb * kSteps + uint32_t(k)) + pass;
-                    const size_t r = size_t(tok) * C + ch;
-                    ic[sl] = coef[r];
-                    ig[sl] = Gp[r];
-                    if (pass) {
-                        il[sl] = coef[r - C];
-                        ir[sl] = tok + 1 < g.T ? int32_t(coef[r + C]) : int32_t(coef[r - C]);
-                    }
-                }
-            }
-            // stage 2: table, symbol and direct count of step 127 - (it - lag)
-            {
-                const int k = kSteps - 1 - (it - kCbLag);
-                const int sl = (kSteps - 1 - d + kCbLag + 8 * P) % P;
-                if (k >= 0 && k < kSteps) {
-                    int32_t mu = ig[sl];
-                    if (pass) mu += 8 * (il[sl] + ir[sl]);
-                    const int32_t kk = mu >> 4;
-                    const uint32_t table = ch * 16u + uint32_t(mu & 15);
-                    zz[sl] = zig16(uint32_t(ic[sl] - kk) & 0xFFFFu);
-                    // entries past the table's n repeat its escape entry, flagged in bit 30
-                    if (zz[sl] < kCbEncHead) ee[sl] = ehead[lane * kCbEncLane + uint32_t(mu & 15) * kCbEncHead + zz[sl]];
-                    else ee[sl] = t.enc8[size_t(table) * 256 + min(zz[sl], 255u)];
-                }
-            }
-            // stage 3: escapes of step 127 - (it - 2 lag), in step order
-            {
-                const int k = kSteps - 1 - (it - 2 * kCbLag);
-                const int sl = (kSteps - 1 - d + 2 * kCbLag + 8 * P) % P;
-                if (k >= 0 && k < kSteps) {
-                    const uint32_t z = zz[sl];
-                    const bool esc = (ee[sl].y & 0x40000000u) != 0;
-                    // escaped values keep decode order: ranked like the words, written backwards
-                    const uint64_t b = __ballot(esc);
-                    const uint32_t mine = uint32_t(b >> half);
-                    if (esc) {
-                        const uint32_t pos = ecnt + __popc(uint32_t(uint64_t(mine) >> (lane + 1)));
-                        if (pos < MAXE) efwd[pos] = uint16_t(z);
-                    }
-                    ecnt += __popc(mine);
-                }
-            }
-            // stage 4: the state update of step 127 - (it - 3 lag)
-            {
-                const int k = kSteps - 1 - (it - 3 * kCbLag);
-                const int sl = (kSteps - 1 - d + 3 * kCbLag + 8 * P) % P;
-                if (k >= 0 && k < kSteps) {
-                    const uint32_t m = ee[sl].x, w = ee[sl].y;
-                    const uint32_t f = w & 0xFFFu;
-                    emit_words(x, cnt, x >= (f << 20), lane, half, wfwd, MAXW);
-                    const uint32_t qt = __umulhi(x + __builtin_amdgcn_ubfe(w, 29, 1), m) >>
-                                        __builtin_amdgcn_ubfe(w, 24, 5);                    // floor(x / f)
-                    x = x + __builtin_amdgcn_ubfe(w, 12, 12) + qt * (kM - f);
-                }
-            }
-        }
-    }
-    reinterpret_cast<uint32_t*>(area)[lane] = x;
-    if (lane == 0) {
-        const uint32_t bytes = (kStreamHead + 2 * cnt + 2 * ecnt + 3) & ~3u;
-        a.meta[sid] = bytes >= RAW ? 0x80000000u : (cnt | (ecnt << 14));
-    }
+    // blockIdx.y is the pass: every stream of the block is of that pass
+    uint16_t* wr = wring + (tid >> 5) * kCbEncRing;
+    uint16_t* er = ering + (tid >> 5) * kCbEncEsc;
+    if (blockIdx.y) encode_cb_stream<true>(a, t, g, sid, ehead, wr, er);
+    else encode_cb_stream<false>(a, t, g, sid, ehead, wr, er);
 }
 
 // --------------------------------------------------------------- index + compaction
@@ -3599,7 +3619,7 @@ hipError_t encode_code(const EncodeLaunch& a, const DevTables& t, hipStream_t st
         const Geo g{a.shape.channels, a.shape.tokens, a.shape.channels / kLanes, a.shape.tokens / 2 / kSteps};
         const dim3 grid(g.ncg * ((g.ntb + kCbEncStreams - 1) / kCbEncStreams), 2);       // y: pass
         timed("encode_streams", st, [&](hipEvent_t e0, hipEvent_t e1) {
-            hipExtLaunchKernelGGL((encode_cb<2, 7>), grid, dim3(kCbEncStreams * 32), 0, st, e0, e1, 0, a, t);
+            hipExtLaunchKernelGGL(encode_cb, grid, dim3(kCbEncStreams * 32), 0, st, e0, e1, 0, a, t);
         });
     } else {
         timed("encode_streams", st, [&](hipEvent_t e0, hipEvent_t e1) {

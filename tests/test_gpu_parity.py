@@ -138,6 +138,41 @@ def test_checkerboard_small(skv, orc):
     full_compare(skv, orc, coef, G, tabs, oshape, "checkerboard 1280x192")
 
 
+def test_checkerboard_escape_bursts_and_raw(skv, orc):
+    """Checkerboard streams whose escaped values come in bursts (a run of
+    coded steps where every lane escapes: more escaped values in 8 steps than
+    the encoder keeps in LDS), one whose every value escapes (stored raw), and
+    near-uniform values (a word from every lane at most steps); containers
+    equal the oracle's, both decode exactly."""
+    cfg = gen.CONFIGS[4].with_tokens(1280, channels=192)
+    coef, G = gen.dckv_draw(cfg, device="cuda")
+    cc, cg = gen.dckv_draw(cfg, gen.CALIB, tokens=256)
+    tabs = skv.fit_tables(skv.INT16, skv.CHECKERBOARD, 1, 1, 192, cc.numpy(), cg.numpy(), 256)
+    c = coef.cpu().numpy().copy()
+    rng = np.random.default_rng(31)
+    # even pass, token block 1, channel group 2: steps 16..39 all escaped (24 x 32 values)
+    for k in range(16, 40):
+        c[2 * (128 + k), 64:96] = rng.choice([30000, -30000, 29000, -29001], size=32)
+    # odd pass, token block 0, channel group 1: steps 100..102 (96 escapes in one 8-step batch)
+    for k in range(100, 103):
+        c[2 * k + 1, 32:64] = rng.integers(-32768, 32768, size=32)
+    # odd pass, token block 2, channel group 4: every value escapes -> stored raw
+    for k in range(128):
+        c[2 * (256 + k) + 1, 128:160] = rng.integers(-32768, 32768, size=32)
+    # even pass, token block 3, channel group 5: values spread over 81 more cells (6,288 bytes, coded)
+    for k in range(128):
+        c[2 * (384 + k), 160:192] = np.clip(c[2 * (384 + k), 160:192].astype(np.int64)
+                                            + rng.integers(-40, 41, size=32), -32768, 32767)
+    coef = torch.from_numpy(c).cuda()
+    oshape = orc.make_shape(orc.INT16, orc.CHECKERBOARD, 1, 1, 1280, 192)
+    want = full_compare(skv, orc, coef, G, tabs, oshape, "checkerboard escape bursts and raw")
+    n = orc.n_streams(oshape)
+    idx = np.frombuffer(want, dtype=np.uint64, count=n + 1, offset=64)
+    raw = idx >> np.uint64(63)
+    assert raw[(1 * 5 + 2) * 6 + 4] == 1, "the all-escaped stream is stored raw"
+    assert raw[(0 * 5 + 1) * 6 + 2] == 0 and raw[(1 * 5 + 0) * 6 + 1] == 0 and raw[(0 * 5 + 3) * 6 + 5] == 0
+
+
 def map_case(skv, orc, T, C, rank, device="cuda"):
     """Checkerboard data with a decoded-neighbour map of the given rank, its
     tables (fitted by the library) and the oracle's shape."""
