@@ -23,6 +23,7 @@ constexpr int kSyms = kLanes * kSteps;
 constexpr int kMaxDirect = 255;
 constexpr size_t kHeaderBytes = 64;
 constexpr size_t kTableRecord = 514;  // u16 n + u16 freq[256]
+constexpr uint32_t kCbHead = 32;       // checkerboard decoder: symbols per table whose starts it keeps in LDS
 constexpr size_t kStateBytes = 4 * kLanes;
 constexpr uint32_t kStreamHead = 4 * kLanes + 4;   // final states + word count
 constexpr uint64_t kRawBit = 1ull << 63;
@@ -92,7 +93,11 @@ struct DevTables {
     uint4* enc = nullptr;          // [n_tables][256] {freq<<20, divisor magic, 4096-freq, cum<<16 | shift}
     uint32_t* fc = nullptr;        // [n_tables][256] freq | cum<<16
     uint8_t* slot = nullptr;       // [n_tables][4096] slot -> symbol
-    uint8_t* half = nullptr;       // checkerboard blobs: [n_tables][2048] symbol of every even slot
+    // checkerboard blobs: the slots of each table past its first kCbHead symbols (the decoder keeps the
+    // starts of those in LDS), one entry per slot: symbol (255 for the escape symbol) | freq << 8 |
+    // cum << 20; table j's run starts at tail_base[j]
+    uint32_t* tail = nullptr;
+    uint32_t* tail_base = nullptr;
     uint2* enc8 = nullptr;         // checkerboard blobs: [n_tables][256] encode entries packed in 8 bytes:
                                    // {magic, f | start << 12 | shift << 24 | inc << 29 | escape << 30}
     uint8_t* base = nullptr;       // exponent-mode blobs: [slabs] class base

@@ -21,6 +21,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <mutex>
+#include <vector>
 
 #include <hip/hip_ext.h>
 
@@ -101,7 +102,8 @@ __device__ __forceinline__ uint32_t unzig(uint32_t z) { return (z >> 1) ^ (0u - 
 
 // --------------------------------------------------------------- tables
 __global__ __launch_bounds__(256) void expand_tables(const uint8_t* rec, uint32_t* tn, uint4* enc, uint32_t* fc,
-                                                     uint8_t* slot, uint8_t* half, uint2* enc8) {
+                                                     uint8_t* slot, uint32_t* tail, const uint32_t* tail_base,
+                                                     uint2* enc8) {
     __shared__ uint32_t cum[257];
     const uint32_t j = blockIdx.x, tid = threadIdx.x;
     const uint8_t* r = rec + size_t(j) * kTableRecord;
@@ -164,13 +166,15 @@ __global__ __launch_bounds__(256) void expand_tables(const uint8_t* rec, uint32_
     if (enc8)
         enc8[size_t(j) * 256 + tid] = make_uint2(e.y, (e.x >> 20) | ((e.w >> 16) << 12) | ((e.w & 31u) << 24) |
                                                           ((e.z >> 24) << 29) | (((e.w >> 8) & 1u) << 30));
-    // checkerboard tables (the ones with half maps) flag their escape symbol in bit 15 (f < 4096)
-    fc[size_t(j) * 256 + tid] = f | (c << 16) | (half && tid == n ? 0x8000u : 0u);
+    fc[size_t(j) * 256 + tid] = f | (c << 16);
     uint8_t* st = slot + size_t(j) * kM;
     for (uint32_t q = c; q < c + f; ++q) st[q] = uint8_t(tid);
-    if (half) {
-        uint8_t* sh = half + size_t(j) * (kM / 2);
-        for (uint32_t q = (c + 1) & ~1u; q < c + f; q += 2) sh[q / 2] = uint8_t(tid);
+    if (tail) {
+        // checkerboard tables: the slots from the start of symbol min(kCbHead, n) on (f < 4096)
+        const uint32_t ts = cum[min(kCbHead, n)];
+        uint32_t* tt = tail + tail_base[j] - ts;
+        const uint32_t ent = (tid == n ? 255u : tid) | (f << 8) | (c << 20);
+        for (uint32_t q = max(c, ts); q < c + f; ++q) tt[q] = ent;
     }
 }
 
@@ -340,10 +344,18 @@ __device__ __forceinline__ void encode_cb_stream(const EncodeLaunch& a, const De
     uint8_t* area = a.scratch + sid * (2 * RAW);
     uint16_t* wfwd = reinterpret_cast<uint16_t*>(area + RAW);           // words, emission order
     uint16_t* efwd = reinterpret_cast<uint16_t*>(area + kStreamHead);   // escaped values, emission order
-    const int16_t* coef = static_cast<const int16_t*>(a.target);
-    const int16_t* Gp = static_cast<const int16_t*>(PASS ? a.aux_odd : a.aux);
-    const size_t C = g.C;
+    const uint32_t C = g.C;
     const uint2* lhead = ehead + lane * kCbEncLane;
+    // rows are addressed from the block's first row (uniform) with 32-bit byte offsets: a block's 16
+    // token blocks span 4096 rows
+    const uint32_t tb0 = __builtin_amdgcn_readfirstlane(tb & ~(kCbEncStreams - 1u));
+    const size_t row0 = size_t(2u * tb0 * kSteps) * C;
+    const char* cbase = reinterpret_cast<const char*>(static_cast<const int16_t*>(a.target) + row0);
+    const char* gbase = reinterpret_cast<const char*>(static_cast<const int16_t*>(PASS ? a.aux_odd : a.aux) + row0);
+    const char* tbase = reinterpret_cast<const char*>(t.enc8);
+    const uint32_t tok0 = 2u * ((tb - tb0) * kSteps) + (PASS ? 1u : 0u);      // row of step 0, from row0
+    const bool last_blk = 2u * (tb * kSteps + kSteps - 1u) + 2u >= g.T;       // step 127's right row is past the end
+    auto at = [](const char* base, uint32_t off) { return int32_t(*reinterpret_cast<const int16_t*>(base + off)); };
 
     // inputs of batch j: step 127 - B j - i in slot i (j = NB loads step 0 again, unused)
     int32_t ic[B], ig[B], il[B], ir[B];
@@ -351,13 +363,12 @@ __device__ __forceinline__ void encode_cb_stream(const EncodeLaunch& a, const De
 #pragma unroll
         for (uint32_t i = 0; i < B; ++i) {
             const uint32_t k = j < NB ? kSteps - 1 - B * j - i : 0u;
-            const uint32_t tok = 2u * (tb * kSteps + k) + (PASS ? 1u : 0u);
-            const size_t r = size_t(tok) * C + ch;
-            ic[i] = coef[r];
-            ig[i] = Gp[r];
+            const uint32_t o = 2u * ((tok0 + 2u * k) * C + ch);               // byte offset of the step's element
+            ic[i] = at(cbase, o);
+            ig[i] = at(gbase, o);
             if constexpr (PASS) {
-                il[i] = coef[r - C];
-                ir[i] = coef[tok + 1 < g.T ? r + C : r - C];
+                il[i] = at(cbase, o - 2u * C);
+                ir[i] = at(cbase, last_blk && k == kSteps - 1 ? o - 2u * C : o + 2u * C);
             }
         }
     };
@@ -376,8 +387,8 @@ __device__ __forceinline__ void encode_cb_stream(const EncodeLaunch& a, const De
             const uint32_t z = zig16(uint32_t(ic[i] - kk) & 0xFFFFu);
             zs[i] = z | (sh << 16);
             // entries past the table's n repeat its escape entry, flagged in bit 30
-            const uint2* gp = z < kCbEncHead ? t.enc8 : t.enc8 + (size_t(ch) * 16u + sh) * 256 + min(z, 255u);
-            ge[i] = *gp;
+            const uint32_t eo = z < kCbEncHead ? 0u : 8u * ((ch * 16u + sh) * 256u + min(z, 255u));
+            ge[i] = *reinterpret_cast<const uint2*>(tbase + eo);
         }
         load_batch(j + 1);
 #pragma unroll
@@ -789,36 +800,242 @@ __global__ __launch_bounds__(256) void decode_streams(DecodeLaunch a, DevTables 
     if (bad) atomicOr(a.status, 1u);
 }
 
-// Checkerboard decoder with everything but the table lookups taken off the
-// state chain.  A step's side input and decoded neighbours (and from them its
-// table and mean) do not depend on the rANS state, so each lane loads them
-// 4 steps ahead.
-// Words come from two 32-word windows of the stream held in registers (lane i
-// of a half holds word base + i and base + 32 + i); a refilling lane fetches
-// its word from the window lane with ds_bpermute, and a window that has been
-// used up is replaced by the next 32 words while the other one is consumed.
-// So a step waits on its slot-map byte and its (frequency, start) word, both
-// in device memory, and on nothing else.  Output and checks are those of
-// decode_streams.
+// Checkerboard decoder.  A step's side input and decoded neighbours (and from
+// them its table and mean) do not depend on the rANS state; its table lookup
+// does.  The block's streams share one channel group, whose 32 x 16 tables
+// the block reads throughout: the starts of each table's first 32 symbols
+// (and of the 33rd) sit in LDS, so a slot below the 33rd start finds its
+// symbol by binary search there (start and frequency from neighbouring
+// starts); the other slots read one entry (symbol, frequency, start) of the
+// table's tail map in device memory, requested before the search so that the
+// two overlap.  Loads and stores share one counter, and a wait for a load is
+// also a wait for every load issued before it (and for every store), so a
+// lookup in device memory waits for whatever else is in flight.  The steps
+// therefore run in batches of 8 with nothing else in flight inside a batch:
+//   * the side inputs and neighbours of batch j + 1 are loaded, and batch j's
+//     outputs stored, between the two batches;
+//   * words come from a 512-word ring of the stream in LDS, escaped values
+//     from a 128-value ring; both are refilled between batches (256 words,
+//     64 values at a time) so that a batch never runs out of words and
+//     rarely of escaped values (past the ring, a value is read from device
+//     memory);
+//   * each table's direct-symbol count, for the escape check, sits in LDS.
+// Output and checks are those of decode_streams.
 // RANGE: token blocks tb_base onwards of the container (the shape is the
 // range's, rows are numbered from its start), and the range's last odd token
 // takes its right neighbour from next_rows when the range stops early.
-//
-// The block's streams share one channel group, whose 32 x 16 tables the block
-// reads throughout; the starts of each table's first 32 symbols (and of the
-// 33rd) sit in LDS, so a slot below the 33rd start finds its symbol by binary
-// search there (start and frequency from neighbouring starts) and only the
-// other lanes read the half slot map and rows from device memory.
-constexpr uint32_t kCbHead = 32;                         // symbols per table whose starts stay in LDS
 constexpr uint32_t kCbDecStreams = 16;                   // streams (half-waves) per block
 constexpr uint32_t kCbHeadRow = kCbHead + 1;
 // a lane's 16 rows take an odd number of dwords, so lanes start on different banks
 constexpr uint32_t kCbHeadLane = 16 * kCbHeadRow + 2;
-template <int kLag, int P, bool RANGE = false>
-__global__ __launch_bounds__(kCbDecStreams * 32) __attribute__((amdgpu_waves_per_eu(6))) void decode_cb(
-    DecodeLaunch a, DevTables t, uint64_t first, uint64_t count) {
+constexpr uint32_t kCbDecBatch = 8;                      // steps per batch
+constexpr uint32_t kCbWordRing = 512, kCbWordChunk = 256;   // words per stream ring / per refill
+constexpr uint32_t kCbEscRing = 128, kCbEscChunk = 64;      // escaped values per stream ring / per refill
+
+template <bool PASS, bool RANGE>
+__device__ __forceinline__ void decode_cb_stream(const DecodeLaunch& a, const DevTables& t, const Geo& g,
+                                                 uint64_t sid, const uint16_t* head, const uint16_t* nlds,
+                                                 const uint32_t* tbase, uint32_t* wring, uint32_t* ering) {
     constexpr uint32_t RAW = 2 * kSyms;
-    __shared__ uint16_t head[kLanes * kCbHeadLane];            // [lane][shift][symbol 0..32] starts
+    constexpr uint32_t B = kCbDecBatch, NB = kSteps / kCbDecBatch;
+    const uint32_t lane = threadIdx.x & 31u, half = threadIdx.x & 32u;
+    const uint32_t cg = uint32_t(sid % g.ncg);
+    const uint32_t tb = uint32_t((sid / g.ncg) % g.ntb);
+    const uint32_t ch = cg * kLanes + lane;
+    const uint32_t C = g.C;
+    const uint64_t xid = RANGE ? index_pos(a, PASS ? 1u : 0u, tb, cg, g.ncg) : sid;
+    const uint64_t e0 = a.index[xid], e1 = a.index[xid + 1];
+    const uint64_t off = e0 & ~kRawBit, end = e1 & ~kRawBit;
+    int16_t* out = static_cast<int16_t*>(a.out);
+    // rows are addressed from the block's first row (uniform) with 32-bit element offsets: a block's
+    // 16 token blocks span 4096 rows (plus the row after them)
+    const uint32_t tb0 = __builtin_amdgcn_readfirstlane(tb & ~(kCbDecStreams - 1u));
+    const size_t row0 = size_t(2u * tb0 * kSteps) * C;
+    int16_t* obase = out + row0;
+    // the odd pass's side input may be the output's odd rows (mapped in place): a lane loads each
+    // element's side input in the batch before the one that stores the element
+    const int16_t* gbase = static_cast<const int16_t*>(PASS ? a.aux_odd : a.aux) + row0;
+    const uint32_t tok0 = 2u * (tb - tb0) * kSteps;          // the stream's first even row, from row0
+    auto row_off = [&](uint32_t k) { return (tok0 + 2u * k + (PASS ? 1u : 0u)) * C + ch; };
+    if (end < off || end > a.payload_bytes) {
+        if (lane == 0) atomicOr(a.status, 1u);
+        return;
+    }
+    const uint64_t size = end - off;
+    if (e0 & kRawBit) {
+        if (size != RAW) {
+            if (lane == 0) atomicOr(a.status, 1u);
+            return;
+        }
+        for (uint32_t k = 0; k < uint32_t(kSteps); ++k)
+            obase[row_off(k)] = reinterpret_cast<const int16_t*>(a.pay + off)[k * kLanes + lane];
+        return;
+    }
+    const uint8_t* sp = a.pay + off;
+    if (size < kStreamHead || size % 4 != 0) {
+        if (lane == 0) atomicOr(a.status, 1u);
+        return;
+    }
+    const uint32_t nw = reinterpret_cast<const uint32_t*>(sp)[32];
+    if (nw > (size - kStreamHead) / 2) {
+        if (lane == 0) atomicOr(a.status, 1u);
+        return;
+    }
+    bool bad = false;
+    uint32_t x = reinterpret_cast<const uint32_t*>(sp)[lane];
+    if (x < kStateLow) bad = true;
+    const uint32_t body = uint32_t(size) - kStreamHead;       // bytes of words, escaped values and pad
+    const uint32_t ebase = kStreamHead + 2 * nw;              // byte offset of the escaped values
+    const uint32_t ecap = (body - 2 * nw) / 2;
+    const uint32_t below = (1u << lane) - 1u;
+    const uint16_t* wr16 = reinterpret_cast<const uint16_t*>(wring);
+    const uint16_t* er16 = reinterpret_cast<const uint16_t*>(ering);
+
+    // ring refills: every load is in bounds of the stream (a lane past it reads the stream's first
+    // dword and keeps 0); words past the count are never used by a valid stream
+    uint32_t wc[4], ec;
+    auto load_words = [&](uint32_t c) {                     // words 256 c .. 256 c + 255: dword q * 32 + lane in wc[q]
+#pragma unroll
+        for (uint32_t q = 0; q < 4; ++q) {
+            const uint32_t bo = 4u * (kCbWordChunk / 2 * c + q * kLanes + lane);
+            const bool in = bo + 4 <= body;
+            const uint32_t v = *reinterpret_cast<const uint32_t*>(sp + (in ? kStreamHead + bo : 0u));
+            wc[q] = in ? v : 0u;
+        }
+    };
+    auto write_words = [&](uint32_t c) {
+#pragma unroll
+        for (uint32_t q = 0; q < 4; ++q) wring[(kCbWordChunk / 2 * c + q * kLanes + lane) % (kCbWordRing / 2)] = wc[q];
+    };
+    auto load_esc = [&](uint32_t c) {                       // escaped values 64 c + 2 lane, + 1 in ec
+        const uint32_t i0 = kCbEscChunk * c + 2 * lane;
+        const bool in0 = i0 < ecap, in1 = i0 + 1 < ecap;
+        const uint32_t v0 = *reinterpret_cast<const uint16_t*>(sp + (in0 ? ebase + 2 * i0 : 0u));
+        const uint32_t v1 = *reinterpret_cast<const uint16_t*>(sp + (in1 ? ebase + 2 * i0 + 2 : 0u));
+        ec = (in0 ? v0 : 0u) | ((in1 ? v1 : 0u) << 16);
+    };
+    auto write_esc = [&](uint32_t c) { ering[(kCbEscChunk / 2 * c + lane) % (kCbEscRing / 2)] = ec; };
+    // side inputs (and the even neighbours) of batch j; j = NB reloads batch 0 (unused)
+    int32_t gin[B], ev[B + 1];
+    auto load_inputs = [&](uint32_t j) {
+        const uint32_t k0 = j < NB ? B * j : 0u;
+#pragma unroll
+        for (uint32_t i = 0; i < B; ++i) gin[i] = gbase[row_off(k0 + i)];
+        if constexpr (PASS) {
+#pragma unroll
+            for (uint32_t i = 0; i <= B; ++i) {
+                // even row left of odd step k0 + i; the last one is the right neighbour of step k0 + 7
+                const uint32_t eo = (tok0 + 2u * (k0 + i)) * C + ch;
+                if (i < B) {
+                    ev[i] = obase[eo];
+                } else {
+                    const bool past = 2u * (tb * kSteps + k0 + i) >= g.T;   // the row after the cache
+                    const int16_t* src = obase + (past ? eo - 2u * C : eo);
+                    if constexpr (RANGE)
+                        if (past && a.next_rows) src = a.next_rows + ch;
+                    ev[i] = *src;
+                }
+            }
+        }
+    };
+
+    uint32_t p = 0, ep = 0;                                  // words and escaped values consumed
+    uint32_t wl = 2 * kCbWordChunk, el = 2 * kCbEscChunk;    // loaded (next chunk to load at wl, el)
+    uint32_t elw = el;                                       // escaped values in the ring
+    load_words(0);
+    write_words(0);
+    load_words(1);
+    write_words(1);
+    load_esc(0);
+    write_esc(0);
+    load_esc(1);
+    write_esc(1);
+    load_inputs(0);
+    bool wpend = false, epend = false;
+    for (uint32_t j = 0; j < NB; ++j) {
+        if (wpend) write_words(wl / kCbWordChunk - 1);
+        if (epend) write_esc(el / kCbEscChunk - 1);
+        elw = el;
+        uint32_t o[B];
+#pragma unroll
+        for (uint32_t i = 0; i < B; ++i) {
+            int32_t mu = gin[i];
+            if constexpr (PASS) mu += 8 * (ev[i] + ev[i + 1]);
+            const int32_t kk = mu >> 4;
+            const uint32_t table = ch * 16u + uint32_t(mu & 15);
+            const uint32_t slot = x & (kM - 1u);
+            const uint32_t sh = table & 15u;
+            const uint32_t hb = lane * kCbHeadLane + sh * kCbHeadRow;
+            const uint32_t ts = head[hb + kCbHead];
+            const bool hit = slot < ts;
+            // slots past the LDS head: one read of the table's tail map, issued before the binary
+            // search so that the two overlap
+            uint32_t te = 0;
+            if (!hit) te = t.tail[tbase[lane * 16u + sh] + (slot - ts)];
+            // symbols 0..31: binary search of the starts in LDS
+            uint32_t zc = 0;
+#pragma unroll
+            for (uint32_t step = kCbHead / 2; step; step >>= 1) zc += head[hb + zc + step] <= slot ? step : 0u;
+            const uint32_t c0 = head[hb + zc], c1 = head[hb + zc + 1];
+            const uint32_t fq = hit ? c1 - c0 : (te >> 8) & 0x0FFFu;
+            const uint32_t cs = hit ? c0 : te >> 20;
+            const uint32_t s = hit ? zc : te & 255u;
+            x = fq * (x >> kProbBits) + slot - cs;
+            // refill in lane order from the word ring
+            const bool need = x < kStateLow;
+            const uint32_t mine = uint32_t(__ballot(need) >> half);
+            if (need) {
+                const uint32_t wi = p + __popc(mine & below);
+                if (wi >= nw) bad = true;
+                x = (x << 16) | uint32_t(wr16[wi % kCbWordRing]);
+            }
+            p += __popc(mine);
+            // escaped values, in lane order, from the escape ring (past it, from device memory)
+            const bool esc = !hit && (te & 255u) == 255u;
+            const uint32_t me = uint32_t(__ballot(esc) >> half);
+            uint32_t z = s;
+            if (esc) {
+                const uint32_t pos = ep + __popc(me & below);
+                uint32_t v = 0;
+                if (pos >= ecap) bad = true;
+                else if (pos < elw) v = er16[pos % kCbEscRing];
+                else v = *reinterpret_cast<const uint16_t*>(sp + ebase + 2 * pos);
+                if (v < nlds[lane * 16u + sh]) bad = true;   // a canonical encoder codes such a value directly
+                z = v;
+            }
+            ep += __popc(me);
+            o[i] = uint32_t(kk) + unzig(z);
+        }
+        // between batches: this batch's outputs, the next batch's inputs, the rings' next chunks
+#pragma unroll
+        for (uint32_t i = 0; i < B; ++i) obase[row_off(B * j + i)] = int16_t(uint16_t(o[i]));
+        load_inputs(j + 1);
+        wpend = wl <= p + kCbWordChunk;
+        if (wpend) {
+            load_words(wl / kCbWordChunk);
+            wl += kCbWordChunk;
+        }
+        epend = el <= ep + kCbEscChunk;
+        if (epend) {
+            load_esc(el / kCbEscChunk);
+            el += kCbEscChunk;
+        }
+    }
+    if (x != kStateLow || p != nw) bad = true;
+    const uint32_t used = kStreamHead + 2 * nw + 2 * ep;
+    if (((used + 3) & ~3u) != size) bad = true;
+    else if (lane < size - used && sp[used + lane] != 0) bad = true;   // zero pad
+    if (bad) atomicOr(a.status, 1u);
+}
+
+template <bool RANGE = false>
+__global__ __launch_bounds__(kCbDecStreams * 32) void decode_cb(DecodeLaunch a, DevTables t, uint64_t first,
+                                                               uint64_t count) {
+    __shared__ uint16_t head[kLanes * kCbHeadLane];                     // [lane][shift][symbol 0..32] starts
+    __shared__ uint16_t nlds[kLanes * 16];                              // [lane][shift] direct symbols
+    __shared__ uint32_t tbase[kLanes * 16];                             // [lane][shift] first tail-map entry
+    __shared__ uint32_t wring[kCbDecStreams * kCbWordRing / 2];         // [stream][word pair mod 256]
+    __shared__ uint32_t ering[kCbDecStreams * kCbEscRing / 2];          // [stream][escape pair mod 64]
     const uint32_t tid = threadIdx.x;
     const Geo g = geometry(a.shape);
     {
@@ -832,169 +1049,19 @@ __global__ __launch_bounds__(kCbDecStreams * 32) __attribute__((amdgpu_waves_per
             head[(j / 16) * kCbHeadLane + (j % 16) * kCbHeadRow + z] =
                 uint16_t(t.fc[size_t(table) * 256 + min(z, rt)] >> 16);
         }
+        for (uint32_t i = tid; i < kLanes * 16; i += blockDim.x) {
+            nlds[i] = uint16_t(t.n[bcg * (kLanes * 16) + i]);
+            tbase[i] = t.tail_base[bcg * (kLanes * 16) + i];
+        }
         __syncthreads();
     }
     uint64_t sid;
     if (!cb_stream<kCbDecStreams>(g, first, sid)) return;
-    const uint32_t lane = tid & 31u, half = tid & 32u;
-    const uint32_t cg = uint32_t(sid % g.ncg);
-    const uint32_t tb = uint32_t((sid / g.ncg) % g.ntb);
-    const uint32_t pass = uint32_t(sid / (uint64_t(g.ncg) * g.ntb));
-    const uint32_t ch = cg * kLanes + lane;
-    const size_t C = g.C;
-    const uint64_t* index = a.index;
-    const uint8_t* pay = a.pay;
-    const uint64_t xid = RANGE ? index_pos(a, pass, tb, cg, g.ncg) : sid;
-    const uint64_t e0 = index[xid], e1 = index[xid + 1];
-    const uint64_t off = e0 & ~kRawBit, end = e1 & ~kRawBit;
-    int16_t* out = static_cast<int16_t*>(a.out);
-    // the odd pass's side input may be the output's odd rows (mapped in place): a lane reads
-    // each element's side input in an earlier pipeline stage than it stores the element
-    const int16_t* Gp = static_cast<const int16_t*>(pass ? a.aux_odd : a.aux);
-    auto row_of = [&](uint32_t k) { return size_t(2u * (tb * kSteps + k) + pass) * C + ch; };
-    if (end < off || end > a.payload_bytes) {
-        if (lane == 0) atomicOr(a.status, 1u);
-        return;
-    }
-    const uint64_t size = end - off;
-    if (e0 & kRawBit) {
-        if (size != RAW) {
-            if (lane == 0) atomicOr(a.status, 1u);
-            return;
-        }
-        for (uint32_t k = 0; k < uint32_t(kSteps); ++k)
-            out[row_of(k)] = reinterpret_cast<const int16_t*>(pay + off)[k * kLanes + lane];
-        return;
-    }
-    const uint8_t* sp = pay + off;
-    if (size < kStreamHead || size % 4 != 0) {
-        if (lane == 0) atomicOr(a.status, 1u);
-        return;
-    }
-    const uint32_t nw = reinterpret_cast<const uint32_t*>(sp)[32];
-    if (nw > (size - kStreamHead) / 2) {
-        if (lane == 0) atomicOr(a.status, 1u);
-        return;
-    }
-    bool bad = false;
-    uint32_t x = reinterpret_cast<const uint32_t*>(sp)[lane];
-    if (x < kStateLow) bad = true;
-    const uint16_t* W = reinterpret_cast<const uint16_t*>(sp + kStreamHead);
-    const uint16_t* E = reinterpret_cast<const uint16_t*>(sp + kStreamHead + 2 * nw);
-    const uint32_t ecap = uint32_t((size - kStreamHead - 2 * nw) / 2);
-    // word windows: words past the stream's count read as 0 (a stream that needs them is corrupt)
-    auto word_at = [&](uint32_t i) -> uint32_t { return i < nw ? uint32_t(W[i]) : 0u; };
-    uint32_t base = 0, cur = word_at(lane), nxt = word_at(32 + lane);
-    uint32_t p = 0, ep = 0;
-    const uint32_t below = (1u << lane) - 1u;
-
-    int32_t ig[P], il[P], ir[P];                           // stage 1: side input and neighbours
-    int32_t kk[P];                                         // stage 2: mean cell
-    uint32_t tab[P];                                       // stage 2: table
-    constexpr int kIters = kSteps + 2 * kLag;
-    static_assert(P >= 2 * kLag + 1 && P % 2 == 0, "ring period covers the pipeline");
-    for (int it0 = 0; it0 < kIters; it0 += P) {
-#pragma unroll
-        for (int d = 0; d < P; ++d) {
-            const int it = it0 + d;
-            // stage 1: loads of step it
-            {
-                const int k = it;
-                const int sl = d % P;
-                if (k < kSteps) {
-                    const size_t r = row_of(uint32_t(k));
-                    ig[sl] = Gp[r];
-                    if (pass) {
-                        const uint32_t tok = 2u * (tb * kSteps + uint32_t(k)) + 1u;
-                        il[sl] = out[r - C];
-                        if constexpr (RANGE)
-                            ir[sl] = tok + 1 < g.T ? int32_t(out[r + C])
-                                                   : int32_t(a.next_rows ? a.next_rows[ch] : out[r - C]);
-                        else
-                            ir[sl] = tok + 1 < g.T ? int32_t(out[r + C]) : int32_t(out[r - C]);
-                    }
-                }
-            }
-            // stage 2: table, mean cell and direct count of step it - lag
-            {
-                const int k = it - kLag;
-                const int sl = (d - kLag + P) % P;
-                if (k >= 0 && k < kSteps) {
-                    int32_t mu = ig[sl];
-                    if (pass) mu += 8 * (il[sl] + ir[sl]);
-                    kk[sl] = mu >> 4;
-                    tab[sl] = ch * 16u + uint32_t(mu & 15);
-                }
-            }
-            // stage 3: the step it - 2 lag
-            {
-                const int k = it - 2 * kLag;
-                const int sl = (d - 2 * kLag + 2 * P) % P;
-                if (k >= 0 && k < kSteps) {
-                    const uint32_t table = tab[sl];
-                    const uint32_t slot = x & (kM - 1u);
-                    // symbols 0..31: binary search of the starts in LDS
-                    const uint32_t hb = lane * kCbHeadLane + (table & 15u) * kCbHeadRow;
-                    const bool hit = slot < head[hb + kCbHead];
-                    uint32_t zc = 0;
-#pragma unroll
-                    for (uint32_t step = kCbHead / 2; step; step >>= 1) zc += head[hb + zc + step] <= slot ? step : 0u;
-                    const uint32_t c0 = head[hb + zc], c1 = head[hb + zc + 1];
-                    // other slots: the even slot's symbol, then the rows of it and of the next symbol in one
-                    // 8-byte read: the odd slot belongs to the next one when that one starts there (never
-                    // past the escape symbol, whose row is flagged in bit 15)
-                    uint32_t s0 = 0;
-                    uint2 fr = make_uint2(0u, 0u);
-                    if (!hit) {
-                        s0 = t.half[size_t(table) * (kM / 2) + (slot >> 1)];
-                        __builtin_memcpy(&fr, t.fc + size_t(table) * 256 + s0, 8);
-                    }
-                    const bool last = (fr.x & 0x8000u) != 0;
-                    const bool adv = !last && slot >= (fr.y >> 16);
-                    const uint32_t s = hit ? zc : s0 + (adv ? 1u : 0u);
-                    const uint32_t fcv = hit ? (c1 - c0) | (c0 << 16) : (adv ? fr.y : fr.x);
-                    x = (fcv & 0x0FFFu) * (x >> kProbBits) + slot - (fcv >> 16);
-                    // refill in lane order from the word windows
-                    const bool need = x < kStateLow;
-                    const uint32_t mine = uint32_t(__ballot(need) >> half);
-                    const uint32_t idx = p + __popc(mine & below) - base;                 // < 64
-                    const int src = int(((idx & 31u) + half) << 2);
-                    const uint32_t wc = __builtin_amdgcn_ds_bpermute(src, int(cur));
-                    const uint32_t wn = __builtin_amdgcn_ds_bpermute(src, int(nxt));
-                    if (need) {
-                        if (p + __popc(mine & below) >= nw) bad = true;
-                        x = (x << 16) | (idx < 32 ? wc : wn);
-                    }
-                    p += __popc(mine);
-                    if (p - base >= 32) {
-                        // the first window is used up: the second moves in and the next 32 words load
-                        base += 32;
-                        cur = nxt;
-                        nxt = word_at(base + 32 + lane);
-                    }
-                    // escaped values, in lane order, from the escape region
-                    const bool esc = (fcv & 0x8000u) != 0;
-                    const uint32_t me = uint32_t(__ballot(esc) >> half);
-                    uint32_t z = s;
-                    if (esc) {
-                        const uint32_t pos = ep + __popc(me & below);
-                        uint32_t v = 0;
-                        if (pos < ecap) v = E[pos];
-                        else bad = true;
-                        if (v < t.n[table]) bad = true;        // a canonical encoder codes such a value directly
-                        z = v;
-                    }
-                    ep += __popc(me);
-                    out[row_of(uint32_t(k))] = int16_t(uint16_t(uint32_t(kk[sl]) + unzig(z)));
-                }
-            }
-        }
-    }
-    if (x != kStateLow || p != nw) bad = true;
-    const uint32_t used = kStreamHead + 2 * nw + 2 * ep;
-    if (((used + 3) & ~3u) != size) bad = true;
-    else if (lane < size - used && sp[used + lane] != 0) bad = true;   // zero pad
-    if (bad) atomicOr(a.status, 1u);
+    uint32_t* wr = wring + (tid >> 5) * (kCbWordRing / 2);
+    uint32_t* er = ering + (tid >> 5) * (kCbEscRing / 2);
+    // every stream of the launch is of one pass
+    if (first >= uint64_t(g.ncg) * g.ntb) decode_cb_stream<true, RANGE>(a, t, g, sid, head, nlds, tbase, wr, er);
+    else decode_cb_stream<false, RANGE>(a, t, g, sid, head, nlds, tbase, wr, er);
 }
 
 // =============================================================== LDS kernels
@@ -3744,7 +3811,7 @@ hipError_t decode_all(const DecodeLaunch& a, const DevTables& t, hipStream_t st)
         x.out = a.next_rows;
         x.next_rows = nullptr;
         timed("decode_streams", st, [&](hipEvent_t e0, hipEvent_t e1) {
-            hipExtLaunchKernelGGL((decode_cb<2, 6, true>), cb_grid(ncg), dim3(kCbDecStreams * 32), 0, st, e0, e1, 0, x,
+            hipExtLaunchKernelGGL((decode_cb<true>), cb_grid(ncg), dim3(kCbDecStreams * 32), 0, st, e0, e1, 0, x,
                                   t, 0, ncg);
         });
     }
@@ -3758,10 +3825,10 @@ hipError_t decode_all(const DecodeLaunch& a, const DevTables& t, hipStream_t st)
         }
         timed("decode_streams", st, [&](hipEvent_t e0, hipEvent_t e1) {
             if (MODE == SKV_CHECKERBOARD && range)
-                hipExtLaunchKernelGGL((decode_cb<2, 6, true>), cb_grid(per), dim3(kCbDecStreams * 32), 0, st, e0, e1, 0, a, t,
+                hipExtLaunchKernelGGL((decode_cb<true>), cb_grid(per), dim3(kCbDecStreams * 32), 0, st, e0, e1, 0, a, t,
                                       ps * per, per);
             else if (MODE == SKV_CHECKERBOARD && fits)
-                hipExtLaunchKernelGGL((decode_cb<2, 6>), cb_grid(per), dim3(kCbDecStreams * 32), 0, st, e0, e1, 0, a, t,
+                hipExtLaunchKernelGGL((decode_cb<false>), cb_grid(per), dim3(kCbDecStreams * 32), 0, st, e0, e1, 0, a, t,
                                       ps * per, per);
             else
                 hipExtLaunchKernelGGL((decode_streams<DT, MODE>), dim3(grid), dim3(256), 0, st, e0, e1, 0, a, t, ps * per, per);
@@ -3786,7 +3853,25 @@ hipError_t build_dev_tables(const uint8_t* blob, DevTables* t, hipStream_t st) {
     if (e == hipSuccess) e = hipMalloc(&t->enc, size_t(nt) * 256 * sizeof(uint4));
     if (e == hipSuccess) e = hipMalloc(&t->fc, size_t(nt) * 256 * 4 + 16);   // + one entry read past the last row
     if (e == hipSuccess) e = hipMalloc(&t->slot, size_t(nt) * kM);
-    if (e == hipSuccess && is_checkerboard(blob[7])) e = hipMalloc(&t->half, size_t(nt) * (kM / 2));
+    std::vector<uint32_t> tail_base;
+    if (e == hipSuccess && is_checkerboard(blob[7])) {
+        // each table's tail: the slots from the start of symbol min(kCbHead, n) to the end
+        tail_base.resize(nt);
+        uint64_t total = 0;
+        for (uint32_t j = 0; j < nt; ++j) {
+            const uint8_t* r = blob + kHeaderBytes + size_t(j) * kTableRecord;
+            const uint32_t n = std::min(kCbHead, rd16(r));
+            uint32_t ts = 0;
+            for (uint32_t z = 0; z < n; ++z) ts += rd16(r + 2 + 2 * z);
+            tail_base[j] = uint32_t(total);
+            total += kM - std::min<uint32_t>(ts, kM);
+        }
+        if (total >> 32) e = hipErrorInvalidValue;
+        if (e == hipSuccess) e = hipMalloc(&t->tail, std::max<uint64_t>(total, 1) * 4);
+        if (e == hipSuccess) e = hipMalloc(&t->tail_base, size_t(nt) * 4);
+        if (e == hipSuccess)
+            e = hipMemcpyAsync(t->tail_base, tail_base.data(), size_t(nt) * 4, hipMemcpyHostToDevice, st);
+    }
     if (e == hipSuccess && is_checkerboard(blob[7])) e = hipMalloc(&t->enc8, size_t(nt) * 256 * sizeof(uint2));
     if (e == hipSuccess && blob[7] == SKV_CHECKERBOARD_MAP) {
         // the map section follows the records (validated with the blob)
@@ -3807,8 +3892,8 @@ hipError_t build_dev_tables(const uint8_t* blob, DevTables* t, hipStream_t st) {
         e = hipMemcpyAsync(t->base, blob + kHeaderBytes + size_t(nt) * kTableRecord, nbase, hipMemcpyHostToDevice, st);
     if (e == hipSuccess) e = hipMemcpyAsync(rec, blob + kHeaderBytes, size_t(nt) * kTableRecord, hipMemcpyHostToDevice, st);
     if (e == hipSuccess) {
-        hipLaunchKernelGGL(expand_tables, dim3(nt), dim3(256), 0, st, rec, t->n, t->enc, t->fc, t->slot, t->half,
-                           t->enc8);
+        hipLaunchKernelGGL(expand_tables, dim3(nt), dim3(256), 0, st, rec, t->n, t->enc, t->fc, t->slot, t->tail,
+                           t->tail_base, t->enc8);
         e = hipGetLastError();
     }
     if (e == hipSuccess) e = hipStreamSynchronize(st);
@@ -3825,7 +3910,8 @@ void free_dev_tables(DevTables* t) {
     if (t->enc) (void)hipFree(t->enc);
     if (t->fc) (void)hipFree(t->fc);
     if (t->slot) (void)hipFree(t->slot);
-    if (t->half) (void)hipFree(t->half);
+    if (t->tail) (void)hipFree(t->tail);
+    if (t->tail_base) (void)hipFree(t->tail_base);
     if (t->enc8) (void)hipFree(t->enc8);
     if (t->base) (void)hipFree(t->base);
     if (t->map_v) (void)hipFree(t->map_v);

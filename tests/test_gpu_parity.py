@@ -597,6 +597,50 @@ def test_decode_range_checkerboard(skv, orc, mapped):
             assert np.array_equal(out.cpu().numpy(), want[256:768])
 
 
+def test_checkerboard_corruption_verdicts(skv, orc):
+    """Damaged checkerboard containers: the decoder reaches the oracle's verdict
+    on every bit flip anywhere in a coded stream (states, word count, words,
+    escaped values, pad), in even and odd passes; where the stream stays
+    consistent both decode alike."""
+    cfg = gen.CONFIGS[4].with_tokens(1024, channels=128)
+    coef, G = gen.dckv_draw(cfg, device="cuda")
+    cc, cg = gen.dckv_draw(cfg, gen.CALIB, tokens=256)
+    tabs = skv.fit_tables(skv.INT16, skv.CHECKERBOARD, 1, 1, 128, cc.numpy(), cg.numpy(), 256)
+    c = coef.cpu().numpy().copy()
+    rng = np.random.default_rng(41)
+    for k in range(20, 30):                                # escaped values in an odd-pass stream
+        c[2 * k + 1, 0:32] = rng.integers(-32768, 32768, size=32)
+    coef = torch.from_numpy(c).cuda()
+    cont = skv.encode(tabs, coef, G)
+    good = cont.cpu().numpy()
+    n, idx, head = _parse(good.tobytes())
+    gn = G.cpu().numpy()
+    trials = refused = 0
+    while trials < 32:
+        st = int(rng.integers(0, n))
+        if idx[st] >> np.uint64(63):
+            continue
+        a = int(idx[st] & np.uint64((1 << 63) - 1))
+        b = int(idx[st + 1] & np.uint64((1 << 63) - 1))
+        bad = good.copy()
+        pos = head + int(rng.integers(a, b))
+        bad[pos] ^= np.uint8(1 << int(rng.integers(0, 8)))
+        say(f"[parity] checkerboard corrupt trial {trials}: stream {st} byte {pos}")
+        want = np.zeros_like(c)
+        rc = orc.decode_rc(tabs.bytes(), bad.tobytes(), gn, want)
+        if rc == orc.E_CORRUPT:
+            with pytest.raises(skv.SkvError) as e:
+                skv.decode(tabs, torch.from_numpy(bad).cuda(), G)
+            assert e.value.status == skv.ERR_CORRUPT
+            refused += 1
+        else:
+            assert rc == orc.OK
+            assert np.array_equal(skv.decode(tabs, torch.from_numpy(bad).cuda(), G).cpu().numpy(), want)
+        trials += 1
+    assert refused >= 16
+    assert torch.equal(skv.decode(tabs, cont, G), coef)
+
+
 def test_corruption_and_wrong_tables(skv, orc):
     cfg = gen.Config(92, "corrupt-bf16", "bf16", 1, 2, 256, 64)
     t, p, tabs, oshape = residual_case(skv, orc, cfg)
