@@ -814,13 +814,14 @@ __global__ __launch_bounds__(256) void decode_streams(DecodeLaunch a, DevTables 
 // therefore run in batches of 8 with nothing else in flight inside a batch:
 //   * the side inputs and neighbours of batch j + 1 are loaded, and batch j's
 //     outputs stored, between the two batches;
-//   * words come from a 512-word ring of the stream in LDS, escaped values
-//     from a 128-value ring; both are refilled between batches (256 words,
-//     64 values at a time) so that a batch never runs out of words and
-//     rarely of escaped values (past the ring, a value is read from device
-//     memory);
+//   * words come from a 384-word ring of the stream in LDS, escaped values
+//     from a 128-value ring; both are refilled between batches (128-word
+//     chunks, one or two, and 64 values at a time) so that a batch never runs
+//     out of words and rarely of escaped values (past the ring, a value is
+//     read from device memory);
 //   * each table's direct-symbol count, for the escape check, sits in LDS.
-// Output and checks are those of decode_streams.
+// The block's LDS (53 KB) and registers (at most 80) leave room for three
+// blocks per CU.  Output and checks are those of decode_streams.
 // RANGE: token blocks tb_base onwards of the container (the shape is the
 // range's, rows are numbered from its start), and the range's last odd token
 // takes its right neighbour from next_rows when the range stops early.
@@ -829,7 +830,7 @@ constexpr uint32_t kCbHeadRow = kCbHead + 1;
 // a lane's 16 rows take an odd number of dwords, so lanes start on different banks
 constexpr uint32_t kCbHeadLane = 16 * kCbHeadRow + 2;
 constexpr uint32_t kCbDecBatch = 8;                      // steps per batch
-constexpr uint32_t kCbWordRing = 512, kCbWordChunk = 256;   // words per stream ring / per refill
+constexpr uint32_t kCbWordRing = 384, kCbWordChunk = 128;   // words per stream ring / per refill
 constexpr uint32_t kCbEscRing = 128, kCbEscChunk = 64;      // escaped values per stream ring / per refill
 
 template <bool PASS, bool RANGE>
@@ -893,19 +894,21 @@ __device__ __forceinline__ void decode_cb_stream(const DecodeLaunch& a, const De
 
     // ring refills: every load is in bounds of the stream (a lane past it reads the stream's first
     // dword and keeps 0); words past the count are never used by a valid stream
+    // a batch consumes at most 256 words; between batches one or two 128-word chunks come in
     uint32_t wc[4], ec;
-    auto load_words = [&](uint32_t c) {                     // words 256 c .. 256 c + 255: dword q * 32 + lane in wc[q]
+    auto load_words = [&](uint32_t c, uint32_t r) {         // words 128 c .. 128 c + 127: dword q * 32 + lane in wc[2 r + q]
 #pragma unroll
-        for (uint32_t q = 0; q < 4; ++q) {
+        for (uint32_t q = 0; q < 2; ++q) {
             const uint32_t bo = 4u * (kCbWordChunk / 2 * c + q * kLanes + lane);
             const bool in = bo + 4 <= body;
             const uint32_t v = *reinterpret_cast<const uint32_t*>(sp + (in ? kStreamHead + bo : 0u));
-            wc[q] = in ? v : 0u;
+            wc[2 * r + q] = in ? v : 0u;
         }
     };
-    auto write_words = [&](uint32_t c) {
+    auto write_words = [&](uint32_t c, uint32_t r) {
 #pragma unroll
-        for (uint32_t q = 0; q < 4; ++q) wring[(kCbWordChunk / 2 * c + q * kLanes + lane) % (kCbWordRing / 2)] = wc[q];
+        for (uint32_t q = 0; q < 2; ++q)
+            wring[(kCbWordChunk / 2 * c + q * kLanes + lane) % (kCbWordRing / 2)] = wc[2 * r + q];
     };
     auto load_esc = [&](uint32_t c) {                       // escaped values 64 c + 2 lane, + 1 in ec
         const uint32_t i0 = kCbEscChunk * c + 2 * lane;
@@ -942,21 +945,27 @@ __device__ __forceinline__ void decode_cb_stream(const DecodeLaunch& a, const De
     uint32_t p = 0, ep = 0;                                  // words and escaped values consumed
     uint32_t wl = 2 * kCbWordChunk, el = 2 * kCbEscChunk;    // loaded (next chunk to load at wl, el)
     uint32_t elw = el;                                       // escaped values in the ring
-    load_words(0);
-    write_words(0);
-    load_words(1);
-    write_words(1);
+    load_words(0, 0);
+    load_words(1, 1);
+    write_words(0, 0);
+    write_words(1, 1);
     load_esc(0);
     write_esc(0);
     load_esc(1);
     write_esc(1);
     load_inputs(0);
-    bool wpend = false, epend = false;
+    uint32_t wpend = 0;                                      // chunks loaded after the last batch (0..2)
+    bool epend = false;
     for (uint32_t j = 0; j < NB; ++j) {
-        if (wpend) write_words(wl / kCbWordChunk - 1);
+        if (wpend == 2) {
+            write_words(wl / kCbWordChunk - 2, 0);
+            write_words(wl / kCbWordChunk - 1, 1);
+        } else if (wpend == 1) {
+            write_words(wl / kCbWordChunk - 1, 0);
+        }
         if (epend) write_esc(el / kCbEscChunk - 1);
         elw = el;
-        uint32_t o[B];
+        uint32_t o[B / 2];                                   // outputs, two per register
 #pragma unroll
         for (uint32_t i = 0; i < B; ++i) {
             int32_t mu = gin[i];
@@ -1004,16 +1013,25 @@ __device__ __forceinline__ void decode_cb_stream(const DecodeLaunch& a, const De
                 z = v;
             }
             ep += __popc(me);
-            o[i] = uint32_t(kk) + unzig(z);
+            const uint32_t ov = (uint32_t(kk) + unzig(z)) & 0xFFFFu;
+            o[i / 2] = i % 2 ? o[i / 2] | (ov << 16) : ov;
         }
         // between batches: this batch's outputs, the next batch's inputs, the rings' next chunks
 #pragma unroll
-        for (uint32_t i = 0; i < B; ++i) obase[row_off(B * j + i)] = int16_t(uint16_t(o[i]));
+        for (uint32_t i = 0; i < B; ++i) obase[row_off(B * j + i)] = int16_t(uint16_t(o[i / 2] >> (16 * (i % 2))));
         load_inputs(j + 1);
-        wpend = wl <= p + kCbWordChunk;
-        if (wpend) {
-            load_words(wl / kCbWordChunk);
+        // words [p, p + 256) must be in the ring at the next batch's start; a chunk overwrites the
+        // words 384 before it, which are consumed once wl < p + 256
+        wpend = 0;
+        if (wl < p + 2 * kCbWordChunk) {
+            load_words(wl / kCbWordChunk, 0);
             wl += kCbWordChunk;
+            wpend = 1;
+            if (wl < p + 2 * kCbWordChunk) {
+                load_words(wl / kCbWordChunk, 1);
+                wl += kCbWordChunk;
+                wpend = 2;
+            }
         }
         epend = el <= ep + kCbEscChunk;
         if (epend) {
@@ -1029,7 +1047,7 @@ __device__ __forceinline__ void decode_cb_stream(const DecodeLaunch& a, const De
 }
 
 template <bool RANGE = false>
-__global__ __launch_bounds__(kCbDecStreams * 32) void decode_cb(DecodeLaunch a, DevTables t, uint64_t first,
+__global__ __launch_bounds__(kCbDecStreams * 32) __attribute__((amdgpu_waves_per_eu(6))) void decode_cb(DecodeLaunch a, DevTables t, uint64_t first,
                                                                uint64_t count) {
     __shared__ uint16_t head[kLanes * kCbHeadLane];                     // [lane][shift][symbol 0..32] starts
     __shared__ uint16_t nlds[kLanes * 16];                              // [lane][shift] direct symbols
