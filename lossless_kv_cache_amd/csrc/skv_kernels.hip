@@ -274,18 +274,25 @@ __global__ __launch_bounds__(256) void encode_streams(EncodeLaunch a, DevTables 
     }
 }
 
-// Stream of this half-wave in the checkerboard kernels: a block codes 8
-// token blocks of one channel group, and the blocks dispatched to one XCD
-// (round-robin over the 8 XCDs) sweep one channel group after another, so the
-// tables an XCD reads at a time (16 per component) stay in its L2.  Returns
-// false for a half-wave past the pass's last token block.
+// Stream of this half-wave in the checkerboard kernels: a block codes HW
+// token blocks of one channel group (64 bytes of each int16 row), and the
+// blocks dispatched to one XCD (round-robin over the 8 XCDs) sweep one pair of
+// channel groups after another, the two groups of a pair taking the same
+// token blocks side by side: the two halves of a 128-byte row line are read
+// (and written) by blocks that run together on one XCD, and the tables the
+// XCD reads at a time (16 per component, two groups) stay in its L2.  Returns
+// the block's index in group-major order (channel group, then token blocks).
 // HW: half-waves (streams) per block.
 template <uint32_t HW = 8>
 __device__ __forceinline__ uint32_t cb_block(const Geo& g) {
     const uint32_t bpc = (g.ntb + HW - 1) / HW;            // blocks per channel group
     const uint32_t total = g.ncg * bpc;
     const uint32_t b = blockIdx.x;
-    return total % 8 == 0 ? (b % 8) * (total / 8) + b / 8 : b;
+    if (total % 8 != 0) return b;
+    const uint32_t q = (b % 8) * (total / 8) + b / 8;      // position in the XCD's sweep
+    if (g.ncg % 2 != 0) return q;
+    const uint32_t pair = q / (2 * bpc), r = q % (2 * bpc);
+    return (2 * pair + (r & 1u)) * bpc + r / 2;
 }
 // The channel group of this block (the same for all its half-waves; ncg or
 // more for a block past the last one).
