@@ -173,6 +173,20 @@ def test_checkerboard_escape_bursts_and_raw(skv, orc):
     assert raw[(0 * 5 + 1) * 6 + 2] == 0 and raw[(1 * 5 + 0) * 6 + 1] == 0 and raw[(0 * 5 + 3) * 6 + 5] == 0
 
 
+@pytest.mark.parametrize("tokens,channels", [(16384, 64), (32768, 160), (16640, 64)])
+def test_checkerboard_block_orders(skv, orc, tokens, channels):
+    """The checkerboard kernels' block orders: channel groups paired on an XCD
+    (an even group count, 8 or more blocks per XCD), one group after another
+    (an odd group count), and dispatch order (a block count that the 8 XCDs do
+    not divide); whole containers equal the oracle's, both decode exactly."""
+    cfg = gen.CONFIGS[4].with_tokens(tokens, channels=channels)
+    coef, G = gen.dckv_draw(cfg, device="cuda")
+    cc, cg = gen.dckv_draw(cfg, gen.CALIB, tokens=256)
+    tabs = skv.fit_tables(skv.INT16, skv.CHECKERBOARD, 1, 1, channels, cc.numpy(), cg.numpy(), 256)
+    oshape = orc.make_shape(orc.INT16, orc.CHECKERBOARD, 1, 1, tokens, channels)
+    full_compare(skv, orc, coef, G, tabs, oshape, f"checkerboard {tokens}x{channels}")
+
+
 def map_case(skv, orc, T, C, rank, device="cuda"):
     """Checkerboard data with a decoded-neighbour map of the given rank, its
     tables (fitted by the library) and the oracle's shape."""
