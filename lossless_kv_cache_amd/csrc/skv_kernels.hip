@@ -3421,7 +3421,7 @@ __device__ __forceinline__ void load16(const int16_t* p, uint32_t (&d)[8]) {
 // the last one (the last odd token's right neighbour), or null for the end of
 // the cache (the last odd token repeats its left row).
 template <uint32_t KT, bool VEC>
-__global__ __launch_bounds__(256) void nbr_map(const int16_t* coef, const int16_t* __restrict__ G, int16_t* out,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KT <= 4 ? 4 : 1))) void nbr_map(const int16_t* coef, const int16_t* __restrict__ G, int16_t* out,
                                                uint32_t T, uint32_t C, const int8_t* __restrict__ V,
                                                const int8_t* __restrict__ U, uint32_t sh_h, uint32_t sh_m,
                                                const int16_t* right) {
@@ -3435,28 +3435,91 @@ __global__ __launch_bounds__(256) void nbr_map(const int16_t* coef, const int16_
     const uint32_t nodd = T / 2;
     const uint32_t W2 = 2 * C;
 
-    // 1. H = N V^T: this lane's A row is odd token u0 + r16 (inputs k < C
-    //    from its left row, k >= C from its right row; 2C is a multiple of
-    //    64 and no 16-wide piece straddles C); the next 64-wide step's inputs
-    //    are loaded while the current one multiplies
+    // 1. H = N V^T over the 2C inputs of odd token u: [its left row | its right
+    //    row], i.e. even rows 2u and 2u + 2.  The workgroup's 64 odd tokens
+    //    share 65 even rows, so the sum runs by column block: for columns
+    //    [x, x + 64) the workgroup loads the 65 rows' columns and both matching
+    //    V slices (V[:, x..] for left rows, V[:, C + x..] for right rows) into
+    //    LDS once, and each wavefront takes the left and the right product of
+    //    its 16 tokens from there (a lane's A row: slot 16 w + r16 on the left,
+    //    the next slot on the right).  The next block's tiles are loaded into
+    //    registers while the current one multiplies.  A 32-wide last block
+    //    (C an odd multiple of 32) is one product: k-quarters 0-1 from the left
+    //    row, 2-3 from the right one.
+    constexpr uint32_t kSlots = kMapTok + 1;                // even rows of the workgroup
+    constexpr uint32_t kAVec = (kSlots * 8 + 255) / 256;    // 16-byte pieces of the row tile per thread
+    constexpr uint32_t kVVec = (2 * K * 4 + 255) / 256;     // of the V tiles
+    __shared__ __align__(16) int16_t atile[kSlots * 64];    // [slot][64 columns]
+    __shared__ __align__(16) int8_t vtile[2 * K * 64];      // [side][rank][64 columns]
+    __shared__ v4i sink[256];                               // stores of pieces past the tiles
     v4i hi[KT], lo[KT];
 #pragma unroll
     for (uint32_t j = 0; j < KT; ++j) hi[j] = lo[j] = v4i{0, 0, 0, 0};
     {
-        const uint32_t u = min(u0 + r16, nodd - 1);           // (always u0 + r16: the grid covers T / 2 exactly)
-        const uint32_t t = 2 * u + 1;
-        const int16_t* lrow = coef + size_t(t - 1) * C;
-        const int16_t* rrow = t + 1 < T ? coef + size_t(t + 1) * C : (right ? right : lrow);
-        auto src = [&](uint32_t kk) { return kk < C ? lrow + kk : rrow + (kk - C); };
-        uint32_t cur[8], nxt[8];
-        load16<VEC>(src(16 * g4), cur);
-        for (uint32_t kb = 0; kb < W2; kb += 64) {
-            const uint32_t kk = kb + 16 * g4;
-            if (kb + 64 < W2) load16<VEC>(src(kk + 64), nxt);
-            v4i bv[KT];
+        const uint32_t ub = blockIdx.x * kMapTok;              // first odd index of the workgroup
+        // even row of slot e: row 2 (ub + e); the slot past the cache's end (the last odd token's
+        // right neighbour) is `right`, or the last odd token's left row again
+        auto slot_row = [&](uint32_t e) __attribute__((always_inline)) -> const int16_t* {
+            const uint32_t r = 2 * (ub + e);
+            return r < T ? coef + size_t(r) * C : (right ? right : coef + size_t(r - 2) * C);
+        };
+        v4i ar[kAVec], vr[kVVec];                          // (native vectors: kept in registers)
+        // a block is 64 or 32 columns wide: 8 or 4 sixteen-byte pieces per row slot, 4 or 2 per V row
+        // and side (shifts: 3 or 2, 2 or 1)
+        auto load_block = [&](uint32_t x) __attribute__((always_inline)) {
+            const uint32_t ws = C - x >= 64 ? 3u : 2u;
 #pragma unroll
-            for (uint32_t j = 0; j < KT; ++j)
-                bv[j] = *reinterpret_cast<const v4i*>(V + size_t(j * 16 + r16) * W2 + kk);
+            for (uint32_t i = 0; i < kAVec; ++i) {
+                const uint32_t idx0 = threadIdx.x + 256 * i;
+                const uint32_t idx = idx0 < (kSlots << ws) ? idx0 : 0u;     // (past the tile: piece 0 again, unused)
+                const int16_t* src = slot_row(idx >> ws) + x + 8 * (idx & ((1u << ws) - 1u));
+                if (VEC) {
+                    ar[i] = *reinterpret_cast<const v4i*>(src);
+                } else {
+                    uint32_t d[4];
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        d[q] = uint32_t(uint16_t(src[2 * q])) | (uint32_t(uint16_t(src[2 * q + 1])) << 16);
+                    ar[i] = v4i{int(d[0]), int(d[1]), int(d[2]), int(d[3])};
+                }
+            }
+            const uint32_t vs = ws - 1u;
+#pragma unroll
+            for (uint32_t i = 0; i < kVVec; ++i) {
+                const uint32_t idx0 = threadIdx.x + 256 * i;
+                const uint32_t idx = idx0 < (2 * K << vs) ? idx0 : 0u;
+                const uint32_t r = idx >> vs;                  // side * K + rank
+                const uint32_t sd = r / K, rk = r % K;
+                vr[i] = *reinterpret_cast<const v4i*>(V + size_t(rk) * W2 + sd * C + x +
+                                                        16 * (idx & ((1u << vs) - 1u)));
+            }
+        };
+        // pieces past the tiles go to a sink, so that every thread stores every piece
+        auto store_block = [&](uint32_t x) __attribute__((always_inline)) {
+            const uint32_t ws = C - x >= 64 ? 3u : 2u, vs = ws - 1u;
+#pragma unroll
+            for (uint32_t i = 0; i < kAVec; ++i) {
+                const uint32_t idx = threadIdx.x + 256 * i;
+                v4i* dst = idx < (kSlots << ws)
+                                 ? reinterpret_cast<v4i*>(atile + (idx >> ws) * 64 + 8 * (idx & ((1u << ws) - 1u)))
+                                 : sink + threadIdx.x;
+                *dst = ar[i];
+            }
+#pragma unroll
+            for (uint32_t i = 0; i < kVVec; ++i) {
+                const uint32_t idx = threadIdx.x + 256 * i;
+                v4i* dst = idx < (2 * K << vs)
+                                 ? reinterpret_cast<v4i*>(vtile + (idx >> vs) * 64 + 16 * (idx & ((1u << vs) - 1u)))
+                                 : sink + threadIdx.x;
+                *dst = vr[i];
+            }
+        };
+        // one product: A = 16 int16 inputs of the lane (split into int8 halves), B = V rows
+        auto product = [&](const int16_t* arow, const int8_t* vside) __attribute__((always_inline)) {
+            uint32_t cur[8];
+            const uint4 c0 = reinterpret_cast<const uint4*>(arow)[0], c1 = reinterpret_cast<const uint4*>(arow)[1];
+            cur[0] = c0.x; cur[1] = c0.y; cur[2] = c0.z; cur[3] = c0.w;
+            cur[4] = c1.x; cur[5] = c1.y; cur[6] = c1.z; cur[7] = c1.w;
             uint32_t pl[4], ph[4];
 #pragma unroll
             for (int d = 0; d < 4; ++d) split4(cur[2 * d], cur[2 * d + 1], pl[d], ph[d]);
@@ -3464,11 +3527,25 @@ __global__ __launch_bounds__(256) void nbr_map(const int16_t* coef, const int16_
             const v4i al = {int(pl[0]), int(pl[1]), int(pl[2]), int(pl[3])};
 #pragma unroll
             for (uint32_t j = 0; j < KT; ++j) {
-                hi[j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(ah, bv[j], hi[j], 0, 0, 0);
-                lo[j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(al, bv[j], lo[j], 0, 0, 0);
+                const v4i bv = *reinterpret_cast<const v4i*>(vside + (j * 16 + r16) * 64);
+                hi[j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(ah, bv, hi[j], 0, 0, 0);
+                lo[j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(al, bv, lo[j], 0, 0, 0);
             }
-#pragma unroll
-            for (int i = 0; i < 8; ++i) cur[i] = nxt[i];
+        };
+        const uint32_t e = w * 16 + r16;                     // the lane's left slot
+        load_block(0);
+        for (uint32_t x = 0; x < C; x += 64) {
+            __syncthreads();                                 // the last block's tiles are no longer read
+            store_block(x);
+            __syncthreads();
+            if (x + 64 < C) load_block(x + 64);
+            if (x + 64 <= C) {
+                product(atile + e * 64 + 16 * g4, vtile + 16 * g4);                     // left rows
+                product(atile + (e + 1) * 64 + 16 * g4, vtile + K * 64 + 16 * g4);      // right rows
+            } else {
+                const uint32_t q = g4 & 1u, sd = g4 >> 1;     // 32-wide block
+                product(atile + (e + sd) * 64 + 16 * q, vtile + sd * K * 64 + 16 * q);
+            }
         }
     }
     // 2. q to LDS: element r of tile j is token 4 g4 + r of the wavefront, rank column 16 j + r16
