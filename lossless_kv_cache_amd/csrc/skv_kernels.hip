@@ -3566,41 +3566,70 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KT <= 4 ? 4
     // 3. out = G + round(U Q^T), transposed so that a lane holds 4 consecutive
     //    channels of one token: A = U rows (channels), B = the wavefront's q
     //    rows (tokens); element r of a tile is channel 4 g4 + r of token r16.
-    //    Up to four 16-channel tiles per round (channels are a multiple of 32,
-    //    not always of 64), their loads issued together.
+    //    Rounds of 64 channels (up to four 16-channel tiles; channels are a
+    //    multiple of 32, not always of 64): the round's U rows go into LDS once
+    //    for the workgroup (the V tile's space), and the next round's U rows and
+    //    side inputs are loaded while the current round multiplies.
     v4i bq[KB];
 #pragma unroll
     for (uint32_t kb = 0; kb < KB; ++kb)
         bq[kb] = *reinterpret_cast<const v4i*>(qw + r16 * KP + kb * 64 + 16 * g4);
     const uint32_t u = u0 + r16;
     const size_t row = size_t(2 * min(u, nodd - 1) + 1) * C;
-    for (uint32_t c0 = 0; c0 < C; c0 += 64) {
-        v4i au[4][KB];
-        uint2 gv[4];
+    constexpr uint32_t kUPieces = K / 16;                   // 16-byte pieces of a U row
+    constexpr uint32_t kUVec = (64 * kUPieces + 255) / 256;
+    int8_t* utile = vtile;                                  // [64 channels][K]
+    v4i ur[kUVec];
+    uint2 gv[4], gn[4];
+    auto load_round = [&](uint32_t c0) __attribute__((always_inline)) {
+        const uint32_t pieces = min(64u, C - c0) * kUPieces;
+#pragma unroll
+        for (uint32_t i = 0; i < kUVec; ++i) {
+            const uint32_t idx0 = threadIdx.x + 256 * i;
+            const uint32_t idx = idx0 < pieces ? idx0 : 0u;
+            ur[i] = *reinterpret_cast<const v4i*>(U + size_t(c0 + idx / kUPieces) * K + 16 * (idx % kUPieces));
+        }
         const uint32_t ntile = min(4u, (C - c0) / 16);       // 2 or 4
 #pragma unroll
         for (uint32_t tt = 0; tt < 4; ++tt) {
-            if (tt >= ntile) break;
-            const uint32_t c = c0 + 16 * tt;
-#pragma unroll
-            for (uint32_t kb = 0; kb < KB; ++kb) {
-                const uint32_t kk = kb * 64 + 16 * g4;
-                au[tt][kb] = kk < K ? *reinterpret_cast<const v4i*>(U + size_t(c + r16) * K + kk) : v4i{0, 0, 0, 0};
-            }
-            const int16_t* gp = G + row + c + 4 * g4;
+            const int16_t* gp = G + row + c0 + 16 * (tt < ntile ? tt : 0u) + 4 * g4;
             if (VEC) {
-                gv[tt] = *reinterpret_cast<const uint2*>(gp);
+                gn[tt] = *reinterpret_cast<const uint2*>(gp);
             } else {
-                gv[tt].x = uint32_t(uint16_t(gp[0])) | (uint32_t(uint16_t(gp[1])) << 16);
-                gv[tt].y = uint32_t(uint16_t(gp[2])) | (uint32_t(uint16_t(gp[3])) << 16);
+                gn[tt].x = uint32_t(uint16_t(gp[0])) | (uint32_t(uint16_t(gp[1])) << 16);
+                gn[tt].y = uint32_t(uint16_t(gp[2])) | (uint32_t(uint16_t(gp[3])) << 16);
             }
         }
+    };
+    auto store_round = [&](uint32_t c0) __attribute__((always_inline)) {
+        const uint32_t pieces = min(64u, C - c0) * kUPieces;
+#pragma unroll
+        for (uint32_t i = 0; i < kUVec; ++i) {
+            const uint32_t idx = threadIdx.x + 256 * i;
+            v4i* dst = idx < pieces ? reinterpret_cast<v4i*>(utile + 16 * idx) : sink + threadIdx.x;
+            *dst = ur[i];
+        }
+    };
+    load_round(0);
+    for (uint32_t c0 = 0; c0 < C; c0 += 64) {
+        __syncthreads();                                     // the last round's (or phase 1's) tile reads are done
+        store_round(c0);
+        __syncthreads();
+#pragma unroll
+        for (uint32_t tt = 0; tt < 4; ++tt) gv[tt] = gn[tt];
+        if (c0 + 64 < C) load_round(c0 + 64);
+        const uint32_t ntile = min(4u, (C - c0) / 16);       // 2 or 4
 #pragma unroll
         for (uint32_t tt = 0; tt < 4; ++tt) {
             if (tt >= ntile) break;
             v4i acc = {0, 0, 0, 0};
 #pragma unroll
-            for (uint32_t kb = 0; kb < KB; ++kb) acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(au[tt][kb], bq[kb], acc, 0, 0, 0);
+            for (uint32_t kb = 0; kb < KB; ++kb) {
+                const uint32_t kk = kb * 64 + 16 * g4;
+                const v4i au = kk < K ? *reinterpret_cast<const v4i*>(utile + (16 * tt + r16) * K + kk)
+                                      : v4i{0, 0, 0, 0};
+                acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(au, bq[kb], acc, 0, 0, 0);
+            }
             const int32_t gq[4] = {int32_t(int16_t(gv[tt].x & 0xFFFFu)), int32_t(gv[tt].x) >> 16,
                                    int32_t(int16_t(gv[tt].y & 0xFFFFu)), int32_t(gv[tt].y) >> 16};
             uint32_t o[4];
