@@ -875,8 +875,15 @@ __device__ __forceinline__ void decode_cb_stream(const DecodeLaunch& a, const De
             if (lane == 0) atomicOr(a.status, 1u);
             return;
         }
-        for (uint32_t k = 0; k < uint32_t(kSteps); ++k)
-            obase[row_off(k)] = reinterpret_cast<const int16_t*>(a.pay + off)[k * kLanes + lane];
+        // a raw stream: its 4096 values in (step, lane) order, 16 steps loaded before any is stored
+        const int16_t* rv = reinterpret_cast<const int16_t*>(a.pay + off);
+        for (uint32_t k0 = 0; k0 < uint32_t(kSteps); k0 += 16) {
+            int16_t v[16];
+#pragma unroll
+            for (uint32_t i = 0; i < 16; ++i) v[i] = rv[(k0 + i) * kLanes + lane];
+#pragma unroll
+            for (uint32_t i = 0; i < 16; ++i) obase[row_off(k0 + i)] = v[i];
+        }
         return;
     }
     const uint8_t* sp = a.pay + off;
