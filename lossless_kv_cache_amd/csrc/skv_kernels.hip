@@ -3456,9 +3456,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KT <= 4 ? 4
     constexpr uint32_t kSlots = kMapTok + 1;                // even rows of the workgroup
     constexpr uint32_t kAVec = (kSlots * 8 + 255) / 256;    // 16-byte pieces of the row tile per thread
     constexpr uint32_t kVVec = (2 * K * 4 + 255) / 256;     // of the V tiles
-    __shared__ __align__(16) int16_t atile[kSlots * 64];    // [slot][64 columns]
-    __shared__ __align__(16) int8_t vtile[2 * K * 64];      // [side][rank][64 columns]
-    __shared__ v4i sink[256];                               // stores of pieces past the tiles
+    __shared__ __align__(16) int16_t atile[2][kSlots * 64]; // two buffers: [slot][64 columns]
+    __shared__ __align__(16) int8_t vtile[2][2 * K * 64];   // two buffers: [side][rank][64 columns]
+    __shared__ v4i sink[64];                                // stores of pieces past the tiles (any content)
     v4i hi[KT], lo[KT];
 #pragma unroll
     for (uint32_t j = 0; j < KT; ++j) hi[j] = lo[j] = v4i{0, 0, 0, 0};
@@ -3502,22 +3502,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KT <= 4 ? 4
             }
         };
         // pieces past the tiles go to a sink, so that every thread stores every piece
-        auto store_block = [&](uint32_t x) __attribute__((always_inline)) {
+        auto store_block = [&](uint32_t x, uint32_t bf) __attribute__((always_inline)) {
             const uint32_t ws = C - x >= 64 ? 3u : 2u, vs = ws - 1u;
 #pragma unroll
             for (uint32_t i = 0; i < kAVec; ++i) {
                 const uint32_t idx = threadIdx.x + 256 * i;
                 v4i* dst = idx < (kSlots << ws)
-                                 ? reinterpret_cast<v4i*>(atile + (idx >> ws) * 64 + 8 * (idx & ((1u << ws) - 1u)))
-                                 : sink + threadIdx.x;
+                               ? reinterpret_cast<v4i*>(atile[bf] + (idx >> ws) * 64 + 8 * (idx & ((1u << ws) - 1u)))
+                               : sink + (threadIdx.x & 63u);
                 *dst = ar[i];
             }
 #pragma unroll
             for (uint32_t i = 0; i < kVVec; ++i) {
                 const uint32_t idx = threadIdx.x + 256 * i;
                 v4i* dst = idx < (2 * K << vs)
-                                 ? reinterpret_cast<v4i*>(vtile + (idx >> vs) * 64 + 16 * (idx & ((1u << vs) - 1u)))
-                                 : sink + threadIdx.x;
+                               ? reinterpret_cast<v4i*>(vtile[bf] + (idx >> vs) * 64 + 16 * (idx & ((1u << vs) - 1u)))
+                               : sink + (threadIdx.x & 63u);
                 *dst = vr[i];
             }
         };
@@ -3539,20 +3539,27 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KT <= 4 ? 4
                 lo[j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(al, bv, lo[j], 0, 0, 0);
             }
         };
+        // two tile buffers: block b in buffer b & 1; block b + 1 goes into the other buffer while block b
+        // multiplies (that buffer's last reader, block b - 1, ended at the barrier before), so one
+        // barrier per block
         const uint32_t e = w * 16 + r16;                     // the lane's left slot
         load_block(0);
-        for (uint32_t x = 0; x < C; x += 64) {
-            __syncthreads();                                 // the last block's tiles are no longer read
-            store_block(x);
-            __syncthreads();
-            if (x + 64 < C) load_block(x + 64);
+        store_block(0, 0);
+        if (64 < C) load_block(64);
+        __syncthreads();
+        for (uint32_t x = 0, bf = 0; x < C; x += 64, bf ^= 1u) {
+            const int16_t* at = atile[bf];
+            const int8_t* vt = vtile[bf];
             if (x + 64 <= C) {
-                product(atile + e * 64 + 16 * g4, vtile + 16 * g4);                     // left rows
-                product(atile + (e + 1) * 64 + 16 * g4, vtile + K * 64 + 16 * g4);      // right rows
+                product(at + e * 64 + 16 * g4, vt + 16 * g4);                         // left rows
+                product(at + (e + 1) * 64 + 16 * g4, vt + K * 64 + 16 * g4);          // right rows
             } else {
                 const uint32_t q = g4 & 1u, sd = g4 >> 1;     // 32-wide block
-                product(atile + (e + sd) * 64 + 16 * q, vtile + sd * K * 64 + 16 * q);
+                product(at + (e + sd) * 64 + 16 * q, vt + sd * K * 64 + 16 * q);
             }
+            if (x + 64 < C) store_block(x + 64, bf ^ 1u);
+            if (x + 128 < C) load_block(x + 128);
+            __syncthreads();
         }
     }
     // 2. q to LDS: element r of tile j is token 4 g4 + r of the wavefront, rank column 16 j + r16
@@ -3585,7 +3592,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KT <= 4 ? 4
     const size_t row = size_t(2 * min(u, nodd - 1) + 1) * C;
     constexpr uint32_t kUPieces = K / 16;                   // 16-byte pieces of a U row
     constexpr uint32_t kUVec = (64 * kUPieces + 255) / 256;
-    int8_t* utile = vtile;                                  // [64 channels][K]
+    int8_t* const ubuf = vtile[0];                           // two buffers of [64 channels][K]
     v4i ur[kUVec];
     uint2 gv[4], gn[4];
     auto load_round = [&](uint32_t c0) __attribute__((always_inline)) {
@@ -3608,23 +3615,25 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KT <= 4 ? 4
             }
         }
     };
-    auto store_round = [&](uint32_t c0) __attribute__((always_inline)) {
+    auto store_round = [&](uint32_t c0, uint32_t bf) __attribute__((always_inline)) {
         const uint32_t pieces = min(64u, C - c0) * kUPieces;
 #pragma unroll
         for (uint32_t i = 0; i < kUVec; ++i) {
             const uint32_t idx = threadIdx.x + 256 * i;
-            v4i* dst = idx < pieces ? reinterpret_cast<v4i*>(utile + 16 * idx) : sink + threadIdx.x;
+            v4i* dst = idx < pieces ? reinterpret_cast<v4i*>(ubuf + bf * 64 * K + 16 * idx) : sink + (threadIdx.x & 63u);
             *dst = ur[i];
         }
     };
+    // as in the first product: round r's U rows in buffer r & 1, one barrier per round (phase 1's
+    // last barrier and phase 2's leave the V tiles free)
     load_round(0);
-    for (uint32_t c0 = 0; c0 < C; c0 += 64) {
-        __syncthreads();                                     // the last round's (or phase 1's) tile reads are done
-        store_round(c0);
-        __syncthreads();
+    store_round(0, 0);
 #pragma unroll
-        for (uint32_t tt = 0; tt < 4; ++tt) gv[tt] = gn[tt];
-        if (c0 + 64 < C) load_round(c0 + 64);
+    for (uint32_t tt = 0; tt < 4; ++tt) gv[tt] = gn[tt];
+    if (64 < C) load_round(64);
+    __syncthreads();
+    for (uint32_t c0 = 0, bf = 0; c0 < C; c0 += 64, bf ^= 1u) {
+        const int8_t* utile = ubuf + bf * 64 * K;
         const uint32_t ntile = min(4u, (C - c0) / 16);       // 2 or 4
 #pragma unroll
         for (uint32_t tt = 0; tt < 4; ++tt) {
@@ -3655,6 +3664,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KT <= 4 ? 4
                 }
             }
         }
+        if (c0 + 64 < C) {
+            store_round(c0 + 64, bf ^ 1u);
+#pragma unroll
+            for (uint32_t tt = 0; tt < 4; ++tt) gv[tt] = gn[tt];
+        }
+        if (c0 + 128 < C) load_round(c0 + 128);
+        __syncthreads();
     }
 }
 
