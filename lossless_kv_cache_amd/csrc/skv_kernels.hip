@@ -1822,9 +1822,6 @@ __device__ __forceinline__ void encode_groups_body(const EncodeLaunch& a, const 
         ring_b[c] = uint32_t(uintptr_t(ring)) + grp * kPairRing * 2;   // LDS byte offsets
         ring32[c] = reinterpret_cast<const uint32_t*>(ring + grp * kPairRing * 2);
     }
-    const uint32_t idle_b = uint32_t(uintptr_t(tile)) + 2 * (threadIdx.x & 63u);
-    uint32_t lowm = upper ? 0u : 0xFFFFFFFFu;
-    asm("" : "+v"(lowm));                                  // kept as a lane mask
 
     const uint32_t rowb = geo.C;
     // target and predictor rows of the slab's channel groups through one buffer resource each:
@@ -1931,21 +1928,35 @@ __device__ __forceinline__ void encode_groups_body(const EncodeLaunch& a, const 
                     ec[c] = entry(c, znext);
                     if constexpr (EXP) escf[c] = (r == kTileSteps - 1 ? 0u : escf[c]) | e.w;
                     // words leave before the state absorbs the symbol
-                    uint32_t xs = x[c];
-                    const bool emit = xs >= e.x;
-                    const uint64_t mw = __ballot(emit);
+                    // emit = x >= threshold, as a lane mask in vcc and a copy in mw; xs = x, or x >> 16
+                    // where a word leaves (one select reading the high half of x)
+                    uint32_t xs;
+                    uint64_t mw;
+                    asm("v_cmp_ge_u32_e32 vcc, %2, %3\n\t"
+                        "s_mov_b64 %1, vcc\n\t"
+                        "v_cndmask_b32_sdwa %0, %2, %2, vcc dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD "
+                        "src1_sel:WORD_1"
+                        : "=v"(xs), "=s"(mw)
+                        : "v"(x[c]), "v"(e.x)
+                        : "vcc");
                     const uint32_t mlo = uint32_t(mw), mhi = uint32_t(mw >> 32);
-                    const uint32_t pp = __popc(mlo) | (__popc(mhi) << 16);
-                    // ring slot: this half's count mod 128 plus the emitting lanes below it in the half
-                    // (an upper lane's mbcnt_lo sees no lower-half flag through lowm); a lane that emits
-                    // nothing stores to its own slot of the idle tile instead, so the store needs no branch
+                    const uint32_t plo = __popc(mlo);
+                    const uint32_t pp = plo | (__popc(mhi) << 16);
+                    // ring slot: this half's count plus the emitting lanes below it in the half, mod 128;
+                    // an upper lane's mbcnt_lo counts every emitting lane of the lower half, which its
+                    // base (the upper count less that number, formed on the scalar unit) takes back out
                     const uint32_t slot = __builtin_amdgcn_mbcnt_hi(
-                        mhi, __builtin_amdgcn_mbcnt_lo(mlo & lowm, __builtin_amdgcn_ubfe(wp[c], fsh, 7)));
-                    const uint32_t ra = ring_b[c] + 2 * (slot & (kPairRing - 1));
-                    uint32_t wa;
-                    asm("v_cndmask_b32_e64 %0, %1, %2, %3" : "=v"(wa) : "v"(idle_b), "v"(ra), "s"(mw));
-                    *reinterpret_cast<lds_u16*>(wa) = uint16_t(xs & 0xFFFFu);
-                    xs = emit ? xs >> 16 : xs;
+                        mhi, __builtin_amdgcn_mbcnt_lo(mlo, __builtin_amdgcn_ubfe(wp[c] - (plo << 16), fsh, 7)));
+                    uint32_t ra;
+                    asm("v_lshl_add_u32 %0, %1, 1, %2" : "=v"(ra) : "v"(slot & (kPairRing - 1)), "v"(ring_b[c]));
+                    // the word is stored by the emitting lanes only (exec narrowed to mw and restored)
+                    uint64_t keep;
+                    asm volatile("s_and_saveexec_b64 %0, %1\n\t"
+                                 "ds_write_b16 %2, %3\n\t"
+                                 "s_or_b64 exec, exec, %0"
+                                 : "=&s"(keep)
+                                 : "s"(mw), "v"(ra), "v"(x[c])
+                                 : "memory");
                     const uint32_t qt = __umulhi(xs + (e.z >> 24), e.y) >> (e.w & 31u);   // floor(xs / f)
                     // x = xs + qt (4096 - f) + start, the start taken from the high half of e.w
                     const uint32_t xq = __umul24(qt, e.z) + xs;
