@@ -1929,11 +1929,13 @@ __device__ __forceinline__ void encode_groups_body(const EncodeLaunch& a, const 
                     if constexpr (EXP) escf[c] = (r == kTileSteps - 1 ? 0u : escf[c]) | e.w;
                     // words leave before the state absorbs the symbol
                     // emit = x >= threshold, as a lane mask in vcc and a copy in mw; xs = x, or x >> 16
-                    // where a word leaves (one select reading the high half of x)
+                    // where a word leaves (one select reading the high half of x).  A VALU read of an SGPR
+                    // that a VALU wrote needs two wait states in between: the copy and one nop
                     uint32_t xs;
                     uint64_t mw;
                     asm("v_cmp_ge_u32_e32 vcc, %2, %3\n\t"
                         "s_mov_b64 %1, vcc\n\t"
+                        "s_nop 0\n\t"
                         "v_cndmask_b32_sdwa %0, %2, %2, vcc dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD "
                         "src1_sel:WORD_1"
                         : "=v"(xs), "=s"(mw)
