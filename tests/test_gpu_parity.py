@@ -323,6 +323,26 @@ def test_e4m3_wide_tables(skv, orc, noise, lo, hi):
 
 
 @pytest.mark.parametrize("exp", [False, True])
+def test_e4m3_encoders_many_draws(skv, orc, exp):
+    """The e4m3 encoders (128 channels: the two-group coders, per-channel or
+    exponent-class tables) over twelve seeded draws: three seeds, predictors
+    at the workload's noise and moved by 2, 5 and 12 steps in value order, so
+    streams range from a few words per step to near-raw.  Every container
+    equals the oracle's and decodes exactly."""
+    mode, omode = (skv.RESIDUAL_EXP, orc.RESIDUAL_EXP) if exp else (skv.RESIDUAL, orc.RESIDUAL)
+    for seed in (90, 91, 92):
+        cfg = gen.Config(seed, f"draws-e4m3-{seed}", "e4m3", 2, 2, 640, 128)
+        t, p0 = gen.residual_array(cfg, device="cuda")
+        ct, cp0 = gen.residual_array(cfg, gen.CALIB, tokens=256)
+        for noise in (0, 2, 5, 12):
+            p = p0 if noise == 0 else _ordered_noise(t, noise, seed)
+            cp = cp0 if noise == 0 else _ordered_noise(ct, noise, seed + 100)
+            tabs = skv.fit_tables(skv.E4M3, mode, 2, 2, 128, ct.numpy(), cp.numpy(), 256)
+            oshape = orc.make_shape(orc.E4M3, omode, 2, 2, 640, 128)
+            full_compare(skv, orc, t, p, tabs, oshape, f"e4m3 seed {seed} noise {noise} exp {exp}")
+
+
+@pytest.mark.parametrize("exp", [False, True])
 @pytest.mark.parametrize("dtype", ["bf16", "e4m3"])
 def test_word_bursts_after_escapes(skv, orc, dtype, exp):
     """Every token block escapes in its first 4 steps and codes rare direct
