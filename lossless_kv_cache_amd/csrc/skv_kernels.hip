@@ -2623,7 +2623,7 @@ __global__ __launch_bounds__(1024, 1) void decode_e4m3(DecodeLaunch a, DevTables
         DecState st[kDecChains];
         uint32_t tb[kDecChains], nw[kDecChains], size[kDecChains], rel[kDecChains];
         uint32_t cw[kDecChains], pva[kDecChains], pvb[kDecChains], rowo[kDecChains];
-        uint32_t ew[kDecChains], ea[kDecChains];
+        uint32_t ew[kDecChains], ea[kDecChains], ewr[kDecChains];
         // ring upkeep, both halves packed (lower in bits 0..15): ldk = chunk held in cw,
         // wrk = last chunk written to the ring, live = 0x8000 in the field of a half with
         // a coded stream
@@ -2701,6 +2701,7 @@ __global__ __launch_bounds__(1024, 1) void decode_e4m3(DecodeLaunch a, DevTables
             ldk[c] = kDecFirst * 0x00010001u;
             wrk[c] = 0x00010001u;
             st[c] = DecState{x, 0u, 0u};
+            ewr[c] = 0;
         }
         if (padv != 0) bad = true;
         __builtin_amdgcn_wave_barrier();
@@ -2769,7 +2770,7 @@ __global__ __launch_bounds__(1024, 1) void decode_e4m3(DecodeLaunch a, DevTables
                         const uint32_t sh = (__builtin_ctz(f | 0x80000000u) >> 3) * 8;   // byte of the value
                         const uint32_t pos = eidx + ea[c];
                         const uint32_t wv = __builtin_amdgcn_ds_bpermute(
-                            int(((pos >> 2) + (upper ? 32u : 0u)) << 2), int(ew[c]));
+                            int(((pos >> 2) + (upper ? 32u : 0u)) << 2), int(ewr[c]));
                         uint32_t e = (wv >> ((pos & 3u) * 8)) & 0xFFu;
                         if (__ballot(f != 0 && pos >= kDecEscWin) != 0) {
                             const uint32_t g = __builtin_amdgcn_raw_buffer_load_b8(
@@ -2801,6 +2802,13 @@ __global__ __launch_bounds__(1024, 1) void decode_e4m3(DecodeLaunch a, DevTables
         // one tile: its steps (with the previous tile's finish inside the first one), its symbols
         // to the tile buffer, ring upkeep; pvp holds the previous tile's predictor row
         auto tile_at = [&](uint32_t T, uint32_t (&pvp)[kDecChains]) {
+            if (T == 1) {
+                // the window dword again, written by a VALU move: its load is waited for once, here,
+                // and not in the escape path, where the wait would also cover every later load (the
+                // predictor rows requested two tiles ahead)
+#pragma unroll
+                for (uint32_t c = 0; c < kDecChains; ++c) asm volatile("v_mov_b32 %0, %1" : "=v"(ewr[c]) : "v"(ew[c]));
+            }
             uint32_t sy[kDecChains][kDecTile];
             DecState s0[kDecChains];
 #pragma unroll
@@ -3099,7 +3107,7 @@ __global__ __launch_bounds__(1024, 1) void decode_bf16(DecodeLaunch a, DevTables
         uint32_t tb[kDecChains], nw[kDecChains], size[kDecChains], rel[kDecChains];
         uint32_t cw[kDecChains], rowo[kDecChains];
         uint2 pva[kDecChains], pvb[kDecChains];
-        uint32_t ew[kDecChains], ea[kDecChains];
+        uint32_t ew[kDecChains], ea[kDecChains], ewr[kDecChains];
         // ring upkeep, both halves packed (lower in bits 0..15): ldk = chunk held in cw,
         // wrk = last chunk written to the ring, live = 0x8000 in the field of a half with
         // a coded stream
@@ -3178,6 +3186,7 @@ __global__ __launch_bounds__(1024, 1) void decode_bf16(DecodeLaunch a, DevTables
             ldk[c] = kBfFirst * 0x00010001u;
             wrk[c] = 0x00010001u;
             st[c] = DecState{x, 0u, 0u};
+            ewr[c] = 0;
         }
         if (padv != 0) bad = true;
         __builtin_amdgcn_wave_barrier();
@@ -3267,7 +3276,7 @@ __global__ __launch_bounds__(1024, 1) void decode_bf16(DecodeLaunch a, DevTables
                         const uint32_t kv = __builtin_ctz(f | 0x80000000u) >> 3;         // value 0..3
                         const uint32_t pos = 2 * eidx + ea[c];
                         const uint32_t wv = __builtin_amdgcn_ds_bpermute(
-                            int(((pos >> 2) + (upper ? 32u : 0u)) << 2), int(ew[c]));
+                            int(((pos >> 2) + (upper ? 32u : 0u)) << 2), int(ewr[c]));
                         uint32_t e = (wv >> ((pos & 3u) * 8)) & 0xFFFFu;
                         if (__ballot(f != 0 && pos >= kDecEscWin) != 0) {
                             const uint32_t g = __builtin_amdgcn_raw_buffer_load_b16(
@@ -3297,6 +3306,13 @@ __global__ __launch_bounds__(1024, 1) void decode_bf16(DecodeLaunch a, DevTables
         // one tile: its steps (with the previous tile's finish inside the first one), its symbols
         // to the tile buffer, ring upkeep; pvp holds the previous tile's predictor row
         auto tile_at = [&](uint32_t T, uint2 (&pvp)[kDecChains]) {
+            if (T == 1) {
+                // the window dword again, written by a VALU move: its load is waited for once, here,
+                // and not in the escape path, where the wait would also cover every later load (the
+                // predictor rows requested two tiles ahead)
+#pragma unroll
+                for (uint32_t c = 0; c < kDecChains; ++c) asm volatile("v_mov_b32 %0, %1" : "=v"(ewr[c]) : "v"(ew[c]));
+            }
             uint32_t sy[kDecChains][kDecTile];
             DecState s0[kDecChains];
 #pragma unroll
