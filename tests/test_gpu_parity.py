@@ -510,13 +510,16 @@ def test_exponent_mode_full_size_bf16(skv, orc, cid):
 RANGES = [(0, 1024), (0, 128), (896, 1024), (256, 640), (128, 1024)]
 
 
-@pytest.mark.parametrize("dtype,aligned", [("e4m3", True), ("bf16", True), ("bf16", False)])
-def test_decode_range(skv, orc, dtype, aligned):
+@pytest.mark.parametrize("dtype,aligned,exp", [("e4m3", True, False), ("e4m3", False, False), ("bf16", True, False),
+                                               ("bf16", False, False), ("e4m3", True, True), ("bf16", True, True),
+                                               ("e4m3", False, True), ("bf16", False, True)])
+def test_decode_range(skv, orc, dtype, aligned, exp):
     """A token range decoded through the offset index equals the same tokens
-    of the oracle's decode of the whole container (e4m3: decode_e4m3; bf16:
-    decode_bf16, or the per-table LDS decoder for unaligned buffers)."""
+    of the oracle's decode of the whole container (decode_e4m3 / decode_bf16
+    with per-channel or exponent-class tables, or the per-table LDS decoder
+    for unaligned buffers)."""
     cfg = gen.Config(95, f"range-{dtype}", dtype, 2, 2, 1024, 256)
-    t, p, tabs, oshape = residual_case(skv, orc, cfg)
+    t, p, tabs, oshape = (exp_case if exp else residual_case)(skv, orc, cfg)
     cont = skv.encode(tabs, t, p)
     torch.cuda.synchronize()
     pn = p.cpu().numpy()
@@ -524,7 +527,7 @@ def test_decode_range(skv, orc, dtype, aligned):
     want = orc.decode(tabs.bytes(), cont.cpu().numpy().tobytes(), pn, pn, threads=8)
     assert np.array_equal(want, t.cpu().numpy())
     for a, b in RANGES:
-        say(f"[parity] range {dtype} aligned={aligned}: tokens [{a}, {b})")
+        say(f"[parity] range {dtype} aligned={aligned} exp={exp}: tokens [{a}, {b})")
         pr = p[:, :, a:b].contiguous()
         out = torch.zeros_like(pr)
         if not aligned:
