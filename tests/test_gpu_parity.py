@@ -437,13 +437,14 @@ def test_exponent_mode_escapes_and_unaligned(skv, orc, dtype):
     assert torch.equal(out, t)
 
 
-@pytest.mark.parametrize("exp", [True, False])
-def test_e4m3_corruption_verdicts(skv, orc, exp):
-    """Damaged e4m3 containers (per-channel or exponent-class tables): the
-    decoder reaches the oracle's verdict on every bit flip in the coded part of
-    a stream (a flip can leave a consistent stream, which both then decode
-    alike), and refuses an index past the payload and another blob."""
-    cfg = gen.Config(100, "exp-corrupt", "e4m3", 1, 2, 512, 128)
+@pytest.mark.parametrize("dtype,exp", [("e4m3", True), ("e4m3", False), ("bf16", True), ("bf16", False)])
+def test_corruption_verdicts(skv, orc, dtype, exp):
+    """Damaged containers (either element type, per-channel or exponent-class
+    tables): the decoder reaches the oracle's verdict on every bit flip in the
+    coded part of a stream (a flip can leave a consistent stream, which both
+    then decode alike), and refuses an index past the payload and another
+    blob."""
+    cfg = gen.Config(100, f"corrupt-{dtype}", dtype, 1, 2, 512, 128)
     t, p, tabs, oshape = exp_case(skv, orc, cfg) if exp else residual_case(skv, orc, cfg)
     cont = skv.encode(tabs, t, p)
     good = cont.cpu().numpy()
@@ -460,7 +461,7 @@ def test_e4m3_corruption_verdicts(skv, orc, exp):
         bad = good.copy()
         pos = head + int(rng.integers(a, a + 132 + 2 * nw))
         bad[pos] ^= np.uint8(1 << int(rng.integers(0, 8)))
-        say(f"[parity] e4m3 corrupt trial {trials} (exponent tables {exp}): stream {st} byte {pos}")
+        say(f"[parity] {dtype} corrupt trial {trials} (exponent tables {exp}): stream {st} byte {pos}")
         want = np.zeros_like(tn)
         rc = orc.decode_rc(tabs.bytes(), bad.tobytes(), pn, want)
         if rc == orc.E_CORRUPT:
@@ -479,7 +480,8 @@ def test_e4m3_corruption_verdicts(skv, orc, exp):
         skv.decode(tabs, torch.from_numpy(bad).cuda(), p)
     assert e.value.status == skv.ERR_CORRUPT
     ct, cp = gen.residual_array(cfg, gen.CALIB, tokens=256)
-    other = skv.fit_tables(skv.E4M3, skv.RESIDUAL if exp else skv.RESIDUAL_EXP, 1, 2, 128, ct.numpy(), cp.numpy(), 256)
+    other = skv.fit_tables(_dt(cfg, skv), skv.RESIDUAL if exp else skv.RESIDUAL_EXP, 1, 2, 128, ct.numpy(), cp.numpy(),
+                           256)
     with pytest.raises(skv.SkvError) as e:
         skv.decode(other, cont, p)
     assert e.value.status == skv.ERR_TABLES
