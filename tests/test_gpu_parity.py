@@ -437,17 +437,24 @@ def test_exponent_mode_escapes_and_unaligned(skv, orc, dtype):
     assert torch.equal(out, t)
 
 
-@pytest.mark.parametrize("dtype,exp", [("e4m3", True), ("e4m3", False), ("bf16", True), ("bf16", False)])
-def test_corruption_verdicts(skv, orc, dtype, exp):
+@pytest.mark.parametrize("dtype,exp,aligned", [("e4m3", True, True), ("e4m3", False, True), ("bf16", True, True),
+                                               ("bf16", False, True), ("e4m3", False, False), ("bf16", True, False)])
+def test_corruption_verdicts(skv, orc, dtype, exp, aligned):
     """Damaged containers (either element type, per-channel or exponent-class
-    tables): the decoder reaches the oracle's verdict on every bit flip in the
-    coded part of a stream (a flip can leave a consistent stream, which both
-    then decode alike), and refuses an index past the payload and another
-    blob."""
+    tables; unaligned buffers take the per-table LDS or per-stream decoder):
+    the decoder reaches the oracle's verdict on every bit flip in the coded
+    part of a stream (a flip can leave a consistent stream, which both then
+    decode alike), and refuses an index past the payload and another blob."""
     cfg = gen.Config(100, f"corrupt-{dtype}", dtype, 1, 2, 512, 128)
     t, p, tabs, oshape = exp_case(skv, orc, cfg) if exp else residual_case(skv, orc, cfg)
     cont = skv.encode(tabs, t, p)
     good = cont.cpu().numpy()
+    pd = p if aligned else _offset_copy(p, 1)
+
+    def dec(tables, c):
+        out = torch.zeros_like(t) if aligned else _offset_copy(torch.zeros_like(t), 1)
+        return skv.decode_into(tables, c, pd, out)
+
     n, idx, head = _parse(good.tobytes())
     rng = np.random.default_rng(8)
     pn, tn = p.cpu().numpy(), t.cpu().numpy()
@@ -461,31 +468,31 @@ def test_corruption_verdicts(skv, orc, dtype, exp):
         bad = good.copy()
         pos = head + int(rng.integers(a, a + 132 + 2 * nw))
         bad[pos] ^= np.uint8(1 << int(rng.integers(0, 8)))
-        say(f"[parity] {dtype} corrupt trial {trials} (exponent tables {exp}): stream {st} byte {pos}")
+        say(f"[parity] {dtype} corrupt trial {trials} (exponent tables {exp}, aligned {aligned}): stream {st} byte {pos}")
         want = np.zeros_like(tn)
         rc = orc.decode_rc(tabs.bytes(), bad.tobytes(), pn, want)
         if rc == orc.E_CORRUPT:
             with pytest.raises(skv.SkvError) as e:
-                skv.decode(tabs, torch.from_numpy(bad).cuda(), p)
+                dec(tabs, torch.from_numpy(bad).cuda())
             assert e.value.status == skv.ERR_CORRUPT
             refused += 1
         else:
             assert rc == orc.OK
-            assert np.array_equal(skv.decode(tabs, torch.from_numpy(bad).cuda(), p).cpu().numpy(), want)
+            assert np.array_equal(dec(tabs, torch.from_numpy(bad).cuda()).cpu().numpy(), want)
         trials += 1
     assert refused >= 20
     bad = good.copy()
     bad[64 + 8 * 3:64 + 8 * 4] = np.frombuffer(struct.pack("<Q", 1 << 40), np.uint8)
     with pytest.raises(skv.SkvError) as e:
-        skv.decode(tabs, torch.from_numpy(bad).cuda(), p)
+        dec(tabs, torch.from_numpy(bad).cuda())
     assert e.value.status == skv.ERR_CORRUPT
     ct, cp = gen.residual_array(cfg, gen.CALIB, tokens=256)
     other = skv.fit_tables(_dt(cfg, skv), skv.RESIDUAL if exp else skv.RESIDUAL_EXP, 1, 2, 128, ct.numpy(), cp.numpy(),
                            256)
     with pytest.raises(skv.SkvError) as e:
-        skv.decode(other, cont, p)
+        dec(other, cont)
     assert e.value.status == skv.ERR_TABLES
-    assert torch.equal(skv.decode(tabs, cont, p), t)
+    assert torch.equal(dec(tabs, cont), t)
 
 
 def test_exponent_mode_full_size_e4m3(skv, orc):
