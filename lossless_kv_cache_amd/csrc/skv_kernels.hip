@@ -3739,14 +3739,17 @@ constexpr uint32_t kLdsThreads = 1024;
 constexpr size_t kLdsLimit = 160 * 1024;
 
 // Work decomposition of the LDS kernels for a residual-mode shape.
-LdsGeo lds_geometry(const skv_shape& s, uint32_t cgw = 1) {
+// max_tbc: token blocks per workgroup at most (a whole slab's 256 for the tiled kernels but the e4m3
+// pair encoders, whose workgroups take 128: measured faster than 256, 64 or 32 on the Qwen3-8B-shaped cache)
+constexpr uint32_t kPairChunk = 128;
+LdsGeo lds_geometry(const skv_shape& s, uint32_t cgw = 1, uint32_t max_tbc = 256) {
     const uint32_t ncg = s.channels / kLanes, ntb = s.tokens / kSteps;
     const uint32_t line = s.dtype == SKV_E4M3 ? 4u : 2u;    // channel groups per 128-byte row segment
     LdsGeo g;
     g.cgw = cgw;
     g.G = (ncg % line == 0) ? line : (ncg % 2 == 0 ? 2u : 1u);
     g.G = std::max(1u, g.G / cgw);
-    g.tbc = std::min<uint32_t>(ntb, 256u);
+    g.tbc = std::min<uint32_t>(ntb, max_tbc);
     // a workgroup's encoder scratch (tbc streams, ncg apart) is addressed with offsets below 2^31
     const uint64_t sstride = uint64_t(ncg) * 2 * kSyms * (s.dtype == SKV_E4M3 ? 1u : 2u);
     while (g.tbc > 1 && uint64_t(g.tbc) * sstride >= (1ull << 31)) g.tbc /= 2;
@@ -3831,7 +3834,7 @@ hipError_t encode_code(const EncodeLaunch& a, const DevTables& t, hipStream_t st
         });
     } else if (DT == SKV_E4M3 && MODE == SKV_RESIDUAL_EXP && fits && ncg % 4 == 0 && aligned &&
                3 * (encode_exp_lds(fc_stride(t)) + 256) <= kLdsLimit) {
-        const LdsGeo lg = lds_geometry(a.shape, 2);
+        const LdsGeo lg = lds_geometry(a.shape, 2, kPairChunk);
         const size_t lp = encode_exp_lds(fc_stride(t));
         hipError_t e = allow_lds(encode_pairs_exp, lp);
         if (e != hipSuccess) return e;
@@ -3841,7 +3844,7 @@ hipError_t encode_code(const EncodeLaunch& a, const DevTables& t, hipStream_t st
         });
     } else if (DT == SKV_E4M3 && MODE == SKV_RESIDUAL && fits && ncg % 4 == 0 &&
                2 * encode_groups_lds(1, fc_stride(t)) + 512 <= kLdsLimit && aligned) {
-        const LdsGeo lg = lds_geometry(a.shape, 2);
+        const LdsGeo lg = lds_geometry(a.shape, 2, kPairChunk);
         const size_t lp = encode_groups_lds(1, fc_stride(t));
         hipError_t e = allow_lds(encode_pairs, lp);
         if (e != hipSuccess) return e;
